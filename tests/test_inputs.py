@@ -1,0 +1,35 @@
+"""Seeded input generator: determinism, casts, recipe structure (CPU only)."""
+import numpy as np
+import pytest
+
+import lla_inputs
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = (np.random.default_rng(5).standard_normal(200000) * 7).astype(np.float32)
+    x[:4] = [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]  # ties to even
+    ours = lla_inputs.round_to_bf16(x)
+    ref = torch.tensor(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+
+
+def test_generate_is_deterministic_and_exactly_cast():
+    w = lla_inputs.WORKLOADS["d12"].with_shape(B=1, H=2, n=32)
+    a = lla_inputs.generate(w)
+    b = lla_inputs.generate(w)
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x, y)
+        assert x.dtype == np.float32 and x.shape == (1, 2, 32, 64)
+        assert np.array_equal(lla_inputs.round_to_bf16(x), x)  # exactly bf16
+
+
+def test_recipes_have_their_structure():
+    q, k, v = lla_inputs.make_inputs(1, 2, 256, 64, 1, "halfnormal")
+    assert (k[..., 0] >= 0).all() and abs(np.std(q) - 64 ** -0.25) < 0.02
+    q, k, v = lla_inputs.make_inputs(1, 2, 64, 64, 2, "rms")
+    assert np.allclose(np.mean(q * q, -1), 1.0, atol=1e-5)
+    q, k, v, ex = lla_inputs.make_inputs(1, 1, 64, 16, 0, "affine_exact", extras=True)
+    q0, k0, _ = lla_inputs.make_inputs(1, 1, 64, 16, 0, "normal")
+    assert np.array_equal(q, q0) and np.array_equal(k, k0)  # same q, k as the plain draw
+    assert np.allclose(v[0, 0], k[0, 0] @ ex["A"][0, 0].T + ex["c"][0, 0])
