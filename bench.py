@@ -1,0 +1,217 @@
+"""Throughput of the causal LLA forward on one MI355X.
+
+One step is one lla_forward call over the whole workload (every query row of every head)
+with q, k, v already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d24] [--path auto]
+
+The default workload is B=2, H=16, n=4096, d=64 with bf16 inputs (head shape of a
+1024-wide, 16-head model), h = 8, lambda = 1e-2.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LLA fwd queries/s + TFLOP/s (% MFMA peak) at B2 H16 n4096 d64 bf16, 1 GPU"
+
+# MI355X published peaks.
+PEAK = {
+    "hbm_GBps": 8000.0,
+    "mfma_f16_TFLOPs": 2516.6,   # dense fp16/bf16 matrix
+    "valu_f64_TFLOPs": 78.6,     # fp64 vector
+    "valu_f32_TFLOPs": 157.3,    # fp32 vector
+}
+
+
+def alg_flops(B, H, n, d, form):
+    """Algorithmic flops of one forward: causal pairs only, the upper triangle of the key
+    covariance, no recomputation.  form "NS": explicit value-key cross moment (the
+    formulation the fp64 path executes); form "min": cross moment applied through a probe
+    pass."""
+    P = B * H * n * (n + 1) // 2
+    N = B * H * n
+    common = 2 * d + 2 * (1 + 2 * d) + d * (d + 1)
+    if form == "NS":
+        return P * (common + 2 * d * d) + N * (d ** 3 / 3 + 2 * d * d + 2 * d * d + 2 * d)
+    return P * (common + 4 * d + 2) + N * (d ** 3 / 3 + 2 * d * d + 4 * d)
+
+
+# Dominant kernel of each path and the arithmetic it performs.
+PATH_INFO = {
+    "exact": dict(kernel="lla_exact_kernel", form="NS", bound="alu", peak=PEAK["valu_f64_TFLOPs"],
+                  arith="f64"),
+}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "local_linear_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, if it was taken
+    on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[f"{kernel}/{workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, seconds):
+    """The fp64 oracle on a bounded random sample of the workload's rows."""
+    import numpy as np
+
+    from oracle import default_workers, lla_rows
+    workers = default_workers()
+    rng = np.random.default_rng(12345)
+    total_cost = w.B * w.H * w.n * (w.n + 1) / 2
+    done_rows, done_cost, elapsed = 0, 0.0, 0.0
+    batch = 8 * workers
+    while elapsed < seconds:
+        rows = [(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.n)))
+                for _ in range(batch)]
+        t0 = time.perf_counter()
+        lla_rows(q, k, v, w.h, w.lam, rows, workers=workers)
+        elapsed += time.perf_counter() - t0
+        done_rows += len(rows)
+        done_cost += sum(i + 1 for (_, _, i) in rows)
+        batch = min(4 * batch, 512 * workers)
+    full_seconds = elapsed * total_cost / done_cost
+    return {
+        "value": w.queries / full_seconds,
+        "unit": "queries/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"{done_rows} uniformly drawn rows of the same workload (seed 12345), "
+                   f"{elapsed:.1f} s in {workers} worker processes; full-workload time "
+                   f"{full_seconds:.0f} s projected with per-row cost i+1"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="d24")
+    ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the LLA forward here is built and measured on a "
+              "single MI355X (heads shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lla_inputs
+    from local_linear_attention_amd import lla_forward_ex, lla_path_available, load_library
+
+    w = lla_inputs.WORKLOADS[args.workload]
+    q, k, v, _ = lla_inputs.generate(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v))
+    out = torch.empty(tq.shape, dtype=torch.float32, device=dev)
+    load_library()
+
+    path = args.path
+    if path == "auto":
+        # the path the library picks by default for this dtype and head size
+        path = "fast" if (w.dtype == "bf16" and lla_path_available("fast", w.dtype, w.d)) \
+            else "exact"
+    info = PATH_INFO[path]
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        lla_forward_ex(tq, tk, tv, w.h, w.lam, path=path, out=out, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for s in range(args.steps):
+        starts[s].record(stream)
+        lla_forward_ex(tq, tk, tv, w.h, w.lam, path=path, out=out, stream=stream)
+        ends[s].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    assert torch.isfinite(out).all().item(), "non-finite output"
+
+    flops = alg_flops(w.B, w.H, w.n, w.d, info["form"])
+    kernel_ms = statistics.mean(per_ms)           # one kernel launch per step
+    achieved_tflops = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = load_traffic(info["kernel"], w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": w.queries / (ms_per_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": info["arith"],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs, h={w.h:g}, "
+                        f"lambda={w.lam:g}",
+            "B": w.B, "H": w.H, "n": w.n, "d": w.d, "input_dtype": w.dtype,
+            "h": w.h, "lambda": w.lam, "path": path, "queries": w.queries,
+        },
+        "tflops": achieved_tflops,
+        "flop_count": {"formulation": info["form"], "flops": flops,
+                       "F_NS": alg_flops(w.B, w.H, w.n, w.d, "NS"),
+                       "F_min": alg_flops(w.B, w.H, w.n, w.d, "min")},
+        "timing_ms": {"median": statistics.median(per_ms), "p10": float(np.percentile(per_ms, 10)),
+                      "p90": float(np.percentile(per_ms, 90))},
+        "roofline": {
+            "kernel": info["kernel"],
+            "bound": info["bound"],
+            "achieved": achieved_tflops,
+            "peak": info["peak"],
+            "unit": "TFLOP/s",
+            "frac": achieved_tflops / info["peak"],
+            "traffic": traffic,
+        },
+        "mfma_peak_frac": achieved_tflops / PEAK["mfma_f16_TFLOPs"],
+        "gfx": torch.cuda.get_device_properties(dev).gcnArchName,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,109 @@
+/*
+ * liblla: causal Local Linear Attention (LLA) forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources: the "Parallax" blog post by Tilde Research, section 2
+ * "Canonical Formulation"; the arXiv HTML page "Parallax: Parameterized Local Linear
+ * Attention for Language Modeling", the LLA definition paragraph):
+ *
+ *   For every batch b, head hd and query row i, LLA fits a local linear model
+ *   b_i + W (x - q_i) to the causal prefix {(k_j, v_j) : j <= i} with kernel weights
+ *   w_ij = exp(q_i . k_j / h) and ridge penalty lambda ||W||_F^2, and returns the
+ *   intercept b_i.  In the centred form of the blog's Appendix E (rank-one split and
+ *   Sherman-Morrison), with a per-row shift m_i and wt_ij = exp(q_i.k_j/h - m_i):
+ *
+ *     b_i = vbar_i - C_vk (C_kk + lambda e^{-m_i} I)^{-1} (kbar_i - q_i)
+ *
+ *   where kbar, vbar are the wt-weighted means of the prefix keys and values and C_kk,
+ *   C_vk the wt-weighted centred key covariance and value-key cross moment.  The
+ *   e^{-m_i} on the ridge makes the max shift exact.
+ *
+ * Layout: q, k, v are [B, H, n, d] contiguous row-major device arrays (batch, head,
+ * position, feature), element type given by `dtype`, 16-byte aligned.  `out` is
+ * [B, H, n, d] contiguous fp32 on the device.  Value width equals d.  Heads are
+ * independent.
+ *
+ * Ownership: the caller owns every buffer.  The library allocates, frees and retains no
+ * device memory and keeps no state between calls; calls are reentrant.  `out` must not
+ * overlap q, k or v.
+ *
+ * Errors: arguments are validated on the host before any HIP call; a failed check
+ * returns its status and touches nothing.  Work is enqueued asynchronously on `stream`
+ * (a hipStream_t; NULL means the default stream); the library never synchronises.
+ * A launch failure returns LLA_ERR_HIP; faults during execution surface at the caller's
+ * next synchronisation of that stream.
+ */
+#ifndef LLA_H_
+#define LLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k and v. */
+typedef enum {
+    LLA_DTYPE_F32 = 0,   /* IEEE binary32 */
+    LLA_DTYPE_BF16 = 1   /* bfloat16 (upper half of binary32) */
+} lla_dtype_t;
+
+typedef enum {
+    LLA_OK = 0,
+    LLA_ERR_NULL = 1,         /* a required pointer is NULL */
+    LLA_ERR_SHAPE = 2,        /* B, H or n < 1, or sizes overflow the index range */
+    LLA_ERR_PARAM = 3,        /* h <= 0, lambda < 0, or either not finite */
+    LLA_ERR_UNSUPPORTED = 4,  /* d not in {16, 32, 64, 128}, unknown dtype, or a forced
+                                 path that does not cover this (dtype, d) */
+    LLA_ERR_WORKSPACE = 5,    /* reserved */
+    LLA_ERR_HIP = 6,          /* a HIP launch or query failed */
+    LLA_ERR_ALIAS = 7         /* out overlaps q, k or v */
+} lla_status_t;
+
+/* Kernel path selection for lla_forward_ex. */
+typedef enum {
+    LLA_PATH_AUTO = 0,   /* fp32 inputs -> EXACT; bf16 inputs -> FAST where built */
+    LLA_PATH_EXACT = 1,  /* fp64 accumulation and solve, any supported (dtype, d) */
+    LLA_PATH_FAST = 2    /* matrix-core path for bf16 inputs (d = 64, 128) */
+} lla_path_t;
+
+/*
+ * Causal LLA forward (spec signature; dtype and stream appended).
+ *   q, k, v : device pointers to [B, H, n, d] arrays of `dtype`
+ *   out     : device pointer to [B, H, n, d] fp32 output
+ *   B, H, n : batch, heads, sequence length (>= 1)
+ *   d       : head dimension, one of 16, 32, 64, 128 (value width is d too)
+ *   h       : kernel bandwidth (> 0), weights exp(q.k / h)
+ *   lambda  : ridge strength (>= 0).  lambda = 0 is accepted; rows whose prefix leaves the
+ *             key covariance singular (i < d for generic keys) then have no unique fit and
+ *             their output is finite but unspecified (pivots below 1e-12 of the largest
+ *             diagonal are dropped).
+ *   dtype   : element type of q, k, v
+ *   stream  : hipStream_t to enqueue on (NULL = default stream)
+ */
+lla_status_t lla_forward(const void* q, const void* k, const void* v, float* out,
+                         int64_t B, int64_t H, int64_t n, int64_t d,
+                         double h, double lambda,
+                         lla_dtype_t dtype, void* stream);
+
+/* Same as lla_forward with an explicit kernel path (for testing and measurement). */
+lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* out,
+                            int64_t B, int64_t H, int64_t n, int64_t d,
+                            double h, double lambda,
+                            lla_dtype_t dtype, void* stream, lla_path_t path);
+
+/* 1 if `path` covers inputs of `dtype` with head dimension `d`, else 0.  Host-only: makes
+ * no HIP call.  LLA_PATH_AUTO and LLA_PATH_EXACT cover every supported (dtype, d). */
+int lla_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d);
+
+/* Static description of a status code; never NULL. */
+const char* lla_status_string(lla_status_t s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int lla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLA_H_ */

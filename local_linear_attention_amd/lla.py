@@ -1,0 +1,128 @@
+"""Thin ctypes binding of liblla (argument marshalling only).
+
+Every step of the forward runs in the library's HIP kernels; this module checks tensor
+shapes, dtypes and devices, allocates the output when asked, and passes raw device
+pointers and the current HIP stream to the C entry points of the same names.  There is
+no CPU fallback: if ``liblla.so`` is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["lla_forward", "lla_forward_ex", "lla_path_available", "lla_status_string",
+           "lla_version", "LLAError",
+           "library_path", "load_library", "STATUS", "PATHS", "DTYPES"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+STATUS = {0: "LLA_OK", 1: "LLA_ERR_NULL", 2: "LLA_ERR_SHAPE", 3: "LLA_ERR_PARAM",
+          4: "LLA_ERR_UNSUPPORTED", 5: "LLA_ERR_WORKSPACE", 6: "LLA_ERR_HIP", 7: "LLA_ERR_ALIAS"}
+PATHS = {"auto": 0, "exact": 1, "fast": 2}
+DTYPES = {"f32": 0, "bf16": 1}
+
+
+class LLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{where}: {self.name} ({lla_status_string(status)})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "liblla.so")
+
+
+def load_library():
+    """Load liblla.so (built in-tree by __graft_entry__.build()); raises if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    i64, f64, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.lla_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int, vp]
+    lib.lla_forward.restype = ctypes.c_int
+    lib.lla_forward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int,
+                                   vp, ctypes.c_int]
+    lib.lla_forward_ex.restype = ctypes.c_int
+    lib.lla_status_string.argtypes = [ctypes.c_int]
+    lib.lla_status_string.restype = ctypes.c_char_p
+    lib.lla_path_available.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64]
+    lib.lla_path_available.restype = ctypes.c_int
+    lib.lla_version.argtypes = []
+    lib.lla_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def lla_status_string(status: int) -> str:
+    return load_library().lla_status_string(int(status)).decode()
+
+
+def lla_path_available(path: str, dtype: str, d: int) -> bool:
+    """Whether kernel path "auto" / "exact" / "fast" covers (dtype "f32"/"bf16", d)."""
+    return bool(load_library().lla_path_available(PATHS[path], DTYPES[dtype], int(d)))
+
+
+def lla_version() -> int:
+    return int(load_library().lla_version())
+
+
+def _marshal(q, k, v, out):
+    import torch
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError(f"q, k, v must share one [B, H, n, d] shape; got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if q.dtype == torch.float32:
+        dtype = DTYPES["f32"]
+    elif q.dtype == torch.bfloat16:
+        dtype = DTYPES["bf16"]
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous float32 tensor of q's shape on q's device")
+    return dtype, out
+
+
+def lla_forward_ex(q, k, v, h: float, lam: float, path: str = "auto", out=None, stream=None):
+    """LLA forward of device tensors q, k, v [B, H, n, d] (fp32 or bf16) -> fp32 out.
+
+    ``path`` is "auto", "exact" or "fast"; ``stream`` a torch stream (default: current)."""
+    import torch
+    dtype, out = _marshal(q, k, v, out)
+    B, H, n, d = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().lla_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       B, H, n, d, float(h), float(lam), dtype,
+                                       ctypes.c_void_p(stream.cuda_stream), PATHS[path])
+    if st != 0:
+        raise LLAError(st, "lla_forward_ex")
+    return out
+
+
+def lla_forward(q, k, v, h: float, lam: float, out=None, stream=None):
+    """LLA forward through the library's default path selection."""
+    import torch
+    dtype, out = _marshal(q, k, v, out)
+    B, H, n, d = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().lla_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    B, H, n, d, float(h), float(lam), dtype,
+                                    ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise LLAError(st, "lla_forward")
+    return out

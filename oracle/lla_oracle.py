@@ -95,10 +95,12 @@ def lla_row(q_i, K, V, h, lam):
 
 
 def _rows_worker(args):
-    q, k, v, h, lam, items = args
-    out = np.empty((len(items), v.shape[-1]), dtype=np.float64)
-    for t, (bh, i) in enumerate(items):
-        out[t] = lla_row(q[bh, i], k[bh, : i + 1], v[bh, : i + 1], h, lam)
+    """Rows of one head: qh [r, d] (the queries of the rows), kh/vh the prefix up to the
+    longest row, idx the row positions."""
+    qh, kh, vh, idx, h, lam = args
+    out = np.empty((len(idx), vh.shape[-1]), dtype=np.float64)
+    for t, i in enumerate(idx):
+        out[t] = lla_row(qh[t], kh[: i + 1], vh[: i + 1], h, lam)
     return out
 
 
@@ -107,33 +109,50 @@ def lla_rows(q, k, v, h, lam, rows, workers=1):
 
     q, k, v: [B, H, n, d] arrays (any float dtype; upcast exactly to fp64).
     rows: iterable of (b, head, i).  Returns an fp64 array [len(rows), d_v].
+    With workers > 1 the rows run in a process pool, in tasks of one head each.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    B, H, n, d = q.shape
-    qf = q.reshape(B * H, n, d)
-    kf = k.reshape(B * H, n, d)
-    vf = v.reshape(B * H, n, v.shape[-1])
-    items = [(b * H + hh, i) for (b, hh, i) in rows]
-    if workers <= 1 or len(items) < 64:
-        return _rows_worker((qf, kf, vf, h, lam, items))
-    # Split the rows into chunks of about equal cost (row i costs ~ i+1).
-    order = sorted(range(len(items)), key=lambda t: -items[t][1])
-    chunks = [[] for _ in range(4 * workers)]
-    loads = [0] * len(chunks)
-    for t in order:
-        c = min(range(len(chunks)), key=loads.__getitem__)
-        chunks[c].append(t)
-        loads[c] += items[t][1] + 1
-    chunks = [c for c in chunks if c]
-    out = np.empty((len(items), vf.shape[-1]), dtype=np.float64)
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    rows = list(rows)
+    dv = v.shape[-1]
+    # Group rows into tasks (one head per task, each task about the same cost).
+    by_head = {}
+    for t, (b, hh, i) in enumerate(rows):
+        by_head.setdefault((b, hh), []).append((i, t))
+    total = sum(i + 1 for (_, _, i) in rows)
+    target = max(1, total // max(1, 4 * workers))
+    tasks = []
+    for (b, hh), lst in by_head.items():
+        lst.sort(reverse=True)
+        cur, cost = [], 0
+        for i, t in lst:
+            cur.append((i, t))
+            cost += i + 1
+            if cost >= target:
+                tasks.append(((b, hh), cur))
+                cur, cost = [], 0
+        if cur:
+            tasks.append(((b, hh), cur))
+
+    def task_args(task):
+        (b, hh), lst = task
+        top = max(i for i, _ in lst) + 1
+        idx = [i for i, _ in lst]
+        return (np.asarray(q[b, hh, idx], np.float64), np.asarray(k[b, hh, :top], np.float64),
+                np.asarray(v[b, hh, :top], np.float64), idx, h, lam)
+
+    out = np.empty((len(rows), dv), dtype=np.float64)
+    if workers <= 1 or len(tasks) < 2:
+        for task in tasks:
+            res = _rows_worker(task_args(task))
+            for r, (_, t) in zip(res, task[1]):
+                out[t] = r
+        return out
     with _cf.ProcessPoolExecutor(max_workers=workers) as ex:
-        futs = {ex.submit(_rows_worker, (qf, kf, vf, h, lam, [items[t] for t in c])): c
-                for c in chunks}
+        futs = {ex.submit(_rows_worker, task_args(task)): task for task in tasks}
         for f in _cf.as_completed(futs):
-            res = f.result()
-            for r, t in zip(res, futs[f]):
+            for r, (_, t) in zip(f.result(), futs[f][1]):
                 out[t] = r
     return out
 

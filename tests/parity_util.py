@@ -1,0 +1,65 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the library
+through its C ABI, pick sample rows, and measure the per-row normwise error."""
+import numpy as np
+
+import lla_inputs
+
+TOL = {"f32": 1e-4, "bf16": 3e-3}   # per-row max|out - ref| / max|ref|
+
+
+def require_gpu():
+    import pytest
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    return torch
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)  # exact: the values are already bf16-representable
+    return t.cuda().contiguous()
+
+
+def run_gpu(q, k, v, dtype, h, lam, path="auto"):
+    import torch
+    from local_linear_attention_amd import lla_forward, lla_forward_ex
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    if path == "default":
+        out = lla_forward(tq, tk, tv, h, lam)
+    else:
+        out = lla_forward_ex(tq, tk, tv, h, lam, path=path)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def row_errors(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row normwise relative error over the last axis."""
+    num = np.max(np.abs(got - ref), axis=-1)
+    den = np.maximum(np.max(np.abs(ref), axis=-1), 1e-30)
+    return num / den
+
+
+def sample_rows(B, H, n, d, seed, per_head=6):
+    """Seeded sample: the hardest rows (i < 2d, around d) of every head, the last row of
+    every head, and random rows."""
+    rng = np.random.default_rng(1000 + seed)
+    fixed = sorted({i for i in (0, 1, 2, 3, d // 2, d - 1, d, d + 1, 2 * d, n - 1) if 0 <= i < n})
+    rows = []
+    for b in range(B):
+        for hh in range(H):
+            pick = set(fixed[:: max(1, len(fixed) // 4)]) | {n - 1}
+            pick |= set(int(x) for x in rng.integers(0, n, per_head))
+            pick |= set(int(x) for x in rng.integers(0, min(n, 2 * d + 2), 2))
+            rows += [(b, hh, i) for i in sorted(pick)]
+    return rows
+
+
+def workload_arrays(name, **shape):
+    w = lla_inputs.WORKLOADS[name]
+    if shape:
+        w = w.with_shape(**shape)
+    q, k, v, _ = lla_inputs.generate(w)
+    return w, q, k, v

@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/lla.h declares, and rejects bad arguments with the documented status before any
+HIP call (the pointers passed here are never dereferenced)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lla.h")
+
+
+def _lib():
+    from local_linear_attention_amd import lla
+    if not os.path.exists(lla.library_path()):
+        pytest.fail("liblla.so is not built (run __graft_entry__.build())")
+    return lla.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(lla_\w+)\s*\(", src, flags=re.M)))
+
+
+def declared_enums():
+    src = open(HEADER).read()
+    return {name: int(val) for name, val in re.findall(r"\b(LLA_\w+)\s*=\s*(\d+)", src)}
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["lla_forward", "lla_forward_ex", "lla_path_available",
+                                    "lla_status_string", "lla_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header_and_binding():
+    from local_linear_attention_amd import lla
+    enums = declared_enums()
+    for code, name in lla.STATUS.items():
+        assert enums[name] == code
+    assert enums["LLA_PATH_AUTO"] == lla.PATHS["auto"]
+    assert enums["LLA_PATH_EXACT"] == lla.PATHS["exact"]
+    assert enums["LLA_PATH_FAST"] == lla.PATHS["fast"]
+    assert enums["LLA_DTYPE_F32"] == lla.DTYPES["f32"]
+    assert enums["LLA_DTYPE_BF16"] == lla.DTYPES["bf16"]
+
+
+def test_version_and_status_strings():
+    lib = _lib()
+    assert lib.lla_version() >= 100
+    for s in range(8):
+        assert lib.lla_status_string(s)
+    assert lib.lla_status_string(99) == b"unknown status"
+
+
+# Distinct fake device addresses, far apart, so only the tested fault triggers.
+Q, K, V, OUT = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def call(lib, q=Q, k=K, v=V, out=OUT, B=1, H=2, n=16, d=64, h=8.0, lam=0.1, dtype=1, path=None):
+    args = [ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), ctypes.c_void_p(out),
+            B, H, n, d, h, lam, dtype, None]
+    if path is None:
+        return lib.lla_forward(*args)
+    return lib.lla_forward_ex(*args, path)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(out=0), 1),
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(n=0), 2), (dict(n=2 ** 31), 2),
+    (dict(B=2 ** 16, H=2 ** 16, n=2), 2),
+    (dict(h=0.0), 3), (dict(h=-1.0), 3), (dict(h=math.inf), 3), (dict(h=math.nan), 3),
+    (dict(lam=-1e-3), 3), (dict(lam=math.nan), 3), (dict(lam=math.inf), 3),
+    (dict(d=48), 4), (dict(d=256), 4), (dict(d=0), 4), (dict(dtype=2), 4),
+    (dict(out=Q + 64), 7), (dict(out=V - 64), 7),
+])
+def test_invalid_arguments_are_rejected_before_any_launch(kw, expect):
+    lib = _lib()
+    assert call(lib, **kw) == expect
+    assert call(lib, path=1, **kw) == expect
+
+
+def test_unknown_path_is_rejected():
+    lib = _lib()
+    assert call(lib, path=7) == 4
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from local_linear_attention_amd import lla
+    monkeypatch.setattr(lla, "_LIB", None)
+    monkeypatch.setattr(lla, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        lla.load_library()
+
+
+def test_path_availability_query():
+    from local_linear_attention_amd import lla
+    for dt in ("f32", "bf16"):
+        for d in (16, 32, 64, 128):
+            assert lla.lla_path_available("auto", dt, d)
+            assert lla.lla_path_available("exact", dt, d)
+        for d in (0, 8, 48, 256):
+            assert not lla.lla_path_available("exact", dt, d)
+    assert not lla.lla_path_available("fast", "f32", 64)  # the matrix-core path is bf16-only
