@@ -45,11 +45,36 @@ def alg_flops(B, H, n, d, form):
     return P * (common + 4 * d + 2) + N * (d ** 3 / 3 + 2 * d * d + 4 * d)
 
 
-# Dominant kernel of each path and the arithmetic it performs.
-PATH_INFO = {
-    "exact": dict(kernel="lla_exact_kernel", form="NS", bound="alu", peak=PEAK["valu_f64_TFLOPs"],
-                  arith="f64"),
+# Arithmetic of each path (the dtype field) and the bound of each kernel.
+PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d: f64)"}
+KERNEL_BOUND = {
+    "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla_stats_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_moments_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
 }
+
+
+def pair_count(BH, lo, hi):
+    """Causal pairs (i, j <= i) of rows lo <= i < hi, over BH heads."""
+    return BH * (hi * (hi + 1) // 2 - lo * (lo + 1) // 2)
+
+
+def kernel_flops(name, B, H, n, d, path):
+    """Algorithmic flops (formulation NS, the one both paths execute) of one launch of a
+    kernel: the fast path splits the rows at 2d between the fp64 kernel and the MFMA
+    kernels; the stats kernel owns the score and first-moment terms of its rows, the
+    moments kernel the second moments, the solve and the assembly."""
+    BH = B * H
+    row0 = min(n, 2 * d) if path == "fast" else n
+    per_query = d ** 3 / 3 + 4 * d * d + 2 * d
+    if name == "lla_exact_kernel":
+        return pair_count(BH, 0, row0) * (2 * d + 2 * (1 + 2 * d) + d * (d + 1) + 2 * d * d) \
+            + BH * row0 * per_query
+    if name == "lla_stats_kernel":
+        return pair_count(BH, row0, n) * (2 * d + 2 * (1 + 2 * d))
+    if name == "lla_moments_kernel":
+        return pair_count(BH, row0, n) * (d * (d + 1) + 2 * d * d) + BH * (n - row0) * per_query
+    raise KeyError(name)
 
 
 def kernel_source_hash():
@@ -126,7 +151,8 @@ def main():
     import torch
 
     import lla_inputs
-    from local_linear_attention_amd import lla_forward_ex, lla_path_available, load_library
+    from local_linear_attention_amd import (lla_forward_ex, lla_path_available, lla_profile_collect,
+                                            lla_profile_enable, load_library)
 
     w = lla_inputs.WORKLOADS[args.workload]
     q, k, v, _ = lla_inputs.generate(w)
@@ -142,7 +168,6 @@ def main():
         # the path the library picks by default for this dtype and head size
         path = "fast" if (w.dtype == "bf16" and lla_path_available("fast", w.dtype, w.d)) \
             else "exact"
-    info = PATH_INFO[path]
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(args.warmup):
@@ -166,10 +191,29 @@ def main():
     ms_per_step = total_ms / args.steps
     assert torch.isfinite(out).all().item(), "non-finite output"
 
-    flops = alg_flops(w.B, w.H, w.n, w.d, info["form"])
-    kernel_ms = statistics.mean(per_ms)           # one kernel launch per step
-    achieved_tflops = flops / (kernel_ms * 1e-3) / 1e12
-    traffic = load_traffic(info["kernel"], w.name)
+    # Kernel-level timing: the same steps again with the library's per-launch HIP events.
+    lla_profile_enable(True)
+    lla_profile_collect()
+    for _ in range(args.steps):
+        lla_forward_ex(tq, tk, tv, w.h, w.lam, path=path, out=out, stream=stream)
+    torch.cuda.synchronize()
+    rec = lla_profile_collect()
+    lla_profile_enable(False)
+    per_kernel = {}
+    for name, ms in rec:
+        per_kernel.setdefault(name, []).append(ms)
+    kernels = {}
+    for name, lst in per_kernel.items():
+        fl = kernel_flops(name, w.B, w.H, w.n, w.d, path)
+        avg = statistics.mean(lst)
+        bound, peak = KERNEL_BOUND[name]
+        kernels[name] = {"launches": len(lst), "avg_ms": avg, "flops": fl,
+                         "tflops": fl / (avg * 1e-3) / 1e12, "bound": bound, "peak": peak}
+    dom = max(kernels, key=lambda nm: kernels[nm]["avg_ms"] * kernels[nm]["launches"])
+    dk = kernels[dom]
+    flops = alg_flops(w.B, w.H, w.n, w.d, "NS")
+    achieved_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    traffic = load_traffic(dom, w.name)
 
     result = {
         "metric": METRIC,
@@ -182,7 +226,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": info["arith"],
+        "dtype": PATH_ARITH[path],
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs, h={w.h:g}, "
@@ -191,18 +235,19 @@ def main():
             "h": w.h, "lambda": w.lam, "path": path, "queries": w.queries,
         },
         "tflops": achieved_tflops,
-        "flop_count": {"formulation": info["form"], "flops": flops,
+        "flop_count": {"formulation": "NS", "flops": flops,
                        "F_NS": alg_flops(w.B, w.H, w.n, w.d, "NS"),
                        "F_min": alg_flops(w.B, w.H, w.n, w.d, "min")},
+        "kernels": kernels,
         "timing_ms": {"median": statistics.median(per_ms), "p10": float(np.percentile(per_ms, 10)),
                       "p90": float(np.percentile(per_ms, 90))},
         "roofline": {
-            "kernel": info["kernel"],
-            "bound": info["bound"],
-            "achieved": achieved_tflops,
-            "peak": info["peak"],
+            "kernel": dom,
+            "bound": dk["bound"],
+            "achieved": dk["tflops"],
+            "peak": dk["peak"],
             "unit": "TFLOP/s",
-            "frac": achieved_tflops / info["peak"],
+            "frac": dk["tflops"] / dk["peak"],
             "traffic": traffic,
         },
         "mfma_peak_frac": achieved_tflops / PEAK["mfma_f16_TFLOPs"],

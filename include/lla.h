@@ -22,9 +22,13 @@
  * [B, H, n, d] contiguous fp32 on the device.  Value width equals d.  Heads are
  * independent.
  *
- * Ownership: the caller owns every buffer.  The library allocates, frees and retains no
- * device memory and keeps no state between calls; calls are reentrant.  `out` must not
- * overlap q, k or v.
+ * Ownership: the caller owns q, k, v and out.  lla_forward_ws allocates nothing: the caller
+ * passes the scratch the fast path needs (lla_workspace_size bytes).  lla_forward and
+ * lla_forward_ex take that scratch from a library-owned, stream-ordered memory pool of the
+ * current device (hipMallocFromPoolAsync / hipFreeAsync on `stream`); the pool keeps its
+ * memory for reuse until the process ends.  No other state persists between calls, and
+ * calls are reentrant.  `out` must not overlap q, k or v.  The current HIP device must be
+ * the device of the pointers and of `stream`.
  *
  * Errors: arguments are validated on the host before any HIP call; a failed check
  * returns its status and touches nothing.  Work is enqueued asynchronously on `stream`
@@ -55,8 +59,8 @@ typedef enum {
     LLA_ERR_PARAM = 3,        /* h <= 0, lambda < 0, or either not finite */
     LLA_ERR_UNSUPPORTED = 4,  /* d not in {16, 32, 64, 128}, unknown dtype, or a forced
                                  path that does not cover this (dtype, d) */
-    LLA_ERR_WORKSPACE = 5,    /* reserved */
-    LLA_ERR_HIP = 6,          /* a HIP launch or query failed */
+    LLA_ERR_WORKSPACE = 5,    /* workspace missing or too small (lla_forward_ws) */
+    LLA_ERR_HIP = 6,          /* a HIP launch, query or scratch allocation failed */
     LLA_ERR_ALIAS = 7         /* out overlaps q, k or v */
 } lla_status_t;
 
@@ -64,7 +68,8 @@ typedef enum {
 typedef enum {
     LLA_PATH_AUTO = 0,   /* fp32 inputs -> EXACT; bf16 inputs -> FAST where built */
     LLA_PATH_EXACT = 1,  /* fp64 accumulation and solve, any supported (dtype, d) */
-    LLA_PATH_FAST = 2    /* matrix-core path for bf16 inputs (d = 64, 128) */
+    LLA_PATH_FAST = 2    /* matrix-core path for bf16 inputs (d = 64); inputs must lie in the
+                            fp16 range, and rows i < 2d still run on the fp64 kernel */
 } lla_path_t;
 
 /*
@@ -86,11 +91,36 @@ lla_status_t lla_forward(const void* q, const void* k, const void* v, float* out
                          double h, double lambda,
                          lla_dtype_t dtype, void* stream);
 
-/* Same as lla_forward with an explicit kernel path (for testing and measurement). */
+/* Same as lla_forward with an explicit kernel path (for testing and measurement).
+ * LLA_PATH_FAST on a (dtype, d) it does not cover returns LLA_ERR_UNSUPPORTED. */
 lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* out,
                             int64_t B, int64_t H, int64_t n, int64_t d,
                             double h, double lambda,
                             lla_dtype_t dtype, void* stream, lla_path_t path);
+
+/* Bytes of device scratch that `path` needs for this problem (0 if none, or if the sizes,
+ * dtype or path are invalid).  The fast path keeps per-row statistics there: 4*(2d+4) bytes
+ * for every row at or beyond position 2d. */
+size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
+                          lla_path_t path);
+
+/* lla_forward_ex with caller-provided scratch: `workspace` is a device pointer to at least
+ * lla_workspace_size(...) bytes, 16-byte aligned, not overlapping any other argument, and
+ * not used by any other work until this call's kernels finish on `stream`.  Allocates
+ * nothing.  A missing or short workspace, when one is needed, returns LLA_ERR_WORKSPACE. */
+lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* out,
+                            int64_t B, int64_t H, int64_t n, int64_t d,
+                            double h, double lambda,
+                            lla_dtype_t dtype, void* stream, lla_path_t path,
+                            void* workspace, size_t workspace_bytes);
+
+/* Kernel-level timing.  While enabled, every kernel launch of the library is bracketed by
+ * HIP events on its stream.  lla_profile_collect waits for the recorded events, writes up to
+ * max_entries kernel names (static strings) and durations in milliseconds in launch order,
+ * returns how many it wrote, and clears the record.  Meant for single-threaded measurement;
+ * lla_profile_enable returns the previous setting. */
+int lla_profile_enable(int enable);
+int lla_profile_collect(const char** names, float* ms, int max_entries);
 
 /* 1 if `path` covers inputs of `dtype` with head dimension `d`, else 0.  Host-only: makes
  * no HIP call.  LLA_PATH_AUTO and LLA_PATH_EXACT cover every supported (dtype, d). */

@@ -4,7 +4,7 @@ The compute lives in ``liblla.so`` (hand-written HIP kernels behind a C ABI decl
 ``include/lla.h``); ``lla`` is the ctypes binding.
 """
 from .lla import (  # noqa: F401
-    LLAError, lla_forward, lla_forward_ex, lla_path_available, lla_status_string, lla_version,
-    library_path,
+    LLAError, library_path, lla_forward, lla_forward_ex, lla_forward_ws, lla_path_available,
+    lla_profile_collect, lla_profile_enable, lla_status_string, lla_version, lla_workspace_size,
     load_library,
 )

@@ -1,18 +1,38 @@
-// C ABI of liblla: argument validation, path selection and launch on the caller's stream.
+// C ABI of liblla: argument validation, path selection, scratch memory, launch on the
+// caller's stream, and kernel-level timing.
 #include "lla.h"
 
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 #include "lla_internal.h"
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + static_cast<uintptr_t>(b_bytes) && b0 < a0 + static_cast<uintptr_t>(a_bytes);
+}
+
+bool supported_shape(int64_t d, lla_dtype_t dtype) {
+    return (dtype == LLA_DTYPE_F32 || dtype == LLA_DTYPE_BF16) &&
+           (d == 16 || d == 32 || d == 64 || d == 128);
+}
+
+lla_status_t validate_sizes(int64_t B, int64_t H, int64_t n, int64_t d) {
+    if (B < 1 || H < 1 || n < 1) return LLA_ERR_SHAPE;
+    // Rows index a 1-D grid and positions an int; element offsets must fit int64 bytes.
+    const int64_t kRowLimit = INT32_MAX;
+    if (B > kRowLimit || H > kRowLimit || n > kRowLimit) return LLA_ERR_SHAPE;
+    if (B * H > kRowLimit / n) return LLA_ERR_SHAPE;
+    if (B * H * n > INT64_MAX / (d * 8)) return LLA_ERR_SHAPE;
+    return LLA_OK;
 }
 
 lla_status_t validate(const void* q, const void* k, const void* v, const float* out,
@@ -21,14 +41,10 @@ lla_status_t validate(const void* q, const void* k, const void* v, const float* 
     if (!q || !k || !v || !out) return LLA_ERR_NULL;
     if (B < 1 || H < 1 || n < 1) return LLA_ERR_SHAPE;
     if (!isfinite(h) || !(h > 0.0) || !isfinite(lambda) || !(lambda >= 0.0)) return LLA_ERR_PARAM;
-    if (dtype != LLA_DTYPE_F32 && dtype != LLA_DTYPE_BF16) return LLA_ERR_UNSUPPORTED;
-    if (d != 16 && d != 32 && d != 64 && d != 128) return LLA_ERR_UNSUPPORTED;
-    // Rows index a 1-D grid and positions an int; element offsets must fit int64 bytes.
-    const int64_t kRowLimit = INT32_MAX;
-    if (B > kRowLimit || H > kRowLimit || n > kRowLimit) return LLA_ERR_SHAPE;
-    if (B * H > kRowLimit / n) return LLA_ERR_SHAPE;
+    if (!supported_shape(d, dtype)) return LLA_ERR_UNSUPPORTED;
+    const lla_status_t st = validate_sizes(B, H, n, d);
+    if (st != LLA_OK) return st;
     const int64_t rows = B * H * n;
-    if (rows > INT64_MAX / (d * 8)) return LLA_ERR_SHAPE;
     const int64_t elt = dtype == LLA_DTYPE_F32 ? 4 : 2;
     const int64_t in_bytes = rows * d * elt, out_bytes = rows * d * 4;
     if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
@@ -37,7 +53,106 @@ lla_status_t validate(const void* q, const void* k, const void* v, const float* 
     return LLA_OK;
 }
 
+// Resolve a requested path to the kernels that run; false if it cannot serve the shape.
+bool resolve_fast(lla_path_t path, int dtype, int64_t d, bool* fast) {
+    switch (path) {
+        case LLA_PATH_EXACT: *fast = false; return true;
+        case LLA_PATH_FAST: *fast = true; return lla::fast_supports(dtype, d);
+        case LLA_PATH_AUTO: *fast = lla::fast_supports(dtype, d); return true;
+    }
+    return false;
+}
+
+// Library-owned stream-ordered memory pool per device, kept warm (no release threshold),
+// from which lla_forward / lla_forward_ex take the fast path's scratch.
+std::mutex g_pool_mu;
+std::vector<hipMemPool_t> g_pools;
+
+hipError_t pool_for_current_device(hipMemPool_t* pool) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if (static_cast<int>(g_pools.size()) <= dev) g_pools.resize(dev + 1, nullptr);
+    if (!g_pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        if ((err = hipMemPoolCreate(&p, &props)) != hipSuccess) return err;
+        uint64_t keep = UINT64_MAX;
+        if ((err = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
+            (void)hipMemPoolDestroy(p);
+            return err;
+        }
+        g_pools[dev] = p;
+    }
+    *pool = g_pools[dev];
+    return hipSuccess;
+}
+
+lla_status_t run(const lla::Problem& p, bool fast, void* ws, size_t ws_bytes, bool may_allocate) {
+    if (!fast) return lla::launch_exact(p, static_cast<int>(p.n)) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    const size_t need = lla::fast_workspace_bytes(p.B, p.H, p.n, p.d);
+    if (need == 0) return lla::launch_fast(p, nullptr) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    if (ws) {
+        if (ws_bytes < need) return LLA_ERR_WORKSPACE;
+        return lla::launch_fast(p, ws) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    }
+    if (!may_allocate) return LLA_ERR_WORKSPACE;
+    hipMemPool_t pool = nullptr;
+    if (pool_for_current_device(&pool) != hipSuccess) return LLA_ERR_HIP;
+    void* scratch = nullptr;
+    if (hipMallocFromPoolAsync(&scratch, need, pool, p.stream) != hipSuccess) return LLA_ERR_HIP;
+    const hipError_t err = lla::launch_fast(p, scratch);
+    const hipError_t ferr = hipFreeAsync(scratch, p.stream);
+    return (err == hipSuccess && ferr == hipSuccess) ? LLA_OK : LLA_ERR_HIP;
+}
+
+// ---- kernel-level timing
+struct ProfEntry {
+    const char* name;
+    hipEvent_t start, stop;
+};
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+std::vector<ProfEntry> g_prof_done;
+std::vector<hipEvent_t> g_prof_free;
+ProfEntry g_prof_open = {nullptr, nullptr, nullptr};
+
+hipEvent_t prof_event() {
+    if (!g_prof_free.empty()) {
+        hipEvent_t e = g_prof_free.back();
+        g_prof_free.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
+
 }  // namespace
+
+namespace lla {
+
+void prof_begin(hipStream_t stream, const char* kernel) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_open = {kernel, prof_event(), nullptr};
+    if (g_prof_open.start) (void)hipEventRecord(g_prof_open.start, stream);
+}
+
+void prof_end(hipStream_t stream) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (!g_prof_open.start) return;
+    g_prof_open.stop = prof_event();
+    if (g_prof_open.stop && hipEventRecord(g_prof_open.stop, stream) == hipSuccess)
+        g_prof_done.push_back(g_prof_open);
+    g_prof_open = {nullptr, nullptr, nullptr};
+}
+
+}  // namespace lla
 
 extern "C" {
 
@@ -48,8 +163,8 @@ const char* lla_status_string(lla_status_t s) {
         case LLA_ERR_SHAPE: return "invalid shape (B, H, n must be >= 1 and within index range)";
         case LLA_ERR_PARAM: return "invalid parameter (h must be > 0, lambda >= 0, both finite)";
         case LLA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or path";
-        case LLA_ERR_WORKSPACE: return "workspace error";
-        case LLA_ERR_HIP: return "HIP launch failed";
+        case LLA_ERR_WORKSPACE: return "workspace missing or smaller than lla_workspace_size";
+        case LLA_ERR_HIP: return "HIP launch or allocation failed";
         case LLA_ERR_ALIAS: return "output overlaps an input";
     }
     return "unknown status";
@@ -58,14 +173,31 @@ const char* lla_status_string(lla_status_t s) {
 int lla_version(void) { return kVersion; }
 
 int lla_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d) {
-    if (dtype != LLA_DTYPE_F32 && dtype != LLA_DTYPE_BF16) return 0;
-    if (d != 16 && d != 32 && d != 64 && d != 128) return 0;
-    switch (path) {
-        case LLA_PATH_AUTO:
-        case LLA_PATH_EXACT: return 1;
-        case LLA_PATH_FAST: return lla::fast_supports(static_cast<int>(dtype), d) ? 1 : 0;
-    }
-    return 0;
+    if (!supported_shape(d, dtype)) return 0;
+    bool fast = false;
+    return resolve_fast(path, static_cast<int>(dtype), d, &fast) ? 1 : 0;
+}
+
+size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
+                          lla_path_t path) {
+    if (!supported_shape(d, dtype) || validate_sizes(B, H, n, d) != LLA_OK) return 0;
+    bool fast = false;
+    if (!resolve_fast(path, static_cast<int>(dtype), d, &fast) || !fast) return 0;
+    return lla::fast_workspace_bytes(B, H, n, d);
+}
+
+lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* out,
+                            int64_t B, int64_t H, int64_t n, int64_t d,
+                            double h, double lambda,
+                            lla_dtype_t dtype, void* stream, lla_path_t path,
+                            void* workspace, size_t workspace_bytes) {
+    const lla_status_t st = validate(q, k, v, out, B, H, n, d, h, lambda, dtype);
+    if (st != LLA_OK) return st;
+    bool fast = false;
+    if (!resolve_fast(path, static_cast<int>(dtype), d, &fast)) return LLA_ERR_UNSUPPORTED;
+    const lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
+                         static_cast<hipStream_t>(stream)};
+    return run(p, fast, workspace, workspace_bytes, false);
 }
 
 lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* out,
@@ -74,19 +206,11 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
                             lla_dtype_t dtype, void* stream, lla_path_t path) {
     const lla_status_t st = validate(q, k, v, out, B, H, n, d, h, lambda, dtype);
     if (st != LLA_OK) return st;
-    if (path != LLA_PATH_AUTO && path != LLA_PATH_EXACT && path != LLA_PATH_FAST)
-        return LLA_ERR_UNSUPPORTED;
-    lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
-                   static_cast<hipStream_t>(stream)};
     bool fast = false;
-    if (path == LLA_PATH_FAST) {
-        if (!lla::fast_supports(p.dtype, d)) return LLA_ERR_UNSUPPORTED;
-        fast = true;
-    } else if (path == LLA_PATH_AUTO) {
-        fast = lla::fast_supports(p.dtype, d);
-    }
-    const hipError_t err = fast ? lla::launch_fast(p) : lla::launch_exact(p);
-    return err == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    if (!resolve_fast(path, static_cast<int>(dtype), d, &fast)) return LLA_ERR_UNSUPPORTED;
+    const lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
+                         static_cast<hipStream_t>(stream)};
+    return run(p, fast, nullptr, 0, true);
 }
 
 lla_status_t lla_forward(const void* q, const void* k, const void* v, float* out,
@@ -94,6 +218,29 @@ lla_status_t lla_forward(const void* q, const void* k, const void* v, float* out
                          double h, double lambda,
                          lla_dtype_t dtype, void* stream) {
     return lla_forward_ex(q, k, v, out, B, H, n, d, h, lambda, dtype, stream, LLA_PATH_AUTO);
+}
+
+int lla_profile_enable(int enable) {
+    return g_prof_on.exchange(enable != 0) ? 1 : 0;
+}
+
+int lla_profile_collect(const char** names, float* ms, int max_entries) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    int count = 0;
+    for (const ProfEntry& e : g_prof_done) {
+        float t = -1.0f;
+        if (hipEventSynchronize(e.stop) != hipSuccess || hipEventElapsedTime(&t, e.start, e.stop) != hipSuccess)
+            t = -1.0f;
+        if (count < max_entries) {
+            if (names) names[count] = e.name;
+            if (ms) ms[count] = t;
+            ++count;
+        }
+        g_prof_free.push_back(e.start);
+        g_prof_free.push_back(e.stop);
+    }
+    g_prof_done.clear();
+    return count;
 }
 
 }  // extern "C"

@@ -46,7 +46,7 @@ template <typename TIn, int D>
 __global__ __launch_bounds__(ExactCfg<D>::TR * ExactCfg<D>::TC)
 void lla_exact_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                       const TIn* __restrict__ v, float* __restrict__ out,
-                      int n, int BH, double inv_h, double lambda) {
+                      int n, int rows, int BH, double inv_h, double lambda) {
     constexpr int TR = ExactCfg<D>::TR, TC = ExactCfg<D>::TC, NT = TR * TC;
     constexpr int RA = D / TR, CB = D / TC;
     constexpr int CHK = 2048 / D;   // keys per staged chunk (16 KiB of fp64 per array)
@@ -68,7 +68,8 @@ void lla_exact_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 
     const int tid = threadIdx.x;
     const int tr = tid / TC, tc = tid % TC;
-    const int i = n - 1 - static_cast<int>(blockIdx.x / BH);  // longest rows first
+    // Rows 0 .. rows-1 of every head, longest rows first.
+    const int i = rows - 1 - static_cast<int>(blockIdx.x / BH);
     const int bh = static_cast<int>(blockIdx.x % BH);
     const int64_t base = static_cast<int64_t>(bh) * n * D;
     const TIn* kh = k + base;
@@ -283,31 +284,34 @@ void lla_exact_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 }
 
 template <typename TIn, int D>
-hipError_t launch_exact_t(const Problem& p) {
+hipError_t launch_exact_t(const Problem& p, int rows) {
     constexpr int NT = ExactCfg<D>::TR * ExactCfg<D>::TC;
     const int BH = static_cast<int>(p.B * p.H);
-    const unsigned rows = static_cast<unsigned>(p.B * p.H * p.n);
-    lla_exact_kernel<TIn, D><<<dim3(rows), dim3(NT), 0, p.stream>>>(
+    const unsigned blocks = static_cast<unsigned>(p.B * p.H * rows);
+    prof_begin(p.stream, "lla_exact_kernel");
+    lla_exact_kernel<TIn, D><<<dim3(blocks), dim3(NT), 0, p.stream>>>(
         static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v),
-        p.out, static_cast<int>(p.n), BH, 1.0 / p.h, p.lambda);
+        p.out, static_cast<int>(p.n), rows, BH, 1.0 / p.h, p.lambda);
+    prof_end(p.stream);
     return hipGetLastError();
 }
 
 template <typename TIn>
-hipError_t launch_exact_d(const Problem& p) {
+hipError_t launch_exact_d(const Problem& p, int rows) {
     switch (p.d) {
-        case 16: return launch_exact_t<TIn, 16>(p);
-        case 32: return launch_exact_t<TIn, 32>(p);
-        case 64: return launch_exact_t<TIn, 64>(p);
-        case 128: return launch_exact_t<TIn, 128>(p);
+        case 16: return launch_exact_t<TIn, 16>(p, rows);
+        case 32: return launch_exact_t<TIn, 32>(p, rows);
+        case 64: return launch_exact_t<TIn, 64>(p, rows);
+        case 128: return launch_exact_t<TIn, 128>(p, rows);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_exact(const Problem& p) {
-    return p.dtype == 0 ? launch_exact_d<float>(p) : launch_exact_d<uint16_t>(p);
+hipError_t launch_exact(const Problem& p, int rows) {
+    if (rows <= 0) return hipSuccess;
+    return p.dtype == 0 ? launch_exact_d<float>(p, rows) : launch_exact_d<uint16_t>(p, rows);
 }
 
 }  // namespace lla

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace lla {
@@ -17,12 +18,18 @@ struct Problem {
     hipStream_t stream;
 };
 
-// fp64-accumulating path: every (dtype, d) the library accepts.
-hipError_t launch_exact(const Problem& p);
+// fp64-accumulating path: every (dtype, d) the library accepts.  Processes rows
+// 0 .. rows-1 of every head (rows = n for the whole problem).
+hipError_t launch_exact(const Problem& p, int rows);
 
-// Matrix-core path for bf16 inputs.  Returns hipErrorNotSupported when (dtype, d) is not
-// covered, before launching anything.
+// Matrix-core path for bf16 inputs: rows i < 2d on the fp64 kernel, the rest on MFMA
+// kernels that keep per-row statistics in `workspace` (fast_workspace_bytes of it).
 bool fast_supports(int dtype, int64_t d);
-hipError_t launch_fast(const Problem& p);
+size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
+hipError_t launch_fast(const Problem& p, void* workspace);
+
+// Kernel-level timing (lla_profile_enable): events recorded around each launch.
+void prof_begin(hipStream_t stream, const char* kernel);
+void prof_end(hipStream_t stream);
 
 }  // namespace lla

@@ -10,8 +10,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["lla_forward", "lla_forward_ex", "lla_path_available", "lla_status_string",
-           "lla_version", "LLAError",
+__all__ = ["lla_forward", "lla_forward_ex", "lla_forward_ws", "lla_workspace_size",
+           "lla_path_available", "lla_profile_enable", "lla_profile_collect",
+           "lla_status_string", "lla_version", "LLAError",
            "library_path", "load_library", "STATUS", "PATHS", "DTYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +56,16 @@ def load_library():
     lib.lla_path_available.restype = ctypes.c_int
     lib.lla_version.argtypes = []
     lib.lla_version.restype = ctypes.c_int
+    lib.lla_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.lla_workspace_size.restype = ctypes.c_size_t
+    lib.lla_forward_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int,
+                                   vp, ctypes.c_int, vp, ctypes.c_size_t]
+    lib.lla_forward_ws.restype = ctypes.c_int
+    lib.lla_profile_enable.argtypes = [ctypes.c_int]
+    lib.lla_profile_enable.restype = ctypes.c_int
+    lib.lla_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p),
+                                        ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+    lib.lla_profile_collect.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -126,3 +137,45 @@ def lla_forward(q, k, v, h: float, lam: float, out=None, stream=None):
     if st != 0:
         raise LLAError(st, "lla_forward")
     return out
+
+
+def lla_workspace_size(B: int, H: int, n: int, d: int, dtype: str, path: str = "auto") -> int:
+    """Bytes of device scratch the chosen path needs (0 if none)."""
+    return int(load_library().lla_workspace_size(B, H, n, d, DTYPES[dtype], PATHS[path]))
+
+
+def lla_forward_ws(q, k, v, h: float, lam: float, workspace, path: str = "auto", out=None,
+                   stream=None):
+    """LLA forward with caller-provided scratch (a device tensor of at least
+    lla_workspace_size bytes, or None when none is needed); allocates nothing but `out`."""
+    import torch
+    dtype, out = _marshal(q, k, v, out)
+    B, H, n, d = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    if workspace is None:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = load_library().lla_forward_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       B, H, n, d, float(h), float(lam), dtype,
+                                       ctypes.c_void_p(stream.cuda_stream), PATHS[path],
+                                       ctypes.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes)
+    if st != 0:
+        raise LLAError(st, "lla_forward_ws")
+    return out
+
+
+def lla_profile_enable(enable: bool = True) -> bool:
+    """Bracket every library kernel launch with HIP events; returns the previous setting."""
+    return bool(load_library().lla_profile_enable(1 if enable else 0))
+
+
+def lla_profile_collect(max_entries: int = 4096):
+    """[(kernel name, milliseconds), ...] of the launches recorded since the last collect."""
+    names = (ctypes.c_char_p * max_entries)()
+    ms = (ctypes.c_float * max_entries)()
+    cnt = load_library().lla_profile_collect(names, ms, max_entries)
+    return [(names[i].decode(), float(ms[i])) for i in range(cnt)]

@@ -31,8 +31,10 @@ def declared_enums():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["lla_forward", "lla_forward_ex", "lla_path_available",
-                                    "lla_status_string", "lla_version"]
+    assert declared_functions() == ["lla_forward", "lla_forward_ex", "lla_forward_ws",
+                                    "lla_path_available", "lla_profile_collect",
+                                    "lla_profile_enable", "lla_status_string", "lla_version",
+                                    "lla_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -110,3 +112,35 @@ def test_path_availability_query():
         for d in (0, 8, 48, 256):
             assert not lla.lla_path_available("exact", dt, d)
     assert not lla.lla_path_available("fast", "f32", 64)  # the matrix-core path is bf16-only
+    assert lla.lla_path_available("fast", "bf16", 64)
+
+
+def test_workspace_size():
+    from local_linear_attention_amd import lla
+    # fast path: 4*(2d+4) bytes for every row at or beyond 2d
+    assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "fast") == 2 * 16 * (4096 - 128) * 132 * 4
+    assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "auto") == 2 * 16 * (4096 - 128) * 132 * 4
+    assert lla.lla_workspace_size(1, 1, 100, 64, "bf16", "fast") == 0      # every row is short
+    assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "exact") == 0
+    assert lla.lla_workspace_size(2, 16, 4096, 64, "f32", "auto") == 0
+    assert lla.lla_workspace_size(2, 16, 4096, 48, "bf16", "auto") == 0     # unsupported d
+    assert lla.lla_workspace_size(0, 16, 4096, 64, "bf16", "auto") == 0     # bad shape
+
+
+def test_forward_ws_validation_before_launch():
+    lib = _lib()
+    args = [ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V), ctypes.c_void_p(OUT),
+            1, 2, 4096, 64, 8.0, 0.1, 1, None, 2]
+    # fast path needs scratch: none or too little is refused before any launch
+    assert lib.lla_forward_ws(*args, None, 0) == 5
+    assert lib.lla_forward_ws(*args, ctypes.c_void_p(0x50000000), 1024) == 5
+    bad = list(args)
+    bad[7] = 32
+    assert lib.lla_forward_ws(*bad, None, 0) == 4  # fast path does not cover d = 32
+
+
+def test_profile_collect_without_launches():
+    from local_linear_attention_amd import lla
+    prev = lla.lla_profile_enable(True)
+    assert lla.lla_profile_collect() == []
+    lla.lla_profile_enable(prev)

@@ -56,6 +56,62 @@ def test_small_shapes_every_row(name, shape, path):
     check(got, ref, w.dtype, path if path != "default" else "auto", f"{name}{shape}")
 
 
+# Matrix-core path (bf16, d = 64): rows below 2d run on the fp64 kernel, the rest on MFMA.
+# Shapes cover no MFMA rows (n <= 2d), one ragged row block, several key tiles with a
+# ragged tail, and several heads and batches.
+FAST_SMALL = [
+    ("d24", {"B": 1, "H": 1, "n": 100}),
+    ("d24", {"B": 1, "H": 1, "n": 129}),
+    ("d24", {"B": 1, "H": 2, "n": 333}),
+    ("d12", {"B": 2, "H": 3, "n": 261}),
+    ("d24", {"B": 1, "H": 1, "n": 700}),
+]
+
+
+@pytest.mark.parametrize("name,shape", FAST_SMALL, ids=[f"{n}-{s}" for n, s in FAST_SMALL])
+def test_fast_path_every_row(name, shape):
+    require_gpu()
+    w, q, k, v = workload_arrays(name, **shape)
+    ref = oracle_forward(q, k, v, w.h, w.lam, workers=WORKERS)
+    got = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="fast")
+    check(got, ref, w.dtype, "fast", f"{name}{shape}")
+
+
+def test_fast_path_workspace_entry_point_matches():
+    torch = require_gpu()
+    from local_linear_attention_amd import lla_forward_ex, lla_forward_ws, lla_workspace_size
+    from parity_util import to_device
+    w, q, k, v = workload_arrays("d24", B=2, H=2, n=400)
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    nbytes = lla_workspace_size(w.B, w.H, w.n, w.d, "bf16", "fast")
+    assert nbytes == w.B * w.H * (w.n - 2 * w.d) * (2 * w.d + 4) * 4
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a = lla_forward_ws(tq, tk, tv, w.h, w.lam, ws, path="fast")
+    b = lla_forward_ex(tq, tk, tv, w.h, w.lam, path="fast")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    from local_linear_attention_amd import LLAError
+    with pytest.raises(LLAError, match="WORKSPACE"):
+        lla_forward_ws(tq, tk, tv, w.h, w.lam, ws[: nbytes // 2], path="fast")
+
+
+def test_profiling_records_each_kernel():
+    torch = require_gpu()
+    from local_linear_attention_amd import lla_forward_ex, lla_profile_collect, lla_profile_enable
+    from parity_util import to_device
+    w, q, k, v = workload_arrays("d24", B=1, H=2, n=300)
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    lla_profile_enable(True)
+    try:
+        lla_forward_ex(tq, tk, tv, w.h, w.lam, path="fast")
+        rec = lla_profile_collect()
+    finally:
+        lla_profile_enable(False)
+    assert [name for name, _ in rec] == ["lla_exact_kernel", "lla_stats_kernel",
+                                         "lla_moments_kernel"]
+    assert all(ms > 0 for _, ms in rec)
+
+
 def test_tiny_affine_lambda_zero_rows_beyond_d():
     require_gpu()
     w, q, k, v = workload_arrays("tiny_affine")
@@ -77,7 +133,8 @@ def test_single_position_returns_value():
 def test_full_size_workload_sampled_rows(name):
     require_gpu()
     w, q, k, v = workload_arrays(name)
-    rows = sample_rows(w.B, w.H, w.n, w.d, w.seed, per_head=4 if w.n > 8192 else 6)
+    per_head = 4 if w.n > 8192 else (40 if w.dtype == "bf16" else 6)
+    rows = sample_rows(w.B, w.H, w.n, w.d, w.seed, per_head=per_head)
     got_full = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="default")
     assert np.isfinite(got_full).all()
     ref = oracle_rows(q, k, v, w.h, w.lam, rows, workers=WORKERS)
