@@ -192,20 +192,72 @@ __global__ __launch_bounds__(256) void lla_stats_kernel(
 
 // ---------------------------------------------------------------------------------------
 // Moments + solve: block = 4 waves, one query per wave (4 consecutive rows of one head).
-constexpr int B_TILE_BYTES = KT * KK_LD * 2 + 2 * FD * XB_LD * 2 + B_WAVES * KT * 2;
+// Keys stream in tiles of 64: while the MFMAs consume tile t from one LDS buffer, the
+// global loads of tile t+1 are in flight into registers and then stored, transposed to
+// feature-major fp16, into the other buffer -- one barrier per tile.
+constexpr int MT = 64;                   // keys per tile
+constexpr int M_LD = MT + 8;             // feature-major fp16 row (elements), 144 B
+constexpr int M_BUF_BYTES = 2 * FD * M_LD * 2 + B_WAVES * MT * 2;  // Kt, Vt, Sw
 constexpr int B_SOLVE_FLOATS = FD * (FD + 1) + 2 * FD;  // A (padded rows) + pivot column + y
-constexpr int B_SMEM = (B_SOLVE_FLOATS * 4 * B_WAVES > B_TILE_BYTES) ? B_SOLVE_FLOATS * 4 * B_WAVES
-                                                                       : B_TILE_BYTES;
+constexpr int B_SMEM = (B_SOLVE_FLOATS * 4 * B_WAVES > 2 * M_BUF_BYTES)
+                           ? B_SOLVE_FLOATS * 4 * B_WAVES : 2 * M_BUF_BYTES;
 
-__global__ __launch_bounds__(256) void lla_moments_kernel(
+struct TileRegs {
+    uint4 k0, k1, v0, v1;   // keys 2p and 2p+1 of the tile, features 8fg .. 8fg+7
+    uint4 kq[2];            // score operand: key 16w + c, features 32ks + 8g .. +8
+};
+
+__device__ __forceinline__ void load_tile(TileRegs& r, const uint16_t* __restrict__ kh,
+                                          const uint16_t* __restrict__ vh, int n, int j0,
+                                          int w, int g, int c) {
+    const int tid = threadIdx.x;
+    const int pr = tid & 31, fg = tid >> 5;
+    const int ja = j0 + 2 * pr, jb = ja + 1;
+    r.k0 = r.k1 = r.v0 = r.v1 = make_uint4(0, 0, 0, 0);
+    if (ja < n) {
+        r.k0 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(ja) * FD + 8 * fg);
+        r.v0 = *reinterpret_cast<const uint4*>(vh + static_cast<int64_t>(ja) * FD + 8 * fg);
+    }
+    if (jb < n) {
+        r.k1 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jb) * FD + 8 * fg);
+        r.v1 = *reinterpret_cast<const uint4*>(vh + static_cast<int64_t>(jb) * FD + 8 * fg);
+    }
+    const int jq = j0 + 16 * w + c;
+    r.kq[0] = r.kq[1] = make_uint4(0, 0, 0, 0);
+    if (jq < n) {
+        r.kq[0] = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 8 * g);
+        r.kq[1] = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 32 + 8 * g);
+    }
+}
+
+// Two bf16 (low and high half of a word) of one feature, keys 2p and 2p+1, as packed fp16.
+__device__ __forceinline__ uint32_t pack_pair(uint32_t wa, uint32_t wb, int hi) {
+    const float a = __uint_as_float(hi ? (wa & 0xffff0000u) : (wa << 16));
+    const float b = __uint_as_float(hi ? (wb & 0xffff0000u) : (wb << 16));
+    // bf16 values in fp16 range convert exactly, so the rounding mode is immaterial.
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+__device__ __forceinline__ void store_tile(const TileRegs& r, unsigned char* buf) {
+    const int tid = threadIdx.x;
+    const int pr = tid & 31, fg = tid >> 5;
+    uint32_t* kt = reinterpret_cast<uint32_t*>(buf);
+    uint32_t* vt = kt + FD * M_LD / 2;
+    const uint32_t ka[4] = {r.k0.x, r.k0.y, r.k0.z, r.k0.w}, kb[4] = {r.k1.x, r.k1.y, r.k1.z, r.k1.w};
+    const uint32_t va[4] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w}, vb[4] = {r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int row = 8 * fg + e;
+        kt[row * (M_LD / 2) + pr] = pack_pair(ka[e >> 1], kb[e >> 1], e & 1);
+        vt[row * (M_LD / 2) + pr] = pack_pair(va[e >> 1], vb[e >> 1], e & 1);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ stats, float* __restrict__ out,
     int n, int row0, int BH, float sl2, float lambda) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint16_t* Kk = reinterpret_cast<uint16_t*>(smem);
-    _Float16* Kt = reinterpret_cast<_Float16*>(smem + KT * KK_LD * 2);
-    _Float16* Vt = Kt + FD * XB_LD;
-    _Float16* Sw = Vt + FD * XB_LD;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
@@ -224,15 +276,13 @@ __global__ __launch_bounds__(256) void lla_moments_kernel(
     const float* st = stats + (static_cast<int64_t>(bh) * nrows + (ic - row0)) * SROW;
 
     // Centring constants of this wave's query, rounded to fp16, for feature c + 16 fb.
-    half8 nkb[4], nvb[4];
+    _Float16 nkb[4], nvb[4];
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
-        const _Float16 kb = static_cast<_Float16>(-st[fb * 16 + c]);
-        const _Float16 vb = static_cast<_Float16>(-st[FD + fb * 16 + c]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { nkb[fb][e] = kb; nvb[fb][e] = vb; }
+        nkb[fb] = static_cast<_Float16>(-st[fb * 16 + c]);
+        nvb[fb] = static_cast<_Float16>(-st[FD + fb * 16 + c]);
     }
-    // Score operands of waves 0 and 1: column c < B_WAVES is query i0 + c.
+    // Score operand: column c < B_WAVES is query i0 + c (the other columns are zero).
     const int qcol = min(i0 + c, n - 1);
     const bool colv = c < B_WAVES;
     const float mcol = stats[(static_cast<int64_t>(bh) * nrows + (qcol - row0)) * SROW + 2 * FD] * LOG2E;
@@ -244,62 +294,75 @@ __global__ __launch_bounds__(256) void lla_moments_kernel(
         qf[ks] = __builtin_bit_cast(bf16x8, raw);
     }
 
+    // sqrt of the shifted weights of key block w (16 keys) for the 4 queries -> Sw buffer.
+    auto scores = [&](const TileRegs& r, unsigned char* buf, int j0) {
+        float4v s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) s = mfma_bf16(__builtin_bit_cast(bf16x8, r.kq[ks]), qf[ks], s);
+        if (colv) {
+            half4 sw4;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int j = j0 + 16 * w + 4 * g + rr;
+                sw4[rr] = static_cast<_Float16>(j <= qcol ? exp2f((s[rr] * sl2 - mcol) * 0.5f) : 0.0f);
+            }
+            _Float16* sw = reinterpret_cast<_Float16*>(buf + 2 * FD * M_LD * 2);
+            *reinterpret_cast<half4*>(sw + c * MT + 16 * w + 4 * g) = sw4;
+        }
+    };
+
     float4v ckk[10], cvk[16];
 #pragma unroll
     for (int t = 0; t < 10; ++t) ckk[t] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 16; ++t) cvk[t] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    const int ntiles = (last + KT) / KT;
+    const int ntiles = (last + MT) / MT;
+    TileRegs regs;
+    load_tile(regs, kh, vh, n, 0, w, g, c);
+    store_tile(regs, smem);
+    scores(regs, smem, 0);
+    __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
-        const int j0 = t * KT;
-        __syncthreads();
-        stage_tile<XB_LD>(kh, vh, n, j0, Kk, Kt, Vt);
-        __syncthreads();
-        if (w < 2) {
-            // sqrt of the shifted weights, exp((s - m)/2), for key block kb = w.
-            float4v s = {0.f, 0.f, 0.f, 0.f};
+        const int j0 = t * MT;
+        unsigned char* cur = smem + (t & 1) * M_BUF_BYTES;
+        unsigned char* nxt = smem + ((t + 1) & 1) * M_BUF_BYTES;
+        const bool more = t + 1 < ntiles;
+        if (more) load_tile(regs, kh, vh, n, j0 + MT, w, g, c);
+        const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
+        const _Float16* Vt = Kt + FD * M_LD;
+        const _Float16* Sw = Vt + FD * M_LD;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(Kk + (w * 16 + c) * KK_LD + ks * 32 + 8 * g));
-                s = mfma_bf16(a, qf[ks], s);
+        for (int sub = 0; sub < 2; ++sub) {
+            if (j0 + 32 * sub > ic) break;  // wave-uniform: the rest lies past this query
+            const half8 sw = *reinterpret_cast<const half8*>(Sw + w * MT + 32 * sub + 8 * g);
+            half8 rk[4];
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) {
+                const half8 kf = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * M_LD + 32 * sub + 8 * g);
+                rk[fb] = (kf + nkb[fb]) * sw;
             }
-            if (colv) {
-                half4 sw4;
+            int idx = 0;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = j0 + w * 16 + 4 * g + r;
-                    sw4[r] = static_cast<_Float16>(j <= qcol ? exp2f((s[r] * sl2 - mcol) * 0.5f) : 0.0f);
-                }
-                *reinterpret_cast<half4*>(Sw + c * KT + w * 16 + 4 * g) = sw4;
+            for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+                for (int fb2 = fb; fb2 < 4; ++fb2) { ckk[idx] = mfma_f16(rk[fb], rk[fb2], ckk[idx]); ++idx; }
+#pragma unroll
+            for (int fv = 0; fv < 4; ++fv) {
+                const half8 vf = *reinterpret_cast<const half8*>(Vt + (fv * 16 + c) * M_LD + 32 * sub + 8 * g);
+                const half8 rv = (vf + nvb[fv]) * sw;
+#pragma unroll
+                for (int fb = 0; fb < 4; ++fb) cvk[fb * 4 + fv] = mfma_f16(rk[fb], rv, cvk[fb * 4 + fv]);
             }
         }
-        __syncthreads();
-        if (j0 > ic) continue;  // wave-uniform: the whole tile lies past this wave's query
-
-        const half8 sw = *reinterpret_cast<const half8*>(Sw + w * KT + 8 * g);
-        half8 rk[4], rv[4];
-#pragma unroll
-        for (int fb = 0; fb < 4; ++fb) {
-            const half8 kf = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * XB_LD + 8 * g);
-            const half8 vf = *reinterpret_cast<const half8*>(Vt + (fb * 16 + c) * XB_LD + 8 * g);
-            rk[fb] = (kf + nkb[fb]) * sw;
-            rv[fb] = (vf + nvb[fb]) * sw;
+        if (more) {
+            store_tile(regs, nxt);
+            scores(regs, nxt, j0 + MT);
         }
-        int idx = 0;
-#pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-            for (int fb2 = fb; fb2 < 4; ++fb2) { ckk[idx] = mfma_f16(rk[fb], rk[fb2], ckk[idx]); ++idx; }
-#pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-            for (int fv = 0; fv < 4; ++fv) cvk[fb * 4 + fv] = mfma_f16(rk[fb], rv[fv], cvk[fb * 4 + fv]);
+        __syncthreads();
     }
-    __syncthreads();  // tile buffers are dead; the solve area aliases them
 
-    // ---- ridge-rescaled SPD solve, lane a owns row a
+    // ---- ridge-rescaled SPD solve, lane a owns row a (the solve area aliases the tiles)
     constexpr int ALD = FD + 1;
     float* A = reinterpret_cast<float*>(smem) + w * B_SOLVE_FLOATS;
     float* colb = A + FD * ALD;
@@ -332,6 +395,10 @@ __global__ __launch_bounds__(256) void lla_moments_kernel(
     float ar[FD];
 #pragma unroll
     for (int b = 0; b < FD; ++b) ar[b] = A[lane * ALD + b];
+    // Park C_vk^T in the (now free) matrix area during the elimination, lane-private.
+    float4v* park = reinterpret_cast<float4v*>(A) + lane * 16;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) park[t] = cvk[t];
     const float qa = bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]);
     float z = st[lane] - qa;
 
@@ -367,9 +434,11 @@ __global__ __launch_bounds__(256) void lla_moments_kernel(
     for (int fb = 0; fb < 4; ++fb) {
         const float4v yy = *reinterpret_cast<const float4v*>(yv + fb * 16 + 4 * g);
 #pragma unroll
-        for (int fv = 0; fv < 4; ++fv)
+        for (int fv = 0; fv < 4; ++fv) {
+            const float4v cv = park[fb * 4 + fv];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part[fv] = fmaf(cvk[fb * 4 + fv][r], yy[r], part[fv]);
+            for (int r = 0; r < 4; ++r) part[fv] = fmaf(cv[r], yy[r], part[fv]);
+        }
     }
 #pragma unroll
     for (int fv = 0; fv < 4; ++fv) {
