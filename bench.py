@@ -49,6 +49,7 @@ def alg_flops(B, H, n, d, form):
 PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d: f64)"}
 KERNEL_BOUND = {
     "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla_short_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_stats_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_moments_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
 }
@@ -61,13 +62,13 @@ def pair_count(BH, lo, hi):
 
 def kernel_flops(name, B, H, n, d, path):
     """Algorithmic flops (formulation NS, the one both paths execute) of one launch of a
-    kernel: the fast path splits the rows at 2d between the fp64 kernel and the MFMA
-    kernels; the stats kernel owns the score and first-moment terms of its rows, the
+    kernel: the fast path splits the rows at 2d between an fp64 kernel (short rows) and the
+    MFMA kernels; the stats kernel owns the score and first-moment terms of its rows, the
     moments kernel the second moments, the solve and the assembly."""
     BH = B * H
     row0 = min(n, 2 * d) if path == "fast" else n
     per_query = d ** 3 / 3 + 4 * d * d + 2 * d
-    if name == "lla_exact_kernel":
+    if name in ("lla_exact_kernel", "lla_short_kernel"):
         return pair_count(BH, 0, row0) * (2 * d + 2 * (1 + 2 * d) + d * (d + 1) + 2 * d * d) \
             + BH * row0 * per_query
     if name == "lla_stats_kernel":

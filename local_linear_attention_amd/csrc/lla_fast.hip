@@ -48,6 +48,12 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr int A_WAVES = 4, A_QW = 16, A_QB = A_WAVES * A_QW;  // stats: 64 queries / block
 constexpr int B_WAVES = 4;                                     // moments: 1 query per wave
 
+// Compiler fence for wave-private LDS exchanges: a lane reads words that other lanes of
+// the same wave stored, so no LDS access may move across a publish/consume boundary.
+// (A blocked variant of the solve below was miscompiled without such fences on gfx950:
+// an LDS access moved across a dependent one.  The fences cost no instructions.)
+#define LDS_FENCE() __asm__ volatile("" ::: "memory")
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
@@ -382,9 +388,11 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
                 ++idx;
             }
     }
+    LDS_FENCE();
     const float m_x = st[2 * FD] * LOG2E;
     const float lam_s = lambda * exp2f(-m_x);
     A[lane * ALD + lane] += lam_s;
+    LDS_FENCE();
     float dmax = A[lane * ALD + lane];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, off));
@@ -395,10 +403,13 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     float ar[FD];
 #pragma unroll
     for (int b = 0; b < FD; ++b) ar[b] = A[lane * ALD + b];
+    LDS_FENCE();
     // Park C_vk^T in the (now free) matrix area during the elimination, lane-private.
     float4v* park = reinterpret_cast<float4v*>(A) + lane * 16;
 #pragma unroll
     for (int t = 0; t < 16; ++t) park[t] = cvk[t];
+    // The accumulators must really leave the registers: no store-to-load forwarding.
+    LDS_FENCE();
     const float qa = bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]);
     float z = st[lane] - qa;
 
@@ -408,6 +419,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 #pragma unroll
     for (int p = 0; p < FD; ++p) {
         colb[lane] = ar[p];
+        LDS_FENCE();
         const float piv = colb[p];
         const float inv = piv > thresh ? 1.0f / piv : 0.0f;
         const float f = lane > p ? ar[p] * inv : 0.0f;
@@ -415,6 +427,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         z = fmaf(-f, zp, z);
 #pragma unroll
         for (int b = p + 1; b < FD; ++b) ar[b] = fmaf(-f, colb[b], ar[b]);
+        LDS_FENCE();
     }
     // Back substitution U y = z, column by column.
     float ylane = 0.0f;
@@ -427,6 +440,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         z = fmaf(-ar[p], yp, z);
     }
     yv[lane] = ylane;
+    LDS_FENCE();
 
     // b = vbar - C_vk y; lane holds C_vk^T[fb*16 + 4g + r][fv*16 + c].
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -452,6 +466,168 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Rows i < 2d of the bf16 path, exactly in fp64: one wave per row, 4 consecutive rows per
+// block sharing the (at most 2d-key) prefix staged in LDS as fp32 (exact for bf16).
+//   scores -> m, weights, omega; kbar, vbar (lane = feature);
+//   row a of C_kk = sum_j w_j (k_ja - kbar_a) k_j   (the k_j - kbar centring of the right
+//   factor is implied: sum_j w_j (k_ja - kbar_a) = 0);
+//   LDL^T elimination lane-per-row, back substitution -> y;
+//   probe u_j = (k_j - kbar).y and b = vbar - sum_j w_j u_j (v_j - vbar)  (= vbar - C_vk y).
+constexpr int S_ROWS = 4;
+constexpr int S_KMAX = 2 * FD;
+constexpr int S_LD = FD + 1;    // fp32 row stride (elements)
+
+__device__ __forceinline__ double wave_max_d(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmax(x, __shfl_xor(x, off));
+    return x;
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+__global__ __launch_bounds__(256) void lla_short_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, float* __restrict__ out, int n, int rows, int BH,
+    double inv_h, double lambda) {
+    __shared__ float Ks[S_KMAX * S_LD];
+    __shared__ float Vs[S_KMAX * S_LD];
+    __shared__ double qs[S_ROWS][FD];
+    __shared__ double ws[S_ROWS][S_KMAX];
+    __shared__ double kbs[S_ROWS][FD];
+    __shared__ double xb[S_ROWS][FD];   // pivot-column exchange, then y
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nblk = (rows + S_ROWS - 1) / S_ROWS;
+    const int blk = nblk - 1 - static_cast<int>(blockIdx.x / BH);  // longest rows first
+    const int bh = static_cast<int>(blockIdx.x % BH);
+    const int r0 = blk * S_ROWS;
+    const int i = r0 + w;
+    const bool valid = i < rows;
+    const int ic = min(i, rows - 1);
+    const int nk = min(r0 + S_ROWS, rows);          // keys staged: 0 .. nk-1
+    const int64_t base = static_cast<int64_t>(bh) * n * FD;
+
+    for (int e = tid; e < nk * (FD / 8); e += 256) {
+        const int j = e / (FD / 8), f0 = (e % (FD / 8)) * 8;
+        const uint4 kr = *reinterpret_cast<const uint4*>(k + base + static_cast<int64_t>(j) * FD + f0);
+        const uint4 vr = *reinterpret_cast<const uint4*>(v + base + static_cast<int64_t>(j) * FD + f0);
+        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w}, vw[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t sh = (t & 1) ? 0u : 16u;
+            Ks[j * S_LD + f0 + t] = __uint_as_float((kw[t >> 1] << sh) & 0xffff0000u);
+            Vs[j * S_LD + f0 + t] = __uint_as_float((vw[t >> 1] << sh) & 0xffff0000u);
+        }
+    }
+    qs[w][lane] = static_cast<double>(bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]));
+    __syncthreads();
+
+    // ---- scores of keys lane and lane + 64, running max, weights, omega
+    double s[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int j = lane + 64 * h2;
+        if (j <= ic) {
+            double acc = 0.0;
+#pragma unroll 16
+            for (int a = 0; a < FD; ++a) acc = fma(qs[w][a], static_cast<double>(Ks[j * S_LD + a]), acc);
+            s[h2] = acc * inv_h;
+        }
+    }
+    const double m = wave_max_d(fmax(s[0], s[1]));
+    double wl[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        wl[h2] = (lane + 64 * h2 <= ic) ? exp(s[h2] - m) : 0.0;
+        ws[w][lane + 64 * h2] = wl[h2];
+    }
+    const double omega = wave_sum_d(wl[0] + wl[1]);
+    LDS_FENCE();
+
+    // ---- weighted means, lane = feature
+    double ka = 0.0, va = 0.0;
+    for (int j = 0; j <= ic; ++j) {
+        const double wj = ws[w][j];
+        ka = fma(wj, static_cast<double>(Ks[j * S_LD + lane]), ka);
+        va = fma(wj, static_cast<double>(Vs[j * S_LD + lane]), va);
+    }
+    ka /= omega;
+    va /= omega;
+    kbs[w][lane] = ka;
+
+    // ---- row `lane` of C_kk, plus the rescaled ridge on the diagonal
+    double cr[FD];
+#pragma unroll
+    for (int b = 0; b < FD; ++b) cr[b] = 0.0;
+    for (int j = 0; j <= ic; ++j) {
+        const double t = ws[w][j] * (static_cast<double>(Ks[j * S_LD + lane]) - ka);
+#pragma unroll
+        for (int b = 0; b < FD; ++b) cr[b] = fma(t, static_cast<double>(Ks[j * S_LD + b]), cr[b]);
+    }
+    const double lam_s = lambda * exp(-m);
+    double dmax = 0.0;
+#pragma unroll
+    for (int b = 0; b < FD; ++b) {
+        cr[b] += (b == lane) ? lam_s : 0.0;
+        if (b == lane) dmax = cr[b];
+    }
+    dmax = wave_max_d(dmax);
+    const double thresh = lambda > 0.0 ? 0.0 : 1e-12 * dmax;
+    double z = ka - qs[w][lane];
+
+    // ---- LDL^T elimination (lane owns row), then back substitution
+    double* xw = xb[w];
+    LDS_FENCE();
+#pragma unroll
+    for (int p = 0; p < FD; ++p) {
+        xw[lane] = cr[p];
+        LDS_FENCE();
+        const double piv = xw[p];
+        const double inv = piv > thresh ? 1.0 / piv : 0.0;
+        const double f = lane > p ? cr[p] * inv : 0.0;
+        const double zp = __shfl(z, p);
+        z = fma(-f, zp, z);
+#pragma unroll
+        for (int b = p + 1; b < FD; ++b) cr[b] = fma(-f, xw[b], cr[b]);
+        LDS_FENCE();
+    }
+    double ylane = 0.0;
+#pragma unroll
+    for (int p = FD - 1; p >= 0; --p) {
+        const double dp = __shfl(cr[p], p);
+        const double zp = __shfl(z, p);
+        const double yp = dp > thresh ? zp / dp : 0.0;
+        ylane = lane == p ? yp : ylane;
+        z = fma(-cr[p], yp, z);
+    }
+    xw[lane] = ylane;
+    LDS_FENCE();
+
+    // ---- probe: u_j = (k_j - kbar).y for keys lane, lane + 64; then b = vbar - C_vk y
+    double wu[2] = {0.0, 0.0};
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int j = lane + 64 * h2;
+        if (j <= ic) {
+            double u = 0.0;
+#pragma unroll 16
+            for (int a = 0; a < FD; ++a)
+                u = fma(static_cast<double>(Ks[j * S_LD + a]) - kbs[w][a], xw[a], u);
+            wu[h2] = wl[h2] * u;
+        }
+        ws[w][lane + 64 * h2] = wu[h2];
+    }
+    const double swu = wave_sum_d(wu[0] + wu[1]);
+    LDS_FENCE();
+    double acc = 0.0;
+    for (int j = 0; j <= ic; ++j) acc = fma(ws[w][j], static_cast<double>(Vs[j * S_LD + lane]), acc);
+    if (valid) out[base + static_cast<int64_t>(i) * FD + lane] = static_cast<float>(va - (acc - va * swu));
+}
+
 int fast_row0(int64_t n, int64_t d) { return static_cast<int>(n < 2 * d ? n : 2 * d); }
 
 }  // namespace
@@ -465,7 +641,14 @@ size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
 
 hipError_t launch_fast(const Problem& p, void* workspace) {
     const int row0 = fast_row0(p.n, p.d);
-    hipError_t err = launch_exact(p, row0);
+    const int BHs = static_cast<int>(p.B * p.H);
+    prof_begin(p.stream, "lla_short_kernel");
+    lla_short_kernel<<<dim3(static_cast<unsigned>(BHs) * ((row0 + S_ROWS - 1) / S_ROWS)), dim3(256), 0,
+                       p.stream>>>(static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
+                                   static_cast<const uint16_t*>(p.v), p.out, static_cast<int>(p.n), row0,
+                                   BHs, 1.0 / p.h, p.lambda);
+    prof_end(p.stream);
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess || p.n <= row0) return err;
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;

@@ -107,7 +107,7 @@ def test_profiling_records_each_kernel():
         rec = lla_profile_collect()
     finally:
         lla_profile_enable(False)
-    assert [name for name, _ in rec] == ["lla_exact_kernel", "lla_stats_kernel",
+    assert [name for name, _ in rec] == ["lla_short_kernel", "lla_stats_kernel",
                                          "lla_moments_kernel"]
     assert all(ms > 0 for _, ms in rec)
 
