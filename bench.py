@@ -51,6 +51,7 @@ KERNEL_BOUND = {
     "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_short_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_stats_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_moments_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
 }
 
@@ -71,6 +72,8 @@ def kernel_flops(name, B, H, n, d, path):
     if name in ("lla_exact_kernel", "lla_short_kernel"):
         return pair_count(BH, 0, row0) * (2 * d + 2 * (1 + 2 * d) + d * (d + 1) + 2 * d * d) \
             + BH * row0 * per_query
+    if name == "lla_pack_kernel":
+        return 0                      # data movement only (K, V repacked once)
     if name == "lla_stats_kernel":
         return pair_count(BH, row0, n) * (2 * d + 2 * (1 + 2 * d))
     if name == "lla_moments_kernel":
@@ -88,12 +91,13 @@ def kernel_source_hash():
 
 
 def load_traffic(kernel, workload):
-    """HBM traffic per launch from the committed rocprofv3 PMC summary, if it was taken
-    on the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch (fetched + written) from the committed rocprofv3 counter summary
+    profiles/<kernel>_<workload>_traffic.json, if it was taken on the current kernel
+    sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     try:
-        rec = json.load(open(path))[f"{kernel}/{workload}"]
-    except (OSError, KeyError, ValueError):
+        rec = json.load(open(path))
+    except (OSError, ValueError):
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
@@ -140,6 +144,9 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a reference "
+                         "dispatch of known traffic for hardware-counter runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -163,6 +170,14 @@ def main():
     tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v))
     out = torch.empty(tq.shape, dtype=torch.float32, device=dev)
     load_library()
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     path = args.path
     if path == "auto":

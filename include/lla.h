@@ -99,8 +99,9 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
                             lla_dtype_t dtype, void* stream, lla_path_t path);
 
 /* Bytes of device scratch that `path` needs for this problem (0 if none, or if the sizes,
- * dtype or path are invalid).  The fast path keeps per-row statistics there: 4*(2d+4) bytes
- * for every row at or beyond position 2d. */
+ * dtype or path are invalid).  The fast path keeps per-row statistics there, 4*(2d+4) bytes
+ * for every row at or beyond position 2d, followed by K and V of every head repacked as
+ * fp16 tiles of 64 keys, 2*2*d*64 bytes per tile (zero past n); nothing when n <= 2d. */
 size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                           lla_path_t path);
 

@@ -54,6 +54,11 @@ constexpr int B_WAVES = 4;                                     // moments: 1 que
 // an LDS access moved across a dependent one.  The fences cost no instructions.)
 #define LDS_FENCE() __asm__ volatile("" ::: "memory")
 
+// Value of x in lane `src` (a compile-time lane), broadcast to the wave.
+__device__ __forceinline__ float lane_value(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
@@ -208,60 +213,63 @@ constexpr int B_SOLVE_FLOATS = FD * (FD + 1) + 2 * FD;  // A (padded rows) + piv
 constexpr int B_SMEM = (B_SOLVE_FLOATS * 4 * B_WAVES > 2 * M_BUF_BYTES)
                            ? B_SOLVE_FLOATS * 4 * B_WAVES : 2 * M_BUF_BYTES;
 
-struct TileRegs {
-    uint4 k0, k1, v0, v1;   // keys 2p and 2p+1 of the tile, features 8fg .. 8fg+7
-    uint4 kq[2];            // score operand: key 16w + c, features 32ks + 8g .. +8
-};
+// Keys and values of one 64-key tile, feature-major fp16, as the pack kernel lays them out
+// in the workspace: [K or V][feature][key], 2 x 64 x 64 halves = 16 KiB per tile.
+constexpr int PACK_TILE_HALVES = 2 * FD * MT;
 
-__device__ __forceinline__ void load_tile(TileRegs& r, const uint16_t* __restrict__ kh,
-                                          const uint16_t* __restrict__ vh, int n, int j0,
-                                          int w, int g, int c) {
-    const int tid = threadIdx.x;
-    const int pr = tid & 31, fg = tid >> 5;
-    const int ja = j0 + 2 * pr, jb = ja + 1;
-    r.k0 = r.k1 = r.v0 = r.v1 = make_uint4(0, 0, 0, 0);
+// Pack K and V once into feature-major fp16 tiles (zero past n).  Thread -> keys 2p, 2p+1
+// and features 8fg .. 8fg+7; every store writes packed pairs of keys, 128 contiguous bytes
+// per 32 lanes.  bf16 values in fp16 range convert exactly.
+__global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v,
+                                                       uint16_t* __restrict__ packed, int n,
+                                                       int ntiles) {
+    const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
+    const int tid = threadIdx.x, pr = tid & 31, fg = tid >> 5;
+    const int64_t base = static_cast<int64_t>(bh) * n * FD;
+    const int ja = t * MT + 2 * pr, jb = ja + 1;
+    uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0, v0 = k0, v1 = k0;
     if (ja < n) {
-        r.k0 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(ja) * FD + 8 * fg);
-        r.v0 = *reinterpret_cast<const uint4*>(vh + static_cast<int64_t>(ja) * FD + 8 * fg);
+        k0 = *reinterpret_cast<const uint4*>(k + base + static_cast<int64_t>(ja) * FD + 8 * fg);
+        v0 = *reinterpret_cast<const uint4*>(v + base + static_cast<int64_t>(ja) * FD + 8 * fg);
     }
     if (jb < n) {
-        r.k1 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jb) * FD + 8 * fg);
-        r.v1 = *reinterpret_cast<const uint4*>(vh + static_cast<int64_t>(jb) * FD + 8 * fg);
+        k1 = *reinterpret_cast<const uint4*>(k + base + static_cast<int64_t>(jb) * FD + 8 * fg);
+        v1 = *reinterpret_cast<const uint4*>(v + base + static_cast<int64_t>(jb) * FD + 8 * fg);
     }
-    const int jq = j0 + 16 * w + c;
-    r.kq[0] = r.kq[1] = make_uint4(0, 0, 0, 0);
-    if (jq < n) {
-        r.kq[0] = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 8 * g);
-        r.kq[1] = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 32 + 8 * g);
-    }
-}
-
-// Two bf16 (low and high half of a word) of one feature, keys 2p and 2p+1, as packed fp16.
-__device__ __forceinline__ uint32_t pack_pair(uint32_t wa, uint32_t wb, int hi) {
-    const float a = __uint_as_float(hi ? (wa & 0xffff0000u) : (wa << 16));
-    const float b = __uint_as_float(hi ? (wb & 0xffff0000u) : (wb << 16));
-    // bf16 values in fp16 range convert exactly, so the rounding mode is immaterial.
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
-
-__device__ __forceinline__ void store_tile(const TileRegs& r, unsigned char* buf) {
-    const int tid = threadIdx.x;
-    const int pr = tid & 31, fg = tid >> 5;
-    uint32_t* kt = reinterpret_cast<uint32_t*>(buf);
-    uint32_t* vt = kt + FD * M_LD / 2;
-    const uint32_t ka[4] = {r.k0.x, r.k0.y, r.k0.z, r.k0.w}, kb[4] = {r.k1.x, r.k1.y, r.k1.z, r.k1.w};
-    const uint32_t va[4] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w}, vb[4] = {r.v1.x, r.v1.y, r.v1.z, r.v1.w};
+    uint32_t* dst = reinterpret_cast<uint32_t*>(packed + (static_cast<int64_t>(bh) * ntiles + t) * PACK_TILE_HALVES);
+    const uint32_t ka[4] = {k0.x, k0.y, k0.z, k0.w}, kb[4] = {k1.x, k1.y, k1.z, k1.w};
+    const uint32_t va[4] = {v0.x, v0.y, v0.z, v0.w}, vb[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int row = 8 * fg + e;
-        kt[row * (M_LD / 2) + pr] = pack_pair(ka[e >> 1], kb[e >> 1], e & 1);
-        vt[row * (M_LD / 2) + pr] = pack_pair(va[e >> 1], vb[e >> 1], e & 1);
+        const int hi = e & 1;
+        const uint32_t kwa = ka[e >> 1], kwb = kb[e >> 1], vwa = va[e >> 1], vwb = vb[e >> 1];
+        const float fka = __uint_as_float(hi ? (kwa & 0xffff0000u) : (kwa << 16));
+        const float fkb = __uint_as_float(hi ? (kwb & 0xffff0000u) : (kwb << 16));
+        const float fva = __uint_as_float(hi ? (vwa & 0xffff0000u) : (vwa << 16));
+        const float fvb = __uint_as_float(hi ? (vwb & 0xffff0000u) : (vwb << 16));
+        dst[row * (MT / 2) + pr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fka, fkb));
+        dst[(FD + row) * (MT / 2) + pr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fva, fvb));
     }
+}
+
+// Chunk tid + 256 u (16 B) of a packed tile sits in feature row (tid / 8) + 32 u (K rows
+// then V rows), keys 8 (tid % 8) .. +8; it goes to the same place in the padded LDS tile.
+__device__ __forceinline__ void store_chunks(unsigned char* buf, uint4 x0, uint4 x1, uint4 x2,
+                                             uint4 x3) {
+    const int tid = threadIdx.x;
+    unsigned char* dst = buf + (tid >> 3) * (M_LD * 2) + (tid & 7) * 16;
+    *reinterpret_cast<uint4*>(dst + 0 * 32 * (M_LD * 2)) = x0;
+    *reinterpret_cast<uint4*>(dst + 1 * 32 * (M_LD * 2)) = x1;
+    *reinterpret_cast<uint4*>(dst + 2 * 32 * (M_LD * 2)) = x2;
+    *reinterpret_cast<uint4*>(dst + 3 * 32 * (M_LD * 2)) = x3;
 }
 
 __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ stats, float* __restrict__ out,
+    const uint16_t* __restrict__ v, const float* __restrict__ stats,
+    const uint16_t* __restrict__ packed, float* __restrict__ out,
     int n, int row0, int BH, float sl2, float lambda) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -278,7 +286,6 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const int last = min(i0 + B_WAVES - 1, n - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
     const uint16_t* kh = k + base;
-    const uint16_t* vh = v + base;
     const float* st = stats + (static_cast<int64_t>(bh) * nrows + (ic - row0)) * SROW;
 
     // Centring constants of this wave's query, rounded to fp16, for feature c + 16 fb.
@@ -301,16 +308,18 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     }
 
     // sqrt of the shifted weights of key block w (16 keys) for the 4 queries -> Sw buffer.
-    auto scores = [&](const TileRegs& r, unsigned char* buf, int j0) {
+    auto scores = [&](uint4 kq0, uint4 kq1, unsigned char* buf, int j0) {
         float4v s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) s = mfma_bf16(__builtin_bit_cast(bf16x8, r.kq[ks]), qf[ks], s);
+        s = mfma_bf16(__builtin_bit_cast(bf16x8, kq0), qf[0], s);
+        s = mfma_bf16(__builtin_bit_cast(bf16x8, kq1), qf[1], s);
         if (colv) {
             half4 sw4;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int j = j0 + 16 * w + 4 * g + rr;
-                sw4[rr] = static_cast<_Float16>(j <= qcol ? exp2f((s[rr] * sl2 - mcol) * 0.5f) : 0.0f);
+                // raw v_exp_f32: weights below 2^-126 flush to zero, which changes nothing
+                sw4[rr] = static_cast<_Float16>(
+                    j <= qcol ? __builtin_amdgcn_exp2f((s[rr] * sl2 - mcol) * 0.5f) : 0.0f);
             }
             _Float16* sw = reinterpret_cast<_Float16*>(buf + 2 * FD * M_LD * 2);
             *reinterpret_cast<half4*>(sw + c * MT + 16 * w + 4 * g) = sw4;
@@ -324,17 +333,30 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     for (int t = 0; t < 16; ++t) cvk[t] = float4v{0.f, 0.f, 0.f, 0.f};
 
     const int ntiles = (last + MT) / MT;
-    TileRegs regs;
-    load_tile(regs, kh, vh, n, 0, w, g, c);
-    store_tile(regs, smem);
-    scores(regs, smem, 0);
+    const int ptiles = (n + MT - 1) / MT;
+    const uint16_t* pk = packed + static_cast<int64_t>(bh) * ptiles * PACK_TILE_HALVES + tid * 8;
+    // Prefetch registers: the packed tile's 4 chunks and the score operand (key 16w + c).
+    uint4 x0, x1, x2, x3, kq0, kq1;
+    auto fetch = [&](int tt) {
+        const uint16_t* src = pk + static_cast<int64_t>(tt) * PACK_TILE_HALVES;
+        x0 = *reinterpret_cast<const uint4*>(src);
+        x1 = *reinterpret_cast<const uint4*>(src + 2048);
+        x2 = *reinterpret_cast<const uint4*>(src + 4096);
+        x3 = *reinterpret_cast<const uint4*>(src + 6144);
+        const int jq = min(tt * MT + 16 * w + c, n - 1);   // clamped: masked by the score
+        kq0 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 8 * g);
+        kq1 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 32 + 8 * g);
+    };
+    fetch(0);
+    store_chunks(smem, x0, x1, x2, x3);
+    scores(kq0, kq1, smem, 0);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
         const int j0 = t * MT;
         unsigned char* cur = smem + (t & 1) * M_BUF_BYTES;
         unsigned char* nxt = smem + ((t + 1) & 1) * M_BUF_BYTES;
         const bool more = t + 1 < ntiles;
-        if (more) load_tile(regs, kh, vh, n, j0 + MT, w, g, c);
+        fetch(more ? t + 1 : t);   // unconditional: the last iteration re-reads its own tile
         const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
         const _Float16* Vt = Kt + FD * M_LD;
         const _Float16* Sw = Vt + FD * M_LD;
@@ -362,8 +384,8 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
             }
         }
         if (more) {
-            store_tile(regs, nxt);
-            scores(regs, nxt, j0 + MT);
+            store_chunks(nxt, x0, x1, x2, x3);
+            scores(kq0, kq1, nxt, j0 + MT);
         }
         __syncthreads();
     }
@@ -421,9 +443,11 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         colb[lane] = ar[p];
         LDS_FENCE();
         const float piv = colb[p];
+        // An IEEE divide here (not v_rcp_f32): with the cheaper reciprocal the compiler
+        // sinks the row updates across steps and runs out of registers.
         const float inv = piv > thresh ? 1.0f / piv : 0.0f;
         const float f = lane > p ? ar[p] * inv : 0.0f;
-        const float zp = __shfl(z, p);
+        const float zp = lane_value(z, p);
         z = fmaf(-f, zp, z);
 #pragma unroll
         for (int b = p + 1; b < FD; ++b) ar[b] = fmaf(-f, colb[b], ar[b]);
@@ -433,9 +457,9 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     float ylane = 0.0f;
 #pragma unroll
     for (int p = FD - 1; p >= 0; --p) {
-        const float dp = __shfl(ar[p], p);
-        const float zp = __shfl(z, p);
-        const float yp = dp > thresh ? zp / dp : 0.0f;
+        const float dp = lane_value(ar[p], p);
+        const float zp = lane_value(z, p);
+        const float yp = dp > thresh ? zp * __builtin_amdgcn_rcpf(dp) : 0.0f;
         ylane = lane == p ? yp : ylane;
         z = fmaf(-ar[p], yp, z);
     }
@@ -636,7 +660,10 @@ bool fast_supports(int dtype, int64_t d) { return dtype == 1 && d == FD; }
 
 size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
     const int64_t rows = n - fast_row0(n, d);
-    return rows > 0 ? static_cast<size_t>(B * H * rows * SROW) * sizeof(float) : 0;
+    if (rows <= 0) return 0;
+    const int64_t stats = B * H * rows * SROW * static_cast<int64_t>(sizeof(float));
+    const int64_t tiles = B * H * ((n + MT - 1) / MT) * PACK_TILE_HALVES * 2;
+    return static_cast<size_t>(stats + tiles);
 }
 
 hipError_t launch_fast(const Problem& p, void* workspace) {
@@ -666,6 +693,13 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     const auto* k = static_cast<const uint16_t*>(p.k);
     const auto* v = static_cast<const uint16_t*>(p.v);
     float* stats = static_cast<float*>(workspace);
+    const int ptiles = (n + MT - 1) / MT;
+    uint16_t* packed = reinterpret_cast<uint16_t*>(
+        static_cast<unsigned char*>(workspace) + static_cast<int64_t>(BH) * nrows * SROW * sizeof(float));
+    prof_begin(p.stream, "lla_pack_kernel");
+    lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(k, v, packed, n, ptiles);
+    prof_end(p.stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
 
     const unsigned blocks_a = static_cast<unsigned>(BH) * ((nrows + A_QB - 1) / A_QB);
     prof_begin(p.stream, "lla_stats_kernel");
@@ -676,7 +710,7 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     const unsigned blocks_b = static_cast<unsigned>(BH) * ((nrows + B_WAVES - 1) / B_WAVES);
     prof_begin(p.stream, "lla_moments_kernel");
     lla_moments_kernel<<<dim3(blocks_b), dim3(256), B_SMEM, p.stream>>>(
-        q, k, v, stats, p.out, n, row0, BH, sl2, static_cast<float>(p.lambda));
+        q, k, v, stats, packed, p.out, n, row0, BH, sl2, static_cast<float>(p.lambda));
     prof_end(p.stream);
     return hipGetLastError();
 }

@@ -117,9 +117,11 @@ def test_path_availability_query():
 
 def test_workspace_size():
     from local_linear_attention_amd import lla
-    # fast path: 4*(2d+4) bytes for every row at or beyond 2d
-    assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "fast") == 2 * 16 * (4096 - 128) * 132 * 4
-    assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "auto") == 2 * 16 * (4096 - 128) * 132 * 4
+    # fast path: 4*(2d+4) bytes for every row at or beyond 2d, then fp16 K/V tiles of 64 keys
+    expect = 2 * 16 * (4096 - 128) * 132 * 4 + 2 * 16 * 64 * (2 * 2 * 64 * 64)
+    assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "fast") == expect
+    assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "auto") == expect
+    assert lla.lla_workspace_size(1, 1, 130, 64, "bf16", "fast") == 2 * 132 * 4 + 3 * 2 * 2 * 64 * 64
     assert lla.lla_workspace_size(1, 1, 100, 64, "bf16", "fast") == 0      # every row is short
     assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "exact") == 0
     assert lla.lla_workspace_size(2, 16, 4096, 64, "f32", "auto") == 0
