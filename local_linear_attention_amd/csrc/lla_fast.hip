@@ -204,14 +204,26 @@ __global__ __launch_bounds__(256) void lla_stats_kernel(
 // ---------------------------------------------------------------------------------------
 // Moments + solve: block = 4 waves, one query per wave (4 consecutive rows of one head).
 // Keys stream in tiles of 64: while the MFMAs consume tile t from one LDS buffer, the
-// global loads of tile t+1 are in flight into registers and then stored, transposed to
-// feature-major fp16, into the other buffer -- one barrier per tile.
+// global loads of tile t+1 are in flight into registers and then stored into the other
+// buffer -- one barrier per tile.
+//
+// Shared anchor: the block centres each staged tile once, at a = (kbar, vbar) of its first
+// query rounded to fp16, so every wave only scales: R_k = sw (k - a_k), R_v = sw (v - a_v).
+// Moments about a differ from the centred ones by a rank-one term,
+//   C = sum_j w_j (x_j - a)(y_j - a)^T - S_x S_y^T / omega',   S_x = sum_j w_j (x_j - a),
+// which the block gets from one extra MFMA pair per wave and 32 keys (weights w_j = sw_j^2
+// rounded to fp16, omega' their sum).  Using the same rounded data on both sides keeps the
+// downdated C_kk consistent with C_vk, and a nearby anchor keeps the cancellation small.
 constexpr int MT = 64;                   // keys per tile
 constexpr int M_LD = MT + 8;             // feature-major fp16 row (elements), 144 B
-constexpr int M_BUF_BYTES = 2 * FD * M_LD * 2 + B_WAVES * MT * 2;  // Kt, Vt, Sw
+constexpr int M_SW = 2 * FD * M_LD * 2;  // byte offset of Sw: sqrt-weights, [query][key]
+constexpr int M_SW2 = M_SW + B_WAVES * MT * 2;  // Sw2: fp16 weights, 16 rows (rows >= 4 zero)
+constexpr int M_BUF_BYTES = M_SW2 + 16 * MT * 2;
 constexpr int B_SOLVE_FLOATS = FD * (FD + 1) + 2 * FD;  // A (padded rows) + pivot column + y
-constexpr int B_SMEM = (B_SOLVE_FLOATS * 4 * B_WAVES > 2 * M_BUF_BYTES)
-                           ? B_SOLVE_FLOATS * 4 * B_WAVES : 2 * M_BUF_BYTES;
+constexpr int B_SOLVE_BYTES = B_SOLVE_FLOATS * 4 * B_WAVES;
+constexpr int B_MEAN_FLOATS = 2 * FD + B_WAVES;          // per query: S_k, S_v, omega' parts
+constexpr int B_MEAN_OFF = B_SOLVE_BYTES > 2 * M_BUF_BYTES ? B_SOLVE_BYTES : 2 * M_BUF_BYTES;
+constexpr int B_SMEM = B_MEAN_OFF + B_WAVES * B_MEAN_FLOATS * 4;
 
 // Keys and values of one 64-key tile, feature-major fp16, as the pack kernel lays them out
 // in the workspace: [K or V][feature][key], 2 x 64 x 64 halves = 16 KiB per tile.
@@ -255,15 +267,16 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
 }
 
 // Chunk tid + 256 u (16 B) of a packed tile sits in feature row (tid / 8) + 32 u (K rows
-// then V rows), keys 8 (tid % 8) .. +8; it goes to the same place in the padded LDS tile.
+// then V rows), keys 8 (tid % 8) .. +8; it goes, minus the anchor of that row (an fp16
+// subtraction, rounded once), to the same place in the padded LDS tile.
 __device__ __forceinline__ void store_chunks(unsigned char* buf, uint4 x0, uint4 x1, uint4 x2,
-                                             uint4 x3) {
+                                             uint4 x3, const _Float16 (&na)[4]) {
     const int tid = threadIdx.x;
     unsigned char* dst = buf + (tid >> 3) * (M_LD * 2) + (tid & 7) * 16;
-    *reinterpret_cast<uint4*>(dst + 0 * 32 * (M_LD * 2)) = x0;
-    *reinterpret_cast<uint4*>(dst + 1 * 32 * (M_LD * 2)) = x1;
-    *reinterpret_cast<uint4*>(dst + 2 * 32 * (M_LD * 2)) = x2;
-    *reinterpret_cast<uint4*>(dst + 3 * 32 * (M_LD * 2)) = x3;
+    *reinterpret_cast<half8*>(dst + 0 * 32 * (M_LD * 2)) = __builtin_bit_cast(half8, x0) + na[0];
+    *reinterpret_cast<half8*>(dst + 1 * 32 * (M_LD * 2)) = __builtin_bit_cast(half8, x1) + na[1];
+    *reinterpret_cast<half8*>(dst + 2 * 32 * (M_LD * 2)) = __builtin_bit_cast(half8, x2) + na[2];
+    *reinterpret_cast<half8*>(dst + 3 * 32 * (M_LD * 2)) = __builtin_bit_cast(half8, x3) + na[3];
 }
 
 __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
@@ -288,12 +301,16 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const uint16_t* kh = k + base;
     const float* st = stats + (static_cast<int64_t>(bh) * nrows + (ic - row0)) * SROW;
 
-    // Centring constants of this wave's query, rounded to fp16, for feature c + 16 fb.
-    _Float16 nkb[4], nvb[4];
+    // Negated anchor of this thread's four chunk rows (stats row: kbar[64] then vbar[64]).
+    const float* st0 = stats + (static_cast<int64_t>(bh) * nrows + (i0 - row0)) * SROW;
+    _Float16 nanc[4];
 #pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-        nkb[fb] = static_cast<_Float16>(-st[fb * 16 + c]);
-        nvb[fb] = static_cast<_Float16>(-st[FD + fb * 16 + c]);
+    for (int u = 0; u < 4; ++u) nanc[u] = static_cast<_Float16>(-st0[(tid >> 3) + 32 * u]);
+    // Rows B_WAVES.. of both Sw2 buffers are the zero rows of the weight operand.
+    for (int e = tid; e < 2 * (16 - B_WAVES) * MT / 8; e += 256) {
+        const int bsel = e / ((16 - B_WAVES) * MT / 8), rem = e % ((16 - B_WAVES) * MT / 8);
+        *reinterpret_cast<uint4*>(smem + bsel * M_BUF_BYTES + M_SW2 + B_WAVES * MT * 2 + rem * 16) =
+            make_uint4(0, 0, 0, 0);
     }
     // Score operand: column c < B_WAVES is query i0 + c (the other columns are zero).
     const int qcol = min(i0 + c, n - 1);
@@ -307,7 +324,9 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         qf[ks] = __builtin_bit_cast(bf16x8, raw);
     }
 
-    // sqrt of the shifted weights of key block w (16 keys) for the 4 queries -> Sw buffer.
+    // sqrt of the shifted weights of key block w (16 keys) for the 4 queries -> Sw buffer,
+    // their fp16 squares -> Sw2; om2p sums those squares (query c, keys of block w).
+    float om2p = 0.0f;
     auto scores = [&](uint4 kq0, uint4 kq1, unsigned char* buf, int j0) {
         float4v s = {0.f, 0.f, 0.f, 0.f};
         s = mfma_bf16(__builtin_bit_cast(bf16x8, kq0), qf[0], s);
@@ -321,8 +340,11 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
                 sw4[rr] = static_cast<_Float16>(
                     j <= qcol ? __builtin_amdgcn_exp2f((s[rr] * sl2 - mcol) * 0.5f) : 0.0f);
             }
-            _Float16* sw = reinterpret_cast<_Float16*>(buf + 2 * FD * M_LD * 2);
-            *reinterpret_cast<half4*>(sw + c * MT + 16 * w + 4 * g) = sw4;
+            const half4 w4 = sw4 * sw4;
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW) + c * MT + 16 * w + 4 * g) = sw4;
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW2) + c * MT + 16 * w + 4 * g) = w4;
+            om2p += (static_cast<float>(w4[0]) + static_cast<float>(w4[1])) +
+                    (static_cast<float>(w4[2]) + static_cast<float>(w4[3]));
         }
     };
 
@@ -331,6 +353,8 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     for (int t = 0; t < 10; ++t) ckk[t] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 16; ++t) cvk[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    // S_k, S_v of the block's queries (rows) for features 16 w + c (columns).
+    float4v sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
 
     const int ntiles = (last + MT) / MT;
     const int ptiles = (n + MT - 1) / MT;
@@ -348,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         kq1 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 32 + 8 * g);
     };
     fetch(0);
-    store_chunks(smem, x0, x1, x2, x3);
+    store_chunks(smem, x0, x1, x2, x3, nanc);
     scores(kq0, kq1, smem, 0);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
@@ -359,16 +383,24 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         fetch(more ? t + 1 : t);   // unconditional: the last iteration re-reads its own tile
         const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
         const _Float16* Vt = Kt + FD * M_LD;
-        const _Float16* Sw = Vt + FD * M_LD;
+        const _Float16* Sw = reinterpret_cast<const _Float16*>(cur + M_SW);
+        const _Float16* Sw2 = reinterpret_cast<const _Float16*>(cur + M_SW2);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
+            if (j0 + 32 * sub > last) break;  // block-uniform: past every query of the block
+            {   // S_k, S_v of all 4 queries, feature block w
+                const int ko = (w * 16 + c) * M_LD + 32 * sub + 8 * g;
+                const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * MT + 32 * sub + 8 * g);
+                sk = mfma_f16(w8, *reinterpret_cast<const half8*>(Kt + ko), sk);
+                sv = mfma_f16(w8, *reinterpret_cast<const half8*>(Vt + ko), sv);
+            }
             if (j0 + 32 * sub > ic) break;  // wave-uniform: the rest lies past this query
             const half8 sw = *reinterpret_cast<const half8*>(Sw + w * MT + 32 * sub + 8 * g);
             half8 rk[4];
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb) {
                 const half8 kf = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * M_LD + 32 * sub + 8 * g);
-                rk[fb] = (kf + nkb[fb]) * sw;
+                rk[fb] = kf * sw;
             }
             int idx = 0;
 #pragma unroll
@@ -378,23 +410,51 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 #pragma unroll
             for (int fv = 0; fv < 4; ++fv) {
                 const half8 vf = *reinterpret_cast<const half8*>(Vt + (fv * 16 + c) * M_LD + 32 * sub + 8 * g);
-                const half8 rv = (vf + nvb[fv]) * sw;
+                const half8 rv = vf * sw;
 #pragma unroll
                 for (int fb = 0; fb < 4; ++fb) cvk[fb * 4 + fv] = mfma_f16(rk[fb], rv, cvk[fb * 4 + fv]);
             }
         }
         if (more) {
-            store_chunks(nxt, x0, x1, x2, x3);
+            store_chunks(nxt, x0, x1, x2, x3, nanc);
             scores(kq0, kq1, nxt, j0 + MT);
         }
         __syncthreads();
     }
+
+    // ---- block sums -> LDS (outside the solve area): row r of sk / sv is query r.
+    float* means = reinterpret_cast<float*>(smem + B_MEAN_OFF);
+    om2p += __shfl_xor(om2p, 16);
+    om2p += __shfl_xor(om2p, 32);
+    if (g == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            means[r * B_MEAN_FLOATS + w * 16 + c] = sk[r];
+            means[r * B_MEAN_FLOATS + FD + w * 16 + c] = sv[r];
+        }
+        if (colv) means[c * B_MEAN_FLOATS + 2 * FD + w] = om2p;
+    }
+    __syncthreads();
+    const float* mq = means + w * B_MEAN_FLOATS;
+    float om2 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < B_WAVES; ++t) om2 += mq[2 * FD + t];
+    const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
 
     // ---- ridge-rescaled SPD solve, lane a owns row a (the solve area aliases the tiles)
     constexpr int ALD = FD + 1;
     float* A = reinterpret_cast<float*>(smem) + w * B_SOLVE_FLOATS;
     float* colb = A + FD * ALD;
     float* yv = colb + FD;
+    // Rank-one downdates: C_kk -= S_k S_k^T / omega', C_vk^T -= S_k S_v^T / omega'.
+    float4v skr[4];
+    float skc[4], svc[4];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+        skr[fb] = *reinterpret_cast<const float4v*>(mq + fb * 16 + 4 * g) * iom2;
+        skc[fb] = mq[fb * 16 + c];
+        svc[fb] = mq[FD + fb * 16 + c];
+    }
     {
         int idx = 0;
 #pragma unroll
@@ -404,12 +464,19 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = fb * 16 + 4 * g + r, col = fb2 * 16 + c;
-                    A[row * ALD + col] = ckk[idx][r];
-                    if (fb != fb2) A[col * ALD + row] = ckk[idx][r];
+                    const float val = fmaf(-skr[fb][r], skc[fb2], ckk[idx][r]);
+                    A[row * ALD + col] = val;
+                    if (fb != fb2) A[col * ALD + row] = val;
                 }
                 ++idx;
             }
     }
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int fv = 0; fv < 4; ++fv)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cvk[fb * 4 + fv][r] = fmaf(-skr[fb][r], svc[fv], cvk[fb * 4 + fv][r]);
     LDS_FENCE();
     const float m_x = st[2 * FD] * LOG2E;
     const float lam_s = lambda * exp2f(-m_x);
@@ -426,10 +493,11 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 #pragma unroll
     for (int b = 0; b < FD; ++b) ar[b] = A[lane * ALD + b];
     LDS_FENCE();
-    // Park C_vk^T in the (now free) matrix area during the elimination, lane-private.
-    float4v* park = reinterpret_cast<float4v*>(A) + lane * 16;
+    // Park C_vk^T in the (now free) matrix area during the elimination, lane-private;
+    // entry t of lane l at float4 index 64 t + l keeps the 64 lanes on distinct banks.
+    float4v* park = reinterpret_cast<float4v*>(A) + lane;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) park[t] = cvk[t];
+    for (int t = 0; t < 16; ++t) park[64 * t] = cvk[t];
     // The accumulators must really leave the registers: no store-to-load forwarding.
     LDS_FENCE();
     const float qa = bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]);
@@ -473,7 +541,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         const float4v yy = *reinterpret_cast<const float4v*>(yv + fb * 16 + 4 * g);
 #pragma unroll
         for (int fv = 0; fv < 4; ++fv) {
-            const float4v cv = park[fb * 4 + fv];
+            const float4v cv = park[64 * (fb * 4 + fv)];
 #pragma unroll
             for (int r = 0; r < 4; ++r) part[fv] = fmaf(cv[r], yy[r], part[fv]);
         }
