@@ -388,13 +388,12 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             if (j0 + 32 * sub > last) break;  // block-uniform: past every query of the block
-            {   // S_k, S_v of all 4 queries, feature block w
-                const int ko = (w * 16 + c) * M_LD + 32 * sub + 8 * g;
-                const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * MT + 32 * sub + 8 * g);
-                sk = mfma_f16(w8, *reinterpret_cast<const half8*>(Kt + ko), sk);
-                sv = mfma_f16(w8, *reinterpret_cast<const half8*>(Vt + ko), sv);
-            }
-            if (j0 + 32 * sub > ic) break;  // wave-uniform: the rest lies past this query
+            // Operands of the block sums S_k, S_v (all 4 queries, feature block w).
+            const int ko = (w * 16 + c) * M_LD + 32 * sub + 8 * g;
+            const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * MT + 32 * sub + 8 * g);
+            const half8 kw = *reinterpret_cast<const half8*>(Kt + ko);
+            const half8 vw = *reinterpret_cast<const half8*>(Vt + ko);
+            if (j0 + 32 * sub <= ic) {  // wave-uniform: keys of this query's prefix
             const half8 sw = *reinterpret_cast<const half8*>(Sw + w * MT + 32 * sub + 8 * g);
             half8 rk[4];
 #pragma unroll
@@ -414,6 +413,9 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 #pragma unroll
                 for (int fb = 0; fb < 4; ++fb) cvk[fb * 4 + fv] = mfma_f16(rk[fb], rv, cvk[fb * 4 + fv]);
             }
+            }
+            sk = mfma_f16(w8, kw, sk);
+            sv = mfma_f16(w8, vw, sv);
         }
         if (more) {
             store_chunks(nxt, x0, x1, x2, x3, nanc);
