@@ -229,6 +229,22 @@ constexpr int B_SMEM = B_MEAN_OFF + B_WAVES * B_MEAN_FLOATS * 4;
 // in the workspace: [K or V][feature][key], 2 x 64 x 64 halves = 16 KiB per tile.
 constexpr int PACK_TILE_HALVES = 2 * FD * MT;
 
+// Block b -> (head bh, row block blk).  Work-groups go round-robin to the 8 XCDs, so
+// b % 8 picks the XCD: heads are taken 8 at a time (head 8 G + b % 8 on XCD b % 8) and, in
+// each group of 8, row blocks run longest first.  Each XCD's L2 then holds the packed K/V of
+// about one head at a time instead of a quarter of all heads.
+__device__ __forceinline__ void head_major_block(int b, int BH, int nblk, int* bh, int* blk) {
+    const int full = BH / 8, span = 8 * nblk;
+    int hg, r, hcnt;
+    if (b < full * span) {
+        hg = b / span; r = b - hg * span; hcnt = 8;
+    } else {
+        hg = full; r = b - full * span; hcnt = BH - 8 * full;
+    }
+    *blk = nblk - 1 - r / hcnt;
+    *bh = 8 * hg + r % hcnt;
+}
+
 // Pack K and V once into feature-major fp16 tiles (zero past n).  Thread -> keys 2p, 2p+1
 // and features 8fg .. 8fg+7; every store writes packed pairs of keys, 128 contiguous bytes
 // per 32 lanes.  bf16 values in fp16 range convert exactly.
@@ -290,8 +306,9 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const int g = lane >> 4, c = lane & 15;
     const int nrows = n - row0;
     const int nblk = (nrows + B_WAVES - 1) / B_WAVES;
-    const int blk = nblk - 1 - static_cast<int>(blockIdx.x / BH);  // longest rows first
-    const int bh = static_cast<int>(blockIdx.x % BH);
+    int blk, bh;
+    head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
+
     const int i0 = row0 + blk * B_WAVES;
     const int i = i0 + w;
     const bool valid = i < n;
