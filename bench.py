@@ -51,6 +51,7 @@ KERNEL_BOUND = {
     "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_short_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_stats_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_anchor_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_moments_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
 }
@@ -72,8 +73,8 @@ def kernel_flops(name, B, H, n, d, path):
     if name in ("lla_exact_kernel", "lla_short_kernel"):
         return pair_count(BH, 0, row0) * (2 * d + 2 * (1 + 2 * d) + d * (d + 1) + 2 * d * d) \
             + BH * row0 * per_query
-    if name == "lla_pack_kernel":
-        return 0                      # data movement only (K, V repacked once)
+    if name in ("lla_anchor_kernel", "lla_pack_kernel"):
+        return 0                      # data movement only (K, V summed and repacked once)
     if name == "lla_stats_kernel":
         return pair_count(BH, row0, n) * (2 * d + 2 * (1 + 2 * d))
     if name == "lla_moments_kernel":

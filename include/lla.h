@@ -99,9 +99,11 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
                             lla_dtype_t dtype, void* stream, lla_path_t path);
 
 /* Bytes of device scratch that `path` needs for this problem (0 if none, or if the sizes,
- * dtype or path are invalid).  The fast path keeps per-row statistics there, 4*(2d+4) bytes
- * for every row at or beyond position 2d, followed by K and V of every head repacked as
- * fp16 tiles of 64 keys, 2*2*d*64 bytes per tile (zero past n); nothing when n <= 2d. */
+ * dtype or path are invalid).  Per head, the fast path keeps there: per-row statistics,
+ * 4*(2d+4) bytes for every row at or beyond position 2d; 16*2d floats of partial key/value
+ * sums (the head's centring anchor); K and V repacked as fp16 tiles of 64 keys, each
+ * 2*d*72*2 bytes (feature-major rows of 64 keys plus 8 halves of padding).  Nothing when
+ * n <= 2d.  The fast path serves n up to 4194304 (2^22); AUTO uses the exact path beyond. */
 size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                           lla_path_t path);
 
@@ -123,7 +125,8 @@ lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* 
 int lla_profile_enable(int enable);
 int lla_profile_collect(const char** names, float* ms, int max_entries);
 
-/* 1 if `path` covers inputs of `dtype` with head dimension `d`, else 0.  Host-only: makes
+/* 1 if `path` covers inputs of `dtype` with head dimension `d` (for the fast path: at
+ * some sequence length; see lla_workspace_size for its limit), else 0.  Host-only: makes
  * no HIP call.  LLA_PATH_AUTO and LLA_PATH_EXACT cover every supported (dtype, d). */
 int lla_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d);
 

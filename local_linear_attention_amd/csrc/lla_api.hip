@@ -54,11 +54,11 @@ lla_status_t validate(const void* q, const void* k, const void* v, const float* 
 }
 
 // Resolve a requested path to the kernels that run; false if it cannot serve the shape.
-bool resolve_fast(lla_path_t path, int dtype, int64_t d, bool* fast) {
+bool resolve_fast(lla_path_t path, int dtype, int64_t d, int64_t n, bool* fast) {
     switch (path) {
         case LLA_PATH_EXACT: *fast = false; return true;
-        case LLA_PATH_FAST: *fast = true; return lla::fast_supports(dtype, d);
-        case LLA_PATH_AUTO: *fast = lla::fast_supports(dtype, d); return true;
+        case LLA_PATH_FAST: *fast = true; return lla::fast_supports(dtype, d, n);
+        case LLA_PATH_AUTO: *fast = lla::fast_supports(dtype, d, n); return true;
     }
     return false;
 }
@@ -175,14 +175,14 @@ int lla_version(void) { return kVersion; }
 int lla_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d) {
     if (!supported_shape(d, dtype)) return 0;
     bool fast = false;
-    return resolve_fast(path, static_cast<int>(dtype), d, &fast) ? 1 : 0;
+    return resolve_fast(path, static_cast<int>(dtype), d, 1, &fast) ? 1 : 0;
 }
 
 size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                           lla_path_t path) {
     if (!supported_shape(d, dtype) || validate_sizes(B, H, n, d) != LLA_OK) return 0;
     bool fast = false;
-    if (!resolve_fast(path, static_cast<int>(dtype), d, &fast) || !fast) return 0;
+    if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast) || !fast) return 0;
     return lla::fast_workspace_bytes(B, H, n, d);
 }
 
@@ -194,7 +194,7 @@ lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* 
     const lla_status_t st = validate(q, k, v, out, B, H, n, d, h, lambda, dtype);
     if (st != LLA_OK) return st;
     bool fast = false;
-    if (!resolve_fast(path, static_cast<int>(dtype), d, &fast)) return LLA_ERR_UNSUPPORTED;
+    if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
     const lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream)};
     return run(p, fast, workspace, workspace_bytes, false);
@@ -207,7 +207,7 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
     const lla_status_t st = validate(q, k, v, out, B, H, n, d, h, lambda, dtype);
     if (st != LLA_OK) return st;
     bool fast = false;
-    if (!resolve_fast(path, static_cast<int>(dtype), d, &fast)) return LLA_ERR_UNSUPPORTED;
+    if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
     const lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream)};
     return run(p, fast, nullptr, 0, true);

@@ -33,6 +33,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
@@ -53,6 +54,15 @@ constexpr int B_WAVES = 4;                                     // moments: 1 que
 // (A blocked variant of the solve below was miscompiled without such fences on gfx950:
 // an LDS access moved across a dependent one.  The fences cost no instructions.)
 #define LDS_FENCE() __asm__ volatile("" ::: "memory")
+
+// A wave-uniform pointer, rebuilt from scalar registers so that memory instructions can use
+// the scalar-base addressing form.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    return reinterpret_cast<const unsigned char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 // Value of x in lane `src` (a compile-time lane), broadcast to the wave.
 __device__ __forceinline__ float lane_value(float x, int src) {
@@ -203,31 +213,38 @@ __global__ __launch_bounds__(256) void lla_stats_kernel(
 
 // ---------------------------------------------------------------------------------------
 // Moments + solve: block = 4 waves, one query per wave (4 consecutive rows of one head).
-// Keys stream in tiles of 64: while the MFMAs consume tile t from one LDS buffer, the
-// global loads of tile t+1 are in flight into registers and then stored into the other
-// buffer -- one barrier per tile.
+// Keys stream in tiles of 64 through a ring of three LDS buffers: tile t is consumed by the
+// MFMAs while tile t+1 is landing and tile t+2 is being copied from the workspace straight
+// into LDS (buffer loads with an LDS destination, no registers) -- one barrier per tile.
 //
-// Shared anchor: the block centres each staged tile once, at a = (kbar, vbar) of its first
-// query rounded to fp16, so every wave only scales: R_k = sw (k - a_k), R_v = sw (v - a_v).
-// Moments about a differ from the centred ones by a rank-one term,
+// Anchor: the pack kernel stores each head's keys and values centred at a = (mean k,
+// mean v) of the head rounded to fp16, so every wave only scales: R_k = sw (k - a_k),
+// R_v = sw (v - a_v).  Moments about a differ from the centred ones by a rank-one term,
 //   C = sum_j w_j (x_j - a)(y_j - a)^T - S_x S_y^T / omega',   S_x = sum_j w_j (x_j - a),
 // which the block gets from one extra MFMA pair per wave and 32 keys (weights w_j = sw_j^2
 // rounded to fp16, omega' their sum).  Using the same rounded data on both sides keeps the
-// downdated C_kk consistent with C_vk, and a nearby anchor keeps the cancellation small.
+// downdated C_kk consistent with C_vk; the cancellation in the downdate grows with
+// |kbar_i - a|^2 over the weighted spread of the keys, small while the query's weights are
+// spread over many keys (as on RMS-normalised heads at h = sqrt(d)).
 constexpr int MT = 64;                   // keys per tile
 constexpr int M_LD = MT + 8;             // feature-major fp16 row (elements), 144 B
-constexpr int M_SW = 2 * FD * M_LD * 2;  // byte offset of Sw: sqrt-weights, [query][key]
+// One tile as the pack kernel lays it out in the workspace and the moments kernel copies it,
+// byte for byte, into LDS: [K or V][feature][key], rows of M_LD halves (the last 8 are
+// padding that keeps the 16-byte operand reads conflict-free), 18 KiB per tile.
+constexpr int PACK_TILE_BYTES = 2 * FD * M_LD * 2;
+constexpr int M_LOADS = PACK_TILE_BYTES / 1024;  // wave-wide copies of 16 B per lane per tile
+constexpr int M_WLOADS = (M_LOADS + B_WAVES - 1) / B_WAVES;   // copies issued by each wave
+constexpr int M_NBUF = 3;                // tile ring: compute t, t+1 landing, t+2 in flight
+constexpr int M_SW = PACK_TILE_BYTES;    // byte offset of Sw: sqrt-weights, [query][key]
 constexpr int M_SW2 = M_SW + B_WAVES * MT * 2;  // Sw2: fp16 weights, 16 rows (rows >= 4 zero)
 constexpr int M_BUF_BYTES = M_SW2 + 16 * MT * 2;
 constexpr int B_SOLVE_FLOATS = FD * (FD + 1) + 2 * FD;  // A (padded rows) + pivot column + y
 constexpr int B_SOLVE_BYTES = B_SOLVE_FLOATS * 4 * B_WAVES;
 constexpr int B_MEAN_FLOATS = 2 * FD + B_WAVES;          // per query: S_k, S_v, omega' parts
-constexpr int B_MEAN_OFF = B_SOLVE_BYTES > 2 * M_BUF_BYTES ? B_SOLVE_BYTES : 2 * M_BUF_BYTES;
+constexpr int B_MEAN_OFF = B_SOLVE_BYTES > M_NBUF * M_BUF_BYTES ? B_SOLVE_BYTES : M_NBUF * M_BUF_BYTES;
 constexpr int B_SMEM = B_MEAN_OFF + B_WAVES * B_MEAN_FLOATS * 4;
-
-// Keys and values of one 64-key tile, feature-major fp16, as the pack kernel lays them out
-// in the workspace: [K or V][feature][key], 2 x 64 x 64 halves = 16 KiB per tile.
-constexpr int PACK_TILE_HALVES = 2 * FD * MT;
+constexpr int ANCHOR_SLICES = 16;        // key slices of the per-head anchor sums
+static_assert(PACK_TILE_BYTES % 1024 == 0, "tile image must be whole wave copies");
 
 // Block b -> (head bh, row block blk).  Work-groups go round-robin to the 8 XCDs, so
 // b % 8 picks the XCD: heads are taken 8 at a time (head 8 G + b % 8 on XCD b % 8) and, in
@@ -245,15 +262,42 @@ __device__ __forceinline__ void head_major_block(int b, int BH, int nblk, int* b
     *bh = 8 * hg + r % hcnt;
 }
 
-// Pack K and V once into feature-major fp16 tiles (zero past n).  Thread -> keys 2p, 2p+1
-// and features 8fg .. 8fg+7; every store writes packed pairs of keys, 128 contiguous bytes
-// per 32 lanes.  bf16 values in fp16 range convert exactly.
+// Per-head anchor, pass 1: block (head, slice) sums its slice of the keys and values per
+// feature (fp32; threads t and t + 128 take alternate keys of feature t % 128).
+__global__ __launch_bounds__(256) void lla_anchor_kernel(const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v,
+                                                         float* __restrict__ partial, int n) {
+    __shared__ float half_sum[128];
+    const int bh = static_cast<int>(blockIdx.x) / ANCHOR_SLICES;
+    const int sl = static_cast<int>(blockIdx.x) % ANCHOR_SLICES;
+    const int tid = threadIdx.x, f = tid & 127, ph = tid >> 7;
+    const int len = (n + ANCHOR_SLICES - 1) / ANCHOR_SLICES;
+    const int j_lo = sl * len, j_hi = min(n, j_lo + len);
+    const uint16_t* src = (f < FD ? k : v) + static_cast<int64_t>(bh) * n * FD + (f & (FD - 1));
+    float acc = 0.0f;
+    for (int j = j_lo + ph; j < j_hi; j += 2) acc += bf16_bits_to_f32(src[static_cast<int64_t>(j) * FD]);
+    if (ph == 1) half_sum[f] = acc;
+    __syncthreads();
+    if (ph == 0) partial[(static_cast<int64_t>(bh) * ANCHOR_SLICES + sl) * 2 * FD + f] = acc + half_sum[f];
+}
+
+// Pack K and V once into the LDS image of each tile (zero past n), centred at the head's
+// anchor a = fp16(mean over all keys of k, of v): stored value fp16(x - a), one rounding.
+// Thread -> keys 2p, 2p+1 and features 8fg .. 8fg+7; every store writes a pair of keys.
 __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
-                                                       uint16_t* __restrict__ packed, int n,
+                                                       const float* __restrict__ partial,
+                                                       unsigned char* __restrict__ packed, int n,
                                                        int ntiles) {
+    __shared__ float anc[2 * FD];
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
     const int tid = threadIdx.x, pr = tid & 31, fg = tid >> 5;
+    if (tid < 2 * FD) {
+        float sum = 0.0f;
+        for (int sl = 0; sl < ANCHOR_SLICES; ++sl)
+            sum += partial[(static_cast<int64_t>(bh) * ANCHOR_SLICES + sl) * 2 * FD + tid];
+        anc[tid] = static_cast<float>(static_cast<_Float16>(sum / static_cast<float>(n)));
+    }
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
     const int ja = t * MT + 2 * pr, jb = ja + 1;
     uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0, v0 = k0, v1 = k0;
@@ -265,44 +309,40 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
         k1 = *reinterpret_cast<const uint4*>(k + base + static_cast<int64_t>(jb) * FD + 8 * fg);
         v1 = *reinterpret_cast<const uint4*>(v + base + static_cast<int64_t>(jb) * FD + 8 * fg);
     }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(packed + (static_cast<int64_t>(bh) * ntiles + t) * PACK_TILE_HALVES);
+    __syncthreads();
+    uint32_t* dst = reinterpret_cast<uint32_t*>(packed + (static_cast<int64_t>(bh) * ntiles + t) * PACK_TILE_BYTES);
     const uint32_t ka[4] = {k0.x, k0.y, k0.z, k0.w}, kb[4] = {k1.x, k1.y, k1.z, k1.w};
     const uint32_t va[4] = {v0.x, v0.y, v0.z, v0.w}, vb[4] = {v1.x, v1.y, v1.z, v1.w};
+    const bool za = ja >= n, zb = jb >= n;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int row = 8 * fg + e;
         const int hi = e & 1;
         const uint32_t kwa = ka[e >> 1], kwb = kb[e >> 1], vwa = va[e >> 1], vwb = vb[e >> 1];
-        const float fka = __uint_as_float(hi ? (kwa & 0xffff0000u) : (kwa << 16));
-        const float fkb = __uint_as_float(hi ? (kwb & 0xffff0000u) : (kwb << 16));
-        const float fva = __uint_as_float(hi ? (vwa & 0xffff0000u) : (vwa << 16));
-        const float fvb = __uint_as_float(hi ? (vwb & 0xffff0000u) : (vwb << 16));
-        dst[row * (MT / 2) + pr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fka, fkb));
-        dst[(FD + row) * (MT / 2) + pr] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fva, fvb));
+        const float ak = anc[row], av = anc[FD + row];
+        h16x2 kk, vv;
+        kk[0] = static_cast<_Float16>(za ? 0.0f : __uint_as_float(hi ? (kwa & 0xffff0000u) : (kwa << 16)) - ak);
+        kk[1] = static_cast<_Float16>(zb ? 0.0f : __uint_as_float(hi ? (kwb & 0xffff0000u) : (kwb << 16)) - ak);
+        vv[0] = static_cast<_Float16>(za ? 0.0f : __uint_as_float(hi ? (vwa & 0xffff0000u) : (vwa << 16)) - av);
+        vv[1] = static_cast<_Float16>(zb ? 0.0f : __uint_as_float(hi ? (vwb & 0xffff0000u) : (vwb << 16)) - av);
+        dst[row * (M_LD / 2) + pr] = __builtin_bit_cast(uint32_t, kk);
+        dst[(FD + row) * (M_LD / 2) + pr] = __builtin_bit_cast(uint32_t, vv);
+        if (pr < (M_LD - MT) / 2) {   // row padding
+            dst[row * (M_LD / 2) + MT / 2 + pr] = 0u;
+            dst[(FD + row) * (M_LD / 2) + MT / 2 + pr] = 0u;
+        }
     }
-}
-
-// Chunk tid + 256 u (16 B) of a packed tile sits in feature row (tid / 8) + 32 u (K rows
-// then V rows), keys 8 (tid % 8) .. +8; it goes, minus the anchor of that row (an fp16
-// subtraction, rounded once), to the same place in the padded LDS tile.
-__device__ __forceinline__ void store_chunks(unsigned char* buf, uint4 x0, uint4 x1, uint4 x2,
-                                             uint4 x3, const _Float16 (&na)[4]) {
-    const int tid = threadIdx.x;
-    unsigned char* dst = buf + (tid >> 3) * (M_LD * 2) + (tid & 7) * 16;
-    *reinterpret_cast<half8*>(dst + 0 * 32 * (M_LD * 2)) = __builtin_bit_cast(half8, x0) + na[0];
-    *reinterpret_cast<half8*>(dst + 1 * 32 * (M_LD * 2)) = __builtin_bit_cast(half8, x1) + na[1];
-    *reinterpret_cast<half8*>(dst + 2 * 32 * (M_LD * 2)) = __builtin_bit_cast(half8, x2) + na[2];
-    *reinterpret_cast<half8*>(dst + 3 * 32 * (M_LD * 2)) = __builtin_bit_cast(half8, x3) + na[3];
 }
 
 __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ stats,
-    const uint16_t* __restrict__ packed, float* __restrict__ out,
+    const unsigned char* __restrict__ packed, float* __restrict__ out,
     int n, int row0, int BH, float sl2, float lambda) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(w);   // the same value, as a scalar
     const int g = lane >> 4, c = lane & 15;
     const int nrows = n - row0;
     const int nblk = (nrows + B_WAVES - 1) / B_WAVES;
@@ -318,13 +358,8 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const uint16_t* kh = k + base;
     const float* st = stats + (static_cast<int64_t>(bh) * nrows + (ic - row0)) * SROW;
 
-    // Negated anchor of this thread's four chunk rows (stats row: kbar[64] then vbar[64]).
-    const float* st0 = stats + (static_cast<int64_t>(bh) * nrows + (i0 - row0)) * SROW;
-    _Float16 nanc[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) nanc[u] = static_cast<_Float16>(-st0[(tid >> 3) + 32 * u]);
-    // Rows B_WAVES.. of both Sw2 buffers are the zero rows of the weight operand.
-    for (int e = tid; e < 2 * (16 - B_WAVES) * MT / 8; e += 256) {
+    // Rows B_WAVES.. of every Sw2 buffer are the zero rows of the weight operand.
+    for (int e = tid; e < M_NBUF * (16 - B_WAVES) * MT / 8; e += 256) {
         const int bsel = e / ((16 - B_WAVES) * MT / 8), rem = e % ((16 - B_WAVES) * MT / 8);
         *reinterpret_cast<uint4*>(smem + bsel * M_BUF_BYTES + M_SW2 + B_WAVES * MT * 2 + rem * 16) =
             make_uint4(0, 0, 0, 0);
@@ -375,29 +410,61 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 
     const int ntiles = (last + MT) / MT;
     const int ptiles = (n + MT - 1) / MT;
-    const uint16_t* pk = packed + static_cast<int64_t>(bh) * ptiles * PACK_TILE_HALVES + tid * 8;
-    // Prefetch registers: the packed tile's 4 chunks and the score operand (key 16w + c).
-    uint4 x0, x1, x2, x3, kq0, kq1;
-    auto fetch = [&](int tt) {
-        const uint16_t* src = pk + static_cast<int64_t>(tt) * PACK_TILE_HALVES;
-        x0 = *reinterpret_cast<const uint4*>(src);
-        x1 = *reinterpret_cast<const uint4*>(src + 2048);
-        x2 = *reinterpret_cast<const uint4*>(src + 4096);
-        x3 = *reinterpret_cast<const uint4*>(src + 6144);
-        const int jq = min(tt * MT + 16 * w + c, n - 1);   // clamped: masked by the score
-        kq0 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 8 * g);
-        kq1 = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(jq) * FD + 32 + 8 * g);
+    // The head's tile images as a buffer resource: copies address them with a scalar tile
+    // offset and loop-invariant per-lane offsets, so no vector address registers are rewritten
+    // while earlier loads are still in flight.
+    const __amdgpu_buffer_rsrc_t img = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(packed + static_cast<int64_t>(bh) * ptiles * PACK_TILE_BYTES)),
+        0, ptiles * PACK_TILE_BYTES, 0x00020000);
+    int voff[M_WLOADS];
+#pragma unroll
+    for (int e = 0; e < M_WLOADS; ++e) voff[e] = lane * 16 + min(wu + B_WAVES * e, M_LOADS - 1) * 1024;
+    // The head's keys (bf16, key-major) as a buffer resource for the score operand: lane
+    // reads key 16w + c of the tile, features 8g.. and 32 + 8g..; keys at or past n lie
+    // beyond the resource's size and read as zero (their scores are masked anyway).
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(reinterpret_cast<const unsigned char*>(kh))), 0, n * FD * 2,
+        0x00020000);
+    const int kq_off = (16 * w + c) * FD * 2 + 16 * g;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    auto buf = [&](int tt) { return smem + (tt % M_NBUF) * M_BUF_BYTES; };
+    // Start tile tt: its image goes straight from the workspace into ring buffer tt % 3 (wave
+    // w copies KiB chunks w, w+4, ..., no registers involved; every wave issues exactly
+    // M_WLOADS copies, the surplus ones repeating the last chunk, which rewrites the same
+    // bytes), its score operand (key 16w + c) into q0, q1.  Past the last tile the last one
+    // is re-read into a buffer nobody reads again, which keeps the loads in flight the same.
+    auto issue = [&](int tt, uint4& q0, uint4& q1) {
+        const int ts = min(tt, ntiles - 1);
+        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % M_NBUF) * M_BUF_BYTES);
+#pragma unroll
+        for (int e = 0; e < M_WLOADS; ++e) {
+            const int u = min(wu + B_WAVES * e, M_LOADS - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                img, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
+                16, voff[e], ts * PACK_TILE_BYTES, 0, 0);
+        }
+        q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off, ts * MT * FD * 2, 0));
+        q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off + 64, ts * MT * FD * 2, 0));
     };
-    fetch(0);
-    store_chunks(smem, x0, x1, x2, x3, nanc);
-    scores(kq0, kq1, smem, 0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
+    // Loads complete in order.  After tile t+1's image come 2 + M_WLOADS + 2 more loads (its
+    // score operand, tile t+2's image and score operand), so vmcnt <= that count means it has
+    // landed in LDS.  Encoding: vmcnt (4 bits), expcnt and lgkmcnt at their maxima (no wait).
+    static_assert(M_WLOADS + 4 < 16, "vmcnt operand is 4 bits here");
+    auto wait_tile = [] {
+        __builtin_amdgcn_s_waitcnt((M_WLOADS + 4) | (0x7 << 4) | (0xF << 8));
+        LDS_FENCE();
+    };
+    // Workgroup barrier of the ring: this wave's LDS stores are complete (lgkmcnt 0) and the
+    // copy of the next tile was waited for above; the loads still in flight (the tile two
+    // steps ahead) are deliberately not waited for, which __syncthreads() would do.
+    auto ring_barrier = [] {
+        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+        LDS_FENCE();
+        __builtin_amdgcn_s_barrier();
+        LDS_FENCE();
+    };
+    auto compute = [&](int t, const unsigned char* cur) {
         const int j0 = t * MT;
-        unsigned char* cur = smem + (t & 1) * M_BUF_BYTES;
-        unsigned char* nxt = smem + ((t + 1) & 1) * M_BUF_BYTES;
-        const bool more = t + 1 < ntiles;
-        fetch(more ? t + 1 : t);   // unconditional: the last iteration re-reads its own tile
         const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
         const _Float16* Vt = Kt + FD * M_LD;
         const _Float16* Sw = reinterpret_cast<const _Float16*>(cur + M_SW);
@@ -411,35 +478,56 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
             const half8 kw = *reinterpret_cast<const half8*>(Kt + ko);
             const half8 vw = *reinterpret_cast<const half8*>(Vt + ko);
             if (j0 + 32 * sub <= ic) {  // wave-uniform: keys of this query's prefix
-            const half8 sw = *reinterpret_cast<const half8*>(Sw + w * MT + 32 * sub + 8 * g);
-            half8 rk[4];
+                const half8 sw = *reinterpret_cast<const half8*>(Sw + w * MT + 32 * sub + 8 * g);
+                half8 rk[4];
 #pragma unroll
-            for (int fb = 0; fb < 4; ++fb) {
-                const half8 kf = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * M_LD + 32 * sub + 8 * g);
-                rk[fb] = kf * sw;
-            }
-            int idx = 0;
+                for (int fb = 0; fb < 4; ++fb) {
+                    const half8 kf = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * M_LD + 32 * sub + 8 * g);
+                    rk[fb] = kf * sw;
+                }
+                int idx = 0;
 #pragma unroll
-            for (int fb = 0; fb < 4; ++fb)
+                for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-                for (int fb2 = fb; fb2 < 4; ++fb2) { ckk[idx] = mfma_f16(rk[fb], rk[fb2], ckk[idx]); ++idx; }
+                    for (int fb2 = fb; fb2 < 4; ++fb2) { ckk[idx] = mfma_f16(rk[fb], rk[fb2], ckk[idx]); ++idx; }
 #pragma unroll
-            for (int fv = 0; fv < 4; ++fv) {
-                const half8 vf = *reinterpret_cast<const half8*>(Vt + (fv * 16 + c) * M_LD + 32 * sub + 8 * g);
-                const half8 rv = vf * sw;
+                for (int fv = 0; fv < 4; ++fv) {
+                    const half8 vf = *reinterpret_cast<const half8*>(Vt + (fv * 16 + c) * M_LD + 32 * sub + 8 * g);
+                    const half8 rv = vf * sw;
 #pragma unroll
-                for (int fb = 0; fb < 4; ++fb) cvk[fb * 4 + fv] = mfma_f16(rk[fb], rv, cvk[fb * 4 + fv]);
-            }
+                    for (int fb = 0; fb < 4; ++fb) cvk[fb * 4 + fv] = mfma_f16(rk[fb], rv, cvk[fb * 4 + fv]);
+                }
             }
             sk = mfma_f16(w8, kw, sk);
             sv = mfma_f16(w8, vw, sv);
         }
-        if (more) {
-            store_chunks(nxt, x0, x1, x2, x3, nanc);
-            scores(kq0, kq1, nxt, j0 + MT);
-        }
-        __syncthreads();
+    };
+    uint4 aq0, aq1, bq0, bq1;
+    issue(0, aq0, aq1);
+    issue(1, bq0, bq1);
+    wait_tile();
+    scores(aq0, aq1, buf(0), 0);
+    ring_barrier();
+    for (int t = 0; t < ntiles; t += 2) {
+        // step t: tile t in LDS, tile t+1 landing (operand in B), tile t+2 issued now (A)
+        issue(t + 2, aq0, aq1);
+        compute(t, buf(t));
+        if (t + 1 < ntiles) scores(bq0, bq1, buf(t + 1), (t + 1) * MT);
+        wait_tile();
+        ring_barrier();
+        if (t + 1 >= ntiles) break;
+        // step t+1: the same with the register sets swapped
+        issue(t + 3, bq0, bq1);
+        compute(t + 1, buf(t + 1));
+        if (t + 2 < ntiles) scores(aq0, aq1, buf(t + 2), (t + 2) * MT);
+        wait_tile();
+        ring_barrier();
     }
+
+    // Copies issued past the last tile may still be landing in ring buffers that the solve
+    // area overlaps: wait for all of this wave's loads (the barrier below covers the others).
+    __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
+    LDS_FENCE();
 
     // ---- block sums -> LDS (outside the solve area): row r of sk / sv is query r.
     float* means = reinterpret_cast<float*>(smem + B_MEAN_OFF);
@@ -743,14 +831,18 @@ int fast_row0(int64_t n, int64_t d) { return static_cast<int>(n < 2 * d ? n : 2 
 
 }  // namespace
 
-bool fast_supports(int dtype, int64_t d) { return dtype == 1 && d == FD; }
+bool fast_supports(int dtype, int64_t d, int64_t n) {
+    // Buffer resources address a head's keys and tile images with 32-bit byte offsets.
+    return dtype == 1 && d == FD && n <= kFastMaxN;
+}
 
 size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
     const int64_t rows = n - fast_row0(n, d);
     if (rows <= 0) return 0;
     const int64_t stats = B * H * rows * SROW * static_cast<int64_t>(sizeof(float));
-    const int64_t tiles = B * H * ((n + MT - 1) / MT) * PACK_TILE_HALVES * 2;
-    return static_cast<size_t>(stats + tiles);
+    const int64_t anchors = B * H * ANCHOR_SLICES * 2 * d * static_cast<int64_t>(sizeof(float));
+    const int64_t tiles = B * H * ((n + MT - 1) / MT) * PACK_TILE_BYTES;
+    return static_cast<size_t>(stats + anchors + tiles);
 }
 
 hipError_t launch_fast(const Problem& p, void* workspace) {
@@ -779,12 +871,18 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     const auto* q = static_cast<const uint16_t*>(p.q);
     const auto* k = static_cast<const uint16_t*>(p.k);
     const auto* v = static_cast<const uint16_t*>(p.v);
+    // Workspace: stats rows | per-head anchor partial sums | tile images (16-byte aligned:
+    // every region size is a multiple of 16 bytes).
     float* stats = static_cast<float*>(workspace);
+    float* partial = stats + static_cast<int64_t>(BH) * nrows * SROW;
+    unsigned char* packed = reinterpret_cast<unsigned char*>(partial + static_cast<int64_t>(BH) * ANCHOR_SLICES * 2 * FD);
     const int ptiles = (n + MT - 1) / MT;
-    uint16_t* packed = reinterpret_cast<uint16_t*>(
-        static_cast<unsigned char*>(workspace) + static_cast<int64_t>(BH) * nrows * SROW * sizeof(float));
+    prof_begin(p.stream, "lla_anchor_kernel");
+    lla_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * ANCHOR_SLICES), dim3(256), 0, p.stream>>>(k, v, partial, n);
+    prof_end(p.stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla_pack_kernel");
-    lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(k, v, packed, n, ptiles);
+    lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(k, v, partial, packed, n, ptiles);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 

@@ -23,8 +23,10 @@ struct Problem {
 hipError_t launch_exact(const Problem& p, int rows);
 
 // Matrix-core path for bf16 inputs: rows i < 2d on the fp64 kernel, the rest on MFMA
-// kernels that keep per-row statistics in `workspace` (fast_workspace_bytes of it).
-bool fast_supports(int dtype, int64_t d);
+// kernels that keep per-row statistics and packed key/value tiles in `workspace`
+// (fast_workspace_bytes of it).  Serves d = 64 and n up to kFastMaxN.
+constexpr int64_t kFastMaxN = int64_t(1) << 22;
+bool fast_supports(int dtype, int64_t d, int64_t n);
 size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
 hipError_t launch_fast(const Problem& p, void* workspace);
 

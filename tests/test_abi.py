@@ -117,11 +117,16 @@ def test_path_availability_query():
 
 def test_workspace_size():
     from local_linear_attention_amd import lla
-    # fast path: 4*(2d+4) bytes for every row at or beyond 2d, then fp16 K/V tiles of 64 keys
-    expect = 2 * 16 * (4096 - 128) * 132 * 4 + 2 * 16 * 64 * (2 * 2 * 64 * 64)
+    # fast path, per head: 4*(2d+4) bytes for every row at or beyond 2d, 16*2d floats of
+    # anchor partial sums, then fp16 K/V tiles of 64 keys with 72-half rows
+    tile = 2 * 64 * 72 * 2
+    expect = 2 * 16 * ((4096 - 128) * 132 * 4 + 16 * 128 * 4 + 64 * tile)
     assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "fast") == expect
     assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "auto") == expect
-    assert lla.lla_workspace_size(1, 1, 130, 64, "bf16", "fast") == 2 * 132 * 4 + 3 * 2 * 2 * 64 * 64
+    assert lla.lla_workspace_size(1, 1, 130, 64, "bf16", "fast") == 2 * 132 * 4 + 16 * 128 * 4 + 3 * tile
+    # beyond the fast path's sequence limit AUTO falls back to the exact path (no scratch)
+    assert lla.lla_workspace_size(1, 1, (1 << 22) + 1, 64, "bf16", "fast") == 0
+    assert lla.lla_workspace_size(1, 1, (1 << 22) + 1, 64, "bf16", "auto") == 0
     assert lla.lla_workspace_size(1, 1, 100, 64, "bf16", "fast") == 0      # every row is short
     assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "exact") == 0
     assert lla.lla_workspace_size(2, 16, 4096, 64, "f32", "auto") == 0

@@ -85,7 +85,8 @@ def test_fast_path_workspace_entry_point_matches():
     tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
     nbytes = lla_workspace_size(w.B, w.H, w.n, w.d, "bf16", "fast")
     ntiles = -(-w.n // 64)
-    assert nbytes == w.B * w.H * ((w.n - 2 * w.d) * (2 * w.d + 4) * 4 + ntiles * 2 * 2 * w.d * 64)
+    assert nbytes == w.B * w.H * ((w.n - 2 * w.d) * (2 * w.d + 4) * 4 + 16 * 2 * w.d * 4
+                                  + ntiles * 2 * w.d * 72 * 2)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a = lla_forward_ws(tq, tk, tv, w.h, w.lam, ws, path="fast")
     b = lla_forward_ex(tq, tk, tv, w.h, w.lam, path="fast")
@@ -108,7 +109,7 @@ def test_profiling_records_each_kernel():
         rec = lla_profile_collect()
     finally:
         lla_profile_enable(False)
-    assert [name for name, _ in rec] == ["lla_short_kernel", "lla_pack_kernel",
+    assert [name for name, _ in rec] == ["lla_short_kernel", "lla_anchor_kernel", "lla_pack_kernel",
                                          "lla_stats_kernel", "lla_moments_kernel"]
     assert all(ms > 0 for _, ms in rec)
 
