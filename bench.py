@@ -50,7 +50,7 @@ PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d: f64
 KERNEL_BOUND = {
     "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_short_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
-    "lla_stats_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_rowmax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_anchor_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_moments_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
@@ -65,8 +65,9 @@ def pair_count(BH, lo, hi):
 def kernel_flops(name, B, H, n, d, path):
     """Algorithmic flops (formulation NS, the one both paths execute) of one launch of a
     kernel: the fast path splits the rows at 2d between an fp64 kernel (short rows) and the
-    MFMA kernels; the stats kernel owns the score and first-moment terms of its rows, the
-    moments kernel the second moments, the solve and the assembly."""
+    MFMA kernels; the row-max kernel owns the score term of its rows, the moments kernel the
+    first and second moments, the solve and the assembly (scores it recomputes are not
+    counted again)."""
     BH = B * H
     row0 = min(n, 2 * d) if path == "fast" else n
     per_query = d ** 3 / 3 + 4 * d * d + 2 * d
@@ -75,10 +76,11 @@ def kernel_flops(name, B, H, n, d, path):
             + BH * row0 * per_query
     if name in ("lla_anchor_kernel", "lla_pack_kernel"):
         return 0                      # data movement only (K, V summed and repacked once)
-    if name == "lla_stats_kernel":
-        return pair_count(BH, row0, n) * (2 * d + 2 * (1 + 2 * d))
+    if name == "lla_rowmax_kernel":
+        return pair_count(BH, row0, n) * 2 * d
     if name == "lla_moments_kernel":
-        return pair_count(BH, row0, n) * (d * (d + 1) + 2 * d * d) + BH * (n - row0) * per_query
+        return pair_count(BH, row0, n) * (2 * (1 + 2 * d) + d * (d + 1) + 2 * d * d) \
+            + BH * (n - row0) * per_query
     raise KeyError(name)
 
 

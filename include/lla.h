@@ -99,10 +99,11 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
                             lla_dtype_t dtype, void* stream, lla_path_t path);
 
 /* Bytes of device scratch that `path` needs for this problem (0 if none, or if the sizes,
- * dtype or path are invalid).  Per head, the fast path keeps there: per-row statistics,
- * 4*(2d+4) bytes for every row at or beyond position 2d; 16*2d floats of partial key/value
- * sums (the head's centring anchor); K and V repacked as fp16 tiles of 64 keys, each
- * 2*d*72*2 bytes (feature-major rows of 64 keys plus 8 halves of padding).  Nothing when
+ * dtype or path are invalid).  The fast path keeps there, in regions each rounded up to a
+ * multiple of 256 bytes: one float per row at or beyond position 2d (its score maximum);
+ * 16*2d floats per head of partial key/value sums and 2d floats per head of the centring
+ * anchor; then, per head and tile of 64 keys, K and V as fp16 (2*d*72*2 bytes: feature-major
+ * rows of 64 keys plus 8 halves of padding) and K key-major (64*72*2 bytes).  Nothing when
  * n <= 2d.  The fast path serves n up to 4194304 (2^22); AUTO uses the exact path beyond. */
 size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                           lla_path_t path);

@@ -4,24 +4,26 @@
 //   * rows i < 2d run on the fp64 kernel: their prefixes hold at most 2d keys, so C_kk is
 //     rank-deficient or barely full rank and the ridge lambda e^{-m} alone conditions the
 //     solve -- the normal-equation form then needs more than fp16/fp32 precision;
-//   * rows i >= 2d run here, in two kernels:
-//       lla_stats_kernel    score pass with a running max (FlashAttention-style online
-//                           softmax): m_i, omega_i, kbar_i, vbar_i -> workspace;
-//       lla_moments_kernel  per query, the centred weighted second moments
-//                           C_kk = R_k^T R_k and C_vk^T = R_k^T R_v with
-//                           R_k[j] = sqrt(wt_ij) (k_j - kbar_i), R_v[j] = sqrt(wt_ij) (v_j - vbar_i)
-//                           rounded once to fp16 (the same rounded R_k on both sides keeps the
-//                           two moments consistent), accumulated in fp32 by MFMA; then the
+//   * rows i >= 2d run here:
+//       lla_anchor_kernel   per-head sums of the keys and values (the centring anchor a);
+//       lla_pack_kernel     K, V once into fp16 tiles centred at a (the LDS image the
+//                           moments kernel copies) and K key-major for the score pass;
+//       lla_rowmax_kernel   score pass with a running max: m_i;
+//       lla_moments_kernel  per query, with sw_ij = sqrt(e^{s_ij - m_i}) rounded to fp16,
+//                           R_k[j] = sw (k_j - a_k), R_v[j] = sw (v_j - a_v) (fp16), the
+//                           moments R_k^T R_k and R_k^T R_v on MFMA (fp32 accumulation), the
+//                           block sums S = sum_j sw^2 (x_j - a) and omega' = sum_j sw^2, the
+//                           rank-one downdate to the centred C_kk, C_vk, the means
+//                           kbar = a_k + S_k / omega', vbar = a_v + S_v / omega'; then the
 //                           ridge-rescaled SPD solve (C_kk + lambda e^{-m} I) y = kbar - q by
 //                           LDL^T elimination in one wave, and b = vbar - C_vk y.
 // The estimator, its moments and the centred form follow the "Parallax" blog post, section 2
 // "Canonical Formulation" and Appendix E; the max shift is the safe softmax of the arXiv
-// page's scoring-form paragraph, with the ridge scaled by the same e^{-m}.
+// page's scoring-form paragraph, with the ridge scaled by the same e^{-m}.  The normalisation
+// by omega cancels in b, so unnormalised shifted weights serve throughout.
 //
 // MFMA: v_mfma_f32_16x16x32_{bf16,f16}.  Lane l supplies row/column (l % 16) of A/B and 8
 // consecutive K-slots (l / 16); D[4 (l/16) + r][l % 16] lands in accumulator register r.
-// Any permutation of the K-slots that A and B share leaves the product unchanged, which the
-// stats kernel uses to feed the score tile straight back as the P operand.
 #include "lla_internal.h"
 
 #include <math.h>
@@ -38,16 +40,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int FD = 64;              // head dimension of this path
-constexpr int SROW = 2 * FD + 4;    // workspace row: kbar[FD], vbar[FD], m, omega, 2 pad
-constexpr int KT = 32;              // keys per tile
-constexpr int KK_LD = FD + 8;       // key-major bf16 tile row (elements), 144 B
-constexpr int XA_LD = KT + 4;       // feature-major f16 row in the stats kernel, 72 B
-constexpr int XB_LD = KT + 8;       // feature-major f16 row in the moments kernel, 80 B
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
 
-constexpr int A_WAVES = 4, A_QW = 16, A_QB = A_WAVES * A_QW;  // stats: 64 queries / block
-constexpr int B_WAVES = 4;                                     // moments: 1 query per wave
+constexpr int B_WAVES = 4;          // waves per block of the row-max and moments kernels
 
 // Compiler fence for wave-private LDS exchanges: a lane reads words that other lanes of
 // the same wave stored, so no LDS access may move across a publish/consume boundary.
@@ -78,137 +73,6 @@ __device__ __forceinline__ float4v mfma_bf16(bf16x8 a, bf16x8 b, float4v c) {
 }
 __device__ __forceinline__ float4v mfma_f16(half8 a, half8 b, float4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// Stage one tile of KT keys: 256 threads, thread -> key jj = tid / 8, features f0..f0+7.
-// Keys at or past n are zero.  kk (if non-null) receives the bf16 keys key-major; kt and vt
-// receive keys and values feature-major as fp16 (exact for bf16 values in fp16 range).
-template <int XLD>
-__device__ __forceinline__ void stage_tile(const uint16_t* __restrict__ kh,
-                                           const uint16_t* __restrict__ vh, int n, int j0,
-                                           uint16_t* kk, _Float16* kt, _Float16* vt) {
-    const int tid = threadIdx.x;
-    const int jj = tid >> 3, f0 = (tid & 7) * 8;
-    const int j = j0 + jj;
-    uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-    if (j < n) {
-        kr = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(j) * FD + f0);
-        vr = *reinterpret_cast<const uint4*>(vh + static_cast<int64_t>(j) * FD + f0);
-    }
-    if (kk) *reinterpret_cast<uint4*>(kk + jj * KK_LD + f0) = kr;
-    const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
-    const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t kb = (kw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t vb = (vw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        kt[(f0 + e) * XLD + jj] = static_cast<_Float16>(bf16_bits_to_f32(kb));
-        vt[(f0 + e) * XLD + jj] = static_cast<_Float16>(bf16_bits_to_f32(vb));
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// Score pass: per query, running max m, omega = sum exp(s - m), kbar, vbar.
-// Block = 4 waves x 16 queries; tiles of 32 keys shared through LDS.
-__global__ __launch_bounds__(256) void lla_stats_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, float* __restrict__ stats, int n, int row0, int BH,
-    float sl2) {
-    __shared__ __attribute__((aligned(16))) uint16_t Kk[KT * KK_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 Xt[2 * FD * XA_LD];
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int g = lane >> 4, c = lane & 15;
-    const int nrows = n - row0;
-    const int nblk = (nrows + A_QB - 1) / A_QB;
-    const int blk = nblk - 1 - static_cast<int>(blockIdx.x / BH);  // longest rows first
-    const int bh = static_cast<int>(blockIdx.x % BH);
-    const int q0 = row0 + blk * A_QB;
-    const int qlast = min(q0 + A_QB, n) - 1;
-    const int64_t base = static_cast<int64_t>(bh) * n * FD;
-    const uint16_t* kh = k + base;
-    const uint16_t* vh = v + base;
-
-    const int qi = q0 + w * A_QW + c;     // this lane's query (column c)
-    const int qc = min(qi, n - 1);
-    const int wave_last = min(q0 + w * A_QW + A_QW - 1, n - 1);
-    bf16x8 qf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                                q + base + static_cast<int64_t>(qc) * FD + ks * 32 + 8 * g));
-
-    float m_run = -INFINITY, l_run = 0.0f;
-    float4v o[8];
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) o[mb] = float4v{0.f, 0.f, 0.f, 0.f};
-
-    const int ntiles = (qlast + KT) / KT;
-    for (int t = 0; t < ntiles; ++t) {
-        const int j0 = t * KT;
-        __syncthreads();
-        stage_tile<XA_LD>(kh, vh, n, j0, Kk, Xt, Xt + FD * XA_LD);
-        __syncthreads();
-        if (j0 > wave_last) continue;  // wave-uniform: no key of this tile is in any prefix
-
-        // S^T blocks: lane holds keys j0 + kb*16 + 4g + r for query qi.
-        float x[8];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            float4v s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const uint4*>(Kk + (kb * 16 + c) * KK_LD + ks * 32 + 8 * g));
-                s = mfma_bf16(a, qf[ks], s);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = j0 + kb * 16 + 4 * g + r;
-                const float val = (j <= qc) ? s[r] * sl2 : -INFINITY;
-                x[kb * 4 + r] = val;
-                tmax = fmaxf(tmax, val);
-            }
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);   // finite: key 0 is in every prefix
-        const float alpha = exp2f(m_run - m_new);
-        float psum = 0.0f;
-        half8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pe = exp2f(x[e] - m_new);
-            psum += pe;
-            pb[e] = static_cast<_Float16>(pe);
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        // O^T[f][query] += X^T[f][keys] P^T[keys][query], K-slots = keys {4g..4g+3, 16+4g..}.
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-            o[mb] *= alpha;
-            const _Float16* row = Xt + (mb * 16 + c) * XA_LD;
-            const half4 lo = *reinterpret_cast<const half4*>(row + 4 * g);
-            const half4 hi = *reinterpret_cast<const half4*>(row + 16 + 4 * g);
-            const half8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[mb] = mfma_f16(a, pb, o[mb]);
-        }
-    }
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (qi < n) {
-        float* srow = stats + (static_cast<int64_t>(bh) * nrows + (qi - row0)) * SROW;
-        const float inv = 1.0f / l_tot;
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-            *reinterpret_cast<float4v*>(srow + mb * 16 + 4 * g) = o[mb] * inv;
-        if (g == 0) {
-            srow[2 * FD] = m_run * LN2;   // back to natural units of q.k/h
-            srow[2 * FD + 1] = l_tot;
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -244,6 +108,14 @@ constexpr int B_MEAN_FLOATS = 2 * FD + B_WAVES;          // per query: S_k, S_v,
 constexpr int B_MEAN_OFF = B_SOLVE_BYTES > M_NBUF * M_BUF_BYTES ? B_SOLVE_BYTES : M_NBUF * M_BUF_BYTES;
 constexpr int B_SMEM = B_MEAN_OFF + B_WAVES * B_MEAN_FLOATS * 4;
 constexpr int ANCHOR_SLICES = 16;        // key slices of the per-head anchor sums
+// Keys of one tile key-major (bf16 as given, rows of KM_LD halves: 64 features + 8 of
+// padding), the score operand of the row-max kernel, 9 KiB per tile.
+constexpr int KM_LD = FD + 8;
+constexpr int KM_TILE_BYTES = MT * KM_LD * 2;
+constexpr int KM_LOADS = KM_TILE_BYTES / 1024;
+constexpr int KM_WLOADS = (KM_LOADS + B_WAVES - 1) / B_WAVES;
+constexpr int R_QW = 16, R_QB = B_WAVES * R_QW;  // row-max: 16 queries per wave, 64 per block
+static_assert(KM_TILE_BYTES % 1024 == 0, "key image must be whole wave copies");
 static_assert(PACK_TILE_BYTES % 1024 == 0, "tile image must be whole wave copies");
 
 // Block b -> (head bh, row block blk).  Work-groups go round-robin to the 8 XCDs, so
@@ -284,10 +156,14 @@ __global__ __launch_bounds__(256) void lla_anchor_kernel(const uint16_t* __restr
 // Pack K and V once into the LDS image of each tile (zero past n), centred at the head's
 // anchor a = fp16(mean over all keys of k, of v): stored value fp16(x - a), one rounding.
 // Thread -> keys 2p, 2p+1 and features 8fg .. 8fg+7; every store writes a pair of keys.
+// The same block also writes the tile's keys key-major (bf16, unchanged) for the row-max
+// kernel, and block 0 of each head the head's anchor (fp16 values as floats).
 __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
                                                        const float* __restrict__ partial,
-                                                       unsigned char* __restrict__ packed, int n,
+                                                       float* __restrict__ anchors,
+                                                       unsigned char* __restrict__ packed,
+                                                       unsigned char* __restrict__ kimg, int n,
                                                        int ntiles) {
     __shared__ float anc[2 * FD];
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
@@ -297,6 +173,7 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
         for (int sl = 0; sl < ANCHOR_SLICES; ++sl)
             sum += partial[(static_cast<int64_t>(bh) * ANCHOR_SLICES + sl) * 2 * FD + tid];
         anc[tid] = static_cast<float>(static_cast<_Float16>(sum / static_cast<float>(n)));
+        if (t == 0) anchors[static_cast<int64_t>(bh) * 2 * FD + tid] = anc[tid];
     }
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
     const int ja = t * MT + 2 * pr, jb = ja + 1;
@@ -308,6 +185,15 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
     if (jb < n) {
         k1 = *reinterpret_cast<const uint4*>(k + base + static_cast<int64_t>(jb) * FD + 8 * fg);
         v1 = *reinterpret_cast<const uint4*>(v + base + static_cast<int64_t>(jb) * FD + 8 * fg);
+    }
+    {   // key-major image: key 2p (and 2p+1), features 8fg .. 8fg+7; row padding zero
+        unsigned char* kt = kimg + (static_cast<int64_t>(bh) * ntiles + t) * KM_TILE_BYTES;
+        *reinterpret_cast<uint4*>(kt + (2 * pr) * (KM_LD * 2) + 16 * fg) = k0;
+        *reinterpret_cast<uint4*>(kt + (2 * pr + 1) * (KM_LD * 2) + 16 * fg) = k1;
+        if (fg == 0) {
+            *reinterpret_cast<uint4*>(kt + (2 * pr) * (KM_LD * 2) + 2 * FD) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(kt + (2 * pr + 1) * (KM_LD * 2) + 2 * FD) = make_uint4(0, 0, 0, 0);
+        }
     }
     __syncthreads();
     uint32_t* dst = reinterpret_cast<uint32_t*>(packed + (static_cast<int64_t>(bh) * ntiles + t) * PACK_TILE_BYTES);
@@ -334,10 +220,106 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
     }
 }
 
+// Score pass with a running max (rows i >= 2d): m_i = max_{j <= i} q_i.k_j / h, in log2
+// units.  Block = 4 waves x 16 queries; 64-key tiles of the key-major image stream through
+// a ring of three LDS buffers (copied straight from the workspace); scores on MFMA (bf16):
+// S^T block kb of a tile, lane (g, c) register r = key 16 kb + 4g + r, query c.
+__global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restrict__ q,
+                                                         const unsigned char* __restrict__ kimg,
+                                                         float* __restrict__ mrow, int n, int row0,
+                                                         int BH, float sl2) {
+    __shared__ __attribute__((aligned(16))) unsigned char ring[3 * KM_TILE_BYTES];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int g = lane >> 4, c = lane & 15;
+    const int nrows = n - row0;
+    const int nblk = (nrows + R_QB - 1) / R_QB;
+    int blk, bh;
+    head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
+    const int q0 = row0 + blk * R_QB;
+    const int qlast = min(q0 + R_QB, n) - 1;
+    const int qi = q0 + w * R_QW + c;   // this lane's query (column c)
+    const int qc = min(qi, n - 1);
+    const int wave_first = q0 + w * R_QW;
+    const int wave_last = min(wave_first + R_QW - 1, n - 1);
+    const int64_t base = static_cast<int64_t>(bh) * n * FD;
+    bf16x8 qf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                q + base + static_cast<int64_t>(qc) * FD + ks * 32 + 8 * g));
+
+    const int ntiles = (qlast + MT) / MT;
+    const int ptiles = (n + MT - 1) / MT;
+    const __amdgpu_buffer_rsrc_t img = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(kimg + static_cast<int64_t>(bh) * ptiles * KM_TILE_BYTES)), 0,
+        ptiles * KM_TILE_BYTES, 0x00020000);
+    int voff[KM_WLOADS];
+#pragma unroll
+    for (int e = 0; e < KM_WLOADS; ++e) voff[e] = lane * 16 + min(wu + B_WAVES * e, KM_LOADS - 1) * 1024;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+    // Tile tt -> ring buffer tt % 3; every wave issues KM_WLOADS copies (surplus ones repeat
+    // the last chunk); past the last tile the last one is re-read into a dead buffer.
+    auto issue = [&](int tt) {
+        const int ts = min(tt, ntiles - 1);
+        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % 3) * KM_TILE_BYTES);
+#pragma unroll
+        for (int e = 0; e < KM_WLOADS; ++e) {
+            const int u = min(wu + B_WAVES * e, KM_LOADS - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                img, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
+                16, voff[e], ts * KM_TILE_BYTES, 0, 0);
+        }
+    };
+    // Only tile copies are in flight in the loop: after tile t+1's come tile t+2's
+    // KM_WLOADS, so vmcnt <= KM_WLOADS means tile t+1 has landed.
+    auto next_tile = [] {
+        __builtin_amdgcn_s_waitcnt(KM_WLOADS | (0x7 << 4) | (0xF << 8));
+        LDS_FENCE();
+        __builtin_amdgcn_s_barrier();
+        LDS_FENCE();
+    };
+
+    float m_run = -INFINITY;
+    issue(0);
+    issue(1);
+    next_tile();
+    for (int t = 0; t < ntiles; ++t) {
+        issue(t + 2);
+        const int j0 = t * MT;
+        if (j0 <= wave_last) {   // wave-uniform: some key of the tile is in a prefix
+            const unsigned char* cur = ring + (t % 3) * KM_TILE_BYTES;
+            const bool full = j0 + MT - 1 <= wave_first;   // every key below every query
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                float4v s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const uint4*>(cur + (kb * 16 + c) * (KM_LD * 2) + ks * 64 + 16 * g));
+                    s = mfma_bf16(a, qf[ks], s);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = j0 + kb * 16 + 4 * g + r;
+                    m_run = fmaxf(m_run, (full || j <= qc) ? s[r] : -INFINITY);
+                }
+            }
+        }
+        next_tile();
+    }
+    // Copies past the last tile are still landing in LDS: let them finish before exit.
+    __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
+    m_run = fmaxf(m_run, __shfl_xor(m_run, 16));
+    m_run = fmaxf(m_run, __shfl_xor(m_run, 32));
+    if (g == 0 && qi < n) mrow[static_cast<int64_t>(bh) * nrows + (qi - row0)] = m_run * sl2;
+}
+
 __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ stats,
-    const unsigned char* __restrict__ packed, float* __restrict__ out,
+    const uint16_t* __restrict__ v, const float* __restrict__ mrow,
+    const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
+    float* __restrict__ out,
     int n, int row0, int BH, float sl2, float lambda) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -356,7 +338,6 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const int last = min(i0 + B_WAVES - 1, n - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
     const uint16_t* kh = k + base;
-    const float* st = stats + (static_cast<int64_t>(bh) * nrows + (ic - row0)) * SROW;
 
     // Rows B_WAVES.. of every Sw2 buffer are the zero rows of the weight operand.
     for (int e = tid; e < M_NBUF * (16 - B_WAVES) * MT / 8; e += 256) {
@@ -367,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     // Score operand: column c < B_WAVES is query i0 + c (the other columns are zero).
     const int qcol = min(i0 + c, n - 1);
     const bool colv = c < B_WAVES;
-    const float mcol = stats[(static_cast<int64_t>(bh) * nrows + (qcol - row0)) * SROW + 2 * FD] * LOG2E;
+    const float mcol = mrow[static_cast<int64_t>(bh) * nrows + (qcol - row0)];   // log2 units
     bf16x8 qf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -585,7 +566,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) cvk[fb * 4 + fv][r] = fmaf(-skr[fb][r], svc[fv], cvk[fb * 4 + fv][r]);
     LDS_FENCE();
-    const float m_x = st[2 * FD] * LOG2E;
+    const float m_x = mrow[static_cast<int64_t>(bh) * nrows + (ic - row0)];
     const float lam_s = lambda * exp2f(-m_x);
     A[lane * ALD + lane] += lam_s;
     LDS_FENCE();
@@ -608,7 +589,9 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     // The accumulators must really leave the registers: no store-to-load forwarding.
     LDS_FENCE();
     const float qa = bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]);
-    float z = st[lane] - qa;
+    // kbar = a_k + S_k / omega' (the weighted mean of the centred keys, same weights as C)
+    const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD;
+    float z = fmaf(mq[lane], iom2, anc[lane]) - qa;
 
     // Forward elimination (symmetric, no pivoting): after step p, lane p's registers hold row
     // p of U = D L^T and z holds L^{-1} (kbar - q).  Column p of the trailing matrix equals
@@ -661,7 +644,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     if (valid && g == 0) {
         float* orow = out + base + static_cast<int64_t>(i) * FD;
 #pragma unroll
-        for (int fv = 0; fv < 4; ++fv) orow[fv * 16 + c] = st[FD + fv * 16 + c] - part[fv];
+        for (int fv = 0; fv < 4; ++fv) orow[fv * 16 + c] = fmaf(svc[fv], iom2, anc[FD + fv * 16 + c]) - part[fv];
     }
 }
 
@@ -829,6 +812,26 @@ __global__ __launch_bounds__(256) void lla_short_kernel(
 
 int fast_row0(int64_t n, int64_t d) { return static_cast<int>(n < 2 * d ? n : 2 * d); }
 
+// Fast-path workspace, each region 256-byte aligned:
+//   row maxima [B*H][n - 2d] | anchor partial sums [B*H][16][2d] | anchors [B*H][2d] |
+//   key/value tile images [B*H][tiles] | key-major key images [B*H][tiles].
+struct FastLayout {
+    int64_t mrow, partial, anchors, packed, kimg, total;
+};
+
+FastLayout fast_layout(int64_t BH, int64_t n, int64_t d) {
+    auto up = [](int64_t bytes) { return (bytes + 255) & ~int64_t(255); };
+    const int64_t rows = n - fast_row0(n, d), tiles = (n + MT - 1) / MT;
+    FastLayout L;
+    L.mrow = 0;
+    L.partial = L.mrow + up(BH * rows * 4);
+    L.anchors = L.partial + up(BH * ANCHOR_SLICES * 2 * d * 4);
+    L.packed = L.anchors + up(BH * 2 * d * 4);
+    L.kimg = L.packed + BH * tiles * PACK_TILE_BYTES;
+    L.total = L.kimg + BH * tiles * KM_TILE_BYTES;
+    return L;
+}
+
 }  // namespace
 
 bool fast_supports(int dtype, int64_t d, int64_t n) {
@@ -837,12 +840,8 @@ bool fast_supports(int dtype, int64_t d, int64_t n) {
 }
 
 size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
-    const int64_t rows = n - fast_row0(n, d);
-    if (rows <= 0) return 0;
-    const int64_t stats = B * H * rows * SROW * static_cast<int64_t>(sizeof(float));
-    const int64_t anchors = B * H * ANCHOR_SLICES * 2 * d * static_cast<int64_t>(sizeof(float));
-    const int64_t tiles = B * H * ((n + MT - 1) / MT) * PACK_TILE_BYTES;
-    return static_cast<size_t>(stats + anchors + tiles);
+    if (n - fast_row0(n, d) <= 0) return 0;
+    return static_cast<size_t>(fast_layout(B * H, n, d).total);
 }
 
 hipError_t launch_fast(const Problem& p, void* workspace) {
@@ -871,31 +870,34 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     const auto* q = static_cast<const uint16_t*>(p.q);
     const auto* k = static_cast<const uint16_t*>(p.k);
     const auto* v = static_cast<const uint16_t*>(p.v);
-    // Workspace: stats rows | per-head anchor partial sums | tile images (16-byte aligned:
-    // every region size is a multiple of 16 bytes).
-    float* stats = static_cast<float*>(workspace);
-    float* partial = stats + static_cast<int64_t>(BH) * nrows * SROW;
-    unsigned char* packed = reinterpret_cast<unsigned char*>(partial + static_cast<int64_t>(BH) * ANCHOR_SLICES * 2 * FD);
+    const FastLayout L = fast_layout(BH, n, p.d);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* mrow = reinterpret_cast<float*>(ws + L.mrow);
+    float* partial = reinterpret_cast<float*>(ws + L.partial);
+    float* anchors = reinterpret_cast<float*>(ws + L.anchors);
+    unsigned char* packed = ws + L.packed;
+    unsigned char* kimg = ws + L.kimg;
     const int ptiles = (n + MT - 1) / MT;
     prof_begin(p.stream, "lla_anchor_kernel");
     lla_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * ANCHOR_SLICES), dim3(256), 0, p.stream>>>(k, v, partial, n);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla_pack_kernel");
-    lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(k, v, partial, packed, n, ptiles);
+    lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(
+        k, v, partial, anchors, packed, kimg, n, ptiles);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
-    const unsigned blocks_a = static_cast<unsigned>(BH) * ((nrows + A_QB - 1) / A_QB);
-    prof_begin(p.stream, "lla_stats_kernel");
-    lla_stats_kernel<<<dim3(blocks_a), dim3(256), 0, p.stream>>>(q, k, v, stats, n, row0, BH, sl2);
+    const unsigned blocks_a = static_cast<unsigned>(BH) * ((nrows + R_QB - 1) / R_QB);
+    prof_begin(p.stream, "lla_rowmax_kernel");
+    lla_rowmax_kernel<<<dim3(blocks_a), dim3(256), 0, p.stream>>>(q, kimg, mrow, n, row0, BH, sl2);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     const unsigned blocks_b = static_cast<unsigned>(BH) * ((nrows + B_WAVES - 1) / B_WAVES);
     prof_begin(p.stream, "lla_moments_kernel");
     lla_moments_kernel<<<dim3(blocks_b), dim3(256), B_SMEM, p.stream>>>(
-        q, k, v, stats, packed, p.out, n, row0, BH, sl2, static_cast<float>(p.lambda));
+        q, k, v, mrow, anchors, packed, p.out, n, row0, BH, sl2, static_cast<float>(p.lambda));
     prof_end(p.stream);
     return hipGetLastError();
 }
