@@ -102,7 +102,7 @@ constexpr int M_NBUF = 3;                // tile ring: compute t, t+1 landing, t
 constexpr int M_SW = PACK_TILE_BYTES;    // byte offset of Sw: sqrt-weights, [query][key]
 constexpr int M_SW2 = M_SW + B_WAVES * MT * 2;  // Sw2: fp16 weights, 16 rows (rows >= 4 zero)
 constexpr int M_BUF_BYTES = M_SW2 + 16 * MT * 2;
-constexpr int B_SOLVE_FLOATS = FD * (FD + 1) + 2 * FD;  // A (padded rows) + pivot column + y
+constexpr int B_SOLVE_FLOATS = FD * (FD + 1) + 2 * FD;  // L (padded rows) + pivots + y
 constexpr int B_SOLVE_BYTES = B_SOLVE_FLOATS * 4 * B_WAVES;
 constexpr int B_MEAN_FLOATS = 2 * FD + B_WAVES;          // per query: S_k, S_v, omega' parts
 constexpr int B_MEAN_OFF = B_SOLVE_BYTES > M_NBUF * M_BUF_BYTES ? B_SOLVE_BYTES : M_NBUF * M_BUF_BYTES;
@@ -529,11 +529,15 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     for (int t = 0; t < B_WAVES; ++t) om2 += mq[2 * FD + t];
     const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
 
-    // ---- ridge-rescaled SPD solve, lane a owns row a (the solve area aliases the tiles)
+    // ---- ridge-rescaled SPD solve: blocked LDL^T in 16-column panels.  Each panel is
+    // eliminated lane-per-row (lane a holds the panel part of row a, pivot rows broadcast by
+    // readlane); its multipliers L go to LDS; the trailing blocks of C_kk, still in the MFMA
+    // accumulators, take the update L D L^T on the matrix cores (fp32).  The LDS area holds
+    // Lt[P][a] = L[a][P] (also used to stage each panel), the pivots and y.
     constexpr int ALD = FD + 1;
-    float* A = reinterpret_cast<float*>(smem) + w * B_SOLVE_FLOATS;
-    float* colb = A + FD * ALD;
-    float* yv = colb + FD;
+    float* Lt = reinterpret_cast<float*>(smem) + w * B_SOLVE_FLOATS;
+    float* dvec = Lt + FD * ALD;
+    float* yv = dvec + FD;
     // Rank-one downdates: C_kk -= S_k S_k^T / omega', C_vk^T -= S_k S_v^T / omega'.
     float4v skr[4];
     float skc[4], svc[4];
@@ -543,83 +547,107 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         skc[fb] = mq[fb * 16 + c];
         svc[fb] = mq[FD + fb * 16 + c];
     }
-    {
-        int idx = 0;
+    // Upper 16x16 block (I, J), I <= J, of C_kk is ckk[blk_idx(I, J)].
+    auto blk_idx = [](int I, int J) { return I * 4 - I * (I - 1) / 2 + (J - I); };
+    const float m_x = mrow[static_cast<int64_t>(bh) * nrows + (ic - row0)];
+    const float lam_s = lambda * exp2f(-m_x);
+    float dmax = -INFINITY;
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb)
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-            for (int fb2 = fb; fb2 < 4; ++fb2) {
+        for (int J = I; J < 4; ++J)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = fb * 16 + 4 * g + r, col = fb2 * 16 + c;
-                    const float val = fmaf(-skr[fb][r], skc[fb2], ckk[idx][r]);
-                    A[row * ALD + col] = val;
-                    if (fb != fb2) A[col * ALD + row] = val;
+            for (int r = 0; r < 4; ++r) {
+                float val = fmaf(-skr[I][r], skc[J], ckk[blk_idx(I, J)][r]);
+                if (I == J && 4 * g + r == c) {   // diagonal entry: ridge
+                    val += lam_s;
+                    dmax = fmaxf(dmax, val);
                 }
-                ++idx;
+                ckk[blk_idx(I, J)][r] = val;
             }
-    }
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
         for (int fv = 0; fv < 4; ++fv)
 #pragma unroll
             for (int r = 0; r < 4; ++r) cvk[fb * 4 + fv][r] = fmaf(-skr[fb][r], svc[fv], cvk[fb * 4 + fv][r]);
-    LDS_FENCE();
-    const float m_x = mrow[static_cast<int64_t>(bh) * nrows + (ic - row0)];
-    const float lam_s = lambda * exp2f(-m_x);
-    A[lane * ALD + lane] += lam_s;
-    LDS_FENCE();
-    float dmax = A[lane * ALD + lane];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, off));
     // lambda > 0: drop only pivots that rounding made non-positive; lambda = 0: also drop
     // directions the prefix leaves (numerically) undetermined.
     const float thresh = lambda > 0.0f ? 0.0f : 1e-6f * dmax;
-
-    float ar[FD];
-#pragma unroll
-    for (int b = 0; b < FD; ++b) ar[b] = A[lane * ALD + b];
-    LDS_FENCE();
-    // Park C_vk^T in the (now free) matrix area during the elimination, lane-private;
-    // entry t of lane l at float4 index 64 t + l keeps the 64 lanes on distinct banks.
-    float4v* park = reinterpret_cast<float4v*>(A) + lane;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) park[64 * t] = cvk[t];
-    // The accumulators must really leave the registers: no store-to-load forwarding.
-    LDS_FENCE();
     const float qa = bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]);
     // kbar = a_k + S_k / omega' (the weighted mean of the centred keys, same weights as C)
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD;
     float z = fmaf(mq[lane], iom2, anc[lane]) - qa;
 
-    // Forward elimination (symmetric, no pivoting): after step p, lane p's registers hold row
-    // p of U = D L^T and z holds L^{-1} (kbar - q).  Column p of the trailing matrix equals
-    // its row p, so one LDS word per lane broadcasts the pivot row.
+    float dreg = 0.0f;   // lane P ends up holding the pivot d_P
 #pragma unroll
-    for (int p = 0; p < FD; ++p) {
-        colb[lane] = ar[p];
-        LDS_FENCE();
-        const float piv = colb[p];
-        // An IEEE divide here (not v_rcp_f32): with the cheaper reciprocal the compiler
-        // sinks the row updates across steps and runs out of registers.
-        const float inv = piv > thresh ? 1.0f / piv : 0.0f;
-        const float f = lane > p ? ar[p] * inv : 0.0f;
-        const float zp = lane_value(z, p);
-        z = fmaf(-f, zp, z);
+    for (int K = 0; K < 4; ++K) {
+        // Stage block row K (rows 16K.., columns >= 16K) and read this lane's panel row:
+        // Lf[t] = C[a][16K + t] = C[16K + t][a].  Lanes a < 16K read stale words; their
+        // multipliers are zero below, so those never reach a live value.
 #pragma unroll
-        for (int b = p + 1; b < FD; ++b) ar[b] = fmaf(-f, colb[b], ar[b]);
+        for (int J = K; J < 4; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Lt[(16 * K + 4 * g + r) * ALD + 16 * J + c] = ckk[blk_idx(K, J)][r];
         LDS_FENCE();
+        float Lf[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Lf[t] = Lt[(16 * K + t) * ALD + lane];
+        LDS_FENCE();
+        // Eliminate the panel; Lf[p] becomes this row's multiplier L[a][16K + p].
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int P = 16 * K + p;
+            const float piv = lane_value(Lf[p], P);
+            float inv = __builtin_amdgcn_rcpf(piv);
+            inv = fmaf(inv, fmaf(-piv, inv, 1.0f), inv);   // one Newton step: ~0.5 ulp
+            inv = piv > thresh ? inv : 0.0f;
+            const float f = lane > P ? Lf[p] * inv : 0.0f;
+            z = fmaf(-f, lane_value(z, P), z);
+#pragma unroll
+            for (int t = p + 1; t < 16; ++t) Lf[t] = fmaf(-f, lane_value(Lf[t], P), Lf[t]);
+            dreg = lane == P ? piv : dreg;
+            Lf[p] = f;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Lt[(16 * K + t) * ALD + lane] = Lf[t];
+        dvec[lane] = dreg;
+        LDS_FENCE();
+        if (K < 3) {
+            // Trailing update C_IJ -= L_IK D_K L_JK^T for K < I <= J: 16x16x4 fp32 MFMAs over
+            // the panel columns 16K + 4s + g (K-slot g of step s).
+            float dv[4], Lo[4][4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                dv[s4] = dvec[16 * K + 4 * s4 + g];
+#pragma unroll
+                for (int X = K + 1; X < 4; ++X) Lo[X][s4] = Lt[(16 * K + 4 * s4 + g) * ALD + 16 * X + c];
+            }
+#pragma unroll
+            for (int I = K + 1; I < 4; ++I)
+#pragma unroll
+                for (int J = I; J < 4; ++J)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        ckk[blk_idx(I, J)] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            -Lo[I][s4], dv[s4] * Lo[J][s4], ckk[blk_idx(I, J)], 0, 0, 0);
+            LDS_FENCE();
+        }
     }
-    // Back substitution U y = z, column by column.
+    // Back substitution D L^T y = z, column by column: row b of D L^T is d_b L[P][b].
+    float ul[FD];
+#pragma unroll
+    for (int P = 0; P < FD; ++P) ul[P] = Lt[lane * ALD + P] * dreg;
     float ylane = 0.0f;
 #pragma unroll
-    for (int p = FD - 1; p >= 0; --p) {
-        const float dp = lane_value(ar[p], p);
-        const float zp = lane_value(z, p);
+    for (int P = FD - 1; P >= 0; --P) {
+        const float dp = lane_value(dreg, P);
+        const float zp = lane_value(z, P);
         const float yp = dp > thresh ? zp * __builtin_amdgcn_rcpf(dp) : 0.0f;
-        ylane = lane == p ? yp : ylane;
-        z = fmaf(-ar[p], yp, z);
+        ylane = lane == P ? yp : ylane;
+        z = fmaf(-ul[P], yp, z);
     }
     yv[lane] = ylane;
     LDS_FENCE();
@@ -630,11 +658,9 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     for (int fb = 0; fb < 4; ++fb) {
         const float4v yy = *reinterpret_cast<const float4v*>(yv + fb * 16 + 4 * g);
 #pragma unroll
-        for (int fv = 0; fv < 4; ++fv) {
-            const float4v cv = park[64 * (fb * 4 + fv)];
+        for (int fv = 0; fv < 4; ++fv)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part[fv] = fmaf(cv[r], yy[r], part[fv]);
-        }
+            for (int r = 0; r < 4; ++r) part[fv] = fmaf(cvk[fb * 4 + fv][r], yy[r], part[fv]);
     }
 #pragma unroll
     for (int fv = 0; fv < 4; ++fv) {
