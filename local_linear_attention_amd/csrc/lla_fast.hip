@@ -135,22 +135,35 @@ __device__ __forceinline__ void head_major_block(int b, int BH, int nblk, int* b
 }
 
 // Per-head anchor, pass 1: block (head, slice) sums its slice of the keys and values per
-// feature (fp32; threads t and t + 128 take alternate keys of feature t % 128).
+// feature (fp32).  Thread -> 8 features (16 bytes) of K (groups 0-7) or V (groups 8-15) and
+// every 16th key of the slice; the 16 key phases are then added up through LDS.
 __global__ __launch_bounds__(256) void lla_anchor_kernel(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          float* __restrict__ partial, int n) {
-    __shared__ float half_sum[128];
+    __shared__ float sums[16][2 * FD + 4];
     const int bh = static_cast<int>(blockIdx.x) / ANCHOR_SLICES;
     const int sl = static_cast<int>(blockIdx.x) % ANCHOR_SLICES;
-    const int tid = threadIdx.x, f = tid & 127, ph = tid >> 7;
+    const int tid = threadIdx.x, fgrp = tid & 15, ph = tid >> 4;
     const int len = (n + ANCHOR_SLICES - 1) / ANCHOR_SLICES;
     const int j_lo = sl * len, j_hi = min(n, j_lo + len);
-    const uint16_t* src = (f < FD ? k : v) + static_cast<int64_t>(bh) * n * FD + (f & (FD - 1));
-    float acc = 0.0f;
-    for (int j = j_lo + ph; j < j_hi; j += 2) acc += bf16_bits_to_f32(src[static_cast<int64_t>(j) * FD]);
-    if (ph == 1) half_sum[f] = acc;
+    const uint16_t* src = (fgrp < 8 ? k : v) + static_cast<int64_t>(bh) * n * FD + 8 * (fgrp & 7);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = j_lo + ph; j < j_hi; j += 16) {
+        const uint4 x = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * FD);
+        const uint32_t wds[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] += __uint_as_float((e & 1) ? (wds[e >> 1] & 0xffff0000u) : (wds[e >> 1] << 16));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sums[ph][8 * fgrp + e] = acc[e];
     __syncthreads();
-    if (ph == 0) partial[(static_cast<int64_t>(bh) * ANCHOR_SLICES + sl) * 2 * FD + f] = acc + half_sum[f];
+    if (tid < 2 * FD) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int q2 = 0; q2 < 16; ++q2) tot += sums[q2][tid];
+        partial[(static_cast<int64_t>(bh) * ANCHOR_SLICES + sl) * 2 * FD + tid] = tot;
+    }
 }
 
 // Pack K and V once into the LDS image of each tile (zero past n), centred at the head's
@@ -675,16 +688,21 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Rows i < 2d of the bf16 path, exactly in fp64: one wave per row, 4 consecutive rows per
-// block sharing the (at most 2d-key) prefix staged in LDS as fp32 (exact for bf16).
+// Rows i < 2d of the bf16 path, in fp64: one wave per row, 4 consecutive rows per block
+// sharing the (at most 2d-key) prefix staged in LDS as bf16.
 //   scores -> m, weights, omega; kbar, vbar (lane = feature);
-//   row a of C_kk = sum_j w_j (k_ja - kbar_a) k_j   (the k_j - kbar centring of the right
-//   factor is implied: sum_j w_j (k_ja - kbar_a) = 0);
+//   C_kk = R^T R with R[j] = sqrt(w_j) (k_j - kbar) in fp64 on the matrix cores
+//   (v_mfma_f64_16x16x4f64, 4 keys per step), ridge on the diagonal, then moved to
+//   lane-per-row form through LDS, 16 rows at a time;
 //   LDL^T elimination lane-per-row, back substitution -> y;
 //   probe u_j = (k_j - kbar).y and b = vbar - sum_j w_j u_j (v_j - vbar)  (= vbar - C_vk y).
+// fp64 MFMA output layout: D[4 r + (l / 16)][l % 16] in double register r of lane l.
 constexpr int S_ROWS = 4;
 constexpr int S_KMAX = 2 * FD;
-constexpr int S_LD = FD + 1;    // fp32 row stride (elements)
+constexpr int S_KLD = FD + 2;   // bf16 row stride (halves): 33 words, conflict-free per row
+constexpr int S_TLD = FD + 1;   // fp64 row stride of the transposition buffer
+
+typedef double double4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ double wave_max_d(double x) {
 #pragma unroll
@@ -697,18 +715,20 @@ __device__ __forceinline__ double wave_sum_d(double x) {
     return x;
 }
 
-__global__ __launch_bounds__(256) void lla_short_kernel(
+__global__ __launch_bounds__(256, 2) void lla_short_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ out, int n, int rows, int BH,
     double inv_h, double lambda) {
-    __shared__ float Ks[S_KMAX * S_LD];
-    __shared__ float Vs[S_KMAX * S_LD];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[S_KMAX * S_KLD];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[S_KMAX * S_KLD];
     __shared__ double qs[S_ROWS][FD];
     __shared__ double ws[S_ROWS][S_KMAX];
     __shared__ double kbs[S_ROWS][FD];
-    __shared__ double xb[S_ROWS][FD];   // pivot-column exchange, then y
+    __shared__ double xb[S_ROWS][FD];               // pivot-column exchange, then y
+    __shared__ double tb[S_ROWS][16 * S_TLD];       // 16 rows of C_kk in transit
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
     const int nblk = (rows + S_ROWS - 1) / S_ROWS;
     const int blk = nblk - 1 - static_cast<int>(blockIdx.x / BH);  // longest rows first
     const int bh = static_cast<int>(blockIdx.x % BH);
@@ -718,18 +738,15 @@ __global__ __launch_bounds__(256) void lla_short_kernel(
     const int ic = min(i, rows - 1);
     const int nk = min(r0 + S_ROWS, rows);          // keys staged: 0 .. nk-1
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
+    auto kval = [&](int j, int a) { return static_cast<double>(bf16_bits_to_f32(Ks[j * S_KLD + a])); };
+    auto vval = [&](int j, int a) { return static_cast<double>(bf16_bits_to_f32(Vs[j * S_KLD + a])); };
 
-    for (int e = tid; e < nk * (FD / 8); e += 256) {
-        const int j = e / (FD / 8), f0 = (e % (FD / 8)) * 8;
-        const uint4 kr = *reinterpret_cast<const uint4*>(k + base + static_cast<int64_t>(j) * FD + f0);
-        const uint4 vr = *reinterpret_cast<const uint4*>(v + base + static_cast<int64_t>(j) * FD + f0);
-        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w}, vw[4] = {vr.x, vr.y, vr.z, vr.w};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const uint32_t sh = (t & 1) ? 0u : 16u;
-            Ks[j * S_LD + f0 + t] = __uint_as_float((kw[t >> 1] << sh) & 0xffff0000u);
-            Vs[j * S_LD + f0 + t] = __uint_as_float((vw[t >> 1] << sh) & 0xffff0000u);
-        }
+    for (int e = tid; e < nk * (FD / 2); e += 256) {   // 32-bit words: 2 features
+        const int j = e / (FD / 2), f0 = (e % (FD / 2)) * 2;
+        *reinterpret_cast<uint32_t*>(Ks + j * S_KLD + f0) =
+            *reinterpret_cast<const uint32_t*>(k + base + static_cast<int64_t>(j) * FD + f0);
+        *reinterpret_cast<uint32_t*>(Vs + j * S_KLD + f0) =
+            *reinterpret_cast<const uint32_t*>(v + base + static_cast<int64_t>(j) * FD + f0);
     }
     qs[w][lane] = static_cast<double>(bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]));
     __syncthreads();
@@ -742,7 +759,7 @@ __global__ __launch_bounds__(256) void lla_short_kernel(
         if (j <= ic) {
             double acc = 0.0;
 #pragma unroll 16
-            for (int a = 0; a < FD; ++a) acc = fma(qs[w][a], static_cast<double>(Ks[j * S_LD + a]), acc);
+            for (int a = 0; a < FD; ++a) acc = fma(qs[w][a], kval(j, a), acc);
             s[h2] = acc * inv_h;
         }
     }
@@ -760,36 +777,86 @@ __global__ __launch_bounds__(256) void lla_short_kernel(
     double ka = 0.0, va = 0.0;
     for (int j = 0; j <= ic; ++j) {
         const double wj = ws[w][j];
-        ka = fma(wj, static_cast<double>(Ks[j * S_LD + lane]), ka);
-        va = fma(wj, static_cast<double>(Vs[j * S_LD + lane]), va);
+        ka = fma(wj, kval(j, lane), ka);
+        va = fma(wj, vval(j, lane), va);
     }
     ka /= omega;
     va /= omega;
     kbs[w][lane] = ka;
+    LDS_FENCE();
 
-    // ---- row `lane` of C_kk, plus the rescaled ridge on the diagonal
-    double cr[FD];
+    // ---- C_kk on the matrix cores: upper 16x16 blocks (I, J), I <= J, 4 keys per step.
+    double kb4[4];
 #pragma unroll
-    for (int b = 0; b < FD; ++b) cr[b] = 0.0;
-    for (int j = 0; j <= ic; ++j) {
-        const double t = ws[w][j] * (static_cast<double>(Ks[j * S_LD + lane]) - ka);
+    for (int fb = 0; fb < 4; ++fb) kb4[fb] = kbs[w][16 * fb + c];
+    double4v cacc[10];
 #pragma unroll
-        for (int b = 0; b < FD; ++b) cr[b] = fma(t, static_cast<double>(Ks[j * S_LD + b]), cr[b]);
+    for (int t = 0; t < 10; ++t) cacc[t] = double4v{0.0, 0.0, 0.0, 0.0};
+    const int nsteps = (ic + 4) / 4;
+    for (int st = 0; st < nsteps; ++st) {
+        const int j = 4 * st + g;          // this lane's key (K-slot g)
+        const bool in = j <= ic;
+        const double sw = in ? sqrt(ws[w][j]) : 0.0;
+        double a4[4];
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) a4[fb] = in ? sw * (kval(j, 16 * fb + c) - kb4[fb]) : 0.0;
+        int idx = 0;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int J = I; J < 4; ++J) {
+                cacc[idx] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[I], a4[J], cacc[idx], 0, 0, 0);
+                ++idx;
+            }
     }
+    // ridge on the diagonal (row 4r + g of a diagonal block equals column c), its maximum
     const double lam_s = lambda * exp(-m);
     double dmax = 0.0;
+    {
+        int idx = 0;
 #pragma unroll
-    for (int b = 0; b < FD; ++b) {
-        cr[b] += (b == lane) ? lam_s : 0.0;
-        if (b == lane) dmax = cr[b];
+        for (int I = 0; I < 4; ++I) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * r + g == c) {
+                    cacc[idx][r] += lam_s;
+                    dmax = fmax(dmax, cacc[idx][r]);
+                }
+            idx += 4 - I;
+        }
     }
     dmax = wave_max_d(dmax);
     const double thresh = lambda > 0.0 ? 0.0 : 1e-12 * dmax;
+
+    // ---- to lane-per-row form: pass p stages rows 16p .. 16p+15 and lanes 16p.. read them
+    double cr[FD];
+    double* T = tb[w];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        int idx = 0;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int J = I; J < 4; ++J) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // block (I, J), register r: C[16I + 4r + g][16J + c]
+                    if (I == p) T[(4 * r + g) * S_TLD + 16 * J + c] = cacc[idx][r];
+                    else if (J == p) T[c * S_TLD + 16 * I + 4 * r + g] = cacc[idx][r];
+                }
+                ++idx;
+            }
+        LDS_FENCE();
+        if (g == p) {
+#pragma unroll
+            for (int b = 0; b < FD; ++b) cr[b] = T[c * S_TLD + b];
+        }
+        LDS_FENCE();
+    }
     double z = ka - qs[w][lane];
 
     // ---- LDL^T elimination (lane owns row), then back substitution
     double* xw = xb[w];
-    LDS_FENCE();
 #pragma unroll
     for (int p = 0; p < FD; ++p) {
         xw[lane] = cr[p];
@@ -823,8 +890,7 @@ __global__ __launch_bounds__(256) void lla_short_kernel(
         if (j <= ic) {
             double u = 0.0;
 #pragma unroll 16
-            for (int a = 0; a < FD; ++a)
-                u = fma(static_cast<double>(Ks[j * S_LD + a]) - kbs[w][a], xw[a], u);
+            for (int a = 0; a < FD; ++a) u = fma(kval(j, a) - kbs[w][a], xw[a], u);
             wu[h2] = wl[h2] * u;
         }
         ws[w][lane + 64 * h2] = wu[h2];
@@ -832,7 +898,7 @@ __global__ __launch_bounds__(256) void lla_short_kernel(
     const double swu = wave_sum_d(wu[0] + wu[1]);
     LDS_FENCE();
     double acc = 0.0;
-    for (int j = 0; j <= ic; ++j) acc = fma(ws[w][j], static_cast<double>(Vs[j * S_LD + lane]), acc);
+    for (int j = 0; j <= ic; ++j) acc = fma(ws[w][j], vval(j, lane), acc);
     if (valid) out[base + static_cast<int64_t>(i) * FD + lane] = static_cast<float>(va - (acc - va * swu));
 }
 
