@@ -370,27 +370,35 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         qf[ks] = __builtin_bit_cast(bf16x8, raw);
     }
 
-    // sqrt of the shifted weights of key block w (16 keys) for the 4 queries -> Sw buffer,
-    // their fp16 squares -> Sw2; om2p sums those squares (query c, keys of block w).
+    // Scores of key block w (16 keys) of a tile for the 4 queries: lane (g, c) register r =
+    // query c < 4, key 16w + 4g + r.  Issued before the tile's moments so that the MFMA
+    // latency hides under them; sqrt of the shifted weights (Sw) and their fp16 squares (Sw2)
+    // are stored after.  om2p sums those squares (query c, keys of block w).
     float om2p = 0.0f;
-    auto scores = [&](uint4 kq0, uint4 kq1, unsigned char* buf, int j0) {
+    const float hs = 0.5f * sl2, hm = 0.5f * mcol;
+    auto score_mfma = [&](uint4 kq0, uint4 kq1) {
         float4v s = {0.f, 0.f, 0.f, 0.f};
         s = mfma_bf16(__builtin_bit_cast(bf16x8, kq0), qf[0], s);
-        s = mfma_bf16(__builtin_bit_cast(bf16x8, kq1), qf[1], s);
-        if (colv) {
-            half4 sw4;
+        return mfma_bf16(__builtin_bit_cast(bf16x8, kq1), qf[1], s);
+    };
+    auto score_store = [&](float4v s, unsigned char* buf, int j0) {
+        float e[4];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int j = j0 + 16 * w + 4 * g + rr;
-                // raw v_exp_f32: weights below 2^-126 flush to zero, which changes nothing
-                sw4[rr] = static_cast<_Float16>(
-                    j <= qcol ? __builtin_amdgcn_exp2f((s[rr] * sl2 - mcol) * 0.5f) : 0.0f);
-            }
-            const half4 w4 = sw4 * sw4;
+        for (int rr = 0; rr < 4; ++rr) e[rr] = __builtin_amdgcn_exp2f(fmaf(s[rr], hs, -hm));  // raw v_exp_f32
+        if (j0 + MT - 1 > i0) {   // block-uniform: keys past some query of the block
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) e[rr] = j0 + 16 * w + 4 * g + rr <= qcol ? e[rr] : 0.0f;
+        }
+        half4 sw4;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sw4[rr] = static_cast<_Float16>(e[rr]);
+        const half4 w4 = sw4 * sw4;
+        if (colv) {
             *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW) + c * MT + 16 * w + 4 * g) = sw4;
             *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW2) + c * MT + 16 * w + 4 * g) = w4;
-            om2p += (static_cast<float>(w4[0]) + static_cast<float>(w4[1])) +
-                    (static_cast<float>(w4[2]) + static_cast<float>(w4[3]));
+            const h16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+            om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 0, 1), one, om2p, false);
+            om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 2, 3), one, om2p, false);
         }
     };
 
@@ -500,20 +508,22 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     issue(0, aq0, aq1);
     issue(1, bq0, bq1);
     wait_tile();
-    scores(aq0, aq1, buf(0), 0);
+    score_store(score_mfma(aq0, aq1), buf(0), 0);
     ring_barrier();
     for (int t = 0; t < ntiles; t += 2) {
         // step t: tile t in LDS, tile t+1 landing (operand in B), tile t+2 issued now (A)
+        const float4v sb = score_mfma(bq0, bq1);
         issue(t + 2, aq0, aq1);
         compute(t, buf(t));
-        if (t + 1 < ntiles) scores(bq0, bq1, buf(t + 1), (t + 1) * MT);
+        if (t + 1 < ntiles) score_store(sb, buf(t + 1), (t + 1) * MT);
         wait_tile();
         ring_barrier();
         if (t + 1 >= ntiles) break;
         // step t+1: the same with the register sets swapped
+        const float4v sa = score_mfma(aq0, aq1);
         issue(t + 3, bq0, bq1);
         compute(t + 1, buf(t + 1));
-        if (t + 2 < ntiles) scores(aq0, aq1, buf(t + 2), (t + 2) * MT);
+        if (t + 2 < ntiles) score_store(sa, buf(t + 2), (t + 2) * MT);
         wait_tile();
         ring_barrier();
     }
