@@ -99,9 +99,12 @@ constexpr int PACK_TILE_BYTES = 2 * FD * M_LD * 2;
 constexpr int M_LOADS = PACK_TILE_BYTES / 1024;  // wave-wide copies of 16 B per lane per tile
 constexpr int M_WLOADS = (M_LOADS + B_WAVES - 1) / B_WAVES;   // copies issued by each wave
 constexpr int M_NBUF = 3;                // tile ring: compute t, t+1 landing, t+2 in flight
-constexpr int M_SW = PACK_TILE_BYTES;    // byte offset of Sw: sqrt-weights, [query][key]
-constexpr int M_SW2 = M_SW + B_WAVES * MT * 2;  // Sw2: fp16 weights, 16 rows (rows >= 4 zero)
-constexpr int M_BUF_BYTES = M_SW2 + 16 * MT * 2;
+// Side buffers of a tile, rows of M_LD halves like the tile (16-byte reads by 16 rows at
+// once stay conflict-free): Sw = sqrt-weights [query][key]; Sw2 = fp16 weights, 16 rows of
+// which rows B_WAVES.. stay zero (the unused rows of the block-sum MFMA operand).
+constexpr int M_SW = PACK_TILE_BYTES;
+constexpr int M_SW2 = M_SW + B_WAVES * M_LD * 2;
+constexpr int M_BUF_BYTES = M_SW2 + 16 * M_LD * 2;
 constexpr int B_SOLVE_FLOATS = FD * (FD + 1) + 2 * FD;  // L (padded rows) + pivots + y
 constexpr int B_SOLVE_BYTES = B_SOLVE_FLOATS * 4 * B_WAVES;
 constexpr int B_MEAN_FLOATS = 2 * FD + B_WAVES;          // per query: S_k, S_v, omega' parts
@@ -353,9 +356,9 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const uint16_t* kh = k + base;
 
     // Rows B_WAVES.. of every Sw2 buffer are the zero rows of the weight operand.
-    for (int e = tid; e < M_NBUF * (16 - B_WAVES) * MT / 8; e += 256) {
-        const int bsel = e / ((16 - B_WAVES) * MT / 8), rem = e % ((16 - B_WAVES) * MT / 8);
-        *reinterpret_cast<uint4*>(smem + bsel * M_BUF_BYTES + M_SW2 + B_WAVES * MT * 2 + rem * 16) =
+    for (int e = tid; e < M_NBUF * (16 - B_WAVES) * M_LD / 8; e += 256) {
+        const int bsel = e / ((16 - B_WAVES) * M_LD / 8), rem = e % ((16 - B_WAVES) * M_LD / 8);
+        *reinterpret_cast<uint4*>(smem + bsel * M_BUF_BYTES + M_SW2 + B_WAVES * M_LD * 2 + rem * 16) =
             make_uint4(0, 0, 0, 0);
     }
     // Score operand: column c < B_WAVES is query i0 + c (the other columns are zero).
@@ -394,8 +397,8 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         for (int rr = 0; rr < 4; ++rr) sw4[rr] = static_cast<_Float16>(e[rr]);
         const half4 w4 = sw4 * sw4;
         if (colv) {
-            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW) + c * MT + 16 * w + 4 * g) = sw4;
-            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW2) + c * MT + 16 * w + 4 * g) = w4;
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW) + c * M_LD + 16 * w + 4 * g) = sw4;
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW2) + c * M_LD + 16 * w + 4 * g) = w4;
             const h16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
             om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 0, 1), one, om2p, false);
             om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 2, 3), one, om2p, false);
@@ -476,11 +479,11 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
             if (j0 + 32 * sub > last) break;  // block-uniform: past every query of the block
             // Operands of the block sums S_k, S_v (all 4 queries, feature block w).
             const int ko = (w * 16 + c) * M_LD + 32 * sub + 8 * g;
-            const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * MT + 32 * sub + 8 * g);
+            const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * M_LD + 32 * sub + 8 * g);
             const half8 kw = *reinterpret_cast<const half8*>(Kt + ko);
             const half8 vw = *reinterpret_cast<const half8*>(Vt + ko);
             if (j0 + 32 * sub <= ic) {  // wave-uniform: keys of this query's prefix
-                const half8 sw = *reinterpret_cast<const half8*>(Sw + w * MT + 32 * sub + 8 * g);
+                const half8 sw = *reinterpret_cast<const half8*>(Sw + w * M_LD + 32 * sub + 8 * g);
                 half8 rk[4];
 #pragma unroll
                 for (int fb = 0; fb < 4; ++fb) {
