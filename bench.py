@@ -54,6 +54,13 @@ KERNEL_BOUND = {
     "lla_anchor_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_moments_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_keymom_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_probe_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+}
+PATH_KERNELS = {
+    "exact": ["lla_exact_kernel"],
+    "fast": ["lla_short_kernel", "lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel",
+             "lla_moments_kernel", "lla_keymom_kernel", "lla_probe_kernel"],
 }
 
 
@@ -63,25 +70,37 @@ def pair_count(BH, lo, hi):
 
 
 def kernel_flops(name, B, H, n, d, path):
-    """Algorithmic flops (formulation NS, the one both paths execute) of one launch of a
-    kernel: the fast path splits the rows at 2d between an fp64 kernel (short rows) and the
-    MFMA kernels; the row-max kernel owns the score term of its rows, the moments kernel the
-    first and second moments, the solve and the assembly (scores it recomputes are not
-    counted again)."""
+    """Algorithmic flops of one launch of a kernel, in the formulation that kernel executes.
+    The exact path and the fast path's rows i < 4d form the value-key cross moment (NS);
+    the fast path's rows i >= 4d apply it through the probe pass (min).  Fast path: rows
+    [0, 2d) fp64 short-row kernel; the row-max kernel owns the score term of rows >= 2d;
+    rows [2d, 4d) the explicit moments kernel (first and second moments, solve, assembly);
+    rows [4d, n) the key-moment kernel (first moments, C_kk, solve) and the probe kernel
+    (probe scores and the weighted value sum).  Scores a kernel recomputes are not counted
+    again."""
     BH = B * H
     row0 = min(n, 2 * d) if path == "fast" else n
+    rowp = min(n, 4 * d) if path == "fast" else n
     per_query = d ** 3 / 3 + 4 * d * d + 2 * d
+    moments = 2 * (1 + 2 * d) + d * (d + 1)
     if name in ("lla_exact_kernel", "lla_short_kernel"):
-        return pair_count(BH, 0, row0) * (2 * d + 2 * (1 + 2 * d) + d * (d + 1) + 2 * d * d) \
-            + BH * row0 * per_query
+        return pair_count(BH, 0, row0) * (2 * d + moments + 2 * d * d) + BH * row0 * per_query
     if name in ("lla_anchor_kernel", "lla_pack_kernel"):
         return 0                      # data movement only (K, V summed and repacked once)
     if name == "lla_rowmax_kernel":
         return pair_count(BH, row0, n) * 2 * d
     if name == "lla_moments_kernel":
-        return pair_count(BH, row0, n) * (2 * (1 + 2 * d) + d * (d + 1) + 2 * d * d) \
-            + BH * (n - row0) * per_query
+        return pair_count(BH, row0, rowp) * (moments + 2 * d * d) + BH * (rowp - row0) * per_query
+    if name == "lla_keymom_kernel":
+        return pair_count(BH, rowp, n) * moments + BH * (n - rowp) * (d ** 3 / 3 + 2 * d * d)
+    if name == "lla_probe_kernel":
+        return pair_count(BH, rowp, n) * (4 * d + 2) + BH * (n - rowp) * 4 * d
     raise KeyError(name)
+
+
+def path_flops(B, H, n, d, path):
+    """Algorithmic flops of one forward in the formulations the path executes."""
+    return sum(kernel_flops(k, B, H, n, d, path) for k in PATH_KERNELS[path])
 
 
 def kernel_source_hash():
@@ -141,8 +160,8 @@ def cpu_baseline(w, q, k, v, seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="d24")
     ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -230,7 +249,7 @@ def main():
                          "tflops": fl / (avg * 1e-3) / 1e12, "bound": bound, "peak": peak}
     dom = max(kernels, key=lambda nm: kernels[nm]["avg_ms"] * kernels[nm]["launches"])
     dk = kernels[dom]
-    flops = alg_flops(w.B, w.H, w.n, w.d, "NS")
+    flops = path_flops(w.B, w.H, w.n, w.d, path)
     achieved_tflops = flops / (ms_per_step * 1e-3) / 1e12
     traffic = load_traffic(dom, w.name)
 
@@ -254,7 +273,9 @@ def main():
             "h": w.h, "lambda": w.lam, "path": path, "queries": w.queries,
         },
         "tflops": achieved_tflops,
-        "flop_count": {"formulation": "NS", "flops": flops,
+        "flop_count": {"formulation": ("NS for rows i < 4d, min (probe pass) for rows i >= 4d"
+                                       if path == "fast" else "NS"),
+                       "flops": flops,
                        "F_NS": alg_flops(w.B, w.H, w.n, w.d, "NS"),
                        "F_min": alg_flops(w.B, w.H, w.n, w.d, "min")},
         "kernels": kernels,

@@ -115,6 +115,9 @@ constexpr int ANCHOR_SLICES = 16;        // key slices of the per-head anchor su
 // padding), the score operand of the row-max kernel, 9 KiB per tile.
 constexpr int KM_LD = FD + 8;
 constexpr int KM_TILE_BYTES = MT * KM_LD * 2;
+// Workspace stride of a tile's key-major images: the bf16 keys, then the centred keys
+// fp16(k - a) in the same layout.
+constexpr int KM_STRIDE = 2 * KM_TILE_BYTES;
 constexpr int KM_LOADS = KM_TILE_BYTES / 1024;
 constexpr int KM_WLOADS = (KM_LOADS + B_WAVES - 1) / B_WAVES;
 constexpr int R_QW = 16, R_QB = B_WAVES * R_QW;  // row-max: 16 queries per wave, 64 per block
@@ -172,8 +175,9 @@ __global__ __launch_bounds__(256) void lla_anchor_kernel(const uint16_t* __restr
 // Pack K and V once into the LDS image of each tile (zero past n), centred at the head's
 // anchor a = fp16(mean over all keys of k, of v): stored value fp16(x - a), one rounding.
 // Thread -> keys 2p, 2p+1 and features 8fg .. 8fg+7; every store writes a pair of keys.
-// The same block also writes the tile's keys key-major (bf16, unchanged) for the row-max
-// kernel, and block 0 of each head the head's anchor (fp16 values as floats).
+// The same block also writes the tile's keys key-major, as given (bf16) and centred
+// (fp16(k - a), the same values as the feature-major image), and block 0 of each head the
+// head's anchor (fp16 values as floats).
 __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
                                                        const float* __restrict__ partial,
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
         v1 = *reinterpret_cast<const uint4*>(v + base + static_cast<int64_t>(jb) * FD + 8 * fg);
     }
     {   // key-major image: key 2p (and 2p+1), features 8fg .. 8fg+7; row padding zero
-        unsigned char* kt = kimg + (static_cast<int64_t>(bh) * ntiles + t) * KM_TILE_BYTES;
+        unsigned char* kt = kimg + (static_cast<int64_t>(bh) * ntiles + t) * KM_STRIDE;
         *reinterpret_cast<uint4*>(kt + (2 * pr) * (KM_LD * 2) + 16 * fg) = k0;
         *reinterpret_cast<uint4*>(kt + (2 * pr + 1) * (KM_LD * 2) + 16 * fg) = k1;
         if (fg == 0) {
@@ -212,6 +216,24 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
         }
     }
     __syncthreads();
+    {   // centred keys fp16(k - a), key-major, after the bf16 image; row padding zero
+        unsigned char* kt = kimg + (static_cast<int64_t>(bh) * ntiles + t) * KM_STRIDE + KM_TILE_BYTES;
+        const uint32_t wa[4] = {k0.x, k0.y, k0.z, k0.w}, wb[4] = {k1.x, k1.y, k1.z, k1.w};
+        half8 ca, cb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ak = anc[8 * fg + e];
+            const uint32_t xa = wa[e >> 1], xb = wb[e >> 1];
+            ca[e] = static_cast<_Float16>(ja >= n ? 0.0f : __uint_as_float((e & 1) ? (xa & 0xffff0000u) : (xa << 16)) - ak);
+            cb[e] = static_cast<_Float16>(jb >= n ? 0.0f : __uint_as_float((e & 1) ? (xb & 0xffff0000u) : (xb << 16)) - ak);
+        }
+        *reinterpret_cast<half8*>(kt + (2 * pr) * (KM_LD * 2) + 16 * fg) = ca;
+        *reinterpret_cast<half8*>(kt + (2 * pr + 1) * (KM_LD * 2) + 16 * fg) = cb;
+        if (fg == 0) {
+            *reinterpret_cast<uint4*>(kt + (2 * pr) * (KM_LD * 2) + 2 * FD) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(kt + (2 * pr + 1) * (KM_LD * 2) + 2 * FD) = make_uint4(0, 0, 0, 0);
+        }
+    }
     uint32_t* dst = reinterpret_cast<uint32_t*>(packed + (static_cast<int64_t>(bh) * ntiles + t) * PACK_TILE_BYTES);
     const uint32_t ka[4] = {k0.x, k0.y, k0.z, k0.w}, kb[4] = {k1.x, k1.y, k1.z, k1.w};
     const uint32_t va[4] = {v0.x, v0.y, v0.z, v0.w}, vb[4] = {v1.x, v1.y, v1.z, v1.w};
@@ -268,8 +290,8 @@ __global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restr
     const int ntiles = (qlast + MT) / MT;
     const int ptiles = (n + MT - 1) / MT;
     const __amdgpu_buffer_rsrc_t img = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(uniform_ptr(kimg + static_cast<int64_t>(bh) * ptiles * KM_TILE_BYTES)), 0,
-        ptiles * KM_TILE_BYTES, 0x00020000);
+        const_cast<unsigned char*>(uniform_ptr(kimg + static_cast<int64_t>(bh) * ptiles * KM_STRIDE)), 0,
+        ptiles * KM_STRIDE, 0x00020000);
     int voff[KM_WLOADS];
 #pragma unroll
     for (int e = 0; e < KM_WLOADS; ++e) voff[e] = lane * 16 + min(wu + B_WAVES * e, KM_LOADS - 1) * 1024;
@@ -284,7 +306,7 @@ __global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restr
             const int u = min(wu + B_WAVES * e, KM_LOADS - 1);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 img, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
-                16, voff[e], ts * KM_TILE_BYTES, 0, 0);
+                16, voff[e], ts * KM_STRIDE, 0, 0);
         }
     };
     // Only tile copies are in flight in the loop: after tile t+1's come tile t+2's
@@ -331,27 +353,114 @@ __global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restr
     if (g == 0 && qi < n) mrow[static_cast<int64_t>(bh) * nrows + (qi - row0)] = m_run * sl2;
 }
 
+// Upper 16x16 block (I, J), I <= J, of a symmetric 64x64 matrix held as 10 MFMA accumulators.
+__device__ __forceinline__ constexpr int ublk(int I, int J) { return I * 4 - I * (I - 1) / 2 + (J - I); }
+
+// Solve (C + ridge) y = z for one query, one wave: blocked LDL^T in 16-column panels.
+//   ckk: the upper blocks of the SPD matrix in MFMA accumulator layout (lane (g, c)
+//        register r of ckk[ublk(I, J)] = entry (16 I + 4 g + r, 16 J + c)); overwritten.
+//   z: this lane's right-hand-side entry (row = lane).  Pivots <= thresh are dropped (their
+//        unknowns become zero).  Lt: this wave's LDS area, FD * (FD + 1) + FD floats.
+// Returns y[lane].  Each panel is eliminated lane-per-row (lane a holds the panel part of
+// row a, pivot rows broadcast by readlane) and its multipliers go to LDS as
+// Lt[P][a] = L[a][P]; the trailing blocks, still in the accumulators, take the update
+// L D L^T on the matrix cores (fp32); D L^T y = z is then solved backwards.
+__device__ __forceinline__ float ldl_solve_wave(float4v (&ckk)[10], float z, const float thresh, float* Lt,
+                                                const int lane, const int g, const int c) {
+    constexpr int ALD = FD + 1;
+    float* dvec = Lt + FD * ALD;
+    float dreg = 0.0f;   // lane P ends up holding the pivot d_P
+#pragma unroll
+    for (int K = 0; K < 4; ++K) {
+        // Stage block row K (rows 16K.., columns >= 16K) and read this lane's panel row:
+        // Lf[t] = C[a][16K + t] = C[16K + t][a].  Lanes a < 16K read stale words; their
+        // multipliers are zero below, so those never reach a live value.
+#pragma unroll
+        for (int J = K; J < 4; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Lt[(16 * K + 4 * g + r) * ALD + 16 * J + c] = ckk[ublk(K, J)][r];
+        LDS_FENCE();
+        float Lf[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Lf[t] = Lt[(16 * K + t) * ALD + lane];
+        LDS_FENCE();
+        // Eliminate the panel; Lf[p] becomes this row's multiplier L[a][16K + p].
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int P = 16 * K + p;
+            const float piv = lane_value(Lf[p], P);
+            float inv = __builtin_amdgcn_rcpf(piv);
+            inv = fmaf(inv, fmaf(-piv, inv, 1.0f), inv);   // one Newton step: ~0.5 ulp
+            inv = piv > thresh ? inv : 0.0f;
+            const float f = lane > P ? Lf[p] * inv : 0.0f;
+            z = fmaf(-f, lane_value(z, P), z);
+#pragma unroll
+            for (int t = p + 1; t < 16; ++t) Lf[t] = fmaf(-f, lane_value(Lf[t], P), Lf[t]);
+            dreg = lane == P ? piv : dreg;
+            Lf[p] = f;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Lt[(16 * K + t) * ALD + lane] = Lf[t];
+        dvec[lane] = dreg;
+        LDS_FENCE();
+        if (K < 3) {
+            // Trailing update C_IJ -= L_IK D_K L_JK^T for K < I <= J: 16x16x4 fp32 MFMAs over
+            // the panel columns 16K + 4s + g (K-slot g of step s).
+            float dv[4], Lo[4][4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                dv[s4] = dvec[16 * K + 4 * s4 + g];
+#pragma unroll
+                for (int X = K + 1; X < 4; ++X) Lo[X][s4] = Lt[(16 * K + 4 * s4 + g) * ALD + 16 * X + c];
+            }
+#pragma unroll
+            for (int I = K + 1; I < 4; ++I)
+#pragma unroll
+                for (int J = I; J < 4; ++J)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        ckk[ublk(I, J)] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            -Lo[I][s4], dv[s4] * Lo[J][s4], ckk[ublk(I, J)], 0, 0, 0);
+            LDS_FENCE();
+        }
+    }
+    // Back substitution D L^T y = z, column by column: row b of D L^T is d_b L[P][b].
+    float ul[FD];
+#pragma unroll
+    for (int P = 0; P < FD; ++P) ul[P] = Lt[lane * ALD + P] * dreg;
+    float ylane = 0.0f;
+#pragma unroll
+    for (int P = FD - 1; P >= 0; --P) {
+        const float dp = lane_value(dreg, P);
+        const float zp = lane_value(z, P);
+        const float yp = dp > thresh ? zp * __builtin_amdgcn_rcpf(dp) : 0.0f;
+        ylane = lane == P ? yp : ylane;
+        z = fmaf(-ul[P], yp, z);
+    }
+    return ylane;
+}
+
 __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ mrow,
     const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
     float* __restrict__ out,
-    int n, int row0, int BH, float sl2, float lambda) {
+    int n, int row0, int row1, int BH, float sl2, float lambda) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);   // the same value, as a scalar
     const int g = lane >> 4, c = lane & 15;
-    const int nrows = n - row0;
-    const int nblk = (nrows + B_WAVES - 1) / B_WAVES;
+    const int nrows = n - row0;   // rows of the row-max array
+    const int nblk = (row1 - row0 + B_WAVES - 1) / B_WAVES;
     int blk, bh;
     head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
 
     const int i0 = row0 + blk * B_WAVES;
     const int i = i0 + w;
-    const bool valid = i < n;
-    const int ic = min(i, n - 1);
-    const int last = min(i0 + B_WAVES - 1, n - 1);
+    const bool valid = i < row1;
+    const int ic = min(i, row1 - 1);
+    const int last = min(i0 + B_WAVES - 1, row1 - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
     const uint16_t* kh = k + base;
 
@@ -362,7 +471,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
             make_uint4(0, 0, 0, 0);
     }
     // Score operand: column c < B_WAVES is query i0 + c (the other columns are zero).
-    const int qcol = min(i0 + c, n - 1);
+    const int qcol = min(i0 + c, row1 - 1);
     const bool colv = c < B_WAVES;
     const float mcol = mrow[static_cast<int64_t>(bh) * nrows + (qcol - row0)];   // log2 units
     bf16x8 qf[2];
@@ -555,15 +664,9 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     for (int t = 0; t < B_WAVES; ++t) om2 += mq[2 * FD + t];
     const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
 
-    // ---- ridge-rescaled SPD solve: blocked LDL^T in 16-column panels.  Each panel is
-    // eliminated lane-per-row (lane a holds the panel part of row a, pivot rows broadcast by
-    // readlane); its multipliers L go to LDS; the trailing blocks of C_kk, still in the MFMA
-    // accumulators, take the update L D L^T on the matrix cores (fp32).  The LDS area holds
-    // Lt[P][a] = L[a][P] (also used to stage each panel), the pivots and y.
-    constexpr int ALD = FD + 1;
+    // ---- ridge-rescaled SPD solve (blocked LDL^T, this wave's LDS area), then b.
     float* Lt = reinterpret_cast<float*>(smem) + w * B_SOLVE_FLOATS;
-    float* dvec = Lt + FD * ALD;
-    float* yv = dvec + FD;
+    float* yv = Lt + FD * (FD + 1) + FD;
     // Rank-one downdates: C_kk -= S_k S_k^T / omega', C_vk^T -= S_k S_v^T / omega'.
     float4v skr[4];
     float skc[4], svc[4];
@@ -573,8 +676,6 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         skc[fb] = mq[fb * 16 + c];
         svc[fb] = mq[FD + fb * 16 + c];
     }
-    // Upper 16x16 block (I, J), I <= J, of C_kk is ckk[blk_idx(I, J)].
-    auto blk_idx = [](int I, int J) { return I * 4 - I * (I - 1) / 2 + (J - I); };
     const float m_x = mrow[static_cast<int64_t>(bh) * nrows + (ic - row0)];
     const float lam_s = lambda * exp2f(-m_x);
     float dmax = -INFINITY;
@@ -584,12 +685,12 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         for (int J = I; J < 4; ++J)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float val = fmaf(-skr[I][r], skc[J], ckk[blk_idx(I, J)][r]);
+                float val = fmaf(-skr[I][r], skc[J], ckk[ublk(I, J)][r]);
                 if (I == J && 4 * g + r == c) {   // diagonal entry: ridge
                     val += lam_s;
                     dmax = fmaxf(dmax, val);
                 }
-                ckk[blk_idx(I, J)][r] = val;
+                ckk[ublk(I, J)][r] = val;
             }
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb)
@@ -607,74 +708,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD;
     float z = fmaf(mq[lane], iom2, anc[lane]) - qa;
 
-    float dreg = 0.0f;   // lane P ends up holding the pivot d_P
-#pragma unroll
-    for (int K = 0; K < 4; ++K) {
-        // Stage block row K (rows 16K.., columns >= 16K) and read this lane's panel row:
-        // Lf[t] = C[a][16K + t] = C[16K + t][a].  Lanes a < 16K read stale words; their
-        // multipliers are zero below, so those never reach a live value.
-#pragma unroll
-        for (int J = K; J < 4; ++J)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Lt[(16 * K + 4 * g + r) * ALD + 16 * J + c] = ckk[blk_idx(K, J)][r];
-        LDS_FENCE();
-        float Lf[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) Lf[t] = Lt[(16 * K + t) * ALD + lane];
-        LDS_FENCE();
-        // Eliminate the panel; Lf[p] becomes this row's multiplier L[a][16K + p].
-#pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            const int P = 16 * K + p;
-            const float piv = lane_value(Lf[p], P);
-            float inv = __builtin_amdgcn_rcpf(piv);
-            inv = fmaf(inv, fmaf(-piv, inv, 1.0f), inv);   // one Newton step: ~0.5 ulp
-            inv = piv > thresh ? inv : 0.0f;
-            const float f = lane > P ? Lf[p] * inv : 0.0f;
-            z = fmaf(-f, lane_value(z, P), z);
-#pragma unroll
-            for (int t = p + 1; t < 16; ++t) Lf[t] = fmaf(-f, lane_value(Lf[t], P), Lf[t]);
-            dreg = lane == P ? piv : dreg;
-            Lf[p] = f;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) Lt[(16 * K + t) * ALD + lane] = Lf[t];
-        dvec[lane] = dreg;
-        LDS_FENCE();
-        if (K < 3) {
-            // Trailing update C_IJ -= L_IK D_K L_JK^T for K < I <= J: 16x16x4 fp32 MFMAs over
-            // the panel columns 16K + 4s + g (K-slot g of step s).
-            float dv[4], Lo[4][4];
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                dv[s4] = dvec[16 * K + 4 * s4 + g];
-#pragma unroll
-                for (int X = K + 1; X < 4; ++X) Lo[X][s4] = Lt[(16 * K + 4 * s4 + g) * ALD + 16 * X + c];
-            }
-#pragma unroll
-            for (int I = K + 1; I < 4; ++I)
-#pragma unroll
-                for (int J = I; J < 4; ++J)
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4)
-                        ckk[blk_idx(I, J)] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                            -Lo[I][s4], dv[s4] * Lo[J][s4], ckk[blk_idx(I, J)], 0, 0, 0);
-            LDS_FENCE();
-        }
-    }
-    // Back substitution D L^T y = z, column by column: row b of D L^T is d_b L[P][b].
-    float ul[FD];
-#pragma unroll
-    for (int P = 0; P < FD; ++P) ul[P] = Lt[lane * ALD + P] * dreg;
-    float ylane = 0.0f;
-#pragma unroll
-    for (int P = FD - 1; P >= 0; --P) {
-        const float dp = lane_value(dreg, P);
-        const float zp = lane_value(z, P);
-        const float yp = dp > thresh ? zp * __builtin_amdgcn_rcpf(dp) : 0.0f;
-        ylane = lane == P ? yp : ylane;
-        z = fmaf(-ul[P], yp, z);
-    }
+    const float ylane = ldl_solve_wave(ckk, z, thresh, Lt, lane, g, c);
     yv[lane] = ylane;
     LDS_FENCE();
 
@@ -697,6 +731,457 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
         float* orow = out + base + static_cast<int64_t>(i) * FD;
 #pragma unroll
         for (int fv = 0; fv < 4; ++fv) orow[fv * 16 + c] = fmaf(svc[fv], iom2, anc[FD + fv * 16 + c]) - part[fv];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Rows i >= 4d: the cross moment C_vk is never formed.  Pass 1 (lla_keymom_kernel) builds
+// the key moments and solves for y; pass 2 (lla_probe_kernel) applies C_vk to y in one
+// attention-like sweep:
+//   b_i = vbar_i - C_vk y_i = a_v + (1/omega') sum_j w_ij t_ij (v_j - a_v),
+//   t_ij = 1 + S_k.yh_i / omega' - (k_j - a).yh_i,   yh_i = omega' y_i,
+// because the weighted sum of k_j - kbar_i vanishes (the t_ij sum, weighted, to omega').
+// Both passes take the weights from bitwise the same score arithmetic.
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+constexpr int KQ = 4;                        // queries per wave of pass 1
+constexpr int K_BQ = B_WAVES * KQ;           // 16 queries per block: the score MFMA's columns
+constexpr int K_IMG = FD * M_LD * 2;         // fp16 key image of a tile (first half of the tile image)
+constexpr int K_LOADS = K_IMG / 1024;
+constexpr int K_WLOADS = (K_LOADS + B_WAVES - 1) / B_WAVES;
+constexpr int K_SW = K_IMG;                  // sqrt-weights [query][key], rows of M_LD halves
+constexpr int K_SW2 = K_SW + K_BQ * M_LD * 2;   // fp16 weights, 16 rows (rows >= K_BQ zero)
+constexpr int K_BUF = K_SW2 + 16 * M_LD * 2;
+constexpr int K_SOLVE_FLOATS = FD * (FD + 1) + FD;
+constexpr int K_SOLVE_BYTES = K_SOLVE_FLOATS * 4 * B_WAVES;
+constexpr int K_MEAN_OFF = K_SOLVE_BYTES > M_NBUF * K_BUF ? K_SOLVE_BYTES : M_NBUF * K_BUF;
+constexpr int K_SMEM = K_MEAN_OFF + (K_BQ * FD + B_WAVES * 16) * 4;
+constexpr int P_YLD = 2 * FD;                // per query: yh hi (fp16) | yh lo (fp16)
+constexpr int P_QSC = 4;                     // per query: gamma, 2^-e, 1/omega', unused
+static_assert(K_IMG % 1024 == 0, "key image must be whole wave copies");
+static_assert(K_BQ <= 16, "score MFMA has 16 query columns");
+
+// Pass 1.  Block = 4 waves x KQ queries = 16 consecutive queries; wave w owns queries
+// i0 + w + 4 qq (interleaved, so the causal tail splits evenly).  Per 64-key tile: scores of
+// key block w for all 16 queries (one bf16 MFMA pair), sqrt-weights and fp16 weights to LDS;
+// per 32-key half, each wave forms R = sqrt(w) (k - a) for its queries from the shared fp16
+// key image (one rounding) and accumulates C_kk = sum R R^T (10 upper blocks per query), and
+// the block sums S_k = sum w (k - a) of all 16 queries (one MFMA, features 16w..).  Then per
+// query: (C_kk - S_k S_k^T / omega' + lambda e^{-m} I) y = kbar - q, kbar = a + S_k / omega',
+// and the scaled solution yh 2^e = omega' y 2^e in [2^13, 2^14) goes out as fp16 hi + lo
+// parts with gamma = 1 + S_k.yh / omega'.
+__global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mrow,
+    const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
+    _Float16* __restrict__ yhl, float* __restrict__ qsc,
+    int n, int row0, int rowp, int BH, float sl2, float lambda) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int g = lane >> 4, c = lane & 15;
+    const int nrows = n - row0;   // rows of the row-max array
+    const int prows = n - rowp;   // rows of this path
+    const int nblk = (prows + K_BQ - 1) / K_BQ;
+    int blk, bh;
+    head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
+
+    const int i0 = rowp + blk * K_BQ;
+    const int last = min(i0 + K_BQ - 1, n - 1);
+    const int64_t base = static_cast<int64_t>(bh) * n * FD;
+    const uint16_t* kh = k + base;
+
+    if (K_BQ < 16) {   // rows K_BQ.. of every Sw2 buffer: the zero rows of the weight operand
+        for (int e = tid; e < M_NBUF * (16 - K_BQ) * M_LD / 8; e += 256) {
+            const int bsel = e / ((16 - K_BQ) * M_LD / 8), rem = e % ((16 - K_BQ) * M_LD / 8);
+            *reinterpret_cast<uint4*>(smem + bsel * K_BUF + K_SW2 + K_BQ * M_LD * 2 + rem * 16) =
+                make_uint4(0, 0, 0, 0);
+        }
+    }
+    // Score operand: column c < K_BQ is query i0 + c.
+    const int qcol = min(i0 + c, n - 1);
+    const bool colv = c < K_BQ;
+    const float mcol = mrow[static_cast<int64_t>(bh) * nrows + (qcol - row0)];   // log2 units
+    bf16x8 qf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (colv) raw = *reinterpret_cast<const uint4*>(q + base + static_cast<int64_t>(qcol) * FD + ks * 32 + 8 * g);
+        qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+
+    // Scores of key block w (16 keys) of a tile: lane (g, c) register r = query c, key
+    // 16w + 4g + r.  Issued before the tile's moments, stored after.  om2p sums the fp16
+    // weights of query c over this lane's keys.
+    float om2p = 0.0f;
+    const float hs = 0.5f * sl2, hm = 0.5f * mcol;
+    auto score_mfma = [&](uint4 kq0, uint4 kq1) {
+        float4v s = {0.f, 0.f, 0.f, 0.f};
+        s = mfma_bf16(__builtin_bit_cast(bf16x8, kq0), qf[0], s);
+        return mfma_bf16(__builtin_bit_cast(bf16x8, kq1), qf[1], s);
+    };
+    auto score_store = [&](float4v s, unsigned char* buf, int j0) {
+        float e[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) e[rr] = __builtin_amdgcn_exp2f(fmaf(s[rr], hs, -hm));
+        if (j0 + MT - 1 > i0) {   // block-uniform: keys past some query of the block
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) e[rr] = j0 + 16 * w + 4 * g + rr <= qcol ? e[rr] : 0.0f;
+        }
+        half4 sw4;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sw4[rr] = static_cast<_Float16>(e[rr]);
+        const half4 w4 = sw4 * sw4;
+        if (colv) {
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + K_SW) + c * M_LD + 16 * w + 4 * g) = sw4;
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + K_SW2) + c * M_LD + 16 * w + 4 * g) = w4;
+            const h16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+            om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 0, 1), one, om2p, false);
+            om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 2, 3), one, om2p, false);
+        }
+    };
+
+    float4v ckk[KQ][10];
+#pragma unroll
+    for (int qq = 0; qq < KQ; ++qq)
+#pragma unroll
+        for (int t = 0; t < 10; ++t) ckk[qq][t] = float4v{0.f, 0.f, 0.f, 0.f};
+    // S_k of the block's queries: lane (g, c) register r = query 4g + r, feature 16w + c.
+    float4v sk = {0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = (last + MT) / MT;
+    const int ptiles = (n + MT - 1) / MT;
+    // The key half of the head's tile images, copied straight into LDS (wave w takes KiB
+    // chunks w, w+4, w+8; every wave issues exactly K_WLOADS copies, surplus ones repeating
+    // the last chunk).  Score operand (key 16w + c, bf16) read through a buffer resource whose
+    // size ends at key n, so keys past n read as zero.
+    const __amdgpu_buffer_rsrc_t img = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(packed + static_cast<int64_t>(bh) * ptiles * PACK_TILE_BYTES)),
+        0, ptiles * PACK_TILE_BYTES, 0x00020000);
+    int voff[K_WLOADS];
+#pragma unroll
+    for (int e = 0; e < K_WLOADS; ++e) voff[e] = lane * 16 + min(wu + B_WAVES * e, K_LOADS - 1) * 1024;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(reinterpret_cast<const unsigned char*>(kh))), 0, n * FD * 2,
+        0x00020000);
+    const int kq_off = (16 * w + c) * FD * 2 + 16 * g;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    auto buf = [&](int tt) { return smem + (tt % M_NBUF) * K_BUF; };
+    auto issue = [&](int tt, uint4& q0, uint4& q1) {
+        const int ts = min(tt, ntiles - 1);
+        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % M_NBUF) * K_BUF);
+#pragma unroll
+        for (int e = 0; e < K_WLOADS; ++e) {
+            const int u = min(wu + B_WAVES * e, K_LOADS - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                img, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
+                16, voff[e], ts * PACK_TILE_BYTES, 0, 0);
+        }
+        q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off, ts * MT * FD * 2, 0));
+        q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off + 64, ts * MT * FD * 2, 0));
+    };
+    // After tile t+1's copies come its 2 operand loads and tile t+2's K_WLOADS + 2 loads.
+    static_assert(K_WLOADS + 4 < 16, "vmcnt operand is 4 bits here");
+    auto wait_tile = [] {
+        __builtin_amdgcn_s_waitcnt((K_WLOADS + 4) | (0x7 << 4) | (0xF << 8));
+        LDS_FENCE();
+    };
+    auto ring_barrier = [] {
+        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+        LDS_FENCE();
+        __builtin_amdgcn_s_barrier();
+        LDS_FENCE();
+    };
+    auto compute = [&](int t, const unsigned char* cur) {
+        const int j0 = t * MT;
+        const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
+        const _Float16* Sw = reinterpret_cast<const _Float16*>(cur + K_SW);
+        const _Float16* Sw2 = reinterpret_cast<const _Float16*>(cur + K_SW2);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            if (j0 + 32 * sub > last) break;   // block-uniform: past every query of the block
+            const int ko = 32 * sub + 8 * g;
+            half8 kf[4];
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) kf[fb] = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * M_LD + ko);
+            const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * M_LD + ko);
+            const half8 kw = wu == 0 ? kf[0] : wu == 1 ? kf[1] : wu == 2 ? kf[2] : kf[3];
+#pragma unroll
+            for (int qq = 0; qq < KQ; ++qq) {
+                const int iq = i0 + wu + 4 * qq;
+                if (iq < n && j0 + 32 * sub <= iq) {   // wave-uniform: keys of this query's prefix
+                    const half8 sw = *reinterpret_cast<const half8*>(Sw + (wu + 4 * qq) * M_LD + ko);
+                    half8 rk[4];
+#pragma unroll
+                    for (int fb = 0; fb < 4; ++fb) rk[fb] = kf[fb] * sw;
+                    int idx = 0;
+#pragma unroll
+                    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+                        for (int fb2 = fb; fb2 < 4; ++fb2) {
+                            ckk[qq][idx] = mfma_f16(rk[fb], rk[fb2], ckk[qq][idx]);
+                            ++idx;
+                        }
+                }
+            }
+            sk = mfma_f16(w8, kw, sk);
+        }
+    };
+    uint4 aq0, aq1, bq0, bq1;
+    issue(0, aq0, aq1);
+    issue(1, bq0, bq1);
+    wait_tile();
+    score_store(score_mfma(aq0, aq1), buf(0), 0);
+    ring_barrier();
+    for (int t = 0; t < ntiles; t += 2) {
+        const float4v sb = score_mfma(bq0, bq1);
+        issue(t + 2, aq0, aq1);
+        compute(t, buf(t));
+        if (t + 1 < ntiles) score_store(sb, buf(t + 1), (t + 1) * MT);
+        wait_tile();
+        ring_barrier();
+        if (t + 1 >= ntiles) break;
+        const float4v sa = score_mfma(aq0, aq1);
+        issue(t + 3, bq0, bq1);
+        compute(t + 1, buf(t + 1));
+        if (t + 2 < ntiles) score_store(sa, buf(t + 2), (t + 2) * MT);
+        wait_tile();
+        ring_barrier();
+    }
+    // Copies issued past the last tile may still be landing in ring buffers that the solve
+    // area overlaps: wait for this wave's loads (the barrier below covers the others).
+    __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
+    LDS_FENCE();
+
+    // ---- block sums -> LDS (outside the solve area)
+    float* skm = reinterpret_cast<float*>(smem + K_MEAN_OFF);   // [query][feature]
+    float* omp = skm + K_BQ * FD;                                // [wave][query]
+    om2p += __shfl_xor(om2p, 16);
+    om2p += __shfl_xor(om2p, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (4 * g + r < K_BQ) skm[(4 * g + r) * FD + 16 * w + c] = sk[r];
+    if (g == 0 && colv) omp[w * 16 + c] = om2p;
+    __syncthreads();
+
+    float* Lt = reinterpret_cast<float*>(smem) + w * K_SOLVE_FLOATS;
+    const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD;
+#pragma unroll
+    for (int qq = 0; qq < KQ; ++qq) {
+        const int ql = wu + 4 * qq;
+        const int iq = i0 + ql;
+        if (iq >= n) break;   // wave-uniform; later qq are further out
+        float om2 = 0.0f;
+#pragma unroll
+        for (int t = 0; t < B_WAVES; ++t) om2 += omp[t * 16 + ql];
+        const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
+        const float* mq = skm + ql * FD;
+        float4v skr[4];
+        float skc[4];
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) {
+            skr[fb] = *reinterpret_cast<const float4v*>(mq + fb * 16 + 4 * g) * iom2;
+            skc[fb] = mq[fb * 16 + c];
+        }
+        const float m_x = mrow[static_cast<int64_t>(bh) * nrows + (iq - row0)];
+        const float lam_s = lambda * exp2f(-m_x);
+        float dmax = -INFINITY;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int J = I; J < 4; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float val = fmaf(-skr[I][r], skc[J], ckk[qq][ublk(I, J)][r]);
+                    if (I == J && 4 * g + r == c) {   // diagonal entry: ridge
+                        val += lam_s;
+                        dmax = fmaxf(dmax, val);
+                    }
+                    ckk[qq][ublk(I, J)][r] = val;
+                }
+        dmax = wave_max_f(dmax);
+        const float thresh = lambda > 0.0f ? 0.0f : 1e-6f * dmax;
+        const float qa = bf16_bits_to_f32(q[base + static_cast<int64_t>(iq) * FD + lane]);
+        const float sk_l = mq[lane];
+        const float z = fmaf(sk_l, iom2, anc[lane]) - qa;
+        const float y = ldl_solve_wave(ckk[qq], z, thresh, Lt, lane, g, c);
+        // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together).
+        const float yh = y * om2;
+        const float amax = wave_max_f(fabsf(yh));
+        int ex = 0;
+        (void)frexpf(amax, &ex);
+        ex = max(ex, -100);   // keeps 2^(14 - ex) finite
+        const float sig = amax > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
+        const float ys = yh * sig;
+        const _Float16 hi = static_cast<_Float16>(ys);
+        const _Float16 lo = static_cast<_Float16>(ys - static_cast<float>(hi));
+        const float dot = wave_sum_f(sk_l * (static_cast<float>(hi) + static_cast<float>(lo)));
+        const int64_t qrow = static_cast<int64_t>(bh) * prows + (iq - rowp);
+        yhl[qrow * P_YLD + lane] = hi;
+        yhl[qrow * P_YLD + FD + lane] = lo;
+        if (lane == 0)
+            *reinterpret_cast<float4v*>(qsc + qrow * P_QSC) = float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, 0.0f};
+    }
+}
+
+// Pass 2.  Block = 8 waves x 16 queries; each 64-key tile (bf16 keys and fp16 centred keys,
+// both key-major, and fp16 centred values feature-major) streams through a ring of three LDS
+// buffers.  Per tile and wave, for key block kb (16 keys):
+//   S^T = K Q^T (bf16 MFMA pair: pass 1's operands in pass 1's order, so bitwise its scores),
+//   U^T = (K - a) (yh_hi + yh_lo)^T 2^e (four fp16 MFMAs),
+//   P = fp16(w (gamma - U 2^-e)) with w = fp16(sqrt-weight)^2 as in pass 1;
+// lane (g, c) register r holds key 16 kb + 4g + r of query c, which is already the A
+// operand of O += P (V - a_v) over 32-key steps (K-slots: keys 4g.., then 16 + 4g..).
+constexpr int P_WAVES = 8;
+constexpr int P_QW = 16;
+constexpr int P_QB = P_WAVES * P_QW;
+constexpr int P_BUF = 2 * KM_TILE_BYTES + FD * M_LD * 2;   // bf16 K | fp16 K - a | fp16 V - a_v
+constexpr int P_LOADS = P_BUF / 1024;
+constexpr int P_WLOADS = (P_LOADS + P_WAVES - 1) / P_WAVES;
+constexpr int P_SMEM = 3 * P_BUF;
+static_assert(P_BUF % 1024 == 0 && 2 * KM_TILE_BYTES % 1024 == 0, "probe images must be whole wave copies");
+
+__global__ __launch_bounds__(512, 1) void lla_probe_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
+    const unsigned char* __restrict__ packed, const unsigned char* __restrict__ kimg,
+    const _Float16* __restrict__ yhl, const float* __restrict__ qsc, float* __restrict__ out,
+    int n, int row0, int rowp, int BH, float sl2) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int g = lane >> 4, c = lane & 15;
+    const int nrows = n - row0, prows = n - rowp;
+    const int nblk = (prows + P_QB - 1) / P_QB;
+    int blk, bh;
+    head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
+    const int i0 = rowp + blk * P_QB;
+    const int qw0 = i0 + P_QW * wu;                   // this wave's first query
+    const int qc = min(qw0 + c, n - 1);               // column query of this lane
+    const int wave_last = min(qw0 + P_QW - 1, n - 1);
+    const int block_last = min(i0 + P_QB - 1, n - 1);
+    const int64_t base = static_cast<int64_t>(bh) * n * FD;
+    const int64_t qrow = static_cast<int64_t>(bh) * prows + (qc - rowp);
+
+    bf16x8 qf[2];
+    half8 yh[2], yl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + base + static_cast<int64_t>(qc) * FD + 32 * ks + 8 * g));
+        yh[ks] = *reinterpret_cast<const half8*>(yhl + qrow * P_YLD + 32 * ks + 8 * g);
+        yl[ks] = *reinterpret_cast<const half8*>(yhl + qrow * P_YLD + FD + 32 * ks + 8 * g);
+    }
+    const float4v sc = *reinterpret_cast<const float4v*>(qsc + qrow * P_QSC);
+    const float gam = sc[0], isig = sc[1];
+    const float hs = 0.5f * sl2, hm = 0.5f * mrow[static_cast<int64_t>(bh) * nrows + (qc - row0)];
+
+    const int ntiles = block_last / MT + 1;
+    const int ptiles = (n + MT - 1) / MT;
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(kimg + static_cast<int64_t>(bh) * ptiles * KM_STRIDE)), 0,
+        ptiles * KM_STRIDE, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(packed + static_cast<int64_t>(bh) * ptiles * PACK_TILE_BYTES)), 0,
+        ptiles * PACK_TILE_BYTES, 0x00020000);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    // Chunk u of a ring buffer: u < 18 from the key-major images, else from the value half
+    // of the tile image.  Wave w issues chunks w, w+8, w+16, w+24 (the last clamped to 26).
+    auto issue = [&](int tt) {
+        const int ts = min(tt, ntiles - 1);
+        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % 3) * P_BUF);
+#pragma unroll
+        for (int e = 0; e < P_WLOADS; ++e) {
+            const int u = min(wu + P_WAVES * e, P_LOADS - 1);
+            auto* ldst = reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024));
+            if (u < 2 * KM_TILE_BYTES / 1024)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, ldst, 16, lane * 16 + u * 1024, ts * KM_STRIDE, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, ldst, 16, lane * 16 + K_IMG + (u - 2 * KM_TILE_BYTES / 1024) * 1024,
+                                                         ts * PACK_TILE_BYTES, 0, 0);
+        }
+    };
+    // Loads complete in order: vmcnt <= P_WLOADS means all but the newest tile have landed.
+    static_assert(P_WLOADS < 16, "vmcnt operand is 4 bits here");
+    auto wait_and_sync = [] {
+        __builtin_amdgcn_s_waitcnt(P_WLOADS | (0x7 << 4) | (0x0 << 8));
+        LDS_FENCE();
+        __builtin_amdgcn_s_barrier();
+        LDS_FENCE();
+    };
+
+    float4v o[4];
+#pragma unroll
+    for (int fv = 0; fv < 4; ++fv) o[fv] = float4v{0.f, 0.f, 0.f, 0.f};
+    issue(0);
+    issue(1);
+    wait_and_sync();
+    for (int t = 0; t < ntiles; ++t) {
+        issue(t + 2);
+        const int j0 = t * MT;
+        if (j0 <= wave_last) {   // wave-uniform
+            const unsigned char* cur = smem + (t % 3) * P_BUF;
+            const unsigned char* KB = cur;
+            const unsigned char* KC = cur + KM_TILE_BYTES;
+            const _Float16* VI = reinterpret_cast<const _Float16*>(cur + 2 * KM_TILE_BYTES);
+            const bool full = j0 + MT - 1 <= qw0;   // every key below every query of the wave
+            half4 p[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int ro = (kb * 16 + c) * (KM_LD * 2) + 16 * g;
+                float4v s = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+                s = mfma_bf16(*reinterpret_cast<const bf16x8*>(KB + ro), qf[0], s);
+                s = mfma_bf16(*reinterpret_cast<const bf16x8*>(KB + ro + 64), qf[1], s);
+                const half8 c0 = *reinterpret_cast<const half8*>(KC + ro);
+                const half8 c1 = *reinterpret_cast<const half8*>(KC + ro + 64);
+                u = mfma_f16(c0, yh[0], u);
+                u = mfma_f16(c1, yh[1], u);
+                u = mfma_f16(c0, yl[0], u);
+                u = mfma_f16(c1, yl[1], u);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float e = __builtin_amdgcn_exp2f(fmaf(s[r], hs, -hm));
+                    if (!full) e = j0 + kb * 16 + 4 * g + r <= qc ? e : 0.0f;
+                    const _Float16 swh = static_cast<_Float16>(e);
+                    const _Float16 wv = swh * swh;
+                    p[kb][r] = static_cast<_Float16>(static_cast<float>(wv) * fmaf(-u[r], isig, gam));
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const half8 pa = __builtin_shufflevector(p[2 * ks], p[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int fv = 0; fv < 4; ++fv) {
+                    const _Float16* vr = VI + (fv * 16 + c) * M_LD + 32 * ks + 4 * g;
+                    const half4 v0 = *reinterpret_cast<const half4*>(vr);
+                    const half4 v1 = *reinterpret_cast<const half4*>(vr + 16);
+                    o[fv] = mfma_f16(pa, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), o[fv]);
+                }
+            }
+        }
+        wait_and_sync();
+    }
+    // Copies issued past the last tile are still landing in LDS: let them finish before exit.
+    __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
+
+    // Output rows: lane (g, c) register r = query qw0 + 4g + r, feature 16 fv + c.
+    const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD + FD;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = qw0 + 4 * g + r;
+        if (i < n) {
+            const float iom = qsc[(static_cast<int64_t>(bh) * prows + (i - rowp)) * P_QSC + 2];
+            float* orow = out + base + static_cast<int64_t>(i) * FD;
+#pragma unroll
+            for (int fv = 0; fv < 4; ++fv) orow[fv * 16 + c] = fmaf(o[fv][r], iom, anc[fv * 16 + c]);
+        }
     }
 }
 
@@ -915,25 +1400,31 @@ __global__ __launch_bounds__(256, 2) void lla_short_kernel(
     if (valid) out[base + static_cast<int64_t>(i) * FD + lane] = static_cast<float>(va - (acc - va * swu));
 }
 
+// Rows [0, 2d): fp64 short-row kernel; [2d, 4d): explicit moments; [4d, n): probe path.
 int fast_row0(int64_t n, int64_t d) { return static_cast<int>(n < 2 * d ? n : 2 * d); }
+int fast_rowp(int64_t n, int64_t d) { return static_cast<int>(n < 4 * d ? n : 4 * d); }
 
 // Fast-path workspace, each region 256-byte aligned:
 //   row maxima [B*H][n - 2d] | anchor partial sums [B*H][16][2d] | anchors [B*H][2d] |
-//   key/value tile images [B*H][tiles] | key-major key images [B*H][tiles].
+//   key/value tile images [B*H][tiles] | key-major key images (bf16, centred fp16)
+//   [B*H][tiles] | probe solutions (fp16 hi, lo) [B*H][n - 4d][2d] |
+//   probe scalars [B*H][n - 4d][4].
 struct FastLayout {
-    int64_t mrow, partial, anchors, packed, kimg, total;
+    int64_t mrow, partial, anchors, packed, kimg, yhl, qsc, total;
 };
 
 FastLayout fast_layout(int64_t BH, int64_t n, int64_t d) {
     auto up = [](int64_t bytes) { return (bytes + 255) & ~int64_t(255); };
-    const int64_t rows = n - fast_row0(n, d), tiles = (n + MT - 1) / MT;
+    const int64_t rows = n - fast_row0(n, d), prows = n - fast_rowp(n, d), tiles = (n + MT - 1) / MT;
     FastLayout L;
     L.mrow = 0;
     L.partial = L.mrow + up(BH * rows * 4);
     L.anchors = L.partial + up(BH * ANCHOR_SLICES * 2 * d * 4);
     L.packed = L.anchors + up(BH * 2 * d * 4);
     L.kimg = L.packed + BH * tiles * PACK_TILE_BYTES;
-    L.total = L.kimg + BH * tiles * KM_TILE_BYTES;
+    L.yhl = L.kimg + BH * tiles * KM_STRIDE;
+    L.qsc = L.yhl + up(BH * prows * P_YLD * 2);
+    L.total = L.qsc + up(BH * prows * P_QSC * 4);
     return L;
 }
 
@@ -965,6 +1456,12 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     std::call_once(attr_once, [] {
         attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_moments_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, B_SMEM);
+        if (attr_err == hipSuccess)
+            attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_keymom_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, K_SMEM);
+        if (attr_err == hipSuccess)
+            attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_probe_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
     });
     if (attr_err != hipSuccess) return attr_err;
 
@@ -982,6 +1479,9 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     float* anchors = reinterpret_cast<float*>(ws + L.anchors);
     unsigned char* packed = ws + L.packed;
     unsigned char* kimg = ws + L.kimg;
+    _Float16* yhl = reinterpret_cast<_Float16*>(ws + L.yhl);
+    float* qsc = reinterpret_cast<float*>(ws + L.qsc);
+    const int rowp = fast_rowp(p.n, p.d);
     const int ptiles = (n + MT - 1) / MT;
     prof_begin(p.stream, "lla_anchor_kernel");
     lla_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * ANCHOR_SLICES), dim3(256), 0, p.stream>>>(k, v, partial, n);
@@ -999,11 +1499,27 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
-    const unsigned blocks_b = static_cast<unsigned>(BH) * ((nrows + B_WAVES - 1) / B_WAVES);
-    prof_begin(p.stream, "lla_moments_kernel");
-    lla_moments_kernel<<<dim3(blocks_b), dim3(256), B_SMEM, p.stream>>>(
-        q, k, v, mrow, anchors, packed, p.out, n, row0, BH, sl2, static_cast<float>(p.lambda));
-    prof_end(p.stream);
+    if (rowp > row0) {
+        const unsigned blocks_b = static_cast<unsigned>(BH) * ((rowp - row0 + B_WAVES - 1) / B_WAVES);
+        prof_begin(p.stream, "lla_moments_kernel");
+        lla_moments_kernel<<<dim3(blocks_b), dim3(256), B_SMEM, p.stream>>>(
+            q, k, v, mrow, anchors, packed, p.out, n, row0, rowp, BH, sl2, static_cast<float>(p.lambda));
+        prof_end(p.stream);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (n > rowp) {
+        const unsigned blocks_k = static_cast<unsigned>(BH) * ((n - rowp + K_BQ - 1) / K_BQ);
+        prof_begin(p.stream, "lla_keymom_kernel");
+        lla_keymom_kernel<<<dim3(blocks_k), dim3(256), K_SMEM, p.stream>>>(
+            q, k, mrow, anchors, packed, yhl, qsc, n, row0, rowp, BH, sl2, static_cast<float>(p.lambda));
+        prof_end(p.stream);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        const unsigned blocks_p = static_cast<unsigned>(BH) * ((n - rowp + P_QB - 1) / P_QB);
+        prof_begin(p.stream, "lla_probe_kernel");
+        lla_probe_kernel<<<dim3(blocks_p), dim3(P_WAVES * 64), P_SMEM, p.stream>>>(
+            q, mrow, anchors, packed, kimg, yhl, qsc, p.out, n, row0, rowp, BH, sl2);
+        prof_end(p.stream);
+    }
     return hipGetLastError();
 }
 

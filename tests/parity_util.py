@@ -63,3 +63,19 @@ def workload_arrays(name, **shape):
         w = w.with_shape(**shape)
     q, k, v, _ = lla_inputs.generate(w)
     return w, q, k, v
+
+
+def fast_workspace_bytes(BH, n, d=64):
+    """Scratch bytes of the bf16 matrix-core path, region by region (each rounded up to
+    256 B where the library rounds it): row maxima of rows >= 2d, anchor partial sums,
+    anchors, then per head and 64-key tile the fp16 K/V image (72-half rows) and the two
+    key-major key images (bf16, centred fp16), then per probe row (rows >= 4d) the fp16
+    hi/lo solution and four scalars."""
+    up = lambda x: (x + 255) // 256 * 256
+    tiles = -(-n // 64)
+    prows = n - min(n, 4 * d)
+    if n - min(n, 2 * d) <= 0:
+        return 0
+    return (up(BH * (n - 2 * d) * 4) + up(BH * 16 * 2 * d * 4) + up(BH * 2 * d * 4)
+            + BH * tiles * (2 * d * 72 * 2 + 2 * 64 * 72 * 2)
+            + up(BH * prows * 2 * d * 2) + up(BH * prows * 4 * 4))

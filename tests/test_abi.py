@@ -117,16 +117,11 @@ def test_path_availability_query():
 
 def test_workspace_size():
     from local_linear_attention_amd import lla
-    # fast path: row maxima, anchor partial sums, anchors (each region rounded up to 256 B),
-    # then per head and 64-key tile the fp16 K/V image (72-half rows) and the key-major keys
-    def fast_bytes(BH, n, d=64):
-        up = lambda x: (x + 255) // 256 * 256
-        tiles = -(-n // 64)
-        return (up(BH * (n - 2 * d) * 4) + up(BH * 16 * 2 * d * 4) + up(BH * 2 * d * 4)
-                + BH * tiles * (2 * d * 72 * 2 + 64 * 72 * 2))
+    from parity_util import fast_workspace_bytes as fast_bytes
     assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "fast") == fast_bytes(32, 4096)
     assert lla.lla_workspace_size(2, 16, 4096, 64, "bf16", "auto") == fast_bytes(32, 4096)
     assert lla.lla_workspace_size(1, 1, 130, 64, "bf16", "fast") == fast_bytes(1, 130)
+    assert lla.lla_workspace_size(1, 3, 300, 64, "bf16", "fast") == fast_bytes(3, 300)
     # beyond the fast path's sequence limit AUTO falls back to the exact path (no scratch)
     assert lla.lla_workspace_size(1, 1, (1 << 22) + 1, 64, "bf16", "fast") == 0
     assert lla.lla_workspace_size(1, 1, (1 << 22) + 1, 64, "bf16", "auto") == 0

@@ -84,10 +84,8 @@ def test_fast_path_workspace_entry_point_matches():
     w, q, k, v = workload_arrays("d24", B=2, H=2, n=400)
     tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
     nbytes = lla_workspace_size(w.B, w.H, w.n, w.d, "bf16", "fast")
-    up = lambda x: (x + 255) // 256 * 256
-    BH, ntiles = w.B * w.H, -(-w.n // 64)
-    assert nbytes == (up(BH * (w.n - 2 * w.d) * 4) + up(BH * 16 * 2 * w.d * 4) + up(BH * 2 * w.d * 4)
-                      + BH * ntiles * (2 * w.d * 72 * 2 + 64 * 72 * 2))
+    from parity_util import fast_workspace_bytes
+    assert nbytes == fast_workspace_bytes(w.B * w.H, w.n, w.d)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a = lla_forward_ws(tq, tk, tv, w.h, w.lam, ws, path="fast")
     b = lla_forward_ex(tq, tk, tv, w.h, w.lam, path="fast")
@@ -111,7 +109,8 @@ def test_profiling_records_each_kernel():
     finally:
         lla_profile_enable(False)
     assert [name for name, _ in rec] == ["lla_short_kernel", "lla_anchor_kernel", "lla_pack_kernel",
-                                         "lla_rowmax_kernel", "lla_moments_kernel"]
+                                         "lla_rowmax_kernel", "lla_moments_kernel", "lla_keymom_kernel",
+                                         "lla_probe_kernel"]
     assert all(ms > 0 for _, ms in rec)
 
 
