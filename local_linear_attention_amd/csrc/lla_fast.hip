@@ -389,14 +389,15 @@ __device__ __forceinline__ float ldl_solve_wave(float4v (&ckk)[10], float z, con
         for (int p = 0; p < 16; ++p) {
             const int P = 16 * K + p;
             const float piv = lane_value(Lf[p], P);
-            float inv = __builtin_amdgcn_rcpf(piv);
-            inv = fmaf(inv, fmaf(-piv, inv, 1.0f), inv);   // one Newton step: ~0.5 ulp
-            inv = piv > thresh ? inv : 0.0f;
-            const float f = lane > P ? Lf[p] * inv : 0.0f;
+            // Reciprocal pivot (about 1 ulp); a dropped pivot gets a zero column of L.
+            const float inv = piv > thresh ? __builtin_amdgcn_rcpf(piv) : 0.0f;
+            int row = lane;
+            asm volatile("" : "+v"(row));   // row test per step: no precomputed lane masks
+            const float f = row > P ? Lf[p] * inv : 0.0f;
             z = fmaf(-f, lane_value(z, P), z);
 #pragma unroll
             for (int t = p + 1; t < 16; ++t) Lf[t] = fmaf(-f, lane_value(Lf[t], P), Lf[t]);
-            dreg = lane == P ? piv : dreg;
+            dreg = row == P ? piv : dreg;
             Lf[p] = f;
         }
 #pragma unroll
@@ -424,20 +425,15 @@ __device__ __forceinline__ float ldl_solve_wave(float4v (&ckk)[10], float z, con
             LDS_FENCE();
         }
     }
-    // Back substitution D L^T y = z, column by column: row b of D L^T is d_b L[P][b].
-    float ul[FD];
+    // Back substitution L^T y = x with x = D^{-1} z (zero at dropped pivots), from the last
+    // column: y_P = x_P, then x_a -= L[P][a] y_P, where L[P][a] = Lt[a][P] is zero unless
+    // P > a.  Each x_a is final once its own step has passed, so x ends as y.
+    float inv_d = __builtin_amdgcn_rcpf(dreg);
+    inv_d = fmaf(inv_d, fmaf(-dreg, inv_d, 1.0f), inv_d);   // one Newton step: ~0.5 ulp
+    float x = dreg > thresh ? z * inv_d : 0.0f;
 #pragma unroll
-    for (int P = 0; P < FD; ++P) ul[P] = Lt[lane * ALD + P] * dreg;
-    float ylane = 0.0f;
-#pragma unroll
-    for (int P = FD - 1; P >= 0; --P) {
-        const float dp = lane_value(dreg, P);
-        const float zp = lane_value(z, P);
-        const float yp = dp > thresh ? zp * __builtin_amdgcn_rcpf(dp) : 0.0f;
-        ylane = lane == P ? yp : ylane;
-        z = fmaf(-ul[P], yp, z);
-    }
-    return ylane;
+    for (int P = FD - 1; P >= 0; --P) x = fmaf(-Lt[lane * ALD + P], lane_value(x, P), x);
+    return x;
 }
 
 __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
@@ -742,15 +738,33 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 //   t_ij = 1 + S_k.yh_i / omega' - (k_j - a).yh_i,   yh_i = omega' y_i,
 // because the weighted sum of k_j - kbar_i vanishes (the t_ij sum, weighted, to omega').
 // Both passes take the weights from bitwise the same score arithmetic.
+// x moved within each row of 16 lanes by a DPP pattern (quad_perm, row_mirror, ...).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
+// Reductions over the 16 lanes of each row (every lane gets its row's result), then over
+// the wave through the four row leaders.
+__device__ __forceinline__ float row_max_f(float x) {
+    x = fmaxf(x, dpp_f<DPP_QUAD_1032>(x));
+    x = fmaxf(x, dpp_f<DPP_QUAD_2301>(x));
+    x = fmaxf(x, dpp_f<DPP_ROW_HALF_MIRROR>(x));
+    return fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
+}
+__device__ __forceinline__ float row_sum_f(float x) {
+    x += dpp_f<DPP_QUAD_1032>(x);
+    x += dpp_f<DPP_QUAD_2301>(x);
+    x += dpp_f<DPP_ROW_HALF_MIRROR>(x);
+    return x + dpp_f<DPP_ROW_MIRROR>(x);
+}
 __device__ __forceinline__ float wave_max_f(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+    x = row_max_f(x);
+    return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 __device__ __forceinline__ float wave_sum_f(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    x = row_sum_f(x);
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 
 constexpr int KQ = 4;                        // queries per wave of pass 1
