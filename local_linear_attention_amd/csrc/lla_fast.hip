@@ -775,7 +775,9 @@ constexpr int K_WLOADS = (K_LOADS + B_WAVES - 1) / B_WAVES;
 constexpr int K_SW = K_IMG;                  // sqrt-weights [query][key], rows of M_LD halves
 constexpr int K_SW2 = K_SW + K_BQ * M_LD * 2;   // fp16 weights, 16 rows (rows >= K_BQ zero)
 constexpr int K_BUF = K_SW2 + 16 * M_LD * 2;
-constexpr int K_SOLVE_FLOATS = FD * (FD + 1) + FD;
+constexpr int GS_LD = 68;                    // solve staging: row stride (floats)
+constexpr int GS_QS = 16 * GS_LD + 16;       // query stride: the 4 queries' rows on distinct banks
+constexpr int K_SOLVE_FLOATS = KQ * GS_QS + KQ * FD;   // per wave: staging + pivots
 constexpr int K_SOLVE_BYTES = K_SOLVE_FLOATS * 4 * B_WAVES;
 constexpr int K_MEAN_OFF = K_SOLVE_BYTES > M_NBUF * K_BUF ? K_SOLVE_BYTES : M_NBUF * K_BUF;
 constexpr int K_SMEM = K_MEAN_OFF + (K_BQ * FD + B_WAVES * 16) * 4;
@@ -783,6 +785,177 @@ constexpr int P_YLD = 2 * FD;                // per query: yh hi (fp16) | yh lo 
 constexpr int P_QSC = 4;                     // per query: gamma, 2^-e, 1/omega', unused
 static_assert(K_IMG % 1024 == 0, "key image must be whole wave copies");
 static_assert(K_BQ <= 16, "score MFMA has 16 query columns");
+
+// Lane p of each row of 16 lanes, broadcast to its row (p a compile-time lane).
+__device__ __forceinline__ float row_bcast(float x, int p) {
+    const int xi = __builtin_bit_cast(int, x);
+    int r;
+    switch (p) {
+        case 0: r = __builtin_amdgcn_update_dpp(0, xi, 0x150, 0xF, 0xF, false); break;
+        case 1: r = __builtin_amdgcn_update_dpp(0, xi, 0x151, 0xF, 0xF, false); break;
+        case 2: r = __builtin_amdgcn_update_dpp(0, xi, 0x152, 0xF, 0xF, false); break;
+        case 3: r = __builtin_amdgcn_update_dpp(0, xi, 0x153, 0xF, 0xF, false); break;
+        case 4: r = __builtin_amdgcn_update_dpp(0, xi, 0x154, 0xF, 0xF, false); break;
+        case 5: r = __builtin_amdgcn_update_dpp(0, xi, 0x155, 0xF, 0xF, false); break;
+        case 6: r = __builtin_amdgcn_update_dpp(0, xi, 0x156, 0xF, 0xF, false); break;
+        case 7: r = __builtin_amdgcn_update_dpp(0, xi, 0x157, 0xF, 0xF, false); break;
+        case 8: r = __builtin_amdgcn_update_dpp(0, xi, 0x158, 0xF, 0xF, false); break;
+        case 9: r = __builtin_amdgcn_update_dpp(0, xi, 0x159, 0xF, 0xF, false); break;
+        case 10: r = __builtin_amdgcn_update_dpp(0, xi, 0x15A, 0xF, 0xF, false); break;
+        case 11: r = __builtin_amdgcn_update_dpp(0, xi, 0x15B, 0xF, 0xF, false); break;
+        case 12: r = __builtin_amdgcn_update_dpp(0, xi, 0x15C, 0xF, 0xF, false); break;
+        case 13: r = __builtin_amdgcn_update_dpp(0, xi, 0x15D, 0xF, 0xF, false); break;
+        case 14: r = __builtin_amdgcn_update_dpp(0, xi, 0x15E, 0xF, 0xF, false); break;
+        default: r = __builtin_amdgcn_update_dpp(0, xi, 0x15F, 0xF, 0xF, false); break;
+    }
+    return __builtin_bit_cast(float, r);
+}
+
+// Solve (C_q + ridge) y_q = z_q for the KQ = 4 queries of a wave at once: LDL^T in 16-column
+// panels with the rows of query G on lanes 16 G .. 16 G + 15 (lane 16 G + l holds rows
+// l + 16 j, j = 0..3), pivot rows broadcast within each row of 16 lanes.
+//   The matrix of query q is C_q - s_q s_q^T / omega'_q + lam[q] I, where
+//   ckk[q]: the upper 16x16 blocks of C_q in MFMA accumulator layout (lane (g, c) register r
+//           of ckk[q][ublk(I, J)] = entry (16 I + 4 g + r, 16 J + c)); consumed;
+//   skq: s of this lane's query (LDS, 64 floats); sks[j] = s[l + 16 j] / omega'.
+//   zr[j]: right-hand side of row l + 16 j of this lane's query (updated).
+//   thr: pivots <= thr are dropped, their unknowns set to zero.
+//   Sg: this wave's LDS area of K_SOLVE_FLOATS floats.
+// Panel K is staged from the accumulators to the row layout through LDS, eliminated there,
+// and its multipliers go back through LDS as MFMA operands for the trailing update
+// C_IJ -= L_IK D_K L_JK^T (fp32 16x16x4 MFMAs, per query) of the blocks still in the
+// accumulators; the multipliers stay in registers for the back substitution, which forms
+// each y_P as x_P minus a row-of-16 reduction.  Returns y in yr[j].
+// Panel K of group_solve (a template, so that every register index is a constant).
+template <int K>
+__device__ __forceinline__ void group_panel(float4v (&ckk)[KQ][10], float (&zr)[4], const float thr,
+                                            const float (&lam)[KQ], const float (&sks)[4], const float* skq,
+                                            float* Sg, float (&Lk)[4][4][16], float (&dk)[4], const int g,
+                                            const int c) {
+    const int G = g, l = c;   // row layout: query G, row offset l
+    float* Dg = Sg + KQ * GS_QS;
+    // Block row K of every query, ridge on the diagonal: Sg[q][t][col] = C_q[16 K + t][col].
+#pragma unroll
+    for (int q = 0; q < KQ; ++q)
+#pragma unroll
+        for (int J = K; J < 4; ++J)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float val = ckk[q][ublk(K, J)][r];
+                if (J == K) val += 4 * g + r == c ? lam[q] : 0.0f;
+                Sg[q * GS_QS + (4 * g + r) * GS_LD + 16 * J + c] = val;
+            }
+    LDS_FENCE();
+    // Panel rows of this lane's query: Lf[j][t] = C[16 K + t][l + 16 j] = C[l + 16 j][16 K + t].
+    float Lf[4][16];
+#pragma unroll
+    for (int j = K; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Lf[j][t] = Sg[G * GS_QS + t * GS_LD + 16 * j + l];
+    LDS_FENCE();
+    // Rank-one downdate, applied to each entry once, as its panel is staged (the trailing
+    // updates are linear, so it commutes with them): C -= S_k S_k^T / omega'.
+    float skt[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) skt[t] = skq[16 * K + t];
+#pragma unroll
+    for (int j = K; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Lf[j][t] = fmaf(-sks[j], skt[t], Lf[j][t]);
+    float d = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const float piv = row_bcast(Lf[K][p], p);
+        // Reciprocal pivot (about 1 ulp); a dropped pivot gets a zero column of L.
+        const float inv = piv > thr ? __builtin_amdgcn_rcpf(piv) : 0.0f;
+        int row = l;
+        asm volatile("" : "+v"(row));   // row tests per step: no precomputed lane masks
+        float f[4];
+#pragma unroll
+        for (int j = K + 1; j < 4; ++j) f[j] = Lf[j][p] * inv;
+        f[K] = row > p ? Lf[K][p] * inv : 0.0f;
+        const float zp = row_bcast(zr[K], p);
+#pragma unroll
+        for (int j = K; j < 4; ++j) zr[j] = fmaf(-f[j], zp, zr[j]);
+#pragma unroll
+        for (int t = p + 1; t < 16; ++t) {
+            const float bt = row_bcast(Lf[K][t], p);
+#pragma unroll
+            for (int j = K; j < 4; ++j) Lf[j][t] = fmaf(-f[j], bt, Lf[j][t]);
+        }
+        d = row == p ? piv : d;
+#pragma unroll
+        for (int j = K; j < 4; ++j) Lf[j][p] = f[j];
+    }
+    dk[K] = d;
+#pragma unroll
+    for (int j = K; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Lk[K][j][t] = Lf[j][t];
+    if (K < 3) {
+        // Multipliers of the later blocks' rows and the pivots, read back per query as
+        // MFMA operands over the panel columns 16 K + 4 s + g (K-slot g of step s).
+#pragma unroll
+        for (int j = K + 1; j < 4; ++j)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) Sg[G * GS_QS + t * GS_LD + 16 * j + l] = Lf[j][t];
+        Dg[G * FD + 16 * K + l] = d;
+        LDS_FENCE();
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+            float dv[4], Lo[4][4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                dv[s4] = Dg[q * FD + 16 * K + 4 * s4 + g];
+#pragma unroll
+                for (int X = K + 1; X < 4; ++X) Lo[X][s4] = Sg[q * GS_QS + (4 * s4 + g) * GS_LD + 16 * X + c];
+            }
+#pragma unroll
+            for (int I = K + 1; I < 4; ++I)
+#pragma unroll
+                for (int J = I; J < 4; ++J)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        ckk[q][ublk(I, J)] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            -Lo[I][s4], dv[s4] * Lo[J][s4], ckk[q][ublk(I, J)], 0, 0, 0);
+        }
+        LDS_FENCE();
+    }
+}
+
+__device__ __forceinline__ void group_solve(float4v (&ckk)[KQ][10], float (&zr)[4], const float thr,
+                                            const float (&lam)[KQ], const float (&sks)[4], const float* skq,
+                                            float* Sg, float (&yr)[4], const int g, const int c) {
+    float Lk[4][4][16];       // Lk[K][j][t] = L[l + 16 j][16 K + t], j >= K
+    float dk[4];              // pivot of row l + 16 K
+    group_panel<0>(ckk, zr, thr, lam, sks, skq, Sg, Lk, dk, g, c);
+    group_panel<1>(ckk, zr, thr, lam, sks, skq, Sg, Lk, dk, g, c);
+    group_panel<2>(ckk, zr, thr, lam, sks, skq, Sg, Lk, dk, g, c);
+    group_panel<3>(ckk, zr, thr, lam, sks, skq, Sg, Lk, dk, g, c);
+    const int l = c;
+    // Back substitution L^T y = x, x = D^{-1} z (zero at dropped pivots), from the last row:
+    // y_P = x_P - sum_{b > P} L[b][P] y_b, the sum over this query's 16 lanes.  L[b][P] is
+    // zero for rows b <= P of the diagonal block, and y of rows not yet solved is zero.
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float inv_d = __builtin_amdgcn_rcpf(dk[j]);
+        inv_d = fmaf(inv_d, fmaf(-dk[j], inv_d, 1.0f), inv_d);   // one Newton step: ~0.5 ulp
+        x[j] = dk[j] > thr ? zr[j] * inv_d : 0.0f;
+        yr[j] = 0.0f;
+    }
+#pragma unroll
+    for (int P = FD - 1; P >= 0; --P) {
+        const int jP = P / 16, p = P % 16;
+        float part = 0.0f;
+#pragma unroll
+        for (int j = jP; j < 4; ++j) part = fmaf(Lk[jP][j][p], yr[j], part);
+        const float sum = row_sum_f(part);
+        int row = l;
+        asm volatile("" : "+v"(row));
+        yr[jP] = row == p ? x[jP] - sum : yr[jP];
+    }
+}
 
 // Pass 1.  Block = 4 waves x KQ queries = 16 consecutive queries; wave w owns queries
 // i0 + w + 4 qq (interleaved, so the causal tail splits evenly).  Per 64-key tile: scores of
@@ -987,62 +1160,91 @@ __global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
     if (g == 0 && colv) omp[w * 16 + c] = om2p;
     __syncthreads();
 
-    float* Lt = reinterpret_cast<float*>(smem) + w * K_SOLVE_FLOATS;
+    // ---- the 4 solves at once; row layout: lane 16 G + l holds rows l + 16 j of query
+    // i0 + wu + 4 G (a query past n is solved but not stored).  z = kbar - q with
+    // kbar = a + S_k / omega'.
+    float* Sg = reinterpret_cast<float*>(smem) + w * K_SOLVE_FLOATS;
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD;
+    float lam_q[KQ];
 #pragma unroll
     for (int qq = 0; qq < KQ; ++qq) {
-        const int ql = wu + 4 * qq;
-        const int iq = i0 + ql;
-        if (iq >= n) break;   // wave-uniform; later qq are further out
-        float om2 = 0.0f;
+        const int iq = min(i0 + wu + 4 * qq, n - 1);
+        lam_q[qq] = lambda * exp2f(-mrow[static_cast<int64_t>(bh) * nrows + (iq - row0)]);
+    }
+    const int G = g, l = c;
+    const int qlG = wu + 4 * G;
+    const int iqG = i0 + qlG;
+    const int iqc = min(iqG, n - 1);
+    float om2 = 0.0f;
 #pragma unroll
-        for (int t = 0; t < B_WAVES; ++t) om2 += omp[t * 16 + ql];
-        const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
-        const float* mq = skm + ql * FD;
-        float4v skr[4];
-        float skc[4];
+    for (int t = 0; t < B_WAVES; ++t) om2 += omp[t * 16 + qlG];
+    const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
+    const float* mqG = skm + qlG * FD;
+    float zr[4], skv[4], sks[4], yr[4];
 #pragma unroll
-        for (int fb = 0; fb < 4; ++fb) {
-            skr[fb] = *reinterpret_cast<const float4v*>(mq + fb * 16 + 4 * g) * iom2;
-            skc[fb] = mq[fb * 16 + c];
-        }
-        const float m_x = mrow[static_cast<int64_t>(bh) * nrows + (iq - row0)];
-        const float lam_s = lambda * exp2f(-m_x);
-        float dmax = -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+        const int a = l + 16 * j;
+        skv[j] = mqG[a];
+        sks[j] = skv[j] * iom2;
+        zr[j] = fmaf(skv[j], iom2, anc[a]) - bf16_bits_to_f32(q[base + static_cast<int64_t>(iqc) * FD + a]);
+    }
+    // lambda > 0: drop only pivots that rounding made non-positive; lambda = 0: also drop
+    // directions the prefix leaves (numerically) undetermined, below 1e-6 of the largest
+    // diagonal entry of the (downdated) matrix.
+    float thr = 0.0f;
+    if (!(lambda > 0.0f)) {
+        float dm[KQ];
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+        for (int qq = 0; qq < KQ; ++qq) {
+            const float* mq = skm + (wu + 4 * qq) * FD;
+            float oq = 0.0f;
 #pragma unroll
-            for (int J = I; J < 4; ++J)
+            for (int t = 0; t < B_WAVES; ++t) oq += omp[t * 16 + wu + 4 * qq];
+            float dmax = -INFINITY;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float val = fmaf(-skr[I][r], skc[J], ckk[qq][ublk(I, J)][r]);
-                    if (I == J && 4 * g + r == c) {   // diagonal entry: ridge
-                        val += lam_s;
-                        dmax = fmaxf(dmax, val);
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r == c) {
+                        const float sv = mq[16 * I + c];
+                        dmax = fmaxf(dmax, ckk[qq][ublk(I, I)][r] - sv * sv / oq + lam_q[qq]);
                     }
-                    ckk[qq][ublk(I, J)][r] = val;
-                }
-        dmax = wave_max_f(dmax);
-        const float thresh = lambda > 0.0f ? 0.0f : 1e-6f * dmax;
-        const float qa = bf16_bits_to_f32(q[base + static_cast<int64_t>(iq) * FD + lane]);
-        const float sk_l = mq[lane];
-        const float z = fmaf(sk_l, iom2, anc[lane]) - qa;
-        const float y = ldl_solve_wave(ckk[qq], z, thresh, Lt, lane, g, c);
-        // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together).
-        const float yh = y * om2;
-        const float amax = wave_max_f(fabsf(yh));
-        int ex = 0;
-        (void)frexpf(amax, &ex);
-        ex = max(ex, -100);   // keeps 2^(14 - ex) finite
-        const float sig = amax > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
-        const float ys = yh * sig;
-        const _Float16 hi = static_cast<_Float16>(ys);
-        const _Float16 lo = static_cast<_Float16>(ys - static_cast<float>(hi));
-        const float dot = wave_sum_f(sk_l * (static_cast<float>(hi) + static_cast<float>(lo)));
-        const int64_t qrow = static_cast<int64_t>(bh) * prows + (iq - rowp);
-        yhl[qrow * P_YLD + lane] = hi;
-        yhl[qrow * P_YLD + FD + lane] = lo;
-        if (lane == 0)
+            dm[qq] = wave_max_f(dmax);
+        }
+        thr = 1e-6f * (G == 0 ? dm[0] : G == 1 ? dm[1] : G == 2 ? dm[2] : dm[3]);
+    }
+    group_solve(ckk, zr, thr, lam_q, sks, mqG, Sg, yr, g, c);
+    // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together), and
+    // gamma = 1 + S_k . yh / omega'.
+    float yh[4], amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        yh[j] = yr[j] * om2;
+        amax = fmaxf(amax, fabsf(yh[j]));
+    }
+    amax = row_max_f(amax);
+    int ex = 0;
+    (void)frexpf(amax, &ex);
+    ex = max(ex, -100);   // keeps 2^(14 - ex) finite
+    const float sig = amax > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
+    _Float16 hi[4], lo[4];
+    float dot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float ys = yh[j] * sig;
+        hi[j] = static_cast<_Float16>(ys);
+        lo[j] = static_cast<_Float16>(ys - static_cast<float>(hi[j]));
+        dot = fmaf(skv[j], static_cast<float>(hi[j]) + static_cast<float>(lo[j]), dot);
+    }
+    dot = row_sum_f(dot);
+    if (iqG < n) {
+        const int64_t qrow = static_cast<int64_t>(bh) * prows + (iqG - rowp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            yhl[qrow * P_YLD + l + 16 * j] = hi[j];
+            yhl[qrow * P_YLD + FD + l + 16 * j] = lo[j];
+        }
+        if (l == 0)
             *reinterpret_cast<float4v*>(qsc + qrow * P_QSC) = float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, 0.0f};
     }
 }
