@@ -741,7 +741,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
 // x moved within each row of 16 lanes by a DPP pattern (quad_perm, row_mirror, ...).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
 // Reductions over the 16 lanes of each row (every lane gets its row's result), then over
@@ -791,22 +791,22 @@ __device__ __forceinline__ float row_bcast(float x, int p) {
     const int xi = __builtin_bit_cast(int, x);
     int r;
     switch (p) {
-        case 0: r = __builtin_amdgcn_update_dpp(0, xi, 0x150, 0xF, 0xF, false); break;
-        case 1: r = __builtin_amdgcn_update_dpp(0, xi, 0x151, 0xF, 0xF, false); break;
-        case 2: r = __builtin_amdgcn_update_dpp(0, xi, 0x152, 0xF, 0xF, false); break;
-        case 3: r = __builtin_amdgcn_update_dpp(0, xi, 0x153, 0xF, 0xF, false); break;
-        case 4: r = __builtin_amdgcn_update_dpp(0, xi, 0x154, 0xF, 0xF, false); break;
-        case 5: r = __builtin_amdgcn_update_dpp(0, xi, 0x155, 0xF, 0xF, false); break;
-        case 6: r = __builtin_amdgcn_update_dpp(0, xi, 0x156, 0xF, 0xF, false); break;
-        case 7: r = __builtin_amdgcn_update_dpp(0, xi, 0x157, 0xF, 0xF, false); break;
-        case 8: r = __builtin_amdgcn_update_dpp(0, xi, 0x158, 0xF, 0xF, false); break;
-        case 9: r = __builtin_amdgcn_update_dpp(0, xi, 0x159, 0xF, 0xF, false); break;
-        case 10: r = __builtin_amdgcn_update_dpp(0, xi, 0x15A, 0xF, 0xF, false); break;
-        case 11: r = __builtin_amdgcn_update_dpp(0, xi, 0x15B, 0xF, 0xF, false); break;
-        case 12: r = __builtin_amdgcn_update_dpp(0, xi, 0x15C, 0xF, 0xF, false); break;
-        case 13: r = __builtin_amdgcn_update_dpp(0, xi, 0x15D, 0xF, 0xF, false); break;
-        case 14: r = __builtin_amdgcn_update_dpp(0, xi, 0x15E, 0xF, 0xF, false); break;
-        default: r = __builtin_amdgcn_update_dpp(0, xi, 0x15F, 0xF, 0xF, false); break;
+        case 0: r = __builtin_amdgcn_update_dpp(0, xi, 0x150, 0xF, 0xF, true); break;
+        case 1: r = __builtin_amdgcn_update_dpp(0, xi, 0x151, 0xF, 0xF, true); break;
+        case 2: r = __builtin_amdgcn_update_dpp(0, xi, 0x152, 0xF, 0xF, true); break;
+        case 3: r = __builtin_amdgcn_update_dpp(0, xi, 0x153, 0xF, 0xF, true); break;
+        case 4: r = __builtin_amdgcn_update_dpp(0, xi, 0x154, 0xF, 0xF, true); break;
+        case 5: r = __builtin_amdgcn_update_dpp(0, xi, 0x155, 0xF, 0xF, true); break;
+        case 6: r = __builtin_amdgcn_update_dpp(0, xi, 0x156, 0xF, 0xF, true); break;
+        case 7: r = __builtin_amdgcn_update_dpp(0, xi, 0x157, 0xF, 0xF, true); break;
+        case 8: r = __builtin_amdgcn_update_dpp(0, xi, 0x158, 0xF, 0xF, true); break;
+        case 9: r = __builtin_amdgcn_update_dpp(0, xi, 0x159, 0xF, 0xF, true); break;
+        case 10: r = __builtin_amdgcn_update_dpp(0, xi, 0x15A, 0xF, 0xF, true); break;
+        case 11: r = __builtin_amdgcn_update_dpp(0, xi, 0x15B, 0xF, 0xF, true); break;
+        case 12: r = __builtin_amdgcn_update_dpp(0, xi, 0x15C, 0xF, 0xF, true); break;
+        case 13: r = __builtin_amdgcn_update_dpp(0, xi, 0x15D, 0xF, 0xF, true); break;
+        case 14: r = __builtin_amdgcn_update_dpp(0, xi, 0x15E, 0xF, 0xF, true); break;
+        default: r = __builtin_amdgcn_update_dpp(0, xi, 0x15F, 0xF, 0xF, true); break;
     }
     return __builtin_bit_cast(float, r);
 }
@@ -1101,24 +1101,23 @@ __global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb) kf[fb] = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * M_LD + ko);
             const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * M_LD + ko);
-            const half8 kw = wu == 0 ? kf[0] : wu == 1 ? kf[1] : wu == 2 ? kf[2] : kf[3];
+            const half8 kw = *reinterpret_cast<const half8*>(Kt + (wu * 16 + c) * M_LD + ko);   // = kf[w]
+            // Every query of the wave takes the whole half-tile: keys past a query carry
+            // weight zero, so one straight-line block lets loads, forming and MFMAs overlap.
 #pragma unroll
             for (int qq = 0; qq < KQ; ++qq) {
-                const int iq = i0 + wu + 4 * qq;
-                if (iq < n && j0 + 32 * sub <= iq) {   // wave-uniform: keys of this query's prefix
-                    const half8 sw = *reinterpret_cast<const half8*>(Sw + (wu + 4 * qq) * M_LD + ko);
-                    half8 rk[4];
+                const half8 sw = *reinterpret_cast<const half8*>(Sw + (wu + 4 * qq) * M_LD + ko);
+                half8 rk[4];
 #pragma unroll
-                    for (int fb = 0; fb < 4; ++fb) rk[fb] = kf[fb] * sw;
-                    int idx = 0;
+                for (int fb = 0; fb < 4; ++fb) rk[fb] = kf[fb] * sw;
+                int idx = 0;
 #pragma unroll
-                    for (int fb = 0; fb < 4; ++fb)
+                for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-                        for (int fb2 = fb; fb2 < 4; ++fb2) {
-                            ckk[qq][idx] = mfma_f16(rk[fb], rk[fb2], ckk[qq][idx]);
-                            ++idx;
-                        }
-                }
+                    for (int fb2 = fb; fb2 < 4; ++fb2) {
+                        ckk[qq][idx] = mfma_f16(rk[fb], rk[fb2], ckk[qq][idx]);
+                        ++idx;
+                    }
             }
             sk = mfma_f16(w8, kw, sk);
         }
