@@ -55,12 +55,13 @@ KERNEL_BOUND = {
     "lla_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_moments_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_keymom_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_rows_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_probe_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
 }
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
-    "fast": ["lla_short_kernel", "lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel",
-             "lla_moments_kernel", "lla_keymom_kernel", "lla_probe_kernel"],
+    "fast": ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel",
+             "lla_probe_kernel"],
 }
 
 
@@ -93,6 +94,9 @@ def kernel_flops(name, B, H, n, d, path):
         return pair_count(BH, row0, rowp) * (moments + 2 * d * d) + BH * (rowp - row0) * per_query
     if name == "lla_keymom_kernel":
         return pair_count(BH, rowp, n) * moments + BH * (n - rowp) * (d ** 3 / 3 + 2 * d * d)
+    if name == "lla_rows_kernel":     # one launch: short rows, rows [2d, 4d), key moments of rows >= 4d
+        return sum(kernel_flops(part, B, H, n, d, path)
+                   for part in ("lla_short_kernel", "lla_moments_kernel", "lla_keymom_kernel"))
     if name == "lla_probe_kernel":
         return pair_count(BH, rowp, n) * (4 * d + 2) + BH * (n - rowp) * 4 * d
     raise KeyError(name)

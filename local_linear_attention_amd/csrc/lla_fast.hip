@@ -436,13 +436,12 @@ __device__ __forceinline__ float ldl_solve_wave(float4v (&ckk)[10], float z, con
     return x;
 }
 
-__global__ __launch_bounds__(256, 2) void lla_moments_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__device__ __forceinline__ void moments_block(
+    const int bidx, unsigned char* smem, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ mrow,
     const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
     float* __restrict__ out,
     int n, int row0, int row1, int BH, float sl2, float lambda) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);   // the same value, as a scalar
@@ -450,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void lla_moments_kernel(
     const int nrows = n - row0;   // rows of the row-max array
     const int nblk = (row1 - row0 + B_WAVES - 1) / B_WAVES;
     int blk, bh;
-    head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
+    head_major_block(bidx, BH, nblk, &bh, &blk);
 
     const int i0 = row0 + blk * B_WAVES;
     const int i = i0 + w;
@@ -966,12 +965,11 @@ __device__ __forceinline__ void group_solve(float4v (&ckk)[KQ][10], float (&zr)[
 // query: (C_kk - S_k S_k^T / omega' + lambda e^{-m} I) y = kbar - q, kbar = a + S_k / omega',
 // and the scaled solution yh 2^e = omega' y 2^e in [2^13, 2^14) goes out as fp16 hi + lo
 // parts with gamma = 1 + S_k.yh / omega'.
-__global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mrow,
-    const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
+__device__ __forceinline__ void keymom_block(
+    const int bidx, unsigned char* smem, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ mrow, const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
     _Float16* __restrict__ yhl, float* __restrict__ qsc,
     int n, int row0, int rowp, int BH, float sl2, float lambda) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -980,7 +978,7 @@ __global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
     const int prows = n - rowp;   // rows of this path
     const int nblk = (prows + K_BQ - 1) / K_BQ;
     int blk, bh;
-    head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
+    head_major_block(bidx, BH, nblk, &bh, &blk);
 
     const int i0 = rowp + blk * K_BQ;
     const int last = min(i0 + K_BQ - 1, n - 1);
@@ -1063,9 +1061,13 @@ __global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
     const int kq_off = (16 * w + c) * FD * 2 + 16 * g;
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     auto buf = [&](int tt) { return smem + (tt % M_NBUF) * K_BUF; };
+    // Tile tt: its score operand first, then its image, so that waiting for the operand
+    // (vector loads complete in issue order) does not also wait for the copies.
     auto issue = [&](int tt, uint4& q0, uint4& q1) {
         const int ts = min(tt, ntiles - 1);
         const uint32_t dst = lds0 + static_cast<uint32_t>((tt % M_NBUF) * K_BUF);
+        q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off, ts * MT * FD * 2, 0));
+        q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off + 64, ts * MT * FD * 2, 0));
 #pragma unroll
         for (int e = 0; e < K_WLOADS; ++e) {
             const int u = min(wu + B_WAVES * e, K_LOADS - 1);
@@ -1073,13 +1075,11 @@ __global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
                 img, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
                 16, voff[e], ts * PACK_TILE_BYTES, 0, 0);
         }
-        q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off, ts * MT * FD * 2, 0));
-        q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off + 64, ts * MT * FD * 2, 0));
     };
-    // After tile t+1's copies come its 2 operand loads and tile t+2's K_WLOADS + 2 loads.
-    static_assert(K_WLOADS + 4 < 16, "vmcnt operand is 4 bits here");
+    // After tile t+1's copies come tile t+2's 2 + K_WLOADS loads.
+    static_assert(K_WLOADS + 2 < 16, "vmcnt operand is 4 bits here");
     auto wait_tile = [] {
-        __builtin_amdgcn_s_waitcnt((K_WLOADS + 4) | (0x7 << 4) | (0xF << 8));
+        __builtin_amdgcn_s_waitcnt((K_WLOADS + 2) | (0x7 << 4) | (0xF << 8));
         LDS_FENCE();
     };
     auto ring_barrier = [] {
@@ -1088,14 +1088,13 @@ __global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
         __builtin_amdgcn_s_barrier();
         LDS_FENCE();
     };
-    auto compute = [&](int t, const unsigned char* cur) {
+    auto compute = [&](int t, const unsigned char* cur, int sub) {
         const int j0 = t * MT;
         const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
         const _Float16* Sw = reinterpret_cast<const _Float16*>(cur + K_SW);
         const _Float16* Sw2 = reinterpret_cast<const _Float16*>(cur + K_SW2);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            if (j0 + 32 * sub > last) break;   // block-uniform: past every query of the block
+        {
+            if (j0 + 32 * sub > last) return;   // block-uniform: past every query of the block
             const int ko = 32 * sub + 8 * g;
             half8 kf[4];
 #pragma unroll
@@ -1122,6 +1121,8 @@ __global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
             sk = mfma_f16(w8, kw, sk);
         }
     };
+    // Step t: tile t in LDS, tile t+1's image landing and its score operand (issued a step
+    // ago) in B, tile t+2 issued now into A; tile t+1's scores are taken between the halves.
     uint4 aq0, aq1, bq0, bq1;
     issue(0, aq0, aq1);
     issue(1, bq0, bq1);
@@ -1129,16 +1130,18 @@ __global__ __launch_bounds__(256, 2) void lla_keymom_kernel(
     score_store(score_mfma(aq0, aq1), buf(0), 0);
     ring_barrier();
     for (int t = 0; t < ntiles; t += 2) {
-        const float4v sb = score_mfma(bq0, bq1);
         issue(t + 2, aq0, aq1);
-        compute(t, buf(t));
+        compute(t, buf(t), 0);
+        const float4v sb = score_mfma(bq0, bq1);
+        compute(t, buf(t), 1);
         if (t + 1 < ntiles) score_store(sb, buf(t + 1), (t + 1) * MT);
         wait_tile();
         ring_barrier();
         if (t + 1 >= ntiles) break;
-        const float4v sa = score_mfma(aq0, aq1);
         issue(t + 3, bq0, bq1);
-        compute(t + 1, buf(t + 1));
+        compute(t + 1, buf(t + 1), 0);
+        const float4v sa = score_mfma(aq0, aq1);
+        compute(t + 1, buf(t + 1), 1);
         if (t + 2 < ntiles) score_store(sa, buf(t + 2), (t + 2) * MT);
         wait_tile();
         ring_barrier();
@@ -1428,23 +1431,35 @@ __device__ __forceinline__ double wave_sum_d(double x) {
     return x;
 }
 
-__global__ __launch_bounds__(256, 2) void lla_short_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+// LDS of a short-row block: staged K, V (bf16), then per wave q, weights, kbar, the
+// pivot-column exchange (then y) and 16 rows of C_kk in transit (fp64).
+constexpr int SB_KS = 0;
+constexpr int SB_VS = SB_KS + S_KMAX * S_KLD * 2;
+constexpr int SB_QS = SB_VS + S_KMAX * S_KLD * 2;
+constexpr int SB_WS = SB_QS + S_ROWS * FD * 8;
+constexpr int SB_KBS = SB_WS + S_ROWS * S_KMAX * 8;
+constexpr int SB_XB = SB_KBS + S_ROWS * FD * 8;
+constexpr int SB_TB = SB_XB + S_ROWS * FD * 8;
+constexpr int S_SMEM = SB_TB + S_ROWS * 16 * S_TLD * 8;
+static_assert(SB_QS % 16 == 0, "fp64 areas stay aligned");
+
+__device__ __forceinline__ void short_block(
+    const int bidx, unsigned char* smem, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ out, int n, int rows, int BH,
     double inv_h, double lambda) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[S_KMAX * S_KLD];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[S_KMAX * S_KLD];
-    __shared__ double qs[S_ROWS][FD];
-    __shared__ double ws[S_ROWS][S_KMAX];
-    __shared__ double kbs[S_ROWS][FD];
-    __shared__ double xb[S_ROWS][FD];               // pivot-column exchange, then y
-    __shared__ double tb[S_ROWS][16 * S_TLD];       // 16 rows of C_kk in transit
+    uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + SB_KS);
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem + SB_VS);
+    double (*qs)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_QS);
+    double (*ws)[S_KMAX] = reinterpret_cast<double (*)[S_KMAX]>(smem + SB_WS);
+    double (*kbs)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_KBS);
+    double (*xb)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_XB);              // pivot-column exchange, then y
+    double (*tb)[16 * S_TLD] = reinterpret_cast<double (*)[16 * S_TLD]>(smem + SB_TB);   // 16 rows of C_kk in transit
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
     const int nblk = (rows + S_ROWS - 1) / S_ROWS;
-    const int blk = nblk - 1 - static_cast<int>(blockIdx.x / BH);  // longest rows first
-    const int bh = static_cast<int>(blockIdx.x % BH);
+    const int blk = nblk - 1 - bidx / BH;  // longest rows first
+    const int bh = bidx % BH;
     const int r0 = blk * S_ROWS;
     const int i = r0 + w;
     const bool valid = i < rows;
@@ -1615,6 +1630,67 @@ __global__ __launch_bounds__(256, 2) void lla_short_kernel(
     if (valid) out[base + static_cast<int64_t>(i) * FD + lane] = static_cast<float>(va - (acc - va * swu));
 }
 
+// All row work after the row maxima in one launch: short rows (fp64), rows [2d, 4d)
+// (explicit moments) and the key-moment blocks of rows >= 4d.  The short and explicit blocks
+// (the "aux" blocks) fill every other run of R_CHUNK dispatch positions at the start, so
+// that a CU tends to hold one aux block, mostly latency-bound, beside a key-moment block,
+// mostly on the matrix cores (the dispatcher places blocks b and b + CU count together).
+struct RowsArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* mrow;
+    const float* anchors;
+    const unsigned char* packed;
+    _Float16* yhl;
+    float* qsc;
+    float* out;
+    int n, row0, rowp, BH, n_short, n_mom, n_key;
+    float sl2, lambda;
+    double inv_h, lambda_d;
+};
+constexpr int R_CHUNK = 256;
+
+// Dispatch position b -> key-moment block *key or aux block *aux (the other one -1): runs of
+// up to R_CHUNK key-moment blocks and R_CHUNK aux blocks alternate, key-moment first, while
+// both kinds remain; then the rest of whichever kind is left.  A bijection from
+// [0, n_key + n_aux); a position past that range gets neither role.
+__device__ __forceinline__ void rows_block_role(int b, int n_key, int n_aux, int* key, int* aux) {
+    const int both = min(n_key, n_aux) / R_CHUNK;   // full rounds of one run of each kind
+    if (b < 2 * both * R_CHUNK) {
+        const int r = b / (2 * R_CHUNK), o = b % (2 * R_CHUNK);
+        if (o < R_CHUNK) *key = r * R_CHUNK + o;
+        else *aux = r * R_CHUNK + o - R_CHUNK;
+        return;
+    }
+    b -= 2 * both * R_CHUNK;
+    const int kr = n_key - both * R_CHUNK, ar = n_aux - both * R_CHUNK;   // left of each kind
+    const int kc = min(R_CHUNK, kr);   // one more (partial) key-moment run, then the aux left,
+    if (b < kc) { *key = both * R_CHUNK + b; return; }   // then the key-moment blocks left
+    b -= kc;
+    if (b < ar) { *aux = both * R_CHUNK + b; return; }
+    b -= ar;
+    if (b < kr - kc) *key = both * R_CHUNK + kc + b;
+}
+constexpr int R_SMEM = K_SMEM > S_SMEM ? (K_SMEM > B_SMEM ? K_SMEM : B_SMEM) : (S_SMEM > B_SMEM ? S_SMEM : B_SMEM);
+
+__global__ __launch_bounds__(256, 2) void lla_rows_kernel(const RowsArgs a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int n_aux = a.n_short + a.n_mom;
+    int aux = -1, key = -1;
+    rows_block_role(static_cast<int>(blockIdx.x), a.n_key, n_aux, &key, &aux);
+    if (aux >= 0) {
+        if (aux < a.n_short)
+            short_block(aux, smem, a.q, a.k, a.v, a.out, a.n, a.row0, a.BH, a.inv_h, a.lambda_d);
+        else
+            moments_block(aux - a.n_short, smem, a.q, a.k, a.v, a.mrow, a.anchors, a.packed, a.out, a.n, a.row0,
+                          a.rowp, a.BH, a.sl2, a.lambda);
+    } else if (key >= 0) {
+        keymom_block(key, smem, a.q, a.k, a.mrow, a.anchors, a.packed, a.yhl, a.qsc, a.n, a.row0, a.rowp, a.BH,
+                     a.sl2, a.lambda);
+    }
+}
+
 // Rows [0, 2d): fp64 short-row kernel; [2d, 4d): explicit moments; [4d, n): probe path.
 int fast_row0(int64_t n, int64_t d) { return static_cast<int>(n < 2 * d ? n : 2 * d); }
 int fast_rowp(int64_t n, int64_t d) { return static_cast<int>(n < 4 * d ? n : 4 * d); }
@@ -1656,24 +1732,11 @@ size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
 }
 
 hipError_t launch_fast(const Problem& p, void* workspace) {
-    const int row0 = fast_row0(p.n, p.d);
-    const int BHs = static_cast<int>(p.B * p.H);
-    prof_begin(p.stream, "lla_short_kernel");
-    lla_short_kernel<<<dim3(static_cast<unsigned>(BHs) * ((row0 + S_ROWS - 1) / S_ROWS)), dim3(256), 0,
-                       p.stream>>>(static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k),
-                                   static_cast<const uint16_t*>(p.v), p.out, static_cast<int>(p.n), row0,
-                                   BHs, 1.0 / p.h, p.lambda);
-    prof_end(p.stream);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || p.n <= row0) return err;
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(attr_once, [] {
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_moments_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, B_SMEM);
-        if (attr_err == hipSuccess)
-            attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_keymom_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, K_SMEM);
+        attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_rows_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, R_SMEM);
         if (attr_err == hipSuccess)
             attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_probe_kernel),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
@@ -1682,57 +1745,60 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
 
     const int n = static_cast<int>(p.n);
     const int BH = static_cast<int>(p.B * p.H);
-    const int nrows = n - row0;
+    const int row0 = fast_row0(p.n, p.d);
+    const int rowp = fast_rowp(p.n, p.d);
     const float sl2 = static_cast<float>(LOG2E / p.h);
     const auto* q = static_cast<const uint16_t*>(p.q);
     const auto* k = static_cast<const uint16_t*>(p.k);
     const auto* v = static_cast<const uint16_t*>(p.v);
-    const FastLayout L = fast_layout(BH, n, p.d);
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* mrow = reinterpret_cast<float*>(ws + L.mrow);
-    float* partial = reinterpret_cast<float*>(ws + L.partial);
-    float* anchors = reinterpret_cast<float*>(ws + L.anchors);
-    unsigned char* packed = ws + L.packed;
-    unsigned char* kimg = ws + L.kimg;
-    _Float16* yhl = reinterpret_cast<_Float16*>(ws + L.yhl);
-    float* qsc = reinterpret_cast<float*>(ws + L.qsc);
-    const int rowp = fast_rowp(p.n, p.d);
-    const int ptiles = (n + MT - 1) / MT;
-    prof_begin(p.stream, "lla_anchor_kernel");
-    lla_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * ANCHOR_SLICES), dim3(256), 0, p.stream>>>(k, v, partial, n);
-    prof_end(p.stream);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    prof_begin(p.stream, "lla_pack_kernel");
-    lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(
-        k, v, partial, anchors, packed, kimg, n, ptiles);
-    prof_end(p.stream);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-
-    const unsigned blocks_a = static_cast<unsigned>(BH) * ((nrows + R_QB - 1) / R_QB);
-    prof_begin(p.stream, "lla_rowmax_kernel");
-    lla_rowmax_kernel<<<dim3(blocks_a), dim3(256), 0, p.stream>>>(q, kimg, mrow, n, row0, BH, sl2);
-    prof_end(p.stream);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-
-    if (rowp > row0) {
-        const unsigned blocks_b = static_cast<unsigned>(BH) * ((rowp - row0 + B_WAVES - 1) / B_WAVES);
-        prof_begin(p.stream, "lla_moments_kernel");
-        lla_moments_kernel<<<dim3(blocks_b), dim3(256), B_SMEM, p.stream>>>(
-            q, k, v, mrow, anchors, packed, p.out, n, row0, rowp, BH, sl2, static_cast<float>(p.lambda));
+    RowsArgs ra{};
+    ra.q = q; ra.k = k; ra.v = v; ra.out = p.out;
+    ra.n = n; ra.row0 = row0; ra.rowp = rowp; ra.BH = BH;
+    ra.sl2 = sl2; ra.lambda = static_cast<float>(p.lambda);
+    ra.inv_h = 1.0 / p.h; ra.lambda_d = p.lambda;
+    ra.n_short = BH * ((row0 + S_ROWS - 1) / S_ROWS);
+    ra.n_mom = rowp > row0 ? BH * ((rowp - row0 + B_WAVES - 1) / B_WAVES) : 0;
+    const int n_key = n > rowp ? BH * ((n - rowp + K_BQ - 1) / K_BQ) : 0;
+    ra.n_key = n_key;
+    hipError_t err;
+    const unsigned char* kimg_c = nullptr;
+    if (n > row0) {
+        const FastLayout L = fast_layout(BH, n, p.d);
+        unsigned char* ws = static_cast<unsigned char*>(workspace);
+        float* mrow = reinterpret_cast<float*>(ws + L.mrow);
+        float* partial = reinterpret_cast<float*>(ws + L.partial);
+        float* anchors = reinterpret_cast<float*>(ws + L.anchors);
+        unsigned char* packed = ws + L.packed;
+        unsigned char* kimg = ws + L.kimg;
+        kimg_c = kimg;
+        ra.mrow = mrow; ra.anchors = anchors; ra.packed = packed;
+        ra.yhl = reinterpret_cast<_Float16*>(ws + L.yhl);
+        ra.qsc = reinterpret_cast<float*>(ws + L.qsc);
+        const int ptiles = (n + MT - 1) / MT;
+        prof_begin(p.stream, "lla_anchor_kernel");
+        lla_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * ANCHOR_SLICES), dim3(256), 0, p.stream>>>(k, v, partial, n);
+        prof_end(p.stream);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        prof_begin(p.stream, "lla_pack_kernel");
+        lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(
+            k, v, partial, anchors, packed, kimg, n, ptiles);
+        prof_end(p.stream);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        const unsigned blocks_a = static_cast<unsigned>(BH) * ((n - row0 + R_QB - 1) / R_QB);
+        prof_begin(p.stream, "lla_rowmax_kernel");
+        lla_rowmax_kernel<<<dim3(blocks_a), dim3(256), 0, p.stream>>>(q, kimg, mrow, n, row0, BH, sl2);
         prof_end(p.stream);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    if (n > rowp) {
-        const unsigned blocks_k = static_cast<unsigned>(BH) * ((n - rowp + K_BQ - 1) / K_BQ);
-        prof_begin(p.stream, "lla_keymom_kernel");
-        lla_keymom_kernel<<<dim3(blocks_k), dim3(256), K_SMEM, p.stream>>>(
-            q, k, mrow, anchors, packed, yhl, qsc, n, row0, rowp, BH, sl2, static_cast<float>(p.lambda));
-        prof_end(p.stream);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+    prof_begin(p.stream, "lla_rows_kernel");
+    lla_rows_kernel<<<dim3(static_cast<unsigned>(ra.n_short + ra.n_mom + n_key)), dim3(256), R_SMEM, p.stream>>>(ra);
+    prof_end(p.stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (n_key > 0) {
         const unsigned blocks_p = static_cast<unsigned>(BH) * ((n - rowp + P_QB - 1) / P_QB);
         prof_begin(p.stream, "lla_probe_kernel");
         lla_probe_kernel<<<dim3(blocks_p), dim3(P_WAVES * 64), P_SMEM, p.stream>>>(
-            q, mrow, anchors, packed, kimg, yhl, qsc, p.out, n, row0, rowp, BH, sl2);
+            q, ra.mrow, ra.anchors, ra.packed, kimg_c, ra.yhl, ra.qsc, p.out, n, row0, rowp, BH, sl2);
         prof_end(p.stream);
     }
     return hipGetLastError();

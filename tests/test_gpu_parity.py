@@ -108,9 +108,8 @@ def test_profiling_records_each_kernel():
         rec = lla_profile_collect()
     finally:
         lla_profile_enable(False)
-    assert [name for name, _ in rec] == ["lla_short_kernel", "lla_anchor_kernel", "lla_pack_kernel",
-                                         "lla_rowmax_kernel", "lla_moments_kernel", "lla_keymom_kernel",
-                                         "lla_probe_kernel"]
+    assert [name for name, _ in rec] == ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel",
+                                         "lla_rows_kernel", "lla_probe_kernel"]
     assert all(ms > 0 for _, ms in rec)
 
 
