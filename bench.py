@@ -164,8 +164,8 @@ def cpu_baseline(w, q, k, v, seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="d24")
     ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -103,7 +103,9 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
  * multiple of 256 bytes: one float per row at or beyond position 2d (its score maximum);
  * 16*2d floats per head of partial key/value sums and 2d floats per head of the centring
  * anchor; then, per head and tile of 64 keys, K and V as fp16 (2*d*72*2 bytes: feature-major
- * rows of 64 keys plus 8 halves of padding) and K key-major (64*72*2 bytes).  Nothing when
+ * rows of 64 keys plus 8 halves of padding) and K key-major twice, as given and centred as
+ * fp16 (2*64*72*2 bytes); then, per row at or beyond position 4d, the row's solution as two
+ * fp16 parts (2*d*2 bytes) and four floats (16 bytes, one region each).  Nothing when
  * n <= 2d.  The fast path serves n up to 4194304 (2^22); AUTO uses the exact path beyond. */
 size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                           lla_path_t path);
