@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace lla {
 namespace {
@@ -1251,16 +1252,18 @@ __device__ __forceinline__ void keymom_block(
     }
 }
 
-// Pass 2.  Block = 8 waves x 16 queries; each 64-key tile (bf16 keys and fp16 centred keys,
-// both key-major, and fp16 centred values feature-major) streams through a ring of three LDS
-// buffers.  Per tile and wave, for key block kb (16 keys):
+// Pass 2.  Block = 8 waves x 32 queries (two sets of 16 per wave, which share the key and
+// value operands); each 64-key tile (bf16 keys and fp16 centred keys, both key-major, and
+// fp16 centred values feature-major) streams through a ring of three LDS buffers.  Per tile,
+// wave and query set, for key block kb (16 keys):
 //   S^T = K Q^T (bf16 MFMA pair: pass 1's operands in pass 1's order, so bitwise its scores),
 //   U^T = (K - a) (yh_hi + yh_lo)^T 2^e (four fp16 MFMAs),
-//   P = fp16(w (gamma - U 2^-e)) with w = fp16(sqrt-weight)^2 as in pass 1;
+//   P = fp16(w fp16(gamma - U 2^-e)) with w = fp16(sqrt-weight)^2 as in pass 1 (packed fp16);
 // lane (g, c) register r holds key 16 kb + 4g + r of query c, which is already the A
 // operand of O += P (V - a_v) over 32-key steps (K-slots: keys 4g.., then 16 + 4g..).
 constexpr int P_WAVES = 8;
-constexpr int P_QW = 16;
+constexpr int P_SETS = 2;                    // query sets of 16 per wave
+constexpr int P_QW = 16 * P_SETS;
 constexpr int P_QB = P_WAVES * P_QW;
 constexpr int P_BUF = 2 * KM_TILE_BYTES + FD * M_LD * 2;   // bf16 K | fp16 K - a | fp16 V - a_v
 constexpr int P_LOADS = P_BUF / 1024;
@@ -1283,23 +1286,32 @@ __global__ __launch_bounds__(512, 1) void lla_probe_kernel(
     head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
     const int i0 = rowp + blk * P_QB;
     const int qw0 = i0 + P_QW * wu;                   // this wave's first query
-    const int qc = min(qw0 + c, n - 1);               // column query of this lane
     const int wave_last = min(qw0 + P_QW - 1, n - 1);
     const int block_last = min(i0 + P_QB - 1, n - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
-    const int64_t qrow = static_cast<int64_t>(bh) * prows + (qc - rowp);
 
-    bf16x8 qf[2];
-    half8 yh[2], yl[2];
+    // Query set st: column c is query qw0 + 16 st + c (clamped to n - 1).
+    bf16x8 qf[P_SETS][2];
+    half8 yh[P_SETS][2], yl[P_SETS][2];
+    float gam[P_SETS], isig[P_SETS], hm[P_SETS];
+    int qc[P_SETS];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + base + static_cast<int64_t>(qc) * FD + 32 * ks + 8 * g));
-        yh[ks] = *reinterpret_cast<const half8*>(yhl + qrow * P_YLD + 32 * ks + 8 * g);
-        yl[ks] = *reinterpret_cast<const half8*>(yhl + qrow * P_YLD + FD + 32 * ks + 8 * g);
+    for (int st = 0; st < P_SETS; ++st) {
+        qc[st] = min(qw0 + 16 * st + c, n - 1);
+        const int64_t qrow = static_cast<int64_t>(bh) * prows + (qc[st] - rowp);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            qf[st][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                        q + base + static_cast<int64_t>(qc[st]) * FD + 32 * ks + 8 * g));
+            yh[st][ks] = *reinterpret_cast<const half8*>(yhl + qrow * P_YLD + 32 * ks + 8 * g);
+            yl[st][ks] = *reinterpret_cast<const half8*>(yhl + qrow * P_YLD + FD + 32 * ks + 8 * g);
+        }
+        const float4v sc = *reinterpret_cast<const float4v*>(qsc + qrow * P_QSC);
+        gam[st] = sc[0];
+        isig[st] = sc[1];
+        hm[st] = 0.5f * mrow[static_cast<int64_t>(bh) * nrows + (qc[st] - row0)];
     }
-    const float4v sc = *reinterpret_cast<const float4v*>(qsc + qrow * P_QSC);
-    const float gam = sc[0], isig = sc[1];
-    const float hs = 0.5f * sl2, hm = 0.5f * mrow[static_cast<int64_t>(bh) * nrows + (qc - row0)];
+    const float hs = 0.5f * sl2;
 
     const int ntiles = block_last / MT + 1;
     const int ptiles = (n + MT - 1) / MT;
@@ -1335,72 +1347,90 @@ __global__ __launch_bounds__(512, 1) void lla_probe_kernel(
         LDS_FENCE();
     };
 
-    float4v o[4];
+    float4v o[P_SETS][4];
 #pragma unroll
-    for (int fv = 0; fv < 4; ++fv) o[fv] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < P_SETS; ++st)
+#pragma unroll
+        for (int fv = 0; fv < 4; ++fv) o[st][fv] = float4v{0.f, 0.f, 0.f, 0.f};
     issue(0);
     issue(1);
     wait_and_sync();
     for (int t = 0; t < ntiles; ++t) {
         issue(t + 2);
         const int j0 = t * MT;
-        if (j0 <= wave_last) {   // wave-uniform
+        // A tile wholly below the wave's first query needs no causal mask: that case (all
+        // tiles but the last one or two of a wave) takes a copy of the body without it.
+        auto tile_body = [&](auto masked) {
             const unsigned char* cur = smem + (t % 3) * P_BUF;
             const unsigned char* KB = cur;
             const unsigned char* KC = cur + KM_TILE_BYTES;
             const _Float16* VI = reinterpret_cast<const _Float16*>(cur + 2 * KM_TILE_BYTES);
-            const bool full = j0 + MT - 1 <= qw0;   // every key below every query of the wave
-            half4 p[4];
+            half4 p[P_SETS][4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int ro = (kb * 16 + c) * (KM_LD * 2) + 16 * g;
-                float4v s = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-                s = mfma_bf16(*reinterpret_cast<const bf16x8*>(KB + ro), qf[0], s);
-                s = mfma_bf16(*reinterpret_cast<const bf16x8*>(KB + ro + 64), qf[1], s);
+                const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(KB + ro);
+                const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(KB + ro + 64);
                 const half8 c0 = *reinterpret_cast<const half8*>(KC + ro);
                 const half8 c1 = *reinterpret_cast<const half8*>(KC + ro + 64);
-                u = mfma_f16(c0, yh[0], u);
-                u = mfma_f16(c1, yh[1], u);
-                u = mfma_f16(c0, yl[0], u);
-                u = mfma_f16(c1, yl[1], u);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float e = __builtin_amdgcn_exp2f(fmaf(s[r], hs, -hm));
-                    if (!full) e = j0 + kb * 16 + 4 * g + r <= qc ? e : 0.0f;
-                    const _Float16 swh = static_cast<_Float16>(e);
-                    const _Float16 wv = swh * swh;
-                    p[kb][r] = static_cast<_Float16>(static_cast<float>(wv) * fmaf(-u[r], isig, gam));
+                for (int st = 0; st < P_SETS; ++st) {
+                    float4v sv = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+                    sv = mfma_bf16(k0, qf[st][0], sv);
+                    sv = mfma_bf16(k1, qf[st][1], sv);
+                    u = mfma_f16(c0, yh[st][0], u);
+                    u = mfma_f16(c1, yh[st][1], u);
+                    u = mfma_f16(c0, yl[st][0], u);
+                    u = mfma_f16(c1, yl[st][1], u);
+                    const bool full = !decltype(masked)::value || j0 + MT - 1 <= qw0 + 16 * st;
+                    half4 sw4, t4;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float e = __builtin_amdgcn_exp2f(fmaf(sv[r], hs, -hm[st]));
+                        if (!full) e = j0 + kb * 16 + 4 * g + r <= qc[st] ? e : 0.0f;
+                        sw4[r] = static_cast<_Float16>(e);
+                        t4[r] = static_cast<_Float16>(fmaf(-u[r], isig[st], gam[st]));
+                    }
+                    p[st][kb] = (sw4 * sw4) * t4;   // w = fp16(sw^2) exactly as pass 1, then P = fp16(w t)
                 }
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const half8 pa = __builtin_shufflevector(p[2 * ks], p[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int fv = 0; fv < 4; ++fv) {
                     const _Float16* vr = VI + (fv * 16 + c) * M_LD + 32 * ks + 4 * g;
                     const half4 v0 = *reinterpret_cast<const half4*>(vr);
                     const half4 v1 = *reinterpret_cast<const half4*>(vr + 16);
-                    o[fv] = mfma_f16(pa, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7), o[fv]);
+                    const half8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int st = 0; st < P_SETS; ++st) {
+                        const half8 pa = __builtin_shufflevector(p[st][2 * ks], p[st][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                        o[st][fv] = mfma_f16(pa, vb, o[st][fv]);
+                    }
                 }
             }
-        }
+        };
+        if (j0 + MT - 1 <= qw0) tile_body(std::false_type{});
+        else if (j0 <= wave_last) tile_body(std::true_type{});   // wave-uniform
         wait_and_sync();
     }
     // Copies issued past the last tile are still landing in LDS: let them finish before exit.
     __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
 
-    // Output rows: lane (g, c) register r = query qw0 + 4g + r, feature 16 fv + c.
+    // Output rows: lane (g, c) register r of set st = query qw0 + 16 st + 4g + r, feature 16 fv + c.
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD + FD;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = qw0 + 4 * g + r;
-        if (i < n) {
-            const float iom = qsc[(static_cast<int64_t>(bh) * prows + (i - rowp)) * P_QSC + 2];
-            float* orow = out + base + static_cast<int64_t>(i) * FD;
+    for (int st = 0; st < P_SETS; ++st)
 #pragma unroll
-            for (int fv = 0; fv < 4; ++fv) orow[fv * 16 + c] = fmaf(o[fv][r], iom, anc[fv * 16 + c]);
+        for (int r = 0; r < 4; ++r) {
+            const int i = qw0 + 16 * st + 4 * g + r;
+            if (i < n) {
+                const float iom = qsc[(static_cast<int64_t>(bh) * prows + (i - rowp)) * P_QSC + 2];
+                float* orow = out + base + static_cast<int64_t>(i) * FD;
+#pragma unroll
+                for (int fv = 0; fv < 4; ++fv) orow[fv * 16 + c] = fmaf(o[st][fv][r], iom, anc[fv * 16 + c]);
+            }
         }
-    }
 }
 
 // ---------------------------------------------------------------------------------------

@@ -20,10 +20,21 @@ EXACT_BOUND = 2e-6   # fp64 path: fp32 output rounding plus fp64 arithmetic
 WORKERS = 8
 
 
-def check(got, ref, dtype, path, label):
+def check(got, ref, dtype, path, label, positions=None, d=None):
+    """Per-row normwise errors against the oracle, within the tolerance.  With the rows'
+    positions in their sequence and the head size, the worst error of each row range of
+    the matrix-core path is reported too: fp64 short rows (i < 2d), explicit cross moment
+    (2d <= i < 4d), probe pass (i >= 4d)."""
     err = row_errors(got, ref)
     worst = float(err.max())
-    print(f"[parity] {label} path={path} rows={err.size} max_row_err={worst:.3e}", flush=True)
+    ranges = ""
+    if positions is not None and d is not None:
+        pos = np.broadcast_to(np.asarray(positions), err.shape)
+        for name, lo, hi in (("i<2d", 0, 2 * d), ("2d<=i<4d", 2 * d, 4 * d), ("i>=4d", 4 * d, None)):
+            sel = (pos >= lo) & ((pos < hi) if hi is not None else True)
+            if sel.any():
+                ranges += f" {name}:{float(err[sel].max()):.2e}"
+    print(f"[parity] {label} path={path} rows={err.size} max_row_err={worst:.3e}{ranges}", flush=True)
     assert np.isfinite(got).all(), label
     assert worst <= TOL[dtype], (label, worst)
     if path == "exact":
@@ -74,7 +85,7 @@ def test_fast_path_every_row(name, shape):
     w, q, k, v = workload_arrays(name, **shape)
     ref = oracle_forward(q, k, v, w.h, w.lam, workers=WORKERS)
     got = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="fast")
-    check(got, ref, w.dtype, "fast", f"{name}{shape}")
+    check(got, ref, w.dtype, "fast", f"{name}{shape}", positions=np.arange(w.n), d=w.d)
 
 
 def test_fast_path_workspace_entry_point_matches():
@@ -140,7 +151,7 @@ def test_full_size_workload_sampled_rows(name):
     assert np.isfinite(got_full).all()
     ref = oracle_rows(q, k, v, w.h, w.lam, rows, workers=WORKERS)
     got = np.stack([got_full[b, hh, i] for (b, hh, i) in rows])
-    check(got, ref, w.dtype, "auto", f"{name} full-size sampled")
+    check(got, ref, w.dtype, "auto", f"{name} full-size sampled", positions=np.array([i for (_, _, i) in rows]), d=w.d)
 
 
 # ---------------------------------------------------------------- properties
