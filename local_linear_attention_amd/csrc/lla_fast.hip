@@ -121,7 +121,7 @@ constexpr int KM_TILE_BYTES = MT * KM_LD * 2;
 constexpr int KM_STRIDE = 2 * KM_TILE_BYTES;
 constexpr int KM_LOADS = KM_TILE_BYTES / 1024;
 constexpr int KM_WLOADS = (KM_LOADS + B_WAVES - 1) / B_WAVES;
-constexpr int R_QW = 16, R_QB = B_WAVES * R_QW;  // row-max: 16 queries per wave, 64 per block
+constexpr int R_SETS = 2, R_QW = 16 * R_SETS, R_QB = B_WAVES * R_QW;  // row-max: 2 sets of 16 queries per wave
 static_assert(KM_TILE_BYTES % 1024 == 0, "key image must be whole wave copies");
 static_assert(PACK_TILE_BYTES % 1024 == 0, "tile image must be whole wave copies");
 
@@ -260,9 +260,10 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
 }
 
 // Score pass with a running max (rows i >= 2d): m_i = max_{j <= i} q_i.k_j / h, in log2
-// units.  Block = 4 waves x 16 queries; 64-key tiles of the key-major image stream through
-// a ring of three LDS buffers (copied straight from the workspace); scores on MFMA (bf16):
-// S^T block kb of a tile, lane (g, c) register r = key 16 kb + 4g + r, query c.
+// units.  Block = 4 waves x 2 sets of 16 queries (the sets share the key operands); 64-key
+// tiles of the key-major image stream through a ring of three LDS buffers (copied straight
+// from the workspace); scores on MFMA (bf16): S^T block kb of a tile, lane (g, c) register
+// r = key 16 kb + 4g + r, query c of the set.
 __global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restrict__ q,
                                                          const unsigned char* __restrict__ kimg,
                                                          float* __restrict__ mrow, int n, int row0,
@@ -277,16 +278,20 @@ __global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restr
     head_major_block(static_cast<int>(blockIdx.x), BH, nblk, &bh, &blk);
     const int q0 = row0 + blk * R_QB;
     const int qlast = min(q0 + R_QB, n) - 1;
-    const int qi = q0 + w * R_QW + c;   // this lane's query (column c)
-    const int qc = min(qi, n - 1);
-    const int wave_first = q0 + w * R_QW;
+    const int wave_first = q0 + wu * R_QW;
     const int wave_last = min(wave_first + R_QW - 1, n - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
-    bf16x8 qf[2];
+    int qi[R_SETS], qc[R_SETS];   // set st: column c is query wave_first + 16 st + c
+    bf16x8 qf[R_SETS][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                                q + base + static_cast<int64_t>(qc) * FD + ks * 32 + 8 * g));
+    for (int st = 0; st < R_SETS; ++st) {
+        qi[st] = wave_first + 16 * st + c;
+        qc[st] = min(qi[st], n - 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            qf[st][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                        q + base + static_cast<int64_t>(qc[st]) * FD + ks * 32 + 8 * g));
+    }
 
     const int ntiles = (qlast + MT) / MT;
     const int ptiles = (n + MT - 1) / MT;
@@ -319,39 +324,50 @@ __global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restr
         LDS_FENCE();
     };
 
-    float m_run = -INFINITY;
+    float m_run[R_SETS];
+#pragma unroll
+    for (int st = 0; st < R_SETS; ++st) m_run[st] = -INFINITY;
     issue(0);
     issue(1);
     next_tile();
     for (int t = 0; t < ntiles; ++t) {
         issue(t + 2);
         const int j0 = t * MT;
-        if (j0 <= wave_last) {   // wave-uniform: some key of the tile is in a prefix
+        // Tiles wholly below the wave's first query need no causal mask (a copy without it).
+        auto tile_body = [&](auto masked) {
             const unsigned char* cur = ring + (t % 3) * KM_TILE_BYTES;
-            const bool full = j0 + MT - 1 <= wave_first;   // every key below every query
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                float4v s = {0.f, 0.f, 0.f, 0.f};
+                bf16x8 a[2];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 a = __builtin_bit_cast(
+                for (int ks = 0; ks < 2; ++ks)
+                    a[ks] = __builtin_bit_cast(
                         bf16x8, *reinterpret_cast<const uint4*>(cur + (kb * 16 + c) * (KM_LD * 2) + ks * 64 + 16 * g));
-                    s = mfma_bf16(a, qf[ks], s);
-                }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = j0 + kb * 16 + 4 * g + r;
-                    m_run = fmaxf(m_run, (full || j <= qc) ? s[r] : -INFINITY);
+                for (int st = 0; st < R_SETS; ++st) {
+                    float4v s = {0.f, 0.f, 0.f, 0.f};
+                    s = mfma_bf16(a[0], qf[st][0], s);
+                    s = mfma_bf16(a[1], qf[st][1], s);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = j0 + kb * 16 + 4 * g + r;
+                        m_run[st] = fmaxf(m_run[st], (!decltype(masked)::value || j <= qc[st]) ? s[r] : -INFINITY);
+                    }
                 }
             }
-        }
+        };
+        if (j0 + MT - 1 <= wave_first) tile_body(std::false_type{});
+        else if (j0 <= wave_last) tile_body(std::true_type{});   // wave-uniform
         next_tile();
     }
     // Copies past the last tile are still landing in LDS: let them finish before exit.
     __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
-    m_run = fmaxf(m_run, __shfl_xor(m_run, 16));
-    m_run = fmaxf(m_run, __shfl_xor(m_run, 32));
-    if (g == 0 && qi < n) mrow[static_cast<int64_t>(bh) * nrows + (qi - row0)] = m_run * sl2;
+#pragma unroll
+    for (int st = 0; st < R_SETS; ++st) {
+        float m = fmaxf(m_run[st], __shfl_xor(m_run[st], 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (g == 0 && qi[st] < n) mrow[static_cast<int64_t>(bh) * nrows + (qi[st] - row0)] = m * sl2;
+    }
 }
 
 // Upper 16x16 block (I, J), I <= J, of a symmetric 64x64 matrix held as 10 MFMA accumulators.
