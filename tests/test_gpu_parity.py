@@ -133,6 +133,55 @@ def test_tiny_affine_lambda_zero_rows_beyond_d():
     check(got[..., w.d:, :], ref[..., w.d:, :], w.dtype, "exact", "tiny_affine rows>=d")
 
 
+def test_fast_path_lambda_zero_rows_beyond_d():
+    # lambda = 0 on the matrix-core path: rows i >= d have a unique minimiser ([Blog] §2 with
+    # the ridge removed); rows i < d are rank-deficient and only need to be finite.
+    require_gpu()
+    w, q, k, v = workload_arrays("d24", B=1, H=2, n=400)
+    ref = oracle_forward(q, k, v, w.h, 0.0, workers=WORKERS)
+    got = run_gpu(q, k, v, w.dtype, w.h, 0.0, path="fast")
+    assert np.isfinite(got).all()
+    check(got[..., w.d:, :], ref[..., w.d:, :], w.dtype, "fast", "d24 lambda=0 rows>=d",
+          positions=np.arange(w.d, w.n), d=w.d)
+
+
+def test_fast_path_large_lambda():
+    # lambda -> infinity drives b_i to the softmax-weighted mean of the values ([Blog] §2):
+    # the ridge term dominates every regime of the path (fp64 short rows, explicit rows,
+    # probe rows with tiny solutions and their 2^e scaling).
+    require_gpu()
+    w, q, k, v = workload_arrays("d24", B=1, H=2, n=400)
+    ref = oracle_forward(q, k, v, w.h, 1e8, workers=WORKERS)
+    got = run_gpu(q, k, v, w.dtype, w.h, 1e8, path="fast")
+    check(got, ref, w.dtype, "fast", "d24 lambda=1e8", positions=np.arange(w.n), d=w.d)
+
+
+def test_fast_path_linear_in_values():
+    # b is linear in V.  Doubling V is exact in bf16 and in every product and sum that
+    # touches V except fp16 subnormals (|x| < 2^-14), whose grid does not scale: the output
+    # doubles to within rounding far below the tolerance.
+    require_gpu()
+    w, q, k, v = workload_arrays("d24", B=1, H=2, n=333)
+    a = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="fast")
+    b = run_gpu(q, k, 2.0 * v, w.dtype, w.h, w.lam, path="fast")
+    err = float(row_errors(b, 2.0 * a).max())
+    print(f"[linearity] max per-row |b(2v) - 2 b(v)| / |2 b(v)| = {err:.2e}", flush=True)
+    assert err <= 1e-5
+
+
+def test_fast_path_long_sequence_sampled_rows():
+    # n = 16384 on the matrix-core path: many tiles per head, the probe pass over long
+    # prefixes, the full XCD-ordered grid.
+    require_gpu()
+    w, q, k, v = workload_arrays("d24", B=1, H=2, n=16384)
+    rows = sample_rows(w.B, w.H, w.n, w.d, w.seed, per_head=8)
+    got_full = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="fast")
+    assert np.isfinite(got_full).all()
+    ref = oracle_rows(q, k, v, w.h, w.lam, rows, workers=WORKERS)
+    got = np.stack([got_full[b, hh, i] for (b, hh, i) in rows])
+    check(got, ref, w.dtype, "fast", "d24 n=16384 sampled", positions=np.array([i for (_, _, i) in rows]), d=w.d)
+
+
 def test_single_position_returns_value():
     require_gpu()
     w, q, k, v = workload_arrays("d24", B=2, H=3, n=1)
