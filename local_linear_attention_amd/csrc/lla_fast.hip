@@ -1268,26 +1268,28 @@ __device__ __forceinline__ void keymom_block(
     }
 }
 
-// Pass 2.  Block = 8 waves x 32 queries (two sets of 16 per wave, which share the key and
-// value operands); each 64-key tile (bf16 keys and fp16 centred keys, both key-major, and
-// fp16 centred values feature-major) streams through a ring of three LDS buffers.  Per tile,
+// Pass 2.  Block = 4 waves x 32 queries (two sets of 16 per wave, which share the key and
+// value operands), two blocks per CU; each 64-key tile (bf16 keys and fp16 centred keys, both
+// key-major, and fp16 centred values feature-major) is copied into one of two LDS buffers
+// while the other is in use.  Per tile,
 // wave and query set, for key block kb (16 keys):
 //   S^T = K Q^T (bf16 MFMA pair: pass 1's operands in pass 1's order, so bitwise its scores),
 //   U^T = (K - a) (yh_hi + yh_lo)^T 2^e (four fp16 MFMAs),
 //   P = fp16(w fp16(gamma - U 2^-e)) with w = fp16(sqrt-weight)^2 as in pass 1 (packed fp16);
 // lane (g, c) register r holds key 16 kb + 4g + r of query c, which is already the A
 // operand of O += P (V - a_v) over 32-key steps (K-slots: keys 4g.., then 16 + 4g..).
-constexpr int P_WAVES = 8;
+constexpr int P_WAVES = 4;
+constexpr int P_NBUF = 2;
 constexpr int P_SETS = 2;                    // query sets of 16 per wave
 constexpr int P_QW = 16 * P_SETS;
 constexpr int P_QB = P_WAVES * P_QW;
 constexpr int P_BUF = 2 * KM_TILE_BYTES + FD * M_LD * 2;   // bf16 K | fp16 K - a | fp16 V - a_v
 constexpr int P_LOADS = P_BUF / 1024;
 constexpr int P_WLOADS = (P_LOADS + P_WAVES - 1) / P_WAVES;
-constexpr int P_SMEM = 3 * P_BUF;
+constexpr int P_SMEM = P_NBUF * P_BUF;
 static_assert(P_BUF % 1024 == 0 && 2 * KM_TILE_BYTES % 1024 == 0, "probe images must be whole wave copies");
 
-__global__ __launch_bounds__(512, 1) void lla_probe_kernel(
+__global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
     const unsigned char* __restrict__ packed, const unsigned char* __restrict__ kimg,
     const _Float16* __restrict__ yhl, const float* __restrict__ qsc, float* __restrict__ out,
@@ -1338,11 +1340,11 @@ __global__ __launch_bounds__(512, 1) void lla_probe_kernel(
         const_cast<unsigned char*>(uniform_ptr(packed + static_cast<int64_t>(bh) * ptiles * PACK_TILE_BYTES)), 0,
         ptiles * PACK_TILE_BYTES, 0x00020000);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-    // Chunk u of a ring buffer: u < 18 from the key-major images, else from the value half
-    // of the tile image.  Wave w issues chunks w, w+8, w+16, w+24 (the last clamped to 26).
+    // Chunk u of a buffer: u < 18 from the key-major images, else from the value half of the
+    // tile image.  Wave w issues chunks w, w+4, ..., w+24 (the last ones clamped to 26).
     auto issue = [&](int tt) {
         const int ts = min(tt, ntiles - 1);
-        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % 3) * P_BUF);
+        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % P_NBUF) * P_BUF);
 #pragma unroll
         for (int e = 0; e < P_WLOADS; ++e) {
             const int u = min(wu + P_WAVES * e, P_LOADS - 1);
@@ -1354,10 +1356,10 @@ __global__ __launch_bounds__(512, 1) void lla_probe_kernel(
                                                          ts * PACK_TILE_BYTES, 0, 0);
         }
     };
-    // Loads complete in order: vmcnt <= P_WLOADS means all but the newest tile have landed.
-    static_assert(P_WLOADS < 16, "vmcnt operand is 4 bits here");
+    // The copies of the next tile have landed (all loads waited for) and every wave is done
+    // with the buffer they will overwrite next.
     auto wait_and_sync = [] {
-        __builtin_amdgcn_s_waitcnt(P_WLOADS | (0x7 << 4) | (0x0 << 8));
+        __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0x0 << 8));
         LDS_FENCE();
         __builtin_amdgcn_s_barrier();
         LDS_FENCE();
@@ -1369,15 +1371,14 @@ __global__ __launch_bounds__(512, 1) void lla_probe_kernel(
 #pragma unroll
         for (int fv = 0; fv < 4; ++fv) o[st][fv] = float4v{0.f, 0.f, 0.f, 0.f};
     issue(0);
-    issue(1);
     wait_and_sync();
     for (int t = 0; t < ntiles; ++t) {
-        issue(t + 2);
+        issue(t + 1);   // into the buffer tile t-1 used
         const int j0 = t * MT;
         // A tile wholly below the wave's first query needs no causal mask: that case (all
         // tiles but the last one or two of a wave) takes a copy of the body without it.
         auto tile_body = [&](auto masked) {
-            const unsigned char* cur = smem + (t % 3) * P_BUF;
+            const unsigned char* cur = smem + (t % P_NBUF) * P_BUF;
             const unsigned char* KB = cur;
             const unsigned char* KC = cur + KM_TILE_BYTES;
             const _Float16* VI = reinterpret_cast<const _Float16*>(cur + 2 * KM_TILE_BYTES);
