@@ -20,6 +20,14 @@ Workloads (the shapes of the pages' settings, synthetic stand-ins for their data
                 headline throughput workload).
 * ``long``      B1 H8 n16384 d128, bf16, q,k RMS-normalised, v ~ N(0,1); h = sqrt(128),
                 lambda = 1e-1 (long context, large head).
+* ``parallax_d12``, ``parallax_d24``: the q, k, v of ``d12`` and ``d24`` (same seeds and
+                recipes, so bit-identical) plus a Parallax probe rho (``generate_probe``);
+                h as there, lambda unused.
+
+Probe recipe (Parallax workloads): ``numpy.random.default_rng([seed, 1])`` -- a stream of
+its own, so drawing rho changes none of q, k, v -- draws rho ``[B,H,n,d]`` standard normal
+in fp64; rho is RMS-normalised like q and k (the pages' Parallax layers apply RMSNorm to
+rho) and cast once to the workload's storage dtype.
 
 Recipe: ``numpy.random.default_rng(seed)`` draws, in fp64 and in this order, q, k, v
 (each ``[B,H,n,d]`` standard normal) and then the workload's extras (A ``[B,H,d,d]``,
@@ -36,7 +44,8 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "round_to_bf16", "generate"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_probe", "round_to_bf16", "generate",
+           "generate_probe"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -71,6 +80,8 @@ WORKLOADS = {
     "d12": Workload("d12", 4, 12, 2048, 64, "bf16", 8.0, 1e-1, 2, "rms"),
     "d24": Workload("d24", 2, 16, 4096, 64, "bf16", 8.0, 1e-2, 3, "rms_affine_noisy"),
     "long": Workload("long", 1, 8, 16384, 128, "bf16", math.sqrt(128.0), 1e-1, 4, "rms"),
+    "parallax_d12": Workload("parallax_d12", 4, 12, 2048, 64, "bf16", 8.0, 0.0, 2, "rms"),
+    "parallax_d24": Workload("parallax_d24", 2, 16, 4096, 64, "bf16", 8.0, 0.0, 3, "rms_affine_noisy"),
 }
 
 
@@ -139,3 +150,17 @@ def generate(w: Workload):
     plus the fp64 pre-cast arrays: ``(q, k, v, (q64, k64, v64))``."""
     q64, k64, v64 = make_inputs(w.B, w.H, w.n, w.d, w.seed, w.recipe)
     return cast(q64, w.dtype), cast(k64, w.dtype), cast(v64, w.dtype), (q64, k64, v64)
+
+
+def make_probe(B: int, H: int, n: int, d: int, seed: int) -> np.ndarray:
+    """Draw the fp64 (pre-cast) Parallax probe rho ``[B,H,n,d]``: standard normal from the
+    stream ``default_rng([seed, 1])``, RMS-normalised."""
+    rng = np.random.default_rng([seed, 1])
+    return _rms(rng.standard_normal((B, H, n, d)))
+
+
+def generate_probe(w: Workload):
+    """Return the probe of workload ``w`` as a float32 array holding the cast values, plus
+    the fp64 pre-cast array: ``(rho, rho64)``."""
+    rho64 = make_probe(w.B, w.H, w.n, w.d, w.seed)
+    return cast(rho64, w.dtype), rho64

@@ -49,7 +49,7 @@ import os
 
 import numpy as np
 
-__all__ = ["lla_row", "lla_row_parts", "lla_forward", "lla_rows"]
+__all__ = ["lla_row", "lla_row_parts", "lla_forward", "lla_rows", "map_rows"]
 
 
 def lla_row_parts(q_i, K, V, h, lam):
@@ -96,27 +96,31 @@ def lla_row(q_i, K, V, h, lam):
 
 def _rows_worker(args):
     """Rows of one head: qh [r, d] (the queries of the rows), kh/vh the prefix up to the
-    longest row, idx the row positions."""
-    qh, kh, vh, idx, h, lam = args
+    longest row, xh [r, .] an optional per-row extra input (or None), idx the row positions."""
+    fn, qh, kh, vh, xh, idx, extra = args
     out = np.empty((len(idx), vh.shape[-1]), dtype=np.float64)
     for t, i in enumerate(idx):
-        out[t] = lla_row(qh[t], kh[: i + 1], vh[: i + 1], h, lam)
+        if xh is None:
+            out[t] = fn(qh[t], kh[: i + 1], vh[: i + 1], *extra)
+        else:
+            out[t] = fn(qh[t], kh[: i + 1], vh[: i + 1], xh[t], *extra)
     return out
 
 
-def lla_rows(q, k, v, h, lam, rows, workers=1):
-    """LLA outputs for a list of (b, head, i) rows.
+def map_rows(fn, q, k, v, rows, extra, per_row=None, workers=1):
+    """Apply a row function to a list of (b, head, i) rows of [B, H, n, .] inputs.
 
-    q, k, v: [B, H, n, d] arrays (any float dtype; upcast exactly to fp64).
-    rows: iterable of (b, head, i).  Returns an fp64 array [len(rows), d_v].
-    With workers > 1 the rows run in a process pool, in tasks of one head each.
+    ``fn(q_i, K, V, [x_i,] *extra)`` receives the query, the causal key and value prefixes
+    (rows 0..i) and, when ``per_row`` is given, that array's row i.  Returns an fp64 array
+    [len(rows), d_v].  With workers > 1 the rows run in a process pool, in tasks of one
+    head each of about the same cost.
     """
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
+    x = None if per_row is None else np.asarray(per_row)
     rows = list(rows)
     dv = v.shape[-1]
-    # Group rows into tasks (one head per task, each task about the same cost).
     by_head = {}
     for t, (b, hh, i) in enumerate(rows):
         by_head.setdefault((b, hh), []).append((i, t))
@@ -139,8 +143,9 @@ def lla_rows(q, k, v, h, lam, rows, workers=1):
         (b, hh), lst = task
         top = max(i for i, _ in lst) + 1
         idx = [i for i, _ in lst]
-        return (np.asarray(q[b, hh, idx], np.float64), np.asarray(k[b, hh, :top], np.float64),
-                np.asarray(v[b, hh, :top], np.float64), idx, h, lam)
+        xh = None if x is None else np.asarray(x[b, hh, idx], np.float64)
+        return (fn, np.asarray(q[b, hh, idx], np.float64), np.asarray(k[b, hh, :top], np.float64),
+                np.asarray(v[b, hh, :top], np.float64), xh, idx, tuple(extra))
 
     out = np.empty((len(rows), dv), dtype=np.float64)
     if workers <= 1 or len(tasks) < 2:
@@ -155,6 +160,16 @@ def lla_rows(q, k, v, h, lam, rows, workers=1):
             for r, (_, t) in zip(f.result(), futs[f][1]):
                 out[t] = r
     return out
+
+
+def lla_rows(q, k, v, h, lam, rows, workers=1):
+    """LLA outputs for a list of (b, head, i) rows.
+
+    q, k, v: [B, H, n, d] arrays (any float dtype; upcast exactly to fp64).
+    rows: iterable of (b, head, i).  Returns an fp64 array [len(rows), d_v].
+    With workers > 1 the rows run in a process pool, in tasks of one head each.
+    """
+    return map_rows(lla_row, q, k, v, rows, (h, lam), workers=workers)
 
 
 def lla_forward(q, k, v, h, lam, workers=1):

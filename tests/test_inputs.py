@@ -33,3 +33,17 @@ def test_recipes_have_their_structure():
     q0, k0, _ = lla_inputs.make_inputs(1, 1, 64, 16, 0, "normal")
     assert np.array_equal(q, q0) and np.array_equal(k, k0)  # same q, k as the plain draw
     assert np.allclose(v[0, 0], k[0, 0] @ ex["A"][0, 0].T + ex["c"][0, 0])
+
+
+def test_probe_stream_is_separate_and_rms_normalised():
+    w = lla_inputs.WORKLOADS["parallax_d24"].with_shape(B=1, H=2, n=48)
+    base = lla_inputs.WORKLOADS["d24"].with_shape(B=1, H=2, n=48)
+    a, b = lla_inputs.generate(w), lla_inputs.generate(base)
+    for x, y in zip(a[:3], b[:3]):   # the probe draw leaves q, k, v untouched
+        assert np.array_equal(x, y)
+    rho, rho64 = lla_inputs.generate_probe(w)
+    rho2, _ = lla_inputs.generate_probe(w)
+    assert np.array_equal(rho, rho2) and rho.shape == (1, 2, 48, 64) and rho.dtype == np.float32
+    assert np.array_equal(lla_inputs.round_to_bf16(rho), rho)
+    assert np.allclose(np.mean(rho64 * rho64, -1), 1.0, atol=1e-5)
+    assert not np.allclose(rho64, lla_inputs.make_inputs(1, 2, 48, 64, w.seed, "rms")[0])
