@@ -1,5 +1,6 @@
 /*
- * liblla: causal Local Linear Attention (LLA) forward on AMD Instinct MI355X (gfx950).
+ * liblla: causal Local Linear Attention (LLA) forward, and the Parallax forward with a given
+ * probe, on AMD Instinct MI355X (gfx950).
  *
  * The operation (sources: the "Parallax" blog post by Tilde Research, section 2
  * "Canonical Formulation"; the arXiv HTML page "Parallax: Parameterized Local Linear
@@ -119,6 +120,52 @@ lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* 
                             double h, double lambda,
                             lla_dtype_t dtype, void* stream, lla_path_t path,
                             void* workspace, size_t workspace_bytes);
+
+/*
+ * Causal Parallax forward with a caller-supplied probe (sources: the "Parallax" blog post,
+ * section 2, "Additive Correction to Softmax" and "Parallax", where the boundary factor
+ * eta is set to 0 and the probe is given instead of solved; Appendix B of the same post
+ * derives the additive form; section 3, "One extra branch, no extra I/O", gives the
+ * streaming two-branch form the fast path follows):
+ *
+ *   o_i = vbar_i - Sigma_KV^(i) rho_i,   p_ij = softmax_j(q_i . k_j / h) over j <= i,
+ *   vbar_i = sum_j p_ij v_j,  kbar_i = sum_j p_ij k_j,
+ *   Sigma_KV^(i) = sum_j p_ij (v_j - vbar_i)(k_j - kbar_i)^T.
+ *
+ * rho is the probe, an input here ([B, H, n, d], same dtype and layout as q; the pages
+ * produce it by a learned projection of the layer input, which stays with the caller).
+ * A zero probe gives softmax attention.  Arguments as for lla_forward, without lambda;
+ * out must not overlap q, k, v or rho.  Paths: FAST is one streaming pass on the matrix
+ * cores for bf16 inputs with d = 64 and n up to 4194304 (keys and values must lie in the
+ * fp16 range); EXACT accumulates in fp64 and serves every supported (dtype, d); AUTO takes
+ * FAST where it applies.  Validation, errors, streams and scratch ownership are as for the
+ * LLA entry points above (lla_parallax_forward and _ex take scratch from the library pool;
+ * _ws allocates nothing).
+ */
+lla_status_t lla_parallax_forward(const void* q, const void* k, const void* v, const void* rho,
+                                  float* out, int64_t B, int64_t H, int64_t n, int64_t d,
+                                  double h, lla_dtype_t dtype, void* stream);
+
+lla_status_t lla_parallax_forward_ex(const void* q, const void* k, const void* v, const void* rho,
+                                     float* out, int64_t B, int64_t H, int64_t n, int64_t d,
+                                     double h, lla_dtype_t dtype, void* stream, lla_path_t path);
+
+/* Bytes of device scratch the Parallax `path` needs (0 if none, or if the arguments are
+ * invalid).  The fast path keeps there, per head and tile of 64 keys, in regions each rounded
+ * up to a multiple of 256 bytes: the tile image (K key-major as given, 64*72*2 bytes, then V
+ * feature-major as fp16, 64*72*2 bytes), the tile's key sum (d floats) and its largest key
+ * norm (one float).  The exact path needs none. */
+size_t lla_parallax_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
+                                   lla_path_t path);
+
+/* lla_parallax_forward_ex with caller-provided scratch, under the rules of lla_forward_ws. */
+lla_status_t lla_parallax_forward_ws(const void* q, const void* k, const void* v, const void* rho,
+                                     float* out, int64_t B, int64_t H, int64_t n, int64_t d,
+                                     double h, lla_dtype_t dtype, void* stream, lla_path_t path,
+                                     void* workspace, size_t workspace_bytes);
+
+/* As lla_path_available, for the Parallax paths. */
+int lla_parallax_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d);
 
 /* Kernel-level timing.  While enabled, every kernel launch of the library is bracketed by
  * HIP events on its stream.  lla_profile_collect waits for the recorded events, writes up to

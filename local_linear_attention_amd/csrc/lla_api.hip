@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 
 bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -92,22 +92,69 @@ hipError_t pool_for_current_device(hipMemPool_t* pool) {
     return hipSuccess;
 }
 
-lla_status_t run(const lla::Problem& p, bool fast, void* ws, size_t ws_bytes, bool may_allocate) {
-    if (!fast) return lla::launch_exact(p, static_cast<int>(p.n)) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
-    const size_t need = lla::fast_workspace_bytes(p.B, p.H, p.n, p.d);
-    if (need == 0) return lla::launch_fast(p, nullptr) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+// Launch with the scratch `need` bytes: none, the caller's workspace, or (when allowed) a
+// block of the library pool freed in stream order after the launch.
+template <typename Launch>
+lla_status_t run_scratch(size_t need, hipStream_t stream, void* ws, size_t ws_bytes, bool may_allocate,
+                         Launch launch) {
+    if (need == 0) return launch(nullptr) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
     if (ws) {
         if (ws_bytes < need) return LLA_ERR_WORKSPACE;
-        return lla::launch_fast(p, ws) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+        return launch(ws) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
     }
     if (!may_allocate) return LLA_ERR_WORKSPACE;
     hipMemPool_t pool = nullptr;
     if (pool_for_current_device(&pool) != hipSuccess) return LLA_ERR_HIP;
     void* scratch = nullptr;
-    if (hipMallocFromPoolAsync(&scratch, need, pool, p.stream) != hipSuccess) return LLA_ERR_HIP;
-    const hipError_t err = lla::launch_fast(p, scratch);
-    const hipError_t ferr = hipFreeAsync(scratch, p.stream);
+    if (hipMallocFromPoolAsync(&scratch, need, pool, stream) != hipSuccess) return LLA_ERR_HIP;
+    const hipError_t err = launch(scratch);
+    const hipError_t ferr = hipFreeAsync(scratch, stream);
     return (err == hipSuccess && ferr == hipSuccess) ? LLA_OK : LLA_ERR_HIP;
+}
+
+lla_status_t run(const lla::Problem& p, bool fast, void* ws, size_t ws_bytes, bool may_allocate) {
+    if (!fast) return lla::launch_exact(p, static_cast<int>(p.n)) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    return run_scratch(lla::fast_workspace_bytes(p.B, p.H, p.n, p.d), p.stream, ws, ws_bytes, may_allocate,
+                       [&](void* w) { return lla::launch_fast(p, w); });
+}
+
+// ---- Parallax
+lla_status_t validate_parallax(const void* q, const void* k, const void* v, const void* rho, const float* out,
+                               int64_t B, int64_t H, int64_t n, int64_t d, double h, lla_dtype_t dtype) {
+    if (!rho) return LLA_ERR_NULL;
+    const lla_status_t st = validate(q, k, v, out, B, H, n, d, h, 0.0, dtype);
+    if (st != LLA_OK) return st;
+    const int64_t rows = B * H * n;
+    const int64_t elt = dtype == LLA_DTYPE_F32 ? 4 : 2;
+    if (overlaps(out, rows * d * 4, rho, rows * d * elt)) return LLA_ERR_ALIAS;
+    return LLA_OK;
+}
+
+bool resolve_parallax_fast(lla_path_t path, int dtype, int64_t d, int64_t n, bool* fast) {
+    switch (path) {
+        case LLA_PATH_EXACT: *fast = false; return true;
+        case LLA_PATH_FAST: *fast = true; return lla::parallax_fast_supports(dtype, d, n);
+        case LLA_PATH_AUTO: *fast = lla::parallax_fast_supports(dtype, d, n); return true;
+    }
+    return false;
+}
+
+lla_status_t run_parallax(const lla::Problem& p, bool fast, void* ws, size_t ws_bytes, bool may_allocate) {
+    if (!fast) return lla::launch_parallax_exact(p) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    return run_scratch(lla::parallax_workspace_bytes(p.B, p.H, p.n, p.d), p.stream, ws, ws_bytes, may_allocate,
+                       [&](void* w) { return lla::launch_parallax_fast(p, w); });
+}
+
+lla_status_t parallax_entry(const void* q, const void* k, const void* v, const void* rho, float* out,
+                            int64_t B, int64_t H, int64_t n, int64_t d, double h, lla_dtype_t dtype,
+                            void* stream, lla_path_t path, void* ws, size_t ws_bytes, bool may_allocate) {
+    const lla_status_t st = validate_parallax(q, k, v, rho, out, B, H, n, d, h, dtype);
+    if (st != LLA_OK) return st;
+    bool fast = false;
+    if (!resolve_parallax_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
+    const lla::Problem p{q, k, v, out, B, H, n, d, h, 0.0, static_cast<int>(dtype),
+                         static_cast<hipStream_t>(stream), rho};
+    return run_parallax(p, fast, ws, ws_bytes, may_allocate);
 }
 
 // ---- kernel-level timing
@@ -218,6 +265,40 @@ lla_status_t lla_forward(const void* q, const void* k, const void* v, float* out
                          double h, double lambda,
                          lla_dtype_t dtype, void* stream) {
     return lla_forward_ex(q, k, v, out, B, H, n, d, h, lambda, dtype, stream, LLA_PATH_AUTO);
+}
+
+lla_status_t lla_parallax_forward(const void* q, const void* k, const void* v, const void* rho, float* out,
+                                  int64_t B, int64_t H, int64_t n, int64_t d, double h,
+                                  lla_dtype_t dtype, void* stream) {
+    return parallax_entry(q, k, v, rho, out, B, H, n, d, h, dtype, stream, LLA_PATH_AUTO, nullptr, 0, true);
+}
+
+lla_status_t lla_parallax_forward_ex(const void* q, const void* k, const void* v, const void* rho, float* out,
+                                     int64_t B, int64_t H, int64_t n, int64_t d, double h,
+                                     lla_dtype_t dtype, void* stream, lla_path_t path) {
+    return parallax_entry(q, k, v, rho, out, B, H, n, d, h, dtype, stream, path, nullptr, 0, true);
+}
+
+lla_status_t lla_parallax_forward_ws(const void* q, const void* k, const void* v, const void* rho, float* out,
+                                     int64_t B, int64_t H, int64_t n, int64_t d, double h,
+                                     lla_dtype_t dtype, void* stream, lla_path_t path,
+                                     void* workspace, size_t workspace_bytes) {
+    return parallax_entry(q, k, v, rho, out, B, H, n, d, h, dtype, stream, path, workspace, workspace_bytes,
+                          false);
+}
+
+size_t lla_parallax_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
+                                   lla_path_t path) {
+    if (!supported_shape(d, dtype) || validate_sizes(B, H, n, d) != LLA_OK) return 0;
+    bool fast = false;
+    if (!resolve_parallax_fast(path, static_cast<int>(dtype), d, n, &fast) || !fast) return 0;
+    return lla::parallax_workspace_bytes(B, H, n, d);
+}
+
+int lla_parallax_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d) {
+    if (!supported_shape(d, dtype)) return 0;
+    bool fast = false;
+    return resolve_parallax_fast(path, static_cast<int>(dtype), d, 1, &fast) ? 1 : 0;
 }
 
 int lla_profile_enable(int enable) {

@@ -1,0 +1,71 @@
+// Device-side helpers shared by the matrix-core kernels of liblla (gfx950): operand
+// vector types, MFMA wrappers, wave-uniform pointers and the XCD-aware block order.
+//
+// MFMA: v_mfma_f32_16x16x32_{bf16,f16}.  Lane l supplies row/column (l % 16) of A/B and 8
+// consecutive K-slots (l / 16); D[4 (l/16) + r][l % 16] lands in accumulator register r.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lla {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int FD = 64;              // head dimension of the matrix-core kernels
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Compiler fence for wave-private LDS exchanges: a lane reads words that other lanes of
+// the same wave stored, so no LDS access may move across a publish/consume boundary.
+// (A blocked variant of the LLA solve was miscompiled without such fences on gfx950:
+// an LDS access moved across a dependent one.  The fences cost no instructions.)
+#define LDS_FENCE() __asm__ volatile("" ::: "memory")
+
+// A wave-uniform pointer, rebuilt from scalar registers so that memory instructions can use
+// the scalar-base addressing form.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    return reinterpret_cast<const unsigned char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Value of x in lane `src` (a compile-time lane), broadcast to the wave.
+__device__ __forceinline__ float lane_value(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float4v mfma_bf16(bf16x8 a, bf16x8 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4v mfma_f16(half8 a, half8 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Block b -> (head bh, row block blk).  Work-groups go round-robin to the 8 XCDs, so
+// b % 8 picks the XCD: heads are taken 8 at a time (head 8 G + b % 8 on XCD b % 8) and, in
+// each group of 8, row blocks run longest first.  Each XCD's L2 then holds the packed K/V of
+// about one head at a time instead of a quarter of all heads.
+__device__ __forceinline__ void head_major_block(int b, int BH, int nblk, int* bh, int* blk) {
+    const int full = BH / 8, span = 8 * nblk;
+    int hg, r, hcnt;
+    if (b < full * span) {
+        hg = b / span; r = b - hg * span; hcnt = 8;
+    } else {
+        hg = full; r = b - full * span; hcnt = BH - 8 * full;
+    }
+    *blk = nblk - 1 - r / hcnt;
+    *bh = 8 * hg + r % hcnt;
+}
+
+}  // namespace
+}  // namespace lla

@@ -16,6 +16,7 @@ struct Problem {
     double h, lambda;
     int dtype;            // 0 = f32, 1 = bf16
     hipStream_t stream;
+    const void* rho;      // Parallax probe [B, H, n, d] (Parallax entry points only)
 };
 
 // fp64-accumulating path: every (dtype, d) the library accepts.  Processes rows
@@ -29,6 +30,14 @@ constexpr int64_t kFastMaxN = int64_t(1) << 22;
 bool fast_supports(int dtype, int64_t d, int64_t n);
 size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
 hipError_t launch_fast(const Problem& p, void* workspace);
+
+// Parallax forward with a given probe.  Fast path: bf16, d = 64, n up to kFastMaxN, with
+// tile images and per-tile key statistics in `workspace` (parallax_workspace_bytes);
+// exact path: fp64, every (dtype, d) the library accepts, no workspace.
+bool parallax_fast_supports(int dtype, int64_t d, int64_t n);
+size_t parallax_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
+hipError_t launch_parallax_fast(const Problem& p, void* workspace);
+hipError_t launch_parallax_exact(const Problem& p);
 
 // Kernel-level timing (lla_profile_enable): events recorded around each launch.
 void prof_begin(hipStream_t stream, const char* kernel);

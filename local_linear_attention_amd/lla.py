@@ -11,7 +11,9 @@ import ctypes
 import os
 
 __all__ = ["lla_forward", "lla_forward_ex", "lla_forward_ws", "lla_workspace_size",
-           "lla_path_available", "lla_profile_enable", "lla_profile_collect",
+           "lla_path_available", "lla_parallax_forward", "lla_parallax_forward_ex",
+           "lla_parallax_forward_ws", "lla_parallax_workspace_size", "lla_parallax_path_available",
+           "lla_profile_enable", "lla_profile_collect",
            "lla_status_string", "lla_version", "LLAError",
            "library_path", "load_library", "STATUS", "PATHS", "DTYPES"]
 
@@ -61,6 +63,18 @@ def load_library():
     lib.lla_forward_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int,
                                    vp, ctypes.c_int, vp, ctypes.c_size_t]
     lib.lla_forward_ws.restype = ctypes.c_int
+    lib.lla_parallax_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f64, ctypes.c_int, vp]
+    lib.lla_parallax_forward.restype = ctypes.c_int
+    lib.lla_parallax_forward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f64, ctypes.c_int, vp,
+                                            ctypes.c_int]
+    lib.lla_parallax_forward_ex.restype = ctypes.c_int
+    lib.lla_parallax_forward_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f64, ctypes.c_int, vp,
+                                            ctypes.c_int, vp, ctypes.c_size_t]
+    lib.lla_parallax_forward_ws.restype = ctypes.c_int
+    lib.lla_parallax_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.lla_parallax_workspace_size.restype = ctypes.c_size_t
+    lib.lla_parallax_path_available.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64]
+    lib.lla_parallax_path_available.restype = ctypes.c_int
     lib.lla_profile_enable.argtypes = [ctypes.c_int]
     lib.lla_profile_enable.restype = ctypes.c_int
     lib.lla_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p),
@@ -165,6 +179,72 @@ def lla_forward_ws(q, k, v, h: float, lam: float, workspace, path: str = "auto",
                                        ctypes.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes)
     if st != 0:
         raise LLAError(st, "lla_forward_ws")
+    return out
+
+
+def _marshal_probe(q, rho):
+    if rho.shape != q.shape or rho.dtype != q.dtype:
+        raise ValueError(f"rho must have q's shape and dtype; got {tuple(rho.shape)}, {rho.dtype}")
+    if not rho.is_cuda or not rho.is_contiguous() or rho.device != q.device:
+        raise ValueError("rho must be a contiguous device tensor on q's device")
+
+
+def lla_parallax_forward(q, k, v, rho, h: float, path: str = "auto", out=None, stream=None):
+    """Parallax forward of device tensors q, k, v, rho [B, H, n, d] (fp32 or bf16) -> fp32
+    out: o_i = softmax attention - Sigma_KV rho_i.  ``path`` is "auto", "exact" or "fast"."""
+    import torch
+    dtype, out = _marshal(q, k, v, out)
+    _marshal_probe(q, rho)
+    B, H, n, d = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load_library()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), rho.data_ptr(), out.data_ptr(), B, H, n, d, float(h),
+            dtype, ctypes.c_void_p(stream.cuda_stream))
+    if path == "auto":
+        st = lib.lla_parallax_forward(*args)
+    else:
+        st = lib.lla_parallax_forward_ex(*args, PATHS[path])
+    if st != 0:
+        raise LLAError(st, "lla_parallax_forward")
+    return out
+
+
+def lla_parallax_forward_ex(q, k, v, rho, h: float, path: str = "auto", out=None, stream=None):
+    """lla_parallax_forward with an explicit kernel path."""
+    return lla_parallax_forward(q, k, v, rho, h, path=path, out=out, stream=stream)
+
+
+def lla_parallax_workspace_size(B: int, H: int, n: int, d: int, dtype: str, path: str = "auto") -> int:
+    """Bytes of device scratch the chosen Parallax path needs (0 if none)."""
+    return int(load_library().lla_parallax_workspace_size(B, H, n, d, DTYPES[dtype], PATHS[path]))
+
+
+def lla_parallax_path_available(path: str, dtype: str, d: int) -> bool:
+    """Whether Parallax kernel path "auto" / "exact" / "fast" covers (dtype, d)."""
+    return bool(load_library().lla_parallax_path_available(PATHS[path], DTYPES[dtype], int(d)))
+
+
+def lla_parallax_forward_ws(q, k, v, rho, h: float, workspace, path: str = "auto", out=None, stream=None):
+    """Parallax forward with caller-provided scratch (a device tensor of at least
+    lla_parallax_workspace_size bytes, or None when none is needed)."""
+    import torch
+    dtype, out = _marshal(q, k, v, out)
+    _marshal_probe(q, rho)
+    B, H, n, d = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    if workspace is None:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = load_library().lla_parallax_forward_ws(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), rho.data_ptr(), out.data_ptr(), B, H, n, d, float(h), dtype,
+        ctypes.c_void_p(stream.cuda_stream), PATHS[path], ctypes.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes)
+    if st != 0:
+        raise LLAError(st, "lla_parallax_forward_ws")
     return out
 
 

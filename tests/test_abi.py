@@ -32,6 +32,9 @@ def declared_enums():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["lla_forward", "lla_forward_ex", "lla_forward_ws",
+                                    "lla_parallax_forward", "lla_parallax_forward_ex",
+                                    "lla_parallax_forward_ws", "lla_parallax_path_available",
+                                    "lla_parallax_workspace_size",
                                     "lla_path_available", "lla_profile_collect",
                                     "lla_profile_enable", "lla_status_string", "lla_version",
                                     "lla_workspace_size"]
@@ -149,3 +152,72 @@ def test_profile_collect_without_launches():
     prev = lla.lla_profile_enable(True)
     assert lla.lla_profile_collect() == []
     lla.lla_profile_enable(prev)
+
+
+# ---------------------------------------------------------------- Parallax entry points
+RHO = 0x60000000
+
+
+def call_parallax(lib, q=Q, k=K, v=V, rho=RHO, out=OUT, B=1, H=2, n=16, d=64, h=8.0, dtype=1, path=None):
+    args = [ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), ctypes.c_void_p(rho),
+            ctypes.c_void_p(out), B, H, n, d, h, dtype, None]
+    if path is None:
+        return lib.lla_parallax_forward(*args)
+    return lib.lla_parallax_forward_ex(*args, path)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(rho=0), 1), (dict(out=0), 1),
+    (dict(B=0), 2), (dict(n=0), 2), (dict(n=2 ** 31), 2),
+    (dict(h=0.0), 3), (dict(h=-2.0), 3), (dict(h=math.nan), 3), (dict(h=math.inf), 3),
+    (dict(d=48), 4), (dict(d=256), 4), (dict(dtype=2), 4),
+    (dict(out=Q + 64), 7), (dict(out=RHO - 64), 7), (dict(out=RHO + 128), 7),
+])
+def test_parallax_invalid_arguments_are_rejected_before_any_launch(kw, expect):
+    lib = _lib()
+    assert call_parallax(lib, **kw) == expect
+    assert call_parallax(lib, path=1, **kw) == expect
+    assert call_parallax(lib, path=2, **kw) == expect
+
+
+def test_parallax_unknown_or_uncovered_path_is_rejected():
+    lib = _lib()
+    assert call_parallax(lib, path=7) == 4
+    assert call_parallax(lib, path=2, d=32) == 4      # the matrix-core path is d = 64 only
+    assert call_parallax(lib, path=2, dtype=0) == 4   # and bf16 only
+
+
+def parallax_workspace_bytes(BH, n):
+    """Scratch of the Parallax matrix-core path: per head and 64-key tile the image (bf16 K
+    key-major with 72-half rows, fp16 V feature-major with 72-half rows), the tile key sum
+    (64 floats) and the largest key norm (one float), each region rounded up to 256 B."""
+    up = lambda x: (x + 255) // 256 * 256
+    tiles = -(-n // 64)
+    return up(BH * tiles * (64 * 72 * 2 + 64 * 72 * 2)) + up(BH * tiles * 64 * 4) + up(BH * tiles * 4)
+
+
+def test_parallax_workspace_size_and_paths():
+    from local_linear_attention_amd import lla
+    assert lla.lla_parallax_workspace_size(2, 16, 4096, 64, "bf16", "fast") == parallax_workspace_bytes(32, 4096)
+    assert lla.lla_parallax_workspace_size(2, 16, 4096, 64, "bf16", "auto") == parallax_workspace_bytes(32, 4096)
+    assert lla.lla_parallax_workspace_size(1, 3, 1, 64, "bf16", "fast") == parallax_workspace_bytes(3, 1)
+    assert lla.lla_parallax_workspace_size(1, 1, 300, 64, "bf16", "exact") == 0
+    assert lla.lla_parallax_workspace_size(1, 1, 300, 64, "f32", "auto") == 0
+    assert lla.lla_parallax_workspace_size(1, 1, (1 << 22) + 1, 64, "bf16", "auto") == 0
+    assert lla.lla_parallax_workspace_size(1, 1, 300, 48, "bf16", "auto") == 0
+    for dt in ("f32", "bf16"):
+        for d in (16, 32, 64, 128):
+            assert lla.lla_parallax_path_available("auto", dt, d)
+            assert lla.lla_parallax_path_available("exact", dt, d)
+        assert not lla.lla_parallax_path_available("exact", dt, 48)
+    assert lla.lla_parallax_path_available("fast", "bf16", 64)
+    assert not lla.lla_parallax_path_available("fast", "bf16", 128)
+    assert not lla.lla_parallax_path_available("fast", "f32", 64)
+
+
+def test_parallax_ws_validation_before_launch():
+    lib = _lib()
+    args = [ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V), ctypes.c_void_p(RHO),
+            ctypes.c_void_p(OUT), 1, 2, 4096, 64, 8.0, 1, None, 2]
+    assert lib.lla_parallax_forward_ws(*args, None, 0) == 5
+    assert lib.lla_parallax_forward_ws(*args, ctypes.c_void_p(0x50000000), 4096) == 5
