@@ -1,12 +1,16 @@
-"""Throughput of the causal LLA forward on one MI355X.
+"""Throughput of the causal LLA forward (or the Parallax forward with a given probe) on one
+MI355X.
 
-One step is one lla_forward call over the whole workload (every query row of every head)
-with q, k, v already resident in HBM.  Prints one JSON line.
+One step is one lla_forward call (lla_parallax_forward with --method parallax) over the whole
+workload (every query row of every head) with the inputs already resident in HBM.  Prints
+one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d24] [--path auto]
+                    [--method lla|parallax]
 
 The default workload is B=2, H=16, n=4096, d=64 with bf16 inputs (head shape of a
-1024-wide, 16-head model), h = 8, lambda = 1e-2.
+1024-wide, 16-head model), h = 8, lambda = 1e-2; with --method parallax the same q, k, v
+plus an RMS-normalised probe (workload parallax_d24).
 """
 from __future__ import annotations
 
@@ -22,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "LLA fwd queries/s + TFLOP/s (% MFMA peak) at B2 H16 n4096 d64 bf16, 1 GPU"
+METRIC_PARALLAX = "Parallax fwd (given probe) queries/s + TFLOP/s (% MFMA peak) at B2 H16 n4096 d64 bf16, 1 GPU"
 
 # MI355X published peaks.
 PEAK = {
@@ -57,12 +62,27 @@ KERNEL_BOUND = {
     "lla_keymom_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_rows_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_probe_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_parallax_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla_parallax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_parallax_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
 }
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
     "fast": ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel",
              "lla_probe_kernel"],
 }
+PARALLAX_KERNELS = {
+    "exact": ["lla_parallax_exact_kernel"],
+    "fast": ["lla_parallax_pack_kernel", "lla_parallax_kernel"],
+}
+
+
+def parallax_flops(B, H, n, d):
+    """Algorithmic flops of one Parallax forward (given probe): per causal pair the score
+    (2d), the probe score (2d), the covariance-branch weight P1 s2 (1), the two weight sums
+    (2) and the two weighted value sums (4d); per query the merge (4d)."""
+    P = B * H * n * (n + 1) // 2
+    return P * (8 * d + 3) + B * H * n * 4 * d
 
 
 def pair_count(BH, lo, hi):
@@ -99,6 +119,10 @@ def kernel_flops(name, B, H, n, d, path):
                    for part in ("lla_short_kernel", "lla_moments_kernel", "lla_keymom_kernel"))
     if name == "lla_probe_kernel":
         return pair_count(BH, rowp, n) * (4 * d + 2) + BH * (n - rowp) * 4 * d
+    if name in ("lla_parallax_kernel", "lla_parallax_exact_kernel"):
+        return parallax_flops(B, H, n, d)
+    if name == "lla_parallax_pack_kernel":
+        return 0                      # data movement only (K, V repacked once)
     raise KeyError(name)
 
 
@@ -130,11 +154,12 @@ def load_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, seconds):
-    """The fp64 oracle on a bounded random sample of the workload's rows."""
+def cpu_baseline(w, q, k, v, seconds, rho=None):
+    """The fp64 oracle (LLA, or Parallax when a probe is given) on a bounded random sample of
+    the workload's rows."""
     import numpy as np
 
-    from oracle import default_workers, lla_rows
+    from oracle import default_workers, lla_rows, parallax_rows
     workers = default_workers()
     rng = np.random.default_rng(12345)
     total_cost = w.B * w.H * w.n * (w.n + 1) / 2
@@ -144,7 +169,10 @@ def cpu_baseline(w, q, k, v, seconds):
         rows = [(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.n)))
                 for _ in range(batch)]
         t0 = time.perf_counter()
-        lla_rows(q, k, v, w.h, w.lam, rows, workers=workers)
+        if rho is None:
+            lla_rows(q, k, v, w.h, w.lam, rows, workers=workers)
+        else:
+            parallax_rows(q, k, v, rho, w.h, rows, workers=workers)
         elapsed += time.perf_counter() - t0
         done_rows += len(rows)
         done_cost += sum(i + 1 for (_, _, i) in rows)
@@ -166,7 +194,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="d24")
+    ap.add_argument("--method", default="lla", choices=["lla", "parallax"])
+    ap.add_argument("--workload", default=None,
+                    help="default: d24 (LLA) or parallax_d24 (Parallax)")
     ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -185,15 +215,19 @@ def main():
     import torch
 
     import lla_inputs
-    from local_linear_attention_amd import (lla_forward_ex, lla_path_available, lla_profile_collect,
-                                            lla_profile_enable, load_library)
+    from local_linear_attention_amd import (lla_forward_ex, lla_parallax_forward, lla_parallax_path_available,
+                                            lla_path_available, lla_profile_collect, lla_profile_enable,
+                                            load_library)
 
-    w = lla_inputs.WORKLOADS[args.workload]
+    parallax = args.method == "parallax"
+    w = lla_inputs.WORKLOADS[args.workload or ("parallax_d24" if parallax else "d24")]
     q, k, v, _ = lla_inputs.generate(w)
+    rho = lla_inputs.generate_probe(w)[0] if parallax else None
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v))
+    tr = torch.from_numpy(rho).to(tdt).to(dev).contiguous() if parallax else None
     out = torch.empty(tq.shape, dtype=torch.float32, device=dev)
     load_library()
 
@@ -206,14 +240,20 @@ def main():
         del src, dst
 
     path = args.path
+    available = lla_parallax_path_available if parallax else lla_path_available
     if path == "auto":
         # the path the library picks by default for this dtype and head size
-        path = "fast" if (w.dtype == "bf16" and lla_path_available("fast", w.dtype, w.d)) \
-            else "exact"
+        path = "fast" if (w.dtype == "bf16" and available("fast", w.dtype, w.d)) else "exact"
     stream = torch.cuda.current_stream(dev)
 
+    def step():
+        if parallax:
+            lla_parallax_forward(tq, tk, tv, tr, w.h, path=path, out=out, stream=stream)
+        else:
+            lla_forward_ex(tq, tk, tv, w.h, w.lam, path=path, out=out, stream=stream)
+
     for _ in range(args.warmup):
-        lla_forward_ex(tq, tk, tv, w.h, w.lam, path=path, out=out, stream=stream)
+        step()
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -224,7 +264,7 @@ def main():
     t_all0.record(stream)
     for s in range(args.steps):
         starts[s].record(stream)
-        lla_forward_ex(tq, tk, tv, w.h, w.lam, path=path, out=out, stream=stream)
+        step()
         ends[s].record(stream)
     t_all1.record(stream)
     torch.cuda.synchronize()
@@ -237,7 +277,7 @@ def main():
     lla_profile_enable(True)
     lla_profile_collect()
     for _ in range(args.steps):
-        lla_forward_ex(tq, tk, tv, w.h, w.lam, path=path, out=out, stream=stream)
+        step()
     torch.cuda.synchronize()
     rec = lla_profile_collect()
     lla_profile_enable(False)
@@ -253,12 +293,27 @@ def main():
                          "tflops": fl / (avg * 1e-3) / 1e12, "bound": bound, "peak": peak}
     dom = max(kernels, key=lambda nm: kernels[nm]["avg_ms"] * kernels[nm]["launches"])
     dk = kernels[dom]
-    flops = path_flops(w.B, w.H, w.n, w.d, path)
+    flops = parallax_flops(w.B, w.H, w.n, w.d) if parallax else path_flops(w.B, w.H, w.n, w.d, path)
     achieved_tflops = flops / (ms_per_step * 1e-3) / 1e12
     traffic = load_traffic(dom, w.name)
 
+    if parallax:
+        config_text = f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs and probe, h={w.h:g}"
+        flop_count = {"formulation": "Parallax: per pair 8d + 3 (two scores, one weight product, "
+                                     "two weight sums, two value sums), per query 4d",
+                      "flops": flops}
+        arith = {"exact": "f64", "fast": "bf16 scores / f16 weights and values, f32 accumulate"}[path]
+    else:
+        config_text = (f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs, h={w.h:g}, "
+                       f"lambda={w.lam:g}")
+        flop_count = {"formulation": ("NS for rows i < 4d, min (probe pass) for rows i >= 4d"
+                                      if path == "fast" else "NS"),
+                      "flops": flops,
+                      "F_NS": alg_flops(w.B, w.H, w.n, w.d, "NS"),
+                      "F_min": alg_flops(w.B, w.H, w.n, w.d, "min")}
+        arith = PATH_ARITH[path]
     result = {
-        "metric": METRIC,
+        "metric": METRIC_PARALLAX if parallax else METRIC,
         "value": w.queries / (ms_per_step * 1e-3),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -268,20 +323,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": PATH_ARITH[path],
+        "dtype": arith,
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs, h={w.h:g}, "
-                        f"lambda={w.lam:g}",
+            "workload": config_text,
             "B": w.B, "H": w.H, "n": w.n, "d": w.d, "input_dtype": w.dtype,
-            "h": w.h, "lambda": w.lam, "path": path, "queries": w.queries,
+            "h": w.h, "lambda": None if parallax else w.lam, "path": path, "queries": w.queries,
         },
         "tflops": achieved_tflops,
-        "flop_count": {"formulation": ("NS for rows i < 4d, min (probe pass) for rows i >= 4d"
-                                       if path == "fast" else "NS"),
-                       "flops": flops,
-                       "F_NS": alg_flops(w.B, w.H, w.n, w.d, "NS"),
-                       "F_min": alg_flops(w.B, w.H, w.n, w.d, "min")},
+        "flop_count": flop_count,
         "kernels": kernels,
         "timing_ms": {"median": statistics.median(per_ms), "p10": float(np.percentile(per_ms, 10)),
                       "p90": float(np.percentile(per_ms, 90))},
@@ -298,7 +348,7 @@ def main():
         "gfx": torch.cuda.get_device_properties(dev).gcnArchName,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, rho=rho)
     print(json.dumps(result), flush=True)
 
 

@@ -152,9 +152,9 @@ lla_status_t lla_parallax_forward_ex(const void* q, const void* k, const void* v
 
 /* Bytes of device scratch the Parallax `path` needs (0 if none, or if the arguments are
  * invalid).  The fast path keeps there, per head and tile of 64 keys, in regions each rounded
- * up to a multiple of 256 bytes: the tile image (K key-major as given, 64*72*2 bytes, then V
- * feature-major as fp16, 64*72*2 bytes), the tile's key sum (d floats) and its largest key
- * norm (one float).  The exact path needs none. */
+ * up to a multiple of 256 bytes: the tile image of 18432 bytes (K key-major as given, 64*72*2
+ * bytes, then V feature-major as fp16, 64*68*2 bytes, then padding), the tile's key sum
+ * (d floats) and its largest key norm (one float).  The exact path needs none. */
 size_t lla_parallax_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                                    lla_path_t path);
 

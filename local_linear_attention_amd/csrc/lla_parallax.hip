@@ -17,7 +17,9 @@
 //   * the probe scores are centred, s2_j = rho . (k_j - a) with a the head's mean key: a
 //     constant shift of s2 cancels in the merge, and centring keeps P2 small, so its fp16
 //     rounding error is small;
-//   * s2 is scaled by a per-query power of two sigma that keeps |P2| below 2^14 (P1 <= 1 and
+//   * the running max is moved only when a score exceeds it by more than 2^8 in weight
+//     (a lane-local test; the rescale is exact whenever it happens), so P1 < 2^8;
+//   * s2 is scaled by a per-query power of two sigma that keeps |P2| below 2^14 (P1 < 2^8 and
 //     |s2| <= |rho| (max_j |k_j| + |a|)), so that P2 fits fp16; the merge divides by it;
 //   * P1 and P2 enter the P V products as fp16 (v as fp16, exact for bf16 values in the fp16
 //     range); d1 and d2 sum the same rounded values, so the rounding only perturbs weights.
@@ -34,16 +36,19 @@ namespace {
 
 constexpr int MT = 64;                       // keys per tile
 constexpr int KM_LD = FD + 8;                // key-major bf16 row (halves): 64 features + 8 padding
-constexpr int V_LD = MT + 8;                 // feature-major fp16 row (halves): 64 keys + 8 padding
+// Feature-major fp16 row (halves): 64 keys + 4 of padding.  A row is 34 banks, so the 16
+// rows that one 8-byte read of 16 lanes touches fall on distinct bank pairs.
+constexpr int V_LD = MT + 4;
 constexpr int X_KIMG = MT * KM_LD * 2;       // 9 KiB
-constexpr int X_TILE = X_KIMG + FD * V_LD * 2;   // tile image: bf16 K key-major | fp16 V feature-major
+// Tile image: bf16 K key-major | fp16 V feature-major, padded to whole KiB (the tail unused).
+constexpr int X_TILE = (X_KIMG + FD * V_LD * 2 + 1023) / 1024 * 1024;
 constexpr int X_WAVES = 4;
 constexpr int X_SETS = 2;                    // query sets of 16 per wave
 constexpr int X_QW = 16 * X_SETS;
 constexpr int X_QB = X_WAVES * X_QW;         // 128 queries per block
 constexpr int X_LOADS = X_TILE / 1024;       // wave-wide copies of 16 B per lane per tile
 constexpr int X_WLOADS = (X_LOADS + X_WAVES - 1) / X_WAVES;
-constexpr int X_NBUF = 2;
+constexpr int X_NBUF = 3;                    // tile ring: compute t, t+1 landing, t+2 in flight
 static_assert(X_TILE % 1024 == 0 && X_KIMG % 1024 == 0, "tile image must be whole wave copies");
 
 __device__ __forceinline__ float wave_max64(float x) {
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(256) void lla_parallax_pack_kernel(const uint16_t* 
 
 // The streaming pass.  Block = 4 waves x 32 queries (two sets of 16 per wave, which share
 // the key and value operands), two blocks per CU; each tile image is copied straight into
-// one of two LDS buffers while the other is in use.  Per tile, wave and query set:
+// a ring of three LDS buffers, two tiles ahead of the one in use.  Per tile, wave and query set:
 // the tile in two steps of 32 keys:
 //   S1^T = K Q^T and S2^T = K R^T (bf16 MFMA pairs, one K operand for both), lane (g, c)
 //   register r = key 16 kb + 4g + r of query c;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
 
     // Query set st: column c is query qw0 + 16 st + c (clamped to n - 1).
     bf16x8 qf[X_SETS][2], rf[X_SETS][2];
-    float cst[X_SETS], sg[X_SETS];
+    float csg[X_SETS], sg[X_SETS];   // per query: -(rho . a) sigma and sigma
     int qc[X_SETS];
 #pragma unroll
     for (int st = 0; st < X_SETS; ++st) {
@@ -185,7 +190,6 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
             const uint4 qr = *reinterpret_cast<const uint4*>(q + off);
             const uint4 rr = *reinterpret_cast<const uint4*>(rho + off);
             qf[st][ks] = __builtin_bit_cast(bf16x8, qr);
-            rf[st][ks] = __builtin_bit_cast(bf16x8, rr);
             const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -198,46 +202,112 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
         pd += __shfl_xor(pd, 32);
         pn += __shfl_xor(pn, 16);
         pn += __shfl_xor(pn, 32);
-        cst[st] = pd;   // rho . a
-        // sigma = 2^(14 - e) with |rho| rbound = f 2^e, f in [0.5, 1): |s2| sigma < 2^14.
+        // sigma = 2^(14 - e) with |rho| rbound = f 2^e, f in [0.5, 1): P1 <= 1 and
+        // |s2 - rho.a| sigma < 2^14, so |P2| < 2^14.
         const float bound = sqrtf(pn) * rbound;
         int ex = 0;
         (void)frexpf(bound, &ex);
-        ex = min(max(ex, -100), 120);
+        ex = min(max(ex, -100), 100);
         sg[st] = (bound > 0.0f && bound < INFINITY) ? ldexpf(1.0f, 14 - ex) : 1.0f;
+        csg[st] = -pd * sg[st];   // -(rho . a) sigma: the initial value of the probe-score sums
+        // The probe operand carries sigma: a power of two, exact in bf16.
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint4 rr = *reinterpret_cast<const uint4*>(rho + base + static_cast<int64_t>(qc[st]) * FD + 32 * ks + 8 * g);
+            const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
+            bf16x8 sc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sc[e] = static_cast<__bf16>(sg[st] * __uint_as_float((e & 1) ? (rw[e >> 1] & 0xffff0000u)
+                                                                              : (rw[e >> 1] << 16)));
+            rf[st][ks] = sc;
+        }
     }
 
     const __amdgpu_buffer_rsrc_t ires = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(uniform_ptr(img + static_cast<int64_t>(bh) * ptiles * X_TILE)), 0,
         ptiles * X_TILE, 0x00020000);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
-    // Tile tt -> buffer tt % 2; wave w copies KiB chunks w, w+4, ... (the surplus ones
-    // repeat the last chunk); past the last tile the last one is re-read.
-    auto issue = [&](int tt) {
+    // Tile tt -> buffer tt % 3; wave w copies KiB chunks w, w+4, ... of the first NCH chunks of
+    // the tile image (the surplus ones repeat the last chunk); past the last tile the last one
+    // is re-read into a dead buffer.
+    auto issue = [&](auto nch, int tt) {
+        constexpr int NCH = decltype(nch)::value, NW = (NCH + X_WAVES - 1) / X_WAVES;
         const int ts = min(tt, ntiles - 1);
         const uint32_t dst = lds0 + static_cast<uint32_t>((tt % X_NBUF) * X_TILE);
 #pragma unroll
-        for (int e = 0; e < X_WLOADS; ++e) {
-            const int u = min(wu + X_WAVES * e, X_LOADS - 1);
+        for (int e = 0; e < NW; ++e) {
+            const int u = min(wu + X_WAVES * e, NCH - 1);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ires, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
                 16, lane * 16 + u * 1024, ts * X_TILE, 0, 0);
         }
     };
-    // The next tile's copies have landed (the only loads in flight) and every wave is done
-    // with the buffer they overwrite next.
-    auto wait_and_sync = [] {
-        __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0x0 << 8));
+    // Tile t+1 has landed -- only tile t+2's copies (NW per wave) may still be in flight: they
+    // are the only vector loads in the loops -- and every wave is done with the buffer the
+    // next copies overwrite.
+    auto next_tile = [](auto nch) {
+        constexpr int NW = (decltype(nch)::value + X_WAVES - 1) / X_WAVES;
+        static_assert(NW < 16, "vmcnt operand is 4 bits here");
+        __builtin_amdgcn_s_waitcnt(NW | (0x7 << 4) | (0x0 << 8));
         LDS_FENCE();
         __builtin_amdgcn_s_barrier();
         LDS_FENCE();
     };
+    using KeysOnly = std::integral_constant<int, X_KIMG / 1024>;
+    using WholeTile = std::integral_constant<int, X_LOADS>;
 
-    float m_run[X_SETS], d1p[X_SETS], d2p[X_SETS];
+    // ---- pass 1: row maxima m_i = max_{j <= i} q_i.k_j, keys only.  Lane (g, c) register r of
+    // a score block = key 16 kb + 4g + r of query c of the set.
+    float mloc[X_SETS] = {-INFINITY, -INFINITY};
+    issue(KeysOnly{}, 0);
+    issue(KeysOnly{}, 1);
+    next_tile(KeysOnly{});
+    for (int t = 0; t < ntiles; ++t) {
+        issue(KeysOnly{}, t + 2);
+        const int j0 = t * MT;
+        auto tile_max = [&](auto masked) {
+            const unsigned char* cur = ring + (t % X_NBUF) * X_TILE;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int ro = (kb * 16 + c) * (KM_LD * 2) + 16 * g;
+                const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(cur + ro);
+                const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cur + ro + 64);
+#pragma unroll
+                for (int st = 0; st < X_SETS; ++st) {
+                    float4v a = {0.f, 0.f, 0.f, 0.f};
+                    a = mfma_bf16(k0, qf[st][0], a);
+                    a = mfma_bf16(k1, qf[st][1], a);
+                    const bool full = !decltype(masked)::value || j0 + MT - 1 <= qw0 + 16 * st;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        mloc[st] = fmaxf(mloc[st], (full || j0 + kb * 16 + 4 * g + r <= qc[st]) ? a[r] : -INFINITY);
+                }
+            }
+        };
+        if (j0 + MT - 1 <= qw0) tile_max(std::false_type{});
+        else if (j0 <= wave_last) tile_max(std::true_type{});   // wave-uniform
+        next_tile(KeysOnly{});
+    }
+    // Every wave is done with the ring (and its copies have landed) before pass 2 refills it.
+    __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0x0 << 8));
+    LDS_FENCE();
+    __builtin_amdgcn_s_barrier();
+    LDS_FENCE();
+    float mrow[X_SETS];   // log2 units
+#pragma unroll
+    for (int st = 0; st < X_SETS; ++st) {
+        float m = fmaxf(mloc[st], __shfl_xor(mloc[st], 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        mrow[st] = m * sl2;
+    }
+
+    // ---- pass 2: weights P1 = 2^(s1 log2e/h - m) <= 1 and P2 = P1 (s2 - rho.a) sigma, and the
+    // sums d1, d2, O1, O2, in two 32-key steps per tile.
+    float d1p[X_SETS], d2p[X_SETS];
     float4v o1[X_SETS][4], o2[X_SETS][4];
 #pragma unroll
     for (int st = 0; st < X_SETS; ++st) {
-        m_run[st] = -INFINITY;
         d1p[st] = 0.0f;
         d2p[st] = 0.0f;
 #pragma unroll
@@ -247,18 +317,22 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
         }
     }
     const h16x2 one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-    issue(0);
-    wait_and_sync();
+    float4v csv[X_SETS];   // initial value of the probe-score sums
+#pragma unroll
+    for (int st = 0; st < X_SETS; ++st) csv[st] = float4v{csg[st], csg[st], csg[st], csg[st]};
+    issue(WholeTile{}, 0);
+    issue(WholeTile{}, 1);
+    next_tile(WholeTile{});
     for (int t = 0; t < ntiles; ++t) {
-        issue(t + 1);   // into the buffer tile t-1 used
+        issue(WholeTile{}, t + 2);   // into the buffer tile t-1 used
         const int j0 = t * MT;
         // Every tile a wave takes starts at or below its first query (tiles and waves are
-        // aligned to 64 and 32 rows), so each query has at least one key in it.  A tile
-        // wholly below the wave's first query needs no causal mask.
+        // aligned to 64 and 32 rows); a tile wholly below the wave's first query needs no
+        // causal mask.
         auto tile_body = [&](auto masked) {
             const unsigned char* cur = ring + (t % X_NBUF) * X_TILE;
             const _Float16* VI = reinterpret_cast<const _Float16*>(cur + X_KIMG);
-            // Two 32-key steps; K-slots of lane group g in a step: keys 4g.. and 16 + 4g..
+            // K-slots of lane group g in step ks: keys 32 ks + 4g.. and 32 ks + 16 + 4g..
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 float4v s1[X_SETS][2], s2[X_SETS][2];
@@ -269,47 +343,25 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
                     const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cur + ro + 64);
 #pragma unroll
                     for (int st = 0; st < X_SETS; ++st) {
-                        float4v a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+                        float4v a = {0.f, 0.f, 0.f, 0.f};
                         a = mfma_bf16(k0, qf[st][0], a);
-                        s1[st][hb] = mfma_bf16(k1, qf[st][1], a);
-                        b = mfma_bf16(k0, rf[st][0], b);
-                        s2[st][hb] = mfma_bf16(k1, rf[st][1], b);
+                        s1[st][hb] = mfma_bf16(k1, qf[st][1], a);   // pass 1's operands and order
+                        const float4v b = mfma_bf16(k0, rf[st][0], csv[st]);
+                        s2[st][hb] = mfma_bf16(k1, rf[st][1], b);   // (rho . (k - a)) sigma
                     }
                 }
                 half4 p1[X_SETS][2], p2[X_SETS][2];
 #pragma unroll
                 for (int st = 0; st < X_SETS; ++st) {
-                    const bool full = !decltype(masked)::value || j0 + MT - 1 <= qw0 + 16 * st;
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = j0 + (2 * ks + hb) * 16 + 4 * g + r;
-                            mx = fmaxf(mx, (full || j <= qc[st]) ? s1[st][hb][r] : -INFINITY);
-                        }
-                    mx = fmaxf(mx, __shfl_xor(mx, 16));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    const float m_new = fmaxf(m_run[st], mx * sl2);
-                    if (__any(m_new > m_run[st])) {   // wave-uniform
-                        const float alpha = __builtin_amdgcn_exp2f(m_run[st] - m_new);
-                        d1p[st] *= alpha;
-                        d2p[st] *= alpha;
-#pragma unroll
-                        for (int fv = 0; fv < 4; ++fv) {
-                            o1[st][fv] *= alpha;
-                            o2[st][fv] *= alpha;
-                        }
-                    }
-                    m_run[st] = m_new;
+                    const bool full = !decltype(masked)::value || j0 + 32 * ks + 31 <= qw0 + 16 * st;
 #pragma unroll
                     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            float e = __builtin_amdgcn_exp2f(fmaf(s1[st][hb][r], sl2, -m_new));
+                            float e = __builtin_amdgcn_exp2f(fmaf(s1[st][hb][r], sl2, -mrow[st]));
                             if (!full) e = j0 + (2 * ks + hb) * 16 + 4 * g + r <= qc[st] ? e : 0.0f;
                             p1[st][hb][r] = static_cast<_Float16>(e);
-                            p2[st][hb][r] = static_cast<_Float16>(e * ((s2[st][hb][r] - cst[st]) * sg[st]));
+                            p2[st][hb][r] = static_cast<_Float16>(e * s2[st][hb][r]);
                         }
                         d1p[st] = __builtin_amdgcn_fdot2(__builtin_shufflevector(p1[st][hb], p1[st][hb], 0, 1), one2, d1p[st], false);
                         d1p[st] = __builtin_amdgcn_fdot2(__builtin_shufflevector(p1[st][hb], p1[st][hb], 2, 3), one2, d1p[st], false);
@@ -335,8 +387,10 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
         };
         if (j0 + MT - 1 <= qw0) tile_body(std::false_type{});
         else if (j0 <= wave_last) tile_body(std::true_type{});   // wave-uniform
-        wait_and_sync();
+        next_tile(WholeTile{});
     }
+    // Copies past the last tile are still landing in LDS: let them finish before exit.
+    __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
 
     // Merge: o = O1/d1 - (O2/d1 - (O1/d1)(d2/d1)) / sigma; lane (g, c) register r of set st
     // is feature 16 fv + 4g + r of query qw0 + 16 st + c.
