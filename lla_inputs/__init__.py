@@ -24,6 +24,17 @@ Workloads (the shapes of the pages' settings, synthetic stand-ins for their data
                 recipes, so bit-identical) plus a Parallax probe rho (``generate_probe``);
                 h as there, lambda unused.
 
+Decode workloads (``DECODE_WORKLOADS``, Parallax decode: one query per (batch, head) against a
+key-value cache of L positions; batch and context sizes from the pages' decode sweep):
+
+* ``decode_b8_l8192``  B8 H16 L8192 d64 bf16 (seed 5); h = 8.
+* ``decode_b1_l32768`` B1 H16 L32768 d64 bf16 (seed 6): the sweep's longest context.
+* ``decode_b64_l1024`` B64 H16 L1024 d64 bf16 (seed 7): many short caches.
+* ``decode_d128``      B8 H8 L8192 d128 bf16 (seed 8); h = sqrt(128): the I/O-matched head size.
+Decode recipe: ``default_rng(seed)`` draws, in fp64 and in this order, q ``[B,H,d]``, k and v
+``[B,H,L,d]`` (standard normal), then rho ``[B,H,d]``; q, k and rho are RMS-normalised, v is
+left as drawn; all four are cast once to the storage dtype.
+
 Probe recipe (Parallax workloads): ``numpy.random.default_rng([seed, 1])`` -- a stream of
 its own, so drawing rho changes none of q, k, v -- draws rho ``[B,H,n,d]`` standard normal
 in fp64; rho is RMS-normalised like q and k (the pages' Parallax layers apply RMSNorm to
@@ -45,7 +56,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "make_probe", "round_to_bf16", "generate",
-           "generate_probe"]
+           "generate_probe", "DecodeWorkload", "DECODE_WORKLOADS", "generate_decode"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -164,3 +175,41 @@ def generate_probe(w: Workload):
     the fp64 pre-cast array: ``(rho, rho64)``."""
     rho64 = make_probe(w.B, w.H, w.n, w.d, w.seed)
     return cast(rho64, w.dtype), rho64
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    L: int   # cached positions; the query is the newest one and sees all of them
+    d: int
+    dtype: str
+    h: float
+    seed: int
+
+    @property
+    def queries(self) -> int:
+        return self.B * self.H
+
+    def with_shape(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+DECODE_WORKLOADS = {
+    "decode_b8_l8192": DecodeWorkload("decode_b8_l8192", 8, 16, 8192, 64, "bf16", 8.0, 5),
+    "decode_b1_l32768": DecodeWorkload("decode_b1_l32768", 1, 16, 32768, 64, "bf16", 8.0, 6),
+    "decode_b64_l1024": DecodeWorkload("decode_b64_l1024", 64, 16, 1024, 64, "bf16", 8.0, 7),
+    "decode_d128": DecodeWorkload("decode_d128", 8, 8, 8192, 128, "bf16", math.sqrt(128.0), 8),
+}
+
+
+def generate_decode(w: DecodeWorkload):
+    """Return (q [B,H,d], k [B,H,L,d], v [B,H,L,d], rho [B,H,d]) of a decode workload as
+    float32 arrays holding the cast values."""
+    rng = np.random.default_rng(w.seed)
+    q = _rms(rng.standard_normal((w.B, w.H, w.d)))
+    k = _rms(rng.standard_normal((w.B, w.H, w.L, w.d)))
+    v = rng.standard_normal((w.B, w.H, w.L, w.d))
+    rho = _rms(rng.standard_normal((w.B, w.H, w.d)))
+    return tuple(cast(x, w.dtype) for x in (q, k, v, rho))

@@ -35,7 +35,8 @@ import numpy as np
 
 from .lla_oracle import map_rows
 
-__all__ = ["parallax_row", "parallax_row_parts", "parallax_rows", "parallax_forward"]
+__all__ = ["parallax_row", "parallax_row_parts", "parallax_rows", "parallax_forward",
+           "parallax_decode"]
 
 
 def parallax_row_parts(q_i, K, V, rho_i, h):
@@ -78,3 +79,21 @@ def parallax_forward(q, k, v, rho, h, workers=1):
     B, H, n, _ = q.shape
     rows = [(b, hh, i) for b in range(B) for hh in range(H) for i in range(n)]
     return parallax_rows(q, k, v, rho, h, rows, workers=workers).reshape(B, H, n, -1)
+
+
+
+def parallax_decode(q, k, v, rho, h):
+    """Parallax decode step: one query per (batch, head) against its whole key-value cache.
+
+    q, rho: [B, H, d]; k: [B, H, L, d]; v: [B, H, L, d_v].  Every cached key is in the
+    query's prefix (the query is the newest position; its own key is the cache's last
+    entry), so each output is parallax_row over the full cache.  Returns [B, H, d_v] fp64.
+    (The decode setting of the "Parallax" blog post, section 3 "Optimized Decode Kernel".)
+    """
+    q = np.asarray(q)
+    B, H, _ = q.shape
+    out = np.empty((B, H, np.asarray(v).shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for hh in range(H):
+            out[b, hh] = parallax_row(q[b, hh], k[b, hh], v[b, hh], rho[b, hh], h)
+    return out

@@ -47,3 +47,13 @@ def test_probe_stream_is_separate_and_rms_normalised():
     assert np.array_equal(lla_inputs.round_to_bf16(rho), rho)
     assert np.allclose(np.mean(rho64 * rho64, -1), 1.0, atol=1e-5)
     assert not np.allclose(rho64, lla_inputs.make_inputs(1, 2, 48, 64, w.seed, "rms")[0])
+
+
+def test_decode_generator_is_deterministic_and_cast():
+    w = lla_inputs.DECODE_WORKLOADS["decode_b8_l8192"].with_shape(B=2, H=3, L=40)
+    a, b = lla_inputs.generate_decode(w), lla_inputs.generate_decode(w)
+    shapes = [(2, 3, 64), (2, 3, 40, 64), (2, 3, 40, 64), (2, 3, 64)]
+    for x, y, shp in zip(a, b, shapes):
+        assert np.array_equal(x, y) and x.shape == shp and x.dtype == np.float32
+        assert np.array_equal(lla_inputs.round_to_bf16(x), x)
+    assert np.allclose(np.mean(a[1].astype(np.float64) ** 2, -1), 1.0, atol=2e-2)

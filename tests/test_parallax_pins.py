@@ -222,3 +222,31 @@ def test_row_subset_and_pool_match_full_forward():
     parts = parallax_row_parts(q[0, 0, 9], k[0, 0, :10], v[0, 0, :10], rho[0, 0, 9], w.h)
     assert abs(parts["p"].sum() - 1.0) < 1e-14
     assert np.array_equal(parts["o"], full[0, 0, 9])
+
+
+# ---------------------------------------------------------------- decode (one query against a cache)
+def test_decode_is_the_last_row_of_the_causal_forward():
+    from oracle import parallax_decode
+    rng = np.random.default_rng(81)
+    B, H, L, d = 2, 3, 37, 5
+    qs, k, v, rhos = (rng.standard_normal((B, H, L, d)) for _ in range(4))
+    full = parallax_forward(qs, k, v, rhos, 1.3)
+    dec = parallax_decode(qs[:, :, -1], k, v, rhos[:, :, -1], 1.3)
+    assert np.array_equal(dec, full[:, :, -1])
+
+
+def test_decode_ignores_cache_order_and_negligible_keys():
+    # every cached key is visible to the decode query: the output does not depend on the
+    # order of the cache, and a key whose weight underflows changes nothing
+    from oracle import parallax_decode
+    rng = np.random.default_rng(82)
+    B, H, L, d = 1, 2, 50, 6
+    q, rho = rng.standard_normal((B, H, d)), rng.standard_normal((B, H, d))
+    k, v = rng.standard_normal((B, H, L, d)), rng.standard_normal((B, H, L, d))
+    base = parallax_decode(q, k, v, rho, 0.9)
+    perm = rng.permutation(L)
+    assert relerr(parallax_decode(q, k[:, :, perm], v[:, :, perm], rho, 0.9), base) < 1e-12
+    far = -50.0 * q[:, :, None, :] / np.linalg.norm(q, axis=-1)[..., None, None]
+    k2 = np.concatenate([k, far], axis=2)
+    v2 = np.concatenate([v, rng.standard_normal((B, H, 1, d))], axis=2)
+    assert relerr(parallax_decode(q, k2, v2, rho, 0.9), base) < 1e-12
