@@ -65,6 +65,8 @@ KERNEL_BOUND = {
     "lla_parallax_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_parallax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_parallax_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla_parallax_decode_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla_parallax_merge_kernel": ("hbm", PEAK["hbm_GBps"]),
 }
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
@@ -131,12 +133,16 @@ def path_flops(B, H, n, d, path):
     return sum(kernel_flops(k, B, H, n, d, path) for k in PATH_KERNELS[path])
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel):
+    """Hash of the HIP source file that defines `kernel` plus the shared headers: a traffic
+    record taken on other sources of that kernel is stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "local_linear_attention_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    names = sorted(os.listdir(csrc))
+    for name in names:
+        path = os.path.join(csrc, name)
+        if name.endswith(".h") or (name.endswith(".hip") and f"void {kernel}(" in open(path).read()):
+            h.update(open(path, "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -149,7 +155,7 @@ def load_traffic(kernel, workload):
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -189,14 +195,133 @@ def cpu_baseline(w, q, k, v, seconds, rho=None):
     }
 
 
+METRIC_DECODE = "Parallax decode (given probe) queries/s and HBM GB/s at B8 H16 L8192 d64 bf16, 1 GPU"
+
+
+def decode_bytes(B, H, L, d, elt):
+    """Algorithmic HBM bytes of one decode step: the cache (K and V) read once, q and rho
+    read, the fp32 output written."""
+    return 2 * B * H * L * d * elt + 2 * B * H * d * elt + B * H * d * 4
+
+
+def decode_cpu_baseline(w, q, k, v, rho, seconds):
+    """The fp64 decode oracle on whole heads drawn at random, projected to the workload."""
+    import numpy as np
+
+    from oracle import parallax_decode
+    rng = np.random.default_rng(12345)
+    done, elapsed = 0, 0.0
+    while elapsed < seconds and done < w.B * w.H:
+        b, hh = int(rng.integers(w.B)), int(rng.integers(w.H))
+        t0 = time.perf_counter()
+        parallax_decode(q[b:b + 1, hh:hh + 1], k[b:b + 1, hh:hh + 1], v[b:b + 1, hh:hh + 1],
+                        rho[b:b + 1, hh:hh + 1], w.h)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    full = elapsed * w.B * w.H / done
+    return {"value": w.queries / full, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (batch, head) caches drawn at random (seed 12345), {elapsed:.1f} s in one "
+                      f"process; full-step time {full:.1f} s projected per head"}
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    import lla_inputs
+    from local_linear_attention_amd import lla_parallax_decode, lla_profile_collect, lla_profile_enable
+
+    w = lla_inputs.DECODE_WORKLOADS[args.workload or "decode_b8_l8192"]
+    q, k, v, rho = lla_inputs.generate_decode(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    tq, tk, tv, tr = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v, rho))
+    out = torch.empty(tq.shape, dtype=torch.float32, device=dev)
+    if args.copy_calibration_mib > 0:
+        src = torch.ones((args.copy_calibration_mib << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        lla_parallax_decode(tq, tk, tv, tr, w.h, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s_ in range(args.steps):
+        starts[s_].record(stream)
+        step()
+        ends[s_].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    per_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    assert torch.isfinite(out).all().item(), "non-finite output"
+
+    lla_profile_enable(True)
+    lla_profile_collect()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    rec = lla_profile_collect()
+    lla_profile_enable(False)
+    per_kernel = {}
+    for name, ms in rec:
+        per_kernel.setdefault(name, []).append(ms)
+    elt = 4 if w.dtype == "f32" else 2
+    nbytes = decode_bytes(w.B, w.H, w.L, w.d, elt)
+    kernels = {name: {"launches": len(lst), "avg_ms": statistics.mean(lst)} for name, lst in per_kernel.items()}
+    dk = kernels["lla_parallax_decode_kernel"]
+    # the decode kernel moves every byte of the step but the merge's partial sums
+    dk["bytes"] = nbytes
+    dk["GBps"] = nbytes / (dk["avg_ms"] * 1e-3) / 1e9
+    traffic = load_traffic("lla_parallax_decode_kernel", w.name)
+    result = {
+        "metric": METRIC_DECODE,
+        "value": w.queries / (ms_per_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 inputs)" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B{w.B} H{w.H} L{w.L} d{w.d} {w.dtype} cache, one query and probe per "
+                               f"head, h={w.h:g}",
+                   "B": w.B, "H": w.H, "L": w.L, "d": w.d, "input_dtype": w.dtype, "queries": w.queries},
+        "hbm_GBps": nbytes / (ms_per_step * 1e-3) / 1e9,
+        "kernels": kernels,
+        "timing_ms": {"median": statistics.median(per_ms), "p10": float(np.percentile(per_ms, 10)),
+                      "p90": float(np.percentile(per_ms, 90))},
+        "roofline": {"kernel": "lla_parallax_decode_kernel", "bound": "hbm", "achieved": dk["GBps"],
+                     "peak": PEAK["hbm_GBps"], "unit": "GB/s", "frac": dk["GBps"] / PEAK["hbm_GBps"],
+                     "traffic": traffic},
+        "gfx": torch.cuda.get_device_properties(dev).gcnArchName,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = decode_cpu_baseline(w, q, k, v, rho, min(args.cpu_seconds, 10.0))
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--method", default="lla", choices=["lla", "parallax"])
+    ap.add_argument("--method", default="lla", choices=["lla", "parallax", "parallax_decode"])
     ap.add_argument("--workload", default=None,
-                    help="default: d24 (LLA) or parallax_d24 (Parallax)")
+                    help="default: d24 (LLA), parallax_d24 (Parallax), decode_b8_l8192 (decode)")
     ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,6 +335,10 @@ def main():
               "single MI355X (heads shard across GPUs with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.method == "parallax_decode":
+        bench_decode(args)
+        return
 
     import numpy as np
     import torch

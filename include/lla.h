@@ -167,6 +167,39 @@ lla_status_t lla_parallax_forward_ws(const void* q, const void* k, const void* v
 /* As lla_path_available, for the Parallax paths. */
 int lla_parallax_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d);
 
+/*
+ * Parallax decode step with a caller-supplied probe: one query per (batch, head) against a
+ * key-value cache (sources: the "Parallax" blog post, section 2 "Parallax" for the forward
+ * equation, section 3 "Optimized Decode Kernel" and Appendix C for the decode setting):
+ *
+ *   out[b, hd] = vbar - Sigma_KV rho[b, hd], with p_j = softmax_j(q[b, hd] . k[b, hd, j] / h)
+ *   over every cached position j < L (the query is the newest position; its own key is the
+ *   cache's last entry), vbar = sum_j p_j v_j, Sigma_KV = sum_j p_j (v_j - vbar)(k_j - kbar)^T.
+ *
+ *   q, rho : device pointers to [B, H, d] arrays of `dtype` (one row per head)
+ *   k, v   : device pointers to the cache, [B, H, L, d] of `dtype`, contiguous
+ *   out    : device pointer to [B, H, d] fp32 output, not overlapping any input
+ *   L      : cached positions (>= 1); d in {16, 32, 64, 128}; h > 0
+ * Every supported (dtype, d) runs on the same kernels (fp32 arithmetic; the step is bound by
+ * reading the cache).  The cache is split into chunks across workgroups; when a head has
+ * more than one chunk, a second launch merges their partial sums, which live in scratch
+ * (lla_parallax_decode_workspace_size bytes: per head and chunk, 4 + 2d floats).
+ * lla_parallax_decode takes that scratch from the library pool; lla_parallax_decode_ws uses
+ * the caller's (allocates nothing; LLA_ERR_WORKSPACE if missing or short).  Validation,
+ * errors and streams as for lla_forward.
+ */
+lla_status_t lla_parallax_decode(const void* q, const void* k, const void* v, const void* rho,
+                                 float* out, int64_t B, int64_t H, int64_t L, int64_t d,
+                                 double h, lla_dtype_t dtype, void* stream);
+
+size_t lla_parallax_decode_workspace_size(int64_t B, int64_t H, int64_t L, int64_t d,
+                                          lla_dtype_t dtype);
+
+lla_status_t lla_parallax_decode_ws(const void* q, const void* k, const void* v, const void* rho,
+                                    float* out, int64_t B, int64_t H, int64_t L, int64_t d,
+                                    double h, lla_dtype_t dtype, void* stream,
+                                    void* workspace, size_t workspace_bytes);
+
 /* Kernel-level timing.  While enabled, every kernel launch of the library is bracketed by
  * HIP events on its stream.  lla_profile_collect waits for the recorded events, writes up to
  * max_entries kernel names (static strings) and durations in milliseconds in launch order,

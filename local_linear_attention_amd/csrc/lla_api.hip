@@ -145,6 +145,27 @@ lla_status_t run_parallax(const lla::Problem& p, bool fast, void* ws, size_t ws_
                        [&](void* w) { return lla::launch_parallax_fast(p, w); });
 }
 
+// ---- Parallax decode
+lla_status_t decode_entry(const void* q, const void* k, const void* v, const void* rho, float* out,
+                          int64_t B, int64_t H, int64_t L, int64_t d, double h, lla_dtype_t dtype,
+                          void* stream, void* ws, size_t ws_bytes, bool may_allocate) {
+    if (!q || !k || !v || !rho || !out) return LLA_ERR_NULL;
+    if (B < 1 || H < 1 || L < 1) return LLA_ERR_SHAPE;
+    if (!isfinite(h) || !(h > 0.0)) return LLA_ERR_PARAM;
+    if (!supported_shape(d, dtype)) return LLA_ERR_UNSUPPORTED;
+    lla_status_t st = validate_sizes(B, H, L, d);
+    if (st != LLA_OK) return st;
+    const int64_t elt = dtype == LLA_DTYPE_F32 ? 4 : 2;
+    const int64_t row_bytes = B * H * d * elt, cache_bytes = B * H * L * d * elt, out_bytes = B * H * d * 4;
+    if (overlaps(out, out_bytes, q, row_bytes) || overlaps(out, out_bytes, rho, row_bytes) ||
+        overlaps(out, out_bytes, k, cache_bytes) || overlaps(out, out_bytes, v, cache_bytes))
+        return LLA_ERR_ALIAS;
+    const lla::Problem p{q, k, v, out, B, H, L, d, h, 0.0, static_cast<int>(dtype),
+                         static_cast<hipStream_t>(stream), rho};
+    return run_scratch(lla::decode_workspace_bytes(B, H, L, d), p.stream, ws, ws_bytes, may_allocate,
+                       [&](void* w) { return lla::launch_parallax_decode(p, w); });
+}
+
 lla_status_t parallax_entry(const void* q, const void* k, const void* v, const void* rho, float* out,
                             int64_t B, int64_t H, int64_t n, int64_t d, double h, lla_dtype_t dtype,
                             void* stream, lla_path_t path, void* ws, size_t ws_bytes, bool may_allocate) {
@@ -299,6 +320,23 @@ int lla_parallax_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d) {
     if (!supported_shape(d, dtype)) return 0;
     bool fast = false;
     return resolve_parallax_fast(path, static_cast<int>(dtype), d, 1, &fast) ? 1 : 0;
+}
+
+lla_status_t lla_parallax_decode(const void* q, const void* k, const void* v, const void* rho, float* out,
+                                 int64_t B, int64_t H, int64_t L, int64_t d, double h,
+                                 lla_dtype_t dtype, void* stream) {
+    return decode_entry(q, k, v, rho, out, B, H, L, d, h, dtype, stream, nullptr, 0, true);
+}
+
+lla_status_t lla_parallax_decode_ws(const void* q, const void* k, const void* v, const void* rho, float* out,
+                                    int64_t B, int64_t H, int64_t L, int64_t d, double h,
+                                    lla_dtype_t dtype, void* stream, void* workspace, size_t workspace_bytes) {
+    return decode_entry(q, k, v, rho, out, B, H, L, d, h, dtype, stream, workspace, workspace_bytes, false);
+}
+
+size_t lla_parallax_decode_workspace_size(int64_t B, int64_t H, int64_t L, int64_t d, lla_dtype_t dtype) {
+    if (!supported_shape(d, dtype) || validate_sizes(B, H, L, d) != LLA_OK) return 0;
+    return lla::decode_workspace_bytes(B, H, L, d);
 }
 
 int lla_profile_enable(int enable) {

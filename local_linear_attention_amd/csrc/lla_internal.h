@@ -39,6 +39,12 @@ size_t parallax_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
 hipError_t launch_parallax_fast(const Problem& p, void* workspace);
 hipError_t launch_parallax_exact(const Problem& p);
 
+// Parallax decode with a given probe: q, rho [B, H, d] against a cache k, v [B, H, L, d]
+// (L in Problem::n).  Every (dtype, d) the library accepts; the per-chunk partial sums go
+// to `workspace` (decode_workspace_bytes of it; none when a head is one chunk).
+size_t decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d);
+hipError_t launch_parallax_decode(const Problem& p, void* workspace);
+
 // Kernel-level timing (lla_profile_enable): events recorded around each launch.
 void prof_begin(hipStream_t stream, const char* kernel);
 void prof_end(hipStream_t stream);

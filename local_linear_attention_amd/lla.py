@@ -13,6 +13,7 @@ import os
 __all__ = ["lla_forward", "lla_forward_ex", "lla_forward_ws", "lla_workspace_size",
            "lla_path_available", "lla_parallax_forward", "lla_parallax_forward_ex",
            "lla_parallax_forward_ws", "lla_parallax_workspace_size", "lla_parallax_path_available",
+           "lla_parallax_decode", "lla_parallax_decode_ws", "lla_parallax_decode_workspace_size",
            "lla_profile_enable", "lla_profile_collect",
            "lla_status_string", "lla_version", "LLAError",
            "library_path", "load_library", "STATUS", "PATHS", "DTYPES"]
@@ -75,6 +76,13 @@ def load_library():
     lib.lla_parallax_workspace_size.restype = ctypes.c_size_t
     lib.lla_parallax_path_available.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64]
     lib.lla_parallax_path_available.restype = ctypes.c_int
+    lib.lla_parallax_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f64, ctypes.c_int, vp]
+    lib.lla_parallax_decode.restype = ctypes.c_int
+    lib.lla_parallax_decode_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f64, ctypes.c_int, vp, vp,
+                                           ctypes.c_size_t]
+    lib.lla_parallax_decode_ws.restype = ctypes.c_int
+    lib.lla_parallax_decode_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.lla_parallax_decode_workspace_size.restype = ctypes.c_size_t
     lib.lla_profile_enable.argtypes = [ctypes.c_int]
     lib.lla_profile_enable.restype = ctypes.c_int
     lib.lla_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p),
@@ -245,6 +253,74 @@ def lla_parallax_forward_ws(q, k, v, rho, h: float, workspace, path: str = "auto
         ctypes.c_void_p(stream.cuda_stream), PATHS[path], ctypes.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes)
     if st != 0:
         raise LLAError(st, "lla_parallax_forward_ws")
+    return out
+
+
+def _marshal_decode(q, k, v, rho, out):
+    import torch
+    if q.dim() != 3 or k.dim() != 4 or k.shape != v.shape or q.shape != rho.shape \
+            or tuple(q.shape) != (k.shape[0], k.shape[1], k.shape[3]):
+        raise ValueError(f"decode takes q, rho [B, H, d] and k, v [B, H, L, d]; got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}, {tuple(rho.shape)}")
+    if not (q.dtype == k.dtype == v.dtype == rho.dtype):
+        raise ValueError("q, k, v, rho must share one dtype")
+    if q.dtype == torch.float32:
+        dtype = DTYPES["f32"]
+    elif q.dtype == torch.bfloat16:
+        dtype = DTYPES["bf16"]
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("rho", rho)):
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous device tensor on q's device")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous float32 tensor of q's shape on q's device")
+    return dtype, out
+
+
+def lla_parallax_decode(q, k, v, rho, h: float, out=None, stream=None):
+    """Parallax decode step: q, rho [B, H, d] against the cache k, v [B, H, L, d] (fp32 or
+    bf16) -> fp32 out [B, H, d]."""
+    import torch
+    dtype, out = _marshal_decode(q, k, v, rho, out)
+    B, H, L, d = k.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().lla_parallax_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), rho.data_ptr(),
+                                            out.data_ptr(), B, H, L, d, float(h), dtype,
+                                            ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise LLAError(st, "lla_parallax_decode")
+    return out
+
+
+def lla_parallax_decode_workspace_size(B: int, H: int, L: int, d: int, dtype: str) -> int:
+    """Bytes of device scratch a decode step needs (0 if none)."""
+    return int(load_library().lla_parallax_decode_workspace_size(B, H, L, d, DTYPES[dtype]))
+
+
+def lla_parallax_decode_ws(q, k, v, rho, h: float, workspace, out=None, stream=None):
+    """Parallax decode step with caller-provided scratch (a device tensor of at least
+    lla_parallax_decode_workspace_size bytes, or None when none is needed)."""
+    import torch
+    dtype, out = _marshal_decode(q, k, v, rho, out)
+    B, H, L, d = k.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    if workspace is None:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = load_library().lla_parallax_decode_ws(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), rho.data_ptr(), out.data_ptr(), B, H, L, d, float(h), dtype,
+        ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes)
+    if st != 0:
+        raise LLAError(st, "lla_parallax_decode_ws")
     return out
 
 

@@ -32,6 +32,8 @@ def declared_enums():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["lla_forward", "lla_forward_ex", "lla_forward_ws",
+                                    "lla_parallax_decode", "lla_parallax_decode_workspace_size",
+                                    "lla_parallax_decode_ws",
                                     "lla_parallax_forward", "lla_parallax_forward_ex",
                                     "lla_parallax_forward_ws", "lla_parallax_path_available",
                                     "lla_parallax_workspace_size",
@@ -223,3 +225,50 @@ def test_parallax_ws_validation_before_launch():
             ctypes.c_void_p(OUT), 1, 2, 4096, 64, 8.0, 1, None, 2]
     assert lib.lla_parallax_forward_ws(*args, None, 0) == 5
     assert lib.lla_parallax_forward_ws(*args, ctypes.c_void_p(0x50000000), 4096) == 5
+
+
+# ---------------------------------------------------------------- Parallax decode
+def call_decode(lib, q=Q, k=K, v=V, rho=RHO, out=OUT, B=2, H=3, L=100, d=64, h=8.0, dtype=1):
+    return lib.lla_parallax_decode(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v),
+                                   ctypes.c_void_p(rho), ctypes.c_void_p(out), B, H, L, d, h, dtype, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(rho=0), 1), (dict(out=0), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(L=0), 2), (dict(L=2 ** 31), 2),
+    (dict(h=0.0), 3), (dict(h=math.inf), 3), (dict(h=math.nan), 3),
+    (dict(d=48), 4), (dict(d=256), 4), (dict(dtype=2), 4),
+    (dict(out=Q + 64), 7), (dict(out=RHO - 64), 7), (dict(out=K + 4096), 7), (dict(out=V + 64), 7),
+])
+def test_decode_invalid_arguments_are_rejected_before_any_launch(kw, expect):
+    assert call_decode(_lib(), **kw) == expect
+
+
+def decode_split(BH, L):
+    """Chunks per head of the decode kernels: about 1024 blocks in all, chunks of 256 to 2048
+    keys, none empty."""
+    s = max(1, -(-1024 // BH))
+    s = min(s, -(-L // 256))
+    s = max(s, -(-L // 2048))
+    c = -(-L // s)
+    return -(-L // c), c
+
+
+def test_decode_workspace_size():
+    from local_linear_attention_amd import lla
+    for B, H, L, d in ((8, 16, 8192, 64), (1, 16, 32768, 64), (64, 16, 1024, 64), (8, 8, 8192, 128),
+                       (1, 1, 300, 16), (4, 4, 200, 32), (512, 16, 256, 64)):
+        S, _ = decode_split(B * H, L)
+        expect = 0 if S == 1 else B * H * S * (4 + 2 * d) * 4
+        assert lla.lla_parallax_decode_workspace_size(B, H, L, d, "bf16") == expect, (B, H, L, d)
+        assert lla.lla_parallax_decode_workspace_size(B, H, L, d, "f32") == expect
+    assert lla.lla_parallax_decode_workspace_size(1, 1, 1, 64, "bf16") == 0
+    assert lla.lla_parallax_decode_workspace_size(1, 1, 100, 48, "bf16") == 0
+
+
+def test_decode_ws_validation_before_launch():
+    lib = _lib()
+    args = [ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V), ctypes.c_void_p(RHO),
+            ctypes.c_void_p(OUT), 1, 2, 4096, 64, 8.0, 1, None]
+    assert lib.lla_parallax_decode_ws(*args, None, 0) == 5
+    assert lib.lla_parallax_decode_ws(*args, ctypes.c_void_p(0x50000000), 64) == 5
