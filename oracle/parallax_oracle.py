@@ -36,7 +36,7 @@ import numpy as np
 from .lla_oracle import map_rows
 
 __all__ = ["parallax_row", "parallax_row_parts", "parallax_rows", "parallax_forward",
-           "parallax_decode"]
+           "parallax_decode", "parallax_backward"]
 
 
 def parallax_row_parts(q_i, K, V, rho_i, h):
@@ -97,3 +97,40 @@ def parallax_decode(q, k, v, rho, h):
         for hh in range(H):
             out[b, hh] = parallax_row(q[b, hh], k[b, hh], v[b, hh], rho[b, hh], h)
     return out
+
+
+def _parallax_head_torch(Q, K, V, R, h):
+    """Causal Parallax forward of one head in torch fp64 ops: the definition
+    o_i = vbar_i - Sigma_KV rho_i with Sigma_KV rho_i expanded as
+    sum_j p_ij (v_j - vbar_i)(u_ij - ubar_i), u_ij = rho_i . k_j, ubar_i = kbar_i . rho_i."""
+    import torch
+    n = Q.shape[0]
+    S = (Q @ K.T) / h
+    mask = torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1)
+    P = torch.softmax(S.masked_fill(mask, float("-inf")), dim=-1)
+    Vbar = P @ V
+    Kbar = P @ K
+    U = R @ K.T
+    Ubar = (Kbar * R).sum(-1, keepdim=True)
+    W = P * (U - Ubar)                                   # p_ij (u_ij - ubar_i)
+    sigma_rho = W @ V - Vbar * W.sum(-1, keepdim=True)   # sum_j p_ij (v_j - vbar_i)(u_ij - ubar_i)
+    return Vbar - sigma_rho
+
+
+def parallax_backward(q, k, v, rho, h, dout):
+    """Gradients (dq, dk, dv, drho) of sum(o * dout) for the causal Parallax forward with a
+    given probe, in fp64, by reverse-mode differentiation (torch autograd on the CPU) of the
+    definition above, head by head.  All arrays [B, H, n, d]; returns fp64 numpy arrays.
+    (The backward the "Parallax" blog post outlines in Appendix F, "Parallax backward".)"""
+    import torch
+    q, k, v, rho, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, rho, dout))
+    grads = [np.empty_like(x) for x in (q, k, v, rho)]
+    B, H = q.shape[:2]
+    for b in range(B):
+        for hh in range(H):
+            ts = [torch.tensor(x[b, hh], dtype=torch.float64, requires_grad=True) for x in (q, k, v, rho)]
+            o = _parallax_head_torch(*ts, h)
+            (o * torch.tensor(dout[b, hh], dtype=torch.float64)).sum().backward()
+            for g, t in zip(grads, ts):
+                g[b, hh] = t.grad.numpy()
+    return tuple(grads)

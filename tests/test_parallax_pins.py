@@ -250,3 +250,100 @@ def test_decode_ignores_cache_order_and_negligible_keys():
     k2 = np.concatenate([k, far], axis=2)
     v2 = np.concatenate([v, rng.standard_normal((B, H, 1, d))], axis=2)
     assert relerr(parallax_decode(q, k2, v2, rho, 0.9), base) < 1e-12
+
+
+# ---------------------------------------------------------------- backward
+def _bwd_case(seed, B=1, H=2, n=7, d=3, qscale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, n, d)) * qscale
+    k, v, rho, dout = (rng.standard_normal((B, H, n, d)) for _ in range(4))
+    return q, k, v, rho, dout
+
+
+def test_backward_forward_matches_the_definition():
+    # the oracle differentiates a torch transcription of the definition; it must be the
+    # same function as the pinned numpy forward
+    import torch
+    from oracle.parallax_oracle import _parallax_head_torch
+    q, k, v, rho, _ = _bwd_case(91, n=12, d=4)
+    ref = parallax_forward(q, k, v, rho, 1.3)
+    for hh in range(2):
+        got = _parallax_head_torch(*(torch.tensor(x[0, hh]) for x in (q, k, v, rho)), 1.3).numpy()
+        assert relerr(got, ref[0, hh]) < 1e-12
+
+
+def test_backward_matches_central_differences():
+    # every gradient entry against a central difference of sum(o * dout), with o from the
+    # numpy forward (no autograd involved)
+    from oracle import parallax_backward
+    q, k, v, rho, dout = _bwd_case(92, qscale=1.5)
+    h = 0.9
+    grads = parallax_backward(q, k, v, rho, h, dout)
+    base = [q, k, v, rho]
+    eps = 1e-6
+    for which, g in enumerate(grads):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(g.shape):
+            xs = [x.copy() for x in base]
+            xs[which][idx] += eps
+            lp = np.sum(parallax_forward(*xs, h) * dout)
+            xs[which][idx] -= 2 * eps
+            lm = np.sum(parallax_forward(*xs, h) * dout)
+            num[idx] = (lp - lm) / (2 * eps)
+        assert np.max(np.abs(num - g)) <= 1e-7 * max(1.0, np.max(np.abs(g))), which
+
+
+def closed_form_backward(q, k, v, rho, h, dout):
+    """The gradients in closed form, one head (the row-tile / column-tile quantities of the
+    blog's Appendix F, derived from the scoring form o_i = sum_j a_ij v_j,
+    a_ij = p_ij (1 - (u_ij - ubar_i))): g = dO V^T, G_i = sum_j p_ij g_ij,
+    dp = g (1 - u + ubar) + u G, du = p (G - g), ds = p (dp - sum_j p dp),
+    dq = ds K / h, dk = ds^T Q / h + du^T R, dv = a^T dO, drho = du K."""
+    n = q.shape[0]
+    s = q @ k.T / h
+    s[np.triu_indices(n, 1)] = -np.inf
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    u = rho @ k.T
+    ubar = np.sum(p * u, -1, keepdims=True)
+    a = p * (1 - u + ubar)
+    g = dout @ v.T
+    G = np.sum(p * g, -1, keepdims=True)
+    dp = g * (1 - u + ubar) + u * G
+    du = p * (G - g)
+    ds = p * (dp - np.sum(p * dp, -1, keepdims=True))
+    return ds @ k / h, ds.T @ q / h + du.T @ rho, a.T @ dout, du @ k
+
+
+def test_backward_closed_form():
+    from oracle import parallax_backward
+    q, k, v, rho, dout = _bwd_case(93, B=2, H=2, n=20, d=5, qscale=1.2)
+    grads = parallax_backward(q, k, v, rho, 1.1, dout)
+    for b in range(2):
+        for hh in range(2):
+            cf = closed_form_backward(q[b, hh], k[b, hh], v[b, hh], rho[b, hh], 1.1, dout[b, hh])
+            for got, ref in zip((g[b, hh] for g in grads), cf):
+                assert relerr(got, ref) < 1e-10
+
+
+def test_backward_zero_probe_is_softmax_attention_backward():
+    # with rho = 0 the gradients are those of softmax attention (FlashAttention's closed
+    # form: dv = P^T dO, ds = P (dO V^T - rowsum(P dO V^T)), dq = ds K / h, dk = ds^T Q / h)
+    from oracle import parallax_backward
+    q, k, v, _, dout = _bwd_case(94, n=15, d=4)
+    rho = np.zeros_like(q)
+    dq, dk, dv, drho = parallax_backward(q, k, v, rho, 1.7, dout)
+    for hh in range(2):
+        Q, K, V, dO = q[0, hh], k[0, hh], v[0, hh], dout[0, hh]
+        s = Q @ K.T / 1.7
+        s[np.triu_indices(15, 1)] = -np.inf
+        P = np.exp(s - s.max(-1, keepdims=True))
+        P /= P.sum(-1, keepdims=True)
+        dP = dO @ V.T
+        dS = P * (dP - np.sum(P * dP, -1, keepdims=True))
+        assert relerr(dv[0, hh], P.T @ dO) < 1e-12
+        assert relerr(dq[0, hh], dS @ K / 1.7) < 1e-12
+        assert relerr(dk[0, hh], dS.T @ Q / 1.7) < 1e-12
+        # the probe gradient is then drho_i = sum_j p_ij (G_i - g_ij) k_j, not zero
+        G = np.sum(P * dP, -1, keepdims=True)
+        assert relerr(drho[0, hh], (P * (G - dP)) @ K) < 1e-12
