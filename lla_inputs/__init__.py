@@ -31,6 +31,8 @@ key-value cache of L positions; batch and context sizes from the pages' decode s
 * ``decode_b1_l32768`` B1 H16 L32768 d64 bf16 (seed 6): the sweep's longest context.
 * ``decode_b64_l1024`` B64 H16 L1024 d64 bf16 (seed 7): many short caches.
 * ``decode_d128``      B8 H8 L8192 d128 bf16 (seed 8); h = sqrt(128): the I/O-matched head size.
+* ``lla_decode_b8_l8192`` the q, k, v of ``decode_b8_l8192`` (same seed, bit-identical) for the
+                LLA decode step, lambda = 1e-2 (as the headline forward workload).
 Decode recipe: ``default_rng(seed)`` draws, in fp64 and in this order, q ``[B,H,d]``, k and v
 ``[B,H,L,d]`` (standard normal), then rho ``[B,H,d]``; q, k and rho are RMS-normalised, v is
 left as drawn; all four are cast once to the storage dtype.
@@ -187,6 +189,7 @@ class DecodeWorkload:
     dtype: str
     h: float
     seed: int
+    lam: float = 0.0   # ridge of the LLA decode step (unused by Parallax)
 
     @property
     def queries(self) -> int:
@@ -201,6 +204,7 @@ DECODE_WORKLOADS = {
     "decode_b1_l32768": DecodeWorkload("decode_b1_l32768", 1, 16, 32768, 64, "bf16", 8.0, 6),
     "decode_b64_l1024": DecodeWorkload("decode_b64_l1024", 64, 16, 1024, 64, "bf16", 8.0, 7),
     "decode_d128": DecodeWorkload("decode_d128", 8, 8, 8192, 128, "bf16", math.sqrt(128.0), 8),
+    "lla_decode_b8_l8192": DecodeWorkload("lla_decode_b8_l8192", 8, 16, 8192, 64, "bf16", 8.0, 5, 1e-2),
 }
 
 

@@ -49,7 +49,7 @@ import os
 
 import numpy as np
 
-__all__ = ["lla_row", "lla_row_parts", "lla_forward", "lla_rows", "map_rows"]
+__all__ = ["lla_row", "lla_row_parts", "lla_forward", "lla_rows", "map_rows", "lla_decode"]
 
 
 def lla_row_parts(q_i, K, V, h, lam):
@@ -183,3 +183,18 @@ def lla_forward(q, k, v, h, lam, workers=1):
 
 def default_workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
+
+
+def lla_decode(q, k, v, h, lam):
+    """LLA decode step: one query per (batch, head) against its whole key-value cache.
+
+    q: [B, H, d]; k: [B, H, L, d]; v: [B, H, L, d_v].  The query is the newest position and
+    every cached key is in its prefix, so each output is lla_row over the full cache.
+    Returns [B, H, d_v] fp64."""
+    q = np.asarray(q)
+    B, H, _ = q.shape
+    out = np.empty((B, H, np.asarray(v).shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for hh in range(H):
+            out[b, hh] = lla_row(q[b, hh], k[b, hh], v[b, hh], h, lam)
+    return out

@@ -274,3 +274,15 @@ def test_tiny_golden_fixture_unchanged():
     w = lla_inputs.WORKLOADS["tiny"]
     q, k, v, _ = lla_inputs.generate(w)
     assert relerr(lla_forward(q, k, v, w.h, w.lam)[0, 0], stored) < 1e-13
+
+
+def test_decode_is_the_last_row_and_ignores_cache_order():
+    from oracle import lla_decode
+    rng = np.random.default_rng(101)
+    B, H, L, d = 2, 2, 30, 4
+    qs, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    full = lla_forward(qs, k, v, 1.4, 0.05)
+    dec = lla_decode(qs[:, :, -1], k, v, 1.4, 0.05)
+    assert np.array_equal(dec, full[:, :, -1])
+    perm = rng.permutation(L)
+    assert relerr(lla_decode(qs[:, :, -1], k[:, :, perm], v[:, :, perm], 1.4, 0.05), dec) < 1e-10
