@@ -168,6 +168,35 @@ lla_status_t lla_parallax_forward_ws(const void* q, const void* k, const void* v
 int lla_parallax_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d);
 
 /*
+ * LLA decode step: one query per (batch, head) against a key-value cache, every cached
+ * position in its prefix (the LLA estimator of the "Parallax" blog post, section 2
+ * "Canonical Formulation", for the newest position; centred form of its Appendix E):
+ *
+ *   out[b, hd] = vbar - C_vk (C_kk + lambda e^{-m} I)^{-1} (kbar - q[b, hd])
+ *
+ * with the weights exp(q . k_j / h - m) over the cache, as in lla_forward's last row.
+ *   q      : device pointer to [B, H, d] (one row per head); k, v: the cache [B, H, L, d]
+ *   out    : device pointer to [B, H, d] fp32, not overlapping any input
+ *   L >= 1, d in {16, 32, 64, 128}, h > 0, lambda >= 0 (lambda = 0 as for lla_forward)
+ * Three launches: chunk statistics, chunk moments on the matrix cores (fp64 for fp32 inputs
+ * and for L < 2d, fp32 otherwise), and a per-head merge, LDL^T solve (fp64) and assembly.
+ * Scratch (lla_decode_workspace_size bytes): per head and chunk the statistics (2 + d
+ * doubles, the region rounded up to 256 bytes) and the moments (d/16 (d/16 + 1)/2 + (d/16)^2
+ * blocks of 256 values plus d values, fp64 or fp32 as above).  lla_decode takes it from the
+ * library pool; lla_decode_ws uses the caller's (allocates nothing).  Validation, errors and
+ * streams as for lla_forward.
+ */
+lla_status_t lla_decode(const void* q, const void* k, const void* v, float* out,
+                        int64_t B, int64_t H, int64_t L, int64_t d, double h, double lambda,
+                        lla_dtype_t dtype, void* stream);
+
+size_t lla_decode_workspace_size(int64_t B, int64_t H, int64_t L, int64_t d, lla_dtype_t dtype);
+
+lla_status_t lla_decode_ws(const void* q, const void* k, const void* v, float* out,
+                           int64_t B, int64_t H, int64_t L, int64_t d, double h, double lambda,
+                           lla_dtype_t dtype, void* stream, void* workspace, size_t workspace_bytes);
+
+/*
  * Parallax decode step with a caller-supplied probe: one query per (batch, head) against a
  * key-value cache (sources: the "Parallax" blog post, section 2 "Parallax" for the forward
  * equation, section 3 "Optimized Decode Kernel" and Appendix C for the decode setting):

@@ -5,7 +5,8 @@ The compute lives in ``liblla.so`` (hand-written HIP kernels behind a C ABI decl
 ``include/lla.h``); ``lla`` is the ctypes binding.
 """
 from .lla import (  # noqa: F401
-    LLAError, library_path, lla_forward, lla_forward_ex, lla_forward_ws, lla_parallax_decode,
+    LLAError, library_path, lla_decode, lla_decode_workspace_size, lla_decode_ws, lla_forward, lla_forward_ex,
+    lla_forward_ws, lla_parallax_decode,
     lla_parallax_decode_workspace_size, lla_parallax_decode_ws, lla_parallax_forward,
     lla_parallax_forward_ex, lla_parallax_forward_ws, lla_parallax_path_available,
     lla_parallax_workspace_size, lla_path_available, lla_profile_collect, lla_profile_enable,

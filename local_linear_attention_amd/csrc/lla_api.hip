@@ -166,6 +166,27 @@ lla_status_t decode_entry(const void* q, const void* k, const void* v, const voi
                        [&](void* w) { return lla::launch_parallax_decode(p, w); });
 }
 
+// ---- LLA decode
+lla_status_t lla_decode_entry(const void* q, const void* k, const void* v, float* out, int64_t B, int64_t H,
+                              int64_t L, int64_t d, double h, double lambda, lla_dtype_t dtype, void* stream,
+                              void* ws, size_t ws_bytes, bool may_allocate) {
+    if (!q || !k || !v || !out) return LLA_ERR_NULL;
+    if (B < 1 || H < 1 || L < 1) return LLA_ERR_SHAPE;
+    if (!isfinite(h) || !(h > 0.0) || !isfinite(lambda) || !(lambda >= 0.0)) return LLA_ERR_PARAM;
+    if (!supported_shape(d, dtype)) return LLA_ERR_UNSUPPORTED;
+    const lla_status_t st = validate_sizes(B, H, L, d);
+    if (st != LLA_OK) return st;
+    const int64_t elt = dtype == LLA_DTYPE_F32 ? 4 : 2;
+    const int64_t row_bytes = B * H * d * elt, cache_bytes = B * H * L * d * elt, out_bytes = B * H * d * 4;
+    if (overlaps(out, out_bytes, q, row_bytes) || overlaps(out, out_bytes, k, cache_bytes) ||
+        overlaps(out, out_bytes, v, cache_bytes))
+        return LLA_ERR_ALIAS;
+    const lla::Problem p{q, k, v, out, B, H, L, d, h, lambda, static_cast<int>(dtype),
+                         static_cast<hipStream_t>(stream), nullptr};
+    return run_scratch(lla::lla_decode_workspace_bytes(B, H, L, d, static_cast<int>(dtype)), p.stream, ws, ws_bytes,
+                       may_allocate, [&](void* w) { return lla::launch_lla_decode(p, w); });
+}
+
 lla_status_t parallax_entry(const void* q, const void* k, const void* v, const void* rho, float* out,
                             int64_t B, int64_t H, int64_t n, int64_t d, double h, lla_dtype_t dtype,
                             void* stream, lla_path_t path, void* ws, size_t ws_bytes, bool may_allocate) {
@@ -337,6 +358,22 @@ lla_status_t lla_parallax_decode_ws(const void* q, const void* k, const void* v,
 size_t lla_parallax_decode_workspace_size(int64_t B, int64_t H, int64_t L, int64_t d, lla_dtype_t dtype) {
     if (!supported_shape(d, dtype) || validate_sizes(B, H, L, d) != LLA_OK) return 0;
     return lla::decode_workspace_bytes(B, H, L, d);
+}
+
+lla_status_t lla_decode(const void* q, const void* k, const void* v, float* out, int64_t B, int64_t H,
+                        int64_t L, int64_t d, double h, double lambda, lla_dtype_t dtype, void* stream) {
+    return lla_decode_entry(q, k, v, out, B, H, L, d, h, lambda, dtype, stream, nullptr, 0, true);
+}
+
+lla_status_t lla_decode_ws(const void* q, const void* k, const void* v, float* out, int64_t B, int64_t H,
+                           int64_t L, int64_t d, double h, double lambda, lla_dtype_t dtype, void* stream,
+                           void* workspace, size_t workspace_bytes) {
+    return lla_decode_entry(q, k, v, out, B, H, L, d, h, lambda, dtype, stream, workspace, workspace_bytes, false);
+}
+
+size_t lla_decode_workspace_size(int64_t B, int64_t H, int64_t L, int64_t d, lla_dtype_t dtype) {
+    if (!supported_shape(d, dtype) || validate_sizes(B, H, L, d) != LLA_OK) return 0;
+    return lla::lla_decode_workspace_bytes(B, H, L, d, static_cast<int>(dtype));
 }
 
 int lla_profile_enable(int enable) {

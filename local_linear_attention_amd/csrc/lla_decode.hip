@@ -28,6 +28,9 @@
 
 #include <math.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace lla {
 namespace {
 
@@ -47,6 +50,14 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
 }
+
+__device__ __forceinline__ double load_elem_d(const float* p, int64_t i) { return static_cast<double>(p[i]); }
+__device__ __forceinline__ double load_elem_d(const uint16_t* p, int64_t i) {
+    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[i]) << 16));
+}
+
+// fp64 moments for fp32 inputs and for caches shorter than 2d, fp32 moments otherwise.
+bool lla_decode_fp64(int dtype, int64_t L, int64_t d) { return dtype == 0 || L < 2 * d; }
 
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {   // over G consecutive lanes
@@ -284,6 +295,472 @@ size_t decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d) {
 
 hipError_t launch_parallax_decode(const Problem& p, void* workspace) {
     return p.dtype == 0 ? launch_decode_d<float>(p, workspace) : launch_decode_d<uint16_t>(p, workspace);
+}
+
+// =======================================================================================
+// LLA decode step: b = vbar - C_vk (C_kk + lambda e^{-m} I)^{-1} (kbar - q) over each head's
+// whole cache -- the LLA row of the "Parallax" blog post, section 2 "Canonical Formulation"
+// (centred form of its Appendix E), for the newest position.  Three launches:
+//   lla_decode_stats_kernel    per chunk: scores x = q.k log2e/h, chunk max m_c,
+//                              omega_c = sum 2^(x - m_c), S_k,c = sum 2^(x - m_c) k;
+//   lla_decode_moments_kernel  per chunk: the head's max M, omega and kbar from the chunk
+//                              statistics; weights w = 2^(x - M); 64-key sub-tiles staged
+//                              in LDS feature-major as R_k = sqrt(w)(k - kbar), R_v = sqrt(w) v;
+//                              C_kk (upper 16x16 blocks) += R_k R_k^T and C_vk += R_v R_k^T on
+//                              the matrix cores (16x16x4, fp32 or fp64); S_v = sum w v;
+//   lla_decode_solve_kernel    per head: sums the chunks' moments, adds the ridge
+//                              lambda 2^-M to the diagonal, LDL^T in LDS (fp64), solves for y
+//                              and writes b = S_v/omega - C_vk y.
+// C_vk needs no centring of v: sum_j w_j (k_j - kbar) = 0 makes sum_j w_j vbar (k_j - kbar)^T
+// vanish.  Moments in fp64 for fp32 inputs and for caches shorter than 2d (where the ridge
+// alone conditions the solve); in fp32 otherwise.
+namespace {
+
+typedef double double4v __attribute__((ext_vector_type(4)));
+typedef float float4x __attribute__((ext_vector_type(4)));
+
+template <typename TA> struct Acc4;
+template <> struct Acc4<float> { using type = float4x; };
+template <> struct Acc4<double> { using type = double4v; };
+
+__device__ __forceinline__ float4x mfma4(float a, float b, float4x c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ double4v mfma4(double a, double b, double4v c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+// Row of the 16x16 output block held in register r of lane (g, c) (column c): the fp32
+// instruction places rows 4g + r, the fp64 one rows 4r + g.
+template <typename TA> __device__ __forceinline__ int acc_row(int g, int r);
+template <> __device__ __forceinline__ int acc_row<float>(int g, int r) { return 4 * g + r; }
+template <> __device__ __forceinline__ int acc_row<double>(int g, int r) { return 4 * r + g; }
+
+constexpr int LD_SUB = 64;             // keys per staged sub-tile
+constexpr int LD_LDW = LD_SUB + 2;     // row stride of the feature-major stage (elements)
+
+// Blocks of a chunk's moments: the upper 16x16 blocks (I <= J) of C_kk row by row, then the
+// NB x NB blocks of C_vk.
+template <int D>
+struct MomBlocks {
+    static constexpr int NB = D / 16, NKK = NB * (NB + 1) / 2, NT = NKK + NB * NB;
+    static constexpr int kind(int b) { return b < NKK ? 0 : 1; }
+    static constexpr int I(int b) {
+        if (b >= NKK) return (b - NKK) / NB;
+        int i = 0, r = b;
+        while (r >= NB - i) { r -= NB - i; ++i; }
+        return i;
+    }
+    static constexpr int J(int b) {
+        if (b >= NKK) return (b - NKK) % NB;
+        int i = 0, r = b;
+        while (r >= NB - i) { r -= NB - i; ++i; }
+        return i + r;
+    }
+};
+
+// acc[t] += op(block B0 + t) for t in Bs, with every block's rows and kind fixed at compile
+// time (so the operand arrays stay in registers).
+template <int D, int B0, typename TA, typename AccT, int N, int... Bs>
+__device__ __forceinline__ void mfma_blocks(const TA (&ak)[D / 16], const TA (&av)[D / 16], AccT (&acc)[N],
+                                            std::integer_sequence<int, Bs...>) {
+    using MB = MomBlocks<D>;
+    ((acc[Bs] = mfma4(std::integral_constant<int, MB::kind(B0 + Bs)>::value == 0
+                          ? ak[std::integral_constant<int, MB::I(B0 + Bs)>::value]
+                          : av[std::integral_constant<int, MB::I(B0 + Bs)>::value],
+                      ak[std::integral_constant<int, MB::J(B0 + Bs)>::value], acc[Bs])),
+     ...);
+}
+
+// Chunks per head for the LLA decode kernels: about 1024 blocks in all, 512 to DC_CMAX keys
+// per chunk (the moments written per chunk stay small next to the cache), none empty.
+void lla_decode_split(int64_t BH, int64_t L, int* S, int* C) {
+    int64_t s = (1024 + BH - 1) / BH;
+    const int64_t by_len = (L + 511) / 512;
+    if (s > by_len) s = by_len;
+    const int64_t min_s = (L + DC_CMAX - 1) / DC_CMAX;
+    if (s < min_s) s = min_s;
+    if (s < 1) s = 1;
+    const int64_t c = (L + s - 1) / s;
+    *C = static_cast<int>(c);
+    *S = static_cast<int>((L + c - 1) / c);
+}
+
+template <typename TIn, int D>
+__global__ __launch_bounds__(DC_THREADS) void lla_decode_stats_kernel(const TIn* __restrict__ q,
+                                                                      const TIn* __restrict__ k,
+                                                                      double* __restrict__ stats, int L, int S,
+                                                                      int C, float sl2) {
+    constexpr int G = D / 8, KPP = DC_THREADS / G;
+    __shared__ float sx[DC_CMAX];
+    __shared__ float red[DC_THREADS / 64];
+    __shared__ float acc[KPP][D + 1];
+    const int tid = threadIdx.x, fg = tid % G, kl = tid / G;
+    const int bh = static_cast<int>(blockIdx.x) / S, sidx = static_cast<int>(blockIdx.x) % S;
+    const int j0 = sidx * C;
+    const int cnt = min(L, j0 + C) - j0;
+    const TIn* kh = k + (static_cast<int64_t>(bh) * L + j0) * D + 8 * fg;
+    float qv[8];
+    load8(q + static_cast<int64_t>(bh) * D + 8 * fg, qv);
+    float mloc = -INFINITY;
+#pragma unroll 4
+    for (int jj = kl; jj < cnt; jj += KPP) {
+        float kv[8];
+        load8(kh + static_cast<int64_t>(jj) * D, kv);
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf(qv[e], kv[e], a);
+        const float x = group_sum<G>(a) * sl2;
+        if (fg == 0) sx[jj] = x;
+        mloc = fmaxf(mloc, x);
+    }
+    const float m = block_reduce(mloc, true, red);
+    float om = 0.0f;
+    for (int jj = tid; jj < cnt; jj += DC_THREADS) {
+        const float e = exp2f(sx[jj] - m);
+        sx[jj] = e;
+        om += e;
+    }
+    const float omega = block_reduce(om, false, red);
+    float sk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int jj = kl; jj < cnt; jj += KPP) {
+        float kv[8];
+        load8(kh + static_cast<int64_t>(jj) * D, kv);
+        const float e = sx[jj];
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) sk[c8] = fmaf(e, kv[c8], sk[c8]);
+    }
+#pragma unroll
+    for (int c8 = 0; c8 < 8; ++c8) acc[kl][8 * fg + c8] = sk[c8];
+    __syncthreads();
+    double* st = stats + (static_cast<int64_t>(bh) * S + sidx) * (2 + D);
+    if (tid < D) {
+        double t = 0.0;
+        for (int l = 0; l < KPP; ++l) t += acc[l][tid];
+        st[2 + tid] = t;
+    }
+    if (tid == 0) {
+        st[0] = m;
+        st[1] = omega;
+    }
+}
+
+// The head's max M, omega and kbar (relative to M) from its chunks' statistics.
+template <int D>
+__device__ __forceinline__ void head_stats(const double* __restrict__ hs, int S, double* M_out, double* om_out,
+                                           double* kbar, int tid, int nthreads) {
+    double M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmax(M, hs[s * (2 + D)]);
+    double om = 0.0;
+    for (int s = 0; s < S; ++s) om += hs[s * (2 + D) + 1] * exp2(hs[s * (2 + D)] - M);
+    for (int f = tid; f < D; f += nthreads) {
+        double t = 0.0;
+        for (int s = 0; s < S; ++s) t += hs[s * (2 + D) + 2 + f] * exp2(hs[s * (2 + D)] - M);
+        kbar[f] = t / om;
+    }
+    *M_out = M;
+    *om_out = om;
+}
+
+template <int D, typename TA>
+constexpr int mom_smem_bytes() {
+    return (2 * D * LD_LDW + D) * static_cast<int>(sizeof(TA)) + (DC_THREADS / (D / 8)) * (D + 1) * 4;
+}
+
+// The whole chunk loop of wave W (its accumulator blocks are compile-time), so that the
+// accumulators stay in registers; every wave runs the same staging and barriers.
+template <typename TIn, int D, typename TA, int W>
+__device__ __forceinline__ void moments_wave(const TIn* __restrict__ qh, const TIn* __restrict__ kh,
+                                             const TIn* __restrict__ vh, TA* rk, TA* rv, const TA* kb, float* svs,
+                                             float Mf, int j0, int jend, int fg, int kl, int g, int c, float sl2,
+                                             TA* __restrict__ mo) {
+    using MB = MomBlocks<D>;
+    using AccT = typename Acc4<TA>::type;
+    constexpr int G = D / 8, KPP = DC_THREADS / G;
+    constexpr int B0 = W * MB::NT / 4, B1 = (W + 1) * MB::NT / 4;
+    float qv[8];
+    load8(qh, qv);
+    TA kbl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kbl[e] = kb[8 * fg + e];
+    float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    constexpr int NA = B1 > B0 ? B1 - B0 : 1;   // a wave may own no block (d = 16)
+    AccT acc[NA];
+#pragma unroll
+    for (int t = 0; t < NA; ++t) acc[t] = AccT{0, 0, 0, 0};
+    for (int js = j0; js < jend; js += LD_SUB) {
+        // stage: key js + jj on lanes kl*G.. (all lanes take part in the sums; keys past the
+        // chunk are zero rows)
+#pragma unroll
+        for (int p = 0; p < (LD_SUB + KPP - 1) / KPP; ++p) {
+            const int jj = kl + KPP * p;
+            const bool in = jj < LD_SUB && js + jj < jend;
+            float kv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, vv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (in) {
+                load8(kh + static_cast<int64_t>(js + jj) * D, kv);
+                load8(vh + static_cast<int64_t>(js + jj) * D, vv);
+            }
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaf(qv[e], kv[e], a);
+            const float x = group_sum<G>(a) * sl2;
+            const float w = in ? exp2f(x - Mf) : 0.0f;
+            const TA sw = sqrt(static_cast<TA>(w));
+            if (jj < LD_SUB) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    rk[(8 * fg + e) * LD_LDW + jj] = in ? sw * (static_cast<TA>(kv[e]) - kbl[e]) : static_cast<TA>(0);
+                    rv[(8 * fg + e) * LD_LDW + jj] = sw * static_cast<TA>(vv[e]);
+                    sv[e] = fmaf(w, vv[e], sv[e]);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int s4 = 0; s4 < LD_SUB / 4; ++s4) {
+            TA ak[MB::NB], av[MB::NB];
+#pragma unroll
+            for (int I = 0; I < MB::NB; ++I) {
+                ak[I] = rk[(16 * I + c) * LD_LDW + 4 * s4 + g];
+                av[I] = rv[(16 * I + c) * LD_LDW + 4 * s4 + g];
+            }
+            if constexpr (B1 > B0) mfma_blocks<D, B0>(ak, av, acc, std::make_integer_sequence<int, B1 - B0>{});
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int b = B0; b < B1; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mo[b * 256 + acc_row<TA>(g, r) * 16 + c] = acc[b - B0][r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) svs[kl * (D + 1) + 8 * fg + e] = sv[e];
+}
+
+template <typename TIn, int D, typename TA>
+__global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const double* __restrict__ stats, TA* __restrict__ mom, int L, int S, int C, float sl2) {
+    using MB = MomBlocks<D>;
+    constexpr int G = D / 8, KPP = DC_THREADS / G;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    TA* rk = reinterpret_cast<TA*>(lds);
+    TA* rv = rk + D * LD_LDW;
+    TA* kb = rv + D * LD_LDW;
+    float* svs = reinterpret_cast<float*>(kb + D);
+    __shared__ double hM;
+    __shared__ double kbd[D];
+    const int tid = threadIdx.x, fg = tid % G, kl = tid / G;
+    const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh = static_cast<int>(blockIdx.x) / S, sidx = static_cast<int>(blockIdx.x) % S;
+    const int j0 = sidx * C;
+    const int jend = min(L, j0 + C);
+    {
+        double M, om;
+        head_stats<D>(stats + static_cast<int64_t>(bh) * S * (2 + D), S, &M, &om, kbd, tid, DC_THREADS);
+        (void)om;
+        if (tid == 0) hM = M;
+        __syncthreads();
+        if (tid < D) kb[tid] = static_cast<TA>(kbd[tid]);
+        __syncthreads();
+    }
+    const float Mf = static_cast<float>(hM);
+    const TIn* qh = q + static_cast<int64_t>(bh) * D + 8 * fg;
+    const TIn* kh = k + static_cast<int64_t>(bh) * L * D + 8 * fg;
+    const TIn* vh = v + static_cast<int64_t>(bh) * L * D + 8 * fg;
+    TA* mo = mom + (static_cast<int64_t>(bh) * S + sidx) * (MB::NT * 256 + D);
+    switch (wu) {
+        case 0: moments_wave<TIn, D, TA, 0>(qh, kh, vh, rk, rv, kb, svs, Mf, j0, jend, fg, kl, g, c, sl2, mo); break;
+        case 1: moments_wave<TIn, D, TA, 1>(qh, kh, vh, rk, rv, kb, svs, Mf, j0, jend, fg, kl, g, c, sl2, mo); break;
+        case 2: moments_wave<TIn, D, TA, 2>(qh, kh, vh, rk, rv, kb, svs, Mf, j0, jend, fg, kl, g, c, sl2, mo); break;
+        default: moments_wave<TIn, D, TA, 3>(qh, kh, vh, rk, rv, kb, svs, Mf, j0, jend, fg, kl, g, c, sl2, mo); break;
+    }
+    __syncthreads();
+    if (tid < D) {
+        double t = 0.0;
+        for (int l = 0; l < KPP; ++l) t += svs[l * (D + 1) + tid];
+        mo[MB::NT * 256 + tid] = static_cast<TA>(t);
+    }
+}
+
+// Per head: A = sum of the chunks' C_kk + lambda 2^-M I (fp64, LDS), LDL^T, y, b.
+template <typename TIn, int D, typename TA>
+__global__ __launch_bounds__(DC_THREADS) void lla_decode_solve_kernel(
+    const TIn* __restrict__ q, const double* __restrict__ stats, const TA* __restrict__ mom,
+    float* __restrict__ out, int S, double lambda) {
+    using MB = MomBlocks<D>;
+    constexpr int LDA = D + 1;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    double* A = reinterpret_cast<double*>(lds);      // [D][D+1]
+    double* z = A + D * LDA;                         // kbar - q, then y
+    double* dg = z + D;                              // pivots (0 where dropped)
+    double* kbd = dg + D;
+    double* red = kbd + D;                           // [DC_THREADS]
+    __shared__ double hM, hOm, hthr;
+    const int tid = threadIdx.x, bh = static_cast<int>(blockIdx.x);
+    {
+        double M, om;
+        head_stats<D>(stats + static_cast<int64_t>(bh) * S * (2 + D), S, &M, &om, kbd, tid, DC_THREADS);
+        if (tid == 0) {
+            hM = M;
+            hOm = om;
+        }
+    }
+    __syncthreads();
+    const double ridge = lambda * exp2(-hM);
+    const TA* mh = mom + static_cast<int64_t>(bh) * S * (MB::NT * 256 + D);
+    for (int e = tid; e < MB::NKK * 256; e += DC_THREADS) {
+        const int b = e >> 8, rc = e & 255, row = rc >> 4, col = rc & 15;
+        int I = 0, rem = b;
+        while (rem >= MB::NB - I) { rem -= MB::NB - I; ++I; }
+        const int J = I + rem;
+        double t = 0.0;
+        for (int s = 0; s < S; ++s) t += static_cast<double>(mh[static_cast<int64_t>(s) * (MB::NT * 256 + D) + e]);
+        const int i = 16 * I + row, j = 16 * J + col;
+        if (i == j) t += ridge;
+        A[i * LDA + j] = t;
+        A[j * LDA + i] = t;
+    }
+    if (tid < D) z[tid] = kbd[tid] - static_cast<double>(load_elem_d(q, static_cast<int64_t>(bh) * D + tid));
+    __syncthreads();
+    // lambda > 0: drop only pivots that rounding made non-positive; lambda = 0: also those
+    // below 1e-12 of the largest diagonal entry (directions the cache leaves undetermined).
+    double dmax = 0.0;
+    for (int i = tid; i < D; i += DC_THREADS) dmax = fmax(dmax, A[i * LDA + i]);
+    red[tid] = dmax;
+    __syncthreads();
+    if (tid == 0) {
+        double mx = 0.0;
+        for (int i = 0; i < DC_THREADS; ++i) mx = fmax(mx, red[i]);
+        hthr = lambda > 0.0 ? 0.0 : 1e-12 * mx;
+    }
+    __syncthreads();
+    const double thr = hthr;
+    for (int kk = 0; kk < D; ++kk) {
+        const double piv = A[kk * LDA + kk];
+        const bool keep = piv > thr;
+        if (keep) {   // thread per row i of the trailing lower triangle; column kk is only read
+            const double ip = 1.0 / piv;
+            for (int i = kk + 1 + tid; i < D; i += DC_THREADS) {
+                const double li = A[i * LDA + kk] * ip;
+                for (int j = kk + 1; j <= i; ++j) A[i * LDA + j] -= li * A[j * LDA + kk];
+            }
+        }
+        __syncthreads();
+        for (int i = kk + 1 + tid; i < D; i += DC_THREADS) A[i * LDA + kk] = keep ? A[i * LDA + kk] * (1.0 / piv) : 0.0;
+        if (tid == 0) dg[kk] = keep ? piv : 0.0;
+        __syncthreads();
+    }
+    // L D L^T y = z: forward (unit lower), diagonal, backward
+    for (int kk = 0; kk < D; ++kk) {
+        const double yk = z[kk];
+        for (int i = kk + 1 + tid; i < D; i += DC_THREADS) z[i] -= A[i * LDA + kk] * yk;
+        __syncthreads();
+    }
+    for (int i = tid; i < D; i += DC_THREADS) z[i] = dg[i] > 0.0 ? z[i] / dg[i] : 0.0;
+    __syncthreads();
+    for (int kk = D - 1; kk >= 0; --kk) {
+        const double yk = z[kk];
+        for (int i = tid; i < kk; i += DC_THREADS) z[i] -= A[kk * LDA + i] * yk;
+        __syncthreads();
+    }
+    // b_f = S_v,f / omega - sum_g C_vk[f][g] y_g; thread (slice sl, feature f)
+    constexpr int SL = DC_THREADS / D;
+    const int f = tid % D, sl = tid / D;
+    double acc = 0.0;
+    for (int gi = sl; gi < D; gi += SL) {
+        const int b = MB::NKK + (f >> 4) * MB::NB + (gi >> 4);
+        const int e = b * 256 + (f & 15) * 16 + (gi & 15);
+        double t = 0.0;
+        for (int s = 0; s < S; ++s) t += static_cast<double>(mh[static_cast<int64_t>(s) * (MB::NT * 256 + D) + e]);
+        acc += t * z[gi];
+    }
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < D) {
+        double t = 0.0;
+        for (int l = 0; l < SL; ++l) t += red[l * D + tid];
+        double svf = 0.0;
+        for (int s = 0; s < S; ++s) svf += static_cast<double>(mh[static_cast<int64_t>(s) * (MB::NT * 256 + D) + MB::NT * 256 + tid]);
+        out[static_cast<int64_t>(bh) * D + tid] = static_cast<float>(svf / hOm - t);
+    }
+}
+
+template <int D, typename TA>
+constexpr int solve_smem_bytes() {
+    return (D * (D + 1) + 3 * D + DC_THREADS) * 8;
+}
+
+template <typename TIn, int D, typename TA>
+hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
+    using MB = MomBlocks<D>;
+    const int64_t BH = p.B * p.H;
+    int S = 1, C = 1;
+    lla_decode_split(BH, p.n, &S, &C);
+    const float sl2 = static_cast<float>(DC_LOG2E / p.h);
+    double* stats = static_cast<double*>(workspace);
+    TA* mom = reinterpret_cast<TA*>(reinterpret_cast<unsigned char*>(workspace) +
+                                    ((BH * S * (2 + D) * 8 + 255) & ~int64_t(255)));
+    static_assert(mom_smem_bytes<D, TA>() <= 160 * 1024 && solve_smem_bytes<D, TA>() <= 160 * 1024, "LDS");
+    static const hipError_t attr_err = [] {   // once per instantiation
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_solve_kernel<TIn, D, TA>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, solve_smem_bytes<D, TA>());
+        return e;
+    }();
+    hipError_t err = attr_err;
+    if (err != hipSuccess) return err;
+    const unsigned blocks = static_cast<unsigned>(BH * S);
+    prof_begin(p.stream, "lla_decode_stats_kernel");
+    lla_decode_stats_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), 0, p.stream>>>(
+        static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), stats, static_cast<int>(p.n), S, C, sl2);
+    prof_end(p.stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    prof_begin(p.stream, "lla_decode_moments_kernel");
+    lla_decode_moments_kernel<TIn, D, TA><<<dim3(blocks), dim3(DC_THREADS), mom_smem_bytes<D, TA>(), p.stream>>>(
+        static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, mom,
+        static_cast<int>(p.n), S, C, sl2);
+    prof_end(p.stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    prof_begin(p.stream, "lla_decode_solve_kernel");
+    lla_decode_solve_kernel<TIn, D, TA><<<dim3(static_cast<unsigned>(BH)), dim3(DC_THREADS), solve_smem_bytes<D, TA>(),
+                                          p.stream>>>(static_cast<const TIn*>(p.q), stats, mom, p.out, S, p.lambda);
+    prof_end(p.stream);
+    (void)MB::NT;
+    return hipGetLastError();
+}
+
+template <typename TIn, int D>
+hipError_t launch_lla_decode_p(const Problem& p, void* workspace) {
+    if (lla_decode_fp64(p.dtype, p.n, D)) return launch_lla_decode_t<TIn, D, double>(p, workspace);
+    return launch_lla_decode_t<TIn, D, float>(p, workspace);
+}
+
+template <typename TIn>
+hipError_t launch_lla_decode_d(const Problem& p, void* workspace) {
+    switch (p.d) {
+        case 16: return launch_lla_decode_p<TIn, 16>(p, workspace);
+        case 32: return launch_lla_decode_p<TIn, 32>(p, workspace);
+        case 64: return launch_lla_decode_p<TIn, 64>(p, workspace);
+        case 128: return launch_lla_decode_p<TIn, 128>(p, workspace);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+size_t lla_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int dtype) {
+    int S = 1, C = 1;
+    lla_decode_split(B * H, L, &S, &C);
+    const int64_t nb = d / 16, nt = nb * (nb + 1) / 2 + nb * nb;
+    const int64_t ta = lla_decode_fp64(dtype, L, d) ? 8 : 4;
+    return static_cast<size_t>(((B * H * S * (2 + d) * 8 + 255) & ~int64_t(255)) + B * H * S * (nt * 256 + d) * ta);
+}
+
+hipError_t launch_lla_decode(const Problem& p, void* workspace) {
+    return p.dtype == 0 ? launch_lla_decode_d<float>(p, workspace) : launch_lla_decode_d<uint16_t>(p, workspace);
 }
 
 }  // namespace lla

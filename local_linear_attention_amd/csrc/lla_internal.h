@@ -45,6 +45,11 @@ hipError_t launch_parallax_exact(const Problem& p);
 size_t decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d);
 hipError_t launch_parallax_decode(const Problem& p, void* workspace);
 
+// LLA decode: q [B, H, d] against a cache k, v [B, H, L, d] (L in Problem::n), every
+// (dtype, d); chunk statistics and moments go to `workspace` (lla_decode_workspace_bytes).
+size_t lla_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int dtype);
+hipError_t launch_lla_decode(const Problem& p, void* workspace);
+
 // Kernel-level timing (lla_profile_enable): events recorded around each launch.
 void prof_begin(hipStream_t stream, const char* kernel);
 void prof_end(hipStream_t stream);

@@ -14,6 +14,7 @@ __all__ = ["lla_forward", "lla_forward_ex", "lla_forward_ws", "lla_workspace_siz
            "lla_path_available", "lla_parallax_forward", "lla_parallax_forward_ex",
            "lla_parallax_forward_ws", "lla_parallax_workspace_size", "lla_parallax_path_available",
            "lla_parallax_decode", "lla_parallax_decode_ws", "lla_parallax_decode_workspace_size",
+           "lla_decode", "lla_decode_ws", "lla_decode_workspace_size",
            "lla_profile_enable", "lla_profile_collect",
            "lla_status_string", "lla_version", "LLAError",
            "library_path", "load_library", "STATUS", "PATHS", "DTYPES"]
@@ -83,6 +84,12 @@ def load_library():
     lib.lla_parallax_decode_ws.restype = ctypes.c_int
     lib.lla_parallax_decode_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.lla_parallax_decode_workspace_size.restype = ctypes.c_size_t
+    lib.lla_decode.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int, vp]
+    lib.lla_decode.restype = ctypes.c_int
+    lib.lla_decode_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int, vp, vp, ctypes.c_size_t]
+    lib.lla_decode_ws.restype = ctypes.c_int
+    lib.lla_decode_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.lla_decode_workspace_size.restype = ctypes.c_size_t
     lib.lla_profile_enable.argtypes = [ctypes.c_int]
     lib.lla_profile_enable.restype = ctypes.c_int
     lib.lla_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_char_p),
@@ -322,6 +329,43 @@ def lla_parallax_decode_ws(q, k, v, rho, h: float, workspace, out=None, stream=N
     if st != 0:
         raise LLAError(st, "lla_parallax_decode_ws")
     return out
+
+
+def lla_decode(q, k, v, h: float, lam: float, out=None, stream=None, workspace=None, use_ws=False):
+    """LLA decode step: q [B, H, d] against the cache k, v [B, H, L, d] (fp32 or bf16) -> fp32
+    out [B, H, d].  With ``use_ws`` the caller's ``workspace`` tensor (or None when none is
+    needed) is passed to lla_decode_ws instead of the library pool."""
+    import torch
+    dtype, out = _marshal_decode(q, k, v, q, out)
+    B, H, L, d = k.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    lib = load_library()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d, float(h), float(lam), dtype,
+            ctypes.c_void_p(stream.cuda_stream))
+    if use_ws:
+        if workspace is None:
+            ws_ptr, ws_bytes = None, 0
+        else:
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous device tensor")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        st = lib.lla_decode_ws(*args, ctypes.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes)
+    else:
+        st = lib.lla_decode(*args)
+    if st != 0:
+        raise LLAError(st, "lla_decode_ws" if use_ws else "lla_decode")
+    return out
+
+
+def lla_decode_ws(q, k, v, h: float, lam: float, workspace, out=None, stream=None):
+    """lla_decode with caller-provided scratch (allocates nothing but `out`)."""
+    return lla_decode(q, k, v, h, lam, out=out, stream=stream, workspace=workspace, use_ws=True)
+
+
+def lla_decode_workspace_size(B: int, H: int, L: int, d: int, dtype: str) -> int:
+    """Bytes of device scratch an LLA decode step needs."""
+    return int(load_library().lla_decode_workspace_size(B, H, L, d, DTYPES[dtype]))
 
 
 def lla_profile_enable(enable: bool = True) -> bool:

@@ -31,7 +31,8 @@ def declared_enums():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["lla_forward", "lla_forward_ex", "lla_forward_ws",
+    assert declared_functions() == ["lla_decode", "lla_decode_workspace_size", "lla_decode_ws",
+                                    "lla_forward", "lla_forward_ex", "lla_forward_ws",
                                     "lla_parallax_decode", "lla_parallax_decode_workspace_size",
                                     "lla_parallax_decode_ws",
                                     "lla_parallax_forward", "lla_parallax_forward_ex",
@@ -272,3 +273,51 @@ def test_decode_ws_validation_before_launch():
             ctypes.c_void_p(OUT), 1, 2, 4096, 64, 8.0, 1, None]
     assert lib.lla_parallax_decode_ws(*args, None, 0) == 5
     assert lib.lla_parallax_decode_ws(*args, ctypes.c_void_p(0x50000000), 64) == 5
+
+
+# ---------------------------------------------------------------- LLA decode
+def call_lla_decode(lib, q=Q, k=K, v=V, out=OUT, B=2, H=3, L=100, d=64, h=8.0, lam=0.01, dtype=1):
+    return lib.lla_decode(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), ctypes.c_void_p(out),
+                          B, H, L, d, h, lam, dtype, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(out=0), 1),
+    (dict(B=0), 2), (dict(L=0), 2), (dict(L=2 ** 31), 2),
+    (dict(h=0.0), 3), (dict(h=math.nan), 3), (dict(lam=-1.0), 3), (dict(lam=math.inf), 3),
+    (dict(d=48), 4), (dict(dtype=2), 4),
+    (dict(out=Q + 64), 7), (dict(out=K + 4096), 7), (dict(out=V - 64), 7),
+])
+def test_lla_decode_invalid_arguments_are_rejected_before_any_launch(kw, expect):
+    assert call_lla_decode(_lib(), **kw) == expect
+
+
+def lla_decode_split(BH, L):
+    """Chunks per head of the LLA decode kernels: about 1024 blocks in all, chunks of 512 to
+    2048 keys, none empty."""
+    s = -(-1024 // BH)
+    s = min(s, -(-L // 512))
+    s = max(s, -(-L // 2048), 1)
+    c = -(-L // s)
+    return -(-L // c)
+
+
+def test_lla_decode_workspace_size():
+    from local_linear_attention_amd import lla
+    for B, H, L, d, dt in ((8, 16, 8192, 64, "bf16"), (1, 1, 100, 64, "bf16"), (2, 3, 700, 16, "f32"),
+                           (1, 2, 5000, 128, "bf16"), (4, 4, 1000, 32, "f32")):
+        S = lla_decode_split(B * H, L)
+        nb = d // 16
+        nt = nb * (nb + 1) // 2 + nb * nb
+        ta = 8 if (dt == "f32" or L < 2 * d) else 4
+        stats = -(-(B * H * S * (2 + d) * 8) // 256) * 256
+        assert lla.lla_decode_workspace_size(B, H, L, d, dt) == stats + B * H * S * (nt * 256 + d) * ta, (B, H, L, d)
+    assert lla.lla_decode_workspace_size(1, 1, 100, 48, "bf16") == 0
+
+
+def test_lla_decode_ws_validation_before_launch():
+    lib = _lib()
+    args = [ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V), ctypes.c_void_p(OUT),
+            1, 2, 4096, 64, 8.0, 0.01, 1, None]
+    assert lib.lla_decode_ws(*args, None, 0) == 5
+    assert lib.lla_decode_ws(*args, ctypes.c_void_p(0x50000000), 64) == 5

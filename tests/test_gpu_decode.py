@@ -1,10 +1,16 @@
-"""GPU parity of the Parallax decode step (one query per head against its key-value cache)
-against the fp64 oracle.
+"""GPU parity of the two decode steps (one query per head against its key-value cache)
+against the fp64 oracles.
 
-Every (batch, head) output is compared: small caches (one chunk per head, written
-directly) and long ones (several chunks merged by the second launch), every supported head
-size and both dtypes, and the four decode workloads at full size.  The kernels compute in
-fp32, so besides the contract bars (1e-4 fp32, 3e-3 bf16 inputs) they are held to 2e-5.
+Parallax decode: every (batch, head) output is compared: small caches (one chunk per head,
+written directly) and long ones (several chunks merged by the second launch), every
+supported head size and both dtypes, and the four decode workloads at full size.  The
+kernels compute in fp32, so besides the contract bars (1e-4 fp32, 3e-3 bf16 inputs) they
+are held to 2e-5.
+
+LLA decode: every (batch, head) output against the LLA oracle applied to the head's whole
+cache: caches shorter than twice the head size (fp64 moments), longer ones (fp32 matrix-core
+moments, several chunks), every head size, both dtypes, lambda at 0 and at a size where the
+result is softmax attention, the decode workload at full size, and the workspace entry point.
 """
 import numpy as np
 import pytest
@@ -122,3 +128,95 @@ def test_decode_matches_the_forward_last_row():
     got = run(q, k, v, rho, "bf16", w.h)
     err = float(row_errors(got, fwd.cpu().numpy()[:, :, -1].astype(np.float64)).max())
     assert err <= FP32_BOUND, err
+
+
+# ---------------------------------------------------------------- LLA decode
+def run_lla(q, k, v, dtype, h, lam):
+    import torch
+    from local_linear_attention_amd import lla_decode
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    out = lla_decode(tq, tk, tv, h, lam)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def check_lla(got, ref, dtype, label):
+    err = row_errors(got, ref)
+    worst = float(err.max())
+    print(f"[lla decode parity] {label} rows={err.size} max_row_err={worst:.3e}", flush=True)
+    assert np.isfinite(got).all(), label
+    assert worst <= TOL[dtype], (label, worst)
+
+
+LLA_SMALL = [
+    {"B": 1, "H": 1, "L": 1},
+    {"B": 2, "H": 3, "L": 2},
+    {"B": 2, "H": 3, "L": 63},
+    {"B": 1, "H": 2, "L": 100},               # L < 2d: fp64 moments
+    {"B": 1, "H": 2, "L": 129},               # fp32 moments, three sub-tiles with a ragged one
+    {"B": 2, "H": 2, "L": 700},
+    {"B": 1, "H": 1, "L": 5000},              # several chunks
+    {"B": 3, "H": 2, "L": 700, "d": 16},
+    {"B": 3, "H": 2, "L": 700, "d": 32},
+    {"B": 2, "H": 2, "L": 1000, "d": 128, "h": 11.3},
+    {"B": 1, "H": 2, "L": 300, "d": 128, "h": 11.3},   # L > 2d at d = 128
+    {"B": 2, "H": 3, "L": 900, "dtype": "f32"},
+    {"B": 1, "H": 2, "L": 40, "dtype": "f32"},
+    {"B": 1, "H": 2, "L": 600, "d": 128, "dtype": "f32", "h": 11.3},
+    {"B": 300, "H": 4, "L": 200},
+]
+
+
+@pytest.mark.parametrize("shape", LLA_SMALL, ids=[str(s) for s in LLA_SMALL])
+def test_lla_decode_small_caches_every_head(shape):
+    require_gpu()
+    from oracle import lla_decode as oracle_lla_decode
+    w, q, k, v, _ = arrays("lla_decode_b8_l8192", **shape)
+    ref = oracle_lla_decode(q, k, v, w.h, w.lam)
+    got = run_lla(q, k, v, w.dtype, w.h, w.lam)
+    check_lla(got, ref, w.dtype, str(shape))
+
+
+@pytest.mark.parametrize("lam", [0.0, 1e8])
+def test_lla_decode_lambda_extremes(lam):
+    # lambda = 0 on caches longer than d (full-rank key covariance); lambda -> infinity gives
+    # softmax attention
+    require_gpu()
+    from oracle import lla_decode as oracle_lla_decode
+    w, q, k, v, _ = arrays("lla_decode_b8_l8192", B=2, H=2, L=800)
+    ref = oracle_lla_decode(q, k, v, w.h, lam)
+    got = run_lla(q, k, v, w.dtype, w.h, lam)
+    check_lla(got, ref, w.dtype, f"lambda={lam:g}")
+
+
+def test_lla_decode_workload_and_forward_last_row():
+    torch = require_gpu()
+    from local_linear_attention_amd import (lla_decode, lla_decode_workspace_size, lla_decode_ws, lla_forward_ex,
+                                            lla_profile_collect, lla_profile_enable)
+    from oracle import lla_decode as oracle_lla_decode
+    w, q, k, v, _ = arrays("lla_decode_b8_l8192")
+    ref = oracle_lla_decode(q, k, v, w.h, w.lam)
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    nbytes = lla_decode_workspace_size(w.B, w.H, w.L, w.d, "bf16")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    lla_profile_enable(True)
+    try:
+        a = lla_decode_ws(tq, tk, tv, w.h, w.lam, ws)
+        rec = lla_profile_collect()
+    finally:
+        lla_profile_enable(False)
+    b = lla_decode(tq, tk, tv, w.h, w.lam)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert [n for n, _ in rec] == ["lla_decode_stats_kernel", "lla_decode_moments_kernel", "lla_decode_solve_kernel"]
+    check_lla(a.cpu().numpy().astype(np.float64), ref, "bf16", "lla_decode_b8_l8192")
+    # the LLA forward's last row over the same positions (matrix-core path) agrees
+    w2, q2, k2, v2, _ = arrays("lla_decode_b8_l8192", B=1, H=2, L=700)
+    qs = np.array(lla_inputs.round_to_bf16(np.random.default_rng(11).standard_normal(k2.shape).astype(np.float32)))
+    qs[:, :, -1] = q2
+    fwd = lla_forward_ex(*(to_device(x, "bf16") for x in (qs, k2, v2)), w2.h, w2.lam, path="fast")
+    torch.cuda.synchronize()
+    dec = run_lla(q2, k2, v2, "bf16", w2.h, w2.lam)
+    err = float(row_errors(dec, fwd.cpu().numpy()[:, :, -1].astype(np.float64)).max())
+    print(f"[lla decode vs forward last row] {err:.2e}", flush=True)
+    assert err <= 2 * TOL["bf16"]
