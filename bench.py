@@ -1,16 +1,18 @@
-"""Throughput of the causal LLA forward (or the Parallax forward with a given probe) on one
-MI355X.
+"""Throughput of the causal LLA forward (or the Parallax forward with a given probe, or one of
+the two decode steps) on one MI355X.
 
-One step is one lla_forward call (lla_parallax_forward with --method parallax) over the whole
-workload (every query row of every head) with the inputs already resident in HBM.  Prints
-one JSON line.
+One step is one lla_forward call (lla_parallax_forward with --method parallax; one decode
+call, one query per head against its whole cache, with --method parallax_decode or
+lla_decode) over the whole workload with the inputs already resident in HBM.  Prints one
+JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d24] [--path auto]
-                    [--method lla|parallax]
+                    [--method lla|parallax|parallax_decode|lla_decode]
 
 The default workload is B=2, H=16, n=4096, d=64 with bf16 inputs (head shape of a
 1024-wide, 16-head model), h = 8, lambda = 1e-2; with --method parallax the same q, k, v
-plus an RMS-normalised probe (workload parallax_d24).
+plus an RMS-normalised probe (workload parallax_d24).  The decode methods default to eight
+sequences of 16 heads with 8192 cached bf16 keys and values each.
 """
 from __future__ import annotations
 
@@ -34,6 +36,8 @@ PEAK = {
     "mfma_f16_TFLOPs": 2516.6,   # dense fp16/bf16 matrix
     "valu_f64_TFLOPs": 78.6,     # fp64 vector
     "valu_f32_TFLOPs": 157.3,    # fp32 vector
+    "mfma_f32_TFLOPs": 157.3,    # dense fp32 matrix
+    "mfma_f64_TFLOPs": 78.6,     # dense fp64 matrix
 }
 
 
@@ -67,6 +71,10 @@ KERNEL_BOUND = {
     "lla_parallax_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_parallax_decode_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_parallax_merge_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla_decode_stats_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla_decode_moments_kernel": ("mfma", PEAK["mfma_f32_TFLOPs"]),
+    "lla_decode_reduce_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla_decode_solve_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
 }
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
@@ -196,26 +204,76 @@ def cpu_baseline(w, q, k, v, seconds, rho=None):
 
 
 METRIC_DECODE = "Parallax decode (given probe) queries/s and HBM GB/s at B8 H16 L8192 d64 bf16, 1 GPU"
+METRIC_LLA_DECODE = "LLA decode queries/s and HBM GB/s at B8 H16 L8192 d64 bf16, 1 GPU"
 
 
-def decode_bytes(B, H, L, d, elt):
-    """Algorithmic HBM bytes of one decode step: the cache (K and V) read once, q and rho
-    read, the fp32 output written."""
-    return 2 * B * H * L * d * elt + 2 * B * H * d * elt + B * H * d * 4
+def decode_bytes(B, H, L, d, elt, nvec=2):
+    """Algorithmic HBM bytes of one decode step: the cache (K and V) read once, the nvec
+    per-head input vectors (q, and rho for Parallax) read, the fp32 output written."""
+    return 2 * B * H * L * d * elt + nvec * B * H * d * elt + B * H * d * 4
+
+
+def lla_moment_flops(B, H, L, d):
+    """Algorithmic flops of the LLA decode moments: per cached key the upper triangle of the
+    weighted key covariance (d(d+1)/2 products and adds), the value-key cross moment (d^2)
+    and the weighted value sum (d)."""
+    return B * H * L * (d * (d + 1) + 2 * d * d + 2 * d)
+
+
+def lla_solve_flops(B, H, d):
+    """Per head: LDL^T factorisation (d^3/3), two triangular solves and the value
+    correction (2 d^2 each)."""
+    return B * H * (d ** 3 / 3 + 2 * d * d + 2 * d * d)
+
+
+def lla_decode_chunks(BH, L):
+    """Chunks per head of the LLA decode launches (the library's split: about 1024 blocks,
+    512 to 2048 keys per chunk)."""
+    s = min(-(-1024 // BH), -(-L // 512))
+    s = max(s, -(-L // 2048), 1)
+    c = -(-L // s)
+    return -(-L // c)
+
+
+def decode_kernel_units(name, w, elt):
+    """(algorithmic amount, unit) of one launch of each decode kernel at workload w."""
+    B, H, L, d = w.B, w.H, w.L, w.d
+    if name == "lla_parallax_decode_kernel":
+        # moves every byte of the step but the merge's partial sums
+        return decode_bytes(B, H, L, d, elt), "B"
+    if name == "lla_decode_stats_kernel":
+        # reads the keys and the query
+        return B * H * L * d * elt + B * H * d * elt, "B"
+    if name == "lla_decode_moments_kernel":
+        return lla_moment_flops(B, H, L, d), "flop"
+    if name == "lla_decode_reduce_kernel":
+        # reads every chunk's moments, writes the heads' fp64 sums
+        nb = d // 16
+        e = (nb * (nb + 1) // 2 + nb * nb) * 256 + d
+        S = lla_decode_chunks(B * H, L)
+        ta = 8 if (w.dtype == "f32" or L < 2 * d) else 4
+        return B * H * S * e * ta + B * H * e * 8, "B"
+    if name == "lla_decode_solve_kernel":
+        return lla_solve_flops(B, H, d), "flop"
+    return None, None
 
 
 def decode_cpu_baseline(w, q, k, v, rho, seconds):
-    """The fp64 decode oracle on whole heads drawn at random, projected to the workload."""
+    """The fp64 decode oracle (Parallax when a probe is given, else LLA) on whole heads drawn
+    at random, projected to the workload."""
     import numpy as np
 
-    from oracle import parallax_decode
+    from oracle import lla_decode, parallax_decode
     rng = np.random.default_rng(12345)
     done, elapsed = 0, 0.0
     while elapsed < seconds and done < w.B * w.H:
         b, hh = int(rng.integers(w.B)), int(rng.integers(w.H))
+        sl = (slice(b, b + 1), slice(hh, hh + 1))
         t0 = time.perf_counter()
-        parallax_decode(q[b:b + 1, hh:hh + 1], k[b:b + 1, hh:hh + 1], v[b:b + 1, hh:hh + 1],
-                        rho[b:b + 1, hh:hh + 1], w.h)
+        if rho is None:
+            lla_decode(q[sl], k[sl], v[sl], w.h, w.lam)
+        else:
+            parallax_decode(q[sl], k[sl], v[sl], rho[sl], w.h)
         elapsed += time.perf_counter() - t0
         done += 1
     full = elapsed * w.B * w.H / done
@@ -229,14 +287,18 @@ def bench_decode(args):
     import torch
 
     import lla_inputs
-    from local_linear_attention_amd import lla_parallax_decode, lla_profile_collect, lla_profile_enable
+    from local_linear_attention_amd import lla_decode, lla_parallax_decode, lla_profile_collect, lla_profile_enable
 
-    w = lla_inputs.DECODE_WORKLOADS[args.workload or "decode_b8_l8192"]
+    parallax = args.method == "parallax_decode"
+    w = lla_inputs.DECODE_WORKLOADS[args.workload or ("decode_b8_l8192" if parallax else "lla_decode_b8_l8192")]
     q, k, v, rho = lla_inputs.generate_decode(w)
+    if not parallax:
+        rho = None
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    tq, tk, tv, tr = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v, rho))
+    tq, tk, tv = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v))
+    tr = torch.from_numpy(rho).to(tdt).to(dev).contiguous() if parallax else None
     out = torch.empty(tq.shape, dtype=torch.float32, device=dev)
     if args.copy_calibration_mib > 0:
         src = torch.ones((args.copy_calibration_mib << 20) // 4, dtype=torch.float32, device=dev)
@@ -247,7 +309,10 @@ def bench_decode(args):
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        lla_parallax_decode(tq, tk, tv, tr, w.h, out=out, stream=stream)
+        if parallax:
+            lla_parallax_decode(tq, tk, tv, tr, w.h, out=out, stream=stream)
+        else:
+            lla_decode(tq, tk, tv, w.h, w.lam, out=out, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -277,15 +342,37 @@ def bench_decode(args):
     for name, ms in rec:
         per_kernel.setdefault(name, []).append(ms)
     elt = 4 if w.dtype == "f32" else 2
-    nbytes = decode_bytes(w.B, w.H, w.L, w.d, elt)
-    kernels = {name: {"launches": len(lst), "avg_ms": statistics.mean(lst)} for name, lst in per_kernel.items()}
-    dk = kernels["lla_parallax_decode_kernel"]
-    # the decode kernel moves every byte of the step but the merge's partial sums
-    dk["bytes"] = nbytes
-    dk["GBps"] = nbytes / (dk["avg_ms"] * 1e-3) / 1e9
-    traffic = load_traffic("lla_parallax_decode_kernel", w.name)
+    nbytes = decode_bytes(w.B, w.H, w.L, w.d, elt, nvec=2 if parallax else 1)
+    kernels = {}
+    for name, lst in per_kernel.items():
+        avg = statistics.mean(lst)
+        amount, unit = decode_kernel_units(name, w, elt)
+        bound, peak = KERNEL_BOUND[name]
+        ent = {"launches": len(lst), "avg_ms": avg, "bound": bound, "peak": peak}
+        if unit == "B":
+            ent.update(bytes=amount, GBps=amount / (avg * 1e-3) / 1e9)
+        elif unit == "flop":
+            ent.update(flops=amount, tflops=amount / (avg * 1e-3) / 1e12)
+        kernels[name] = ent
+    dom = max(kernels, key=lambda nm: kernels[nm]["avg_ms"] * kernels[nm]["launches"])
+    dk = kernels[dom]
+    if "GBps" in dk:
+        achieved, unit = dk["GBps"], "GB/s"
+    else:
+        achieved, unit = dk["tflops"], "TFLOP/s"
+    traffic = load_traffic(dom, w.name)
+    if parallax:
+        config_text = f"{w.name}: B{w.B} H{w.H} L{w.L} d{w.d} {w.dtype} cache, one query and probe per head, h={w.h:g}"
+    else:
+        config_text = f"{w.name}: B{w.B} H{w.H} L{w.L} d{w.d} {w.dtype} cache, one query per head, h={w.h:g}, " \
+                      f"lambda={w.lam:g}"
+    if parallax:
+        arith = "f32 (bf16 inputs)" if w.dtype == "bf16" else "f32"
+    else:
+        arith = ("f32 scores, f64 moments and solve" if w.dtype == "f32" or w.L < 2 * w.d
+                 else "f32 scores and matrix-core moments, f64 solve")
     result = {
-        "metric": METRIC_DECODE,
+        "metric": METRIC_DECODE if parallax else METRIC_LLA_DECODE,
         "value": w.queries / (ms_per_step * 1e-3),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -295,17 +382,16 @@ def bench_decode(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (bf16 inputs)" if w.dtype == "bf16" else "f32",
+        "dtype": arith,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: B{w.B} H{w.H} L{w.L} d{w.d} {w.dtype} cache, one query and probe per "
-                               f"head, h={w.h:g}",
+        "config": {"workload": config_text,
                    "B": w.B, "H": w.H, "L": w.L, "d": w.d, "input_dtype": w.dtype, "queries": w.queries},
         "hbm_GBps": nbytes / (ms_per_step * 1e-3) / 1e9,
         "kernels": kernels,
         "timing_ms": {"median": statistics.median(per_ms), "p10": float(np.percentile(per_ms, 10)),
                       "p90": float(np.percentile(per_ms, 90))},
-        "roofline": {"kernel": "lla_parallax_decode_kernel", "bound": "hbm", "achieved": dk["GBps"],
-                     "peak": PEAK["hbm_GBps"], "unit": "GB/s", "frac": dk["GBps"] / PEAK["hbm_GBps"],
+        "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": achieved,
+                     "peak": dk["peak"], "unit": unit, "frac": achieved / dk["peak"],
                      "traffic": traffic},
         "gfx": torch.cuda.get_device_properties(dev).gcnArchName,
     }
@@ -319,9 +405,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--method", default="lla", choices=["lla", "parallax", "parallax_decode"])
+    ap.add_argument("--method", default="lla", choices=["lla", "parallax", "parallax_decode", "lla_decode"])
     ap.add_argument("--workload", default=None,
-                    help="default: d24 (LLA), parallax_d24 (Parallax), decode_b8_l8192 (decode)")
+                    help="default: d24 (LLA), parallax_d24 (Parallax), decode_b8_l8192 (Parallax decode), "
+                         "lla_decode_b8_l8192 (LLA decode)")
     ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -336,7 +423,7 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    if args.method == "parallax_decode":
+    if args.method in ("parallax_decode", "lla_decode"):
         bench_decode(args)
         return
 

@@ -391,7 +391,6 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_stats_kernel(const TIn*
                                                                       double* __restrict__ stats, int L, int S,
                                                                       int C, float sl2) {
     constexpr int G = D / 8, KPP = DC_THREADS / G;
-    __shared__ float sx[DC_CMAX];
     __shared__ float red[DC_THREADS / 64];
     __shared__ float acc[KPP][D + 1];
     const int tid = threadIdx.x, fg = tid % G, kl = tid / G;
@@ -401,7 +400,10 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_stats_kernel(const TIn*
     const TIn* kh = k + (static_cast<int64_t>(bh) * L + j0) * D + 8 * fg;
     float qv[8];
     load8(q + static_cast<int64_t>(bh) * D + 8 * fg, qv);
-    float mloc = -INFINITY;
+    // one read of the keys: each lane group keeps its own running max mt and rescales its
+    // omega and key sum when the max grows (a select, not a branch: groups differ)
+    float mt = -INFINITY, om = 0.0f;
+    float sk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int jj = kl; jj < cnt; jj += KPP) {
         float kv[8];
@@ -410,28 +412,19 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_stats_kernel(const TIn*
 #pragma unroll
         for (int e = 0; e < 8; ++e) a = fmaf(qv[e], kv[e], a);
         const float x = group_sum<G>(a) * sl2;
-        if (fg == 0) sx[jj] = x;
-        mloc = fmaxf(mloc, x);
-    }
-    const float m = block_reduce(mloc, true, red);
-    float om = 0.0f;
-    for (int jj = tid; jj < cnt; jj += DC_THREADS) {
-        const float e = exp2f(sx[jj] - m);
-        sx[jj] = e;
-        om += e;
-    }
-    const float omega = block_reduce(om, false, red);
-    float sk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int jj = kl; jj < cnt; jj += KPP) {
-        float kv[8];
-        load8(kh + static_cast<int64_t>(jj) * D, kv);
-        const float e = sx[jj];
+        const float mn = fmaxf(mt, x);
+        const float sc = exp2f(mt - mn);   // 0 on the group's first key
+        const float w = exp2f(x - mn);
+        om = fmaf(om, sc, w);
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) sk[c8] = fmaf(e, kv[c8], sk[c8]);
+        for (int e = 0; e < 8; ++e) sk[e] = fmaf(sk[e], sc, w * kv[e]);
+        mt = mn;
     }
+    const float m = block_reduce(mt, true, red);   // cnt >= 1: finite
+    const float sc = exp2f(mt - m);                // 0 for groups that saw no key
+    const float omega = block_reduce(fg == 0 ? om * sc : 0.0f, false, red);
 #pragma unroll
-    for (int c8 = 0; c8 < 8; ++c8) acc[kl][8 * fg + c8] = sk[c8];
+    for (int e = 0; e < 8; ++e) acc[kl][8 * fg + e] = sk[e] * sc;
     __syncthreads();
     double* st = stats + (static_cast<int64_t>(bh) * S + sidx) * (2 + D);
     if (tid < D) {
@@ -445,19 +438,49 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_stats_kernel(const TIn*
     }
 }
 
-// The head's max M, omega and kbar (relative to M) from its chunks' statistics.
-template <int D>
-__device__ __forceinline__ void head_stats(const double* __restrict__ hs, int S, double* M_out, double* om_out,
-                                           double* kbar, int tid, int nthreads) {
-    double M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmax(M, hs[s * (2 + D)]);
-    double om = 0.0;
-    for (int s = 0; s < S; ++s) om += hs[s * (2 + D) + 1] * exp2(hs[s * (2 + D)] - M);
-    for (int f = tid; f < D; f += nthreads) {
-        double t = 0.0;
-        for (int s = 0; s < S; ++s) t += hs[s * (2 + D) + 2 + f] * exp2(hs[s * (2 + D)] - M);
-        kbar[f] = t / om;
+// Block-wide max or sum of one double per thread (every thread gets the result).
+__device__ __forceinline__ double block_reduce_d(double x, bool is_max, double* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const double y = __shfl_xor(x, o);
+        x = is_max ? fmax(x, y) : x + y;
     }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double r = red[0];
+#pragma unroll
+    for (int i = 1; i < DC_THREADS / 64; ++i) r = is_max ? fmax(r, red[i]) : r + red[i];
+    return r;
+}
+
+// The head's max M, omega and kbar (relative to M, into LDS kbar[D]) from its S chunks'
+// statistics, with the whole block: chunks over threads for M and omega, (feature, chunk
+// slice) pairs for kbar.  sh: DC_THREADS doubles of LDS.  Ends with a barrier.
+template <int D>
+__device__ __forceinline__ void head_stats(const double* __restrict__ hs, int S, double* sh, double* kbar,
+                                           double* M_out, double* om_out) {
+    constexpr int SL = DC_THREADS / D;
+    const int tid = threadIdx.x;
+    double m = -INFINITY;
+    for (int s = tid; s < S; s += DC_THREADS) m = fmax(m, hs[s * (2 + D)]);
+    const double M = block_reduce_d(m, true, sh);
+    double o = 0.0;
+    for (int s = tid; s < S; s += DC_THREADS) o += hs[s * (2 + D) + 1] * exp2(hs[s * (2 + D)] - M);
+    const double om = block_reduce_d(o, false, sh + 8);
+    const int f = tid % D, sl = tid / D;
+    double t = 0.0;
+    for (int s = sl; s < S; s += SL) t += hs[s * (2 + D) + 2 + f] * exp2(hs[s * (2 + D)] - M);
+    __syncthreads();
+    sh[tid] = t;
+    __syncthreads();
+    if (tid < D) {
+        double r = 0.0;
+#pragma unroll
+        for (int l = 0; l < SL; ++l) r += sh[l * D + tid];
+        kbar[tid] = r / om;
+    }
+    __syncthreads();
     *M_out = M;
     *om_out = om;
 }
@@ -547,7 +570,7 @@ __global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
     TA* rv = rk + D * LD_LDW;
     TA* kb = rv + D * LD_LDW;
     float* svs = reinterpret_cast<float*>(kb + D);
-    __shared__ double hM;
+    __shared__ double sh[DC_THREADS];
     __shared__ double kbd[D];
     const int tid = threadIdx.x, fg = tid % G, kl = tid / G;
     const int lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -555,16 +578,11 @@ __global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
     const int bh = static_cast<int>(blockIdx.x) / S, sidx = static_cast<int>(blockIdx.x) % S;
     const int j0 = sidx * C;
     const int jend = min(L, j0 + C);
-    {
-        double M, om;
-        head_stats<D>(stats + static_cast<int64_t>(bh) * S * (2 + D), S, &M, &om, kbd, tid, DC_THREADS);
-        (void)om;
-        if (tid == 0) hM = M;
-        __syncthreads();
-        if (tid < D) kb[tid] = static_cast<TA>(kbd[tid]);
-        __syncthreads();
-    }
-    const float Mf = static_cast<float>(hM);
+    double M, om;
+    head_stats<D>(stats + static_cast<int64_t>(bh) * S * (2 + D), S, sh, kbd, &M, &om);
+    if (tid < D) kb[tid] = static_cast<TA>(kbd[tid]);
+    __syncthreads();
+    const float Mf = static_cast<float>(M);
     const TIn* qh = q + static_cast<int64_t>(bh) * D + 8 * fg;
     const TIn* kh = k + static_cast<int64_t>(bh) * L * D + 8 * fg;
     const TIn* vh = v + static_cast<int64_t>(bh) * L * D + 8 * fg;
@@ -583,132 +601,155 @@ __global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
     }
 }
 
-// Per head: A = sum of the chunks' C_kk + lambda 2^-M I (fp64, LDS), LDL^T, y, b.
-template <typename TIn, int D, typename TA>
+// Sum of the S chunks' moments of each head, in chunk order (fp64): one thread per entry.
+template <typename TA>
+__global__ __launch_bounds__(DC_THREADS) void lla_decode_reduce_kernel(const TA* __restrict__ mom,
+                                                                       double* __restrict__ sum, int S, int E,
+                                                                       int blocks_per_head) {
+    const int bh = static_cast<int>(blockIdx.x) / blocks_per_head;
+    const int e = (static_cast<int>(blockIdx.x) % blocks_per_head) * DC_THREADS + static_cast<int>(threadIdx.x);
+    if (e >= E) return;
+    const TA* p = mom + static_cast<int64_t>(bh) * S * E + e;
+    double t0 = 0.0, t1 = 0.0, t2 = 0.0, t3 = 0.0;
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+        t0 += static_cast<double>(p[static_cast<int64_t>(s) * E]);
+        t1 += static_cast<double>(p[static_cast<int64_t>(s + 1) * E]);
+        t2 += static_cast<double>(p[static_cast<int64_t>(s + 2) * E]);
+        t3 += static_cast<double>(p[static_cast<int64_t>(s + 3) * E]);
+    }
+    for (; s < S; ++s) t0 += static_cast<double>(p[static_cast<int64_t>(s) * E]);
+    sum[static_cast<int64_t>(bh) * E + e] = (t0 + t1) + (t2 + t3);
+}
+
+// Index of entry (i, j), i <= j, of C_kk in a head's moment blocks.
+template <int D>
+__device__ __forceinline__ int kk_index(int i, int j) {
+    constexpr int NB = D / 16;
+    const int I = i >> 4, J = j >> 4;
+    return (I * NB - I * (I - 1) / 2 + (J - I)) * 256 + (i & 15) * 16 + (j & 15);
+}
+
+// Per head: A = C_kk + lambda 2^-M I (fp64), solved for y with A y = kbar - q by Gauss-Jordan
+// elimination: thread (ti, tj) of a 16 x 16 grid holds the TS x TS tile of A at rows
+// ti*TS.., columns tj*TS.. in registers; step p publishes column p (double-buffered in LDS,
+// one barrier per step) and every thread eliminates it from its rows other than p.  On the
+// symmetric trailing block row p equals column p, and the columns of earlier pivots are
+// already zero in row p, so column p alone drives the update.  The pivots are those of
+// LDL^T; a pivot that is not positive (lambda > 0: made so by rounding) or below 1e-12 of the
+// largest diagonal entry (lambda = 0: a direction the cache leaves undetermined) is skipped
+// and its unknown set to 0.  Then b = S_v/omega - C_vk y.
+// mom: the head's summed moments (TM = double) or, with one chunk per head, the chunk's own.
+template <typename TIn, int D, typename TM>
 __global__ __launch_bounds__(DC_THREADS) void lla_decode_solve_kernel(
-    const TIn* __restrict__ q, const double* __restrict__ stats, const TA* __restrict__ mom,
+    const TIn* __restrict__ q, const double* __restrict__ stats, const TM* __restrict__ mom,
     float* __restrict__ out, int S, double lambda) {
     using MB = MomBlocks<D>;
-    constexpr int LDA = D + 1;
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    double* A = reinterpret_cast<double*>(lds);      // [D][D+1]
-    double* z = A + D * LDA;                         // kbar - q, then y
-    double* dg = z + D;                              // pivots (0 where dropped)
-    double* kbd = dg + D;
-    double* red = kbd + D;                           // [DC_THREADS]
-    __shared__ double hM, hOm, hthr;
+    constexpr int TS = D / 16, E = MB::NT * 256 + D;
+    __shared__ double sh[DC_THREADS];
+    __shared__ double kbd[D];
+    __shared__ double colb[2][D];
+    __shared__ double zb[2];
+    __shared__ double dg[D];
+    __shared__ double ys[D];
     const int tid = threadIdx.x, bh = static_cast<int>(blockIdx.x);
-    {
-        double M, om;
-        head_stats<D>(stats + static_cast<int64_t>(bh) * S * (2 + D), S, &M, &om, kbd, tid, DC_THREADS);
-        if (tid == 0) {
-            hM = M;
-            hOm = om;
-        }
-    }
-    __syncthreads();
-    const double ridge = lambda * exp2(-hM);
-    const TA* mh = mom + static_cast<int64_t>(bh) * S * (MB::NT * 256 + D);
-    for (int e = tid; e < MB::NKK * 256; e += DC_THREADS) {
-        const int b = e >> 8, rc = e & 255, row = rc >> 4, col = rc & 15;
-        int I = 0, rem = b;
-        while (rem >= MB::NB - I) { rem -= MB::NB - I; ++I; }
-        const int J = I + rem;
-        double t = 0.0;
-        for (int s = 0; s < S; ++s) t += static_cast<double>(mh[static_cast<int64_t>(s) * (MB::NT * 256 + D) + e]);
-        const int i = 16 * I + row, j = 16 * J + col;
-        if (i == j) t += ridge;
-        A[i * LDA + j] = t;
-        A[j * LDA + i] = t;
-    }
-    if (tid < D) z[tid] = kbd[tid] - static_cast<double>(load_elem_d(q, static_cast<int64_t>(bh) * D + tid));
-    __syncthreads();
-    // lambda > 0: drop only pivots that rounding made non-positive; lambda = 0: also those
-    // below 1e-12 of the largest diagonal entry (directions the cache leaves undetermined).
+    const int ti = tid >> 4, tj = tid & 15;
+    double M, om;
+    head_stats<D>(stats + static_cast<int64_t>(bh) * S * (2 + D), S, sh, kbd, &M, &om);
+    const double ridge = lambda * exp2(-M);
+    const TM* mh = mom + static_cast<int64_t>(bh) * E;
+    double a[TS][TS];
     double dmax = 0.0;
-    for (int i = tid; i < D; i += DC_THREADS) dmax = fmax(dmax, A[i * LDA + i]);
-    red[tid] = dmax;
-    __syncthreads();
-    if (tid == 0) {
-        double mx = 0.0;
-        for (int i = 0; i < DC_THREADS; ++i) mx = fmax(mx, red[i]);
-        hthr = lambda > 0.0 ? 0.0 : 1e-12 * mx;
-    }
-    __syncthreads();
-    const double thr = hthr;
-    for (int kk = 0; kk < D; ++kk) {
-        const double piv = A[kk * LDA + kk];
-        const bool keep = piv > thr;
-        if (keep) {   // thread per row i of the trailing lower triangle; column kk is only read
-            const double ip = 1.0 / piv;
-            for (int i = kk + 1 + tid; i < D; i += DC_THREADS) {
-                const double li = A[i * LDA + kk] * ip;
-                for (int j = kk + 1; j <= i; ++j) A[i * LDA + j] -= li * A[j * LDA + kk];
-            }
+#pragma unroll
+    for (int ia = 0; ia < TS; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < TS; ++ib) {
+            const int i = ti * TS + ia, j = tj * TS + ib;
+            a[ia][ib] = static_cast<double>(mh[i <= j ? kk_index<D>(i, j) : kk_index<D>(j, i)]) + (i == j ? ridge : 0.0);
+            if (i == j) dmax = fmax(dmax, a[ia][ib]);
         }
-        __syncthreads();
-        for (int i = kk + 1 + tid; i < D; i += DC_THREADS) A[i * LDA + kk] = keep ? A[i * LDA + kk] * (1.0 / piv) : 0.0;
-        if (tid == 0) dg[kk] = keep ? piv : 0.0;
-        __syncthreads();
+    const double thr = lambda > 0.0 ? 0.0 : 1e-12 * block_reduce_d(dmax, true, sh);
+    double z = tid < D ? kbd[tid] - load_elem_d(q, static_cast<int64_t>(bh) * D + tid) : 0.0;
+    for (int pb = 0; pb < 16; ++pb) {
+#pragma unroll
+        for (int pp = 0; pp < TS; ++pp) {
+            const int p = pb * TS + pp;
+            double* cb = colb[p & 1];
+            if (tj == pb) {
+#pragma unroll
+                for (int ia = 0; ia < TS; ++ia) cb[ti * TS + ia] = a[ia][pp];
+            }
+            if (tid == p) zb[p & 1] = z;
+            __syncthreads();
+            const double piv = cb[p];
+            if (piv > thr) {
+                const double f = 1.0 / piv;
+                double rp[TS];
+#pragma unroll
+                for (int ib = 0; ib < TS; ++ib) rp[ib] = tj * TS + ib > p ? cb[tj * TS + ib] : 0.0;
+#pragma unroll
+                for (int ia = 0; ia < TS; ++ia) {
+                    const int i = ti * TS + ia;
+                    const double cr = i == p ? 0.0 : cb[i] * f;
+#pragma unroll
+                    for (int ib = 0; ib < TS; ++ib) a[ia][ib] = fma(-cr, rp[ib], a[ia][ib]);
+                }
+                if (tid < D && tid != p) z = fma(-cb[tid] * f, zb[p & 1], z);
+            }
+            if (tid == 0) dg[p] = piv > thr ? piv : 0.0;
+        }
     }
-    // L D L^T y = z: forward (unit lower), diagonal, backward
-    for (int kk = 0; kk < D; ++kk) {
-        const double yk = z[kk];
-        for (int i = kk + 1 + tid; i < D; i += DC_THREADS) z[i] -= A[i * LDA + kk] * yk;
-        __syncthreads();
-    }
-    for (int i = tid; i < D; i += DC_THREADS) z[i] = dg[i] > 0.0 ? z[i] / dg[i] : 0.0;
     __syncthreads();
-    for (int kk = D - 1; kk >= 0; --kk) {
-        const double yk = z[kk];
-        for (int i = tid; i < kk; i += DC_THREADS) z[i] -= A[kk * LDA + i] * yk;
-        __syncthreads();
-    }
+    if (tid < D) ys[tid] = dg[tid] > 0.0 ? z / dg[tid] : 0.0;
+    __syncthreads();
     // b_f = S_v,f / omega - sum_g C_vk[f][g] y_g; thread (slice sl, feature f)
     constexpr int SL = DC_THREADS / D;
     const int f = tid % D, sl = tid / D;
     double acc = 0.0;
     for (int gi = sl; gi < D; gi += SL) {
-        const int b = MB::NKK + (f >> 4) * MB::NB + (gi >> 4);
-        const int e = b * 256 + (f & 15) * 16 + (gi & 15);
-        double t = 0.0;
-        for (int s = 0; s < S; ++s) t += static_cast<double>(mh[static_cast<int64_t>(s) * (MB::NT * 256 + D) + e]);
-        acc += t * z[gi];
+        const int e = (MB::NKK + (f >> 4) * MB::NB + (gi >> 4)) * 256 + (f & 15) * 16 + (gi & 15);
+        acc = fma(static_cast<double>(mh[e]), ys[gi], acc);
     }
-    red[tid] = acc;
+    sh[tid] = acc;
     __syncthreads();
     if (tid < D) {
         double t = 0.0;
-        for (int l = 0; l < SL; ++l) t += red[l * D + tid];
-        double svf = 0.0;
-        for (int s = 0; s < S; ++s) svf += static_cast<double>(mh[static_cast<int64_t>(s) * (MB::NT * 256 + D) + MB::NT * 256 + tid]);
-        out[static_cast<int64_t>(bh) * D + tid] = static_cast<float>(svf / hOm - t);
+#pragma unroll
+        for (int l = 0; l < SL; ++l) t += sh[l * D + tid];
+        out[static_cast<int64_t>(bh) * D + tid] = static_cast<float>(static_cast<double>(mh[MB::NT * 256 + tid]) / om - t);
     }
 }
 
-template <int D, typename TA>
-constexpr int solve_smem_bytes() {
-    return (D * (D + 1) + 3 * D + DC_THREADS) * 8;
+// Workspace: chunk statistics, then the chunks' moments, then (several chunks per head) the
+// heads' summed moments; each region starts on a 256-byte boundary.
+struct LlaDecodeLayout {
+    int64_t stats_bytes, mom_bytes, sum_bytes;
+};
+LlaDecodeLayout lla_decode_layout(int64_t BH, int64_t L, int64_t d, int64_t ta_bytes) {
+    int S = 1, C = 1;
+    lla_decode_split(BH, L, &S, &C);
+    const int64_t nb = d / 16, e = (nb * (nb + 1) / 2 + nb * nb) * 256 + d;
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    return {up(BH * S * (2 + d) * 8), up(BH * S * e * ta_bytes), S > 1 ? BH * e * 8 : 0};
 }
 
 template <typename TIn, int D, typename TA>
 hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
     using MB = MomBlocks<D>;
+    constexpr int E = MB::NT * 256 + D;
     const int64_t BH = p.B * p.H;
     int S = 1, C = 1;
     lla_decode_split(BH, p.n, &S, &C);
     const float sl2 = static_cast<float>(DC_LOG2E / p.h);
-    double* stats = static_cast<double*>(workspace);
-    TA* mom = reinterpret_cast<TA*>(reinterpret_cast<unsigned char*>(workspace) +
-                                    ((BH * S * (2 + D) * 8 + 255) & ~int64_t(255)));
-    static_assert(mom_smem_bytes<D, TA>() <= 160 * 1024 && solve_smem_bytes<D, TA>() <= 160 * 1024, "LDS");
+    const LlaDecodeLayout lay = lla_decode_layout(BH, p.n, D, sizeof(TA));
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    double* stats = reinterpret_cast<double*>(ws);
+    TA* mom = reinterpret_cast<TA*>(ws + lay.stats_bytes);
+    double* msum = reinterpret_cast<double*>(ws + lay.stats_bytes + lay.mom_bytes);
+    static_assert(mom_smem_bytes<D, TA>() <= 150 * 1024, "LDS");
     static const hipError_t attr_err = [] {   // once per instantiation
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_solve_kernel<TIn, D, TA>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, solve_smem_bytes<D, TA>());
-        return e;
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
     }();
     hipError_t err = attr_err;
     if (err != hipSuccess) return err;
@@ -724,11 +765,22 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
         static_cast<int>(p.n), S, C, sl2);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    prof_begin(p.stream, "lla_decode_solve_kernel");
-    lla_decode_solve_kernel<TIn, D, TA><<<dim3(static_cast<unsigned>(BH)), dim3(DC_THREADS), solve_smem_bytes<D, TA>(),
-                                          p.stream>>>(static_cast<const TIn*>(p.q), stats, mom, p.out, S, p.lambda);
+    if (S > 1) {
+        const int bph = (E + DC_THREADS - 1) / DC_THREADS;
+        prof_begin(p.stream, "lla_decode_reduce_kernel");
+        lla_decode_reduce_kernel<TA><<<dim3(static_cast<unsigned>(BH * bph)), dim3(DC_THREADS), 0, p.stream>>>(
+            mom, msum, S, E, bph);
+        prof_end(p.stream);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        prof_begin(p.stream, "lla_decode_solve_kernel");
+        lla_decode_solve_kernel<TIn, D, double><<<dim3(static_cast<unsigned>(BH)), dim3(DC_THREADS), 0, p.stream>>>(
+            static_cast<const TIn*>(p.q), stats, msum, p.out, S, p.lambda);
+    } else {
+        prof_begin(p.stream, "lla_decode_solve_kernel");
+        lla_decode_solve_kernel<TIn, D, TA><<<dim3(static_cast<unsigned>(BH)), dim3(DC_THREADS), 0, p.stream>>>(
+            static_cast<const TIn*>(p.q), stats, mom, p.out, S, p.lambda);
+    }
     prof_end(p.stream);
-    (void)MB::NT;
     return hipGetLastError();
 }
 
@@ -752,11 +804,8 @@ hipError_t launch_lla_decode_d(const Problem& p, void* workspace) {
 }  // namespace
 
 size_t lla_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int dtype) {
-    int S = 1, C = 1;
-    lla_decode_split(B * H, L, &S, &C);
-    const int64_t nb = d / 16, nt = nb * (nb + 1) / 2 + nb * nb;
-    const int64_t ta = lla_decode_fp64(dtype, L, d) ? 8 : 4;
-    return static_cast<size_t>(((B * H * S * (2 + d) * 8 + 255) & ~int64_t(255)) + B * H * S * (nt * 256 + d) * ta);
+    const LlaDecodeLayout lay = lla_decode_layout(B * H, L, d, lla_decode_fp64(dtype, L, d) ? 8 : 4);
+    return static_cast<size_t>(lay.stats_bytes + lay.mom_bytes + lay.sum_bytes);
 }
 
 hipError_t launch_lla_decode(const Problem& p, void* workspace) {

@@ -305,13 +305,16 @@ def lla_decode_split(BH, L):
 def test_lla_decode_workspace_size():
     from local_linear_attention_amd import lla
     for B, H, L, d, dt in ((8, 16, 8192, 64, "bf16"), (1, 1, 100, 64, "bf16"), (2, 3, 700, 16, "f32"),
-                           (1, 2, 5000, 128, "bf16"), (4, 4, 1000, 32, "f32")):
+                           (1, 2, 5000, 128, "bf16"), (4, 4, 1000, 32, "f32"), (64, 16, 1024, 64, "bf16")):
         S = lla_decode_split(B * H, L)
         nb = d // 16
         nt = nb * (nb + 1) // 2 + nb * nb
         ta = 8 if (dt == "f32" or L < 2 * d) else 4
+        e = nt * 256 + d
         stats = -(-(B * H * S * (2 + d) * 8) // 256) * 256
-        assert lla.lla_decode_workspace_size(B, H, L, d, dt) == stats + B * H * S * (nt * 256 + d) * ta, (B, H, L, d)
+        mom = -(-(B * H * S * e * ta) // 256) * 256
+        summed = B * H * e * 8 if S > 1 else 0
+        assert lla.lla_decode_workspace_size(B, H, L, d, dt) == stats + mom + summed, (B, H, L, d)
     assert lla.lla_decode_workspace_size(1, 1, 100, 48, "bf16") == 0
 
 

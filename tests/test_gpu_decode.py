@@ -163,7 +163,9 @@ LLA_SMALL = [
     {"B": 2, "H": 3, "L": 900, "dtype": "f32"},
     {"B": 1, "H": 2, "L": 40, "dtype": "f32"},
     {"B": 1, "H": 2, "L": 600, "d": 128, "dtype": "f32", "h": 11.3},
-    {"B": 300, "H": 4, "L": 200},
+    {"B": 300, "H": 4, "L": 200},             # one chunk per head: the solve reads the chunk's moments
+    {"B": 64, "H": 16, "L": 1024},            # one chunk per head, fp32 moments
+    {"B": 1, "H": 1, "L": 40000},             # 79 chunks summed by the reduce launch
 ]
 
 
@@ -208,7 +210,8 @@ def test_lla_decode_workload_and_forward_last_row():
     b = lla_decode(tq, tk, tv, w.h, w.lam)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    assert [n for n, _ in rec] == ["lla_decode_stats_kernel", "lla_decode_moments_kernel", "lla_decode_solve_kernel"]
+    assert [n for n, _ in rec] == ["lla_decode_stats_kernel", "lla_decode_moments_kernel", "lla_decode_reduce_kernel",
+                                   "lla_decode_solve_kernel"]
     check_lla(a.cpu().numpy().astype(np.float64), ref, "bf16", "lla_decode_b8_l8192")
     # the LLA forward's last row over the same positions (matrix-core path) agrees
     w2, q2, k2, v2, _ = arrays("lla_decode_b8_l8192", B=1, H=2, L=700)
