@@ -168,6 +168,64 @@ lla_status_t lla_parallax_forward_ws(const void* q, const void* k, const void* v
 int lla_parallax_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d);
 
 /*
+ * Parallax forward that also writes the per-row log-sum-exp its backward reads (the cached
+ * row statistics of the "Parallax" blog post, Appendix F, "Parallax backward"):
+ *
+ *   lse [B, H, n] fp32:  lse_i = log2 sum_{j <= i} 2^(x_ij),  x_ij = q_i . k_j log2(e) / h,
+ *   so that p_ij = 2^(x_ij - lse_i).
+ *
+ * Arguments as for lla_parallax_forward_ex plus `lse` (device, not overlapping any other
+ * argument) and an optional caller workspace: with workspace NULL the scratch comes from the
+ * library pool; otherwise it must hold lla_parallax_workspace_size(...) bytes
+ * (LLA_ERR_WORKSPACE if short) and nothing is allocated.  The forward's kernels run (the
+ * fast one with an epilogue that also writes lse), so out is identical to
+ * lla_parallax_forward_ex's.
+ */
+lla_status_t lla_parallax_forward_stats(const void* q, const void* k, const void* v, const void* rho,
+                                        float* out, float* lse,
+                                        int64_t B, int64_t H, int64_t n, int64_t d, double h,
+                                        lla_dtype_t dtype, void* stream, lla_path_t path,
+                                        void* workspace, size_t workspace_bytes);
+
+/*
+ * Parallax backward: the gradients of sum(o * dout) with respect to q, k, v and rho for
+ * the forward above (the row-tile and column-tile passes of the "Parallax" blog post,
+ * Appendix F, "Parallax backward"; the page's formulas are stripped, so the closed form is
+ * derived from the scoring form o_i = sum_j a_ij v_j, a_ij = p_ij (1 - u_ij + ubar_i),
+ * u_ij = rho_i . k_j, ubar_i = sum_j p_ij u_ij):
+ *
+ *   g_ij = dout_i . v_j,  G_i = sum_j p_ij g_ij,  D_i = G_i (1 + 2 ubar_i) - sum_j p_ij g_ij u_ij,
+ *   ds_ij = p_ij (g_ij (1 - u_ij + ubar_i) + u_ij G_i - D_i),  du_ij = p_ij (G_i - g_ij),
+ *   dq_i = sum_j ds_ij k_j / h,  drho_i = sum_j du_ij k_j,
+ *   dk_j = sum_{i >= j} (ds_ij q_i / h + du_ij rho_i),  dv_j = sum_{i >= j} a_ij dout_i.
+ *
+ * q, k, v, rho: the forward's inputs; dout [B, H, n, d] in their dtype; lse: what
+ * lla_parallax_forward_stats wrote for them (a shift: the fast path renormalises the
+ * weights itself); dq, dk, dv, drho [B, H, n, d] fp32 outputs (fully written; none may
+ * overlap another argument).  Paths: FAST (bf16, d = 64, n up to 4194304): four launches on
+ * the matrix cores -- tile packing; a sweep over each row's keys for Z, ubar, G and D with
+ * the same products as the passes (so that sum_j ds_ij vanishes to rounding); a column pass
+ * for dk and dv; a row pass for dq and drho -- with the pair weights as bf16 hi + lo parts;
+ * EXACT (every supported dtype and d): fp64, recomputes every row statistic and does not
+ * read lse (it must still be a valid pointer); AUTO takes FAST where it applies.  Workspace
+ * as for lla_parallax_forward_stats (size from lla_parallax_backward_workspace_size).
+ * Validation happens before any launch; errors as for the forward entry points.
+ */
+lla_status_t lla_parallax_backward(const void* q, const void* k, const void* v, const void* rho,
+                                   const void* dout, const float* lse,
+                                   float* dq, float* dk, float* dv, float* drho,
+                                   int64_t B, int64_t H, int64_t n, int64_t d, double h,
+                                   lla_dtype_t dtype, void* stream, lla_path_t path,
+                                   void* workspace, size_t workspace_bytes);
+
+/* Bytes of device scratch lla_parallax_backward needs on `path` (0 if invalid).  FAST: per
+ * head and 64-position tile, a query image of 55296 bytes (q, rho, dout as bf16 rows of 72
+ * halves and feature-major rows of 68 halves, and four floats per row) and a key image of
+ * 27648 bytes (k, v rows and k feature-major); EXACT: four doubles per row. */
+size_t lla_parallax_backward_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
+                                            lla_path_t path);
+
+/*
  * LLA decode step: one query per (batch, head) against a key-value cache, every cached
  * position in its prefix (the LLA estimator of the "Parallax" blog post, section 2
  * "Canonical Formulation", for the newest position; centred form of its Appendix E):

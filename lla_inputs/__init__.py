@@ -57,8 +57,8 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_probe", "round_to_bf16", "generate",
-           "generate_probe", "DecodeWorkload", "DECODE_WORKLOADS", "generate_decode"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_probe", "make_cotangent", "round_to_bf16", "generate",
+           "generate_probe", "generate_cotangent", "DecodeWorkload", "DECODE_WORKLOADS", "generate_decode"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -177,6 +177,19 @@ def generate_probe(w: Workload):
     the fp64 pre-cast array: ``(rho, rho64)``."""
     rho64 = make_probe(w.B, w.H, w.n, w.d, w.seed)
     return cast(rho64, w.dtype), rho64
+
+
+def make_cotangent(B: int, H: int, n: int, d: int, seed: int) -> np.ndarray:
+    """Draw the fp64 (pre-cast) output cotangent dout ``[B,H,n,d]`` for backward tests and
+    benchmarks: standard normal from the stream ``default_rng([seed, 2])``."""
+    return np.random.default_rng([seed, 2]).standard_normal((B, H, n, d))
+
+
+def generate_cotangent(w: Workload):
+    """The cotangent of workload ``w`` as float32 holding the cast values, plus the fp64
+    pre-cast array: ``(dout, dout64)``."""
+    d64 = make_cotangent(w.B, w.H, w.n, w.d, w.seed)
+    return cast(d64, w.dtype), d64
 
 
 @dataclasses.dataclass(frozen=True)

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 
 bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -130,6 +130,15 @@ lla_status_t validate_parallax(const void* q, const void* k, const void* v, cons
     return LLA_OK;
 }
 
+bool resolve_parallax_bwd_fast(lla_path_t path, int dtype, int64_t d, int64_t n, bool* fast) {
+    switch (path) {
+        case LLA_PATH_EXACT: *fast = false; return true;
+        case LLA_PATH_FAST: *fast = true; return lla::parallax_bwd_fast_supports(dtype, d, n);
+        case LLA_PATH_AUTO: *fast = lla::parallax_bwd_fast_supports(dtype, d, n); return true;
+    }
+    return false;
+}
+
 bool resolve_parallax_fast(lla_path_t path, int dtype, int64_t d, int64_t n, bool* fast) {
     switch (path) {
         case LLA_PATH_EXACT: *fast = false; return true;
@@ -197,6 +206,60 @@ lla_status_t parallax_entry(const void* q, const void* k, const void* v, const v
     const lla::Problem p{q, k, v, out, B, H, n, d, h, 0.0, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream), rho};
     return run_parallax(p, fast, ws, ws_bytes, may_allocate);
+}
+
+lla_status_t parallax_stats_entry(const void* q, const void* k, const void* v, const void* rho, float* out,
+                                  float* stats, int64_t B, int64_t H, int64_t n, int64_t d, double h,
+                                  lla_dtype_t dtype, void* stream, lla_path_t path, void* ws, size_t ws_bytes) {
+    if (!stats) return LLA_ERR_NULL;
+    const lla_status_t st = validate_parallax(q, k, v, rho, out, B, H, n, d, h, dtype);
+    if (st != LLA_OK) return st;
+    const int64_t rows = B * H * n;
+    const int64_t elt = dtype == LLA_DTYPE_F32 ? 4 : 2;
+    const int64_t sb = rows * 4;
+    if (overlaps(stats, sb, q, rows * d * elt) || overlaps(stats, sb, k, rows * d * elt) ||
+        overlaps(stats, sb, v, rows * d * elt) || overlaps(stats, sb, rho, rows * d * elt) ||
+        overlaps(stats, sb, out, rows * d * 4))
+        return LLA_ERR_ALIAS;
+    bool fast = false;
+    if (!resolve_parallax_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
+    lla::Problem p{q, k, v, out, B, H, n, d, h, 0.0, static_cast<int>(dtype), static_cast<hipStream_t>(stream), rho};
+    p.stats = stats;
+    return run_parallax(p, fast, ws, ws_bytes, ws == nullptr);
+}
+
+lla_status_t parallax_bwd_entry(const void* q, const void* k, const void* v, const void* rho, const void* dout,
+                                const float* lse, float* dq, float* dk, float* dv, float* drho, int64_t B,
+                                int64_t H, int64_t n, int64_t d, double h, lla_dtype_t dtype, void* stream,
+                                lla_path_t path, void* ws, size_t ws_bytes) {
+    if (!q || !k || !v || !rho || !dout || !lse || !dq || !dk || !dv || !drho) return LLA_ERR_NULL;
+    if (B < 1 || H < 1 || n < 1) return LLA_ERR_SHAPE;
+    if (!isfinite(h) || !(h > 0.0)) return LLA_ERR_PARAM;
+    if (!supported_shape(d, dtype)) return LLA_ERR_UNSUPPORTED;
+    lla_status_t st = validate_sizes(B, H, n, d);
+    if (st != LLA_OK) return st;
+    const int64_t rows = B * H * n;
+    const int64_t elt = dtype == LLA_DTYPE_F32 ? 4 : 2;
+    const int64_t ib = rows * d * elt, gb = rows * d * 4;
+    const void* ins[6] = {q, k, v, rho, dout, lse};
+    const int64_t in_bytes[6] = {ib, ib, ib, ib, ib, rows * 4};
+    const float* outs[4] = {dq, dk, dv, drho};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], gb, ins[b], in_bytes[b])) return LLA_ERR_ALIAS;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], gb, outs[b], gb)) return LLA_ERR_ALIAS;
+    }
+    bool fast = false;
+    if (!resolve_parallax_bwd_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
+    lla::Problem p{q, k, v, nullptr, B, H, n, d, h, 0.0, static_cast<int>(dtype), static_cast<hipStream_t>(stream),
+                   rho};
+    p.stats = const_cast<float*>(lse);
+    const lla::BwdProblem b{p, dout, dq, dk, dv, drho};
+    return run_scratch(lla::parallax_bwd_workspace_bytes(B, H, n, d, fast), p.stream, ws, ws_bytes, ws == nullptr,
+                       [&](void* w) {
+                           return fast ? lla::launch_parallax_bwd_fast(b, w) : lla::launch_parallax_bwd_exact(b, w);
+                       });
 }
 
 // ---- kernel-level timing
@@ -335,6 +398,30 @@ size_t lla_parallax_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, l
     bool fast = false;
     if (!resolve_parallax_fast(path, static_cast<int>(dtype), d, n, &fast) || !fast) return 0;
     return lla::parallax_workspace_bytes(B, H, n, d);
+}
+
+lla_status_t lla_parallax_forward_stats(const void* q, const void* k, const void* v, const void* rho, float* out,
+                                        float* stats, int64_t B, int64_t H, int64_t n, int64_t d, double h,
+                                        lla_dtype_t dtype, void* stream, lla_path_t path, void* workspace,
+                                        size_t workspace_bytes) {
+    return parallax_stats_entry(q, k, v, rho, out, stats, B, H, n, d, h, dtype, stream, path, workspace,
+                                workspace_bytes);
+}
+
+lla_status_t lla_parallax_backward(const void* q, const void* k, const void* v, const void* rho, const void* dout,
+                                   const float* lse, float* dq, float* dk, float* dv, float* drho, int64_t B,
+                                   int64_t H, int64_t n, int64_t d, double h, lla_dtype_t dtype, void* stream,
+                                   lla_path_t path, void* workspace, size_t workspace_bytes) {
+    return parallax_bwd_entry(q, k, v, rho, dout, lse, dq, dk, dv, drho, B, H, n, d, h, dtype, stream, path,
+                              workspace, workspace_bytes);
+}
+
+size_t lla_parallax_backward_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
+                                            lla_path_t path) {
+    if (B < 1 || H < 1 || n < 1 || !supported_shape(d, dtype) || validate_sizes(B, H, n, d) != LLA_OK) return 0;
+    bool fast = false;
+    if (!resolve_parallax_bwd_fast(path, static_cast<int>(dtype), d, n, &fast)) return 0;
+    return lla::parallax_bwd_workspace_bytes(B, H, n, d, fast);
 }
 
 int lla_parallax_path_available(lla_path_t path, lla_dtype_t dtype, int64_t d) {

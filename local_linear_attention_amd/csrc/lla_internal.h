@@ -17,6 +17,15 @@ struct Problem {
     int dtype;            // 0 = f32, 1 = bf16
     hipStream_t stream;
     const void* rho;      // Parallax probe [B, H, n, d] (Parallax entry points only)
+    float* stats = nullptr;   // Parallax forward: per-row base-2 log-sum-exp [B, H, n], or null
+};
+
+// Parallax backward: gradients of sum(o * dout) for the forward of `p` (q, k, v, rho as in
+// the forward; stats = the log-sum-exp the forward with statistics wrote; out unused).
+struct BwdProblem {
+    Problem p;
+    const void* dout;     // [B, H, n, d], the input dtype
+    float *dq, *dk, *dv, *drho;   // [B, H, n, d] fp32
 };
 
 // fp64-accumulating path: every (dtype, d) the library accepts.  Processes rows
@@ -38,6 +47,15 @@ bool parallax_fast_supports(int dtype, int64_t d, int64_t n);
 size_t parallax_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
 hipError_t launch_parallax_fast(const Problem& p, void* workspace);
 hipError_t launch_parallax_exact(const Problem& p);
+
+// Parallax backward (gradients of sum(out * dout) for the forward with a given probe).
+// Fast path: bf16, d = 64, n up to kFastMaxN; reads the forward's log-sum-exp
+// (Problem::stats) and keeps tile images in `workspace`.  Exact path: fp64, every (dtype, d),
+// recomputes the row statistics itself (per-row fp64 values in `workspace`).
+bool parallax_bwd_fast_supports(int dtype, int64_t d, int64_t n);
+size_t parallax_bwd_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, bool fast);
+hipError_t launch_parallax_bwd_fast(const BwdProblem& b, void* workspace);
+hipError_t launch_parallax_bwd_exact(const BwdProblem& b, void* workspace);
 
 // Parallax decode with a given probe: q, rho [B, H, d] against a cache k, v [B, H, L, d]
 // (L in Problem::n).  Every (dtype, d) the library accepts; the per-chunk partial sums go

@@ -140,10 +140,11 @@ __global__ __launch_bounds__(256) void lla_parallax_pack_kernel(const uint16_t* 
 //   P1 = fp16(2^(s1 log2e/h - m)), P2 = fp16(P1 (s2 - rho.a) sigma);
 //   O^T += V^T P^T (fp16 MFMA, V the A operand), so that lane (g, c) register r of O holds
 //   feature 16 fv + 4g + r of query c -- the same query as the lane's row statistics.
+template <bool kStats>   // kStats: also write the per-row statistics the backward reads
 __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const unsigned char* __restrict__ img,
-    const float* __restrict__ ksum, const float* __restrict__ kmax, float* __restrict__ out, int n, int BH,
-    float sl2) {
+    const float* __restrict__ ksum, const float* __restrict__ kmax, float* __restrict__ out,
+    float* __restrict__ stats, int n, int BH, float sl2) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[X_NBUF * X_TILE];
     __shared__ float akm[FD];
     __shared__ float kbound;
@@ -414,6 +415,9 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
                 }
                 *reinterpret_cast<float4v*>(orow + 16 * fv + 4 * g) = res;
             }
+            if constexpr (kStats) {   // the row's log-sum-exp of the scores, base 2
+                if (g == 0) stats[static_cast<int64_t>(bh) * n + i] = mrow[st] + log2f(d1);
+            }
         }
     }
 }
@@ -434,7 +438,7 @@ constexpr int G_CHK = 256;
 template <typename TIn, int D>
 __global__ __launch_bounds__(G_NT) void lla_parallax_exact_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, const TIn* __restrict__ rho,
-    float* __restrict__ out, int n, int BH, double inv_h) {
+    float* __restrict__ out, float* __restrict__ stats, int n, int BH, double inv_h) {
     constexpr int KL = G_NT / D;   // key lanes of the per-feature sums
     __shared__ double qs[D], rs[D], kbar[D], vbar[D];
     __shared__ double ws[G_CHK];
@@ -527,6 +531,8 @@ __global__ __launch_bounds__(G_NT) void lla_parallax_exact_kernel(
         for (int l = 0; l < KL; ++l) s += red[l * D + tid];
         out[base + static_cast<int64_t>(i) * D + tid] = static_cast<float>(vbar[tid] - s / omega);
     }
+    if (stats != nullptr && tid == 0)   // the row's log-sum-exp of the scores, base 2
+        stats[static_cast<int64_t>(bh) * n + i] = static_cast<float>((m + log(omega)) * 1.4426950408889634);
 }
 
 template <typename TIn, int D>
@@ -536,7 +542,7 @@ hipError_t launch_parallax_exact_t(const Problem& p) {
     prof_begin(p.stream, "lla_parallax_exact_kernel");
     lla_parallax_exact_kernel<TIn, D><<<dim3(blocks), dim3(G_NT), 0, p.stream>>>(
         static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v),
-        static_cast<const TIn*>(p.rho), p.out, static_cast<int>(p.n), BH, 1.0 / p.h);
+        static_cast<const TIn*>(p.rho), p.out, p.stats, static_cast<int>(p.n), BH, 1.0 / p.h);
     prof_end(p.stream);
     return hipGetLastError();
 }
@@ -600,9 +606,14 @@ hipError_t launch_parallax_fast(const Problem& p, void* workspace) {
     if (err != hipSuccess) return err;
     const unsigned blocks = static_cast<unsigned>(BH) * ((n + X_QB - 1) / X_QB);
     prof_begin(p.stream, "lla_parallax_kernel");
-    lla_parallax_kernel<<<dim3(blocks), dim3(X_WAVES * 64), 0, p.stream>>>(
-        static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.rho), img, ksum, kmax, p.out, n, BH,
-        static_cast<float>(LOG2E / p.h));
+    if (p.stats != nullptr)
+        lla_parallax_kernel<true><<<dim3(blocks), dim3(X_WAVES * 64), 0, p.stream>>>(
+            static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.rho), img, ksum, kmax, p.out, p.stats,
+            n, BH, static_cast<float>(LOG2E / p.h));
+    else
+        lla_parallax_kernel<false><<<dim3(blocks), dim3(X_WAVES * 64), 0, p.stream>>>(
+            static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.rho), img, ksum, kmax, p.out, nullptr,
+            n, BH, static_cast<float>(LOG2E / p.h));
     prof_end(p.stream);
     return hipGetLastError();
 }

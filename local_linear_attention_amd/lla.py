@@ -75,6 +75,14 @@ def load_library():
     lib.lla_parallax_forward_ws.restype = ctypes.c_int
     lib.lla_parallax_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.lla_parallax_workspace_size.restype = ctypes.c_size_t
+    lib.lla_parallax_forward_stats.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f64, ctypes.c_int, vp,
+                                               ctypes.c_int, vp, ctypes.c_size_t]
+    lib.lla_parallax_forward_stats.restype = ctypes.c_int
+    lib.lla_parallax_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f64,
+                                          ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_size_t]
+    lib.lla_parallax_backward.restype = ctypes.c_int
+    lib.lla_parallax_backward_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.lla_parallax_backward_workspace_size.restype = ctypes.c_size_t
     lib.lla_parallax_path_available.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64]
     lib.lla_parallax_path_available.restype = ctypes.c_int
     lib.lla_parallax_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f64, ctypes.c_int, vp]
@@ -114,6 +122,17 @@ def lla_version() -> int:
 
 def _marshal(q, k, v, out):
     import torch
+    dtype = _marshal_inputs(q, k, v)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous float32 tensor of q's shape on q's device")
+    return dtype, out
+
+
+def _marshal_inputs(q, k, v):
+    import torch
     if not (q.shape == k.shape == v.shape) or q.dim() != 4:
         raise ValueError(f"q, k, v must share one [B, H, n, d] shape; got {tuple(q.shape)}, "
                          f"{tuple(k.shape)}, {tuple(v.shape)}")
@@ -128,12 +147,7 @@ def _marshal(q, k, v, out):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous() \
-            or out.device != q.device:
-        raise ValueError("out must be a contiguous float32 tensor of q's shape on q's device")
-    return dtype, out
+    return dtype
 
 
 def lla_forward_ex(q, k, v, h: float, lam: float, path: str = "auto", out=None, stream=None):
@@ -238,6 +252,75 @@ def lla_parallax_workspace_size(B: int, H: int, n: int, d: int, dtype: str, path
 def lla_parallax_path_available(path: str, dtype: str, d: int) -> bool:
     """Whether Parallax kernel path "auto" / "exact" / "fast" covers (dtype, d)."""
     return bool(load_library().lla_parallax_path_available(PATHS[path], DTYPES[dtype], int(d)))
+
+
+def _device_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t.data_ptr()
+
+
+def lla_parallax_forward_stats(q, k, v, rho, h: float, path: str = "auto", out=None, lse=None, stream=None,
+                               workspace=None):
+    """Parallax forward that also writes the per-row base-2 log-sum-exp of the scores the
+    backward reads: returns (out [B, H, n, d] fp32, lse [B, H, n] fp32).  ``workspace``:
+    None (library pool) or a device tensor of at least lla_parallax_workspace_size bytes."""
+    import torch
+    dtype, out = _marshal(q, k, v, out)
+    _marshal_probe(q, rho)
+    B, H, n, d = q.shape
+    if lse is None:
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    elif tuple(lse.shape) != (B, H, n) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, n]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    wp = _device_ptr(workspace, "workspace")
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().lla_parallax_forward_stats(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), rho.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, n, d,
+        float(h), dtype, ctypes.c_void_p(stream.cuda_stream), PATHS[path], wp, wb)
+    if st != 0:
+        raise LLAError(st, "lla_parallax_forward_stats")
+    return out, lse
+
+
+def lla_parallax_backward(q, k, v, rho, dout, lse, h: float, path: str = "auto", grads=None, stream=None,
+                          workspace=None):
+    """Gradients (dq, dk, dv, drho), fp32 [B, H, n, d], of sum(o * dout) for the Parallax
+    forward of q, k, v, rho whose log-sum-exp lla_parallax_forward_stats wrote; dout in the
+    inputs' dtype.  ``grads``: optional four preallocated fp32 tensors.  ``workspace``: None
+    (library pool) or a device tensor of at least lla_parallax_backward_workspace_size bytes."""
+    import torch
+    dtype = _marshal_inputs(q, k, v)
+    _marshal_probe(q, rho)
+    _marshal_probe(q, dout)
+    B, H, n, d = q.shape
+    if tuple(lse.shape) != (B, H, n) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, n]")
+    if grads is None:
+        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(4))
+    for gname, gt in zip(("dq", "dk", "dv", "drho"), grads):
+        if gt.shape != q.shape or gt.dtype != torch.float32:
+            raise ValueError(f"{gname} must be float32 of q's shape")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    wp = _device_ptr(workspace, "workspace")
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ptrs = [_device_ptr(t, nm) for t, nm in ((lse, "lse"),) + tuple(zip(grads, ("dq", "dk", "dv", "drho")))]
+    st = load_library().lla_parallax_backward(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), rho.data_ptr(), dout.data_ptr(), *ptrs, B, H, n, d, float(h),
+        dtype, ctypes.c_void_p(stream.cuda_stream), PATHS[path], wp, wb)
+    if st != 0:
+        raise LLAError(st, "lla_parallax_backward")
+    return grads
+
+
+def lla_parallax_backward_workspace_size(B: int, H: int, n: int, d: int, dtype: str, path: str = "auto") -> int:
+    """Bytes of device scratch lla_parallax_backward needs on ``path``."""
+    return int(load_library().lla_parallax_backward_workspace_size(B, H, n, d, DTYPES[dtype], PATHS[path]))
 
 
 def lla_parallax_forward_ws(q, k, v, rho, h: float, workspace, path: str = "auto", out=None, stream=None):

@@ -33,9 +33,11 @@ def declared_enums():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["lla_decode", "lla_decode_workspace_size", "lla_decode_ws",
                                     "lla_forward", "lla_forward_ex", "lla_forward_ws",
+                                    "lla_parallax_backward", "lla_parallax_backward_workspace_size",
                                     "lla_parallax_decode", "lla_parallax_decode_workspace_size",
                                     "lla_parallax_decode_ws",
                                     "lla_parallax_forward", "lla_parallax_forward_ex",
+                                    "lla_parallax_forward_stats",
                                     "lla_parallax_forward_ws", "lla_parallax_path_available",
                                     "lla_parallax_workspace_size",
                                     "lla_path_available", "lla_profile_collect",
@@ -324,3 +326,65 @@ def test_lla_decode_ws_validation_before_launch():
             1, 2, 4096, 64, 8.0, 0.01, 1, None]
     assert lib.lla_decode_ws(*args, None, 0) == 5
     assert lib.lla_decode_ws(*args, ctypes.c_void_p(0x50000000), 64) == 5
+
+
+# ---- Parallax forward with statistics and backward: validation happens before any launch
+# (the fake addresses are never dereferenced).
+RHO, DOUT, STATS, DQ, DK, DV, DR = (0x50000000, 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000,
+                                    0xB0000000)
+
+
+def stats_call(lib, stats=STATS, out=OUT, q=Q, B=1, H=2, n=16, d=64, h=8.0, dtype=1, path=0, ws=None, wsb=0):
+    return lib.lla_parallax_forward_stats(ctypes.c_void_p(q), ctypes.c_void_p(K), ctypes.c_void_p(V),
+                                          ctypes.c_void_p(RHO), ctypes.c_void_p(out),
+                                          ctypes.c_void_p(stats) if stats else None, B, H, n, d, h, dtype, None,
+                                          path, ws, wsb)
+
+
+def bwd_call(lib, dq=DQ, dk=DK, dv=DV, dr=DR, dout=DOUT, stats=STATS, B=1, H=2, n=16, d=64, h=8.0, dtype=1,
+             path=0, ws=None, wsb=0):
+    p = [ctypes.c_void_p(x) if x else None for x in (Q, K, V, RHO, dout, stats, dq, dk, dv, dr)]
+    return lib.lla_parallax_backward(*p, B, H, n, d, h, dtype, None, path, ws, wsb)
+
+
+def test_parallax_forward_stats_validation():
+    lib = _lib()
+    assert stats_call(lib, stats=0) == 1
+    assert stats_call(lib, q=0) == 1
+    assert stats_call(lib, n=0) == 2
+    assert stats_call(lib, h=0.0) == 3
+    assert stats_call(lib, d=48) == 4
+    assert stats_call(lib, dtype=0, path=2) == 4            # FAST is bf16 only
+    assert stats_call(lib, stats=Q + 64) == 7               # stats overlaps q
+    assert stats_call(lib, stats=OUT + 1024) == 7           # lse overlaps out
+    # a caller workspace that is too small
+    assert stats_call(lib, n=4096, path=2, ws=ctypes.c_void_p(0xC0000000), wsb=64) == 5
+
+
+def test_parallax_backward_validation():
+    lib = _lib()
+    for kw in ({"dq": 0}, {"dk": 0}, {"dv": 0}, {"dr": 0}, {"dout": 0}, {"stats": 0}):
+        assert bwd_call(lib, **kw) == 1, kw
+    assert bwd_call(lib, B=0) == 2
+    assert bwd_call(lib, h=-1.0) == 3
+    assert bwd_call(lib, h=float("nan")) == 3
+    assert bwd_call(lib, d=96) == 4
+    assert bwd_call(lib, dtype=0, path=2) == 4
+    assert bwd_call(lib, d=32, path=2) == 4
+    assert bwd_call(lib, dq=DOUT + 8) == 7                  # gradient over an input
+    assert bwd_call(lib, dk=DQ + 16) == 7                   # two gradients overlap
+    assert bwd_call(lib, dr=STATS + 4) == 7                 # gradient over the log-sum-exp
+    assert bwd_call(lib, n=4096, path=2, ws=ctypes.c_void_p(0xC0000000), wsb=1024) == 5
+    assert bwd_call(lib, n=100, path=1, ws=ctypes.c_void_p(0xC0000000), wsb=8) == 5
+
+
+def test_parallax_backward_workspace_size():
+    from local_linear_attention_amd import lla
+    for B, H, n in ((2, 16, 4096), (1, 1, 1), (3, 2, 130)):
+        tiles = -(-n // 64)
+        assert lla.lla_parallax_backward_workspace_size(B, H, n, 64, "bf16", "fast") == B * H * tiles * (55296 + 27648)
+        assert lla.lla_parallax_backward_workspace_size(B, H, n, 64, "bf16", "auto") == B * H * tiles * (55296 + 27648)
+        assert lla.lla_parallax_backward_workspace_size(B, H, n, 64, "bf16", "exact") == B * H * n * 32
+        assert lla.lla_parallax_backward_workspace_size(B, H, n, 32, "f32", "auto") == B * H * n * 32
+    assert lla.lla_parallax_backward_workspace_size(1, 1, 10, 32, "bf16", "fast") == 0
+    assert lla.lla_parallax_backward_workspace_size(1, 1, 10, 48, "bf16", "auto") == 0

@@ -57,3 +57,16 @@ def test_decode_generator_is_deterministic_and_cast():
         assert np.array_equal(x, y) and x.shape == shp and x.dtype == np.float32
         assert np.array_equal(lla_inputs.round_to_bf16(x), x)
     assert np.allclose(np.mean(a[1].astype(np.float64) ** 2, -1), 1.0, atol=2e-2)
+
+
+def test_cotangent_stream_is_separate_and_deterministic():
+    w = lla_inputs.WORKLOADS["parallax_d12"].with_shape(B=1, H=2, n=50)
+    d1, d64 = lla_inputs.generate_cotangent(w)
+    d2, _ = lla_inputs.generate_cotangent(w)
+    assert np.array_equal(d1, d2)
+    assert np.array_equal(d1, lla_inputs.round_to_bf16(d64.astype(np.float32)))
+    q, k, v, _ = lla_inputs.generate(w)
+    rho, _ = lla_inputs.generate_probe(w)
+    for x in (q, k, v, rho):   # its own stream: no draw shared with the forward inputs
+        assert not np.allclose(d1, x)
+    assert abs(float(np.std(d64)) - 1.0) < 0.05
