@@ -7,11 +7,13 @@ lla_decode) over the whole workload with the inputs already resident in HBM.  Pr
 JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload d24] [--path auto]
-                    [--method lla|parallax|parallax_decode|lla_decode]
+                    [--method lla|parallax|parallax_bwd|parallax_decode|lla_decode]
 
 The default workload is B=2, H=16, n=4096, d=64 with bf16 inputs (head shape of a
 1024-wide, 16-head model), h = 8, lambda = 1e-2; with --method parallax the same q, k, v
-plus an RMS-normalised probe (workload parallax_d24).  The decode methods default to eight
+plus an RMS-normalised probe (workload parallax_d24); --method parallax_bwd times the Parallax
+backward (gradients of q, k, v, rho for a seeded output cotangent) on that workload, with the
+forward's log-sum-exp computed once beforehand.  The decode methods default to eight
 sequences of 16 heads with 8192 cached bf16 keys and values each.
 """
 from __future__ import annotations
@@ -71,6 +73,12 @@ KERNEL_BOUND = {
     "lla_parallax_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_parallax_decode_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_parallax_merge_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla_parallax_bwd_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla_parallax_bwd_stats_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_parallax_bwd_kv_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_parallax_bwd_qr_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla_parallax_bwd_exact_rows_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla_parallax_bwd_exact_cols_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_decode_stats_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_decode_moments_kernel": ("mfma", PEAK["mfma_f32_TFLOPs"]),
     "lla_decode_reduce_kernel": ("hbm", PEAK["hbm_GBps"]),
@@ -149,7 +157,8 @@ def kernel_source_hash(kernel):
     names = sorted(os.listdir(csrc))
     for name in names:
         path = os.path.join(csrc, name)
-        if name.endswith(".h") or (name.endswith(".hip") and f"void {kernel}(" in open(path).read()):
+        if name.endswith(".h") or (name.endswith(".hip") and (f"void {kernel}(" in open(path).read()
+                                                             or f'"{kernel}"' in open(path).read())):
             h.update(open(path, "rb").read())
     return h.hexdigest()[:16]
 
@@ -400,12 +409,166 @@ def bench_decode(args):
     print(json.dumps(result), flush=True)
 
 
+METRIC_PARALLAX_BWD = ("Parallax bwd (given probe) queries/s + TFLOP/s (% MFMA peak) at B2 H16 n4096 d64 bf16, "
+                       "1 GPU")
+
+
+def parallax_bwd_flops(B, H, n, d):
+    """Algorithmic flops of one Parallax backward: per causal pair the three products of the
+    pair (score q.k, probe score rho.k, g = dout.v: 2d each) and the five weighted sums that
+    use them (dv, the two terms of dk, dq, drho: 2d each) -- 16d -- plus about 16 flops of
+    pair weights; per row the statistics (4d).  Scores the kernels recompute are not counted
+    again, nor the second (lo) half of the split weights."""
+    P = B * H * n * (n + 1) // 2
+    return P * (16 * d + 16) + B * H * n * 4 * d
+
+
+def parallax_bwd_kernel_flops(name, B, H, n, d):
+    """Algorithmic flops of one launch of each backward kernel (its own products; the split
+    weights' second halves not counted)."""
+    P = B * H * n * (n + 1) // 2
+    if name == "lla_parallax_bwd_stats_kernel":
+        return P * (6 * d + 8)       # the three products and the four row sums
+    if name == "lla_parallax_bwd_kv_kernel":
+        return P * (12 * d + 12)     # the three products, a, ds, du; dv and dk
+    if name == "lla_parallax_bwd_qr_kernel":
+        return P * (10 * d + 10)     # the three products, ds, du; dq and drho
+    if name in ("lla_parallax_bwd_exact_rows_kernel", "lla_parallax_bwd_exact_cols_kernel"):
+        return parallax_bwd_flops(B, H, n, d) // 2
+    return 0                         # packing: data movement only
+
+
+def bench_parallax_bwd(args):
+    import numpy as np
+    import torch
+
+    import lla_inputs
+    from local_linear_attention_amd import (lla_parallax_backward, lla_parallax_backward_workspace_size,
+                                            lla_parallax_forward_stats, lla_profile_collect, lla_profile_enable)
+
+    w = lla_inputs.WORKLOADS[args.workload or "parallax_d24"]
+    q, k, v, _ = lla_inputs.generate(w)
+    rho, _ = lla_inputs.generate_probe(w)
+    dout, _ = lla_inputs.generate_cotangent(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    tq, tk, tv, tr, tdo = (torch.from_numpy(x).to(tdt).to(dev).contiguous() for x in (q, k, v, rho, dout))
+    path = args.path
+    if path == "auto":
+        path = "fast" if w.dtype == "bf16" and w.d == 64 else "exact"
+    _, lse = lla_parallax_forward_stats(tq, tk, tv, tr, w.h, path=path)
+    grads = tuple(torch.empty(tq.shape, dtype=torch.float32, device=dev) for _ in range(4))
+    ws = torch.empty(max(1, lla_parallax_backward_workspace_size(w.B, w.H, w.n, w.d, w.dtype, path)),
+                     dtype=torch.uint8, device=dev)
+    if args.copy_calibration_mib > 0:
+        src = torch.ones((args.copy_calibration_mib << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        lla_parallax_backward(tq, tk, tv, tr, tdo, lse, w.h, path=path, grads=grads, stream=stream, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s_ in range(args.steps):
+        starts[s_].record(stream)
+        step()
+        ends[s_].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    per_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    assert all(torch.isfinite(g).all().item() for g in grads), "non-finite gradient"
+
+    lla_profile_enable(True)
+    lla_profile_collect()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    rec = lla_profile_collect()
+    lla_profile_enable(False)
+    per_kernel = {}
+    for name, ms in rec:
+        per_kernel.setdefault(name, []).append(ms)
+    kernels = {}
+    for name, lst in per_kernel.items():
+        fl = parallax_bwd_kernel_flops(name, w.B, w.H, w.n, w.d)
+        avg = statistics.mean(lst)
+        bound, peak = KERNEL_BOUND[name]
+        kernels[name] = {"launches": len(lst), "avg_ms": avg, "flops": fl, "tflops": fl / (avg * 1e-3) / 1e12,
+                         "bound": bound, "peak": peak}
+    dom = max(kernels, key=lambda nm: kernels[nm]["avg_ms"] * kernels[nm]["launches"])
+    dk = kernels[dom]
+    flops = parallax_bwd_flops(w.B, w.H, w.n, w.d)
+    result = {
+        "metric": METRIC_PARALLAX_BWD,
+        "value": w.queries / (ms_per_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fast": "bf16 products, bf16 hi+lo pair weights, f32 accumulate", "exact": "f64"}[path],
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs, probe and output "
+                               f"cotangent, h={w.h:g}; gradients of q, k, v, rho",
+                   "B": w.B, "H": w.H, "n": w.n, "d": w.d, "input_dtype": w.dtype, "path": path,
+                   "queries": w.queries},
+        "tflops": flops / (ms_per_step * 1e-3) / 1e12,
+        "flop_count": {"formulation": "per pair 16d + 16 (three products, five weighted sums, pair weights), "
+                                      "per row 4d", "flops": flops},
+        "kernels": kernels,
+        "timing_ms": {"median": statistics.median(per_ms), "p10": float(np.percentile(per_ms, 10)),
+                      "p90": float(np.percentile(per_ms, 90))},
+        "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["tflops"], "peak": dk["peak"],
+                     "unit": "TFLOP/s", "frac": dk["tflops"] / dk["peak"], "traffic": load_traffic(dom, w.name)},
+        "mfma_peak_frac": flops / (ms_per_step * 1e-3) / 1e12 / PEAK["mfma_f16_TFLOPs"],
+        "gfx": torch.cuda.get_device_properties(dev).gcnArchName,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = parallax_bwd_cpu_baseline(w, q, k, v, rho, dout, min(args.cpu_seconds, 20.0))
+    print(json.dumps(result), flush=True)
+
+
+def parallax_bwd_cpu_baseline(w, q, k, v, rho, dout, seconds):
+    """The fp64 backward oracle on whole heads drawn at random, projected to the workload."""
+    import numpy as np
+    import torch
+
+    from oracle import parallax_backward
+    rng = np.random.default_rng(12345)
+    done, elapsed = 0, 0.0
+    while elapsed < seconds and done < w.B * w.H:
+        b, hh = int(rng.integers(w.B)), int(rng.integers(w.H))
+        sl = (slice(b, b + 1), slice(hh, hh + 1))
+        t0 = time.perf_counter()
+        parallax_backward(q[sl], k[sl], v[sl], rho[sl], w.h, dout[sl])
+        elapsed += time.perf_counter() - t0
+        done += 1
+    full = elapsed * w.B * w.H / done
+    return {"value": w.queries / full, "unit": "queries/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{done} (batch, head) pairs drawn at random (seed 12345), {elapsed:.1f} s in one process "
+                      f"with {torch.get_num_threads()} BLAS threads; full-step time {full:.1f} s projected per head"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--method", default="lla", choices=["lla", "parallax", "parallax_decode", "lla_decode"])
+    ap.add_argument("--method", default="lla", choices=["lla", "parallax", "parallax_bwd", "parallax_decode", "lla_decode"])
     ap.add_argument("--workload", default=None,
                     help="default: d24 (LLA), parallax_d24 (Parallax), decode_b8_l8192 (Parallax decode), "
                          "lla_decode_b8_l8192 (LLA decode)")
@@ -425,6 +588,9 @@ def main():
 
     if args.method in ("parallax_decode", "lla_decode"):
         bench_decode(args)
+        return
+    if args.method == "parallax_bwd":
+        bench_parallax_bwd(args)
         return
 
     import numpy as np
