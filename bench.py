@@ -57,9 +57,11 @@ def alg_flops(B, H, n, d, form):
 
 
 # Arithmetic of each path (the dtype field) and the bound of each kernel.
-PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d: f64)"}
+PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d: f64)",
+              "cg": "f64 (conjugate gradient over the prefix)"}
 KERNEL_BOUND = {
     "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla_cg_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_short_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_rowmax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_anchor_kernel": ("hbm", PEAK["hbm_GBps"]),
@@ -86,6 +88,7 @@ KERNEL_BOUND = {
 }
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
+    "cg": ["lla_cg_kernel"],
     "fast": ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel",
              "lla_probe_kernel"],
 }
@@ -122,7 +125,9 @@ def kernel_flops(name, B, H, n, d, path):
     rowp = min(n, 4 * d) if path == "fast" else n
     per_query = d ** 3 / 3 + 4 * d * d + 2 * d
     moments = 2 * (1 + 2 * d) + d * (d + 1)
-    if name in ("lla_exact_kernel", "lla_short_kernel"):
+    if name in ("lla_exact_kernel", "lla_short_kernel", "lla_cg_kernel"):
+        # the CG kernel is credited with the direct formulation's count, so that both fp64
+        # paths report comparable rates (its own work depends on the iteration counts)
         return pair_count(BH, 0, row0) * (2 * d + moments + 2 * d * d) + BH * row0 * per_query
     if name in ("lla_anchor_kernel", "lla_pack_kernel"):
         return 0                      # data movement only (K, V summed and repacked once)
@@ -572,7 +577,7 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="default: d24 (LLA), parallax_d24 (Parallax), decode_b8_l8192 (Parallax decode), "
                          "lla_decode_b8_l8192 (LLA decode)")
-    ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast"])
+    ap.add_argument("--path", default="auto", choices=["auto", "exact", "fast", "cg"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

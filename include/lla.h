@@ -69,8 +69,20 @@ typedef enum {
 typedef enum {
     LLA_PATH_AUTO = 0,   /* fp32 inputs -> EXACT; bf16 inputs -> FAST where built */
     LLA_PATH_EXACT = 1,  /* fp64 accumulation and solve, any supported (dtype, d) */
-    LLA_PATH_FAST = 2    /* matrix-core path for bf16 inputs (d = 64); inputs must lie in the
+    LLA_PATH_FAST = 2,   /* matrix-core path for bf16 inputs (d = 64); inputs must lie in the
                             fp16 range, and rows i < 2d still run on the fp64 kernel */
+    LLA_PATH_CG = 3      /* LLA entry points only: fp64 like EXACT, but each query's system
+                            solved by conjugate gradient whose matrix-vector products are passes
+                            over the prefix (the solver of the "Parallax" blog post, section 2,
+                            "Difficulties in Scaling LLA"): no d x d state, one prefix pass per
+                            iteration, at most 4d iterations, stop at residual 1e-10 of the
+                            right-hand side; any supported (dtype, d), no workspace; never
+                            chosen by AUTO.  A row whose iteration does not reach that residual
+                            within 4d iterations is written as NaN: CG needs about sqrt(cond)
+                            iterations, and a ridge lambda e^{-m} far below the spread of the
+                            weighted keys (sharp weights, prefixes shorter than d, lambda = 0)
+                            makes the system too ill-conditioned for that budget; EXACT serves
+                            those rows. */
 } lla_path_t;
 
 /*

@@ -57,6 +57,7 @@ lla_status_t validate(const void* q, const void* k, const void* v, const float* 
 bool resolve_fast(lla_path_t path, int dtype, int64_t d, int64_t n, bool* fast) {
     switch (path) {
         case LLA_PATH_EXACT: *fast = false; return true;
+        case LLA_PATH_CG: *fast = false; return true;
         case LLA_PATH_FAST: *fast = true; return lla::fast_supports(dtype, d, n);
         case LLA_PATH_AUTO: *fast = lla::fast_supports(dtype, d, n); return true;
     }
@@ -349,6 +350,7 @@ lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* 
     if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
     const lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream)};
+    if (path == LLA_PATH_CG) return lla::launch_cg(p) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
     return run(p, fast, workspace, workspace_bytes, false);
 }
 
@@ -362,6 +364,7 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
     if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
     const lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream)};
+    if (path == LLA_PATH_CG) return lla::launch_cg(p) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
     return run(p, fast, nullptr, 0, true);
 }
 

@@ -32,6 +32,10 @@ struct BwdProblem {
 // 0 .. rows-1 of every head (rows = n for the whole problem).
 hipError_t launch_exact(const Problem& p, int rows);
 
+// fp64 path with each query's system solved by conjugate gradient over its prefix (no
+// d x d state): every (dtype, d); no workspace.
+hipError_t launch_cg(const Problem& p);
+
 // Matrix-core path for bf16 inputs: rows i < 2d on the fp64 kernel, the rest on MFMA
 // kernels that keep per-row statistics and packed key/value tiles in `workspace`
 // (fast_workspace_bytes of it).  Serves d = 64 and n up to kFastMaxN.

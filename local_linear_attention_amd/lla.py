@@ -24,7 +24,7 @@ _LIB = None
 
 STATUS = {0: "LLA_OK", 1: "LLA_ERR_NULL", 2: "LLA_ERR_SHAPE", 3: "LLA_ERR_PARAM",
           4: "LLA_ERR_UNSUPPORTED", 5: "LLA_ERR_WORKSPACE", 6: "LLA_ERR_HIP", 7: "LLA_ERR_ALIAS"}
-PATHS = {"auto": 0, "exact": 1, "fast": 2}
+PATHS = {"auto": 0, "exact": 1, "fast": 2, "cg": 3}
 DTYPES = {"f32": 0, "bf16": 1}
 
 

@@ -59,6 +59,7 @@ def test_status_codes_match_header_and_binding():
     assert enums["LLA_PATH_AUTO"] == lla.PATHS["auto"]
     assert enums["LLA_PATH_EXACT"] == lla.PATHS["exact"]
     assert enums["LLA_PATH_FAST"] == lla.PATHS["fast"]
+    assert enums["LLA_PATH_CG"] == lla.PATHS["cg"]
     assert enums["LLA_DTYPE_F32"] == lla.DTYPES["f32"]
     assert enums["LLA_DTYPE_BF16"] == lla.DTYPES["bf16"]
 

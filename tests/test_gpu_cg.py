@@ -1,0 +1,107 @@
+"""GPU parity of the conjugate-gradient LLA path (path "cg": fp64, each query's system
+solved by CG whose matrix-vector products are passes over the prefix) against the fp64
+oracle, and against the direct fp64 path on the same inputs.
+
+Small shapes compare every row (several staged key chunks and a ragged tail, every head
+size, both dtypes, lambda = 0 on rows i >= d); the d = 128 workload at full length compares
+a seeded sample of rows.  Rows whose system is too ill-conditioned for the iteration budget
+come back as NaN, and only those.  Bars: the contract's (1e-4 fp32 inputs, 3e-3 bf16), and 1e-5
+against the oracle on these inputs (the CG stops at a relative residual of 1e-10).
+"""
+import numpy as np
+import pytest
+
+from oracle import lla_forward as oracle_forward
+from oracle import lla_rows as oracle_rows
+from parity_util import TOL, require_gpu, row_errors, run_gpu, sample_rows, workload_arrays
+
+pytestmark = pytest.mark.gpu
+
+CG_BOUND = 1e-5
+
+
+def check(got, ref, dtype, label):
+    err = row_errors(got, ref)
+    worst = float(err.max())
+    print(f"[cg parity] {label} rows={err.size} max_row_err={worst:.3e}", flush=True)
+    assert np.isfinite(got).all(), label
+    assert worst <= TOL[dtype], (label, worst)
+    assert worst <= CG_BOUND, (label, worst)
+
+
+SMALL = [
+    ("tiny", {}),
+    ("tiny", {"B": 2, "H": 3, "n": 77}),
+    ("halfnormal", {"H": 1, "n": 300}),
+    ("d12", {"B": 1, "H": 2, "n": 300}),
+    ("d24", {"B": 1, "H": 2, "n": 333}),
+    ("long", {"B": 1, "H": 1, "n": 200}),
+    ("d12", {"B": 1, "H": 1, "n": 150, "d": 32}),
+    ("d12", {"B": 1, "H": 1, "n": 150, "d": 16}),
+]
+
+
+@pytest.mark.parametrize("name,shape", SMALL, ids=[f"{n}-{s}" for n, s in SMALL])
+def test_every_row(name, shape):
+    require_gpu()
+    w, q, k, v = workload_arrays(name, **shape)
+    ref = oracle_forward(q, k, v, w.h, w.lam, workers=8)
+    got = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="cg")
+    check(got, ref, w.dtype, f"{name}{shape}")
+
+
+def test_ill_conditioned_rows_are_flagged():
+    # fp32 inputs with h = 4 at d = 128: sharp weights and prefixes shorter than d give
+    # systems with condition numbers up to ~1e8, beyond CG's 4d-iteration budget.  Every row
+    # must either match the oracle or be NaN, and only ill-conditioned rows may be NaN.
+    require_gpu()
+    w, q, k, v = workload_arrays("tiny", B=1, H=2, n=130, d=128, dtype="f32")
+    ref = oracle_forward(q, k, v, w.h, w.lam)
+    got = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="cg")
+    flagged = np.isnan(got).all(-1)
+    assert np.array_equal(np.isnan(got).any(-1), flagged)   # whole rows only
+    ok = ~flagged
+    err = row_errors(got[ok], ref[ok])
+    conds = []
+    for hh in range(w.H):
+        for i in range(w.n):
+            if flagged[0, hh, i]:
+                kk, qq = k[0, hh, : i + 1].astype(np.float64), q[0, hh, i].astype(np.float64)
+                s = kk @ qq / w.h
+                wt = np.exp(s - s.max())
+                kc = kk - wt @ kk / wt.sum()
+                A = kc.T @ (wt[:, None] * kc) + w.lam * np.exp(-s.max()) * np.eye(w.d)
+                conds.append(np.linalg.cond(A))
+    print(f"[cg flagged] {int(flagged.sum())} of {flagged.size} rows NaN, min cond of those "
+          f"{min(conds) if conds else float('nan'):.1e}; others max_row_err={float(err.max()):.2e}", flush=True)
+    assert float(err.max()) <= CG_BOUND
+    assert not conds or min(conds) > 1e5
+
+
+def test_lambda_zero_rows_beyond_d():
+    require_gpu()
+    w, q, k, v = workload_arrays("tiny_affine")
+    ref = oracle_forward(q, k, v, w.h, w.lam)
+    got = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="cg")
+    check(got[..., w.d:, :], ref[..., w.d:, :], w.dtype, "tiny_affine rows>=d")
+
+
+def test_agrees_with_the_direct_path():
+    require_gpu()
+    w, q, k, v = workload_arrays("d12", B=1, H=3, n=400)
+    a = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="cg")
+    b = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="exact")
+    err = float(row_errors(a, b).max())
+    print(f"[cg vs exact] max_row_err={err:.3e}", flush=True)
+    assert err <= CG_BOUND
+
+
+def test_d128_workload_full_length_sampled_rows():
+    require_gpu()
+    w, q, k, v = workload_arrays("long", H=2)
+    rows = sample_rows(w.B, w.H, w.n, w.d, w.seed, per_head=4)
+    got_full = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="cg")
+    assert np.isfinite(got_full).all()
+    ref = oracle_rows(q, k, v, w.h, w.lam, rows, workers=8)
+    got = np.stack([got_full[b, hh, i] for (b, hh, i) in rows])
+    check(got, ref, w.dtype, "long (H2) full-length sampled")
