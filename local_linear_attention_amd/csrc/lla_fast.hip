@@ -5,7 +5,8 @@
 //     rank-deficient or barely full rank and the ridge lambda e^{-m} alone conditions the
 //     solve -- the normal-equation form then needs more than fp16/fp32 precision;
 //   * rows i >= 2d run here:
-//       lla_anchor_kernel   per-head sums of the keys and values (the centring anchor a);
+//       lla_anchor_kernel   per-head sums of the keys and values of positions [0, 2d) (the
+//                           centring anchor a: every row of this path has them in its prefix);
 //       lla_pack_kernel     K, V once into fp16 tiles centred at a (the LDS image the
 //                           moments kernel copies) and K key-major for the score pass;
 //       lla_rowmax_kernel   score pass with a running max: m_i;
@@ -44,7 +45,9 @@ constexpr int B_WAVES = 4;          // waves per block of the row-max and moment
 // into LDS (buffer loads with an LDS destination, no registers) -- one barrier per tile.
 //
 // Anchor: the pack kernel stores each head's keys and values centred at a = (mean k,
-// mean v) of the head rounded to fp16, so every wave only scales: R_k = sw (k - a_k),
+// mean v) of its positions [0, 2d) rounded to fp16 -- positions in the prefix of every row
+// this path serves, so no row depends on a later position even through rounding -- and
+// every wave only scales: R_k = sw (k - a_k),
 // R_v = sw (v - a_v).  Moments about a differ from the centred ones by a rank-one term,
 //   C = sum_j w_j (x_j - a)(y_j - a)^T - S_x S_y^T / omega',   S_x = sum_j w_j (x_j - a),
 // which the block gets from one extra MFMA pair per wave and 32 keys (weights w_j = sw_j^2
@@ -86,8 +89,8 @@ constexpr int R_SETS = 2, R_QW = 16 * R_SETS, R_QB = B_WAVES * R_QW;  // row-max
 static_assert(KM_TILE_BYTES % 1024 == 0, "key image must be whole wave copies");
 static_assert(PACK_TILE_BYTES % 1024 == 0, "tile image must be whole wave copies");
 
-// Per-head anchor, pass 1: block (head, slice) sums its slice of the keys and values per
-// feature (fp32).  Thread -> 8 features (16 bytes) of K (groups 0-7) or V (groups 8-15) and
+// Per-head anchor, pass 1: block (head, slice) sums its slice of the keys and values of
+// positions [0, min(n, 2d)) per feature (fp32).  Thread -> 8 features (16 bytes) of K (groups 0-7) or V (groups 8-15) and
 // every 16th key of the slice; the 16 key phases are then added up through LDS.
 __global__ __launch_bounds__(256) void lla_anchor_kernel(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
@@ -96,8 +99,9 @@ __global__ __launch_bounds__(256) void lla_anchor_kernel(const uint16_t* __restr
     const int bh = static_cast<int>(blockIdx.x) / ANCHOR_SLICES;
     const int sl = static_cast<int>(blockIdx.x) % ANCHOR_SLICES;
     const int tid = threadIdx.x, fgrp = tid & 15, ph = tid >> 4;
-    const int len = (n + ANCHOR_SLICES - 1) / ANCHOR_SLICES;
-    const int j_lo = sl * len, j_hi = min(n, j_lo + len);
+    const int na = min(n, 2 * FD);
+    const int len = (na + ANCHOR_SLICES - 1) / ANCHOR_SLICES;
+    const int j_lo = sl * len, j_hi = min(na, j_lo + len);
     const uint16_t* src = (fgrp < 8 ? k : v) + static_cast<int64_t>(bh) * n * FD + 8 * (fgrp & 7);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = j_lo + ph; j < j_hi; j += 16) {
@@ -119,7 +123,8 @@ __global__ __launch_bounds__(256) void lla_anchor_kernel(const uint16_t* __restr
 }
 
 // Pack K and V once into the LDS image of each tile (zero past n), centred at the head's
-// anchor a = fp16(mean over all keys of k, of v): stored value fp16(x - a), one rounding.
+// anchor a = fp16(mean of k, of v over positions [0, 2d)): stored value fp16(x - a), one
+// rounding.
 // Thread -> keys 2p, 2p+1 and features 8fg .. 8fg+7; every store writes a pair of keys.
 // The same block also writes the tile's keys key-major, as given (bf16) and centred
 // (fp16(k - a), the same values as the feature-major image), and block 0 of each head the
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
         float sum = 0.0f;
         for (int sl = 0; sl < ANCHOR_SLICES; ++sl)
             sum += partial[(static_cast<int64_t>(bh) * ANCHOR_SLICES + sl) * 2 * FD + tid];
-        anc[tid] = static_cast<float>(static_cast<_Float16>(sum / static_cast<float>(n)));
+        anc[tid] = static_cast<float>(static_cast<_Float16>(sum / static_cast<float>(min(n, 2 * FD))));
         if (t == 0) anchors[static_cast<int64_t>(bh) * 2 * FD + tid] = anc[tid];
     }
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
