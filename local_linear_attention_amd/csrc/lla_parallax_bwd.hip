@@ -67,6 +67,7 @@ constexpr int KIMG = (KI_KT + TM_BYTES + 1023) / 1024 * 1024;  // 27648
 constexpr int BW = 8;                           // waves per block in both passes
 constexpr int BNT = BW * 64;
 constexpr int BROWS = 16 * BW;                  // keys (column pass) or rows (row pass) per block
+constexpr int KV_NBUF = 2;                      // query images in LDS in the column pass (1 measured slower)
 
 // ---------------------------------------------------------------------------------------
 // Pack: block per (head, tile), thread -> row r = tid / 4 of the tile, features 16 fc ..
@@ -165,6 +166,7 @@ __device__ __forceinline__ bf16x8 tpair(const unsigned char* p) {
 // ---------------------------------------------------------------------------------------
 // Column pass.  Wave w owns keys kw0 .. kw0+15 (lane column c = key kw0 + c).  Per query
 // tile, score blocks rb = 0..3 (rows 16 rb + 4g + r in register r).
+template <int NBUF>   // query images held in LDS: 2 (one barrier per tile) or 1 (two blocks per CU)
 __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_kv_kernel(
     const unsigned char* __restrict__ qimg, const unsigned char* __restrict__ kimg, float* __restrict__ dk,
     float* __restrict__ dv, int n, int BH, int ntiles, float sl2, float inv_h) {
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_kv_kernel(
     __syncthreads();
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
     for (int t = qt0; t < ntiles; ++t) {
-        const int b = (t - qt0) & 1;
+        const int b = NBUF == 2 ? (t - qt0) & 1 : 0;
         if (t + 1 < ntiles) cp.fetch(qih + static_cast<int64_t>(t + 1) * QIMG, tid);
         const int i0 = t * BT;
         if (kw0 <= i0 + BT - 1 && kw0 < n) {   // wave-uniform: some row of the tile sees a key
@@ -260,7 +262,8 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_kv_kernel(
                 }
             }
         }
-        if (t + 1 < ntiles) cp.stash(lds + (b ^ 1) * QIMG, tid);
+        if constexpr (NBUF == 1) __syncthreads();   // every wave is done with the image
+        if (t + 1 < ntiles) cp.stash(lds + (NBUF == 2 ? (b ^ 1) * QIMG : 0), tid);
         __syncthreads();
     }
     // lane (g, c) register r of block fb: feature 16 fb + 4g + r of key kc
@@ -665,8 +668,8 @@ hipError_t launch_parallax_bwd_fast(const BwdProblem& b, void* workspace) {
     unsigned char* qimg = static_cast<unsigned char*>(workspace);
     unsigned char* kimg = qimg + static_cast<int64_t>(BH) * ntiles * QIMG;
     static const hipError_t attr_err = [] {   // once: dynamic LDS above the default limit
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_kv_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * QIMG);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_kv_kernel<KV_NBUF>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, KV_NBUF * QIMG);
         if (e == hipSuccess)
             e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_qr_kernel<true>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, 2 * KIMG);
@@ -691,8 +694,8 @@ hipError_t launch_parallax_bwd_fast(const BwdProblem& b, void* workspace) {
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla_parallax_bwd_kv_kernel");
-    lla_parallax_bwd_kv_kernel<<<dim3(nblk), dim3(BNT), 2 * QIMG, p.stream>>>(qimg, kimg, b.dk, b.dv, n, BH, ntiles,
-                                                                            sl2, inv_h);
+    lla_parallax_bwd_kv_kernel<KV_NBUF><<<dim3(nblk), dim3(BNT), KV_NBUF * QIMG, p.stream>>>(qimg, kimg, b.dk, b.dv, n,
+                                                                                          BH, ntiles, sl2, inv_h);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla_parallax_bwd_qr_kernel");
