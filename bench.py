@@ -249,6 +249,13 @@ def lla_decode_chunks(BH, L):
     return -(-L // c)
 
 
+def lla_decode_three_part(w):
+    """Whether the LLA decode moments run from three-part bf16 operands (bf16 inputs, caches
+    of at least 2d positions, d <= 64): HBM-bound then (the K, V read and the executed
+    matrix-core work take about the same time at peak); otherwise fp32 or fp64 matrix cores."""
+    return w.dtype == "bf16" and w.L >= 2 * w.d and w.d <= 64
+
+
 def decode_kernel_units(name, w, elt):
     """(algorithmic amount, unit) of one launch of each decode kernel at workload w."""
     B, H, L, d = w.B, w.H, w.L, w.d
@@ -259,6 +266,9 @@ def decode_kernel_units(name, w, elt):
         # reads the keys and the query
         return B * H * L * d * elt + B * H * d * elt, "B"
     if name == "lla_decode_moments_kernel":
+        if lla_decode_three_part(w):
+            # reads K and V once and the stats pass's scores
+            return 2 * B * H * L * d * elt + B * H * L * 4, "B"
         return lla_moment_flops(B, H, L, d), "flop"
     if name == "lla_decode_reduce_kernel":
         # reads every chunk's moments, writes the heads' fp64 sums
@@ -362,6 +372,8 @@ def bench_decode(args):
         avg = statistics.mean(lst)
         amount, unit = decode_kernel_units(name, w, elt)
         bound, peak = KERNEL_BOUND[name]
+        if name == "lla_decode_moments_kernel" and unit == "B":
+            bound, peak = "hbm", PEAK["hbm_GBps"]
         ent = {"launches": len(lst), "avg_ms": avg, "bound": bound, "peak": peak}
         if unit == "B":
             ent.update(bytes=amount, GBps=amount / (avg * 1e-3) / 1e9)

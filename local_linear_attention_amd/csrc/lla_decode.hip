@@ -388,8 +388,9 @@ void lla_decode_split(int64_t BH, int64_t L, int* S, int* C) {
 template <typename TIn, int D>
 __global__ __launch_bounds__(DC_THREADS) void lla_decode_stats_kernel(const TIn* __restrict__ q,
                                                                       const TIn* __restrict__ k,
-                                                                      double* __restrict__ stats, int L, int S,
-                                                                      int C, float sl2) {
+                                                                      double* __restrict__ stats,
+                                                                      float* __restrict__ xsc, int L, int S, int C,
+                                                                      float sl2) {
     constexpr int G = D / 8, KPP = DC_THREADS / G;
     __shared__ float red[DC_THREADS / 64];
     __shared__ float acc[KPP][D + 1];
@@ -412,6 +413,7 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_stats_kernel(const TIn*
 #pragma unroll
         for (int e = 0; e < 8; ++e) a = fmaf(qv[e], kv[e], a);
         const float x = group_sum<G>(a) * sl2;
+        if (xsc != nullptr && fg == 0) xsc[static_cast<int64_t>(bh) * L + j0 + jj] = x;
         const float mn = fmaxf(mt, x);
         const float sc = exp2f(mt - mn);   // 0 on the group's first key
         const float w = exp2f(x - mn);
@@ -601,6 +603,212 @@ __global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
     }
 }
 
+// ---- Moments from bf16 three-part operands (bf16 inputs, fp32 moments, d <= 64).
+// R_k = sqrt(w) (k - kbar) and R_v = sqrt(w) v are formed in fp32 from the stats pass's
+// scores and split as r = h + m + l (each bf16; 24 significant bits together); a 16x16
+// block then takes the six products down to 2^-16 of the leading one -- hh, hm, mh, hl, lh,
+// mm -- on v_mfma_f32_16x16x32_bf16 (32 keys per instruction): the dropped terms are below
+// 2^-24 relative, the level of the fp32 accumulation, at about 2.7 times the fp32 MFMA rate.
+// Staging per sub-tile of 32 keys: 16-byte loads of the rows (in flight during the current
+// sub-tile's MFMAs) go to a row-major LDS tile with one weight per key; then thread ->
+// (K or V, feature f, 8 consecutive keys) forms the three parts and writes each with one
+// 16-byte store into the feature-major operand image (two images, one per parity).
+typedef __bf16 bf16x8d __attribute__((ext_vector_type(8)));
+constexpr int M3_SUB = 32;
+constexpr int M3_LD = M3_SUB + 8;   // feature row of a part (halves): 80 bytes
+
+template <int D>
+constexpr int m3_buf_bytes() { return 3 * 2 * D * M3_LD * 2; }   // [part][K, V][feature][M3_LD]
+
+__device__ __forceinline__ float4x mfma_bf(bf16x8d a, bf16x8d b, float4x c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// c += a b for a, b given as three bf16 parts each, smallest products first.
+__device__ __forceinline__ float4x mfma6(const bf16x8d (&a)[3], const bf16x8d (&b)[3], float4x c) {
+    c = mfma_bf(a[1], b[1], c);
+    c = mfma_bf(a[2], b[0], c);
+    c = mfma_bf(a[0], b[2], c);
+    c = mfma_bf(a[1], b[0], c);
+    c = mfma_bf(a[0], b[1], c);
+    return mfma_bf(a[0], b[0], c);
+}
+
+template <int D, int B0, int N, int... Bs>
+__device__ __forceinline__ void mfma3_blocks(const bf16x8d (&kop)[D / 16][3], const bf16x8d (&vop)[D / 16][3],
+                                             float4x (&acc)[N], std::integer_sequence<int, Bs...>) {
+    using MB = MomBlocks<D>;
+    ((acc[Bs] = mfma6(std::integral_constant<int, MB::kind(B0 + Bs)>::value == 0
+                          ? kop[std::integral_constant<int, MB::I(B0 + Bs)>::value]
+                          : vop[std::integral_constant<int, MB::I(B0 + Bs)>::value],
+                      kop[std::integral_constant<int, MB::J(B0 + Bs)>::value], acc[Bs])),
+     ...);
+}
+
+// Row-major staging tile of one sub-tile (bf16 as given): [K, V][key][D + 8].
+template <int D>
+constexpr int m3_raw_bytes() { return 2 * M3_SUB * (D + 8) * 2; }
+template <int D>
+constexpr int m3_smem_bytes() { return 2 * m3_buf_bytes<D>() + m3_raw_bytes<D>(); }
+
+template <typename TIn, int D, int W>
+__device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const TIn* __restrict__ vh,
+                                              const float* __restrict__ xh, const float* kbf, unsigned char* img,
+                                              uint16_t* raw, float* swl, float* svs, float Mf, int j0, int jend,
+                                              int tid, float* __restrict__ mo) {
+    using MB = MomBlocks<D>;
+    constexpr int NB = D / 16;
+    constexpr int B0 = W * MB::NT / 4, B1 = (W + 1) * MB::NT / 4;
+    constexpr int NA = B1 > B0 ? B1 - B0 : 1;
+    constexpr int PAIRS = 8 * D;                                 // (K or V, feature, 8 keys)
+    constexpr int PPT = (PAIRS + DC_THREADS - 1) / DC_THREADS;
+    constexpr int CHUNKS = 2 * M3_SUB * D / 8;                   // 16-byte row pieces per sub-tile
+    constexpr int CPT = (CHUNKS + DC_THREADS - 1) / DC_THREADS;
+    constexpr int RLD = D + 8;                                   // raw row (halves)
+    constexpr int VB = B0 > MB::NKK ? B0 : MB::NKK;
+    constexpr int VI0 = B1 > MB::NKK ? MB::I(VB) : 0;
+    constexpr int VI1 = B1 > MB::NKK ? MB::I(B1 - 1) : -1;
+    constexpr int BUFB = m3_buf_bytes<D>();
+    static_assert(sizeof(TIn) == 2, "three-part moments take bf16 inputs");
+    const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+    float4x acc[NA];
+#pragma unroll
+    for (int t = 0; t < NA; ++t) acc[t] = float4x{0.f, 0.f, 0.f, 0.f};
+    float sv[PPT];
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) sv[e] = 0.0f;
+    uint4 pre[CPT];
+    float xpre = -INFINITY;
+    // 16-byte pieces: piece u -> array u / (M3_SUB D/8), key, features 8 (u % (D/8)) ..
+    auto fetch = [&](int js) {
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            const int u = tid + DC_THREADS * e;
+            const int arr = u / (M3_SUB * D / 8), rem = u % (M3_SUB * D / 8), key = rem / (D / 8), fc = rem % (D / 8);
+            const int j = js + key;
+            pre[e] = uint4{0u, 0u, 0u, 0u};
+            if (u < CHUNKS && j < jend)
+                pre[e] = *reinterpret_cast<const uint4*>((arr == 0 ? kh : vh) + static_cast<int64_t>(j) * D + 8 * fc);
+        }
+        xpre = tid < M3_SUB && js + tid < jend ? xh[js + tid] : -INFINITY;
+    };
+    // raw pieces and weights to LDS, then (after a barrier) the three parts of R_k, R_v
+    auto stash = [&](unsigned char* buf) {
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+            const int u = tid + DC_THREADS * e;
+            if (u < CHUNKS) {
+                const int arr = u / (M3_SUB * D / 8), rem = u % (M3_SUB * D / 8), key = rem / (D / 8), fc = rem % (D / 8);
+                *reinterpret_cast<uint4*>(raw + (arr * M3_SUB + key) * RLD + 8 * fc) = pre[e];
+            }
+        }
+        if (tid < M3_SUB) swl[tid] = exp2f((xpre - Mf) * 0.5f);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PPT; ++e) {
+            const int pp = tid + DC_THREADS * e;
+            if (pp < PAIRS) {
+                const int arr = pp / (4 * D), rem = pp % (4 * D), f = rem % D, kg = rem / D;
+                const float sub = arr == 0 ? kbf[f] : 0.0f;
+                bf16x8d ph, pm, pl;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float sw = swl[8 * kg + t];
+                    const float x = __uint_as_float(static_cast<uint32_t>(raw[(arr * M3_SUB + 8 * kg + t) * RLD + f]) << 16);
+                    const float r = sw * (x - sub);
+                    if (arr == 1) sv[e] = fmaf(sw * sw, x, sv[e]);
+                    const __bf16 h = static_cast<__bf16>(r);
+                    const float r1 = r - static_cast<float>(h);
+                    const __bf16 m = static_cast<__bf16>(r1);
+                    ph[t] = h;
+                    pm[t] = m;
+                    pl[t] = static_cast<__bf16>(r1 - static_cast<float>(m));
+                }
+                unsigned char* row = buf + (arr * D + f) * (M3_LD * 2) + 16 * kg;
+                *reinterpret_cast<bf16x8d*>(row) = ph;
+                *reinterpret_cast<bf16x8d*>(row + 2 * D * M3_LD * 2) = pm;
+                *reinterpret_cast<bf16x8d*>(row + 4 * D * M3_LD * 2) = pl;
+            }
+        }
+    };
+    const int nsub = (jend - j0 + M3_SUB - 1) / M3_SUB;
+    fetch(j0);
+    stash(img);
+    __syncthreads();
+    for (int t = 0; t < nsub; ++t) {
+        if (t + 1 < nsub) fetch(j0 + (t + 1) * M3_SUB);
+        if constexpr (B1 > B0) {
+            const unsigned char* buf = img + (t & 1) * BUFB;
+            bf16x8d kop[NB][3], vop[NB][3];
+#pragma unroll
+            for (int R = 0; R < NB; ++R)
+#pragma unroll
+                for (int lv = 0; lv < 3; ++lv)
+                    kop[R][lv] = *reinterpret_cast<const bf16x8d*>(
+                        buf + ((2 * lv) * D + 16 * R + c) * (M3_LD * 2) + 16 * g);
+#pragma unroll
+            for (int R = VI0; R <= VI1; ++R)
+#pragma unroll
+                for (int lv = 0; lv < 3; ++lv)
+                    vop[R][lv] = *reinterpret_cast<const bf16x8d*>(
+                        buf + ((2 * lv + 1) * D + 16 * R + c) * (M3_LD * 2) + 16 * g);
+            mfma3_blocks<D, B0>(kop, vop, acc, std::make_integer_sequence<int, B1 - B0>{});
+        }
+        if (t + 1 < nsub) stash(img + ((t + 1) & 1) * BUFB);   // its barrier also ends the raw tile's reuse
+        __syncthreads();
+    }
+#pragma unroll
+    for (int b = B0; b < B1; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mo[b * 256 + (4 * g + r) * 16 + c] = acc[b - B0][r];
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+        const int pp = tid + DC_THREADS * e;
+        if (pp < PAIRS && pp >= 4 * D) svs[((pp - 4 * D) / D) * D + (pp - 4 * D) % D] = sv[e];   // [kg][f]
+    }
+}
+
+template <typename TIn, int D>
+__global__ __launch_bounds__(DC_THREADS, 2) void lla_decode_moments3_kernel(
+    const TIn* __restrict__ k, const TIn* __restrict__ v, const double* __restrict__ stats,
+    const float* __restrict__ xsc, float* __restrict__ mom, int L, int S, int C) {
+    using MB = MomBlocks<D>;
+    static_assert(D <= 64, "three-part moments serve d <= 64");
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    __shared__ double sh[DC_THREADS];
+    __shared__ double kbd[D];
+    __shared__ float kbf[D];
+    __shared__ float svs[4 * D];
+    __shared__ float swl[M3_SUB];
+    const int tid = threadIdx.x;
+    const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint16_t* raw = reinterpret_cast<uint16_t*>(lds + 2 * m3_buf_bytes<D>());
+    const int bh = static_cast<int>(blockIdx.x) / S, sidx = static_cast<int>(blockIdx.x) % S;
+    const int j0 = sidx * C;
+    const int jend = min(L, j0 + C);
+    double M, om;
+    head_stats<D>(stats + static_cast<int64_t>(bh) * S * (2 + D), S, sh, kbd, &M, &om);
+    if (tid < D) kbf[tid] = static_cast<float>(kbd[tid]);
+    __syncthreads();
+    const float Mf = static_cast<float>(M);
+    const TIn* kh = k + static_cast<int64_t>(bh) * L * D;
+    const TIn* vh = v + static_cast<int64_t>(bh) * L * D;
+    const float* xh = xsc + static_cast<int64_t>(bh) * L;
+    float* mo = mom + (static_cast<int64_t>(bh) * S + sidx) * (MB::NT * 256 + D);
+    switch (wu) {
+        case 0: moments3_wave<TIn, D, 0>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+        case 1: moments3_wave<TIn, D, 1>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+        case 2: moments3_wave<TIn, D, 2>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+        default: moments3_wave<TIn, D, 3>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float t = 0.0f;
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) t += svs[kg * D + tid];
+        mo[MB::NT * 256 + tid] = t;
+    }
+}
+
 // Sum of the S chunks' moments of each head, in chunk order (fp64): one thread per entry.
 template <typename TA>
 __global__ __launch_bounds__(DC_THREADS) void lla_decode_reduce_kernel(const TA* __restrict__ mom,
@@ -723,14 +931,19 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_solve_kernel(
 // Workspace: chunk statistics, then the chunks' moments, then (several chunks per head) the
 // heads' summed moments; each region starts on a 256-byte boundary.
 struct LlaDecodeLayout {
-    int64_t stats_bytes, mom_bytes, sum_bytes;
+    int64_t stats_bytes, score_bytes, mom_bytes, sum_bytes;
 };
-LlaDecodeLayout lla_decode_layout(int64_t BH, int64_t L, int64_t d, int64_t ta_bytes) {
+// fp32 moments from three-part bf16 operands (they read the stats pass's scores): bf16 inputs
+// with fp32 moments and d <= 64.
+bool lla_decode_three_part(int dtype, int64_t L, int64_t d) { return !lla_decode_fp64(dtype, L, d) && d <= 64; }
+LlaDecodeLayout lla_decode_layout(int64_t BH, int64_t L, int64_t d, int dtype) {
     int S = 1, C = 1;
     lla_decode_split(BH, L, &S, &C);
     const int64_t nb = d / 16, e = (nb * (nb + 1) / 2 + nb * nb) * 256 + d;
+    const int64_t ta = lla_decode_fp64(dtype, L, d) ? 8 : 4;
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
-    return {up(BH * S * (2 + d) * 8), up(BH * S * e * ta_bytes), S > 1 ? BH * e * 8 : 0};
+    return {up(BH * S * (2 + d) * 8), lla_decode_three_part(dtype, L, d) ? up(BH * L * 4) : 0, up(BH * S * e * ta),
+            S > 1 ? BH * e * 8 : 0};
 }
 
 template <typename TIn, int D, typename TA>
@@ -741,28 +954,44 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
     int S = 1, C = 1;
     lla_decode_split(BH, p.n, &S, &C);
     const float sl2 = static_cast<float>(DC_LOG2E / p.h);
-    const LlaDecodeLayout lay = lla_decode_layout(BH, p.n, D, sizeof(TA));
+    const LlaDecodeLayout lay = lla_decode_layout(BH, p.n, D, p.dtype);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     double* stats = reinterpret_cast<double*>(ws);
-    TA* mom = reinterpret_cast<TA*>(ws + lay.stats_bytes);
-    double* msum = reinterpret_cast<double*>(ws + lay.stats_bytes + lay.mom_bytes);
+    float* xsc = lay.score_bytes > 0 ? reinterpret_cast<float*>(ws + lay.stats_bytes) : nullptr;
+    TA* mom = reinterpret_cast<TA*>(ws + lay.stats_bytes + lay.score_bytes);
+    double* msum = reinterpret_cast<double*>(ws + lay.stats_bytes + lay.score_bytes + lay.mom_bytes);
     static_assert(mom_smem_bytes<D, TA>() <= 150 * 1024, "LDS");
     static const hipError_t attr_err = [] {   // once per instantiation
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
+        if constexpr (D <= 64 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value)
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments3_kernel<TIn, D>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, m3_smem_bytes<D>());
+        return e;
     }();
     hipError_t err = attr_err;
     if (err != hipSuccess) return err;
     const unsigned blocks = static_cast<unsigned>(BH * S);
     prof_begin(p.stream, "lla_decode_stats_kernel");
     lla_decode_stats_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), 0, p.stream>>>(
-        static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), stats, static_cast<int>(p.n), S, C, sl2);
+        static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), stats, xsc, static_cast<int>(p.n), S, C, sl2);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla_decode_moments_kernel");
-    lla_decode_moments_kernel<TIn, D, TA><<<dim3(blocks), dim3(DC_THREADS), mom_smem_bytes<D, TA>(), p.stream>>>(
-        static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, mom,
-        static_cast<int>(p.n), S, C, sl2);
+    bool launched = false;
+    if constexpr (D <= 64 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value) {
+        if (xsc != nullptr) {
+            lla_decode_moments3_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), m3_smem_bytes<D>(), p.stream>>>(
+                static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, xsc, mom, static_cast<int>(p.n),
+                S, C);
+            launched = true;
+        }
+    }
+    if (!launched)
+        lla_decode_moments_kernel<TIn, D, TA><<<dim3(blocks), dim3(DC_THREADS), mom_smem_bytes<D, TA>(), p.stream>>>(
+            static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, mom,
+            static_cast<int>(p.n), S, C, sl2);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (S > 1) {
@@ -804,8 +1033,8 @@ hipError_t launch_lla_decode_d(const Problem& p, void* workspace) {
 }  // namespace
 
 size_t lla_decode_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int dtype) {
-    const LlaDecodeLayout lay = lla_decode_layout(B * H, L, d, lla_decode_fp64(dtype, L, d) ? 8 : 4);
-    return static_cast<size_t>(lay.stats_bytes + lay.mom_bytes + lay.sum_bytes);
+    const LlaDecodeLayout lay = lla_decode_layout(B * H, L, d, dtype);
+    return static_cast<size_t>(lay.stats_bytes + lay.score_bytes + lay.mom_bytes + lay.sum_bytes);
 }
 
 hipError_t launch_lla_decode(const Problem& p, void* workspace) {
