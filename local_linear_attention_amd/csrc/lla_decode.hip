@@ -614,8 +614,9 @@ __global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
 // (K or V, feature f, 8 consecutive keys) forms the three parts and writes each with one
 // 16-byte store into the feature-major operand image (two images, one per parity).
 typedef __bf16 bf16x8d __attribute__((ext_vector_type(8)));
-constexpr int M3_SUB = 32;
-constexpr int M3_LD = M3_SUB + 8;   // feature row of a part (halves): 80 bytes
+constexpr int M3_SUB = 64;          // keys per sub-tile: two 32-key MFMA steps
+constexpr int M3_KG = M3_SUB / 8;   // groups of 8 keys per sub-tile
+constexpr int M3_LD = M3_SUB + 8;   // feature row of a part (halves): 144 bytes
 
 template <int D>
 constexpr int m3_buf_bytes() { return 3 * 2 * D * M3_LD * 2; }   // [part][K, V][feature][M3_LD]
@@ -648,7 +649,7 @@ __device__ __forceinline__ void mfma3_blocks(const bf16x8d (&kop)[D / 16][3], co
 template <int D>
 constexpr int m3_raw_bytes() { return 2 * M3_SUB * (D + 8) * 2; }
 template <int D>
-constexpr int m3_smem_bytes() { return 2 * m3_buf_bytes<D>() + m3_raw_bytes<D>(); }
+constexpr int m3_smem_bytes() { return m3_buf_bytes<D>() + m3_raw_bytes<D>(); }
 
 template <typename TIn, int D, int W>
 __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const TIn* __restrict__ vh,
@@ -659,7 +660,7 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
     constexpr int NB = D / 16;
     constexpr int B0 = W * MB::NT / 4, B1 = (W + 1) * MB::NT / 4;
     constexpr int NA = B1 > B0 ? B1 - B0 : 1;
-    constexpr int PAIRS = 8 * D;                                 // (K or V, feature, 8 keys)
+    constexpr int PAIRS = 2 * D * M3_KG;                         // (K or V, feature, 8 keys)
     constexpr int PPT = (PAIRS + DC_THREADS - 1) / DC_THREADS;
     constexpr int CHUNKS = 2 * M3_SUB * D / 8;                   // 16-byte row pieces per sub-tile
     constexpr int CPT = (CHUNKS + DC_THREADS - 1) / DC_THREADS;
@@ -667,7 +668,6 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
     constexpr int VB = B0 > MB::NKK ? B0 : MB::NKK;
     constexpr int VI0 = B1 > MB::NKK ? MB::I(VB) : 0;
     constexpr int VI1 = B1 > MB::NKK ? MB::I(B1 - 1) : -1;
-    constexpr int BUFB = m3_buf_bytes<D>();
     static_assert(sizeof(TIn) == 2, "three-part moments take bf16 inputs");
     const int lane = tid & 63, g = lane >> 4, c = lane & 15;
     float4x acc[NA];
@@ -707,7 +707,7 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
         for (int e = 0; e < PPT; ++e) {
             const int pp = tid + DC_THREADS * e;
             if (pp < PAIRS) {
-                const int arr = pp / (4 * D), rem = pp % (4 * D), f = rem % D, kg = rem / D;
+                const int arr = pp / (M3_KG * D), rem = pp % (M3_KG * D), f = rem % D, kg = rem / D;
                 const float sub = arr == 0 ? kbf[f] : 0.0f;
                 bf16x8d ph, pm, pl;
 #pragma unroll
@@ -730,6 +730,8 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
             }
         }
     };
+    // One operand image: stash's first barrier comes after every wave's MFMAs on it, its
+    // second (the loop's) before the next sub-tile's.
     const int nsub = (jend - j0 + M3_SUB - 1) / M3_SUB;
     fetch(j0);
     stash(img);
@@ -737,23 +739,25 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
     for (int t = 0; t < nsub; ++t) {
         if (t + 1 < nsub) fetch(j0 + (t + 1) * M3_SUB);
         if constexpr (B1 > B0) {
-            const unsigned char* buf = img + (t & 1) * BUFB;
-            bf16x8d kop[NB][3], vop[NB][3];
 #pragma unroll
-            for (int R = 0; R < NB; ++R)
+            for (int ks = 0; ks < M3_SUB / 32; ++ks) {
+                bf16x8d kop[NB][3], vop[NB][3];
 #pragma unroll
-                for (int lv = 0; lv < 3; ++lv)
-                    kop[R][lv] = *reinterpret_cast<const bf16x8d*>(
-                        buf + ((2 * lv) * D + 16 * R + c) * (M3_LD * 2) + 16 * g);
+                for (int R = 0; R < NB; ++R)
 #pragma unroll
-            for (int R = VI0; R <= VI1; ++R)
+                    for (int lv = 0; lv < 3; ++lv)
+                        kop[R][lv] = *reinterpret_cast<const bf16x8d*>(
+                            img + ((2 * lv) * D + 16 * R + c) * (M3_LD * 2) + 64 * ks + 16 * g);
 #pragma unroll
-                for (int lv = 0; lv < 3; ++lv)
-                    vop[R][lv] = *reinterpret_cast<const bf16x8d*>(
-                        buf + ((2 * lv + 1) * D + 16 * R + c) * (M3_LD * 2) + 16 * g);
-            mfma3_blocks<D, B0>(kop, vop, acc, std::make_integer_sequence<int, B1 - B0>{});
+                for (int R = VI0; R <= VI1; ++R)
+#pragma unroll
+                    for (int lv = 0; lv < 3; ++lv)
+                        vop[R][lv] = *reinterpret_cast<const bf16x8d*>(
+                            img + ((2 * lv + 1) * D + 16 * R + c) * (M3_LD * 2) + 64 * ks + 16 * g);
+                mfma3_blocks<D, B0>(kop, vop, acc, std::make_integer_sequence<int, B1 - B0>{});
+            }
         }
-        if (t + 1 < nsub) stash(img + ((t + 1) & 1) * BUFB);   // its barrier also ends the raw tile's reuse
+        if (t + 1 < nsub) stash(img);
         __syncthreads();
     }
 #pragma unroll
@@ -763,7 +767,7 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
         const int pp = tid + DC_THREADS * e;
-        if (pp < PAIRS && pp >= 4 * D) svs[((pp - 4 * D) / D) * D + (pp - 4 * D) % D] = sv[e];   // [kg][f]
+        if (pp < PAIRS && pp >= M3_KG * D) svs[pp - M3_KG * D] = sv[e];   // [kg][f]
     }
 }
 
@@ -777,11 +781,11 @@ __global__ __launch_bounds__(DC_THREADS, 2) void lla_decode_moments3_kernel(
     __shared__ double sh[DC_THREADS];
     __shared__ double kbd[D];
     __shared__ float kbf[D];
-    __shared__ float svs[4 * D];
+    __shared__ float svs[M3_KG * D];
     __shared__ float swl[M3_SUB];
     const int tid = threadIdx.x;
     const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint16_t* raw = reinterpret_cast<uint16_t*>(lds + 2 * m3_buf_bytes<D>());
+    uint16_t* raw = reinterpret_cast<uint16_t*>(lds + m3_buf_bytes<D>());
     const int bh = static_cast<int>(blockIdx.x) / S, sidx = static_cast<int>(blockIdx.x) % S;
     const int j0 = sidx * C;
     const int jend = min(L, j0 + C);
@@ -804,7 +808,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void lla_decode_moments3_kernel(
     if (tid < D) {
         float t = 0.0f;
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) t += svs[kg * D + tid];
+        for (int kg = 0; kg < M3_KG; ++kg) t += svs[kg * D + tid];
         mo[MB::NT * 256 + tid] = t;
     }
 }
