@@ -249,8 +249,8 @@ def lla_decode_chunks(BH, L):
     return -(-L // c)
 
 
-def lla_decode_three_part(w):
-    """Whether the LLA decode moments run from three-part bf16 operands (bf16 inputs, caches
+def lla_decode_split_operands(w):
+    """Whether the LLA decode moments run from split bf16 operands (bf16 inputs, caches
     of at least 2d positions, d <= 64): HBM-bound then (the K, V read and the executed
     matrix-core work take about the same time at peak); otherwise fp32 or fp64 matrix cores."""
     return w.dtype == "bf16" and w.L >= 2 * w.d and w.d <= 64
@@ -266,7 +266,7 @@ def decode_kernel_units(name, w, elt):
         # reads the keys and the query
         return B * H * L * d * elt + B * H * d * elt, "B"
     if name == "lla_decode_moments_kernel":
-        if lla_decode_three_part(w):
+        if lla_decode_split_operands(w):
             # reads K and V once and the stats pass's scores
             return 2 * B * H * L * d * elt + B * H * L * 4, "B"
         return lla_moment_flops(B, H, L, d), "flop"

@@ -300,17 +300,21 @@ hipError_t launch_parallax_decode(const Problem& p, void* workspace) {
 // =======================================================================================
 // LLA decode step: b = vbar - C_vk (C_kk + lambda e^{-m} I)^{-1} (kbar - q) over each head's
 // whole cache -- the LLA row of the "Parallax" blog post, section 2 "Canonical Formulation"
-// (centred form of its Appendix E), for the newest position.  Three launches:
-//   lla_decode_stats_kernel    per chunk: scores x = q.k log2e/h, chunk max m_c,
+// (centred form of its Appendix E), for the newest position.  Launches:
+//   lla_decode_stats_kernel    per chunk: scores x = q.k log2e/h (kept per key when the
+//                              moments use split operands), chunk max m_c,
 //                              omega_c = sum 2^(x - m_c), S_k,c = sum 2^(x - m_c) k;
 //   lla_decode_moments_kernel  per chunk: the head's max M, omega and kbar from the chunk
 //                              statistics; weights w = 2^(x - M); 64-key sub-tiles staged
 //                              in LDS feature-major as R_k = sqrt(w)(k - kbar), R_v = sqrt(w) v;
 //                              C_kk (upper 16x16 blocks) += R_k R_k^T and C_vk += R_v R_k^T on
-//                              the matrix cores (16x16x4, fp32 or fp64); S_v = sum w v;
-//   lla_decode_solve_kernel    per head: sums the chunks' moments, adds the ridge
-//                              lambda 2^-M to the diagonal, LDL^T in LDS (fp64), solves for y
-//                              and writes b = S_v/omega - C_vk y.
+//                              the matrix cores (16x16x4, fp32 or fp64); S_v = sum w v; for
+//                              bf16 inputs with d <= 64, lla_decode_moments_split_kernel
+//                              instead (bf16 split operands, below);
+//   lla_decode_reduce_kernel   (several chunks per head) the chunks' moments summed in fp64;
+//   lla_decode_solve_kernel    per head: adds the ridge lambda 2^-M to the diagonal,
+//                              Gauss-Jordan in registers (fp64), solves for y and writes
+//                              b = S_v/omega - C_vk y.
 // C_vk needs no centring of v: sum_j w_j (k_j - kbar) = 0 makes sum_j w_j vbar (k_j - kbar)^T
 // vanish.  Moments in fp64 for fp32 inputs and for caches shorter than 2d (where the ridge
 // alone conditions the solve); in fp32 otherwise.
@@ -603,42 +607,48 @@ __global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
     }
 }
 
-// ---- Moments from bf16 three-part operands (bf16 inputs, fp32 moments, d <= 64).
+// ---- Moments from split bf16 operands (bf16 inputs, fp32 moments, d <= 64).
 // R_k = sqrt(w) (k - kbar) and R_v = sqrt(w) v are formed in fp32 from the stats pass's
-// scores and split as r = h + m + l (each bf16; 24 significant bits together); a 16x16
-// block then takes the six products down to 2^-16 of the leading one -- hh, hm, mh, hl, lh,
-// mm -- on v_mfma_f32_16x16x32_bf16 (32 keys per instruction): the dropped terms are below
-// 2^-24 relative, the level of the fp32 accumulation, at about 2.7 times the fp32 MFMA rate.
-// Staging per sub-tile of 32 keys: 16-byte loads of the rows (in flight during the current
-// sub-tile's MFMAs) go to a row-major LDS tile with one weight per key; then thread ->
-// (K or V, feature f, 8 consecutive keys) forms the three parts and writes each with one
-// 16-byte store into the feature-major operand image (two images, one per parity).
+// scores and split into M3_PARTS bf16 parts, r = h + l (16 significant bits together); a
+// 16x16 block then takes the products hh, hl, lh on v_mfma_f32_16x16x32_bf16 (32 keys per
+// instruction): the dropped terms are below 2^-16 of each product (with three parts and six
+// products, 2^-24; measured 1.3 times slower for errors that the two-part form already keeps
+// near 1e-5).  Staging per sub-tile of 64 keys: 16-byte loads of the rows (in flight during
+// the current sub-tile's MFMAs) go to a row-major LDS tile with one weight per key; then
+// thread -> (K or V, feature f, 8 consecutive keys) forms the parts and writes each with one
+// 16-byte store into the feature-major operand image.
 typedef __bf16 bf16x8d __attribute__((ext_vector_type(8)));
+constexpr int M3_PARTS = 2;         // bf16 parts per operand (2: hi + lo; 3: hi + mid + lo)
 constexpr int M3_SUB = 64;          // keys per sub-tile: two 32-key MFMA steps
 constexpr int M3_KG = M3_SUB / 8;   // groups of 8 keys per sub-tile
 constexpr int M3_LD = M3_SUB + 8;   // feature row of a part (halves): 144 bytes
 
 template <int D>
-constexpr int m3_buf_bytes() { return 3 * 2 * D * M3_LD * 2; }   // [part][K, V][feature][M3_LD]
+constexpr int msp_buf_bytes() { return M3_PARTS * 2 * D * M3_LD * 2; }   // [part][K, V][feature][M3_LD]
 
 __device__ __forceinline__ float4x mfma_bf(bf16x8d a, bf16x8d b, float4x c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// c += a b for a, b given as three bf16 parts each, smallest products first.
-__device__ __forceinline__ float4x mfma6(const bf16x8d (&a)[3], const bf16x8d (&b)[3], float4x c) {
-    c = mfma_bf(a[1], b[1], c);
-    c = mfma_bf(a[2], b[0], c);
-    c = mfma_bf(a[0], b[2], c);
+// c += a b for a, b given as M3_PARTS bf16 parts each, smallest products first: with three
+// parts hh, hm, mh, hl, lh, mm (dropped terms below 2^-24 relative), with two hh, hl, lh
+// (dropped terms below 2^-16).
+__device__ __forceinline__ float4x mfma_split(const bf16x8d (&a)[M3_PARTS], const bf16x8d (&b)[M3_PARTS], float4x c) {
+    if constexpr (M3_PARTS == 3) {
+        c = mfma_bf(a[1], b[1], c);
+        c = mfma_bf(a[2], b[0], c);
+        c = mfma_bf(a[0], b[2], c);
+    }
     c = mfma_bf(a[1], b[0], c);
     c = mfma_bf(a[0], b[1], c);
     return mfma_bf(a[0], b[0], c);
 }
 
 template <int D, int B0, int N, int... Bs>
-__device__ __forceinline__ void mfma3_blocks(const bf16x8d (&kop)[D / 16][3], const bf16x8d (&vop)[D / 16][3],
+__device__ __forceinline__ void mfma_split_blocks(const bf16x8d (&kop)[D / 16][M3_PARTS],
+                                             const bf16x8d (&vop)[D / 16][M3_PARTS],
                                              float4x (&acc)[N], std::integer_sequence<int, Bs...>) {
     using MB = MomBlocks<D>;
-    ((acc[Bs] = mfma6(std::integral_constant<int, MB::kind(B0 + Bs)>::value == 0
+    ((acc[Bs] = mfma_split(std::integral_constant<int, MB::kind(B0 + Bs)>::value == 0
                           ? kop[std::integral_constant<int, MB::I(B0 + Bs)>::value]
                           : vop[std::integral_constant<int, MB::I(B0 + Bs)>::value],
                       kop[std::integral_constant<int, MB::J(B0 + Bs)>::value], acc[Bs])),
@@ -647,12 +657,12 @@ __device__ __forceinline__ void mfma3_blocks(const bf16x8d (&kop)[D / 16][3], co
 
 // Row-major staging tile of one sub-tile (bf16 as given): [K, V][key][D + 8].
 template <int D>
-constexpr int m3_raw_bytes() { return 2 * M3_SUB * (D + 8) * 2; }
+constexpr int msp_raw_bytes() { return 2 * M3_SUB * (D + 8) * 2; }
 template <int D>
-constexpr int m3_smem_bytes() { return m3_buf_bytes<D>() + m3_raw_bytes<D>(); }
+constexpr int msp_smem_bytes() { return msp_buf_bytes<D>() + msp_raw_bytes<D>(); }
 
 template <typename TIn, int D, int W>
-__device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const TIn* __restrict__ vh,
+__device__ __forceinline__ void moments_split_wave(const TIn* __restrict__ kh, const TIn* __restrict__ vh,
                                               const float* __restrict__ xh, const float* kbf, unsigned char* img,
                                               uint16_t* raw, float* swl, float* svs, float Mf, int j0, int jend,
                                               int tid, float* __restrict__ mo) {
@@ -668,7 +678,7 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
     constexpr int VB = B0 > MB::NKK ? B0 : MB::NKK;
     constexpr int VI0 = B1 > MB::NKK ? MB::I(VB) : 0;
     constexpr int VI1 = B1 > MB::NKK ? MB::I(B1 - 1) : -1;
-    static_assert(sizeof(TIn) == 2, "three-part moments take bf16 inputs");
+    static_assert(sizeof(TIn) == 2, "split-operand moments take bf16 inputs");
     const int lane = tid & 63, g = lane >> 4, c = lane & 15;
     float4x acc[NA];
 #pragma unroll
@@ -691,7 +701,7 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
         }
         xpre = tid < M3_SUB && js + tid < jend ? xh[js + tid] : -INFINITY;
     };
-    // raw pieces and weights to LDS, then (after a barrier) the three parts of R_k, R_v
+    // raw pieces and weights to LDS, then (after a barrier) the parts of R_k, R_v
     auto stash = [&](unsigned char* buf) {
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
@@ -709,24 +719,23 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
             if (pp < PAIRS) {
                 const int arr = pp / (M3_KG * D), rem = pp % (M3_KG * D), f = rem % D, kg = rem / D;
                 const float sub = arr == 0 ? kbf[f] : 0.0f;
-                bf16x8d ph, pm, pl;
+                bf16x8d part[M3_PARTS];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const float sw = swl[8 * kg + t];
                     const float x = __uint_as_float(static_cast<uint32_t>(raw[(arr * M3_SUB + 8 * kg + t) * RLD + f]) << 16);
-                    const float r = sw * (x - sub);
+                    float r = sw * (x - sub);
                     if (arr == 1) sv[e] = fmaf(sw * sw, x, sv[e]);
-                    const __bf16 h = static_cast<__bf16>(r);
-                    const float r1 = r - static_cast<float>(h);
-                    const __bf16 m = static_cast<__bf16>(r1);
-                    ph[t] = h;
-                    pm[t] = m;
-                    pl[t] = static_cast<__bf16>(r1 - static_cast<float>(m));
+#pragma unroll
+                    for (int lv = 0; lv < M3_PARTS; ++lv) {
+                        const __bf16 hp = static_cast<__bf16>(r);
+                        part[lv][t] = hp;
+                        r -= static_cast<float>(hp);
+                    }
                 }
                 unsigned char* row = buf + (arr * D + f) * (M3_LD * 2) + 16 * kg;
-                *reinterpret_cast<bf16x8d*>(row) = ph;
-                *reinterpret_cast<bf16x8d*>(row + 2 * D * M3_LD * 2) = pm;
-                *reinterpret_cast<bf16x8d*>(row + 4 * D * M3_LD * 2) = pl;
+#pragma unroll
+                for (int lv = 0; lv < M3_PARTS; ++lv) *reinterpret_cast<bf16x8d*>(row + lv * 2 * D * M3_LD * 2) = part[lv];
             }
         }
     };
@@ -741,20 +750,20 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
         if constexpr (B1 > B0) {
 #pragma unroll
             for (int ks = 0; ks < M3_SUB / 32; ++ks) {
-                bf16x8d kop[NB][3], vop[NB][3];
+                bf16x8d kop[NB][M3_PARTS], vop[NB][M3_PARTS];
 #pragma unroll
                 for (int R = 0; R < NB; ++R)
 #pragma unroll
-                    for (int lv = 0; lv < 3; ++lv)
+                    for (int lv = 0; lv < M3_PARTS; ++lv)
                         kop[R][lv] = *reinterpret_cast<const bf16x8d*>(
                             img + ((2 * lv) * D + 16 * R + c) * (M3_LD * 2) + 64 * ks + 16 * g);
 #pragma unroll
                 for (int R = VI0; R <= VI1; ++R)
 #pragma unroll
-                    for (int lv = 0; lv < 3; ++lv)
+                    for (int lv = 0; lv < M3_PARTS; ++lv)
                         vop[R][lv] = *reinterpret_cast<const bf16x8d*>(
                             img + ((2 * lv + 1) * D + 16 * R + c) * (M3_LD * 2) + 64 * ks + 16 * g);
-                mfma3_blocks<D, B0>(kop, vop, acc, std::make_integer_sequence<int, B1 - B0>{});
+                mfma_split_blocks<D, B0>(kop, vop, acc, std::make_integer_sequence<int, B1 - B0>{});
             }
         }
         if (t + 1 < nsub) stash(img);
@@ -772,11 +781,11 @@ __device__ __forceinline__ void moments3_wave(const TIn* __restrict__ kh, const 
 }
 
 template <typename TIn, int D>
-__global__ __launch_bounds__(DC_THREADS, 2) void lla_decode_moments3_kernel(
+__global__ __launch_bounds__(DC_THREADS, 2) void lla_decode_moments_split_kernel(
     const TIn* __restrict__ k, const TIn* __restrict__ v, const double* __restrict__ stats,
     const float* __restrict__ xsc, float* __restrict__ mom, int L, int S, int C) {
     using MB = MomBlocks<D>;
-    static_assert(D <= 64, "three-part moments serve d <= 64");
+    static_assert(D <= 64, "split-operand moments serve d <= 64");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ double sh[DC_THREADS];
     __shared__ double kbd[D];
@@ -785,7 +794,7 @@ __global__ __launch_bounds__(DC_THREADS, 2) void lla_decode_moments3_kernel(
     __shared__ float swl[M3_SUB];
     const int tid = threadIdx.x;
     const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint16_t* raw = reinterpret_cast<uint16_t*>(lds + m3_buf_bytes<D>());
+    uint16_t* raw = reinterpret_cast<uint16_t*>(lds + msp_buf_bytes<D>());
     const int bh = static_cast<int>(blockIdx.x) / S, sidx = static_cast<int>(blockIdx.x) % S;
     const int j0 = sidx * C;
     const int jend = min(L, j0 + C);
@@ -799,10 +808,10 @@ __global__ __launch_bounds__(DC_THREADS, 2) void lla_decode_moments3_kernel(
     const float* xh = xsc + static_cast<int64_t>(bh) * L;
     float* mo = mom + (static_cast<int64_t>(bh) * S + sidx) * (MB::NT * 256 + D);
     switch (wu) {
-        case 0: moments3_wave<TIn, D, 0>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
-        case 1: moments3_wave<TIn, D, 1>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
-        case 2: moments3_wave<TIn, D, 2>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
-        default: moments3_wave<TIn, D, 3>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+        case 0: moments_split_wave<TIn, D, 0>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+        case 1: moments_split_wave<TIn, D, 1>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+        case 2: moments_split_wave<TIn, D, 2>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+        default: moments_split_wave<TIn, D, 3>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
     }
     __syncthreads();
     if (tid < D) {
@@ -937,16 +946,16 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_solve_kernel(
 struct LlaDecodeLayout {
     int64_t stats_bytes, score_bytes, mom_bytes, sum_bytes;
 };
-// fp32 moments from three-part bf16 operands (they read the stats pass's scores): bf16 inputs
+// fp32 moments from split bf16 operands (they read the stats pass's scores): bf16 inputs
 // with fp32 moments and d <= 64.
-bool lla_decode_three_part(int dtype, int64_t L, int64_t d) { return !lla_decode_fp64(dtype, L, d) && d <= 64; }
+bool lla_decode_split_operands(int dtype, int64_t L, int64_t d) { return !lla_decode_fp64(dtype, L, d) && d <= 64; }
 LlaDecodeLayout lla_decode_layout(int64_t BH, int64_t L, int64_t d, int dtype) {
     int S = 1, C = 1;
     lla_decode_split(BH, L, &S, &C);
     const int64_t nb = d / 16, e = (nb * (nb + 1) / 2 + nb * nb) * 256 + d;
     const int64_t ta = lla_decode_fp64(dtype, L, d) ? 8 : 4;
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
-    return {up(BH * S * (2 + d) * 8), lla_decode_three_part(dtype, L, d) ? up(BH * L * 4) : 0, up(BH * S * e * ta),
+    return {up(BH * S * (2 + d) * 8), lla_decode_split_operands(dtype, L, d) ? up(BH * L * 4) : 0, up(BH * S * e * ta),
             S > 1 ? BH * e * 8 : 0};
 }
 
@@ -970,8 +979,8 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
                                            hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
         if constexpr (D <= 64 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value)
             if (e == hipSuccess)
-                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments3_kernel<TIn, D>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, m3_smem_bytes<D>());
+                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_split_kernel<TIn, D>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, msp_smem_bytes<D>());
         return e;
     }();
     hipError_t err = attr_err;
@@ -986,7 +995,7 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
     bool launched = false;
     if constexpr (D <= 64 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value) {
         if (xsc != nullptr) {
-            lla_decode_moments3_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), m3_smem_bytes<D>(), p.stream>>>(
+            lla_decode_moments_split_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), msp_smem_bytes<D>(), p.stream>>>(
                 static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, xsc, mom, static_cast<int>(p.n),
                 S, C);
             launched = true;
