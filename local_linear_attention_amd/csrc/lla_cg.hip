@@ -20,6 +20,7 @@
 // The same centred system as the direct fp64 path (lla_exact.hip), so both give the LLA
 // intercept; this one keeps only d-vectors per query (no d x d state) at the price of one
 // prefix pass per iteration.
+#include "lla_device.h"
 #include "lla_internal.h"
 
 #include <math.h>
@@ -27,10 +28,6 @@
 namespace lla {
 namespace {
 
-__device__ __forceinline__ double cg_load(const float* p, int64_t idx) { return static_cast<double>(p[idx]); }
-__device__ __forceinline__ double cg_load(const uint16_t* p, int64_t idx) {
-    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[idx]) << 16));
-}
 
 constexpr int CG_NT = 256;
 constexpr int kCgMaxIterFactor = 4;   // at most 4d iterations (d suffice in exact arithmetic)
@@ -65,7 +62,7 @@ __global__ __launch_bounds__(CG_NT) void lla_cg_kernel(const TIn* __restrict__ q
     const int cnt = i + 1;
     const int fa = tid % D, kl = tid / D;
 
-    for (int e = tid; e < D; e += NT) qs[e] = cg_load(q + base, static_cast<int64_t>(i) * D + e);
+    for (int e = tid; e < D; e += NT) qs[e] = load_f64(q + base, static_cast<int64_t>(i) * D + e);
 
     auto block_sum = [&](double x, bool is_max) {
 #pragma unroll
@@ -98,8 +95,8 @@ __global__ __launch_bounds__(CG_NT) void lla_cg_kernel(const TIn* __restrict__ q
             double kk = 0.0, vv = 0.0;
             if (jj < nk) {
                 const int64_t off = static_cast<int64_t>(c0 + jj) * D + a;
-                kk = cg_load(kh, off);
-                if (with_v) vv = cg_load(vh, off);
+                kk = load_f64(kh, off);
+                if (with_v) vv = load_f64(vh, off);
             }
             Ks[jj * LD + a] = kk;
             if (with_v) Vs[jj * LD + a] = vv;

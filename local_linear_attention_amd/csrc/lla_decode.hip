@@ -24,6 +24,7 @@
 //                               (the blog's Appendix C, item 3, with a separate launch).
 // The probe scores are taken relative to rho . q (t = rho . (k - q)): a constant shift of
 // the probe scores cancels in the merge, and this one is the same in every chunk of a head.
+#include "lla_device.h"
 #include "lla_internal.h"
 
 #include <math.h>
@@ -51,10 +52,6 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
     for (int e = 0; e < 8; ++e) x[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
 }
 
-__device__ __forceinline__ double load_elem_d(const float* p, int64_t i) { return static_cast<double>(p[i]); }
-__device__ __forceinline__ double load_elem_d(const uint16_t* p, int64_t i) {
-    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[i]) << 16));
-}
 
 // fp64 moments for fp32 inputs and for caches shorter than 2d, fp32 moments otherwise.
 bool lla_decode_fp64(int dtype, int64_t L, int64_t d) { return dtype == 0 || L < 2 * d; }
@@ -890,7 +887,7 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_solve_kernel(
             if (i == j) dmax = fmax(dmax, a[ia][ib]);
         }
     const double thr = lambda > 0.0 ? 0.0 : 1e-12 * block_reduce_d(dmax, true, sh);
-    double z = tid < D ? kbd[tid] - load_elem_d(q, static_cast<int64_t>(bh) * D + tid) : 0.0;
+    double z = tid < D ? kbd[tid] - load_f64(q, static_cast<int64_t>(bh) * D + tid) : 0.0;
     for (int pb = 0; pb < 16; ++pb) {
 #pragma unroll
         for (int pp = 0; pp < TS; ++pp) {

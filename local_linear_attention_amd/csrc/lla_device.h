@@ -44,6 +44,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
+// Element idx of an fp32 or bf16 (raw bits) array, exactly, as fp64.
+__device__ __forceinline__ double load_f64(const float* p, int64_t idx) { return static_cast<double>(p[idx]); }
+__device__ __forceinline__ double load_f64(const uint16_t* p, int64_t idx) {
+    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[idx]) << 16));
+}
+
 __device__ __forceinline__ float4v mfma_bf16(bf16x8 a, bf16x8 b, float4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

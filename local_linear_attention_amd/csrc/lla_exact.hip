@@ -22,19 +22,13 @@
 // Thread layout: a TR x TC grid; thread (tr, tc) owns rows a = tr + TR*r (r < D/TR) and
 // columns b = tc + TC*c (c < D/TC) of A and R in registers.  K/V chunks are staged in
 // LDS; the solve broadcasts one pivot column and one right-hand-side row per step.
+#include "lla_device.h"
 #include "lla_internal.h"
 
 #include <math.h>
 
 namespace lla {
 namespace {
-
-__device__ __forceinline__ double load_elem(const float* p, int64_t idx) {
-    return static_cast<double>(p[idx]);
-}
-__device__ __forceinline__ double load_elem(const uint16_t* p, int64_t idx) {
-    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[idx]) << 16));
-}
 
 template <int D> struct ExactCfg;
 template <> struct ExactCfg<16> { static constexpr int TR = 16, TC = 16; };
@@ -76,7 +70,7 @@ void lla_exact_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
     const TIn* vh = v + base;
     const int cnt = i + 1;
 
-    for (int e = tid; e < D; e += NT) qs[e] = load_elem(q + base, static_cast<int64_t>(i) * D + e);
+    for (int e = tid; e < D; e += NT) qs[e] = load_f64(q + base, static_cast<int64_t>(i) * D + e);
 
     // Stage keys [c0, c0 + nk) (and values) as fp64; rows past the prefix are zero.
     auto load_chunk = [&](int c0, int nk, bool with_v) {
@@ -85,8 +79,8 @@ void lla_exact_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
             double kk = 0.0, vv = 0.0;
             if (jj < nk) {
                 const int64_t off = static_cast<int64_t>(c0 + jj) * D + a;
-                kk = load_elem(kh, off);
-                if (with_v) vv = load_elem(vh, off);
+                kk = load_f64(kh, off);
+                if (with_v) vv = load_f64(vh, off);
             }
             Ks[jj * LD + a] = kk;
             if (with_v) Vs[jj * LD + a] = vv;

@@ -427,10 +427,6 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
 // the prefix in chunks of 256 keys: (0) the row max of the scores; (1) omega and the
 // weighted key and value means; (2) u_j = w_j rho . (k_j - kbar) and
 // o = vbar - sum_j u_j (v_j - vbar) / omega  (= vbar - Sigma_KV rho).
-__device__ __forceinline__ double px_load(const float* p, int64_t idx) { return static_cast<double>(p[idx]); }
-__device__ __forceinline__ double px_load(const uint16_t* p, int64_t idx) {
-    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[idx]) << 16));
-}
 
 constexpr int G_NT = 256;
 constexpr int G_CHK = 256;
@@ -449,13 +445,13 @@ __global__ __launch_bounds__(G_NT) void lla_parallax_exact_kernel(
     const int64_t base = static_cast<int64_t>(bh) * n * D;
     const int cnt = i + 1;
     for (int e = tid; e < D; e += G_NT) {
-        qs[e] = px_load(q + base, static_cast<int64_t>(i) * D + e);
-        rs[e] = px_load(rho + base, static_cast<int64_t>(i) * D + e);
+        qs[e] = load_f64(q + base, static_cast<int64_t>(i) * D + e);
+        rs[e] = load_f64(rho + base, static_cast<int64_t>(i) * D + e);
     }
     __syncthreads();
     auto score = [&](int j) {
         double s = 0.0;
-        for (int a = 0; a < D; ++a) s += qs[a] * px_load(k + base, static_cast<int64_t>(j) * D + a);
+        for (int a = 0; a < D; ++a) s += qs[a] * load_f64(k + base, static_cast<int64_t>(j) * D + a);
         return s * inv_h;
     };
     auto block_reduce = [&](double x, bool is_max) {
@@ -485,8 +481,8 @@ __global__ __launch_bounds__(G_NT) void lla_parallax_exact_kernel(
         for (int jj = kl; jj < nk; jj += KL) {
             const double wj = ws[jj];
             const int64_t off = static_cast<int64_t>(c0 + jj) * D + fa;
-            acc_k += wj * px_load(k + base, off);
-            acc_v += wj * px_load(v + base, off);
+            acc_k += wj * load_f64(k + base, off);
+            acc_v += wj * load_f64(v + base, off);
         }
         if (tid < nk) acc_w += ws[tid];
         __syncthreads();
@@ -516,12 +512,12 @@ __global__ __launch_bounds__(G_NT) void lla_parallax_exact_kernel(
         if (tid < nk) {
             const int j = c0 + tid;
             double tj = 0.0;
-            for (int a = 0; a < D; ++a) tj += rs[a] * (px_load(k + base, static_cast<int64_t>(j) * D + a) - kbar[a]);
+            for (int a = 0; a < D; ++a) tj += rs[a] * (load_f64(k + base, static_cast<int64_t>(j) * D + a) - kbar[a]);
             ws[tid] = exp(score(j) - m) * tj;
         }
         __syncthreads();
         for (int jj = kl; jj < nk; jj += KL)
-            acc_o += ws[jj] * (px_load(v + base, static_cast<int64_t>(c0 + jj) * D + fa) - vbar[fa]);
+            acc_o += ws[jj] * (load_f64(v + base, static_cast<int64_t>(c0 + jj) * D + fa) - vbar[fa]);
         __syncthreads();
     }
     red[tid] = acc_o;

@@ -419,10 +419,6 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_qr_kernel(
 
 // ---------------------------------------------------------------------------------------
 // fp64 path.
-__device__ __forceinline__ double ld64(const float* p, int64_t i) { return static_cast<double>(p[i]); }
-__device__ __forceinline__ double ld64(const uint16_t* p, int64_t i) {
-    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[i]) << 16));
-}
 
 constexpr int EB_NT = 256;
 constexpr int EB_CHK = 256;
@@ -472,15 +468,15 @@ __global__ __launch_bounds__(EB_NT) void lla_parallax_bwd_exact_rows_kernel(
     const int64_t base = static_cast<int64_t>(bh) * n * D;
     const int cnt = i + 1;
     for (int e = tid; e < D; e += EB_NT) {
-        qs[e] = ld64(q + base, static_cast<int64_t>(i) * D + e);
-        rs[e] = ld64(rho + base, static_cast<int64_t>(i) * D + e);
-        os[e] = ld64(dout + base, static_cast<int64_t>(i) * D + e);
+        qs[e] = load_f64(q + base, static_cast<int64_t>(i) * D + e);
+        rs[e] = load_f64(rho + base, static_cast<int64_t>(i) * D + e);
+        os[e] = load_f64(dout + base, static_cast<int64_t>(i) * D + e);
     }
     __syncthreads();
     auto dot = [&](const double* a, const TIn* rowp, int j) {
         double s = 0.0;
 #pragma unroll 8
-        for (int e = 0; e < D; ++e) s += a[e] * ld64(rowp + base, static_cast<int64_t>(j) * D + e);
+        for (int e = 0; e < D; ++e) s += a[e] * load_f64(rowp + base, static_cast<int64_t>(j) * D + e);
         return s;
     };
     double mloc = -INFINITY;
@@ -494,8 +490,8 @@ __global__ __launch_bounds__(EB_NT) void lla_parallax_bwd_exact_rows_kernel(
         __syncthreads();
         for (int jj = kl; jj < nk; jj += KL) {
             const int64_t off = static_cast<int64_t>(c0 + jj) * D + fa;
-            ak += c1[jj] * ld64(k + base, off);
-            av += c1[jj] * ld64(v + base, off);
+            ak += c1[jj] * load_f64(k + base, off);
+            av += c1[jj] * load_f64(v + base, off);
         }
         if (tid < nk) aw += c1[tid];
         __syncthreads();
@@ -534,7 +530,7 @@ __global__ __launch_bounds__(EB_NT) void lla_parallax_bwd_exact_rows_kernel(
         }
         __syncthreads();
         for (int jj = kl; jj < nk; jj += KL) {
-            const double kv = ld64(k + base, static_cast<int64_t>(c0 + jj) * D + fa);
+            const double kv = load_f64(k + base, static_cast<int64_t>(c0 + jj) * D + fa);
             aq += c1[jj] * kv;
             ar += c2[jj] * kv;
         }
@@ -571,14 +567,14 @@ __global__ __launch_bounds__(EB_NT) void lla_parallax_bwd_exact_cols_kernel(
     const int bh = static_cast<int>(blockIdx.x % BH);
     const int64_t base = static_cast<int64_t>(bh) * n * D;
     for (int e = tid; e < D; e += EB_NT) {
-        ks[e] = ld64(k + base, static_cast<int64_t>(j) * D + e);
-        vs[e] = ld64(v + base, static_cast<int64_t>(j) * D + e);
+        ks[e] = load_f64(k + base, static_cast<int64_t>(j) * D + e);
+        vs[e] = load_f64(v + base, static_cast<int64_t>(j) * D + e);
     }
     __syncthreads();
     auto dot = [&](const double* a, const TIn* rowp, int i) {
         double s = 0.0;
 #pragma unroll 8
-        for (int e = 0; e < D; ++e) s += a[e] * ld64(rowp + base, static_cast<int64_t>(i) * D + e);
+        for (int e = 0; e < D; ++e) s += a[e] * load_f64(rowp + base, static_cast<int64_t>(i) * D + e);
         return s;
     };
     const int fa = tid % D, kl = tid / D;
@@ -598,9 +594,9 @@ __global__ __launch_bounds__(EB_NT) void lla_parallax_bwd_exact_cols_kernel(
         __syncthreads();
         for (int ii = kl; ii < nr; ii += KL) {
             const int64_t off = static_cast<int64_t>(c0 + ii) * D + fa;
-            akq += cs[ii] * ld64(q + base, off);
-            akr += cu[ii] * ld64(rho + base, off);
-            avd += ca[ii] * ld64(dout + base, off);
+            akq += cs[ii] * load_f64(q + base, off);
+            akr += cu[ii] * load_f64(rho + base, off);
+            avd += ca[ii] * load_f64(dout + base, off);
         }
         __syncthreads();
     }
