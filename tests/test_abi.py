@@ -191,6 +191,24 @@ def test_parallax_unknown_or_uncovered_path_is_rejected():
     assert call_parallax(lib, path=7) == 4
     assert call_parallax(lib, path=2, d=32) == 4      # the matrix-core path is d = 64 only
     assert call_parallax(lib, path=2, dtype=0) == 4   # and bf16 only
+    assert call_parallax(lib, path=3) == 4            # CG solves the LLA system; Parallax has none
+
+
+def test_cg_path_is_an_lla_path_without_scratch():
+    from local_linear_attention_amd import lla
+    lib = _lib()
+    for dt in ("f32", "bf16"):
+        for d in (16, 32, 64, 128):
+            assert lla.lla_path_available("cg", dt, d)
+            assert lla.lla_workspace_size(2, 3, 500, d, dt, "cg") == 0
+    assert not lla.lla_path_available("cg", "bf16", 48)
+    assert not lla.lla_parallax_path_available("cg", "bf16", 64)
+    # validation happens before any launch on the CG path too
+    assert call(lib, path=3, q=0) == 1
+    assert call(lib, path=3, n=0) == 2
+    assert call(lib, path=3, lam=-1.0) == 3
+    assert call(lib, path=3, d=48) == 4
+    assert call(lib, path=3, out=Q + 16) == 7
 
 
 def parallax_workspace_bytes(BH, n):
