@@ -251,9 +251,9 @@ def lla_decode_chunks(BH, L):
 
 def lla_decode_split_operands(w):
     """Whether the LLA decode moments run from split bf16 operands (bf16 inputs, caches
-    of at least 2d positions, d <= 64): HBM-bound then (the K, V read and the executed
-    matrix-core work take about the same time at peak); otherwise fp32 or fp64 matrix cores."""
-    return w.dtype == "bf16" and w.L >= 2 * w.d and w.d <= 64
+    of at least 2d positions): HBM-bound then (the executed matrix-core work takes less time
+    at peak than the K, V read); otherwise fp64 matrix cores."""
+    return w.dtype == "bf16" and w.L >= 2 * w.d
 
 
 def decode_kernel_units(name, w, elt):

@@ -306,7 +306,7 @@ hipError_t launch_parallax_decode(const Problem& p, void* workspace) {
 //                              in LDS feature-major as R_k = sqrt(w)(k - kbar), R_v = sqrt(w) v;
 //                              C_kk (upper 16x16 blocks) += R_k R_k^T and C_vk += R_v R_k^T on
 //                              the matrix cores (16x16x4, fp32 or fp64); S_v = sum w v; for
-//                              bf16 inputs with d <= 64, lla_decode_moments_split_kernel
+//                              bf16 inputs, lla_decode_moments_split_kernel
 //                              instead (bf16 split operands, below);
 //   lla_decode_reduce_kernel   (several chunks per head) the chunks' moments summed in fp64;
 //   lla_decode_solve_kernel    per head: adds the ridge lambda 2^-M to the diagonal,
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
     }
 }
 
-// ---- Moments from split bf16 operands (bf16 inputs, fp32 moments, d <= 64).
+// ---- Moments from split bf16 operands (bf16 inputs, fp32 moments; one block per CU at d = 128).
 // R_k = sqrt(w) (k - kbar) and R_v = sqrt(w) v are formed in fp32 from the stats pass's
 // scores and split into M3_PARTS bf16 parts, r = h + l (16 significant bits together); a
 // 16x16 block then takes the products hh, hl, lh on v_mfma_f32_16x16x32_bf16 (32 keys per
@@ -778,11 +778,11 @@ __device__ __forceinline__ void moments_split_wave(const TIn* __restrict__ kh, c
 }
 
 template <typename TIn, int D>
-__global__ __launch_bounds__(DC_THREADS, 2) void lla_decode_moments_split_kernel(
+__global__ __launch_bounds__(DC_THREADS, D <= 64 ? 2 : 1) void lla_decode_moments_split_kernel(
     const TIn* __restrict__ k, const TIn* __restrict__ v, const double* __restrict__ stats,
     const float* __restrict__ xsc, float* __restrict__ mom, int L, int S, int C) {
     using MB = MomBlocks<D>;
-    static_assert(D <= 64, "split-operand moments serve d <= 64");
+    static_assert(D <= 128, "split-operand moments serve d <= 128");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ double sh[DC_THREADS];
     __shared__ double kbd[D];
@@ -944,8 +944,8 @@ struct LlaDecodeLayout {
     int64_t stats_bytes, score_bytes, mom_bytes, sum_bytes;
 };
 // fp32 moments from split bf16 operands (they read the stats pass's scores): bf16 inputs
-// with fp32 moments and d <= 64.
-bool lla_decode_split_operands(int dtype, int64_t L, int64_t d) { return !lla_decode_fp64(dtype, L, d) && d <= 64; }
+// with fp32 moments.
+bool lla_decode_split_operands(int dtype, int64_t L, int64_t d) { return !lla_decode_fp64(dtype, L, d) && d <= 128; }
 LlaDecodeLayout lla_decode_layout(int64_t BH, int64_t L, int64_t d, int dtype) {
     int S = 1, C = 1;
     lla_decode_split(BH, L, &S, &C);
@@ -974,7 +974,7 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
     static const hipError_t attr_err = [] {   // once per instantiation
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
-        if constexpr (D <= 64 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value)
+        if constexpr (D <= 128 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value)
             if (e == hipSuccess)
                 e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_split_kernel<TIn, D>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, msp_smem_bytes<D>());
@@ -990,7 +990,7 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla_decode_moments_kernel");
     bool launched = false;
-    if constexpr (D <= 64 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value) {
+    if constexpr (D <= 128 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value) {
         if (xsc != nullptr) {
             lla_decode_moments_split_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), msp_smem_bytes<D>(), p.stream>>>(
                 static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, xsc, mom, static_cast<int>(p.n),

@@ -333,7 +333,7 @@ def test_lla_decode_workspace_size():
         ta = 8 if (dt == "f32" or L < 2 * d) else 4
         e = nt * 256 + d
         stats = -(-(B * H * S * (2 + d) * 8) // 256) * 256
-        scores = -(-(B * H * L * 4) // 256) * 256 if (ta == 4 and d <= 64) else 0   # three-part moments
+        scores = -(-(B * H * L * 4) // 256) * 256 if ta == 4 else 0   # split-operand moments
         mom = -(-(B * H * S * e * ta) // 256) * 256
         summed = B * H * e * 8 if S > 1 else 0
         assert lla.lla_decode_workspace_size(B, H, L, d, dt) == stats + scores + mom + summed, (B, H, L, d)
