@@ -305,9 +305,10 @@ hipError_t launch_parallax_decode(const Problem& p, void* workspace) {
 //                              statistics; weights w = 2^(x - M); 64-key sub-tiles staged
 //                              in LDS feature-major as R_k = sqrt(w)(k - kbar), R_v = sqrt(w) v;
 //                              C_kk (upper 16x16 blocks) += R_k R_k^T and C_vk += R_v R_k^T on
-//                              the matrix cores (16x16x4, fp32 or fp64); S_v = sum w v; for
-//                              bf16 inputs, lla_decode_moments_split_kernel
-//                              instead (bf16 split operands, below);
+//                              the matrix cores (fp64 16x16x4); S_v = sum w v; for bf16 inputs
+//                              and caches of at least 2d positions
+//                              lla_decode_moments_split_kernel instead (fp32 moments from bf16
+//                              split operands, below);
 //   lla_decode_reduce_kernel   (several chunks per head) the chunks' moments summed in fp64;
 //   lla_decode_solve_kernel    per head: adds the ridge lambda 2^-M to the diagonal,
 //                              Gauss-Jordan in registers (fp64), solves for y and writes
@@ -321,19 +322,14 @@ typedef double double4v __attribute__((ext_vector_type(4)));
 typedef float float4x __attribute__((ext_vector_type(4)));
 
 template <typename TA> struct Acc4;
-template <> struct Acc4<float> { using type = float4x; };
 template <> struct Acc4<double> { using type = double4v; };
 
-__device__ __forceinline__ float4x mfma4(float a, float b, float4x c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ double4v mfma4(double a, double b, double4v c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
-// Row of the 16x16 output block held in register r of lane (g, c) (column c): the fp32
-// instruction places rows 4g + r, the fp64 one rows 4r + g.
+// Row of the 16x16 output block held in register r of lane (g, c) (column c): the fp64
+// instruction places rows 4r + g (the bf16 16x16x32 one of the split kernel, 4g + r).
 template <typename TA> __device__ __forceinline__ int acc_row(int g, int r);
-template <> __device__ __forceinline__ int acc_row<float>(int g, int r) { return 4 * g + r; }
 template <> __device__ __forceinline__ int acc_row<double>(int g, int r) { return 4 * r + g; }
 
 constexpr int LD_SUB = 64;             // keys per staged sub-tile
@@ -970,15 +966,17 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
     float* xsc = lay.score_bytes > 0 ? reinterpret_cast<float*>(ws + lay.stats_bytes) : nullptr;
     TA* mom = reinterpret_cast<TA*>(ws + lay.stats_bytes + lay.score_bytes);
     double* msum = reinterpret_cast<double*>(ws + lay.stats_bytes + lay.score_bytes + lay.mom_bytes);
-    static_assert(mom_smem_bytes<D, TA>() <= 150 * 1024, "LDS");
+    // TA = float: bf16 inputs, split-operand moments; TA = double: the fp64 moments kernel.
+    constexpr bool kSplit = std::is_same<TA, float>::value;
+    static_assert(!kSplit || std::is_same<TIn, uint16_t>::value, "split-operand moments take bf16 inputs");
+    static_assert(kSplit || mom_smem_bytes<D, TA>() <= 150 * 1024, "LDS");
     static const hipError_t attr_err = [] {   // once per instantiation
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
-        if constexpr (D <= 128 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value)
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_split_kernel<TIn, D>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, msp_smem_bytes<D>());
-        return e;
+        if constexpr (kSplit)
+            return hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_split_kernel<TIn, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, msp_smem_bytes<D>());
+        else
+            return hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
     }();
     hipError_t err = attr_err;
     if (err != hipSuccess) return err;
@@ -989,16 +987,10 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla_decode_moments_kernel");
-    bool launched = false;
-    if constexpr (D <= 128 && std::is_same<TA, float>::value && std::is_same<TIn, uint16_t>::value) {
-        if (xsc != nullptr) {
-            lla_decode_moments_split_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), msp_smem_bytes<D>(), p.stream>>>(
-                static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, xsc, mom, static_cast<int>(p.n),
-                S, C);
-            launched = true;
-        }
-    }
-    if (!launched)
+    if constexpr (kSplit)
+        lla_decode_moments_split_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), msp_smem_bytes<D>(), p.stream>>>(
+            static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, xsc, mom, static_cast<int>(p.n), S, C);
+    else
         lla_decode_moments_kernel<TIn, D, TA><<<dim3(blocks), dim3(DC_THREADS), mom_smem_bytes<D, TA>(), p.stream>>>(
             static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), stats, mom,
             static_cast<int>(p.n), S, C, sl2);
@@ -1025,8 +1017,9 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
 
 template <typename TIn, int D>
 hipError_t launch_lla_decode_p(const Problem& p, void* workspace) {
-    if (lla_decode_fp64(p.dtype, p.n, D)) return launch_lla_decode_t<TIn, D, double>(p, workspace);
-    return launch_lla_decode_t<TIn, D, float>(p, workspace);
+    if constexpr (std::is_same<TIn, uint16_t>::value)
+        if (!lla_decode_fp64(p.dtype, p.n, D)) return launch_lla_decode_t<TIn, D, float>(p, workspace);
+    return launch_lla_decode_t<TIn, D, double>(p, workspace);
 }
 
 template <typename TIn>
