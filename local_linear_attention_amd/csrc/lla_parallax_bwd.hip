@@ -45,6 +45,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace lla {
 namespace {
 
@@ -56,7 +58,7 @@ constexpr int T_LD = BT + 4;                    // feature-major bf16 row, halve
 constexpr int RM_BYTES = BT * R_LD * 2;         // 9216
 constexpr int TM_BYTES = FD * T_LD * 2;         // 8704
 // Query image: q, rho, dout row-major | q, rho, dout feature-major | row statistics
-// (lse, ubar, G, D) as one float4 per row.
+// (lse, 1 + ubar, G, D) as one float4 per row.
 constexpr int QI_Q = 0, QI_R = RM_BYTES, QI_D = 2 * RM_BYTES;
 constexpr int QI_QT = 3 * RM_BYTES, QI_RT = QI_QT + TM_BYTES, QI_DT = QI_RT + TM_BYTES;
 constexpr int QI_ST = QI_DT + TM_BYTES;
@@ -147,12 +149,17 @@ struct ImageCopy {
 
 // x as bf16 hi + lo (x - hi rounded again): about 16 significant bits together.
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 h = static_cast<__bf16>(x[e]);
-        hi[e] = h;
-        lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
+    for (int e = 0; e < 4; ++e) {   // two values per conversion
+        const f32x2 v = {x[2 * e], x[2 * e + 1]};
+        h[e] = __builtin_convertvector(v, bf16x2);
+        l[e] = __builtin_convertvector(v - __builtin_convertvector(h[e], f32x2), bf16x2);
     }
+    hi = bf16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+    lo = bf16x8{l[0][0], l[0][1], l[1][0], l[1][1], l[2][0], l[2][1], l[3][0], l[3][1]};
 }
 
 // 8 K-slots of a feature-major operand: rows (or keys) 4g .. 4g+3 and 16+4g .. 16+4g+3 of a
@@ -224,9 +231,9 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_kv_kernel(
                 U[rb] = mfma_bf16(r1, kb[1], mfma_bf16(r0, kb[0], zero));
                 Gm[rb] = mfma_bf16(d1, vb[1], mfma_bf16(d0, vb[0], zero));
             }
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-                float av[8], sv[8], uv[8];
+            // pair weights of rows 32 ch .. 32 ch + 31; the causal mask only where the tile
+            // reaches below the wave's last key
+            auto weights = [&](auto masked, int ch, float (&av)[8], float (&sv)[8], float (&uv)[8]) {
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
                     const int rb = 2 * ch + hb;
@@ -235,17 +242,23 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_kv_kernel(
                         const int il = 16 * rb + 4 * g + r;
                         const float4v st = *reinterpret_cast<const float4v*>(img + QI_ST + il * 16);
                         float p = __builtin_amdgcn_exp2f(fmaf(S[rb][r], sl2, -st[0]));
-                        p = i0 + il >= kc ? p : 0.0f;
+                        if constexpr (decltype(masked)::value) p = i0 + il >= kc ? p : 0.0f;
                         const float u = U[rb][r], gg = Gm[rb][r];
-                        const float t1 = 1.0f - u + st[1];
-                        const float a = p * t1;
-                        const float dsv = p * (fmaf(gg, t1, fmaf(u, st[2], -st[3]))) * inv_h;
-                        const float duv = p * (st[2] - gg);
-                        av[4 * hb + r] = a;
-                        sv[4 * hb + r] = dsv;
-                        uv[4 * hb + r] = duv;
+                        const float t1 = st[1] - u;   // 1 - u + ubar
+                        av[4 * hb + r] = p * t1;
+                        sv[4 * hb + r] = p * (fmaf(gg, t1, fmaf(u, st[2], -st[3]))) * inv_h;
+                        uv[4 * hb + r] = p * (st[2] - gg);
                     }
                 }
+            };
+            const bool below = i0 >= kw0 + 15;   // every row of the tile sees every key of the wave
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                float av[8], sv[8], uv[8];
+                if (below)
+                    weights(std::false_type{}, ch, av, sv, uv);
+                else
+                    weights(std::true_type{}, ch, av, sv, uv);
                 bf16x8 ah, al, sh, sl, uh, ul;
                 split8(av, ah, al);
                 split8(sv, sh, sl);
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_qr_kernel(
         rb_[ch] = *reinterpret_cast<const bf16x8*>(qiw + QI_R + o);
         db[ch] = *reinterpret_cast<const bf16x8*>(qiw + QI_D + o);
     }
-    const float4v st = *reinterpret_cast<const float4v*>(qiw + QI_ST + ir * 16);   // lse, ubar, G, D
+    const float4v st = *reinterpret_cast<const float4v*>(qiw + QI_ST + ir * 16);   // lse, 1 + ubar, G, D (after the sweep)
     float4v dqa[4], dra[4];
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
@@ -339,23 +352,30 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_qr_kernel(
                 Gm[kb] = mfma_bf16(v1, db[1], mfma_bf16(v0, db[0], zero));
             }
             if constexpr (kSweep) {
+                auto sums = [&](auto masked) {
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = j0 + 16 * kb + 4 * g + r;
-                        float e = __builtin_amdgcn_exp2f(fmaf(S[kb][r], sl2, -st[0]));
-                        e = j <= ic ? e : 0.0f;
-                        const float eg = e * Gm[kb][r];
-                        z += e;
-                        zu = fmaf(e, U[kb][r], zu);
-                        zg += eg;
-                        zgu = fmaf(eg, U[kb][r], zgu);
-                    }
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = j0 + 16 * kb + 4 * g + r;
+                            float e = __builtin_amdgcn_exp2f(fmaf(S[kb][r], sl2, -st[0]));
+                            if constexpr (decltype(masked)::value) e = j <= ic ? e : 0.0f;
+                            const float eg = e * Gm[kb][r];
+                            z += e;
+                            zu = fmaf(e, U[kb][r], zu);
+                            zg += eg;
+                            zgu = fmaf(eg, U[kb][r], zgu);
+                        }
+                };
+                if (j0 + BT - 1 <= iw0)   // every row of the wave sees every key of the tile
+                    sums(std::false_type{});
+                else
+                    sums(std::true_type{});
             } else
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-                float sv[8], uv[8];
+            {
+            // pair weights of keys 32 ch .. 32 ch + 31 (ds without its 1/h, applied to dq at the
+            // end); the causal mask only where the tile reaches past the wave's first row
+            auto weights = [&](auto masked, int ch, float (&sv)[8], float (&uv)[8]) {
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
                     const int kb = 2 * ch + hb;
@@ -363,13 +383,22 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_qr_kernel(
                     for (int r = 0; r < 4; ++r) {
                         const int j = j0 + 16 * kb + 4 * g + r;
                         float p = __builtin_amdgcn_exp2f(fmaf(S[kb][r], sl2, -st[0]));
-                        p = j <= ic ? p : 0.0f;
+                        if constexpr (decltype(masked)::value) p = j <= ic ? p : 0.0f;
                         const float u = U[kb][r], gg = Gm[kb][r];
-                        const float t1 = 1.0f - u + st[1];
-                        sv[4 * hb + r] = p * (fmaf(gg, t1, fmaf(u, st[2], -st[3]))) * inv_h;
+                        const float t1 = st[1] - u;   // 1 - u + ubar
+                        sv[4 * hb + r] = p * fmaf(gg, t1, fmaf(u, st[2], -st[3]));
                         uv[4 * hb + r] = p * (st[2] - gg);
                     }
                 }
+            };
+            const bool below = j0 + BT - 1 <= iw0;   // every row of the wave sees every key of the tile
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                float sv[8], uv[8];
+                if (below)
+                    weights(std::false_type{}, ch, sv, uv);
+                else
+                    weights(std::true_type{}, ch, sv, uv);
                 bf16x8 sh, sl, uh, ul;
                 split8(sv, sh, sl);
                 split8(uv, uh, ul);
@@ -380,13 +409,14 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_qr_kernel(
                     dra[fb] = mfma_bf16(ul, kt, mfma_bf16(uh, kt, dra[fb]));
                 }
             }
+            }
         }
         if (t + 1 <= tl) cp.stash(lds + (b ^ 1) * KIMG, tid);
         __syncthreads();
     }
     if constexpr (kSweep) {
         // row ic's sums are spread over the lane groups g: combine, then lane g = 0 writes
-        // lse, ubar, G, D of the row into its query image
+        // lse, 1 + ubar, G, D of the row into its query image
         z += __shfl_xor(z, 16);
         z += __shfl_xor(z, 32);
         zu += __shfl_xor(zu, 16);
@@ -398,7 +428,7 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_qr_kernel(
         if (g == 0 && ic < n) {
             const float iz = 1.0f / z, ub = zu * iz, G = zg * iz;
             *reinterpret_cast<float4v*>(qiw + QI_ST + ir * 16) =
-                float4v{st[0] + __log2f(z), ub, G, fmaf(G, 1.0f + 2.0f * ub, -zgu * iz)};
+                float4v{st[0] + __log2f(z), 1.0f + ub, G, fmaf(G, 1.0f + 2.0f * ub, -zgu * iz)};
         }
         return;
     }
@@ -410,7 +440,7 @@ __global__ __launch_bounds__(BNT, 1) void lla_parallax_bwd_qr_kernel(
             const int64_t o = (static_cast<int64_t>(bh) * n + i) * FD + c;
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb) {
-                dq[o + 16 * fb] = dqa[fb][r];
+                dq[o + 16 * fb] = dqa[fb][r] * inv_h;
                 drho[o + 16 * fb] = dra[fb][r];
             }
         }
