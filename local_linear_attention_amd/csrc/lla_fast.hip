@@ -1322,11 +1322,12 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
         for (int fv = 0; fv < 4; ++fv) o[st][fv] = float4v{0.f, 0.f, 0.f, 0.f};
     issue(0);
     wait_and_sync();
-    for (int t = 0; t < ntiles; ++t) {
+    // A tile wholly below the wave's first query needs no causal mask: those tiles (all but
+    // the last one or two of a wave) run first, in a loop of their own with the unmasked
+    // body, so the accumulators keep one register assignment from tile to tile.
+    auto tile_step = [&](const int t, auto phase) {
         issue(t + 1);   // into the buffer tile t-1 used
         const int j0 = t * MT;
-        // A tile wholly below the wave's first query needs no causal mask: that case (all
-        // tiles but the last one or two of a wave) takes a copy of the body without it.
         auto tile_body = [&](auto masked) {
             const unsigned char* cur = smem + (t % P_NBUF) * P_BUF;
             const unsigned char* KB = cur;
@@ -1377,10 +1378,13 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
                 }
             }
         };
-        if (j0 + MT - 1 <= qw0) tile_body(std::false_type{});
+        if constexpr (!decltype(phase)::value) tile_body(std::false_type{});
         else if (j0 <= wave_last) tile_body(std::true_type{});   // wave-uniform
         wait_and_sync();
-    }
+    };
+    const int tfull = min(ntiles, (qw0 + 1) / MT);   // tiles t with t MT + MT - 1 <= qw0
+    for (int t = 0; t < tfull; ++t) tile_step(t, std::false_type{});
+    for (int t = tfull; t < ntiles; ++t) tile_step(t, std::true_type{});
     // Copies issued past the last tile are still landing in LDS: let them finish before exit.
     __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
 

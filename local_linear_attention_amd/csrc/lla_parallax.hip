@@ -324,12 +324,13 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
     issue(WholeTile{}, 0);
     issue(WholeTile{}, 1);
     next_tile(WholeTile{});
-    for (int t = 0; t < ntiles; ++t) {
+    // Every tile a wave takes starts at or below its first query (tiles and waves are aligned
+    // to 64 and 32 rows); a tile wholly below the wave's first query needs no causal mask.
+    // Those tiles run first, in a loop of their own with the unmasked body, so the
+    // accumulators keep one register assignment from tile to tile.
+    auto tile_step = [&](const int t, auto phase) {
         issue(WholeTile{}, t + 2);   // into the buffer tile t-1 used
         const int j0 = t * MT;
-        // Every tile a wave takes starts at or below its first query (tiles and waves are
-        // aligned to 64 and 32 rows); a tile wholly below the wave's first query needs no
-        // causal mask.
         auto tile_body = [&](auto masked) {
             const unsigned char* cur = ring + (t % X_NBUF) * X_TILE;
             const _Float16* VI = reinterpret_cast<const _Float16*>(cur + X_KIMG);
@@ -386,10 +387,13 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
                 }
             }
         };
-        if (j0 + MT - 1 <= qw0) tile_body(std::false_type{});
+        if constexpr (!decltype(phase)::value) tile_body(std::false_type{});
         else if (j0 <= wave_last) tile_body(std::true_type{});   // wave-uniform
         next_tile(WholeTile{});
-    }
+    };
+    const int tfull = min(ntiles, (qw0 + 1) / MT);   // tiles t with t MT + MT - 1 <= qw0
+    for (int t = 0; t < tfull; ++t) tile_step(t, std::false_type{});
+    for (int t = tfull; t < ntiles; ++t) tile_step(t, std::true_type{});
     // Copies past the last tile are still landing in LDS: let them finish before exit.
     __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
 
