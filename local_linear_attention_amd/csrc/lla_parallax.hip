@@ -7,19 +7,19 @@
 // additive form of LLA with the boundary factor eta set to 0 and the probe given instead of
 // solved; Appendix B derives the additive form.)
 //
-// Matrix-core path (bf16 inputs, d = 64): one streaming pass per query over the key tiles,
-// in the two-branch form of the blog's section 3 "One extra branch, no extra I/O": the
-// softmax branch keeps the running max m, d1 = sum P1, O1 = sum P1 v with P1 = exp(s - m);
-// the covariance branch shares m, the rescale alpha and the tiles, and keeps
+// Matrix-core path (bf16 inputs, d = 64): the two-branch form of the blog's section 3 "One
+// extra branch, no extra I/O": the softmax branch keeps d1 = sum P1, O1 = sum P1 v with
+// P1 = exp(s - m); the covariance branch shares m and the tiles, and keeps
 // d2 = sum P2, O2 = sum P2 v with P2 = P1 * (rho . k); the result is merged at the end as in
 // the blog's Appendix C (item 3):  o = O1/d1 - (O2/d1 - (O1/d1)(d2/d1)).
 // Differences from the pages' form, none of which changes the result in exact arithmetic:
 //   * the probe scores are centred, s2_j = rho . (k_j - a) with a the head's mean key: a
 //     constant shift of s2 cancels in the merge, and centring keeps P2 small, so its fp16
 //     rounding error is small;
-//   * the running max is moved only when a score exceeds it by more than 2^8 in weight
-//     (a lane-local test; the rescale is exact whenever it happens), so P1 < 2^8;
-//   * s2 is scaled by a per-query power of two sigma that keeps |P2| below 2^14 (P1 < 2^8 and
+//   * m is the row's exact maximum, from a first pass over the key tiles (scores only), so
+//     P1 <= 1 and the second pass needs no rescaling (a running max with rescaling measured
+//     slower: its per-step maximum and test cost more in this loop than the first pass);
+//   * s2 is scaled by a per-query power of two sigma that keeps |P2| below 2^14 (P1 <= 1 and
 //     |s2| <= |rho| (max_j |k_j| + |a|)), so that P2 fits fp16; the merge divides by it;
 //   * P1 and P2 enter the P V products as fp16 (v as fp16, exact for bf16 values in the fp16
 //     range); d1 and d2 sum the same rounded values, so the rounding only perturbs weights.
