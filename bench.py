@@ -82,7 +82,7 @@ KERNEL_BOUND = {
     "lla_parallax_bwd_exact_rows_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_parallax_bwd_exact_cols_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_decode_stats_kernel": ("hbm", PEAK["hbm_GBps"]),
-    "lla_decode_moments_kernel": ("mfma", PEAK["mfma_f32_TFLOPs"]),
+    "lla_decode_moments_kernel": ("mfma", PEAK["mfma_f64_TFLOPs"]),   # hbm when split (see below)
     "lla_decode_reduce_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_decode_solve_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
 }
