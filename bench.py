@@ -182,38 +182,84 @@ def load_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def blas_threads():
+    """Threads of the BLAS library numpy calls in this process (the oracle's workers are
+    forked from it and inherit the setting)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(x.get("num_threads", 1)) for x in threadpool_info() if x.get("user_api") == "blas"] or [1])
+    except Exception:
+        return None
+
+
+def stratified_rows(w, rng, uniform):
+    """The long-context sample: every row i < 2d of head 0, `uniform` rows drawn uniformly over
+    all heads, and the last row of every head."""
+    rows = {(0, 0, i) for i in range(min(w.n, 2 * w.d))}
+    rows |= {(w.B - 1 - b, hh, w.n - 1) for b in range(w.B) for hh in range(w.H)}
+    rows |= {(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.n))) for _ in range(uniform)}
+    return sorted(rows)
+
+
 def cpu_baseline(w, q, k, v, seconds, rho=None):
-    """The fp64 oracle (LLA, or Parallax when a probe is given) on a bounded random sample of
-    the workload's rows."""
+    """The fp64 oracle (LLA, or Parallax when a probe is given) on a bounded sample of the
+    workload's rows, in a process pool with one BLAS thread per worker; the full-workload time
+    is projected from the sample with per-row cost i+1 (a row's prefix length).  Long
+    sequences (n > 8192) take a stratified sample: every row i < 2d of head 0, uniform rows
+    over all heads and the last row of every head."""
     import numpy as np
 
     from oracle import default_workers, lla_rows, parallax_rows
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:   # pragma: no cover
+        threadpool_limits = None
     workers = default_workers()
     rng = np.random.default_rng(12345)
     total_cost = w.B * w.H * w.n * (w.n + 1) / 2
     done_rows, done_cost, elapsed = 0, 0.0, 0.0
-    batch = 8 * workers
-    while elapsed < seconds:
-        rows = [(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.n)))
-                for _ in range(batch)]
-        t0 = time.perf_counter()
+
+    def run(rows):
         if rho is None:
             lla_rows(q, k, v, w.h, w.lam, rows, workers=workers)
         else:
             parallax_rows(q, k, v, rho, w.h, rows, workers=workers)
-        elapsed += time.perf_counter() - t0
-        done_rows += len(rows)
-        done_cost += sum(i + 1 for (_, _, i) in rows)
-        batch = min(4 * batch, 512 * workers)
+
+    limit = threadpool_limits(1, user_api="blas") if threadpool_limits else None
+    try:
+        bt = blas_threads()
+        stratified = w.n > 8192
+        batch = 8 * workers
+        while elapsed < seconds:
+            if stratified and done_rows == 0:
+                rows = stratified_rows(w, rng, 2048)
+            else:
+                rows = [(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.n)))
+                        for _ in range(batch)]
+                batch = min(4 * batch, 512 * workers)
+            t0 = time.perf_counter()
+            run(rows)
+            elapsed += time.perf_counter() - t0
+            done_rows += len(rows)
+            done_cost += sum(i + 1 for (_, _, i) in rows)
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
     full_seconds = elapsed * total_cost / done_cost
+    kind = ("a stratified sample (every row i < 2d of head 0, 2048 uniform rows, the last row of every "
+            "head), then uniform rows" if stratified else "uniformly drawn rows")
     return {
         "value": w.queries / full_seconds,
         "unit": "queries/s",
-        "cores": workers,
+        "cores": workers * (bt or 1),
         "kind": "oracle",
-        "sample": (f"{done_rows} uniformly drawn rows of the same workload (seed 12345), "
-                   f"{elapsed:.1f} s in {workers} worker processes; full-workload time "
-                   f"{full_seconds:.0f} s projected with per-row cost i+1"),
+        "host_cpus": os.cpu_count(),
+        "workers": workers,
+        "blas_threads_per_worker": bt,
+        "sample": (f"{done_rows} rows of the same workload, {kind} (seed 12345): {elapsed:.1f} s in "
+                   f"{workers} worker processes with {bt} BLAS thread(s) each on a host with "
+                   f"{os.cpu_count()} CPUs; the full-workload time, {full_seconds:.0f} s, is a projection "
+                   f"from the sample with per-row cost i+1, not a full run"),
     }
 
 
@@ -614,9 +660,9 @@ def main():
     import torch
 
     import lla_inputs
-    from local_linear_attention_amd import (lla_forward_ex, lla_parallax_forward, lla_parallax_path_available,
-                                            lla_path_available, lla_profile_collect, lla_profile_enable,
-                                            load_library)
+    from local_linear_attention_amd import (lla_forward_ws, lla_parallax_forward_ws, lla_parallax_path_available,
+                                            lla_parallax_workspace_size, lla_path_available, lla_profile_collect,
+                                            lla_profile_enable, lla_workspace_size, load_library)
 
     parallax = args.method == "parallax"
     w = lla_inputs.WORKLOADS[args.workload or ("parallax_d24" if parallax else "d24")]
@@ -644,12 +690,16 @@ def main():
         # the path the library picks by default for this dtype and head size
         path = "fast" if (w.dtype == "bf16" and available("fast", w.dtype, w.d)) else "exact"
     stream = torch.cuda.current_stream(dev)
+    # The caller owns the scratch: one workspace allocated before the timed region and passed
+    # to the _ws entry point, which allocates nothing.
+    ws_size = (lla_parallax_workspace_size if parallax else lla_workspace_size)(w.B, w.H, w.n, w.d, w.dtype, path)
+    ws = torch.empty(ws_size, dtype=torch.uint8, device=dev) if ws_size > 0 else None
 
     def step():
         if parallax:
-            lla_parallax_forward(tq, tk, tv, tr, w.h, path=path, out=out, stream=stream)
+            lla_parallax_forward_ws(tq, tk, tv, tr, w.h, ws, path=path, out=out, stream=stream)
         else:
-            lla_forward_ex(tq, tk, tv, w.h, w.lam, path=path, out=out, stream=stream)
+            lla_forward_ws(tq, tk, tv, w.h, w.lam, ws, path=path, out=out, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -728,6 +778,8 @@ def main():
             "workload": config_text,
             "B": w.B, "H": w.H, "n": w.n, "d": w.d, "input_dtype": w.dtype,
             "h": w.h, "lambda": None if parallax else w.lam, "path": path, "queries": w.queries,
+            "entry_point": (("lla_parallax_forward_ws" if parallax else "lla_forward_ws")
+                            + f" with a caller workspace of {ws_size} bytes"),
         },
         "tflops": achieved_tflops,
         "flop_count": flop_count,

@@ -23,13 +23,16 @@
  * [B, H, n, d] contiguous fp32 on the device.  Value width equals d.  Heads are
  * independent.
  *
- * Ownership: the caller owns q, k, v and out.  lla_forward_ws allocates nothing: the caller
- * passes the scratch the fast path needs (lla_workspace_size bytes).  lla_forward and
- * lla_forward_ex take that scratch from a library-owned, stream-ordered memory pool of the
- * current device (hipMallocFromPoolAsync / hipFreeAsync on `stream`); the pool keeps its
- * memory for reuse until the process ends.  No other state persists between calls, and
- * calls are reentrant.  `out` must not overlap q, k or v.  The current HIP device must be
- * the device of the pointers and of `stream`.
+ * Ownership: the caller owns q, k, v and out.  lla_forward_ws allocates, frees and retains
+ * nothing: the caller passes the scratch the matrix-core path needs
+ * (lla_forward_workspace_bytes bytes; zero when the chosen path needs none), and the call
+ * only enqueues kernels.  lla_forward and lla_forward_ex, whose argument lists carry no
+ * workspace, take that scratch from a library-owned, stream-ordered memory pool of the
+ * current device (hipMallocFromPoolAsync / hipFreeAsync on `stream`); the pool keeps freed
+ * blocks for reuse, so steady-state calls reach no allocator, until lla_pool_trim releases
+ * them.  No other state persists between calls, and calls are reentrant.  `out` must not
+ * overlap q, k or v.  The current HIP device must be the device of the pointers and of
+ * `stream`.
  *
  * Errors: arguments are validated on the host before any HIP call; a failed check
  * returns its status and touches nothing.  Work is enqueued asynchronously on `stream`
@@ -62,7 +65,8 @@ typedef enum {
                                  path that does not cover this (dtype, d) */
     LLA_ERR_WORKSPACE = 5,    /* workspace missing or too small (lla_forward_ws) */
     LLA_ERR_HIP = 6,          /* a HIP launch, query or scratch allocation failed */
-    LLA_ERR_ALIAS = 7         /* out overlaps q, k or v */
+    LLA_ERR_ALIAS = 7         /* an output overlaps an input or another output, or the
+                                 used part of a caller workspace overlaps any argument */
 } lla_status_t;
 
 /* Kernel path selection for lla_forward_ex. */
@@ -123,10 +127,19 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
 size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                           lla_path_t path);
 
+/* Bytes of device scratch lla_forward_ws needs with LLA_PATH_AUTO (the path lla_forward takes)
+ * for this problem: lla_workspace_size(B, H, n, d, dtype, LLA_PATH_AUTO).  0 if the chosen path
+ * needs none or the arguments are invalid.  Host-only: makes no HIP call. */
+size_t lla_forward_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype);
+
 /* lla_forward_ex with caller-provided scratch: `workspace` is a device pointer to at least
- * lla_workspace_size(...) bytes, 16-byte aligned, not overlapping any other argument, and
- * not used by any other work until this call's kernels finish on `stream`.  Allocates
- * nothing.  A missing or short workspace, when one is needed, returns LLA_ERR_WORKSPACE. */
+ * lla_workspace_size(..., path) bytes (lla_forward_workspace_bytes for LLA_PATH_AUTO), 16-byte
+ * aligned, and not used by any other work until this call's kernels finish on `stream`.
+ * Allocates nothing.  Checked on the host before any launch: a missing or short workspace,
+ * when one is needed, returns LLA_ERR_WORKSPACE; a workspace whose first `needed` bytes
+ * overlap q, k, v or out returns LLA_ERR_ALIAS.  The other _ws entry points and the
+ * workspace arguments of lla_parallax_forward_stats and lla_parallax_backward are checked the
+ * same way against all of their own arguments. */
 lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* out,
                             int64_t B, int64_t H, int64_t n, int64_t d,
                             double h, double lambda,
@@ -298,6 +311,12 @@ lla_status_t lla_parallax_decode_ws(const void* q, const void* k, const void* v,
                                     float* out, int64_t B, int64_t H, int64_t L, int64_t d,
                                     double h, lla_dtype_t dtype, void* stream,
                                     void* workspace, size_t workspace_bytes);
+
+/* Returns the memory that the library pool of every device holds for reuse (blocks that
+ * lla_forward, lla_forward_ex and the other pool-backed entry points have freed) to the
+ * system: hipMemPoolTrimTo(pool, 0).  Blocks still in use by enqueued work are kept.  The
+ * next pool-backed call allocates again.  LLA_ERR_HIP if a trim fails. */
+lla_status_t lla_pool_trim(void);
 
 /* Kernel-level timing.  While enabled, every kernel launch of the library is bracketed by
  * HIP events on its stream.  lla_profile_collect waits for the recorded events, writes up to

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -19,6 +20,12 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + static_cast<uintptr_t>(b_bytes) && b0 < a0 + static_cast<uintptr_t>(a_bytes);
 }
+
+// An argument buffer: a caller workspace must not overlap any of them.
+struct Span {
+    const void* p;
+    int64_t bytes;
+};
 
 bool supported_shape(int64_t d, lla_dtype_t dtype) {
     return (dtype == LLA_DTYPE_F32 || dtype == LLA_DTYPE_BF16) &&
@@ -95,12 +102,17 @@ hipError_t pool_for_current_device(hipMemPool_t* pool) {
 
 // Launch with the scratch `need` bytes: none, the caller's workspace, or (when allowed) a
 // block of the library pool freed in stream order after the launch.
+// A caller workspace is checked before any launch: at least `need` bytes (else
+// LLA_ERR_WORKSPACE), and the `need` bytes the kernels use overlap none of `bufs` (else
+// LLA_ERR_ALIAS).
 template <typename Launch>
 lla_status_t run_scratch(size_t need, hipStream_t stream, void* ws, size_t ws_bytes, bool may_allocate,
-                         Launch launch) {
+                         std::initializer_list<Span> bufs, Launch launch) {
     if (need == 0) return launch(nullptr) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
     if (ws) {
         if (ws_bytes < need) return LLA_ERR_WORKSPACE;
+        for (const Span& b : bufs)
+            if (b.p && overlaps(ws, static_cast<int64_t>(need), b.p, b.bytes)) return LLA_ERR_ALIAS;
         return launch(ws) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
     }
     if (!may_allocate) return LLA_ERR_WORKSPACE;
@@ -115,7 +127,9 @@ lla_status_t run_scratch(size_t need, hipStream_t stream, void* ws, size_t ws_by
 
 lla_status_t run(const lla::Problem& p, bool fast, void* ws, size_t ws_bytes, bool may_allocate) {
     if (!fast) return lla::launch_exact(p, static_cast<int>(p.n)) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    const int64_t in_bytes = p.B * p.H * p.n * p.d * (p.dtype == LLA_DTYPE_F32 ? 4 : 2);
     return run_scratch(lla::fast_workspace_bytes(p.B, p.H, p.n, p.d), p.stream, ws, ws_bytes, may_allocate,
+                       {{p.q, in_bytes}, {p.k, in_bytes}, {p.v, in_bytes}, {p.out, p.B * p.H * p.n * p.d * 4}},
                        [&](void* w) { return lla::launch_fast(p, w); });
 }
 
@@ -151,7 +165,10 @@ bool resolve_parallax_fast(lla_path_t path, int dtype, int64_t d, int64_t n, boo
 
 lla_status_t run_parallax(const lla::Problem& p, bool fast, void* ws, size_t ws_bytes, bool may_allocate) {
     if (!fast) return lla::launch_parallax_exact(p) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    const int64_t in_bytes = p.B * p.H * p.n * p.d * (p.dtype == LLA_DTYPE_F32 ? 4 : 2);
     return run_scratch(lla::parallax_workspace_bytes(p.B, p.H, p.n, p.d), p.stream, ws, ws_bytes, may_allocate,
+                       {{p.q, in_bytes}, {p.k, in_bytes}, {p.v, in_bytes}, {p.rho, in_bytes},
+                        {p.out, p.B * p.H * p.n * p.d * 4}, {p.stats, p.B * p.H * p.n * 4}},
                        [&](void* w) { return lla::launch_parallax_fast(p, w); });
 }
 
@@ -173,6 +190,7 @@ lla_status_t decode_entry(const void* q, const void* k, const void* v, const voi
     const lla::Problem p{q, k, v, out, B, H, L, d, h, 0.0, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream), rho};
     return run_scratch(lla::decode_workspace_bytes(B, H, L, d), p.stream, ws, ws_bytes, may_allocate,
+                       {{q, row_bytes}, {rho, row_bytes}, {k, cache_bytes}, {v, cache_bytes}, {out, out_bytes}},
                        [&](void* w) { return lla::launch_parallax_decode(p, w); });
 }
 
@@ -194,7 +212,8 @@ lla_status_t lla_decode_entry(const void* q, const void* k, const void* v, float
     const lla::Problem p{q, k, v, out, B, H, L, d, h, lambda, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream), nullptr};
     return run_scratch(lla::lla_decode_workspace_bytes(B, H, L, d, static_cast<int>(dtype)), p.stream, ws, ws_bytes,
-                       may_allocate, [&](void* w) { return lla::launch_lla_decode(p, w); });
+                       may_allocate, {{q, row_bytes}, {k, cache_bytes}, {v, cache_bytes}, {out, out_bytes}},
+                       [&](void* w) { return lla::launch_lla_decode(p, w); });
 }
 
 lla_status_t parallax_entry(const void* q, const void* k, const void* v, const void* rho, float* out,
@@ -258,6 +277,8 @@ lla_status_t parallax_bwd_entry(const void* q, const void* k, const void* v, con
     p.stats = const_cast<float*>(lse);
     const lla::BwdProblem b{p, dout, dq, dk, dv, drho};
     return run_scratch(lla::parallax_bwd_workspace_bytes(B, H, n, d, fast), p.stream, ws, ws_bytes, ws == nullptr,
+                       {{q, ib}, {k, ib}, {v, ib}, {rho, ib}, {dout, ib}, {lse, rows * 4},
+                        {dq, gb}, {dk, gb}, {dv, gb}, {drho, gb}},
                        [&](void* w) {
                            return fast ? lla::launch_parallax_bwd_fast(b, w) : lla::launch_parallax_bwd_exact(b, w);
                        });
@@ -316,9 +337,9 @@ const char* lla_status_string(lla_status_t s) {
         case LLA_ERR_SHAPE: return "invalid shape (B, H, n must be >= 1 and within index range)";
         case LLA_ERR_PARAM: return "invalid parameter (h must be > 0, lambda >= 0, both finite)";
         case LLA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or path";
-        case LLA_ERR_WORKSPACE: return "workspace missing or smaller than lla_workspace_size";
+        case LLA_ERR_WORKSPACE: return "workspace missing or smaller than the entry point's workspace size";
         case LLA_ERR_HIP: return "HIP launch or allocation failed";
-        case LLA_ERR_ALIAS: return "output overlaps an input";
+        case LLA_ERR_ALIAS: return "an output or the workspace overlaps another argument";
     }
     return "unknown status";
 }
@@ -337,6 +358,17 @@ size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_
     bool fast = false;
     if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast) || !fast) return 0;
     return lla::fast_workspace_bytes(B, H, n, d);
+}
+
+size_t lla_forward_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype) {
+    return lla_workspace_size(B, H, n, d, dtype, LLA_PATH_AUTO);
+}
+
+lla_status_t lla_pool_trim(void) {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    for (hipMemPool_t p : g_pools)
+        if (p && hipMemPoolTrimTo(p, 0) != hipSuccess) return LLA_ERR_HIP;
+    return LLA_OK;
 }
 
 lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* out,

@@ -11,6 +11,7 @@ import ctypes
 import os
 
 __all__ = ["lla_forward", "lla_forward_ex", "lla_forward_ws", "lla_workspace_size",
+           "lla_forward_workspace_bytes", "lla_pool_trim",
            "lla_path_available", "lla_parallax_forward", "lla_parallax_forward_ex",
            "lla_parallax_forward_ws", "lla_parallax_workspace_size", "lla_parallax_path_available",
            "lla_parallax_decode", "lla_parallax_decode_ws", "lla_parallax_decode_workspace_size",
@@ -62,6 +63,10 @@ def load_library():
     lib.lla_version.restype = ctypes.c_int
     lib.lla_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.lla_workspace_size.restype = ctypes.c_size_t
+    lib.lla_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.lla_forward_workspace_bytes.restype = ctypes.c_size_t
+    lib.lla_pool_trim.argtypes = []
+    lib.lla_pool_trim.restype = ctypes.c_int
     lib.lla_forward_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int,
                                    vp, ctypes.c_int, vp, ctypes.c_size_t]
     lib.lla_forward_ws.restype = ctypes.c_int
@@ -185,6 +190,18 @@ def lla_forward(q, k, v, h: float, lam: float, out=None, stream=None):
 def lla_workspace_size(B: int, H: int, n: int, d: int, dtype: str, path: str = "auto") -> int:
     """Bytes of device scratch the chosen path needs (0 if none)."""
     return int(load_library().lla_workspace_size(B, H, n, d, DTYPES[dtype], PATHS[path]))
+
+
+def lla_forward_workspace_bytes(B: int, H: int, n: int, d: int, dtype: str) -> int:
+    """Bytes of device scratch lla_forward_ws needs on the default (auto) path (0 if none)."""
+    return int(load_library().lla_forward_workspace_bytes(B, H, n, d, DTYPES[dtype]))
+
+
+def lla_pool_trim() -> None:
+    """Return the library pool's cached blocks (from pool-backed calls) to the system."""
+    st = load_library().lla_pool_trim()
+    if st != 0:
+        raise LLAError(st, "lla_pool_trim")
 
 
 def lla_forward_ws(q, k, v, h: float, lam: float, workspace, path: str = "auto", out=None,

@@ -35,6 +35,30 @@ def run_gpu(q, k, v, dtype, h, lam, path="auto"):
     return out.cpu().numpy().astype(np.float64)
 
 
+def oracle_workers() -> int:
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_all_rows(q, k, v, h, lam):
+    """The fp64 oracle over every row, in a process pool of one BLAS thread per worker (the
+    workers are forked from this process and inherit the limit): a full-size forward of the
+    d = 64 workloads takes about a minute on 8 to 16 cores."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import lla_forward as oracle_forward
+    with threadpool_limits(1, user_api="blas"):
+        return oracle_forward(q, k, v, h, lam, workers=oracle_workers())
+
+
+def oracle_some_rows(q, k, v, h, lam, rows):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import lla_rows
+    with threadpool_limits(1, user_api="blas"):
+        return lla_rows(q, k, v, h, lam, rows, workers=oracle_workers())
+
+
 def row_errors(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     """Per-row normwise relative error over the last axis."""
     num = np.max(np.abs(got - ref), axis=-1)

@@ -32,7 +32,8 @@ def declared_enums():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["lla_decode", "lla_decode_workspace_size", "lla_decode_ws",
-                                    "lla_forward", "lla_forward_ex", "lla_forward_ws",
+                                    "lla_forward", "lla_forward_ex", "lla_forward_workspace_bytes",
+                                    "lla_forward_ws",
                                     "lla_parallax_backward", "lla_parallax_backward_workspace_size",
                                     "lla_parallax_decode", "lla_parallax_decode_workspace_size",
                                     "lla_parallax_decode_ws",
@@ -40,7 +41,7 @@ def test_header_declares_the_entry_points():
                                     "lla_parallax_forward_stats",
                                     "lla_parallax_forward_ws", "lla_parallax_path_available",
                                     "lla_parallax_workspace_size",
-                                    "lla_path_available", "lla_profile_collect",
+                                    "lla_path_available", "lla_pool_trim", "lla_profile_collect",
                                     "lla_profile_enable", "lla_status_string", "lla_version",
                                     "lla_workspace_size"]
 
@@ -139,6 +140,44 @@ def test_workspace_size():
     assert lla.lla_workspace_size(2, 16, 4096, 64, "f32", "auto") == 0
     assert lla.lla_workspace_size(2, 16, 4096, 48, "bf16", "auto") == 0     # unsupported d
     assert lla.lla_workspace_size(0, 16, 4096, 64, "bf16", "auto") == 0     # bad shape
+
+
+def test_boundary_contract_names():
+    # The scope table's boundary: lla_forward with the spec argument list (dtype and
+    # stream appended), the caller-workspace pair, status strings and the version.
+    lib = _lib()
+    for name in ("lla_forward", "lla_forward_workspace_bytes", "lla_forward_ws", "lla_status_string",
+                 "lla_version"):
+        assert name in declared_functions() and hasattr(lib, name), name
+    from local_linear_attention_amd import lla
+    for args in ((2, 16, 4096, 64, "bf16"), (1, 8, 16384, 128, "bf16"), (1, 4, 1024, 64, "f32"),
+                 (4, 12, 2048, 64, "bf16"), (1, 1, 64, 16, "f32"), (1, 1, 100, 64, "bf16")):
+        assert lla.lla_forward_workspace_bytes(*args) == lla.lla_workspace_size(*args, "auto"), args
+    assert lla.lla_forward_workspace_bytes(0, 16, 4096, 64, "bf16") == 0
+
+
+def test_forward_ws_rejects_overlapping_workspace():
+    lib = _lib()
+    args = [ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V), ctypes.c_void_p(OUT),
+            1, 2, 4096, 64, 8.0, 0.1, 1, None, 2]
+    from local_linear_attention_amd import lla
+    need = lla.lla_workspace_size(1, 2, 4096, 64, "bf16", "fast")
+    in_bytes, out_bytes = 2 * 4096 * 64 * 2, 2 * 4096 * 64 * 4
+    assert need > 0
+    # one byte of overlap is enough, at either end of any argument
+    for ws in (Q, K + in_bytes - 1, V - need + 1, OUT + out_bytes // 2, Q - 256):
+        assert lib.lla_forward_ws(*args, ctypes.c_void_p(ws), need) == 7, hex(ws)
+    # a short workspace is reported as such first
+    assert lib.lla_forward_ws(*args, ctypes.c_void_p(Q), need - 1) == 5
+    # every other workspace-taking entry point checks the same way
+    assert lib.lla_parallax_forward_ws(ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V),
+                                       ctypes.c_void_p(RHO), ctypes.c_void_p(OUT), 1, 2, 4096, 64, 8.0, 1, None, 2,
+                                       ctypes.c_void_p(RHO + 64),
+                                       lla.lla_parallax_workspace_size(1, 2, 4096, 64, "bf16", "fast")) == 7
+    dbytes = lla.lla_decode_workspace_size(1, 2, 4096, 64, "bf16")
+    assert dbytes > 0
+    assert lib.lla_decode_ws(ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V), ctypes.c_void_p(OUT),
+                             1, 2, 4096, 64, 8.0, 0.01, 1, None, ctypes.c_void_p(K + 128), dbytes) == 7
 
 
 def test_forward_ws_validation_before_launch():
