@@ -65,8 +65,10 @@ typedef enum {
                                  path that does not cover this (dtype, d) */
     LLA_ERR_WORKSPACE = 5,    /* workspace missing or too small (lla_forward_ws) */
     LLA_ERR_HIP = 6,          /* a HIP launch, query or scratch allocation failed */
-    LLA_ERR_ALIAS = 7         /* an output overlaps an input or another output, or the
+    LLA_ERR_ALIAS = 7,        /* an output overlaps an input or another output, or the
                                  used part of a caller workspace overlaps any argument */
+    LLA_ERR_SCRATCH_LIMIT = 8 /* lla_forward_noalloc: the problem needs more scratch than
+                                 its static buffer holds (LLA_NOALLOC_SCRATCH_BYTES) */
 } lla_status_t;
 
 /* Kernel path selection for lla_forward_ex. */
@@ -145,6 +147,28 @@ lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* 
                             double h, double lambda,
                             lla_dtype_t dtype, void* stream, lla_path_t path,
                             void* workspace, size_t workspace_bytes);
+
+/* Size of the static device scratch of lla_forward_noalloc, per device. */
+#define LLA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/*
+ * lla_forward_ex for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It runs the same kernels
+ * as lla_forward_ws with their scratch in a static device array of LLA_NOALLOC_SCRATCH_BYTES
+ * (256 MiB) that the library holds on every device it runs on until the process ends; it
+ * calls no allocator.  The caller still passes q, k, v and out as for lla_forward_ex.
+ * A problem whose path needs more scratch than that returns LLA_ERR_SCRATCH_LIMIT before any
+ * launch (the matrix-core path needs lla_forward_workspace_bytes; B2 H16 n4096 d64 takes
+ * about 108 MB).  Every call on a device shares that device's array and nothing in it needs
+ * clearing between calls: calls that overlap in time on one device (two streams, two host
+ * threads) race on it and must be serialised by the caller.  The first call on a device looks
+ * up the array's device address (hipGetSymbolAddress) with that device current; a failed
+ * lookup returns LLA_ERR_HIP.  Validation, errors and streams otherwise as for lla_forward_ex.
+ */
+lla_status_t lla_forward_noalloc(const void* q, const void* k, const void* v, float* out,
+                                 int64_t B, int64_t H, int64_t n, int64_t d,
+                                 double h, double lambda,
+                                 lla_dtype_t dtype, void* stream, lla_path_t path);
 
 /*
  * Causal Parallax forward with a caller-supplied probe (sources: the "Parallax" blog post,

@@ -284,6 +284,36 @@ lla_status_t parallax_bwd_entry(const void* q, const void* k, const void* v, con
                        });
 }
 
+// ---- entry point that allocates nothing: scratch in a static device array
+// For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+// harnesses that forbid it): lla_forward_noalloc runs lla_forward_ws's kernels with their
+// scratch in this file-scope array, which every device the library runs on holds from the
+// module's load until the process ends.  In host code `scratch` names a host-side stand-in:
+// only the address hipGetSymbolAddress returns (kept per device) is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = LLA_NOALLOC_SCRATCH_BYTES;   // 256 MiB per device
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // per device: the device address of `scratch`
+
+// The device address of this device's `scratch`, looked up once per device with that
+// device current (the caller's current device is the one the call runs on).
+hipError_t scratch_for_current_device(void** ptr) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (static_cast<int>(g_scratch_ptr.size()) <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if ((err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 // ---- kernel-level timing
 struct ProfEntry {
     const char* name;
@@ -340,6 +370,8 @@ const char* lla_status_string(lla_status_t s) {
         case LLA_ERR_WORKSPACE: return "workspace missing or smaller than the entry point's workspace size";
         case LLA_ERR_HIP: return "HIP launch or allocation failed";
         case LLA_ERR_ALIAS: return "an output or the workspace overlaps another argument";
+        case LLA_ERR_SCRATCH_LIMIT:
+            return "problem needs more scratch than lla_forward_noalloc's static buffer (LLA_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
@@ -384,6 +416,21 @@ lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* 
                          static_cast<hipStream_t>(stream)};
     if (path == LLA_PATH_CG) return lla::launch_cg(p) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
     return run(p, fast, workspace, workspace_bytes, false);
+}
+
+lla_status_t lla_forward_noalloc(const void* q, const void* k, const void* v, float* out,
+                                 int64_t B, int64_t H, int64_t n, int64_t d,
+                                 double h, double lambda,
+                                 lla_dtype_t dtype, void* stream, lla_path_t path) {
+    const lla_status_t st = validate(q, k, v, out, B, H, n, d, h, lambda, dtype);
+    if (st != LLA_OK) return st;
+    bool fast = false;
+    if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
+    const size_t need = fast ? lla::fast_workspace_bytes(B, H, n, d) : 0;
+    if (need > kNoAllocScratchBytes) return LLA_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    if (need > 0 && scratch_for_current_device(&ws) != hipSuccess) return LLA_ERR_HIP;
+    return lla_forward_ws(q, k, v, out, B, H, n, d, h, lambda, dtype, stream, path, ws, need);
 }
 
 lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* out,

@@ -11,7 +11,7 @@ import ctypes
 import os
 
 __all__ = ["lla_forward", "lla_forward_ex", "lla_forward_ws", "lla_workspace_size",
-           "lla_forward_workspace_bytes", "lla_pool_trim",
+           "lla_forward_workspace_bytes", "lla_pool_trim", "lla_forward_noalloc",
            "lla_path_available", "lla_parallax_forward", "lla_parallax_forward_ex",
            "lla_parallax_forward_ws", "lla_parallax_workspace_size", "lla_parallax_path_available",
            "lla_parallax_decode", "lla_parallax_decode_ws", "lla_parallax_decode_workspace_size",
@@ -24,7 +24,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 STATUS = {0: "LLA_OK", 1: "LLA_ERR_NULL", 2: "LLA_ERR_SHAPE", 3: "LLA_ERR_PARAM",
-          4: "LLA_ERR_UNSUPPORTED", 5: "LLA_ERR_WORKSPACE", 6: "LLA_ERR_HIP", 7: "LLA_ERR_ALIAS"}
+          4: "LLA_ERR_UNSUPPORTED", 5: "LLA_ERR_WORKSPACE", 6: "LLA_ERR_HIP", 7: "LLA_ERR_ALIAS",
+          8: "LLA_ERR_SCRATCH_LIMIT"}
 PATHS = {"auto": 0, "exact": 1, "fast": 2, "cg": 3}
 DTYPES = {"f32": 0, "bf16": 1}
 
@@ -65,6 +66,9 @@ def load_library():
     lib.lla_workspace_size.restype = ctypes.c_size_t
     lib.lla_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.lla_forward_workspace_bytes.restype = ctypes.c_size_t
+    lib.lla_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int, vp,
+                                        ctypes.c_int]
+    lib.lla_forward_noalloc.restype = ctypes.c_int
     lib.lla_pool_trim.argtypes = []
     lib.lla_pool_trim.restype = ctypes.c_int
     lib.lla_forward_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int,
@@ -195,6 +199,22 @@ def lla_workspace_size(B: int, H: int, n: int, d: int, dtype: str, path: str = "
 def lla_forward_workspace_bytes(B: int, H: int, n: int, d: int, dtype: str) -> int:
     """Bytes of device scratch lla_forward_ws needs on the default (auto) path (0 if none)."""
     return int(load_library().lla_forward_workspace_bytes(B, H, n, d, DTYPES[dtype]))
+
+
+def lla_forward_noalloc(q, k, v, h: float, lam: float, path: str = "auto", out=None, stream=None):
+    """LLA forward whose scratch is the library's static device buffer (no allocation by the
+    library; `out` is allocated here unless given)."""
+    import torch
+    dtype, out = _marshal(q, k, v, out)
+    B, H, n, d = q.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = load_library().lla_forward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                            B, H, n, d, float(h), float(lam), dtype,
+                                            ctypes.c_void_p(stream.cuda_stream), PATHS[path])
+    if st != 0:
+        raise LLAError(st, "lla_forward_noalloc")
+    return out
 
 
 def lla_pool_trim() -> None:

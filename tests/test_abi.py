@@ -32,7 +32,8 @@ def declared_enums():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["lla_decode", "lla_decode_workspace_size", "lla_decode_ws",
-                                    "lla_forward", "lla_forward_ex", "lla_forward_workspace_bytes",
+                                    "lla_forward", "lla_forward_ex", "lla_forward_noalloc",
+                                    "lla_forward_workspace_bytes",
                                     "lla_forward_ws",
                                     "lla_parallax_backward", "lla_parallax_backward_workspace_size",
                                     "lla_parallax_decode", "lla_parallax_decode_workspace_size",
@@ -68,7 +69,7 @@ def test_status_codes_match_header_and_binding():
 def test_version_and_status_strings():
     lib = _lib()
     assert lib.lla_version() >= 100
-    for s in range(8):
+    for s in range(9):
         assert lib.lla_status_string(s)
     assert lib.lla_status_string(99) == b"unknown status"
 
