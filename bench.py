@@ -85,13 +85,25 @@ KERNEL_BOUND = {
     "lla_decode_moments_kernel": ("mfma", PEAK["mfma_f64_TFLOPs"]),   # hbm when split (see below)
     "lla_decode_reduce_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_decode_solve_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla8_anchor_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla8_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
+    "lla8_rowmax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla8_keymom_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
+    "lla8_probe_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
 }
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
     "cg": ["lla_cg_kernel"],
     "fast": ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel",
              "lla_probe_kernel"],
+    # d = 128: rows i < 4d on the fp64 kernel, the rest on the d = 128 matrix-core kernels
+    "fast128": ["lla_exact_kernel", "lla8_anchor_kernel", "lla8_pack_kernel", "lla8_rowmax_kernel",
+                "lla8_keymom_kernel", "lla8_probe_kernel"],
 }
+
+
+def path_kernels(path, d):
+    return PATH_KERNELS["fast128" if (path == "fast" and d == 128) else path]
 PARALLAX_KERNELS = {
     "exact": ["lla_parallax_exact_kernel"],
     "fast": ["lla_parallax_pack_kernel", "lla_parallax_kernel"],
@@ -123,16 +135,22 @@ def kernel_flops(name, B, H, n, d, path):
     BH = B * H
     row0 = min(n, 2 * d) if path == "fast" else n
     rowp = min(n, 4 * d) if path == "fast" else n
+    if path == "fast" and d == 128:   # rows < 4d exact (NS), the rest key moments + probe (min)
+        row0 = rowp = min(n, 4 * d)
     per_query = d ** 3 / 3 + 4 * d * d + 2 * d
     moments = 2 * (1 + 2 * d) + d * (d + 1)
     if name in ("lla_exact_kernel", "lla_short_kernel", "lla_cg_kernel"):
         # the CG kernel is credited with the direct formulation's count, so that both fp64
         # paths report comparable rates (its own work depends on the iteration counts)
         return pair_count(BH, 0, row0) * (2 * d + moments + 2 * d * d) + BH * row0 * per_query
-    if name in ("lla_anchor_kernel", "lla_pack_kernel"):
+    if name in ("lla_anchor_kernel", "lla_pack_kernel", "lla8_anchor_kernel", "lla8_pack_kernel"):
         return 0                      # data movement only (K, V summed and repacked once)
-    if name == "lla_rowmax_kernel":
+    if name in ("lla_rowmax_kernel", "lla8_rowmax_kernel"):
         return pair_count(BH, row0, n) * 2 * d
+    if name == "lla8_keymom_kernel":
+        return pair_count(BH, rowp, n) * moments + BH * (n - rowp) * (d ** 3 / 3 + 2 * d * d)
+    if name == "lla8_probe_kernel":
+        return pair_count(BH, rowp, n) * (4 * d + 2) + BH * (n - rowp) * 4 * d
     if name == "lla_moments_kernel":
         return pair_count(BH, row0, rowp) * (moments + 2 * d * d) + BH * (rowp - row0) * per_query
     if name == "lla_keymom_kernel":
@@ -151,7 +169,7 @@ def kernel_flops(name, B, H, n, d, path):
 
 def path_flops(B, H, n, d, path):
     """Algorithmic flops of one forward in the formulations the path executes."""
-    return sum(kernel_flops(k, B, H, n, d, path) for k in PATH_KERNELS[path])
+    return sum(kernel_flops(k, B, H, n, d, path) for k in path_kernels(path, d))
 
 
 def kernel_source_hash(kernel):
@@ -761,8 +779,12 @@ def main():
                       "F_NS": alg_flops(w.B, w.H, w.n, w.d, "NS"),
                       "F_min": alg_flops(w.B, w.H, w.n, w.d, "min")}
         arith = PATH_ARITH[path]
+        if path == "fast" and w.d == 128:
+            arith = "f16 MFMA / f32 accumulate (rows < 4d: f64)"
     result = {
-        "metric": METRIC_PARALLAX if parallax else METRIC,
+        "metric": (METRIC_PARALLAX if parallax else METRIC) if w.name in ("d24", "parallax_d24") else
+                  (f"{'Parallax fwd (given probe)' if parallax else 'LLA fwd'} queries/s + TFLOP/s (% MFMA peak) "
+                   f"at B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype}, 1 GPU"),
         "value": w.queries / (ms_per_step * 1e-3),
         "unit": "queries/s",
         "n_gpus": 1,

@@ -1724,24 +1724,41 @@ FastLayout fast_layout(int64_t BH, int64_t n, int64_t d) {
 
 bool fast_supports(int dtype, int64_t d, int64_t n) {
     // Buffer resources address a head's keys and tile images with 32-bit byte offsets.
-    return dtype == 1 && d == FD && n <= kFastMaxN;
+    return dtype == 1 && ((d == FD && n <= kFastMaxN) || (d == 128 && n <= kFast128MaxN));
 }
 
 size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
+    if (d == 128) return fast128_workspace_bytes(B, H, n);
     if (n - fast_row0(n, d) <= 0) return 0;
     return static_cast<size_t>(fast_layout(B * H, n, d).total);
 }
 
+namespace {
+// Dynamic-LDS limits are set per device, the first time a device launches this path.
+std::mutex g_attr_mu;
+bool g_attr_done[64] = {};
+
+hipError_t ensure_attributes() {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_attr_mu);
+    if (g_attr_done[dev]) return hipSuccess;
+    if ((err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_rows_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, R_SMEM)) != hipSuccess)
+        return err;
+    if ((err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_probe_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM)) != hipSuccess)
+        return err;
+    g_attr_done[dev] = true;
+    return hipSuccess;
+}
+}  // namespace
+
 hipError_t launch_fast(const Problem& p, void* workspace) {
-    static std::once_flag attr_once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(attr_once, [] {
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_rows_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, R_SMEM);
-        if (attr_err == hipSuccess)
-            attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_probe_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, P_SMEM);
-    });
+    if (p.d == 128) return launch_fast128(p, workspace);
+    hipError_t attr_err = ensure_attributes();
     if (attr_err != hipSuccess) return attr_err;
 
     const int n = static_cast<int>(p.n);

@@ -39,10 +39,15 @@ hipError_t launch_cg(const Problem& p);
 // Matrix-core path for bf16 inputs: rows i < 2d on the fp64 kernel, the rest on MFMA
 // kernels that keep per-row statistics and packed key/value tiles in `workspace`
 // (fast_workspace_bytes of it).  Serves d = 64 and n up to kFastMaxN.
+// Also d = 128 (n up to kFast128MaxN) through the kernels of lla_fast128.hip: rows i < 4d on
+// the fp64 kernel, the rest on MFMA with the cross moment applied by a probe pass.
 constexpr int64_t kFastMaxN = int64_t(1) << 22;
+constexpr int64_t kFast128MaxN = int64_t(1) << 21;
 bool fast_supports(int dtype, int64_t d, int64_t n);
 size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
 hipError_t launch_fast(const Problem& p, void* workspace);
+size_t fast128_workspace_bytes(int64_t B, int64_t H, int64_t n);
+hipError_t launch_fast128(const Problem& p, void* workspace);
 
 // Parallax forward with a given probe.  Fast path: bf16, d = 64, n up to kFastMaxN, with
 // tile images and per-tile key statistics in `workspace` (parallax_workspace_bytes);

@@ -89,6 +89,40 @@ def test_fast_path_every_row(name, shape):
     check(got, ref, w.dtype, "fast", f"{name}{shape}", positions=np.arange(w.n), d=w.d)
 
 
+# Matrix-core path at d = 128 (bf16): rows below 4d run on the fp64 kernel, the rest on MFMA
+# (key moments and solve, then the probe pass).  Shapes cover no MFMA rows (n <= 4d), one
+# ragged row block past 4d, several key tiles with a ragged tail, two heads and two batches.
+FAST128_SMALL = [
+    ("long", {"B": 1, "H": 1, "n": 500}),
+    ("long", {"B": 1, "H": 2, "n": 600}),
+    ("long", {"B": 2, "H": 1, "n": 777}),
+    ("long", {"B": 1, "H": 1, "n": 1100}),
+]
+
+
+@pytest.mark.parametrize("name,shape", FAST128_SMALL, ids=[f"{n}-{s}" for n, s in FAST128_SMALL])
+def test_fast_path_d128_every_row(name, shape):
+    require_gpu()
+    w, q, k, v = workload_arrays(name, **shape)
+    ref = oracle_all_rows(q, k, v, w.h, w.lam)
+    got = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="fast")
+    check(got, ref, w.dtype, "fast", f"{name}{shape}", positions=np.arange(w.n), d=w.d)
+
+
+@pytest.mark.parametrize("lam", [0.0, 1e8])
+def test_fast_path_d128_extreme_ridge(lam):
+    # lambda = 0: rows i >= d have a unique minimiser (rows below d only need to be finite);
+    # lambda = 1e8: the ridge dominates and b_i tends to the softmax-weighted mean of the values.
+    require_gpu()
+    w, q, k, v = workload_arrays("long", B=1, H=1, n=800)
+    ref = oracle_all_rows(q, k, v, w.h, lam)
+    got = run_gpu(q, k, v, w.dtype, w.h, lam, path="fast")
+    assert np.isfinite(got).all()
+    lo = w.d if lam == 0.0 else 0
+    check(got[..., lo:, :], ref[..., lo:, :], w.dtype, "fast", f"long n=800 lambda={lam:g}",
+          positions=np.arange(lo, w.n), d=w.d)
+
+
 def test_fast_path_workspace_entry_point_matches():
     torch = require_gpu()
     from local_linear_attention_amd import lla_forward_ex, lla_forward_ws, lla_workspace_size
