@@ -27,6 +27,15 @@ HIPFLAGS = [
 ]
 
 
+# Per-file flags.  The d = 128 kernels run one wave per SIMD with most of the register file
+# in MFMA accumulators: keep those in architectural VGPRs (the AGPR form made the register
+# allocator shuffle accumulators between AGPRs inside the MFMA loop, which halved the
+# matrix-core rate of a single wave).
+FILE_FLAGS = {
+    "lla_fast128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -43,7 +52,8 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        cmd = [cc, *HIPFLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        extra = FILE_FLAGS.get(os.path.basename(src), [])
+        cmd = [cc, *HIPFLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stdout}{res.stderr}")

@@ -284,36 +284,41 @@ __global__ __launch_bounds__(256) void lla8_rowmax_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------------------
-// Key moments and solve (rows i >= row0).  Block = 4 waves, one query each (4 consecutive
-// rows), one block per CU: a wave's 36 accumulator blocks and its solve take about 400
-// registers (accumulators in AGPRs), so one wave per SIMD.  (Two queries per wave, sharing
-// the key operands, overflow the register file into scratch in the loop.)
-// Per 64-key tile: the fp16 centred key image (feature-major) lands in a ring of three LDS
-// buffers straight from the workspace; each wave takes the scores of its 16 keys for the 4
-// queries (four bf16 MFMAs, operands read from global memory a tile ahead) and stores
-// sqrt-weights sw and fp16 weights w = fp16(sw^2) per query; per 32-key half, each wave reads
-// the key image, forms R = sw (k - a) for its query (packed fp16 multiplies) and accumulates
-// the 36 upper blocks of C = R^T R, plus the block sums S_k of the 4 queries for feature
-// blocks w and w + 4.  Keys past a query carry weight zero: one straight-line block per half,
-// no per-query branches.
-constexpr int K8_Q = 1;                               // queries per wave
-constexpr int K8_BQ = NW8 * K8_Q;                     // 4 queries per block
+// Key moments and solve (rows i >= row0).  Block = 8 waves, one query each (8 consecutive
+// rows), two waves per SIMD: a wave's 36 accumulator blocks (144 registers) plus its
+// operands fit the 256 registers a wave has at that occupancy, and the 8 queries share
+// every tile the block brings into LDS.
+// Two LDS rings advance together: the fp16 centred key image (feature-major, with each
+// tile's weights) and the bf16 key image (key-major, the score operand), the latter one
+// tile ahead.  Step t copies key image t + 2 and score image t + 3 straight from the
+// workspace; waves 0-3 take the scores of 16 keys each of tile t + 1 for the 8 queries (four
+// bf16 MFMAs) and store sqrt-weights sw and fp16 weights w = fp16(sw^2) per query; per
+// 32-key half of tile t, every wave reads the key image, forms R = sw (k - a) for its query
+// (packed fp16 multiplies) and accumulates the 36 upper blocks of C = R^T R, plus the block
+// sums S_k of the 8 queries for feature block w.  Keys past a query carry weight zero: one
+// straight-line block per half, no per-query branches.
+constexpr int KW8 = 8;                                // waves per block
+constexpr int K8_BQ = KW8;                            // queries per block, one per wave
 constexpr int K8_SW = F_BYTES;                        // sqrt-weights [query][key], rows of F_LD halves
-constexpr int K8_SW2 = K8_SW + K8_BQ * F_LD * 2;      // fp16 weights, 16 rows (rows >= 4 zero)
-constexpr int K8_BUF = K8_SW2 + 16 * F_LD * 2;        // 20.8 KiB ring buffer
-constexpr int K8_LOADS = F_BYTES / 1024;              // 18 wave copies per tile
-constexpr int K8_WLOADS = (K8_LOADS + NW8 - 1) / NW8; // 5 per wave
+constexpr int K8_SW2 = K8_SW + K8_BQ * F_LD * 2;      // fp16 weights, 16 rows (rows >= 8 zero)
+constexpr int K8_BUF = K8_SW2 + 16 * F_LD * 2;        // key-image ring buffer
+constexpr int K8_LOADS = F_BYTES / 1024;              // 18 wave copies per key image
+constexpr int K8_WLOADS = (K8_LOADS + KW8 - 1) / KW8; // 3 per wave (surplus repeats the last)
+constexpr int K8_SLOADS = KM_BYTES / 1024;            // 17 wave copies per score image
+constexpr int K8_WSLOADS = (K8_SLOADS + KW8 - 1) / KW8;
+constexpr int K8_NBUF = 3;
+constexpr int K8_SRING = K8_NBUF * K8_BUF;            // score-image ring after the key-image ring
+constexpr int K8_RING = K8_SRING + K8_NBUF * KM_BYTES;
 constexpr int S8_LD = D8 + 4;                         // solve staging row stride (floats)
 constexpr int S8_FLOATS = 16 * S8_LD + 16;            // per wave: a block row of 16 + 16 pivots
-constexpr int K8_SOLVE_BYTES = NW8 * S8_FLOATS * 4;
-constexpr int K8_RING = 3 * K8_BUF;
+constexpr int K8_SOLVE_BYTES = KW8 * S8_FLOATS * 4;
 constexpr int K8_MEAN_OFF = K8_RING > K8_SOLVE_BYTES ? K8_RING : K8_SOLVE_BYTES;
-constexpr int K8_SMEM = K8_MEAN_OFF + (K8_BQ * D8 + NW8 * 16) * 4;
+constexpr int K8_SMEM = K8_MEAN_OFF + (K8_BQ * D8 + 4 * 16) * 4;
 static_assert(K8_SMEM <= 160 * 1024, "one block per CU");
 constexpr int P8_YLD = 2 * D8;                        // per query: yh hi (fp16) | yh lo (fp16)
 constexpr int P8_QSC = 4;                             // per query: gamma, 2^-e, 1/omega', unused
-static_assert(K8_BUF % 16 == 0 && K8_MEAN_OFF % 16 == 0, "LDS areas stay 16-byte aligned");
-static_assert(K8_WLOADS + 4 < 16, "vmcnt operand is 4 bits here");
+static_assert(K8_BUF % 16 == 0 && K8_SRING % 16 == 0 && K8_MEAN_OFF % 16 == 0, "LDS areas stay 16-byte aligned");
+static_assert(K8_BQ <= 16, "score MFMA has 16 query columns");
 
 // Sums and maxima over the 64 lanes of a wave (every lane gets the result): DPP within each
 // row of 16 lanes, then the four row results by readlane.
@@ -336,43 +341,48 @@ __device__ __forceinline__ float wave_max8(float x) {
     return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 
-// Panel K of one query's solve (A y = z, A = C - s s^T / omega' + lam I, 128 x 128 SPD) in
-// one wave, a blocked LDL^T factorisation in place:
+// Panel K of one query's solve (A y = z, A = C - s s^T iom + lam I, 128 x 128 SPD,
+// iom = 1 / omega') in one wave, a blocked LDL^T factorisation in place:
 //   ckk: the 36 upper blocks of C in accumulator layout (lane (g, c) register r of block
 //        (I, J) = C[16 I + 4 g + r][16 J + c]).  The trailing blocks (I, J > K) take the update
 //        C_IJ -= L_IK D_K L_JK^T on 16x16x4 fp32 MFMAs; block row K is replaced by the
 //        multipliers, L[16 J + c][16 K + 4 g + r] in register r of block (K, J).
 //   z[h]: right-hand side of row lane + 64 h, forward-eliminated as the pivots pass.
 //   dd[K]: pivot d of row 16 K + c (lane (g, c)).
-//   sks[h] = s[lane + 64 h] / omega'; skq: s in LDS; Sg: this wave's LDS staging area.
-// Block row K is staged through LDS and read back lane-per-row (lane holds rows lane and
-// lane + 64) with the rank-one downdate applied to each entry once (the trailing updates
-// are linear, so it commutes with them); pivots are broadcast with readlane; the
-// multipliers go back through LDS, to the trailing update's operands and to their place.
+//   skq: s in LDS; Sg: this wave's LDS staging area.
+// Block row K is staged through LDS with the rank-one downdate and the ridge applied to
+// each entry once (the trailing updates are linear, so the downdate commutes with them) and
+// read back lane-per-row (lane holds rows lane and lane + 64); pivots are broadcast with
+// readlane; the multipliers go back through LDS, to the trailing update's operands and to
+// their place.
 template <int K>
 __device__ __forceinline__ void panel8(float4v (&ckk)[36], float (&z)[2], float (&dd)[8], const float thr,
-                                       const float lam, const float (&sks)[2], const float* skq, float* Sg,
+                                       const float lam, const float iom, const float* skq, float* Sg,
                                        const int lane, const int g, const int c) {
     constexpr int H0 = K < 4 ? 0 : 1;   // rows lane < 64 lie above every panel K >= 4
     constexpr int HP = (16 * K) / 64;   // the pivot rows of this panel are rows lane + 64 HP
     float* Dg = Sg + 16 * S8_LD;
+    {
+        float srow[4];
 #pragma unroll
-    for (int J = K; J < 8; ++J)
+        for (int r = 0; r < 4; ++r) srow[r] = skq[16 * K + 4 * g + r] * iom;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float val = ckk[ub8(K, J)][r];
-            if (J == K && 4 * g + r == c) val += lam;
-            Sg[(4 * g + r) * S8_LD + 16 * J + c] = val;
+        for (int J = K; J < 8; ++J) {
+            const float scol = skq[16 * J + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float val = fmaf(-srow[r], scol, ckk[ub8(K, J)][r]);
+                if (J == K && 4 * g + r == c) val += lam;
+                Sg[(4 * g + r) * S8_LD + 16 * J + c] = val;
+            }
         }
+    }
     LDS_FENCE();
-    float skt[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) skt[t] = skq[16 * K + t];
     float Lf[2][16];
 #pragma unroll
     for (int h = H0; h < 2; ++h)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) Lf[h][t] = fmaf(-sks[h], skt[t], Sg[t * S8_LD + lane + 64 * h]);
+        for (int t = 0; t < 16; ++t) Lf[h][t] = Sg[t * S8_LD + lane + 64 * h];
     LDS_FENCE();
     // Rows above the panel (lanes < 16 K when HP = 0) read stale words; their multipliers
     // are zero (row test), so those never reach a live value.
@@ -417,48 +427,49 @@ __device__ __forceinline__ void panel8(float4v (&ckk)[36], float (&z)[2], float 
 #pragma unroll
         for (int r = 0; r < 4; ++r) ckk[ub8(K, J)][r] = Sg[(4 * g + r) * S8_LD + 16 * J + c];
     if constexpr (K < 7) {
-        // Trailing update over the panel columns 16 K + 4 s + g (K-slot g of step s).
-        float dv[4], Lo[8][4];
+        // Trailing update over the panel columns 16 K + 4 s + g (K-slot g of step s); the
+        // operands of block row I are read when its blocks are updated.
+        float dv[4];
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            dv[s4] = Dg[4 * s4 + g];
+        for (int s4 = 0; s4 < 4; ++s4) dv[s4] = Dg[4 * s4 + g];
 #pragma unroll
-            for (int X = K + 1; X < 8; ++X) Lo[X][s4] = Sg[(4 * s4 + g) * S8_LD + 16 * X + c];
-        }
+        for (int I = K + 1; I < 8; ++I) {
+            float LoI[4];
 #pragma unroll
-        for (int I = K + 1; I < 8; ++I)
+            for (int s4 = 0; s4 < 4; ++s4) LoI[s4] = -Sg[(4 * s4 + g) * S8_LD + 16 * I + c];
 #pragma unroll
             for (int J = I; J < 8; ++J)
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4)
-                    ckk[ub8(I, J)] = __builtin_amdgcn_mfma_f32_16x16x4f32(-Lo[I][s4], dv[s4] * Lo[J][s4],
-                                                                           ckk[ub8(I, J)], 0, 0, 0);
+                    ckk[ub8(I, J)] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        LoI[s4], dv[s4] * Sg[(4 * s4 + g) * S8_LD + 16 * J + c], ckk[ub8(I, J)], 0, 0, 0);
+        }
     }
     LDS_FENCE();
 }
 
 // One query's solve.  Returns y[J] = y[16 J + c] in lane (g, c) (the same in every g).
 __device__ __forceinline__ void solve8(float4v (&ckk)[36], float (&z)[2], const float thr, const float lam,
-                                       const float (&sks)[2], const float* skq, float* Sg, float (&y)[8],
+                                       const float iom, const float* skq, float* Sg, float (&y)[8],
                                        const int lane, const int g, const int c) {
     float dd[8];
 #pragma unroll
     for (int J = 0; J < 8; ++J) dd[J] = 0.0f;
-    panel8<0>(ckk, z, dd, thr, lam, sks, skq, Sg, lane, g, c);
+    panel8<0>(ckk, z, dd, thr, lam, iom, skq, Sg, lane, g, c);
     __builtin_amdgcn_sched_barrier(0);
-    panel8<1>(ckk, z, dd, thr, lam, sks, skq, Sg, lane, g, c);
+    panel8<1>(ckk, z, dd, thr, lam, iom, skq, Sg, lane, g, c);
     __builtin_amdgcn_sched_barrier(0);
-    panel8<2>(ckk, z, dd, thr, lam, sks, skq, Sg, lane, g, c);
+    panel8<2>(ckk, z, dd, thr, lam, iom, skq, Sg, lane, g, c);
     __builtin_amdgcn_sched_barrier(0);
-    panel8<3>(ckk, z, dd, thr, lam, sks, skq, Sg, lane, g, c);
+    panel8<3>(ckk, z, dd, thr, lam, iom, skq, Sg, lane, g, c);
     __builtin_amdgcn_sched_barrier(0);
-    panel8<4>(ckk, z, dd, thr, lam, sks, skq, Sg, lane, g, c);
+    panel8<4>(ckk, z, dd, thr, lam, iom, skq, Sg, lane, g, c);
     __builtin_amdgcn_sched_barrier(0);
-    panel8<5>(ckk, z, dd, thr, lam, sks, skq, Sg, lane, g, c);
+    panel8<5>(ckk, z, dd, thr, lam, iom, skq, Sg, lane, g, c);
     __builtin_amdgcn_sched_barrier(0);
-    panel8<6>(ckk, z, dd, thr, lam, sks, skq, Sg, lane, g, c);
+    panel8<6>(ckk, z, dd, thr, lam, iom, skq, Sg, lane, g, c);
     __builtin_amdgcn_sched_barrier(0);
-    panel8<7>(ckk, z, dd, thr, lam, sks, skq, Sg, lane, g, c);
+    panel8<7>(ckk, z, dd, thr, lam, iom, skq, Sg, lane, g, c);
     __builtin_amdgcn_sched_barrier(0);
     // x = D^{-1} z (zero at dropped pivots) in the distributed layout: x[J] = x[16 J + c].
 #pragma unroll
@@ -495,9 +506,9 @@ __device__ __forceinline__ void solve8(float4v (&ckk)[36], float (&z)[2], const 
         }
 }
 
-__global__ __launch_bounds__(256, 1) void lla8_keymom_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ mrow,
-    const float* __restrict__ anchors, const unsigned char* __restrict__ kf, _Float16* __restrict__ yhl,
+__global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
+    const unsigned char* __restrict__ kf, const unsigned char* __restrict__ km, _Float16* __restrict__ yhl,
     float* __restrict__ qsc, int n, int row0, int BH, float sl2, float lambda) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -512,11 +523,12 @@ __global__ __launch_bounds__(256, 1) void lla8_keymom_kernel(
     const int64_t base = static_cast<int64_t>(bh) * n * D8;
 
     // Rows K8_BQ.. of every weight buffer: the zero rows of the block-sum MFMA operand.
-    for (int e = tid; e < 3 * (16 - K8_BQ) * F_LD / 8; e += 256) {
+    for (int e = tid; e < K8_NBUF * (16 - K8_BQ) * F_LD / 8; e += KW8 * 64) {
         const int bsel = e / ((16 - K8_BQ) * F_LD / 8), rem = e % ((16 - K8_BQ) * F_LD / 8);
         *reinterpret_cast<uint4*>(smem + bsel * K8_BUF + K8_SW2 + K8_BQ * F_LD * 2 + rem * 16) = make_uint4(0, 0, 0, 0);
     }
-    // Score operand: column c < 4 is query i0 + c (the other columns are zero).
+    // Score operand (waves 0-3): column c < 8 is query i0 + c (the other columns are zero).
+    const bool scorer = wu < 4;
     const int qcol = min(i0 + c, n - 1);
     const bool colv = c < K8_BQ;
     const float mcol = mrow[static_cast<int64_t>(bh) * prows + (qcol - row0)];   // log2 units
@@ -527,141 +539,140 @@ __global__ __launch_bounds__(256, 1) void lla8_keymom_kernel(
         if (colv) raw = *reinterpret_cast<const uint4*>(q + base + static_cast<int64_t>(qcol) * D8 + ks * 32 + 8 * g);
         qf[ks] = __builtin_bit_cast(bf16x8, raw);
     }
-    // Scores of key block w (16 keys) of a tile: lane (g, c) register r = key 16 w + 4 g + r,
-    // query c.  Issued a half-tile before they are stored, so the MFMA latency hides.
     float om2p = 0.0f;   // fp16 weights of query c summed over this lane's keys
     const float hs = 0.5f * sl2, hm = 0.5f * mcol;
-    auto score_mfma = [&](const uint4 (&kq)[4]) {
+    auto kbuf = [&](int tt) { return smem + (tt % K8_NBUF) * K8_BUF; };
+    auto sbuf = [&](int tt) { return smem + K8_SRING + (tt % K8_NBUF) * KM_BYTES; };
+    // Scores of key block w (16 keys) of tile tt from its score image: lane (g, c) register
+    // r = key 16 w + 4 g + r, query c; sqrt-weights and fp16 weights into the key buffer of tt.
+    auto scores = [&](int tt) {
+        const unsigned char* sb = sbuf(tt);
         float4v s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) s = mfma_bf16(__builtin_bit_cast(bf16x8, kq[ks]), qf[ks], s);
-        return s;
-    };
-    auto score_store = [&](float4v s, unsigned char* buf, int j0) {
+        for (int ks = 0; ks < 4; ++ks)
+            s = mfma_bf16(*reinterpret_cast<const bf16x8*>(sb + (16 * wu + c) * (K_LD * 2) + 64 * ks + 16 * g), qf[ks], s);
+        const int j0 = tt * T8;
         float e[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) e[rr] = __builtin_amdgcn_exp2f(fmaf(s[rr], hs, -hm));
         if (j0 + T8 - 1 > i0) {   // block-uniform: keys past some query of the block
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) e[rr] = j0 + 16 * w + 4 * g + rr <= qcol ? e[rr] : 0.0f;
+            for (int rr = 0; rr < 4; ++rr) e[rr] = j0 + 16 * wu + 4 * g + rr <= qcol ? e[rr] : 0.0f;
         }
         half4 sw4;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) sw4[rr] = static_cast<_Float16>(e[rr]);
         const half4 w4 = sw4 * sw4;
         if (colv) {
-            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + K8_SW) + c * F_LD + 16 * w + 4 * g) = sw4;
-            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + K8_SW2) + c * F_LD + 16 * w + 4 * g) = w4;
+            unsigned char* kb = kbuf(tt);
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(kb + K8_SW) + c * F_LD + 16 * wu + 4 * g) = sw4;
+            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(kb + K8_SW2) + c * F_LD + 16 * wu + 4 * g) = w4;
             const h16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
             om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 0, 1), one, om2p, false);
             om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 2, 3), one, om2p, false);
         }
     };
 
-    float4v ckk[K8_Q][36];
+    float4v ckk[36];
 #pragma unroll
-    for (int qq = 0; qq < K8_Q; ++qq)
-#pragma unroll
-        for (int b = 0; b < 36; ++b) ckk[qq][b] = float4v{0.f, 0.f, 0.f, 0.f};
-    // S_k of the block's queries: lane (g, c) register r = query 4 g + r, feature 16 w + c (sk0)
-    // and 16 (w + 4) + c (sk1).
-    float4v sk0 = {0.f, 0.f, 0.f, 0.f}, sk1 = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 36; ++b) ckk[b] = float4v{0.f, 0.f, 0.f, 0.f};
+    // S_k of the block's queries: lane (g, c) register r = query 4 g + r, feature 16 w + c.
+    float4v sk = {0.f, 0.f, 0.f, 0.f};
 
     const int ntiles = last / T8 + 1;
     const int ptiles = (n + T8 - 1) / T8;
-    const __amdgpu_buffer_rsrc_t img = __builtin_amdgcn_make_buffer_rsrc(
+    const __amdgpu_buffer_rsrc_t kimg = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(uniform_ptr(kf + static_cast<int64_t>(bh) * ptiles * F_BYTES)), 0,
         ptiles * F_BYTES, 0x00020000);
-    int voff[K8_WLOADS];
-#pragma unroll
-    for (int e = 0; e < K8_WLOADS; ++e) voff[e] = lane * 16 + min(wu + NW8 * e, K8_LOADS - 1) * 1024;
-    // The head's keys (bf16) for the score operand; keys at or past n lie beyond the
-    // resource's size and read as zero (their weights are masked anyway).
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(uniform_ptr(reinterpret_cast<const unsigned char*>(k + base))), 0, n * D8 * 2,
-        0x00020000);
-    const int kq_off = (16 * w + c) * D8 * 2 + 16 * g;
+    const __amdgpu_buffer_rsrc_t simg = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(km + static_cast<int64_t>(bh) * ptiles * KM_STRIDE8)), 0,
+        ptiles * KM_STRIDE8, 0x00020000);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-    auto buf = [&](int tt) { return smem + (tt % 3) * K8_BUF; };
-    // Tile tt: its score operand first, then its image (wave w copies KiB chunks w, w + 4, ...;
-    // every wave issues exactly K8_WLOADS copies, surplus ones repeating the last chunk).
-    // Past the last tile the last one is re-read into a buffer nobody reads again.
-    auto issue = [&](int tt, uint4 (&kq)[4]) {
+    // Copies of key image tt into key buffer tt % 3 and of score image tt (the bf16 half of
+    // the tile's key-major images) into score buffer tt % 3: wave w copies KiB chunks w,
+    // w + 8, ...; every wave issues the same number of copies, surplus ones repeating the
+    // last chunk.  Tiles past the last one re-read the last into buffers nobody reads again.
+    auto issue_k = [&](int tt) {
         const int ts = min(tt, ntiles - 1);
-        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % 3) * K8_BUF);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            kq[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off + 64 * ks,
-                                                                                      ts * T8 * D8 * 2, 0));
+        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % K8_NBUF) * K8_BUF);
 #pragma unroll
         for (int e = 0; e < K8_WLOADS; ++e) {
-            const int u = min(wu + NW8 * e, K8_LOADS - 1);
+            const int u = min(wu + KW8 * e, K8_LOADS - 1);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                img, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
-                16, voff[e], ts * F_BYTES, 0, 0);
+                kimg, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
+                16, lane * 16 + u * 1024, ts * F_BYTES, 0, 0);
         }
     };
-    // After tile t+1's image come tile t+2's 4 + K8_WLOADS loads.
-    auto wait_tile = [] {
-        __builtin_amdgcn_s_waitcnt((K8_WLOADS + 4) | (0x7 << 4) | (0xF << 8));
+    auto issue_s = [&](int tt) {
+        const int ts = min(tt, ntiles - 1);
+        const uint32_t dst = lds0 + static_cast<uint32_t>(K8_SRING + (tt % K8_NBUF) * KM_BYTES);
+#pragma unroll
+        for (int e = 0; e < K8_WSLOADS; ++e) {
+            const int u = min(wu + KW8 * e, K8_SLOADS - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                simg, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
+                16, lane * 16 + u * 1024, ts * KM_STRIDE8, 0, 0);
+        }
+    };
+    // Loads complete in order; after key image t + 1 and score image t + 2 come key image
+    // t + 2 and score image t + 3, so vmcnt <= K8_WLOADS + K8_WSLOADS means the former two
+    // have landed.  Encoding: vmcnt bits [3:0] and [15:14]; expcnt, lgkmcnt at their maxima.
+    constexpr int K8_VM = K8_WLOADS + K8_WSLOADS;
+    static_assert(K8_VM < 16, "vmcnt low bits");
+    auto wait_tiles = [] {
+        __builtin_amdgcn_s_waitcnt(K8_VM | (0x7 << 4) | (0xF << 8));
         LDS_FENCE();
     };
-    // This wave's LDS stores are complete (lgkmcnt 0); loads still in flight (the tile two
-    // steps ahead) are deliberately not waited for, which __syncthreads() would do.
+    // This wave's LDS stores are complete (lgkmcnt 0); loads still in flight (the images a
+    // step ahead) are deliberately not waited for, which __syncthreads() would do.
     auto ring_barrier = [] {
         __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
         LDS_FENCE();
         __builtin_amdgcn_s_barrier();
         LDS_FENCE();
     };
-    auto compute = [&](int t, const unsigned char* cur, int sub) {
-        const int j0 = t * T8;
-        if (j0 + 32 * sub > last) return;   // block-uniform: past every query of the block
+    // One 32-key half of tile t: R = sw (k - a) (one rounding, packed fp16 multiplies, in
+    // place over the key rows), the 36 upper blocks of R^T R and the block sums of the 8
+    // queries for feature block w.
+    auto compute = [&](int t, int sub) {
+        const unsigned char* cur = kbuf(t);
         const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
         const _Float16* Sw = reinterpret_cast<const _Float16*>(cur + K8_SW);
         const _Float16* Sw2 = reinterpret_cast<const _Float16*>(cur + K8_SW2);
         const int ko = 32 * sub + 8 * g;
-        half8 kf8[8];
+        half8 rk[8];
 #pragma unroll
-        for (int fb = 0; fb < 8; ++fb) kf8[fb] = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * F_LD + ko);
+        for (int fb = 0; fb < 8; ++fb) rk[fb] = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * F_LD + ko);
+        const half8 sw = *reinterpret_cast<const half8*>(Sw + wu * F_LD + ko);
         const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * F_LD + ko);
-        const half8 kw0 = *reinterpret_cast<const half8*>(Kt + (wu * 16 + c) * F_LD + ko);
-        const half8 kw1 = *reinterpret_cast<const half8*>(Kt + ((wu + 4) * 16 + c) * F_LD + ko);
+        const half8 kw = *reinterpret_cast<const half8*>(Kt + (wu * 16 + c) * F_LD + ko);
 #pragma unroll
-        for (int qq = 0; qq < K8_Q; ++qq) {
-            const half8 sw = *reinterpret_cast<const half8*>(Sw + (wu + 4 * qq) * F_LD + ko);
-            half8 rk[8];
+        for (int fb = 0; fb < 8; ++fb) rk[fb] = rk[fb] * sw;
 #pragma unroll
-            for (int fb = 0; fb < 8; ++fb) rk[fb] = kf8[fb] * sw;
+        for (int I = 0; I < 8; ++I)
 #pragma unroll
-            for (int I = 0; I < 8; ++I)
-#pragma unroll
-                for (int J = I; J < 8; ++J) ckk[qq][ub8(I, J)] = mfma_f16(rk[I], rk[J], ckk[qq][ub8(I, J)]);
-        }
-        sk0 = mfma_f16(w8, kw0, sk0);
-        sk1 = mfma_f16(w8, kw1, sk1);
+            for (int J = I; J < 8; ++J) ckk[ub8(I, J)] = mfma_f16(rk[I], rk[J], ckk[ub8(I, J)]);
+        sk = mfma_f16(w8, kw, sk);
     };
-    uint4 aq[4], bq[4];
-    issue(0, aq);
-    issue(1, bq);
-    wait_tile();
-    score_store(score_mfma(aq), buf(0), 0);
+    // Prologue: score image 0, then (key image s + 2, score image s + 3) for s = -2, -1 as in
+    // the loop.  Once score images 0 and 1 and key image 0 have landed, the scores of tile 0.
+    issue_s(0);
+    issue_k(0);
+    issue_s(1);
+    issue_k(1);
+    issue_s(2);
+    __builtin_amdgcn_s_waitcnt(K8_VM | (0x7 << 4) | (0xF << 8));   // s0, k0, s1 landed
     ring_barrier();
-    for (int t = 0; t < ntiles; t += 2) {
-        issue(t + 2, aq);
-        compute(t, buf(t), 0);
-        const float4v sb = score_mfma(bq);
-        compute(t, buf(t), 1);
-        if (t + 1 < ntiles) score_store(sb, buf(t + 1), (t + 1) * T8);
-        wait_tile();
-        ring_barrier();
-        if (t + 1 >= ntiles) break;
-        issue(t + 3, bq);
-        compute(t + 1, buf(t + 1), 0);
-        const float4v sa = score_mfma(aq);
-        compute(t + 1, buf(t + 1), 1);
-        if (t + 2 < ntiles) score_store(sa, buf(t + 2), (t + 2) * T8);
-        wait_tile();
+    if (scorer) scores(0);
+    ring_barrier();
+    // Step t: key image t and its weights are in LDS, and score image t + 1.
+    for (int t = 0; t < ntiles; ++t) {
+        issue_k(t + 2);
+        issue_s(t + 3);
+        if (scorer) scores(t + 1);
+        compute(t, 0);
+        if (t * T8 + 32 <= last) compute(t, 1);
+        wait_tiles();   // key image t + 1 and score image t + 2
         ring_barrier();
     }
     // Copies issued past the last tile may still be landing in ring buffers that the solve
@@ -671,95 +682,83 @@ __global__ __launch_bounds__(256, 1) void lla8_keymom_kernel(
 
     // ---- block sums -> LDS (outside the solve area)
     float* skm = reinterpret_cast<float*>(smem + K8_MEAN_OFF);   // [query][feature]
-    float* omp = skm + K8_BQ * D8;                                // [wave][query]
+    float* omp = skm + K8_BQ * D8;                                // [scoring wave][query]
     om2p += __shfl_xor(om2p, 16);
     om2p += __shfl_xor(om2p, 32);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-        if (4 * g + r < K8_BQ) {
-            skm[(4 * g + r) * D8 + 16 * w + c] = sk0[r];
-            skm[(4 * g + r) * D8 + 16 * (w + 4) + c] = sk1[r];
-        }
-    if (g == 0 && colv) omp[w * 16 + c] = om2p;
+        if (4 * g + r < K8_BQ) skm[(4 * g + r) * D8 + 16 * w + c] = sk[r];
+    if (scorer && g == 0 && colv) omp[w * 16 + c] = om2p;
     __syncthreads();
 
     // ---- the wave's solve; row layout: lane holds rows lane and lane + 64.
     // z = kbar - q with kbar = a + S_k / omega'.
     float* Sg = reinterpret_cast<float*>(smem) + w * S8_FLOATS;
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * D8;
-    // One query's solve and output; called with a compile-time query index so that the
-    // accumulator array stays in registers.
-    auto solve_query = [&](auto qqc) {
-        constexpr int qq = decltype(qqc)::value;
-        const int ql = wu + 4 * qq;
-        const int iq = i0 + ql;
-        const int iqc = min(iq, n - 1);
-        float om2 = 0.0f;
+    const int iq = i0 + wu;
+    const int iqc = min(iq, n - 1);
+    float om2 = 0.0f;
 #pragma unroll
-        for (int t = 0; t < NW8; ++t) om2 += omp[t * 16 + ql];
-        const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
-        const float* skq = skm + ql * D8;
-        const float lam = lambda * exp2f(-mrow[static_cast<int64_t>(bh) * prows + (iqc - row0)]);
-        float z[2], sks[2];
+    for (int t = 0; t < 4; ++t) om2 += omp[t * 16 + wu];
+    const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
+    const float* skq = skm + wu * D8;
+    const float lam = lambda * exp2f(-mrow[static_cast<int64_t>(bh) * prows + (iqc - row0)]);
+    float z[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int a = lane + 64 * h;
-            sks[h] = skq[a] * iom2;
-            z[h] = fmaf(skq[a], iom2, anc[a]) - bf16_bits_to_f32(q[base + static_cast<int64_t>(iqc) * D8 + a]);
-        }
-        // lambda > 0: drop only pivots that rounding made non-positive; lambda = 0: also drop
-        // directions the prefix leaves (numerically) undetermined, below 1e-6 of the largest
-        // diagonal entry of the downdated matrix.
-        float thr = 0.0f;
-        if (!(lambda > 0.0f)) {
-            float dmax = -INFINITY;
+    for (int h = 0; h < 2; ++h) {
+        const int a = lane + 64 * h;
+        z[h] = fmaf(skq[a], iom2, anc[a]) - bf16_bits_to_f32(q[base + static_cast<int64_t>(iqc) * D8 + a]);
+    }
+    // lambda > 0: drop only pivots that rounding made non-positive; lambda = 0: also drop
+    // directions the prefix leaves (numerically) undetermined, below 1e-6 of the largest
+    // diagonal entry of the downdated matrix.
+    float thr = 0.0f;
+    if (!(lambda > 0.0f)) {
+        float dmax = -INFINITY;
 #pragma unroll
-            for (int I = 0; I < 8; ++I)
+        for (int I = 0; I < 8; ++I)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * g + r == c) {
-                        const float sv = skq[16 * I + c];
-                        dmax = fmaxf(dmax, ckk[qq][ub8(I, I)][r] - sv * sv * iom2 + lam);
-                    }
-            thr = 1e-6f * wave_max8(dmax);
-        }
-        float yd[8];
-        solve8(ckk[qq], z, thr, lam, sks, skq, Sg, yd, lane, g, c);
-        LDS_FENCE();
-        // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together), and
-        // gamma = 1 + S_k . yh / omega'.  Lane (g, c) holds rows 16 J + c; lanes g = 0 store.
-        float amax = 0.0f;
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r == c) {
+                    const float sv = skq[16 * I + c];
+                    dmax = fmaxf(dmax, ckk[ub8(I, I)][r] - sv * sv * iom2 + lam);
+                }
+        thr = 1e-6f * wave_max8(dmax);
+    }
+    float yd[8];
+    solve8(ckk, z, thr, lam, iom2, skq, Sg, yd, lane, g, c);
+    LDS_FENCE();
+    // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together), and
+    // gamma = 1 + S_k . yh / omega'.  Lane (g, c) holds rows 16 J + c; lanes g = 0 store.
+    float amax = 0.0f;
 #pragma unroll
-        for (int J = 0; J < 8; ++J) amax = fmaxf(amax, fabsf(yd[J] * om2));
-        amax = wave_max8(amax);
-        int ex = 0;
-        (void)frexpf(amax, &ex);
-        ex = max(ex, -100);   // keeps 2^(14 - ex) finite
-        const float sig = amax > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
-        _Float16 hi[8], lo[8];
-        float dot = 0.0f;
+    for (int J = 0; J < 8; ++J) amax = fmaxf(amax, fabsf(yd[J] * om2));
+    amax = wave_max8(amax);
+    int ex = 0;
+    (void)frexpf(amax, &ex);
+    ex = max(ex, -100);   // keeps 2^(14 - ex) finite
+    const float sig = amax > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
+    _Float16 hi[8], lo[8];
+    float dot = 0.0f;
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+        const float ys = (yd[J] * om2) * sig;
+        hi[J] = static_cast<_Float16>(ys);
+        lo[J] = static_cast<_Float16>(ys - static_cast<float>(hi[J]));
+        dot = fmaf(skq[16 * J + c], static_cast<float>(hi[J]) + static_cast<float>(lo[J]), dot);
+    }
+    dot = wave_sum8(dot) * 0.25f;   // every row of 16 lanes holds the same 128 products
+    if (iq < n && g == 0) {
+        const int64_t qrow = static_cast<int64_t>(bh) * prows + (iq - row0);
 #pragma unroll
         for (int J = 0; J < 8; ++J) {
-            const float ys = (yd[J] * om2) * sig;
-            hi[J] = static_cast<_Float16>(ys);
-            lo[J] = static_cast<_Float16>(ys - static_cast<float>(hi[J]));
-            dot = fmaf(skq[16 * J + c], static_cast<float>(hi[J]) + static_cast<float>(lo[J]), dot);
+            yhl[qrow * P8_YLD + 16 * J + c] = hi[J];
+            yhl[qrow * P8_YLD + D8 + 16 * J + c] = lo[J];
         }
-        dot = wave_sum8(dot) * 0.25f;   // every row of 16 lanes holds the same 128 products
-        if (iq < n && g == 0) {
-            const int64_t qrow = static_cast<int64_t>(bh) * prows + (iq - row0);
-#pragma unroll
-            for (int J = 0; J < 8; ++J) {
-                yhl[qrow * P8_YLD + 16 * J + c] = hi[J];
-                yhl[qrow * P8_YLD + D8 + 16 * J + c] = lo[J];
-            }
-            if (c == 0)
-                *reinterpret_cast<float4v*>(qsc + qrow * P8_QSC) =
-                    float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, 0.0f};
-        }
-    };
-    static_assert(K8_Q == 1, "one solve per wave");
-    solve_query(std::integral_constant<int, 0>{});
+        if (c == 0)
+            *reinterpret_cast<float4v*>(qsc + qrow * P8_QSC) =
+                float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, 0.0f};
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1038,8 +1037,8 @@ hipError_t launch_fast128(const Problem& p, void* workspace) {
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_keymom_kernel");
-    lla8_keymom_kernel<<<dim3(static_cast<unsigned>(BH) * ((prows + K8_BQ - 1) / K8_BQ)), dim3(256), K8_SMEM,
-                         p.stream>>>(q, k, mrow, anchors, kf, yhl, qsc, n, row0, BH, sl2,
+    lla8_keymom_kernel<<<dim3(static_cast<unsigned>(BH) * ((prows + K8_BQ - 1) / K8_BQ)), dim3(KW8 * 64), K8_SMEM,
+                         p.stream>>>(q, mrow, anchors, kf, km, yhl, qsc, n, row0, BH, sl2,
                                      static_cast<float>(p.lambda));
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
