@@ -61,6 +61,7 @@ PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d: f64
               "cg": "f64 (conjugate gradient over the prefix)"}
 KERNEL_BOUND = {
     "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla_exact_list_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_cg_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_short_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_rowmax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
@@ -94,11 +95,13 @@ KERNEL_BOUND = {
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
     "cg": ["lla_cg_kernel"],
+    # the last launch recomputes in fp64 the rows the range and finiteness checks hand back
+    # (none on these workloads)
     "fast": ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel",
-             "lla_probe_kernel"],
+             "lla_probe_kernel", "lla_exact_list_kernel"],
     # d = 128: rows i < 4d on the fp64 kernel, the rest on the d = 128 matrix-core kernels
     "fast128": ["lla_exact_kernel", "lla8_anchor_kernel", "lla8_pack_kernel", "lla8_rowmax_kernel",
-                "lla8_keymom_kernel", "lla8_probe_kernel"],
+                "lla8_keymom_kernel", "lla8_probe_kernel", "lla_exact_list_kernel"],
 }
 
 
@@ -145,6 +148,8 @@ def kernel_flops(name, B, H, n, d, path):
         return pair_count(BH, 0, row0) * (2 * d + moments + 2 * d * d) + BH * row0 * per_query
     if name in ("lla_anchor_kernel", "lla_pack_kernel", "lla8_anchor_kernel", "lla8_pack_kernel"):
         return 0                      # data movement only (K, V summed and repacked once)
+    if name == "lla_exact_list_kernel":
+        return 0                      # rows handed back by the fast path's checks: none here
     if name in ("lla_rowmax_kernel", "lla8_rowmax_kernel"):
         return pair_count(BH, row0, n) * 2 * d
     if name == "lla8_keymom_kernel":

@@ -57,6 +57,33 @@ __device__ __forceinline__ float4v mfma_f16(half8 a, half8 b, float4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Guard of the matrix-core paths' fp16 images.  `guard` (workspace, unsigned words): [0] the
+// number of rows handed back to the fp64 kernel, [1 + 2 bh] and [2 + 2 bh] the largest
+// |k - a| and |v - a_v| of head bh (fp32 bit patterns of non-negative values, so the integer
+// maximum is the float maximum); `list` (workspace): the handed-back rows, entries bh * n + i.
+// A head whose centred keys or values leave the range where their fp16 images are accurate
+// (above 2^14, near the fp16 maximum 65504; or non-zero but below 2^-10, where the fp16
+// spacing is no longer small against them) has every row of the path recomputed in fp64; so
+// has every row whose output is not finite, or whose solve dropped a pivot although the ridge
+// keeps its system positive definite.
+__device__ __forceinline__ bool head_unsafe(const unsigned* guard, int bh) {
+    // Maxima are stored as the bits of non-negative floats, so unsigned order is float
+    // order (and a NaN or inf reads as too large).  Safe range: 2^-10 <= max <= 2^14.
+    const unsigned mk = guard[1 + 2 * bh], mv = guard[2 + 2 * bh];
+    const unsigned hi = 0x46800000u, lo = 0x3A800000u;
+    return mk > hi || mv > hi || (mk != 0u && mk < lo) || (mv != 0u && mv < lo);
+}
+__device__ __forceinline__ void hand_back(unsigned* guard, int* list, int bh, int n, int i) {
+    const unsigned slot = atomicAdd(guard, 1u);
+    list[slot] = bh * n + i;
+}
+// Largest |x| over the wave, then one atomic max per wave into *dst (x >= 0 or NaN).
+__device__ __forceinline__ void wave_atomic_max(unsigned* dst, float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    if ((threadIdx.x & 63) == 0) atomicMax(dst, __float_as_uint(x));
+}
+
 // Block b -> (head bh, row block blk).  Work-groups go round-robin to the 8 XCDs, so
 // b % 8 picks the XCD: heads are taken 8 at a time (head 8 G + b % 8 on XCD b % 8) and, in
 // each group of 8, row blocks run longest first.  Each XCD's L2 then holds the packed K/V of

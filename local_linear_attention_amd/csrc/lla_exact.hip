@@ -36,11 +36,16 @@ template <> struct ExactCfg<32> { static constexpr int TR = 16, TC = 16; };
 template <> struct ExactCfg<64> { static constexpr int TR = 16, TC = 16; };
 template <> struct ExactCfg<128> { static constexpr int TR = 16, TC = 32; };
 
-template <typename TIn, int D>
+// LIST = false: block b computes row rows - 1 - b / BH of head b % BH (rows 0 .. rows-1 of
+// every head, longest first).  LIST = true: the blocks share the *count rows listed in
+// `list` (entry bh * n + i), block b taking entries b, b + gridDim.x, ... -- the rows the
+// matrix-core path hands back (see the guard of lla_fast.hip).
+template <typename TIn, int D, bool LIST>
 __global__ __launch_bounds__(ExactCfg<D>::TR * ExactCfg<D>::TC)
 void lla_exact_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                       const TIn* __restrict__ v, float* __restrict__ out,
-                      int n, int rows, int BH, double inv_h, double lambda) {
+                      int n, int rows, int BH, double inv_h, double lambda,
+                      const int* __restrict__ list, const int* __restrict__ count) {
     constexpr int TR = ExactCfg<D>::TR, TC = ExactCfg<D>::TC, NT = TR * TC;
     constexpr int RA = D / TR, CB = D / TC;
     constexpr int CHK = 2048 / D;   // keys per staged chunk (16 KiB of fp64 per array)
@@ -62,9 +67,7 @@ void lla_exact_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
 
     const int tid = threadIdx.x;
     const int tr = tid / TC, tc = tid % TC;
-    // Rows 0 .. rows-1 of every head, longest rows first.
-    const int i = rows - 1 - static_cast<int>(blockIdx.x / BH);
-    const int bh = static_cast<int>(blockIdx.x % BH);
+    auto row_body = [&](const int i, const int bh) {
     const int64_t base = static_cast<int64_t>(bh) * n * D;
     const TIn* kh = k + base;
     const TIn* vh = v + base;
@@ -275,6 +278,17 @@ void lla_exact_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
         for (int t = 0; t < TR; ++t) acc += part[t * D + tid];
         out[base + static_cast<int64_t>(i) * D + tid] = static_cast<float>(vbar[tid] - acc);
     }
+    };
+    if constexpr (!LIST) {
+        row_body(rows - 1 - static_cast<int>(blockIdx.x / BH), static_cast<int>(blockIdx.x % BH));
+    } else {
+        const int cnt = *count;
+        for (int e = static_cast<int>(blockIdx.x); e < cnt; e += static_cast<int>(gridDim.x)) {
+            const int code = list[e];
+            row_body(code % n, code / n);
+            __syncthreads();   // the next row restages every shared array
+        }
+    }
 }
 
 template <typename TIn, int D>
@@ -283,11 +297,34 @@ hipError_t launch_exact_t(const Problem& p, int rows) {
     const int BH = static_cast<int>(p.B * p.H);
     const unsigned blocks = static_cast<unsigned>(p.B * p.H * rows);
     prof_begin(p.stream, "lla_exact_kernel");
-    lla_exact_kernel<TIn, D><<<dim3(blocks), dim3(NT), 0, p.stream>>>(
+    lla_exact_kernel<TIn, D, false><<<dim3(blocks), dim3(NT), 0, p.stream>>>(
         static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v),
-        p.out, static_cast<int>(p.n), rows, BH, 1.0 / p.h, p.lambda);
+        p.out, static_cast<int>(p.n), rows, BH, 1.0 / p.h, p.lambda, nullptr, nullptr);
     prof_end(p.stream);
     return hipGetLastError();
+}
+
+template <typename TIn, int D>
+hipError_t launch_exact_list_t(const Problem& p, const int* list, const int* count, int blocks) {
+    constexpr int NT = ExactCfg<D>::TR * ExactCfg<D>::TC;
+    const int BH = static_cast<int>(p.B * p.H);
+    prof_begin(p.stream, "lla_exact_list_kernel");
+    lla_exact_kernel<TIn, D, true><<<dim3(static_cast<unsigned>(blocks)), dim3(NT), 0, p.stream>>>(
+        static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v),
+        p.out, static_cast<int>(p.n), 0, BH, 1.0 / p.h, p.lambda, list, count);
+    prof_end(p.stream);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_exact_list_d(const Problem& p, const int* list, const int* count, int blocks) {
+    switch (p.d) {
+        case 16: return launch_exact_list_t<TIn, 16>(p, list, count, blocks);
+        case 32: return launch_exact_list_t<TIn, 32>(p, list, count, blocks);
+        case 64: return launch_exact_list_t<TIn, 64>(p, list, count, blocks);
+        case 128: return launch_exact_list_t<TIn, 128>(p, list, count, blocks);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <typename TIn>
@@ -306,6 +343,12 @@ hipError_t launch_exact_d(const Problem& p, int rows) {
 hipError_t launch_exact(const Problem& p, int rows) {
     if (rows <= 0) return hipSuccess;
     return p.dtype == 0 ? launch_exact_d<float>(p, rows) : launch_exact_d<uint16_t>(p, rows);
+}
+
+hipError_t launch_exact_list(const Problem& p, const int* list, const int* count, int blocks) {
+    if (blocks <= 0) return hipSuccess;
+    return p.dtype == 0 ? launch_exact_list_d<float>(p, list, count, blocks)
+                        : launch_exact_list_d<uint16_t>(p, list, count, blocks);
 }
 
 }  // namespace lla

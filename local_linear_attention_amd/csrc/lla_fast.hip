@@ -94,11 +94,14 @@ static_assert(PACK_TILE_BYTES % 1024 == 0, "tile image must be whole wave copies
 // every 16th key of the slice; the 16 key phases are then added up through LDS.
 __global__ __launch_bounds__(256) void lla_anchor_kernel(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
-                                                         float* __restrict__ partial, int n) {
+                                                         float* __restrict__ partial, unsigned* __restrict__ guard,
+                                                         int n) {
     __shared__ float sums[16][2 * FD + 4];
     const int bh = static_cast<int>(blockIdx.x) / ANCHOR_SLICES;
     const int sl = static_cast<int>(blockIdx.x) % ANCHOR_SLICES;
     const int tid = threadIdx.x, fgrp = tid & 15, ph = tid >> 4;
+    if (sl == 0 && tid < 2) guard[1 + 2 * bh + tid] = 0u;   // the head's range maxima
+    if (blockIdx.x == 0 && tid == 2) guard[0] = 0u;         // no rows handed back yet
     const int na = min(n, 2 * FD);
     const int len = (na + ANCHOR_SLICES - 1) / ANCHOR_SLICES;
     const int j_lo = sl * len, j_hi = min(na, j_lo + len);
@@ -134,7 +137,8 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
                                                        const float* __restrict__ partial,
                                                        float* __restrict__ anchors,
                                                        unsigned char* __restrict__ packed,
-                                                       unsigned char* __restrict__ kimg, int n,
+                                                       unsigned char* __restrict__ kimg,
+                                                       unsigned* __restrict__ guard, int n,
                                                        int ntiles) {
     __shared__ float anc[2 * FD];
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
@@ -189,6 +193,25 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
     const uint32_t ka[4] = {k0.x, k0.y, k0.z, k0.w}, kb[4] = {k1.x, k1.y, k1.z, k1.w};
     const uint32_t va[4] = {v0.x, v0.y, v0.z, v0.w}, vb[4] = {v1.x, v1.y, v1.z, v1.w};
     const bool za = ja >= n, zb = jb >= n;
+    {   // the head's largest centred magnitudes, for the range guard
+        float mk = 0.0f, mv = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int hi = e & 1;
+            const float ak = anc[8 * fg + e], av = anc[FD + 8 * fg + e];
+            const auto f = [&](uint32_t wd) { return __uint_as_float(hi ? (wd & 0xffff0000u) : (wd << 16)); };
+            if (!za) {
+                mk = fmaxf(mk, fabsf(f(ka[e >> 1]) - ak));
+                mv = fmaxf(mv, fabsf(f(va[e >> 1]) - av));
+            }
+            if (!zb) {
+                mk = fmaxf(mk, fabsf(f(kb[e >> 1]) - ak));
+                mv = fmaxf(mv, fabsf(f(vb[e >> 1]) - av));
+            }
+        }
+        wave_atomic_max(guard + 1 + 2 * bh, mk);
+        wave_atomic_max(guard + 2 + 2 * bh, mv);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int row = 8 * fg + e;
@@ -333,7 +356,7 @@ __device__ __forceinline__ constexpr int ublk(int I, int J) { return I * 4 - I *
 // Lt[P][a] = L[a][P]; the trailing blocks, still in the accumulators, take the update
 // L D L^T on the matrix cores (fp32); D L^T y = z is then solved backwards.
 __device__ __forceinline__ float ldl_solve_wave(float4v (&ckk)[10], float z, const float thresh, float* Lt,
-                                                const int lane, const int g, const int c) {
+                                                const int lane, const int g, const int c, bool& dropped) {
     constexpr int ALD = FD + 1;
     float* dvec = Lt + FD * ALD;
     float dreg = 0.0f;   // lane P ends up holding the pivot d_P
@@ -358,6 +381,7 @@ __device__ __forceinline__ float ldl_solve_wave(float4v (&ckk)[10], float z, con
             const float piv = lane_value(Lf[p], P);
             // Reciprocal pivot (about 1 ulp); a dropped pivot gets a zero column of L.
             const float inv = piv > thresh ? __builtin_amdgcn_rcpf(piv) : 0.0f;
+            dropped = dropped || !(piv > thresh);
             int row = lane;
             asm volatile("" : "+v"(row));   // row test per step: no precomputed lane masks
             const float f = row > P ? Lf[p] * inv : 0.0f;
@@ -407,7 +431,7 @@ __device__ __forceinline__ void moments_block(
     const int bidx, unsigned char* smem, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ mrow,
     const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
-    float* __restrict__ out,
+    float* __restrict__ out, unsigned* __restrict__ guard, int* __restrict__ list,
     int n, int row0, int row1, int BH, float sl2, float lambda) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -421,6 +445,10 @@ __device__ __forceinline__ void moments_block(
     const int i0 = row0 + blk * B_WAVES;
     const int i = i0 + w;
     const bool valid = i < row1;
+    if (head_unsafe(guard, bh)) {   // block-uniform: the head's rows go to the fp64 kernel
+        if (valid && lane == 0) hand_back(guard, list, bh, n, i);
+        return;
+    }
     const int ic = min(i, row1 - 1);
     const int last = min(i0 + B_WAVES - 1, row1 - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
@@ -670,7 +698,8 @@ __device__ __forceinline__ void moments_block(
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD;
     float z = fmaf(mq[lane], iom2, anc[lane]) - qa;
 
-    const float ylane = ldl_solve_wave(ckk, z, thresh, Lt, lane, g, c);
+    bool dropped = false;
+    const float ylane = ldl_solve_wave(ckk, z, thresh, Lt, lane, g, c, dropped);
     yv[lane] = ylane;
     LDS_FENCE();
 
@@ -689,11 +718,20 @@ __device__ __forceinline__ void moments_block(
         part[fv] += __shfl_xor(part[fv], 16);
         part[fv] += __shfl_xor(part[fv], 32);
     }
+    bool bad = false;
     if (valid && g == 0) {
         float* orow = out + base + static_cast<int64_t>(i) * FD;
 #pragma unroll
-        for (int fv = 0; fv < 4; ++fv) orow[fv * 16 + c] = fmaf(svc[fv], iom2, anc[FD + fv * 16 + c]) - part[fv];
+        for (int fv = 0; fv < 4; ++fv) {
+            const float o = fmaf(svc[fv], iom2, anc[FD + fv * 16 + c]) - part[fv];
+            bad = bad || !isfinite(o);
+            orow[fv * 16 + c] = o;
+        }
     }
+    // A non-finite row, or a pivot dropped while the ridge keeps the system positive definite
+    // (rounding made it indefinite), goes to the fp64 kernel.
+    const bool any_bad = (__ballot(bad) & 0xFFFFull) != 0;   // every lane takes part
+    if (valid && lane == 0 && (any_bad || (dropped && lambda > 0.0f))) hand_back(guard, list, bh, n, i);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -748,7 +786,7 @@ constexpr int K_SOLVE_BYTES = K_SOLVE_FLOATS * 4 * B_WAVES;
 constexpr int K_MEAN_OFF = K_SOLVE_BYTES > M_NBUF * K_BUF ? K_SOLVE_BYTES : M_NBUF * K_BUF;
 constexpr int K_SMEM = K_MEAN_OFF + (K_BQ * FD + B_WAVES * 16) * 4;
 constexpr int P_YLD = 2 * FD;                // per query: yh hi (fp16) | yh lo (fp16)
-constexpr int P_QSC = 4;                     // per query: gamma, 2^-e, 1/omega', unused
+constexpr int P_QSC = 4;                     // per query: gamma, 2^-e, 1/omega', dropped-pivot flag
 static_assert(K_IMG % 1024 == 0, "key image must be whole wave copies");
 static_assert(K_BQ <= 16, "score MFMA has 16 query columns");
 
@@ -891,7 +929,7 @@ __device__ __forceinline__ void group_panel(float4v (&ckk)[KQ][10], float (&zr)[
 
 __device__ __forceinline__ void group_solve(float4v (&ckk)[KQ][10], float (&zr)[4], const float thr,
                                             const float (&lam)[KQ], const float (&sks)[4], const float* skq,
-                                            float* Sg, float (&yr)[4], const int g, const int c) {
+                                            float* Sg, float (&yr)[4], const int g, const int c, float& dropped) {
     float Lk[4][4][16];       // Lk[K][j][t] = L[l + 16 j][16 K + t], j >= K
     float dk[4];              // pivot of row l + 16 K
     group_panel<0>(ckk, zr, thr, lam, sks, skq, Sg, Lk, dk, g, c);
@@ -903,13 +941,16 @@ __device__ __forceinline__ void group_solve(float4v (&ckk)[KQ][10], float (&zr)[
     // y_P = x_P - sum_{b > P} L[b][P] y_b, the sum over this query's 16 lanes.  L[b][P] is
     // zero for rows b <= P of the diagonal block, and y of rows not yet solved is zero.
     float x[4];
+    float drop = 0.0f;   // 1 if a pivot of this lane's rows was dropped
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float inv_d = __builtin_amdgcn_rcpf(dk[j]);
         inv_d = fmaf(inv_d, fmaf(-dk[j], inv_d, 1.0f), inv_d);   // one Newton step: ~0.5 ulp
         x[j] = dk[j] > thr ? zr[j] * inv_d : 0.0f;
+        drop = dk[j] > thr ? drop : 1.0f;
         yr[j] = 0.0f;
     }
+    dropped = row_max_f(drop);   // over the query's 16 lanes
 #pragma unroll
     for (int P = FD - 1; P >= 0; --P) {
         const int jP = P / 16, p = P % 16;
@@ -935,7 +976,7 @@ __device__ __forceinline__ void group_solve(float4v (&ckk)[KQ][10], float (&zr)[
 __device__ __forceinline__ void keymom_block(
     const int bidx, unsigned char* smem, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float* __restrict__ mrow, const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
-    _Float16* __restrict__ yhl, float* __restrict__ qsc,
+    _Float16* __restrict__ yhl, float* __restrict__ qsc, const unsigned* __restrict__ guard,
     int n, int row0, int rowp, int BH, float sl2, float lambda) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -951,6 +992,7 @@ __device__ __forceinline__ void keymom_block(
     const int last = min(i0 + K_BQ - 1, n - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
     const uint16_t* kh = k + base;
+    if (head_unsafe(guard, bh)) return;   // block-uniform: the probe pass hands the rows back
 
     if (K_BQ < 16) {   // rows K_BQ.. of every Sw2 buffer: the zero rows of the weight operand
         for (int e = tid; e < M_NBUF * (16 - K_BQ) * M_LD / 8; e += 256) {
@@ -1182,7 +1224,8 @@ __device__ __forceinline__ void keymom_block(
         }
         thr = 1e-6f * (G == 0 ? dm[0] : G == 1 ? dm[1] : G == 2 ? dm[2] : dm[3]);
     }
-    group_solve(ckk, zr, thr, lam_q, sks, mqG, Sg, yr, g, c);
+    float dropped = 0.0f;
+    group_solve(ckk, zr, thr, lam_q, sks, mqG, Sg, yr, g, c, dropped);
     // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together), and
     // gamma = 1 + S_k . yh / omega'.
     float yh[4], amax = 0.0f;
@@ -1213,8 +1256,10 @@ __device__ __forceinline__ void keymom_block(
             yhl[qrow * P_YLD + l + 16 * j] = hi[j];
             yhl[qrow * P_YLD + FD + l + 16 * j] = lo[j];
         }
+        // qsc[3] flags a pivot dropped although the ridge keeps the system positive definite.
         if (l == 0)
-            *reinterpret_cast<float4v*>(qsc + qrow * P_QSC) = float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, 0.0f};
+            *reinterpret_cast<float4v*>(qsc + qrow * P_QSC) =
+                float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, lambda > 0.0f ? dropped : 0.0f};
     }
 }
 
@@ -1243,6 +1288,7 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
     const unsigned char* __restrict__ packed, const unsigned char* __restrict__ kimg,
     const _Float16* __restrict__ yhl, const float* __restrict__ qsc, float* __restrict__ out,
+    unsigned* __restrict__ guard, int* __restrict__ list,
     int n, int row0, int rowp, int BH, float sl2) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1257,6 +1303,12 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
     const int wave_last = min(qw0 + P_QW - 1, n - 1);
     const int block_last = min(i0 + P_QB - 1, n - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
+    if (head_unsafe(guard, bh)) {   // block-uniform: the head's rows go to the fp64 kernel
+#pragma unroll
+        for (int st = 0; st < P_SETS; ++st)
+            if (g == 0 && qw0 + 16 * st + c < n) hand_back(guard, list, bh, n, qw0 + 16 * st + c);
+        return;
+    }
 
     // Query set st: column c is query qw0 + 16 st + c (clamped to n - 1).
     bf16x8 qf[P_SETS][2];
@@ -1389,18 +1441,28 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
     __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
 
     // Output rows: lane (g, c) register r of set st = query qw0 + 16 st + 4g + r, feature 16 fv + c.
+    // A row whose output is not finite, or whose solve dropped a pivot (qsc[3]), goes to the
+    // fp64 kernel.
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD + FD;
 #pragma unroll
     for (int st = 0; st < P_SETS; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = qw0 + 16 * st + 4 * g + r;
+            bool bad = false;
             if (i < n) {
-                const float iom = qsc[(static_cast<int64_t>(bh) * prows + (i - rowp)) * P_QSC + 2];
+                const float4v sc = *reinterpret_cast<const float4v*>(qsc + (static_cast<int64_t>(bh) * prows + (i - rowp)) * P_QSC);
                 float* orow = out + base + static_cast<int64_t>(i) * FD;
 #pragma unroll
-                for (int fv = 0; fv < 4; ++fv) orow[fv * 16 + c] = fmaf(o[st][fv][r], iom, anc[fv * 16 + c]);
+                for (int fv = 0; fv < 4; ++fv) {
+                    const float ov = fmaf(o[st][fv][r], sc[2], anc[fv * 16 + c]);
+                    bad = bad || !isfinite(ov);
+                    orow[fv * 16 + c] = ov;
+                }
+                bad = bad || sc[3] != 0.0f;
             }
+            const uint64_t badm = __ballot(bad);   // every lane takes part
+            if (c == 0 && i < n && ((badm >> (16 * g)) & 0xFFFFull) != 0) hand_back(guard, list, bh, n, i);
         }
 }
 
@@ -1646,6 +1708,8 @@ struct RowsArgs {
     _Float16* yhl;
     float* qsc;
     float* out;
+    unsigned* guard;   // range maxima and the count of rows handed back to the fp64 kernel
+    int* list;         // rows handed back
     int n, row0, rowp, BH, n_short, n_mom, n_key;
     float sl2, lambda;
     double inv_h, lambda_d;
@@ -1684,11 +1748,11 @@ __global__ __launch_bounds__(256, 2) void lla_rows_kernel(const RowsArgs a) {
         if (aux < a.n_short)
             short_block(aux, smem, a.q, a.k, a.v, a.out, a.n, a.row0, a.BH, a.inv_h, a.lambda_d);
         else
-            moments_block(aux - a.n_short, smem, a.q, a.k, a.v, a.mrow, a.anchors, a.packed, a.out, a.n, a.row0,
-                          a.rowp, a.BH, a.sl2, a.lambda);
+            moments_block(aux - a.n_short, smem, a.q, a.k, a.v, a.mrow, a.anchors, a.packed, a.out, a.guard, a.list,
+                          a.n, a.row0, a.rowp, a.BH, a.sl2, a.lambda);
     } else if (key >= 0) {
-        keymom_block(key, smem, a.q, a.k, a.mrow, a.anchors, a.packed, a.yhl, a.qsc, a.n, a.row0, a.rowp, a.BH,
-                     a.sl2, a.lambda);
+        keymom_block(key, smem, a.q, a.k, a.mrow, a.anchors, a.packed, a.yhl, a.qsc, a.guard, a.n, a.row0, a.rowp,
+                     a.BH, a.sl2, a.lambda);
     }
 }
 
@@ -1700,9 +1764,10 @@ int fast_rowp(int64_t n, int64_t d) { return static_cast<int>(n < 4 * d ? n : 4 
 //   row maxima [B*H][n - 2d] | anchor partial sums [B*H][16][2d] | anchors [B*H][2d] |
 //   key/value tile images [B*H][tiles] | key-major key images (bf16, centred fp16)
 //   [B*H][tiles] | probe solutions (fp16 hi, lo) [B*H][n - 4d][2d] |
-//   probe scalars [B*H][n - 4d][4].
+//   probe scalars [B*H][n - 4d][4] | guard: count of rows handed back, then per head the
+//   largest |k - a| and |v - a_v| (float bits) [1 + 2 B*H] | rows handed back [B*H][n - 2d].
 struct FastLayout {
-    int64_t mrow, partial, anchors, packed, kimg, yhl, qsc, total;
+    int64_t mrow, partial, anchors, packed, kimg, yhl, qsc, guard, list, total;
 };
 
 FastLayout fast_layout(int64_t BH, int64_t n, int64_t d) {
@@ -1716,7 +1781,9 @@ FastLayout fast_layout(int64_t BH, int64_t n, int64_t d) {
     L.kimg = L.packed + BH * tiles * PACK_TILE_BYTES;
     L.yhl = L.kimg + BH * tiles * KM_STRIDE;
     L.qsc = L.yhl + up(BH * prows * P_YLD * 2);
-    L.total = L.qsc + up(BH * prows * P_QSC * 4);
+    L.guard = L.qsc + up(BH * prows * P_QSC * 4);
+    L.list = L.guard + up((1 + 2 * BH) * 4);
+    L.total = L.list + up(BH * rows * 4);
     return L;
 }
 
@@ -1792,14 +1859,17 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
         ra.mrow = mrow; ra.anchors = anchors; ra.packed = packed;
         ra.yhl = reinterpret_cast<_Float16*>(ws + L.yhl);
         ra.qsc = reinterpret_cast<float*>(ws + L.qsc);
+        ra.guard = reinterpret_cast<unsigned*>(ws + L.guard);
+        ra.list = reinterpret_cast<int*>(ws + L.list);
         const int ptiles = (n + MT - 1) / MT;
         prof_begin(p.stream, "lla_anchor_kernel");
-        lla_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * ANCHOR_SLICES), dim3(256), 0, p.stream>>>(k, v, partial, n);
+        lla_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * ANCHOR_SLICES), dim3(256), 0, p.stream>>>(
+            k, v, partial, ra.guard, n);
         prof_end(p.stream);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         prof_begin(p.stream, "lla_pack_kernel");
         lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(
-            k, v, partial, anchors, packed, kimg, n, ptiles);
+            k, v, partial, anchors, packed, kimg, ra.guard, n, ptiles);
         prof_end(p.stream);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         const unsigned blocks_a = static_cast<unsigned>(BH) * ((n - row0 + R_QB - 1) / R_QB);
@@ -1816,8 +1886,14 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
         const unsigned blocks_p = static_cast<unsigned>(BH) * ((n - rowp + P_QB - 1) / P_QB);
         prof_begin(p.stream, "lla_probe_kernel");
         lla_probe_kernel<<<dim3(blocks_p), dim3(P_WAVES * 64), P_SMEM, p.stream>>>(
-            q, ra.mrow, ra.anchors, ra.packed, kimg_c, ra.yhl, ra.qsc, p.out, n, row0, rowp, BH, sl2);
+            q, ra.mrow, ra.anchors, ra.packed, kimg_c, ra.yhl, ra.qsc, p.out, ra.guard, ra.list, n, row0, rowp, BH,
+            sl2);
         prof_end(p.stream);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (n > row0) {   // rows handed back by the range and finiteness checks, in fp64
+        const int cap = BH * (n - row0);
+        return launch_exact_list(p, ra.list, reinterpret_cast<const int*>(ra.guard), cap < 2048 ? cap : 2048);
     }
     return hipGetLastError();
 }

@@ -61,12 +61,15 @@ __device__ __forceinline__ constexpr int ub8(int I, int J) { return I * 8 - I * 
 // key of the slice; the 8 key phases are added up through LDS.
 __global__ __launch_bounds__(256) void lla8_anchor_kernel(const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
-                                                          float* __restrict__ partial, int n) {
+                                                          float* __restrict__ partial,
+                                                          unsigned* __restrict__ guard, int n) {
     constexpr int NG = 2 * D8 / 8, NPH = 256 / NG;
     __shared__ float sums[NPH][2 * D8 + 4];
     const int bh = static_cast<int>(blockIdx.x) / A8_SLICES;
     const int sl = static_cast<int>(blockIdx.x) % A8_SLICES;
     const int tid = threadIdx.x, fgrp = tid % NG, ph = tid / NG;
+    if (sl == 0 && tid < 2) guard[1 + 2 * bh + tid] = 0u;   // the head's range maxima
+    if (blockIdx.x == 0 && tid == 2) guard[0] = 0u;         // no rows handed back yet
     const int na = min(n, 2 * D8);
     const int len = (na + A8_SLICES - 1) / A8_SLICES;
     const int j_lo = sl * len, j_hi = min(na, j_lo + len);
@@ -106,7 +109,8 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
                                                         float* __restrict__ anchors,
                                                         unsigned char* __restrict__ kf,
                                                         unsigned char* __restrict__ vf,
-                                                        unsigned char* __restrict__ km, int n, int ntiles) {
+                                                        unsigned char* __restrict__ km,
+                                                        unsigned* __restrict__ guard, int n, int ntiles) {
     __shared__ float anc[2 * D8];
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
     const int tid = threadIdx.x;
@@ -125,6 +129,7 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
     unsigned char* kmt = km + tile * KM_STRIDE8;
     uint32_t* kft = reinterpret_cast<uint32_t*>(kf + tile * F_BYTES);
     uint32_t* vft = reinterpret_cast<uint32_t*>(vf + tile * F_BYTES);
+    float mk = 0.0f, mv = 0.0f;   // the largest centred magnitudes, for the range guard
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int fg = (tid >> 5) + 8 * it;   // features 8 fg .. 8 fg + 7
@@ -145,6 +150,14 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
             cb[e] = static_cast<_Float16>(jb < n ? bf16_elem(k1, e) - ak : 0.0f);
             va[e] = static_cast<_Float16>(ja < n ? bf16_elem(v0, e) - av : 0.0f);
             vb[e] = static_cast<_Float16>(jb < n ? bf16_elem(v1, e) - av : 0.0f);
+            if (ja < n) {
+                mk = fmaxf(mk, fabsf(bf16_elem(k0, e) - ak));
+                mv = fmaxf(mv, fabsf(bf16_elem(v0, e) - av));
+            }
+            if (jb < n) {
+                mk = fmaxf(mk, fabsf(bf16_elem(k1, e) - ak));
+                mv = fmaxf(mv, fabsf(bf16_elem(v1, e) - av));
+            }
         }
         // key-major: bf16 as given, then centred fp16; padding (bytes 256..271 of a row) zero
         *reinterpret_cast<uint4*>(kmt + (2 * pr) * (K_LD * 2) + 16 * fg) = k0;
@@ -171,6 +184,8 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
             }
         }
     }
+    wave_atomic_max(guard + 1 + 2 * bh, mk);
+    wave_atomic_max(guard + 2 + 2 * bh, mv);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -316,7 +331,7 @@ constexpr int K8_MEAN_OFF = K8_RING > K8_SOLVE_BYTES ? K8_RING : K8_SOLVE_BYTES;
 constexpr int K8_SMEM = K8_MEAN_OFF + (K8_BQ * D8 + 4 * 16) * 4;
 static_assert(K8_SMEM <= 160 * 1024, "one block per CU");
 constexpr int P8_YLD = 2 * D8;                        // per query: yh hi (fp16) | yh lo (fp16)
-constexpr int P8_QSC = 4;                             // per query: gamma, 2^-e, 1/omega', unused
+constexpr int P8_QSC = 4;                             // per query: gamma, 2^-e, 1/omega', dropped-pivot flag
 static_assert(K8_BUF % 16 == 0 && K8_SRING % 16 == 0 && K8_MEAN_OFF % 16 == 0, "LDS areas stay 16-byte aligned");
 static_assert(K8_BQ <= 16, "score MFMA has 16 query columns");
 
@@ -451,7 +466,7 @@ __device__ __forceinline__ void panel8(float4v (&ckk)[36], float (&z)[2], float 
 // One query's solve.  Returns y[J] = y[16 J + c] in lane (g, c) (the same in every g).
 __device__ __forceinline__ void solve8(float4v (&ckk)[36], float (&z)[2], const float thr, const float lam,
                                        const float iom, const float* skq, float* Sg, float (&y)[8],
-                                       const int lane, const int g, const int c) {
+                                       float& dropped, const int lane, const int g, const int c) {
     float dd[8];
 #pragma unroll
     for (int J = 0; J < 8; ++J) dd[J] = 0.0f;
@@ -476,13 +491,16 @@ __device__ __forceinline__ void solve8(float4v (&ckk)[36], float (&z)[2], const 
     for (int h = 0; h < 2; ++h) Sg[lane + 64 * h] = z[h];
     LDS_FENCE();
     float x[8];
+    float drop = 0.0f;   // 1 if a pivot of this lane's rows was dropped
 #pragma unroll
     for (int J = 0; J < 8; ++J) {
         float inv_d = __builtin_amdgcn_rcpf(dd[J]);
         inv_d = fmaf(inv_d, fmaf(-dd[J], inv_d, 1.0f), inv_d);   // one Newton step: ~0.5 ulp
         x[J] = dd[J] > thr ? Sg[16 * J + c] * inv_d : 0.0f;
+        drop = dd[J] > thr ? drop : 1.0f;
         y[J] = 0.0f;
     }
+    dropped = wave_max8(drop);
     LDS_FENCE();
     // Back substitution L^T y = x from the last row: y_P = x_P - sum_{b > P} L[b][P] y_b.
     // For P = 16 K + 4 g' + r', L[16 J + c][P] is register r' of block (K, J) in lane (g', c):
@@ -509,7 +527,8 @@ __device__ __forceinline__ void solve8(float4v (&ckk)[36], float (&z)[2], const 
 __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
     const unsigned char* __restrict__ kf, const unsigned char* __restrict__ km, _Float16* __restrict__ yhl,
-    float* __restrict__ qsc, int n, int row0, int BH, float sl2, float lambda) {
+    float* __restrict__ qsc, const unsigned* __restrict__ guard, int n, int row0, int BH, float sl2,
+    float lambda) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -521,6 +540,7 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
     const int i0 = row0 + blk * K8_BQ;
     const int last = min(i0 + K8_BQ - 1, n - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * D8;
+    if (head_unsafe(guard, bh)) return;   // block-uniform: the probe pass hands the rows back
 
     // Rows K8_BQ.. of every weight buffer: the zero rows of the block-sum MFMA operand.
     for (int e = tid; e < K8_NBUF * (16 - K8_BQ) * F_LD / 8; e += KW8 * 64) {
@@ -726,7 +746,8 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
         thr = 1e-6f * wave_max8(dmax);
     }
     float yd[8];
-    solve8(ckk, z, thr, lam, iom2, skq, Sg, yd, lane, g, c);
+    float dropped = 0.0f;
+    solve8(ckk, z, thr, lam, iom2, skq, Sg, yd, dropped, lane, g, c);
     LDS_FENCE();
     // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together), and
     // gamma = 1 + S_k . yh / omega'.  Lane (g, c) holds rows 16 J + c; lanes g = 0 store.
@@ -755,9 +776,10 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
             yhl[qrow * P8_YLD + 16 * J + c] = hi[J];
             yhl[qrow * P8_YLD + D8 + 16 * J + c] = lo[J];
         }
+        // qsc[3] flags a pivot dropped although the ridge keeps the system positive definite.
         if (c == 0)
             *reinterpret_cast<float4v*>(qsc + qrow * P8_QSC) =
-                float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, 0.0f};
+                float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, lambda > 0.0f ? dropped : 0.0f};
     }
 }
 
@@ -782,7 +804,7 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
     const unsigned char* __restrict__ km, const unsigned char* __restrict__ vf,
     const _Float16* __restrict__ yhl, const float* __restrict__ qsc, float* __restrict__ out,
-    int n, int row0, int BH, float sl2) {
+    unsigned* __restrict__ guard, int* __restrict__ list, int n, int row0, int BH, float sl2) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -796,6 +818,12 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
     const int wave_last = min(qw0 + P8_QW - 1, n - 1);
     const int block_last = min(i0 + P8_QB - 1, n - 1);
     const int64_t base = static_cast<int64_t>(bh) * n * D8;
+    if (head_unsafe(guard, bh)) {   // block-uniform: the head's rows go to the fp64 kernel
+#pragma unroll
+        for (int st = 0; st < P8_SETS; ++st)
+            if (g == 0 && qw0 + 16 * st + c < n) hand_back(guard, list, bh, n, qw0 + 16 * st + c);
+        return;
+    }
 
     bf16x8 qf[P8_SETS][4];
     half8 yh[P8_SETS][4], yl[P8_SETS][4];
@@ -928,18 +956,29 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
     __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));   // copies past the last tile
 
     // Output rows: lane (g, c) register r of set st = query qw0 + 16 st + 4 g + r, feature 16 fv + c.
+    // A row whose output is not finite, or whose solve dropped a pivot (qsc[3]), goes to the
+    // fp64 kernel.
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * D8 + D8;
 #pragma unroll
     for (int st = 0; st < P8_SETS; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = qw0 + 16 * st + 4 * g + r;
+            bool bad = false;
             if (i < n) {
-                const float iom = qsc[(static_cast<int64_t>(bh) * prows + (i - row0)) * P8_QSC + 2];
+                const float4v sc =
+                    *reinterpret_cast<const float4v*>(qsc + (static_cast<int64_t>(bh) * prows + (i - row0)) * P8_QSC);
                 float* orow = out + base + static_cast<int64_t>(i) * D8;
 #pragma unroll
-                for (int fv = 0; fv < 8; ++fv) orow[fv * 16 + c] = fmaf(o[st][fv][r], iom, anc[fv * 16 + c]);
+                for (int fv = 0; fv < 8; ++fv) {
+                    const float ov = fmaf(o[st][fv][r], sc[2], anc[fv * 16 + c]);
+                    bad = bad || !isfinite(ov);
+                    orow[fv * 16 + c] = ov;
+                }
+                bad = bad || sc[3] != 0.0f;
             }
+            const uint64_t badm = __ballot(bad);   // every lane takes part
+            if (c == 0 && i < n && ((badm >> (16 * g)) & 0xFFFFull) != 0) hand_back(guard, list, bh, n, i);
         }
 }
 
@@ -949,9 +988,11 @@ int fast8_row0(int64_t n) { return static_cast<int>(n < 4 * D8 ? n : 4 * D8); }
 // Workspace, each region 256-byte aligned: row maxima [B*H][n - 4d] | anchor partial sums
 // [B*H][16][2d] | anchors [B*H][2d] | K feature-major images [B*H][tiles] | V feature-major
 // images [B*H][tiles] | key-major images (bf16, centred fp16) [B*H][tiles] | probe solutions
-// (fp16 hi, lo) [B*H][n - 4d][2d] | probe scalars [B*H][n - 4d][4].
+// (fp16 hi, lo) [B*H][n - 4d][2d] | probe scalars [B*H][n - 4d][4] | guard: count of rows
+// handed back, then per head the largest |k - a| and |v - a_v| (float bits) [1 + 2 B*H] |
+// rows handed back [B*H][n - 4d].
 struct Fast8Layout {
-    int64_t mrow, partial, anchors, kf, vf, km, yhl, qsc, total;
+    int64_t mrow, partial, anchors, kf, vf, km, yhl, qsc, guard, list, total;
 };
 
 Fast8Layout fast8_layout(int64_t BH, int64_t n) {
@@ -966,7 +1007,9 @@ Fast8Layout fast8_layout(int64_t BH, int64_t n) {
     L.km = L.vf + BH * tiles * F_BYTES;
     L.yhl = L.km + BH * tiles * KM_STRIDE8;
     L.qsc = L.yhl + up(BH * prows * P8_YLD * 2);
-    L.total = L.qsc + up(BH * prows * P8_QSC * 4);
+    L.guard = L.qsc + up(BH * prows * P8_QSC * 4);
+    L.list = L.guard + up((1 + 2 * BH) * 4);
+    L.total = L.list + up(BH * prows * 4);
     return L;
 }
 
@@ -1020,15 +1063,18 @@ hipError_t launch_fast128(const Problem& p, void* workspace) {
     unsigned char* km = ws + L.km;
     _Float16* yhl = reinterpret_cast<_Float16*>(ws + L.yhl);
     float* qsc = reinterpret_cast<float*>(ws + L.qsc);
+    unsigned* guard = reinterpret_cast<unsigned*>(ws + L.guard);
+    int* list = reinterpret_cast<int*>(ws + L.list);
     const int ptiles = (n + T8 - 1) / T8;
     const int prows = n - row0;
     prof_begin(p.stream, "lla8_anchor_kernel");
-    lla8_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * A8_SLICES), dim3(256), 0, p.stream>>>(k, v, partial, n);
+    lla8_anchor_kernel<<<dim3(static_cast<unsigned>(BH) * A8_SLICES), dim3(256), 0, p.stream>>>(k, v, partial, guard,
+                                                                                              n);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_pack_kernel");
     lla8_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(k, v, partial, anchors, kf,
-                                                                                           vf, km, n, ptiles);
+                                                                                           vf, km, guard, n, ptiles);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_rowmax_kernel");
@@ -1038,15 +1084,18 @@ hipError_t launch_fast128(const Problem& p, void* workspace) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_keymom_kernel");
     lla8_keymom_kernel<<<dim3(static_cast<unsigned>(BH) * ((prows + K8_BQ - 1) / K8_BQ)), dim3(KW8 * 64), K8_SMEM,
-                         p.stream>>>(q, mrow, anchors, kf, km, yhl, qsc, n, row0, BH, sl2,
+                         p.stream>>>(q, mrow, anchors, kf, km, yhl, qsc, guard, n, row0, BH, sl2,
                                      static_cast<float>(p.lambda));
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_probe_kernel");
     lla8_probe_kernel<<<dim3(static_cast<unsigned>(BH) * ((prows + P8_QB - 1) / P8_QB)), dim3(256), P8_SMEM,
-                        p.stream>>>(q, mrow, anchors, km, vf, yhl, qsc, p.out, n, row0, BH, sl2);
+                        p.stream>>>(q, mrow, anchors, km, vf, yhl, qsc, p.out, guard, list, n, row0, BH, sl2);
     prof_end(p.stream);
-    return hipGetLastError();
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // Rows handed back by the range and finiteness checks, in fp64.
+    const int cap = BH * prows;
+    return launch_exact_list(p, list, reinterpret_cast<const int*>(guard), cap < 2048 ? cap : 2048);
 }
 
 }  // namespace lla

@@ -31,6 +31,9 @@ struct BwdProblem {
 // fp64-accumulating path: every (dtype, d) the library accepts.  Processes rows
 // 0 .. rows-1 of every head (rows = n for the whole problem).
 hipError_t launch_exact(const Problem& p, int rows);
+// The same fp64 computation for the *count rows in `list` (entries bh * n + i, device
+// memory, count read by the kernel), over `blocks` workgroups.
+hipError_t launch_exact_list(const Problem& p, const int* list, const int* count, int blocks);
 
 // fp64 path with each query's system solved by conjugate gradient over its prefix (no
 // d x d state): every (dtype, d); no workspace.

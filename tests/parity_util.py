@@ -91,15 +91,30 @@ def workload_arrays(name, **shape):
 
 def fast_workspace_bytes(BH, n, d=64):
     """Scratch bytes of the bf16 matrix-core path, region by region (each rounded up to
-    256 B where the library rounds it): row maxima of rows >= 2d, anchor partial sums,
-    anchors, then per head and 64-key tile the fp16 K/V image (72-half rows) and the two
-    key-major key images (bf16, centred fp16), then per probe row (rows >= 4d) the fp16
-    hi/lo solution and four scalars."""
+    256 B where the library rounds it).
+
+    d = 64: row maxima of rows >= 2d, anchor partial sums, anchors, then per head and 64-key
+    tile the fp16 K/V image (72-half rows) and the two key-major key images (bf16, centred
+    fp16), then per probe row (rows >= 4d) the fp16 hi/lo solution and four scalars, the
+    guard words (count of rows handed back, two maxima per head) and the hand-back list
+    (one slot per row >= 2d).
+
+    d = 128: the same regions for rows >= 4d, with the K and V feature-major images apart
+    (72-half rows) and key-major rows of 136 halves."""
     up = lambda x: (x + 255) // 256 * 256
     tiles = -(-n // 64)
+    if d == 128:
+        prows = n - min(n, 4 * d)
+        if prows <= 0:
+            return 0
+        return (up(BH * prows * 4) + up(BH * 16 * 2 * d * 4) + up(BH * 2 * d * 4)
+                + BH * tiles * (2 * d * 72 * 2 + 2 * 64 * 136 * 2)
+                + up(BH * prows * 2 * d * 2) + up(BH * prows * 4 * 4)
+                + up((1 + 2 * BH) * 4) + up(BH * prows * 4))
     prows = n - min(n, 4 * d)
     if n - min(n, 2 * d) <= 0:
         return 0
     return (up(BH * (n - 2 * d) * 4) + up(BH * 16 * 2 * d * 4) + up(BH * 2 * d * 4)
             + BH * tiles * (2 * d * 72 * 2 + 2 * 64 * 72 * 2)
-            + up(BH * prows * 2 * d * 2) + up(BH * prows * 4 * 4))
+            + up(BH * prows * 2 * d * 2) + up(BH * prows * 4 * 4)
+            + up((1 + 2 * BH) * 4) + up(BH * (n - 2 * d) * 4))

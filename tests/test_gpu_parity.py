@@ -155,7 +155,7 @@ def test_profiling_records_each_kernel():
     finally:
         lla_profile_enable(False)
     assert [name for name, _ in rec] == ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel",
-                                         "lla_rows_kernel", "lla_probe_kernel"]
+                                         "lla_rows_kernel", "lla_probe_kernel", "lla_exact_list_kernel"]
     assert all(ms > 0 for _, ms in rec)
 
 
