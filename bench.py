@@ -57,11 +57,12 @@ def alg_flops(B, H, n, d, form):
 
 
 # Arithmetic of each path (the dtype field) and the bound of each kernel.
-PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d: f64)",
+PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d and rows the check hands back: f64)",
               "cg": "f64 (conjugate gradient over the prefix)"}
 KERNEL_BOUND = {
     "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_exact_list_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla_refine_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_cg_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_short_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_rowmax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
@@ -95,10 +96,9 @@ KERNEL_BOUND = {
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
     "cg": ["lla_cg_kernel"],
-    # the last launch recomputes in fp64 the rows the range and finiteness checks hand back
-    # (none on these workloads)
+    # the last launch recomputes in fp64 the rows the range guard and the checks hand back
     "fast": ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel",
-             "lla_probe_kernel", "lla_exact_list_kernel"],
+             "lla_probe_kernel", "lla_refine_kernel"],
     # d = 128: rows i < 4d on the fp64 kernel, the rest on the d = 128 matrix-core kernels
     "fast128": ["lla_exact_kernel", "lla8_anchor_kernel", "lla8_pack_kernel", "lla8_rowmax_kernel",
                 "lla8_keymom_kernel", "lla8_probe_kernel", "lla_exact_list_kernel"],
@@ -128,16 +128,15 @@ def pair_count(BH, lo, hi):
 
 def kernel_flops(name, B, H, n, d, path):
     """Algorithmic flops of one launch of a kernel, in the formulation that kernel executes.
-    The exact path and the fast path's rows i < 4d form the value-key cross moment (NS);
-    the fast path's rows i >= 4d apply it through the probe pass (min).  Fast path: rows
-    [0, 2d) fp64 short-row kernel; the row-max kernel owns the score term of rows >= 2d;
-    rows [2d, 4d) the explicit moments kernel (first and second moments, solve, assembly);
-    rows [4d, n) the key-moment kernel (first moments, C_kk, solve) and the probe kernel
-    (probe scores and the weighted value sum).  Scores a kernel recomputes are not counted
-    again."""
+    The exact path and the fast path's fp64 rows form the value-key cross moment (NS); the
+    fast path's other rows apply it through the probe pass (min).  Fast path, d = 64: rows
+    [0, 2d) fp64 short-row kernel; the row-max kernel owns the score term of rows >= 2d; rows
+    [2d, n) the key-moment kernel (first moments, C_kk, solve) and the probe kernel (probe
+    scores and the weighted value sum); d = 128 the same with 4d for 2d.  Scores a kernel
+    recomputes, and the probe's check sums (a verification, not part of the estimator), are
+    not counted."""
     BH = B * H
-    row0 = min(n, 2 * d) if path == "fast" else n
-    rowp = min(n, 4 * d) if path == "fast" else n
+    row0 = rowp = min(n, 2 * d) if path == "fast" else n
     if path == "fast" and d == 128:   # rows < 4d exact (NS), the rest key moments + probe (min)
         row0 = rowp = min(n, 4 * d)
     per_query = d ** 3 / 3 + 4 * d * d + 2 * d
@@ -148,8 +147,8 @@ def kernel_flops(name, B, H, n, d, path):
         return pair_count(BH, 0, row0) * (2 * d + moments + 2 * d * d) + BH * row0 * per_query
     if name in ("lla_anchor_kernel", "lla_pack_kernel", "lla8_anchor_kernel", "lla8_pack_kernel"):
         return 0                      # data movement only (K, V summed and repacked once)
-    if name == "lla_exact_list_kernel":
-        return 0                      # rows handed back by the fast path's checks: none here
+    if name in ("lla_exact_list_kernel", "lla_refine_kernel"):
+        return 0                      # rows handed back by the fast path's checks (counted in fallback_rows)
     if name in ("lla_rowmax_kernel", "lla8_rowmax_kernel"):
         return pair_count(BH, row0, n) * 2 * d
     if name == "lla8_keymom_kernel":
@@ -160,9 +159,9 @@ def kernel_flops(name, B, H, n, d, path):
         return pair_count(BH, row0, rowp) * (moments + 2 * d * d) + BH * (rowp - row0) * per_query
     if name == "lla_keymom_kernel":
         return pair_count(BH, rowp, n) * moments + BH * (n - rowp) * (d ** 3 / 3 + 2 * d * d)
-    if name == "lla_rows_kernel":     # one launch: short rows, rows [2d, 4d), key moments of rows >= 4d
+    if name == "lla_rows_kernel":     # one launch: short rows, key moments of rows >= 2d
         return sum(kernel_flops(part, B, H, n, d, path)
-                   for part in ("lla_short_kernel", "lla_moments_kernel", "lla_keymom_kernel"))
+                   for part in ("lla_short_kernel", "lla_keymom_kernel"))
     if name == "lla_probe_kernel":
         return pair_count(BH, rowp, n) * (4 * d + 2) + BH * (n - rowp) * 4 * d
     if name in ("lla_parallax_kernel", "lla_parallax_exact_kernel"):
@@ -744,6 +743,11 @@ def main():
     per_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     ms_per_step = total_ms / args.steps
     assert torch.isfinite(out).all().item(), "non-finite output"
+    # Rows of the last timed step that the matrix-core path's checks sent to the fp64 kernel.
+    fallback_rows = None
+    if not parallax and ws is not None:
+        from local_linear_attention_amd.lla import lla_forward_fallback_rows
+        fallback_rows = lla_forward_fallback_rows(ws, (w.B, w.H, w.n, w.d), w.dtype, path, stream=stream)
 
     # Kernel-level timing: the same steps again with the library's per-launch HIP events.
     lla_profile_enable(True)
@@ -778,14 +782,15 @@ def main():
     else:
         config_text = (f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs, h={w.h:g}, "
                        f"lambda={w.lam:g}")
-        flop_count = {"formulation": ("NS for rows i < 4d, min (probe pass) for rows i >= 4d"
+        split = "4d" if w.d == 128 else "2d"
+        flop_count = {"formulation": (f"NS for rows i < {split}, min (probe pass) for rows i >= {split}"
                                       if path == "fast" else "NS"),
                       "flops": flops,
                       "F_NS": alg_flops(w.B, w.H, w.n, w.d, "NS"),
                       "F_min": alg_flops(w.B, w.H, w.n, w.d, "min")}
         arith = PATH_ARITH[path]
         if path == "fast" and w.d == 128:
-            arith = "f16 MFMA / f32 accumulate (rows < 4d: f64)"
+            arith = "f16 MFMA / f32 accumulate (rows < 4d and rows the check hands back: f64)"
     result = {
         "metric": (METRIC_PARALLAX if parallax else METRIC) if w.name in ("d24", "parallax_d24") else
                   (f"{'Parallax fwd (given probe)' if parallax else 'LLA fwd'} queries/s + TFLOP/s (% MFMA peak) "
@@ -808,6 +813,7 @@ def main():
             "entry_point": (("lla_parallax_forward_ws" if parallax else "lla_forward_ws")
                             + f" with a caller workspace of {ws_size} bytes"),
         },
+        "fallback_rows": fallback_rows,
         "tflops": achieved_tflops,
         "flop_count": flop_count,
         "kernels": kernels,

@@ -336,6 +336,18 @@ lla_status_t lla_parallax_decode_ws(const void* q, const void* k, const void* v,
                                     double h, lla_dtype_t dtype, void* stream,
                                     void* workspace, size_t workspace_bytes);
 
+/* Diagnostic: the number of rows that the matrix-core path of the last lla_forward_ws call on
+ * `workspace` (same B, H, n, d, dtype and path, enqueued on `stream`) recomputed on the fp64
+ * kernel -- rows of a head whose centred keys or values lie outside [2^-10, 2^14] (fp16
+ * range guard), rows whose output was not finite or whose solve dropped a pivot under a
+ * positive ridge, and rows whose reproduction check (see LLA_PATH_FAST) exceeded its bound.
+ * Reads 4 bytes of the workspace and waits for `stream`.  *rows = 0 when the call resolves
+ * to a path without workspace.  LLA_ERR_WORKSPACE if `workspace` is NULL or smaller than
+ * the path needs; LLA_ERR_HIP if the copy fails. */
+lla_status_t lla_forward_fallback_rows(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                                       int64_t n, int64_t d, lla_dtype_t dtype, lla_path_t path, int64_t* rows,
+                                       void* stream);
+
 /* Returns the memory that the library pool of every device holds for reuse (blocks that
  * lla_forward, lla_forward_ex and the other pool-backed entry points have freed) to the
  * system: hipMemPoolTrimTo(pool, 0).  Blocks still in use by enqueued work are kept.  The

@@ -396,6 +396,30 @@ size_t lla_forward_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, l
     return lla_workspace_size(B, H, n, d, dtype, LLA_PATH_AUTO);
 }
 
+lla_status_t lla_forward_fallback_rows(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                                       int64_t n, int64_t d, lla_dtype_t dtype, lla_path_t path, int64_t* rows,
+                                       void* stream) {
+    if (rows == nullptr) return LLA_ERR_NULL;
+    *rows = 0;
+    if (!supported_shape(d, dtype)) return LLA_ERR_UNSUPPORTED;
+    const lla_status_t st = validate_sizes(B, H, n, d);
+    if (st != LLA_OK) return st;
+    bool fast = false;
+    if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
+    if (!fast) return LLA_OK;
+    const int64_t off = lla::fast_fallback_count_offset(B, H, n, d);
+    if (off < 0) return LLA_OK;
+    if (workspace == nullptr || workspace_bytes < lla::fast_workspace_bytes(B, H, n, d)) return LLA_ERR_WORKSPACE;
+    uint32_t count = 0;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(&count, static_cast<const unsigned char*>(workspace) + off, sizeof(count),
+                       hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return LLA_ERR_HIP;
+    *rows = count;
+    return LLA_OK;
+}
+
 lla_status_t lla_pool_trim(void) {
     std::lock_guard<std::mutex> lock(g_pool_mu);
     for (hipMemPool_t p : g_pools)

@@ -20,6 +20,14 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int FD = 64;              // head dimension of the matrix-core kernels
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Reproduction check of the matrix-core paths: NCHK projections of the centred keys on fixed
+// +-1 directions (Walsh functions), 5 KiB per 64-key tile for their fp16 image and the
+// per-key |v - a_v|^2; rows whose estimated relative error exceeds CHK_TOL go to the fp64
+// kernel.
+constexpr int NCHK = 32;
+constexpr int KU_TILE_BYTES = 5 * 1024;
+constexpr float CHK_TOL = 1.5e-3f;
+
 // Compiler fence for wave-private LDS exchanges: a lane reads words that other lanes of
 // the same wave stored, so no LDS access may move across a publish/consume boundary.
 // (A blocked variant of the LLA solve was miscompiled without such fences on gfx950:

@@ -8,16 +8,19 @@
 //       lla_anchor_kernel   per-head sums of the keys and values of positions [0, 2d) (the
 //                           centring anchor a: every row of this path has them in its prefix);
 //       lla_pack_kernel     K, V once into fp16 tiles centred at a (the LDS image the
-//                           moments kernel copies) and K key-major for the score pass;
+//                           key-moment pass copies), K key-major for the score passes, and the
+//                           check image (projected keys, |v - a_v|^2);
 //       lla_rowmax_kernel   score pass with a running max: m_i;
-//       lla_moments_kernel  per query, with sw_ij = sqrt(e^{s_ij - m_i}) rounded to fp16,
-//                           R_k[j] = sw (k_j - a_k), R_v[j] = sw (v_j - a_v) (fp16), the
-//                           moments R_k^T R_k and R_k^T R_v on MFMA (fp32 accumulation), the
-//                           block sums S = sum_j sw^2 (x_j - a) and omega' = sum_j sw^2, the
-//                           rank-one downdate to the centred C_kk, C_vk, the means
-//                           kbar = a_k + S_k / omega', vbar = a_v + S_v / omega'; then the
-//                           ridge-rescaled SPD solve (C_kk + lambda e^{-m} I) y = kbar - q by
-//                           LDL^T elimination in one wave, and b = vbar - C_vk y.
+//       lla_rows_kernel     the short rows, and per query, with sw_ij = sqrt(e^{s_ij - m_i})
+//                           rounded to fp16 and R[j] = sw (k_j - a) (fp16), the key moment
+//                           R^T R on MFMA (fp32 accumulation), the block sums
+//                           S = sum_j sw^2 (k_j - a) and omega' = sum_j sw^2, the rank-one
+//                           downdate to the centred C_kk and the ridge-rescaled SPD solve
+//                           (C_kk + lambda e^{-m} I) y = kbar - q, kbar = a + S / omega';
+//       lla_probe_kernel    b = vbar - C_vk y without forming C_vk (a second attention-like
+//                           sweep over the keys and values), and the per-row check that hands
+//                           rows to the fp64 kernel;
+//       lla_exact_list_kernel  the rows handed back, in fp64.
 // The estimator, its moments and the centred form follow the "Parallax" blog post, section 2
 // "Canonical Formulation" and Appendix E; the max shift is the safe softmax of the arXiv
 // page's scoring-form paragraph, with the ridge scaled by the same e^{-m}.  The normalisation
@@ -36,45 +39,32 @@
 namespace lla {
 namespace {
 
-constexpr int B_WAVES = 4;          // waves per block of the row-max and moments kernels
+constexpr int B_WAVES = 4;          // waves per block of the row-max and key-moment passes
 
 // ---------------------------------------------------------------------------------------
-// Moments + solve: block = 4 waves, one query per wave (4 consecutive rows of one head).
-// Keys stream in tiles of 64 through a ring of three LDS buffers: tile t is consumed by the
-// MFMAs while tile t+1 is landing and tile t+2 is being copied from the workspace straight
+// Key tiles stream in 64-key tiles through a ring of three LDS buffers: tile t is consumed by
+// the MFMAs while tile t+1 is landing and tile t+2 is being copied from the workspace straight
 // into LDS (buffer loads with an LDS destination, no registers) -- one barrier per tile.
 //
 // Anchor: the pack kernel stores each head's keys and values centred at a = (mean k,
 // mean v) of its positions [0, 2d) rounded to fp16 -- positions in the prefix of every row
 // this path serves, so no row depends on a later position even through rounding -- and
-// every wave only scales: R_k = sw (k - a_k),
-// R_v = sw (v - a_v).  Moments about a differ from the centred ones by a rank-one term,
-//   C = sum_j w_j (x_j - a)(y_j - a)^T - S_x S_y^T / omega',   S_x = sum_j w_j (x_j - a),
-// which the block gets from one extra MFMA pair per wave and 32 keys (weights w_j = sw_j^2
-// rounded to fp16, omega' their sum).  Using the same rounded data on both sides keeps the
-// downdated C_kk consistent with C_vk; the cancellation in the downdate grows with
-// |kbar_i - a|^2 over the weighted spread of the keys, small while the query's weights are
-// spread over many keys (as on RMS-normalised heads at h = sqrt(d)).
+// every wave only scales: R = sw (k - a).  Moments about a differ from the centred ones by a
+// rank-one term,
+//   C = sum_j w_j (k_j - a)(k_j - a)^T - S S^T / omega',   S = sum_j w_j (k_j - a),
+// which the block gets from one extra MFMA per wave and 32 keys (weights w_j = sw_j^2 rounded
+// to fp16, omega' their sum).  The cancellation in the downdate grows with |kbar_i - a|^2
+// over the weighted spread of the keys, small while the query's weights are spread over many
+// keys (as on RMS-normalised heads at h = sqrt(d)); the probe pass's check catches the rows
+// where it is not.
 constexpr int MT = 64;                   // keys per tile
 constexpr int M_LD = MT + 8;             // feature-major fp16 row (elements), 144 B
-// One tile as the pack kernel lays it out in the workspace and the moments kernel copies it,
-// byte for byte, into LDS: [K or V][feature][key], rows of M_LD halves (the last 8 are
+// One tile as the pack kernel lays it out in the workspace (the key-moment pass copies its key
+// half, the probe pass its value half, byte for byte, into LDS): [K or V][feature][key], rows
+// of M_LD halves (the last 8 are
 // padding that keeps the 16-byte operand reads conflict-free), 18 KiB per tile.
 constexpr int PACK_TILE_BYTES = 2 * FD * M_LD * 2;
-constexpr int M_LOADS = PACK_TILE_BYTES / 1024;  // wave-wide copies of 16 B per lane per tile
-constexpr int M_WLOADS = (M_LOADS + B_WAVES - 1) / B_WAVES;   // copies issued by each wave
 constexpr int M_NBUF = 3;                // tile ring: compute t, t+1 landing, t+2 in flight
-// Side buffers of a tile, rows of M_LD halves like the tile (16-byte reads by 16 rows at
-// once stay conflict-free): Sw = sqrt-weights [query][key]; Sw2 = fp16 weights, 16 rows of
-// which rows B_WAVES.. stay zero (the unused rows of the block-sum MFMA operand).
-constexpr int M_SW = PACK_TILE_BYTES;
-constexpr int M_SW2 = M_SW + B_WAVES * M_LD * 2;
-constexpr int M_BUF_BYTES = M_SW2 + 16 * M_LD * 2;
-constexpr int B_SOLVE_FLOATS = FD * (FD + 1) + 2 * FD;  // L (padded rows) + pivots + y
-constexpr int B_SOLVE_BYTES = B_SOLVE_FLOATS * 4 * B_WAVES;
-constexpr int B_MEAN_FLOATS = 2 * FD + B_WAVES;          // per query: S_k, S_v, omega' parts
-constexpr int B_MEAN_OFF = B_SOLVE_BYTES > M_NBUF * M_BUF_BYTES ? B_SOLVE_BYTES : M_NBUF * M_BUF_BYTES;
-constexpr int B_SMEM = B_MEAN_OFF + B_WAVES * B_MEAN_FLOATS * 4;
 constexpr int ANCHOR_SLICES = 16;        // key slices of the per-head anchor sums
 // Keys of one tile key-major (bf16 as given, rows of KM_LD halves: 64 features + 8 of
 // padding), the score operand of the row-max kernel, 9 KiB per tile.
@@ -88,6 +78,11 @@ constexpr int KM_WLOADS = (KM_LOADS + B_WAVES - 1) / B_WAVES;
 constexpr int R_SETS = 2, R_QW = 16 * R_SETS, R_QB = B_WAVES * R_QW;  // row-max: 2 sets of 16 queries per wave
 static_assert(KM_TILE_BYTES % 1024 == 0, "key image must be whole wave copies");
 static_assert(PACK_TILE_BYTES % 1024 == 0, "tile image must be whole wave copies");
+// Check image of a tile: the centred keys projected on NCHK fixed +-1 directions (Walsh
+// functions of odd index 2t + 1, fp16, feature-major [direction][key] rows of M_LD halves),
+// then |v_j - a_v|^2 per key (fp32), padded to whole KiB.
+constexpr int KU_NRM = NCHK * M_LD * 2;
+static_assert(KU_NRM + MT * 4 <= KU_TILE_BYTES, "check image layout");
 
 // Per-head anchor, pass 1: block (head, slice) sums its slice of the keys and values of
 // positions [0, min(n, 2d)) per feature (fp32).  Thread -> 8 features (16 bytes) of K (groups 0-7) or V (groups 8-15) and
@@ -138,9 +133,12 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
                                                        float* __restrict__ anchors,
                                                        unsigned char* __restrict__ packed,
                                                        unsigned char* __restrict__ kimg,
+                                                       unsigned char* __restrict__ kuimg,
                                                        unsigned* __restrict__ guard, int n,
                                                        int ntiles) {
     __shared__ float anc[2 * FD];
+    __shared__ float kst[MT][FD + 1];   // centred fp16 keys of the tile, as floats
+    __shared__ float vpart[8][MT];      // |v - a_v|^2 over each thread's 8 features
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
     const int tid = threadIdx.x, pr = tid & 31, fg = tid >> 5;
     if (tid < 2 * FD) {
@@ -193,6 +191,7 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
     const uint32_t ka[4] = {k0.x, k0.y, k0.z, k0.w}, kb[4] = {k1.x, k1.y, k1.z, k1.w};
     const uint32_t va[4] = {v0.x, v0.y, v0.z, v0.w}, vb[4] = {v1.x, v1.y, v1.z, v1.w};
     const bool za = ja >= n, zb = jb >= n;
+    float vsa = 0.0f, vsb = 0.0f;   // |v - a_v|^2 of keys 2p, 2p+1 over this thread's features
     {   // the head's largest centred magnitudes, for the range guard
         float mk = 0.0f, mv = 0.0f;
 #pragma unroll
@@ -229,6 +228,42 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
             dst[row * (M_LD / 2) + MT / 2 + pr] = 0u;
             dst[(FD + row) * (M_LD / 2) + MT / 2 + pr] = 0u;
         }
+        kst[2 * pr][row] = static_cast<float>(kk[0]);
+        kst[2 * pr + 1][row] = static_cast<float>(kk[1]);
+        vsa = fmaf(static_cast<float>(vv[0]), static_cast<float>(vv[0]), vsa);
+        vsb = fmaf(static_cast<float>(vv[1]), static_cast<float>(vv[1]), vsb);
+    }
+    vpart[fg][2 * pr] = vsa;
+    vpart[fg][2 * pr + 1] = vsb;
+    __syncthreads();
+    // Check image: thread j < 64 takes key j through a 64-point Walsh-Hadamard transform
+    // (X[m] = sum_f (-1)^popcount(f & m) x_f) and keeps the odd-index coefficients.
+    unsigned char* kut = kuimg + (static_cast<int64_t>(bh) * ntiles + t) * KU_TILE_BYTES;
+    if (tid < MT) {
+        float x[FD];
+#pragma unroll
+        for (int f = 0; f < FD; ++f) x[f] = kst[tid][f];
+#pragma unroll
+        for (int hh = 1; hh < FD; hh <<= 1)
+#pragma unroll
+            for (int i = 0; i < FD; i += 2 * hh)
+#pragma unroll
+                for (int e = i; e < i + hh; ++e) {
+                    const float a0 = x[e], a1 = x[e + hh];
+                    x[e] = a0 + a1;
+                    x[e + hh] = a0 - a1;
+                }
+        _Float16* kur = reinterpret_cast<_Float16*>(kut);
+#pragma unroll
+        for (int tq = 0; tq < NCHK; ++tq) kur[tq * M_LD + tid] = static_cast<_Float16>(x[2 * tq + 1]);
+        float nv = 0.0f;
+#pragma unroll
+        for (int f8 = 0; f8 < 8; ++f8) nv += vpart[f8][tid];
+        reinterpret_cast<float*>(kut + KU_NRM)[tid] = nv;
+    } else if (tid < MT + NCHK) {   // row padding of the projections
+        *reinterpret_cast<uint4*>(kut + (tid - MT) * M_LD * 2 + MT * 2) = make_uint4(0, 0, 0, 0);
+    } else if (tid < MT + NCHK + 16) {   // tail after the norms
+        *reinterpret_cast<uint4*>(kut + KU_NRM + MT * 4 + (tid - MT - NCHK) * 16) = make_uint4(0, 0, 0, 0);
     }
 }
 
@@ -346,396 +381,8 @@ __global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restr
 // Upper 16x16 block (I, J), I <= J, of a symmetric 64x64 matrix held as 10 MFMA accumulators.
 __device__ __forceinline__ constexpr int ublk(int I, int J) { return I * 4 - I * (I - 1) / 2 + (J - I); }
 
-// Solve (C + ridge) y = z for one query, one wave: blocked LDL^T in 16-column panels.
-//   ckk: the upper blocks of the SPD matrix in MFMA accumulator layout (lane (g, c)
-//        register r of ckk[ublk(I, J)] = entry (16 I + 4 g + r, 16 J + c)); overwritten.
-//   z: this lane's right-hand-side entry (row = lane).  Pivots <= thresh are dropped (their
-//        unknowns become zero).  Lt: this wave's LDS area, FD * (FD + 1) + FD floats.
-// Returns y[lane].  Each panel is eliminated lane-per-row (lane a holds the panel part of
-// row a, pivot rows broadcast by readlane) and its multipliers go to LDS as
-// Lt[P][a] = L[a][P]; the trailing blocks, still in the accumulators, take the update
-// L D L^T on the matrix cores (fp32); D L^T y = z is then solved backwards.
-__device__ __forceinline__ float ldl_solve_wave(float4v (&ckk)[10], float z, const float thresh, float* Lt,
-                                                const int lane, const int g, const int c, bool& dropped) {
-    constexpr int ALD = FD + 1;
-    float* dvec = Lt + FD * ALD;
-    float dreg = 0.0f;   // lane P ends up holding the pivot d_P
-#pragma unroll
-    for (int K = 0; K < 4; ++K) {
-        // Stage block row K (rows 16K.., columns >= 16K) and read this lane's panel row:
-        // Lf[t] = C[a][16K + t] = C[16K + t][a].  Lanes a < 16K read stale words; their
-        // multipliers are zero below, so those never reach a live value.
-#pragma unroll
-        for (int J = K; J < 4; ++J)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Lt[(16 * K + 4 * g + r) * ALD + 16 * J + c] = ckk[ublk(K, J)][r];
-        LDS_FENCE();
-        float Lf[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) Lf[t] = Lt[(16 * K + t) * ALD + lane];
-        LDS_FENCE();
-        // Eliminate the panel; Lf[p] becomes this row's multiplier L[a][16K + p].
-#pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            const int P = 16 * K + p;
-            const float piv = lane_value(Lf[p], P);
-            // Reciprocal pivot (about 1 ulp); a dropped pivot gets a zero column of L.
-            const float inv = piv > thresh ? __builtin_amdgcn_rcpf(piv) : 0.0f;
-            dropped = dropped || !(piv > thresh);
-            int row = lane;
-            asm volatile("" : "+v"(row));   // row test per step: no precomputed lane masks
-            const float f = row > P ? Lf[p] * inv : 0.0f;
-            z = fmaf(-f, lane_value(z, P), z);
-#pragma unroll
-            for (int t = p + 1; t < 16; ++t) Lf[t] = fmaf(-f, lane_value(Lf[t], P), Lf[t]);
-            dreg = row == P ? piv : dreg;
-            Lf[p] = f;
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) Lt[(16 * K + t) * ALD + lane] = Lf[t];
-        dvec[lane] = dreg;
-        LDS_FENCE();
-        if (K < 3) {
-            // Trailing update C_IJ -= L_IK D_K L_JK^T for K < I <= J: 16x16x4 fp32 MFMAs over
-            // the panel columns 16K + 4s + g (K-slot g of step s).
-            float dv[4], Lo[4][4];
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                dv[s4] = dvec[16 * K + 4 * s4 + g];
-#pragma unroll
-                for (int X = K + 1; X < 4; ++X) Lo[X][s4] = Lt[(16 * K + 4 * s4 + g) * ALD + 16 * X + c];
-            }
-#pragma unroll
-            for (int I = K + 1; I < 4; ++I)
-#pragma unroll
-                for (int J = I; J < 4; ++J)
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4)
-                        ckk[ublk(I, J)] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                            -Lo[I][s4], dv[s4] * Lo[J][s4], ckk[ublk(I, J)], 0, 0, 0);
-            LDS_FENCE();
-        }
-    }
-    // Back substitution L^T y = x with x = D^{-1} z (zero at dropped pivots), from the last
-    // column: y_P = x_P, then x_a -= L[P][a] y_P, where L[P][a] = Lt[a][P] is zero unless
-    // P > a.  Each x_a is final once its own step has passed, so x ends as y.
-    float inv_d = __builtin_amdgcn_rcpf(dreg);
-    inv_d = fmaf(inv_d, fmaf(-dreg, inv_d, 1.0f), inv_d);   // one Newton step: ~0.5 ulp
-    float x = dreg > thresh ? z * inv_d : 0.0f;
-#pragma unroll
-    for (int P = FD - 1; P >= 0; --P) x = fmaf(-Lt[lane * ALD + P], lane_value(x, P), x);
-    return x;
-}
-
-__device__ __forceinline__ void moments_block(
-    const int bidx, unsigned char* smem, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ mrow,
-    const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
-    float* __restrict__ out, unsigned* __restrict__ guard, int* __restrict__ list,
-    int n, int row0, int row1, int BH, float sl2, float lambda) {
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wu = __builtin_amdgcn_readfirstlane(w);   // the same value, as a scalar
-    const int g = lane >> 4, c = lane & 15;
-    const int nrows = n - row0;   // rows of the row-max array
-    const int nblk = (row1 - row0 + B_WAVES - 1) / B_WAVES;
-    int blk, bh;
-    head_major_block(bidx, BH, nblk, &bh, &blk);
-
-    const int i0 = row0 + blk * B_WAVES;
-    const int i = i0 + w;
-    const bool valid = i < row1;
-    if (head_unsafe(guard, bh)) {   // block-uniform: the head's rows go to the fp64 kernel
-        if (valid && lane == 0) hand_back(guard, list, bh, n, i);
-        return;
-    }
-    const int ic = min(i, row1 - 1);
-    const int last = min(i0 + B_WAVES - 1, row1 - 1);
-    const int64_t base = static_cast<int64_t>(bh) * n * FD;
-    const uint16_t* kh = k + base;
-
-    // Rows B_WAVES.. of every Sw2 buffer are the zero rows of the weight operand.
-    for (int e = tid; e < M_NBUF * (16 - B_WAVES) * M_LD / 8; e += 256) {
-        const int bsel = e / ((16 - B_WAVES) * M_LD / 8), rem = e % ((16 - B_WAVES) * M_LD / 8);
-        *reinterpret_cast<uint4*>(smem + bsel * M_BUF_BYTES + M_SW2 + B_WAVES * M_LD * 2 + rem * 16) =
-            make_uint4(0, 0, 0, 0);
-    }
-    // Score operand: column c < B_WAVES is query i0 + c (the other columns are zero).
-    const int qcol = min(i0 + c, row1 - 1);
-    const bool colv = c < B_WAVES;
-    const float mcol = mrow[static_cast<int64_t>(bh) * nrows + (qcol - row0)];   // log2 units
-    bf16x8 qf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (colv) raw = *reinterpret_cast<const uint4*>(q + base + static_cast<int64_t>(qcol) * FD + ks * 32 + 8 * g);
-        qf[ks] = __builtin_bit_cast(bf16x8, raw);
-    }
-
-    // Scores of key block w (16 keys) of a tile for the 4 queries: lane (g, c) register r =
-    // query c < 4, key 16w + 4g + r.  Issued before the tile's moments so that the MFMA
-    // latency hides under them; sqrt of the shifted weights (Sw) and their fp16 squares (Sw2)
-    // are stored after.  om2p sums those squares (query c, keys of block w).
-    float om2p = 0.0f;
-    const float hs = 0.5f * sl2, hm = 0.5f * mcol;
-    auto score_mfma = [&](uint4 kq0, uint4 kq1) {
-        float4v s = {0.f, 0.f, 0.f, 0.f};
-        s = mfma_bf16(__builtin_bit_cast(bf16x8, kq0), qf[0], s);
-        return mfma_bf16(__builtin_bit_cast(bf16x8, kq1), qf[1], s);
-    };
-    auto score_store = [&](float4v s, unsigned char* buf, int j0) {
-        float e[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) e[rr] = __builtin_amdgcn_exp2f(fmaf(s[rr], hs, -hm));  // raw v_exp_f32
-        if (j0 + MT - 1 > i0) {   // block-uniform: keys past some query of the block
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) e[rr] = j0 + 16 * w + 4 * g + rr <= qcol ? e[rr] : 0.0f;
-        }
-        half4 sw4;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sw4[rr] = static_cast<_Float16>(e[rr]);
-        const half4 w4 = sw4 * sw4;
-        if (colv) {
-            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW) + c * M_LD + 16 * w + 4 * g) = sw4;
-            *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(buf + M_SW2) + c * M_LD + 16 * w + 4 * g) = w4;
-            const h16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-            om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 0, 1), one, om2p, false);
-            om2p = __builtin_amdgcn_fdot2(__builtin_shufflevector(w4, w4, 2, 3), one, om2p, false);
-        }
-    };
-
-    float4v ckk[10], cvk[16];
-#pragma unroll
-    for (int t = 0; t < 10; ++t) ckk[t] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 16; ++t) cvk[t] = float4v{0.f, 0.f, 0.f, 0.f};
-    // S_k, S_v of the block's queries (rows) for features 16 w + c (columns).
-    float4v sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-
-    const int ntiles = (last + MT) / MT;
-    const int ptiles = (n + MT - 1) / MT;
-    // The head's tile images as a buffer resource: copies address them with a scalar tile
-    // offset and loop-invariant per-lane offsets, so no vector address registers are rewritten
-    // while earlier loads are still in flight.
-    const __amdgpu_buffer_rsrc_t img = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(uniform_ptr(packed + static_cast<int64_t>(bh) * ptiles * PACK_TILE_BYTES)),
-        0, ptiles * PACK_TILE_BYTES, 0x00020000);
-    int voff[M_WLOADS];
-#pragma unroll
-    for (int e = 0; e < M_WLOADS; ++e) voff[e] = lane * 16 + min(wu + B_WAVES * e, M_LOADS - 1) * 1024;
-    // The head's keys (bf16, key-major) as a buffer resource for the score operand: lane
-    // reads key 16w + c of the tile, features 8g.. and 32 + 8g..; keys at or past n lie
-    // beyond the resource's size and read as zero (their scores are masked anyway).
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned char*>(uniform_ptr(reinterpret_cast<const unsigned char*>(kh))), 0, n * FD * 2,
-        0x00020000);
-    const int kq_off = (16 * w + c) * FD * 2 + 16 * g;
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-    auto buf = [&](int tt) { return smem + (tt % M_NBUF) * M_BUF_BYTES; };
-    // Start tile tt: its image goes straight from the workspace into ring buffer tt % 3 (wave
-    // w copies KiB chunks w, w+4, ..., no registers involved; every wave issues exactly
-    // M_WLOADS copies, the surplus ones repeating the last chunk, which rewrites the same
-    // bytes), its score operand (key 16w + c) into q0, q1.  Past the last tile the last one
-    // is re-read into a buffer nobody reads again, which keeps the loads in flight the same.
-    auto issue = [&](int tt, uint4& q0, uint4& q1) {
-        const int ts = min(tt, ntiles - 1);
-        const uint32_t dst = lds0 + static_cast<uint32_t>((tt % M_NBUF) * M_BUF_BYTES);
-#pragma unroll
-        for (int e = 0; e < M_WLOADS; ++e) {
-            const int u = min(wu + B_WAVES * e, M_LOADS - 1);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                img, reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024)),
-                16, voff[e], ts * PACK_TILE_BYTES, 0, 0);
-        }
-        q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off, ts * MT * FD * 2, 0));
-        q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kq_off + 64, ts * MT * FD * 2, 0));
-    };
-    // Loads complete in order.  After tile t+1's image come 2 + M_WLOADS + 2 more loads (its
-    // score operand, tile t+2's image and score operand), so vmcnt <= that count means it has
-    // landed in LDS.  Encoding: vmcnt (4 bits), expcnt and lgkmcnt at their maxima (no wait).
-    static_assert(M_WLOADS + 4 < 16, "vmcnt operand is 4 bits here");
-    auto wait_tile = [] {
-        __builtin_amdgcn_s_waitcnt((M_WLOADS + 4) | (0x7 << 4) | (0xF << 8));
-        LDS_FENCE();
-    };
-    // Workgroup barrier of the ring: this wave's LDS stores are complete (lgkmcnt 0) and the
-    // copy of the next tile was waited for above; the loads still in flight (the tile two
-    // steps ahead) are deliberately not waited for, which __syncthreads() would do.
-    auto ring_barrier = [] {
-        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
-        LDS_FENCE();
-        __builtin_amdgcn_s_barrier();
-        LDS_FENCE();
-    };
-    auto compute = [&](int t, const unsigned char* cur) {
-        const int j0 = t * MT;
-        const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
-        const _Float16* Vt = Kt + FD * M_LD;
-        const _Float16* Sw = reinterpret_cast<const _Float16*>(cur + M_SW);
-        const _Float16* Sw2 = reinterpret_cast<const _Float16*>(cur + M_SW2);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            if (j0 + 32 * sub > last) break;  // block-uniform: past every query of the block
-            // Operands of the block sums S_k, S_v (all 4 queries, feature block w).
-            const int ko = (w * 16 + c) * M_LD + 32 * sub + 8 * g;
-            const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * M_LD + 32 * sub + 8 * g);
-            const half8 kw = *reinterpret_cast<const half8*>(Kt + ko);
-            const half8 vw = *reinterpret_cast<const half8*>(Vt + ko);
-            if (j0 + 32 * sub <= ic) {  // wave-uniform: keys of this query's prefix
-                const half8 sw = *reinterpret_cast<const half8*>(Sw + w * M_LD + 32 * sub + 8 * g);
-                half8 rk[4];
-#pragma unroll
-                for (int fb = 0; fb < 4; ++fb) {
-                    const half8 kf = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * M_LD + 32 * sub + 8 * g);
-                    rk[fb] = kf * sw;
-                }
-                int idx = 0;
-#pragma unroll
-                for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-                    for (int fb2 = fb; fb2 < 4; ++fb2) { ckk[idx] = mfma_f16(rk[fb], rk[fb2], ckk[idx]); ++idx; }
-#pragma unroll
-                for (int fv = 0; fv < 4; ++fv) {
-                    const half8 vf = *reinterpret_cast<const half8*>(Vt + (fv * 16 + c) * M_LD + 32 * sub + 8 * g);
-                    const half8 rv = vf * sw;
-#pragma unroll
-                    for (int fb = 0; fb < 4; ++fb) cvk[fb * 4 + fv] = mfma_f16(rk[fb], rv, cvk[fb * 4 + fv]);
-                }
-            }
-            sk = mfma_f16(w8, kw, sk);
-            sv = mfma_f16(w8, vw, sv);
-        }
-    };
-    uint4 aq0, aq1, bq0, bq1;
-    issue(0, aq0, aq1);
-    issue(1, bq0, bq1);
-    wait_tile();
-    score_store(score_mfma(aq0, aq1), buf(0), 0);
-    ring_barrier();
-    for (int t = 0; t < ntiles; t += 2) {
-        // step t: tile t in LDS, tile t+1 landing (operand in B), tile t+2 issued now (A)
-        const float4v sb = score_mfma(bq0, bq1);
-        issue(t + 2, aq0, aq1);
-        compute(t, buf(t));
-        if (t + 1 < ntiles) score_store(sb, buf(t + 1), (t + 1) * MT);
-        wait_tile();
-        ring_barrier();
-        if (t + 1 >= ntiles) break;
-        // step t+1: the same with the register sets swapped
-        const float4v sa = score_mfma(aq0, aq1);
-        issue(t + 3, bq0, bq1);
-        compute(t + 1, buf(t + 1));
-        if (t + 2 < ntiles) score_store(sa, buf(t + 2), (t + 2) * MT);
-        wait_tile();
-        ring_barrier();
-    }
-
-    // Copies issued past the last tile may still be landing in ring buffers that the solve
-    // area overlaps: wait for all of this wave's loads (the barrier below covers the others).
-    __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
-    LDS_FENCE();
-
-    // ---- block sums -> LDS (outside the solve area): row r of sk / sv is query r.
-    float* means = reinterpret_cast<float*>(smem + B_MEAN_OFF);
-    om2p += __shfl_xor(om2p, 16);
-    om2p += __shfl_xor(om2p, 32);
-    if (g == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            means[r * B_MEAN_FLOATS + w * 16 + c] = sk[r];
-            means[r * B_MEAN_FLOATS + FD + w * 16 + c] = sv[r];
-        }
-        if (colv) means[c * B_MEAN_FLOATS + 2 * FD + w] = om2p;
-    }
-    __syncthreads();
-    const float* mq = means + w * B_MEAN_FLOATS;
-    float om2 = 0.0f;
-#pragma unroll
-    for (int t = 0; t < B_WAVES; ++t) om2 += mq[2 * FD + t];
-    const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
-
-    // ---- ridge-rescaled SPD solve (blocked LDL^T, this wave's LDS area), then b.
-    float* Lt = reinterpret_cast<float*>(smem) + w * B_SOLVE_FLOATS;
-    float* yv = Lt + FD * (FD + 1) + FD;
-    // Rank-one downdates: C_kk -= S_k S_k^T / omega', C_vk^T -= S_k S_v^T / omega'.
-    float4v skr[4];
-    float skc[4], svc[4];
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-        skr[fb] = *reinterpret_cast<const float4v*>(mq + fb * 16 + 4 * g) * iom2;
-        skc[fb] = mq[fb * 16 + c];
-        svc[fb] = mq[FD + fb * 16 + c];
-    }
-    const float m_x = mrow[static_cast<int64_t>(bh) * nrows + (ic - row0)];
-    const float lam_s = lambda * exp2f(-m_x);
-    float dmax = -INFINITY;
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int J = I; J < 4; ++J)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float val = fmaf(-skr[I][r], skc[J], ckk[ublk(I, J)][r]);
-                if (I == J && 4 * g + r == c) {   // diagonal entry: ridge
-                    val += lam_s;
-                    dmax = fmaxf(dmax, val);
-                }
-                ckk[ublk(I, J)][r] = val;
-            }
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int fv = 0; fv < 4; ++fv)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) cvk[fb * 4 + fv][r] = fmaf(-skr[fb][r], svc[fv], cvk[fb * 4 + fv][r]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, off));
-    // lambda > 0: drop only pivots that rounding made non-positive; lambda = 0: also drop
-    // directions the prefix leaves (numerically) undetermined.
-    const float thresh = lambda > 0.0f ? 0.0f : 1e-6f * dmax;
-    const float qa = bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]);
-    // kbar = a_k + S_k / omega' (the weighted mean of the centred keys, same weights as C)
-    const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD;
-    float z = fmaf(mq[lane], iom2, anc[lane]) - qa;
-
-    bool dropped = false;
-    const float ylane = ldl_solve_wave(ckk, z, thresh, Lt, lane, g, c, dropped);
-    yv[lane] = ylane;
-    LDS_FENCE();
-
-    // b = vbar - C_vk y; lane holds C_vk^T[fb*16 + 4g + r][fv*16 + c].
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb) {
-        const float4v yy = *reinterpret_cast<const float4v*>(yv + fb * 16 + 4 * g);
-#pragma unroll
-        for (int fv = 0; fv < 4; ++fv)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) part[fv] = fmaf(cvk[fb * 4 + fv][r], yy[r], part[fv]);
-    }
-#pragma unroll
-    for (int fv = 0; fv < 4; ++fv) {
-        part[fv] += __shfl_xor(part[fv], 16);
-        part[fv] += __shfl_xor(part[fv], 32);
-    }
-    bool bad = false;
-    if (valid && g == 0) {
-        float* orow = out + base + static_cast<int64_t>(i) * FD;
-#pragma unroll
-        for (int fv = 0; fv < 4; ++fv) {
-            const float o = fmaf(svc[fv], iom2, anc[FD + fv * 16 + c]) - part[fv];
-            bad = bad || !isfinite(o);
-            orow[fv * 16 + c] = o;
-        }
-    }
-    // A non-finite row, or a pivot dropped while the ridge keeps the system positive definite
-    // (rounding made it indefinite), goes to the fp64 kernel.
-    const bool any_bad = (__ballot(bad) & 0xFFFFull) != 0;   // every lane takes part
-    if (valid && lane == 0 && (any_bad || (dropped && lambda > 0.0f))) hand_back(guard, list, bh, n, i);
-}
-
 // ---------------------------------------------------------------------------------------
-// Rows i >= 4d: the cross moment C_vk is never formed.  Pass 1 (lla_keymom_kernel) builds
+// Rows i >= 2d: the cross moment C_vk is never formed.  Pass 1 (the key-moment blocks) builds
 // the key moments and solves for y; pass 2 (lla_probe_kernel) applies C_vk to y in one
 // attention-like sweep:
 //   b_i = vbar_i - C_vk y_i = a_v + (1/omega') sum_j w_ij t_ij (v_j - a_v),
@@ -786,7 +433,10 @@ constexpr int K_SOLVE_BYTES = K_SOLVE_FLOATS * 4 * B_WAVES;
 constexpr int K_MEAN_OFF = K_SOLVE_BYTES > M_NBUF * K_BUF ? K_SOLVE_BYTES : M_NBUF * K_BUF;
 constexpr int K_SMEM = K_MEAN_OFF + (K_BQ * FD + B_WAVES * 16) * 4;
 constexpr int P_YLD = 2 * FD;                // per query: yh hi (fp16) | yh lo (fp16)
-constexpr int P_QSC = 4;                     // per query: gamma, 2^-e, 1/omega', dropped-pivot flag
+constexpr int P_QSC = 8;                     // per query: gamma, 2^-e, 1/omega', dropped-pivot flag,
+                                             // weighted mean |k - a|^2, 3 unused
+// Per query, the check's target: the NCHK projections of q - a + lambda e^{-m} y.
+constexpr int P_CHK = NCHK;
 static_assert(K_IMG % 1024 == 0, "key image must be whole wave copies");
 static_assert(K_BQ <= 16, "score MFMA has 16 query columns");
 
@@ -976,8 +626,8 @@ __device__ __forceinline__ void group_solve(float4v (&ckk)[KQ][10], float (&zr)[
 __device__ __forceinline__ void keymom_block(
     const int bidx, unsigned char* smem, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float* __restrict__ mrow, const float* __restrict__ anchors, const unsigned char* __restrict__ packed,
-    _Float16* __restrict__ yhl, float* __restrict__ qsc, const unsigned* __restrict__ guard,
-    int n, int row0, int rowp, int BH, float sl2, float lambda) {
+    _Float16* __restrict__ yhl, float* __restrict__ qsc, float* __restrict__ chk,
+    const unsigned* __restrict__ guard, int n, int row0, int rowp, int BH, float sl2, float lambda) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -1224,8 +874,47 @@ __device__ __forceinline__ void keymom_block(
         }
         thr = 1e-6f * (G == 0 ? dm[0] : G == 1 ? dm[1] : G == 2 ? dm[2] : dm[3]);
     }
+    // The check's key scale: trace of sum R R^T (before the downdate) / omega', the weighted
+    // mean of |k - a|^2.
+    float trq[KQ];
+#pragma unroll
+    for (int qq = 0; qq < KQ; ++qq) {
+        float tr = 0.0f;
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tr += 4 * g + r == c ? ckk[qq][ublk(I, I)][r] : 0.0f;
+        trq[qq] = wave_sum_f(tr);
+    }
+    const float trG = G == 0 ? trq[0] : G == 1 ? trq[1] : G == 2 ? trq[2] : trq[3];
+    const float lamG = G == 0 ? lam_q[0] : G == 1 ? lam_q[1] : G == 2 ? lam_q[2] : lam_q[3];
     float dropped = 0.0f;
     group_solve(ckk, zr, thr, lam_q, sks, mqG, Sg, yr, g, c, dropped);
+    // Check target: the LLA weights reproduce linear functions of the keys, so applied to the
+    // centred keys they give q - a + lambda e^{-m} y (exactly, for the y they were formed
+    // with); projected on the NCHK directions, direction t at feature f = l + 16 j carrying
+    // the sign (-1)^popcount(f & (2t + 1)).
+    float cv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int a = l + 16 * j;
+        cv[j] = bf16_bits_to_f32(q[base + static_cast<int64_t>(iqc) * FD + a]) - anc[a] + lamG * yr[j];
+    }
+    float chk_lo = 0.0f, chk_hi = 0.0f;   // directions l and l + 16
+#pragma unroll
+    for (int tq = 0; tq < NCHK; ++tq) {
+        const int m = 2 * tq + 1;
+        const bool sl = (__builtin_popcount(l & (m & 15)) & 1) != 0;
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool sj = (__builtin_popcount(j & (m >> 4)) & 1) != 0;
+            part += (sl != sj) ? -cv[j] : cv[j];
+        }
+        const float sum = row_sum_f(part);
+        if (tq < 16) chk_lo = l == tq ? sum : chk_lo;
+        else chk_hi = l == tq - 16 ? sum : chk_hi;
+    }
     // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together), and
     // gamma = 1 + S_k . yh / omega'.
     float yh[4], amax = 0.0f;
@@ -1257,9 +946,13 @@ __device__ __forceinline__ void keymom_block(
             yhl[qrow * P_YLD + FD + l + 16 * j] = lo[j];
         }
         // qsc[3] flags a pivot dropped although the ridge keeps the system positive definite.
-        if (l == 0)
+        if (l == 0) {
             *reinterpret_cast<float4v*>(qsc + qrow * P_QSC) =
                 float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, lambda > 0.0f ? dropped : 0.0f};
+            *reinterpret_cast<float4v*>(qsc + qrow * P_QSC + 4) = float4v{trG * iom2, 0.0f, 0.0f, 0.0f};
+        }
+        chk[qrow * P_CHK + l] = chk_lo;
+        chk[qrow * P_CHK + 16 + l] = chk_hi;
     }
 }
 
@@ -1272,13 +965,20 @@ __device__ __forceinline__ void keymom_block(
 //   U^T = (K - a) (yh_hi + yh_lo)^T 2^e (four fp16 MFMAs),
 //   P = fp16(w fp16(gamma - U 2^-e)) with w = fp16(sqrt-weight)^2 as in pass 1 (packed fp16);
 // lane (g, c) register r holds key 16 kb + 4g + r of query c, which is already the A
-// operand of O += P (V - a_v) over 32-key steps (K-slots: keys 4g.., then 16 + 4g..).
+// operand of O += P (V - a_v) over 32-key steps (K-slots: keys 4g.., then 16 + 4g..), and
+// of the check sums OK += P (projected K - a), with sum w |v - a_v|^2 on the side.
+//   The check: the LLA weights l_j = P_j / omega' reproduce the centred query,
+// sum_j l_j (k_j - a) = q - a + lambda e^{-m} y, for the y the weights were formed with and
+// the moments of the same rounded data; the fp16 factor R of pass 1 breaks that identity by
+// as much as its rounding moves y.  The projected deviation, in units of the weighted rms of
+// |k - a| and scaled by the weighted rms of |v - a_v| over |b|, tracks the row's relative
+// error; rows above CHK_TOL go to the fp64 kernel.
 constexpr int P_WAVES = 4;
 constexpr int P_NBUF = 2;
 constexpr int P_SETS = 2;                    // query sets of 16 per wave
 constexpr int P_QW = 16 * P_SETS;
 constexpr int P_QB = P_WAVES * P_QW;
-constexpr int P_BUF = 2 * KM_TILE_BYTES + FD * M_LD * 2;   // bf16 K | fp16 K - a | fp16 V - a_v
+constexpr int P_BUF = 2 * KM_TILE_BYTES + FD * M_LD * 2 + KU_TILE_BYTES;   // bf16 K | fp16 K - a | fp16 V - a_v | check image
 constexpr int P_LOADS = P_BUF / 1024;
 constexpr int P_WLOADS = (P_LOADS + P_WAVES - 1) / P_WAVES;
 constexpr int P_SMEM = P_NBUF * P_BUF;
@@ -1287,8 +987,8 @@ static_assert(P_BUF % 1024 == 0 && 2 * KM_TILE_BYTES % 1024 == 0, "probe images 
 __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
     const unsigned char* __restrict__ packed, const unsigned char* __restrict__ kimg,
-    const _Float16* __restrict__ yhl, const float* __restrict__ qsc, float* __restrict__ out,
-    unsigned* __restrict__ guard, int* __restrict__ list,
+    const unsigned char* __restrict__ kuimg, const _Float16* __restrict__ yhl, const float* __restrict__ qsc,
+    const float* __restrict__ chk, float* __restrict__ out, unsigned* __restrict__ guard, int* __restrict__ list,
     int n, int row0, int rowp, int BH, float sl2) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1341,9 +1041,13 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(uniform_ptr(packed + static_cast<int64_t>(bh) * ptiles * PACK_TILE_BYTES)), 0,
         ptiles * PACK_TILE_BYTES, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ures = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(kuimg + static_cast<int64_t>(bh) * ptiles * KU_TILE_BYTES)), 0,
+        ptiles * KU_TILE_BYTES, 0x00020000);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-    // Chunk u of a buffer: u < 18 from the key-major images, else from the value half of the
-    // tile image.  Wave w issues chunks w, w+4, ..., w+24 (the last ones clamped to 26).
+    // Chunk u of a buffer: u < 18 from the key-major images, u < 27 from the value half of the
+    // tile image, the rest from the check image.  Wave w issues chunks w, w+4, ..., w+28.
+    constexpr int U_KM = 2 * KM_TILE_BYTES / 1024, U_V = U_KM + FD * M_LD * 2 / 1024;
     auto issue = [&](int tt) {
         const int ts = min(tt, ntiles - 1);
         const uint32_t dst = lds0 + static_cast<uint32_t>((tt % P_NBUF) * P_BUF);
@@ -1351,11 +1055,14 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
         for (int e = 0; e < P_WLOADS; ++e) {
             const int u = min(wu + P_WAVES * e, P_LOADS - 1);
             auto* ldst = reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024));
-            if (u < 2 * KM_TILE_BYTES / 1024)
+            if (u < U_KM)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, ldst, 16, lane * 16 + u * 1024, ts * KM_STRIDE, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, ldst, 16, lane * 16 + K_IMG + (u - 2 * KM_TILE_BYTES / 1024) * 1024,
+            else if (u < U_V)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, ldst, 16, lane * 16 + K_IMG + (u - U_KM) * 1024,
                                                          ts * PACK_TILE_BYTES, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ures, ldst, 16, lane * 16 + (u - U_V) * 1024,
+                                                         ts * KU_TILE_BYTES, 0, 0);
         }
     };
     // The copies of the next tile have landed (all loads waited for) and every wave is done
@@ -1367,11 +1074,16 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
         LDS_FENCE();
     };
 
-    float4v o[P_SETS][4];
+    float4v o[P_SETS][4], ok[P_SETS][NCHK / 16];
+    float wvn[P_SETS];   // sum w |v - a_v|^2 of query c over this lane's keys
 #pragma unroll
-    for (int st = 0; st < P_SETS; ++st)
+    for (int st = 0; st < P_SETS; ++st) {
 #pragma unroll
         for (int fv = 0; fv < 4; ++fv) o[st][fv] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < NCHK / 16; ++db) ok[st][db] = float4v{0.f, 0.f, 0.f, 0.f};
+        wvn[st] = 0.0f;
+    }
     issue(0);
     wait_and_sync();
     // A tile wholly below the wave's first query needs no causal mask: those tiles (all but
@@ -1385,6 +1097,8 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
             const unsigned char* KB = cur;
             const unsigned char* KC = cur + KM_TILE_BYTES;
             const _Float16* VI = reinterpret_cast<const _Float16*>(cur + 2 * KM_TILE_BYTES);
+            const _Float16* UI = reinterpret_cast<const _Float16*>(cur + 2 * KM_TILE_BYTES + FD * M_LD * 2);
+            const float* NR = reinterpret_cast<const float*>(cur + 2 * KM_TILE_BYTES + FD * M_LD * 2 + KU_NRM);
             half4 p[P_SETS][4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -1411,7 +1125,11 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
                         sw4[r] = static_cast<_Float16>(e);
                         t4[r] = static_cast<_Float16>(fmaf(-u[r], isig[st], gam[st]));
                     }
-                    p[st][kb] = (sw4 * sw4) * t4;   // w = fp16(sw^2) exactly as pass 1, then P = fp16(w t)
+                    const half4 w4 = sw4 * sw4;   // w = fp16(sw^2) exactly as pass 1
+                    p[st][kb] = w4 * t4;          // P = fp16(w t)
+                    const float4v nr = *reinterpret_cast<const float4v*>(NR + kb * 16 + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) wvn[st] = fmaf(static_cast<float>(w4[r]), nr[r], wvn[st]);
                 }
             }
 #pragma unroll
@@ -1428,6 +1146,18 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
                         o[st][fv] = mfma_f16(pa, vb, o[st][fv]);
                     }
                 }
+#pragma unroll
+                for (int db = 0; db < NCHK / 16; ++db) {
+                    const _Float16* ur = UI + (db * 16 + c) * M_LD + 32 * ks + 4 * g;
+                    const half4 u0 = *reinterpret_cast<const half4*>(ur);
+                    const half4 u1 = *reinterpret_cast<const half4*>(ur + 16);
+                    const half8 ub = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int st = 0; st < P_SETS; ++st) {
+                        const half8 pa = __builtin_shufflevector(p[st][2 * ks], p[st][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                        ok[st][db] = mfma_f16(pa, ub, ok[st][db]);
+                    }
+                }
             }
         };
         if constexpr (!decltype(phase)::value) tile_body(std::false_type{});
@@ -1440,30 +1170,44 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
     // Copies issued past the last tile are still landing in LDS: let them finish before exit.
     __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));
 
-    // Output rows: lane (g, c) register r of set st = query qw0 + 16 st + 4g + r, feature 16 fv + c.
-    // A row whose output is not finite, or whose solve dropped a pivot (qsc[3]), goes to the
-    // fp64 kernel.
+    // Output rows: lane (g, c) register r of set st = query qw0 + 16 st + 4g + r, feature 16 fv + c
+    // (direction 16 db + c of the check sums).  A row goes to the fp64 kernel if its output is
+    // not finite, its solve dropped a pivot (qsc[3]), or its check exceeds CHK_TOL.
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * FD + FD;
 #pragma unroll
-    for (int st = 0; st < P_SETS; ++st)
+    for (int st = 0; st < P_SETS; ++st) {
+        // sum_j w_j |v_j - a_v|^2 of query c (over all keys), then of query 4g + r below
+        float vq = wvn[st];
+        vq += __shfl_xor(vq, 16);
+        vq += __shfl_xor(vq, 32);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = qw0 + 16 * st + 4 * g + r;
-            bool bad = false;
-            if (i < n) {
-                const float4v sc = *reinterpret_cast<const float4v*>(qsc + (static_cast<int64_t>(bh) * prows + (i - rowp)) * P_QSC);
-                float* orow = out + base + static_cast<int64_t>(i) * FD;
+            const int64_t qrow = static_cast<int64_t>(bh) * prows + (min(i, n - 1) - rowp);
+            const float4v sc = *reinterpret_cast<const float4v*>(qsc + qrow * P_QSC);
+            const float kn2 = qsc[qrow * P_QSC + 4];
+            float bb = 0.0f, rr = 0.0f;
 #pragma unroll
-                for (int fv = 0; fv < 4; ++fv) {
-                    const float ov = fmaf(o[st][fv][r], sc[2], anc[fv * 16 + c]);
-                    bad = bad || !isfinite(ov);
-                    orow[fv * 16 + c] = ov;
-                }
-                bad = bad || sc[3] != 0.0f;
+            for (int fv = 0; fv < 4; ++fv) {
+                const float ov = fmaf(o[st][fv][r], sc[2], anc[fv * 16 + c]);
+                bb = fmaf(ov, ov, bb);
+                if (i < n) out[base + static_cast<int64_t>(i) * FD + fv * 16 + c] = ov;
             }
+#pragma unroll
+            for (int db = 0; db < NCHK / 16; ++db) {
+                const float dv = fmaf(ok[st][db][r], sc[2], -chk[qrow * P_CHK + 16 * db + c]);
+                rr = fmaf(dv, dv, rr);
+            }
+            bb = row_sum_f(bb);
+            rr = row_sum_f(rr);
+            const float vn2 = __shfl(vq, 4 * g + r) * sc[2];
+            // (|res| / |k - a|_rms)^2 (|v - a_v|_rms / |b|)^2 against CHK_TOL^2; NaN fails.
+            const float est2 = (rr * (1.0f / NCHK)) * vn2 / (kn2 * bb);
+            const bool bad = i < n && (!(est2 <= CHK_TOL * CHK_TOL) || sc[3] != 0.0f);
             const uint64_t badm = __ballot(bad);   // every lane takes part
             if (c == 0 && i < n && ((badm >> (16 * g)) & 0xFFFFull) != 0) hand_back(guard, list, bh, n, i);
         }
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1693,11 +1437,230 @@ __device__ __forceinline__ void short_block(
     if (valid) out[base + static_cast<int64_t>(i) * FD + lane] = static_cast<float>(va - (acc - va * swu));
 }
 
-// All row work after the row maxima in one launch: short rows (fp64), rows [2d, 4d)
-// (explicit moments) and the key-moment blocks of rows >= 4d.  The short and explicit blocks
-// (the "aux" blocks) fill every other run of R_CHUNK dispatch positions at the start, so
-// that a CU tends to hold one aux block, mostly latency-bound, beside a key-moment block,
-// mostly on the matrix cores (the dispatcher places blocks b and b + CU count together).
+// Rows handed back by the range guard and the checks, in fp64: one wave per listed row, its
+// prefix streamed through LDS 64 keys at a time (scores recomputed in each pass), with the
+// arithmetic of the short rows: weights e^{s - m}, kbar and vbar (lane = feature), C_kk about
+// kbar on the matrix cores (v_mfma_f64_16x16x4f64), lane-per-row LDL^T, and
+// b = vbar - C_vk y through u_j = (k_j - kbar).y.  Any prefix length; the wave's latency
+// scales with the prefix, not with a block-wide elimination.
+constexpr int RF_WAVES = 4;
+constexpr int RF_KLD = FD + 2;    // bf16 row stride (halves) of a staged chunk: 33 words
+struct RefineWave {
+    double qs[FD];                // the query
+    double ws[MT];                // per-chunk weights (then w_j u_j)
+    double kb[FD];                // kbar
+    double xb[FD];                // pivot-row exchange, then y
+    double tb[16 * S_TLD];        // 16 rows of C_kk in transit
+    uint16_t ks[MT * RF_KLD];     // staged keys
+    uint16_t vs[MT * RF_KLD];     // staged values
+};
+
+__global__ __launch_bounds__(RF_WAVES * 64) void lla_refine_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    float* __restrict__ out, const int* __restrict__ list, const unsigned* __restrict__ count, int n,
+    double inv_h, double lambda) {
+    __shared__ RefineWave lds[RF_WAVES];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    RefineWave& L = lds[w];
+    const int total = static_cast<int>(*count);
+    for (int e = static_cast<int>(blockIdx.x) * RF_WAVES + w; e < total;
+         e += static_cast<int>(gridDim.x) * RF_WAVES) {
+        const int code = list[e];
+        const int bh = code / n, i = code % n, cnt = i + 1;
+        const int64_t base = static_cast<int64_t>(bh) * n * FD;
+        const uint16_t* kh = k + base;
+        const uint16_t* vh = v + base;
+        L.qs[lane] = static_cast<double>(bf16_bits_to_f32(q[base + static_cast<int64_t>(i) * FD + lane]));
+        // Stage keys (and values) c0 .. c0 + 63 of the prefix, zero past it: lane j copies
+        // row c0 + j (8 x 16 bytes).
+        auto stage = [&](int c0, bool with_v) {
+            const int j = c0 + lane;
+#pragma unroll
+            for (int u = 0; u < FD / 8; ++u) {
+                uint4 kx = make_uint4(0, 0, 0, 0), vx = kx;
+                if (j < cnt) {
+                    kx = *reinterpret_cast<const uint4*>(kh + static_cast<int64_t>(j) * FD + 8 * u);
+                    if (with_v) vx = *reinterpret_cast<const uint4*>(vh + static_cast<int64_t>(j) * FD + 8 * u);
+                }
+                const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w}, vw[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+                for (int h2 = 0; h2 < 4; ++h2) {
+                    *reinterpret_cast<uint32_t*>(L.ks + lane * RF_KLD + 8 * u + 2 * h2) = kw[h2];
+                    if (with_v) *reinterpret_cast<uint32_t*>(L.vs + lane * RF_KLD + 8 * u + 2 * h2) = vw[h2];
+                }
+            }
+            LDS_FENCE();
+        };
+        auto kval = [&](int jj, int a) { return static_cast<double>(bf16_bits_to_f32(L.ks[jj * RF_KLD + a])); };
+        auto vval = [&](int jj, int a) { return static_cast<double>(bf16_bits_to_f32(L.vs[jj * RF_KLD + a])); };
+        auto score = [&](int jj) {   // staged key jj (this lane's), scaled by 1/h
+            double acc = 0.0;
+#pragma unroll 16
+            for (int a = 0; a < FD; ++a) acc = fma(L.qs[a], kval(jj, a), acc);
+            return acc * inv_h;
+        };
+        LDS_FENCE();
+
+        // ---- pass 1: the row maximum of the scores
+        double mloc = -INFINITY;
+        for (int c0 = 0; c0 < cnt; c0 += MT) {
+            stage(c0, false);
+            if (c0 + lane < cnt) mloc = fmax(mloc, score(lane));
+            LDS_FENCE();
+        }
+        const double m = wave_max_d(mloc);
+
+        // ---- pass 2: omega, kbar, vbar (lane = feature)
+        double om = 0.0, ka = 0.0, va = 0.0;
+        for (int c0 = 0; c0 < cnt; c0 += MT) {
+            stage(c0, true);
+            const double wj = c0 + lane < cnt ? exp(score(lane) - m) : 0.0;
+            L.ws[lane] = wj;
+            om += wj;
+            LDS_FENCE();
+            const int nk = min(MT, cnt - c0);
+            for (int jj = 0; jj < nk; ++jj) {
+                const double wv = L.ws[jj];
+                ka = fma(wv, kval(jj, lane), ka);
+                va = fma(wv, vval(jj, lane), va);
+            }
+            LDS_FENCE();
+        }
+        om = wave_sum_d(om);
+        ka /= om;
+        va /= om;
+        L.kb[lane] = ka;
+        LDS_FENCE();
+
+        // ---- pass 3: C_kk = R^T R, R[j] = sqrt(w_j) (k_j - kbar), upper 16x16 blocks, 4 keys a step
+        double kb4[4];
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) kb4[fb] = L.kb[16 * fb + c];
+        double4v cacc[10];
+#pragma unroll
+        for (int t = 0; t < 10; ++t) cacc[t] = double4v{0.0, 0.0, 0.0, 0.0};
+        for (int c0 = 0; c0 < cnt; c0 += MT) {
+            stage(c0, false);
+            L.ws[lane] = c0 + lane < cnt ? exp(score(lane) - m) : 0.0;
+            LDS_FENCE();
+            const int nk = min(MT, cnt - c0);
+            for (int st = 0; st < (nk + 3) / 4; ++st) {
+                const int jj = 4 * st + g;
+                const bool in = jj < nk;
+                const double sw = in ? sqrt(L.ws[jj]) : 0.0;
+                double a4[4];
+#pragma unroll
+                for (int fb = 0; fb < 4; ++fb) a4[fb] = in ? sw * (kval(jj, 16 * fb + c) - kb4[fb]) : 0.0;
+                int idx = 0;
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int J = I; J < 4; ++J) {
+                        cacc[idx] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[I], a4[J], cacc[idx], 0, 0, 0);
+                        ++idx;
+                    }
+            }
+            LDS_FENCE();
+        }
+        // ridge on the diagonal, its largest entry
+        const double lam_s = lambda * exp(-m);
+        double dmax = 0.0;
+        {
+            int idx = 0;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * r + g == c) {
+                        cacc[idx][r] += lam_s;
+                        dmax = fmax(dmax, cacc[idx][r]);
+                    }
+                idx += 4 - I;
+            }
+        }
+        dmax = wave_max_d(dmax);
+        const double thresh = lambda > 0.0 ? 0.0 : 1e-12 * dmax;
+
+        // ---- to lane-per-row form through LDS, 16 rows at a time
+        double cr[FD];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+            int idx = 0;
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int J = I; J < 4; ++J) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (I == pp) L.tb[(4 * r + g) * S_TLD + 16 * J + c] = cacc[idx][r];
+                        else if (J == pp) L.tb[c * S_TLD + 16 * I + 4 * r + g] = cacc[idx][r];
+                    }
+                    ++idx;
+                }
+            LDS_FENCE();
+            if (g == pp) {
+#pragma unroll
+                for (int b = 0; b < FD; ++b) cr[b] = L.tb[c * S_TLD + b];
+            }
+            LDS_FENCE();
+        }
+        double z = ka - L.qs[lane];
+
+        // ---- LDL^T elimination (lane owns row), back substitution
+#pragma unroll
+        for (int pp = 0; pp < FD; ++pp) {
+            L.xb[lane] = cr[pp];
+            LDS_FENCE();
+            const double piv = L.xb[pp];
+            const double inv = piv > thresh ? 1.0 / piv : 0.0;
+            const double f = lane > pp ? cr[pp] * inv : 0.0;
+            const double zp = __shfl(z, pp);
+            z = fma(-f, zp, z);
+#pragma unroll
+            for (int b = pp + 1; b < FD; ++b) cr[b] = fma(-f, L.xb[b], cr[b]);
+            LDS_FENCE();
+        }
+        double ylane = 0.0;
+#pragma unroll
+        for (int pp = FD - 1; pp >= 0; --pp) {
+            const double dp = __shfl(cr[pp], pp);
+            const double zp = __shfl(z, pp);
+            const double yp = dp > thresh ? zp / dp : 0.0;
+            ylane = lane == pp ? yp : ylane;
+            z = fma(-cr[pp], yp, z);
+        }
+        L.xb[lane] = ylane;
+        LDS_FENCE();
+
+        // ---- pass 4: u_j = (k_j - kbar).y, then b = vbar - C_vk y
+        double swu = 0.0, acc = 0.0;
+        for (int c0 = 0; c0 < cnt; c0 += MT) {
+            stage(c0, true);
+            double wu = 0.0;
+            if (c0 + lane < cnt) {
+                double u = 0.0;
+#pragma unroll 16
+                for (int a = 0; a < FD; ++a) u = fma(kval(lane, a) - L.kb[a], L.xb[a], u);
+                wu = exp(score(lane) - m) * u;
+            }
+            L.ws[lane] = wu;
+            swu += wu;
+            LDS_FENCE();
+            const int nk = min(MT, cnt - c0);
+            for (int jj = 0; jj < nk; ++jj) acc = fma(L.ws[jj], vval(jj, lane), acc);
+            LDS_FENCE();
+        }
+        swu = wave_sum_d(swu);
+        out[base + static_cast<int64_t>(i) * FD + lane] = static_cast<float>(va - (acc - va * swu));
+    }
+}
+
+// All row work after the row maxima in one launch: short rows (fp64) and the key-moment
+// blocks of rows >= 2d.  The short blocks (the "aux" blocks) fill every other run of R_CHUNK
+// dispatch positions at the start, so that a CU tends to hold one aux block, mostly
+// latency-bound, beside a key-moment block, mostly on the matrix cores (the dispatcher places
+// blocks b and b + CU count together).
 struct RowsArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -1707,10 +1670,11 @@ struct RowsArgs {
     const unsigned char* packed;
     _Float16* yhl;
     float* qsc;
+    float* chk;
     float* out;
     unsigned* guard;   // range maxima and the count of rows handed back to the fp64 kernel
     int* list;         // rows handed back
-    int n, row0, rowp, BH, n_short, n_mom, n_key;
+    int n, row0, rowp, BH, n_short, n_key;
     float sl2, lambda;
     double inv_h, lambda_d;
 };
@@ -1737,51 +1701,48 @@ __device__ __forceinline__ void rows_block_role(int b, int n_key, int n_aux, int
     b -= ar;
     if (b < kr - kc) *key = both * R_CHUNK + kc + b;
 }
-constexpr int R_SMEM = K_SMEM > S_SMEM ? (K_SMEM > B_SMEM ? K_SMEM : B_SMEM) : (S_SMEM > B_SMEM ? S_SMEM : B_SMEM);
+constexpr int R_SMEM = K_SMEM > S_SMEM ? K_SMEM : S_SMEM;
 
 __global__ __launch_bounds__(256, 2) void lla_rows_kernel(const RowsArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int n_aux = a.n_short + a.n_mom;
     int aux = -1, key = -1;
-    rows_block_role(static_cast<int>(blockIdx.x), a.n_key, n_aux, &key, &aux);
+    rows_block_role(static_cast<int>(blockIdx.x), a.n_key, a.n_short, &key, &aux);
     if (aux >= 0) {
-        if (aux < a.n_short)
-            short_block(aux, smem, a.q, a.k, a.v, a.out, a.n, a.row0, a.BH, a.inv_h, a.lambda_d);
-        else
-            moments_block(aux - a.n_short, smem, a.q, a.k, a.v, a.mrow, a.anchors, a.packed, a.out, a.guard, a.list,
-                          a.n, a.row0, a.rowp, a.BH, a.sl2, a.lambda);
+        short_block(aux, smem, a.q, a.k, a.v, a.out, a.n, a.row0, a.BH, a.inv_h, a.lambda_d);
     } else if (key >= 0) {
-        keymom_block(key, smem, a.q, a.k, a.mrow, a.anchors, a.packed, a.yhl, a.qsc, a.guard, a.n, a.row0, a.rowp,
-                     a.BH, a.sl2, a.lambda);
+        keymom_block(key, smem, a.q, a.k, a.mrow, a.anchors, a.packed, a.yhl, a.qsc, a.chk, a.guard, a.n, a.row0,
+                     a.rowp, a.BH, a.sl2, a.lambda);
     }
 }
 
-// Rows [0, 2d): fp64 short-row kernel; [2d, 4d): explicit moments; [4d, n): probe path.
+// Rows [0, 2d): fp64 short-row kernel; [2d, n): key moments and probe pass.
 int fast_row0(int64_t n, int64_t d) { return static_cast<int>(n < 2 * d ? n : 2 * d); }
-int fast_rowp(int64_t n, int64_t d) { return static_cast<int>(n < 4 * d ? n : 4 * d); }
 
 // Fast-path workspace, each region 256-byte aligned:
 //   row maxima [B*H][n - 2d] | anchor partial sums [B*H][16][2d] | anchors [B*H][2d] |
 //   key/value tile images [B*H][tiles] | key-major key images (bf16, centred fp16)
-//   [B*H][tiles] | probe solutions (fp16 hi, lo) [B*H][n - 4d][2d] |
-//   probe scalars [B*H][n - 4d][4] | guard: count of rows handed back, then per head the
-//   largest |k - a| and |v - a_v| (float bits) [1 + 2 B*H] | rows handed back [B*H][n - 2d].
+//   [B*H][tiles] | check images [B*H][tiles] | probe solutions (fp16 hi, lo) [B*H][n - 2d][2d] |
+//   probe scalars [B*H][n - 2d][8] | check targets [B*H][n - 2d][32] | guard: count of rows
+//   handed back, then per head the largest |k - a| and |v - a_v| (float bits) [1 + 2 B*H] |
+//   rows handed back [B*H][n - 2d].
 struct FastLayout {
-    int64_t mrow, partial, anchors, packed, kimg, yhl, qsc, guard, list, total;
+    int64_t mrow, partial, anchors, packed, kimg, kuimg, yhl, qsc, chk, guard, list, total;
 };
 
 FastLayout fast_layout(int64_t BH, int64_t n, int64_t d) {
     auto up = [](int64_t bytes) { return (bytes + 255) & ~int64_t(255); };
-    const int64_t rows = n - fast_row0(n, d), prows = n - fast_rowp(n, d), tiles = (n + MT - 1) / MT;
+    const int64_t rows = n - fast_row0(n, d), prows = rows, tiles = (n + MT - 1) / MT;
     FastLayout L;
     L.mrow = 0;
     L.partial = L.mrow + up(BH * rows * 4);
     L.anchors = L.partial + up(BH * ANCHOR_SLICES * 2 * d * 4);
     L.packed = L.anchors + up(BH * 2 * d * 4);
     L.kimg = L.packed + BH * tiles * PACK_TILE_BYTES;
-    L.yhl = L.kimg + BH * tiles * KM_STRIDE;
+    L.kuimg = L.kimg + BH * tiles * KM_STRIDE;
+    L.yhl = L.kuimg + BH * tiles * KU_TILE_BYTES;
     L.qsc = L.yhl + up(BH * prows * P_YLD * 2);
-    L.guard = L.qsc + up(BH * prows * P_QSC * 4);
+    L.chk = L.qsc + up(BH * prows * P_QSC * 4);
+    L.guard = L.chk + up(BH * prows * P_CHK * 4);
     L.list = L.guard + up((1 + 2 * BH) * 4);
     L.total = L.list + up(BH * rows * 4);
     return L;
@@ -1798,6 +1759,12 @@ size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
     if (d == 128) return fast128_workspace_bytes(B, H, n);
     if (n - fast_row0(n, d) <= 0) return 0;
     return static_cast<size_t>(fast_layout(B * H, n, d).total);
+}
+
+int64_t fast_fallback_count_offset(int64_t B, int64_t H, int64_t n, int64_t d) {
+    if (d == 128) return fast128_fallback_count_offset(B, H, n);
+    if (n - fast_row0(n, d) <= 0) return -1;
+    return fast_layout(B * H, n, d).guard;
 }
 
 namespace {
@@ -1831,7 +1798,7 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     const int n = static_cast<int>(p.n);
     const int BH = static_cast<int>(p.B * p.H);
     const int row0 = fast_row0(p.n, p.d);
-    const int rowp = fast_rowp(p.n, p.d);
+    const int rowp = row0;   // the key-moment and probe passes start where the short rows end
     const float sl2 = static_cast<float>(LOG2E / p.h);
     const auto* q = static_cast<const uint16_t*>(p.q);
     const auto* k = static_cast<const uint16_t*>(p.k);
@@ -1842,11 +1809,11 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
     ra.sl2 = sl2; ra.lambda = static_cast<float>(p.lambda);
     ra.inv_h = 1.0 / p.h; ra.lambda_d = p.lambda;
     ra.n_short = BH * ((row0 + S_ROWS - 1) / S_ROWS);
-    ra.n_mom = rowp > row0 ? BH * ((rowp - row0 + B_WAVES - 1) / B_WAVES) : 0;
     const int n_key = n > rowp ? BH * ((n - rowp + K_BQ - 1) / K_BQ) : 0;
     ra.n_key = n_key;
     hipError_t err;
     const unsigned char* kimg_c = nullptr;
+    const unsigned char* kuimg_c = nullptr;
     if (n > row0) {
         const FastLayout L = fast_layout(BH, n, p.d);
         unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -1860,6 +1827,8 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
         ra.yhl = reinterpret_cast<_Float16*>(ws + L.yhl);
         ra.qsc = reinterpret_cast<float*>(ws + L.qsc);
         ra.guard = reinterpret_cast<unsigned*>(ws + L.guard);
+        ra.chk = reinterpret_cast<float*>(ws + L.chk);
+        kuimg_c = ws + L.kuimg;
         ra.list = reinterpret_cast<int*>(ws + L.list);
         const int ptiles = (n + MT - 1) / MT;
         prof_begin(p.stream, "lla_anchor_kernel");
@@ -1869,7 +1838,7 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
         if ((err = hipGetLastError()) != hipSuccess) return err;
         prof_begin(p.stream, "lla_pack_kernel");
         lla_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(
-            k, v, partial, anchors, packed, kimg, ra.guard, n, ptiles);
+            k, v, partial, anchors, packed, kimg, ws + L.kuimg, ra.guard, n, ptiles);
         prof_end(p.stream);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         const unsigned blocks_a = static_cast<unsigned>(BH) * ((n - row0 + R_QB - 1) / R_QB);
@@ -1879,21 +1848,25 @@ hipError_t launch_fast(const Problem& p, void* workspace) {
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     prof_begin(p.stream, "lla_rows_kernel");
-    lla_rows_kernel<<<dim3(static_cast<unsigned>(ra.n_short + ra.n_mom + n_key)), dim3(256), R_SMEM, p.stream>>>(ra);
+    lla_rows_kernel<<<dim3(static_cast<unsigned>(ra.n_short + n_key)), dim3(256), R_SMEM, p.stream>>>(ra);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (n_key > 0) {
         const unsigned blocks_p = static_cast<unsigned>(BH) * ((n - rowp + P_QB - 1) / P_QB);
         prof_begin(p.stream, "lla_probe_kernel");
         lla_probe_kernel<<<dim3(blocks_p), dim3(P_WAVES * 64), P_SMEM, p.stream>>>(
-            q, ra.mrow, ra.anchors, ra.packed, kimg_c, ra.yhl, ra.qsc, p.out, ra.guard, ra.list, n, row0, rowp, BH,
-            sl2);
+            q, ra.mrow, ra.anchors, ra.packed, kimg_c, kuimg_c, ra.yhl, ra.qsc, ra.chk, p.out, ra.guard, ra.list, n,
+            row0, rowp, BH, sl2);
         prof_end(p.stream);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
-    if (n > row0) {   // rows handed back by the range and finiteness checks, in fp64
+    if (n > row0) {   // rows handed back by the range guard and the checks, in fp64
         const int cap = BH * (n - row0);
-        return launch_exact_list(p, ra.list, reinterpret_cast<const int*>(ra.guard), cap < 2048 ? cap : 2048);
+        const int waves = cap < 4096 ? cap : 4096;
+        prof_begin(p.stream, "lla_refine_kernel");
+        lla_refine_kernel<<<dim3(static_cast<unsigned>((waves + RF_WAVES - 1) / RF_WAVES)), dim3(RF_WAVES * 64), 0,
+                            p.stream>>>(q, k, v, p.out, ra.list, ra.guard, n, 1.0 / p.h, p.lambda);
+        prof_end(p.stream);
     }
     return hipGetLastError();
 }

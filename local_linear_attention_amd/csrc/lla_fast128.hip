@@ -49,6 +49,11 @@ constexpr int F_BYTES = D8 * F_LD * 2;       // one tile of K (or V) feature-maj
 constexpr int K_LD = D8 + 8;                 // key-major row: 128 features + 8 halves padding (272 B)
 constexpr int KM_BYTES = T8 * K_LD * 2;      // one tile key-major: 17 KiB
 constexpr int KM_STRIDE8 = 2 * KM_BYTES;     // workspace: bf16 keys as given, then fp16 centred keys
+// Check image of a tile: projections of the centred keys on the Walsh functions of index
+// 4t + 1 (fp16, [direction][key] rows of F_LD halves), then |v - a_v|^2 per key (fp32).
+constexpr int KU8_NRM = NCHK * F_LD * 2;
+static_assert(KU8_NRM + T8 * 4 <= KU_TILE_BYTES, "check image layout");
+__device__ __forceinline__ constexpr int chk8_mask(int t) { return 4 * t + 1; }
 constexpr int A8_SLICES = 16;                // key slices of the anchor sums
 static_assert(F_BYTES % 1024 == 0 && KM_BYTES % 1024 == 0, "tile images are whole wave copies");
 
@@ -110,8 +115,11 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
                                                         unsigned char* __restrict__ kf,
                                                         unsigned char* __restrict__ vf,
                                                         unsigned char* __restrict__ km,
+                                                        unsigned char* __restrict__ kuf,
                                                         unsigned* __restrict__ guard, int n, int ntiles) {
     __shared__ float anc[2 * D8];
+    __shared__ float kst[T8][D8 + 1];   // centred fp16 keys of the tile, as floats
+    __shared__ float vpart[8][T8];      // |v - a_v|^2 over each thread's 16 features
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
     const int tid = threadIdx.x;
     {
@@ -130,6 +138,7 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
     uint32_t* kft = reinterpret_cast<uint32_t*>(kf + tile * F_BYTES);
     uint32_t* vft = reinterpret_cast<uint32_t*>(vf + tile * F_BYTES);
     float mk = 0.0f, mv = 0.0f;   // the largest centred magnitudes, for the range guard
+    float vsa = 0.0f, vsb = 0.0f;  // |v - a_v|^2 of keys 2p, 2p+1 over this thread's features
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int fg = (tid >> 5) + 8 * it;   // features 8 fg .. 8 fg + 7
@@ -175,6 +184,10 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int f = 8 * fg + e;
+            kst[2 * pr][f] = static_cast<float>(ca[e]);
+            kst[2 * pr + 1][f] = static_cast<float>(cb[e]);
+            vsa = fmaf(static_cast<float>(va[e]), static_cast<float>(va[e]), vsa);
+            vsb = fmaf(static_cast<float>(vb[e]), static_cast<float>(vb[e]), vsb);
             const h16x2 kk = {ca[e], cb[e]}, vv = {va[e], vb[e]};
             kft[f * (F_LD / 2) + pr] = __builtin_bit_cast(uint32_t, kk);
             vft[f * (F_LD / 2) + pr] = __builtin_bit_cast(uint32_t, vv);
@@ -186,6 +199,38 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
     }
     wave_atomic_max(guard + 1 + 2 * bh, mk);
     wave_atomic_max(guard + 2 + 2 * bh, mv);
+    vpart[tid >> 5][2 * pr] = vsa;
+    vpart[tid >> 5][2 * pr + 1] = vsb;
+    __syncthreads();
+    // Check image: thread j < 64 takes key j through a 128-point Walsh-Hadamard transform
+    // (X[m] = sum_f (-1)^popcount(f & m) x_f) and keeps the coefficients m = 4t + 1.
+    unsigned char* kut = kuf + tile * KU_TILE_BYTES;
+    if (tid < T8) {
+        float x[D8];
+#pragma unroll
+        for (int f = 0; f < D8; ++f) x[f] = kst[tid][f];
+#pragma unroll
+        for (int hh = 1; hh < D8; hh <<= 1)
+#pragma unroll
+            for (int i = 0; i < D8; i += 2 * hh)
+#pragma unroll
+                for (int e = i; e < i + hh; ++e) {
+                    const float a0 = x[e], a1 = x[e + hh];
+                    x[e] = a0 + a1;
+                    x[e + hh] = a0 - a1;
+                }
+        _Float16* kur = reinterpret_cast<_Float16*>(kut);
+#pragma unroll
+        for (int tq = 0; tq < NCHK; ++tq) kur[tq * F_LD + tid] = static_cast<_Float16>(x[chk8_mask(tq)]);
+        float nv = 0.0f;
+#pragma unroll
+        for (int f8 = 0; f8 < 8; ++f8) nv += vpart[f8][tid];
+        reinterpret_cast<float*>(kut + KU8_NRM)[tid] = nv;
+    } else if (tid < T8 + NCHK) {   // row padding of the projections
+        *reinterpret_cast<uint4*>(kut + (tid - T8) * F_LD * 2 + T8 * 2) = make_uint4(0, 0, 0, 0);
+    } else if (tid < T8 + NCHK + 16) {   // tail after the norms
+        *reinterpret_cast<uint4*>(kut + KU8_NRM + T8 * 4 + (tid - T8 - NCHK) * 16) = make_uint4(0, 0, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -331,7 +376,9 @@ constexpr int K8_MEAN_OFF = K8_RING > K8_SOLVE_BYTES ? K8_RING : K8_SOLVE_BYTES;
 constexpr int K8_SMEM = K8_MEAN_OFF + (K8_BQ * D8 + 4 * 16) * 4;
 static_assert(K8_SMEM <= 160 * 1024, "one block per CU");
 constexpr int P8_YLD = 2 * D8;                        // per query: yh hi (fp16) | yh lo (fp16)
-constexpr int P8_QSC = 4;                             // per query: gamma, 2^-e, 1/omega', dropped-pivot flag
+constexpr int P8_QSC = 8;                             // per query: gamma, 2^-e, 1/omega', dropped-pivot flag,
+                                                      // weighted mean |k - a|^2, 3 unused
+constexpr int P8_CHK = NCHK;                          // per query: the check's target (below)
 static_assert(K8_BUF % 16 == 0 && K8_SRING % 16 == 0 && K8_MEAN_OFF % 16 == 0, "LDS areas stay 16-byte aligned");
 static_assert(K8_BQ <= 16, "score MFMA has 16 query columns");
 
@@ -347,6 +394,12 @@ __device__ __forceinline__ float wave_sum8(float x) {
     x += dpp8<0x141>(x);   // row_half_mirror
     x += dpp8<0x140>(x);   // row_mirror
     return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+__device__ __forceinline__ float row_sum8(float x) {   // over each row of 16 lanes
+    x += dpp8<0xB1>(x);
+    x += dpp8<0x4E>(x);
+    x += dpp8<0x141>(x);
+    return x + dpp8<0x140>(x);
 }
 __device__ __forceinline__ float wave_max8(float x) {
     x = fmaxf(x, dpp8<0xB1>(x));
@@ -527,8 +580,8 @@ __device__ __forceinline__ void solve8(float4v (&ckk)[36], float (&z)[2], const 
 __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
     const unsigned char* __restrict__ kf, const unsigned char* __restrict__ km, _Float16* __restrict__ yhl,
-    float* __restrict__ qsc, const unsigned* __restrict__ guard, int n, int row0, int BH, float sl2,
-    float lambda) {
+    float* __restrict__ qsc, float* __restrict__ chk, const unsigned* __restrict__ guard, int n, int row0,
+    int BH, float sl2, float lambda) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -745,9 +798,39 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
                 }
         thr = 1e-6f * wave_max8(dmax);
     }
+    // The check's key scale: trace of sum R R^T (before the downdate) / omega'.
+    float tr = 0.0f;
+#pragma unroll
+    for (int I = 0; I < 8; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tr += 4 * g + r == c ? ckk[ub8(I, I)][r] : 0.0f;
+    tr = wave_sum8(tr);
     float yd[8];
     float dropped = 0.0f;
     solve8(ckk, z, thr, lam, iom2, skq, Sg, yd, dropped, lane, g, c);
+    // Check target: the LLA weights applied to the centred keys give q - a + lambda e^{-m} y
+    // (for the y they were formed with); its projections on directions t = 8 g + tt, the
+    // sign of feature f = 16 J + c being (-1)^popcount(f & (4t + 1)).
+    float cv[8];
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+        const int a = 16 * J + c;
+        cv[J] = bf16_bits_to_f32(q[base + static_cast<int64_t>(iqc) * D8 + a]) - anc[a] + lam * yd[J];
+    }
+    float chk_c = 0.0f;   // direction 8 g + c, for lanes c < 8
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const int ml = chk8_mask(tt) & 15, mh = 2 * g + (tt >= 4 ? 1 : 0);   // bits of 4 (8g + tt) + 1
+        const bool sl = (__builtin_popcount(c & ml) & 1) != 0;
+        float part = 0.0f;
+#pragma unroll
+        for (int J = 0; J < 8; ++J) {
+            const bool sj = (__builtin_popcount(J & mh) & 1) != 0;
+            part += (sl != sj) ? -cv[J] : cv[J];
+        }
+        const float sum = row_sum8(part);
+        chk_c = c == tt ? sum : chk_c;
+    }
     LDS_FENCE();
     // yh 2^e with max |.| in [2^13, 2^14), as fp16 hi + lo (about 22 bits together), and
     // gamma = 1 + S_k . yh / omega'.  Lane (g, c) holds rows 16 J + c; lanes g = 0 store.
@@ -777,10 +860,13 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
             yhl[qrow * P8_YLD + D8 + 16 * J + c] = lo[J];
         }
         // qsc[3] flags a pivot dropped although the ridge keeps the system positive definite.
-        if (c == 0)
+        if (c == 0) {
             *reinterpret_cast<float4v*>(qsc + qrow * P8_QSC) =
                 float4v{fmaf(dot / sig, iom2, 1.0f), 1.0f / sig, iom2, lambda > 0.0f ? dropped : 0.0f};
+            *reinterpret_cast<float4v*>(qsc + qrow * P8_QSC + 4) = float4v{tr * iom2, 0.0f, 0.0f, 0.0f};
+        }
     }
+    if (iq < n && c < 8) chk[(static_cast<int64_t>(bh) * prows + (iq - row0)) * P8_CHK + 8 * g + c] = chk_c;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -794,17 +880,18 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
 // register r holds key 16 kb + 4 g + r of query c, already the A operand of O += P (V - a_v)
 // over 32-key steps.
 constexpr int P8_SETS = 2, P8_QW = 16 * P8_SETS, P8_QB = NW8 * P8_QW;
-constexpr int P8_BUF = KM_STRIDE8 + F_BYTES;           // bf16 K | fp16 K - a | fp16 V - a_v
-constexpr int P8_LOADS = P8_BUF / 1024;                // 52
-constexpr int P8_WLOADS = (P8_LOADS + NW8 - 1) / NW8;  // 13
+constexpr int P8_BUF = KM_STRIDE8 + F_BYTES + KU_TILE_BYTES;   // bf16 K | fp16 K - a | fp16 V - a_v | check image
+constexpr int P8_LOADS = P8_BUF / 1024;                // 57
+constexpr int P8_WLOADS = (P8_LOADS + NW8 - 1) / NW8;  // 15 (the surplus repeat the last chunk)
 constexpr int P8_SMEM = 2 * P8_BUF;
-static_assert(P8_LOADS == NW8 * P8_WLOADS, "every wave copies the same number of chunks");
+
 
 __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ mrow, const float* __restrict__ anchors,
     const unsigned char* __restrict__ km, const unsigned char* __restrict__ vf,
-    const _Float16* __restrict__ yhl, const float* __restrict__ qsc, float* __restrict__ out,
-    unsigned* __restrict__ guard, int* __restrict__ list, int n, int row0, int BH, float sl2) {
+    const unsigned char* __restrict__ kuf, const _Float16* __restrict__ yhl, const float* __restrict__ qsc,
+    const float* __restrict__ chk, float* __restrict__ out, unsigned* __restrict__ guard, int* __restrict__ list,
+    int n, int row0, int BH, float sl2) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -855,21 +942,27 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
     const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(uniform_ptr(vf + static_cast<int64_t>(bh) * ptiles * F_BYTES)), 0,
         ptiles * F_BYTES, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ures = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(uniform_ptr(kuf + static_cast<int64_t>(bh) * ptiles * KU_TILE_BYTES)), 0,
+        ptiles * KU_TILE_BYTES, 0x00020000);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-    // Chunk u of a buffer: u < 34 from the key-major images, else from the value image.
-    // Wave w issues chunks w, w + 4, ..., w + 48.
+    // Chunk u of a buffer: u < 34 from the key-major images, u < 52 from the value image, the
+    // rest from the check image.  Wave w issues chunks w, w + 4, ... (clamped to the last).
+    constexpr int U_KM = KM_STRIDE8 / 1024, U_V = U_KM + F_BYTES / 1024;
     auto issue = [&](int tt) {
         const int ts = min(tt, ntiles - 1);
         const uint32_t dst = lds0 + static_cast<uint32_t>((tt % 2) * P8_BUF);
 #pragma unroll
         for (int e = 0; e < P8_WLOADS; ++e) {
-            const int u = wu + NW8 * e;
+            const int u = min(wu + NW8 * e, P8_LOADS - 1);
             auto* ldst = reinterpret_cast<__attribute__((address_space(3))) void*>(static_cast<uintptr_t>(dst + u * 1024));
-            if (u < KM_STRIDE8 / 1024)
+            if (u < U_KM)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, ldst, 16, lane * 16 + u * 1024, ts * KM_STRIDE8, 0, 0);
+            else if (u < U_V)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, ldst, 16, lane * 16 + (u - U_KM) * 1024, ts * F_BYTES, 0, 0);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, ldst, 16, lane * 16 + (u - KM_STRIDE8 / 1024) * 1024,
-                                                         ts * F_BYTES, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ures, ldst, 16, lane * 16 + (u - U_V) * 1024,
+                                                         ts * KU_TILE_BYTES, 0, 0);
         }
     };
     // The copies of the next tile have landed (all loads waited for) and every wave is done
@@ -881,11 +974,16 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
         LDS_FENCE();
     };
 
-    float4v o[P8_SETS][8];
+    float4v o[P8_SETS][8], ok[P8_SETS][NCHK / 16];
+    float wvn[P8_SETS];   // sum w |v - a_v|^2 of query c over this lane's keys
 #pragma unroll
-    for (int st = 0; st < P8_SETS; ++st)
+    for (int st = 0; st < P8_SETS; ++st) {
 #pragma unroll
         for (int fv = 0; fv < 8; ++fv) o[st][fv] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < NCHK / 16; ++db) ok[st][db] = float4v{0.f, 0.f, 0.f, 0.f};
+        wvn[st] = 0.0f;
+    }
     issue(0);
     wait_and_sync();
     auto tile_step = [&](const int t, auto phase) {
@@ -896,6 +994,8 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
             const unsigned char* KB = cur;
             const unsigned char* KC = cur + KM_BYTES;
             const _Float16* VI = reinterpret_cast<const _Float16*>(cur + KM_STRIDE8);
+            const _Float16* UI = reinterpret_cast<const _Float16*>(cur + KM_STRIDE8 + F_BYTES);
+            const float* NR = reinterpret_cast<const float*>(cur + KM_STRIDE8 + F_BYTES + KU8_NRM);
             half4 p[P8_SETS][4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -925,7 +1025,11 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
                         sw4[r] = static_cast<_Float16>(e);
                         t4[r] = static_cast<_Float16>(fmaf(-u[r], isig[st], gam[st]));
                     }
-                    p[st][kb] = (sw4 * sw4) * t4;   // w = fp16(sw^2) as in the key-moment kernel, then fp16(w t)
+                    const half4 w4 = sw4 * sw4;   // w = fp16(sw^2) as in the key-moment kernel
+                    p[st][kb] = w4 * t4;          // then fp16(w t)
+                    const float4v nr = *reinterpret_cast<const float4v*>(NR + kb * 16 + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) wvn[st] = fmaf(static_cast<float>(w4[r]), nr[r], wvn[st]);
                 }
             }
 #pragma unroll
@@ -942,6 +1046,18 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
                         o[st][fv] = mfma_f16(pa, vb, o[st][fv]);
                     }
                 }
+#pragma unroll
+                for (int db = 0; db < NCHK / 16; ++db) {
+                    const _Float16* ur = UI + (db * 16 + c) * F_LD + 32 * ks + 4 * g;
+                    const half4 u0 = *reinterpret_cast<const half4*>(ur);
+                    const half4 u1 = *reinterpret_cast<const half4*>(ur + 16);
+                    const half8 ub = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int st = 0; st < P8_SETS; ++st) {
+                        const half8 pa = __builtin_shufflevector(p[st][2 * ks], p[st][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                        ok[st][db] = mfma_f16(pa, ub, ok[st][db]);
+                    }
+                }
             }
         };
         if constexpr (!decltype(phase)::value) tile_body(std::false_type{});
@@ -955,31 +1071,44 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
     for (int t = tfull; t < ntiles; ++t) tile_step(t, std::true_type{});
     __builtin_amdgcn_s_waitcnt(0x0 | (0x7 << 4) | (0xF << 8));   // copies past the last tile
 
-    // Output rows: lane (g, c) register r of set st = query qw0 + 16 st + 4 g + r, feature 16 fv + c.
-    // A row whose output is not finite, or whose solve dropped a pivot (qsc[3]), goes to the
-    // fp64 kernel.
+    // Output rows: lane (g, c) register r of set st = query qw0 + 16 st + 4 g + r, feature 16 fv + c
+    // (direction 16 db + c of the check sums).  A row goes to the fp64 kernel if its output is
+    // not finite, its solve dropped a pivot (qsc[3]), or its check exceeds CHK_TOL: the
+    // projected deviation of sum_j P_ij (k_j - a) / omega' from q - a + lambda e^{-m} y, in
+    // units of the weighted rms |k - a|, times the weighted rms |v - a_v| over |b|.
     const float* anc = anchors + static_cast<int64_t>(bh) * 2 * D8 + D8;
 #pragma unroll
-    for (int st = 0; st < P8_SETS; ++st)
+    for (int st = 0; st < P8_SETS; ++st) {
+        float vq = wvn[st];   // sum_j w_j |v_j - a_v|^2 of query c, then of query 4 g + r below
+        vq += __shfl_xor(vq, 16);
+        vq += __shfl_xor(vq, 32);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = qw0 + 16 * st + 4 * g + r;
-            bool bad = false;
-            if (i < n) {
-                const float4v sc =
-                    *reinterpret_cast<const float4v*>(qsc + (static_cast<int64_t>(bh) * prows + (i - row0)) * P8_QSC);
-                float* orow = out + base + static_cast<int64_t>(i) * D8;
+            const int64_t qrow = static_cast<int64_t>(bh) * prows + (min(i, n - 1) - row0);
+            const float4v sc = *reinterpret_cast<const float4v*>(qsc + qrow * P8_QSC);
+            const float kn2 = qsc[qrow * P8_QSC + 4];
+            float bb = 0.0f, rr = 0.0f;
 #pragma unroll
-                for (int fv = 0; fv < 8; ++fv) {
-                    const float ov = fmaf(o[st][fv][r], sc[2], anc[fv * 16 + c]);
-                    bad = bad || !isfinite(ov);
-                    orow[fv * 16 + c] = ov;
-                }
-                bad = bad || sc[3] != 0.0f;
+            for (int fv = 0; fv < 8; ++fv) {
+                const float ov = fmaf(o[st][fv][r], sc[2], anc[fv * 16 + c]);
+                bb = fmaf(ov, ov, bb);
+                if (i < n) out[base + static_cast<int64_t>(i) * D8 + fv * 16 + c] = ov;
             }
+#pragma unroll
+            for (int db = 0; db < NCHK / 16; ++db) {
+                const float dv = fmaf(ok[st][db][r], sc[2], -chk[qrow * P8_CHK + 16 * db + c]);
+                rr = fmaf(dv, dv, rr);
+            }
+            bb = row_sum8(bb);
+            rr = row_sum8(rr);
+            const float vn2 = __shfl(vq, 4 * g + r) * sc[2];
+            const float est2 = (rr * (1.0f / NCHK)) * vn2 / (kn2 * bb);
+            const bool bad = i < n && (!(est2 <= CHK_TOL * CHK_TOL) || sc[3] != 0.0f);
             const uint64_t badm = __ballot(bad);   // every lane takes part
             if (c == 0 && i < n && ((badm >> (16 * g)) & 0xFFFFull) != 0) hand_back(guard, list, bh, n, i);
         }
+    }
 }
 
 // Rows [0, 4d): the fp64 kernel; rows [4d, n): this path.
@@ -987,12 +1116,13 @@ int fast8_row0(int64_t n) { return static_cast<int>(n < 4 * D8 ? n : 4 * D8); }
 
 // Workspace, each region 256-byte aligned: row maxima [B*H][n - 4d] | anchor partial sums
 // [B*H][16][2d] | anchors [B*H][2d] | K feature-major images [B*H][tiles] | V feature-major
-// images [B*H][tiles] | key-major images (bf16, centred fp16) [B*H][tiles] | probe solutions
-// (fp16 hi, lo) [B*H][n - 4d][2d] | probe scalars [B*H][n - 4d][4] | guard: count of rows
-// handed back, then per head the largest |k - a| and |v - a_v| (float bits) [1 + 2 B*H] |
-// rows handed back [B*H][n - 4d].
+// images [B*H][tiles] | key-major images (bf16, centred fp16) [B*H][tiles] | check images
+// [B*H][tiles] | probe solutions (fp16 hi, lo) [B*H][n - 4d][2d] | probe scalars
+// [B*H][n - 4d][8] | check targets [B*H][n - 4d][32] | guard: count of rows handed back,
+// then per head the largest |k - a| and |v - a_v| (float bits) [1 + 2 B*H] | rows handed
+// back [B*H][n - 4d].
 struct Fast8Layout {
-    int64_t mrow, partial, anchors, kf, vf, km, yhl, qsc, guard, list, total;
+    int64_t mrow, partial, anchors, kf, vf, km, kuf, yhl, qsc, chk, guard, list, total;
 };
 
 Fast8Layout fast8_layout(int64_t BH, int64_t n) {
@@ -1005,9 +1135,11 @@ Fast8Layout fast8_layout(int64_t BH, int64_t n) {
     L.kf = L.anchors + up(BH * 2 * D8 * 4);
     L.vf = L.kf + BH * tiles * F_BYTES;
     L.km = L.vf + BH * tiles * F_BYTES;
-    L.yhl = L.km + BH * tiles * KM_STRIDE8;
+    L.kuf = L.km + BH * tiles * KM_STRIDE8;
+    L.yhl = L.kuf + BH * tiles * KU_TILE_BYTES;
     L.qsc = L.yhl + up(BH * prows * P8_YLD * 2);
-    L.guard = L.qsc + up(BH * prows * P8_QSC * 4);
+    L.chk = L.qsc + up(BH * prows * P8_QSC * 4);
+    L.guard = L.chk + up(BH * prows * P8_CHK * 4);
     L.list = L.guard + up((1 + 2 * BH) * 4);
     L.total = L.list + up(BH * prows * 4);
     return L;
@@ -1041,6 +1173,11 @@ size_t fast128_workspace_bytes(int64_t B, int64_t H, int64_t n) {
     return static_cast<size_t>(fast8_layout(B * H, n).total);
 }
 
+int64_t fast128_fallback_count_offset(int64_t B, int64_t H, int64_t n) {
+    if (n - fast8_row0(n) <= 0) return -1;
+    return fast8_layout(B * H, n).guard;
+}
+
 hipError_t launch_fast128(const Problem& p, void* workspace) {
     hipError_t err;
     const int n = static_cast<int>(p.n);
@@ -1063,6 +1200,8 @@ hipError_t launch_fast128(const Problem& p, void* workspace) {
     unsigned char* km = ws + L.km;
     _Float16* yhl = reinterpret_cast<_Float16*>(ws + L.yhl);
     float* qsc = reinterpret_cast<float*>(ws + L.qsc);
+    float* chk = reinterpret_cast<float*>(ws + L.chk);
+    unsigned char* kuf = ws + L.kuf;
     unsigned* guard = reinterpret_cast<unsigned*>(ws + L.guard);
     int* list = reinterpret_cast<int*>(ws + L.list);
     const int ptiles = (n + T8 - 1) / T8;
@@ -1074,7 +1213,8 @@ hipError_t launch_fast128(const Problem& p, void* workspace) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_pack_kernel");
     lla8_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(k, v, partial, anchors, kf,
-                                                                                           vf, km, guard, n, ptiles);
+                                                                                           vf, km, kuf, guard, n,
+                                                                                           ptiles);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_rowmax_kernel");
@@ -1084,13 +1224,14 @@ hipError_t launch_fast128(const Problem& p, void* workspace) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_keymom_kernel");
     lla8_keymom_kernel<<<dim3(static_cast<unsigned>(BH) * ((prows + K8_BQ - 1) / K8_BQ)), dim3(KW8 * 64), K8_SMEM,
-                         p.stream>>>(q, mrow, anchors, kf, km, yhl, qsc, guard, n, row0, BH, sl2,
+                         p.stream>>>(q, mrow, anchors, kf, km, yhl, qsc, chk, guard, n, row0, BH, sl2,
                                      static_cast<float>(p.lambda));
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     prof_begin(p.stream, "lla8_probe_kernel");
     lla8_probe_kernel<<<dim3(static_cast<unsigned>(BH) * ((prows + P8_QB - 1) / P8_QB)), dim3(256), P8_SMEM,
-                        p.stream>>>(q, mrow, anchors, km, vf, yhl, qsc, p.out, guard, list, n, row0, BH, sl2);
+                        p.stream>>>(q, mrow, anchors, km, vf, kuf, yhl, qsc, chk, p.out, guard, list, n, row0, BH,
+                                    sl2);
     prof_end(p.stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // Rows handed back by the range and finiteness checks, in fp64.

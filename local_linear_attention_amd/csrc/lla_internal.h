@@ -51,6 +51,10 @@ size_t fast_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
 hipError_t launch_fast(const Problem& p, void* workspace);
 size_t fast128_workspace_bytes(int64_t B, int64_t H, int64_t n);
 hipError_t launch_fast128(const Problem& p, void* workspace);
+// Byte offset, within that workspace, of the count (32-bit unsigned) of rows the path's
+// checks handed to the fp64 kernel on its last use; -1 when the problem needs no workspace.
+int64_t fast_fallback_count_offset(int64_t B, int64_t H, int64_t n, int64_t d);
+int64_t fast128_fallback_count_offset(int64_t B, int64_t H, int64_t n);
 
 // Parallax forward with a given probe.  Fast path: bf16, d = 64, n up to kFastMaxN, with
 // tile images and per-tile key statistics in `workspace` (parallax_workspace_bytes);

@@ -12,6 +12,7 @@ import os
 
 __all__ = ["lla_forward", "lla_forward_ex", "lla_forward_ws", "lla_workspace_size",
            "lla_forward_workspace_bytes", "lla_pool_trim", "lla_forward_noalloc",
+           "lla_forward_fallback_rows",
            "lla_path_available", "lla_parallax_forward", "lla_parallax_forward_ex",
            "lla_parallax_forward_ws", "lla_parallax_workspace_size", "lla_parallax_path_available",
            "lla_parallax_decode", "lla_parallax_decode_ws", "lla_parallax_decode_workspace_size",
@@ -71,6 +72,9 @@ def load_library():
     lib.lla_forward_noalloc.restype = ctypes.c_int
     lib.lla_pool_trim.argtypes = []
     lib.lla_pool_trim.restype = ctypes.c_int
+    lib.lla_forward_fallback_rows.argtypes = [vp, ctypes.c_size_t, i64, i64, i64, i64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.POINTER(i64), vp]
+    lib.lla_forward_fallback_rows.restype = ctypes.c_int
     lib.lla_forward_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f64, f64, ctypes.c_int,
                                    vp, ctypes.c_int, vp, ctypes.c_size_t]
     lib.lla_forward_ws.restype = ctypes.c_int
@@ -246,6 +250,27 @@ def lla_forward_ws(q, k, v, h: float, lam: float, workspace, path: str = "auto",
     if st != 0:
         raise LLAError(st, "lla_forward_ws")
     return out
+
+
+def lla_forward_fallback_rows(workspace, shape, dtype: str, path: str = "auto", stream=None) -> int:
+    """Rows that the matrix-core path of the last lla_forward_ws call on `workspace` (a device
+    tensor; problem `shape` = (B, H, n, d), input dtype "bf16" or "f32") recomputed on the
+    fp64 kernel.  Waits for `stream` (default: the current stream)."""
+    import torch
+    B, H, n, d = (int(x) for x in shape)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if workspace is None:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rows = ctypes.c_int64(0)
+    st = load_library().lla_forward_fallback_rows(ctypes.c_void_p(ws_ptr) if ws_ptr else None, ws_bytes,
+                                                  B, H, n, d, DTYPES[dtype], PATHS[path], ctypes.byref(rows),
+                                                  ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise LLAError(st, "lla_forward_fallback_rows")
+    return rows.value
 
 
 def _marshal_probe(q, rho):

@@ -89,15 +89,52 @@ def workload_arrays(name, **shape):
     return w, q, k, v
 
 
+ENVELOPE_CASES = ("sharp_h", "q_x3", "rank16_keys", "v_2^-16", "v_2^17", "k_offset", "k_x64_h_x64")
+
+
+def envelope_case(name, case):
+    """Inputs outside the RMS-normalised, h = sqrt(d) regime of the pages' workloads, built
+    from workload `name` at a small shape (every value bf16-representable):
+    sharp_h: h / 2 (sharper weights); q_x3: queries x 3 (the same, through q); rank16_keys:
+    keys confined to a random 16-dimensional subspace, re-normalised; v_2^-16, v_2^17:
+    values scaled out of fp16's normal range either way; k_offset: keys + 4 (a common
+    offset); k_x64_h_x64: keys x 64 with h x 64 (the same weights, large keys)."""
+    import lla_inputs
+    shape = dict(B=1, H=2, n=700) if lla_inputs.WORKLOADS[name].d == 128 else dict(B=1, H=2, n=600)
+    w, q, k, v = workload_arrays(name, **shape)
+    r = lla_inputs.round_to_bf16
+    h, lam = w.h, w.lam
+    if case == "sharp_h":
+        h = w.h / 2
+    elif case == "q_x3":
+        q = r(q * 3.0)
+    elif case == "rank16_keys":
+        rng = np.random.default_rng(16)
+        basis = np.linalg.qr(rng.standard_normal((w.d, 16)))[0]
+        kk = k @ basis @ basis.T
+        k = r(kk / np.sqrt(np.mean(kk ** 2, axis=-1, keepdims=True)))
+    elif case == "v_2^-16":
+        v = r(v * 2.0 ** -16)
+    elif case == "v_2^17":
+        v = r(v * 2.0 ** 17)
+    elif case == "k_offset":
+        k = r(k + 4.0)
+    elif case == "k_x64_h_x64":
+        k, h = r(k * 64.0), w.h * 64.0
+    else:
+        raise KeyError(case)
+    return w, q, k, v, h, lam
+
+
 def fast_workspace_bytes(BH, n, d=64):
     """Scratch bytes of the bf16 matrix-core path, region by region (each rounded up to
     256 B where the library rounds it).
 
     d = 64: row maxima of rows >= 2d, anchor partial sums, anchors, then per head and 64-key
-    tile the fp16 K/V image (72-half rows) and the two key-major key images (bf16, centred
-    fp16), then per probe row (rows >= 4d) the fp16 hi/lo solution and four scalars, the
-    guard words (count of rows handed back, two maxima per head) and the hand-back list
-    (one slot per row >= 2d).
+    tile the fp16 K/V image (72-half rows), the two key-major key images (bf16, centred
+    fp16) and the 5 KiB check image, then per row >= 2d the fp16 hi/lo solution, eight
+    scalars and 32 check targets, the guard words (count of rows handed back, two maxima per
+    head) and the hand-back list (one slot per row >= 2d).
 
     d = 128: the same regions for rows >= 4d, with the K and V feature-major images apart
     (72-half rows) and key-major rows of 136 halves."""
@@ -108,13 +145,13 @@ def fast_workspace_bytes(BH, n, d=64):
         if prows <= 0:
             return 0
         return (up(BH * prows * 4) + up(BH * 16 * 2 * d * 4) + up(BH * 2 * d * 4)
-                + BH * tiles * (2 * d * 72 * 2 + 2 * 64 * 136 * 2)
-                + up(BH * prows * 2 * d * 2) + up(BH * prows * 4 * 4)
+                + BH * tiles * (2 * d * 72 * 2 + 2 * 64 * 136 * 2 + 5 * 1024)
+                + up(BH * prows * 2 * d * 2) + up(BH * prows * 8 * 4) + up(BH * prows * 32 * 4)
                 + up((1 + 2 * BH) * 4) + up(BH * prows * 4))
-    prows = n - min(n, 4 * d)
-    if n - min(n, 2 * d) <= 0:
+    prows = n - min(n, 2 * d)
+    if prows <= 0:
         return 0
-    return (up(BH * (n - 2 * d) * 4) + up(BH * 16 * 2 * d * 4) + up(BH * 2 * d * 4)
-            + BH * tiles * (2 * d * 72 * 2 + 2 * 64 * 72 * 2)
-            + up(BH * prows * 2 * d * 2) + up(BH * prows * 4 * 4)
-            + up((1 + 2 * BH) * 4) + up(BH * (n - 2 * d) * 4))
+    return (up(BH * prows * 4) + up(BH * 16 * 2 * d * 4) + up(BH * 2 * d * 4)
+            + BH * tiles * (2 * d * 72 * 2 + 2 * 64 * 72 * 2 + 5 * 1024)
+            + up(BH * prows * 2 * d * 2) + up(BH * prows * 8 * 4) + up(BH * prows * 32 * 4)
+            + up((1 + 2 * BH) * 4) + up(BH * prows * 4))

@@ -32,7 +32,8 @@ def declared_enums():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["lla_decode", "lla_decode_workspace_size", "lla_decode_ws",
-                                    "lla_forward", "lla_forward_ex", "lla_forward_noalloc",
+                                    "lla_forward", "lla_forward_ex", "lla_forward_fallback_rows",
+                                    "lla_forward_noalloc",
                                     "lla_forward_workspace_bytes",
                                     "lla_forward_ws",
                                     "lla_parallax_backward", "lla_parallax_backward_workspace_size",
@@ -182,6 +183,28 @@ def test_forward_ws_rejects_overlapping_workspace():
     assert dbytes > 0
     assert lib.lla_decode_ws(ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V), ctypes.c_void_p(OUT),
                              1, 2, 4096, 64, 8.0, 0.01, 1, None, ctypes.c_void_p(K + 128), dbytes) == 7
+
+
+def test_fallback_rows_query_validation_before_any_copy():
+    # Every case returns before the library touches the device (no GPU here).
+    lib = _lib()
+    rows = ctypes.c_int64(-1)
+    ws = ctypes.c_void_p(0x7f0000000000)
+    def q(ws_ptr, nbytes, B=1, H=2, n=4096, d=64, dtype=1, path=0, out=ctypes.byref(rows)):
+        return lib.lla_forward_fallback_rows(ws_ptr, nbytes, B, H, n, d, dtype, path, out, None)
+    assert q(ws, 1 << 30, out=None) == 1                      # NULL result pointer
+    assert q(ws, 1 << 30, d=48) == 4                          # unsupported head dimension
+    assert q(ws, 1 << 30, B=0) == 2                           # bad shape
+    rows.value = -1
+    assert q(ws, 1 << 30, path=1) == 0 and rows.value == 0    # exact path: no workspace, no rows
+    rows.value = -1
+    assert q(ws, 1 << 30, dtype=0) == 0 and rows.value == 0   # fp32 resolves to the exact path
+    rows.value = -1
+    assert q(ws, 1 << 30, n=100) == 0 and rows.value == 0     # every row short: no workspace
+    assert q(None, 0) == 5                                     # fast path needs its workspace
+    from local_linear_attention_amd import lla
+    need = lla.lla_workspace_size(1, 2, 4096, 64, "bf16", "auto")
+    assert q(ws, need - 1) == 5
 
 
 def test_forward_ws_validation_before_launch():

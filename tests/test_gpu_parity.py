@@ -123,6 +123,29 @@ def test_fast_path_d128_extreme_ridge(lam):
           positions=np.arange(lo, w.n), d=w.d)
 
 
+@pytest.mark.parametrize("name", ["d24", "long"])
+@pytest.mark.parametrize("case", ["sharp_h", "q_x3", "rank16_keys", "v_2^-16", "v_2^17", "k_offset",
+                                  "k_x64_h_x64"])
+def test_default_path_envelope_every_row(name, case):
+    # Inputs outside the RMS-normalised regime: AUTO (the matrix-core path for bf16) must still
+    # hold the tolerance on every row, handing the rows its checks reject to the fp64 kernel.
+    torch = require_gpu()
+    from local_linear_attention_amd.lla import lla_forward_fallback_rows, lla_forward_workspace_bytes, lla_forward_ws
+    from parity_util import envelope_case, to_device
+    w, q, k, v, h, lam = envelope_case(name, case)
+    ref = oracle_all_rows(q, k, v, h, lam)
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    nbytes = lla_forward_workspace_bytes(w.B, w.H, w.n, w.d, "bf16")
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    got = lla_forward_ws(tq, tk, tv, h, lam, ws).cpu().numpy().astype(np.float64)
+    back = lla_forward_fallback_rows(ws, (w.B, w.H, w.n, w.d), "bf16")
+    err = row_errors(got, ref)
+    print(f"[envelope] {name} {case}: rows handed back {back} of {w.B * w.H * w.n}, "
+          f"max row err {np.max(err):.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert np.max(err) <= TOL["bf16"]
+
+
 def test_fast_path_workspace_entry_point_matches():
     torch = require_gpu()
     from local_linear_attention_amd import lla_forward_ex, lla_forward_ws, lla_workspace_size
@@ -155,7 +178,7 @@ def test_profiling_records_each_kernel():
     finally:
         lla_profile_enable(False)
     assert [name for name, _ in rec] == ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel",
-                                         "lla_rows_kernel", "lla_probe_kernel", "lla_exact_list_kernel"]
+                                         "lla_rows_kernel", "lla_probe_kernel", "lla_refine_kernel"]
     assert all(ms > 0 for _, ms in rec)
 
 
