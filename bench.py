@@ -57,7 +57,7 @@ def alg_flops(B, H, n, d, form):
 
 
 # Arithmetic of each path (the dtype field) and the bound of each kernel.
-PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 2d and rows the check hands back: f64)",
+PATH_ARITH = {"exact": "f64", "fast": "f16 MFMA / f32 accumulate (rows < 3d and rows the check hands back: f64)",
               "cg": "f64 (conjugate gradient over the prefix)"}
 KERNEL_BOUND = {
     "lla_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
@@ -136,9 +136,9 @@ def kernel_flops(name, B, H, n, d, path):
     recomputes, and the probe's check sums (a verification, not part of the estimator), are
     not counted."""
     BH = B * H
-    row0 = rowp = min(n, 2 * d) if path == "fast" else n
-    if path == "fast" and d == 128:   # rows < 4d exact (NS), the rest key moments + probe (min)
-        row0 = rowp = min(n, 4 * d)
+    # fp64 rows (NS): i < 3d at d = 64 (short-row blocks), i < 4d at d = 128 (fp64 kernel); the
+    # rest key moments + probe (min)
+    row0 = rowp = (min(n, 4 * d) if d == 128 else min(n, 3 * d)) if path == "fast" else n
     per_query = d ** 3 / 3 + 4 * d * d + 2 * d
     moments = 2 * (1 + 2 * d) + d * (d + 1)
     if name in ("lla_exact_kernel", "lla_short_kernel", "lla_cg_kernel"):
@@ -782,7 +782,7 @@ def main():
     else:
         config_text = (f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs, h={w.h:g}, "
                        f"lambda={w.lam:g}")
-        split = "4d" if w.d == 128 else "2d"
+        split = "4d" if w.d == 128 else "3d"
         flop_count = {"formulation": (f"NS for rows i < {split}, min (probe pass) for rows i >= {split}"
                                       if path == "fast" else "NS"),
                       "flops": flops,

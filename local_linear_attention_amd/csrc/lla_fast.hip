@@ -1,10 +1,11 @@
 // Matrix-core path of the causal LLA forward for bf16 inputs, head dimension 64.
 //
 // Work split (rows are query positions i of one head):
-//   * rows i < 2d run on the fp64 kernel: their prefixes hold at most 2d keys, so C_kk is
-//     rank-deficient or barely full rank and the ridge lambda e^{-m} alone conditions the
-//     solve -- the normal-equation form then needs more than fp16/fp32 precision;
-//   * rows i >= 2d run here:
+//   * rows i < 3d run in fp64 (the short-row blocks of lla_rows_kernel): their prefixes hold
+//     at most 3d keys, so C_kk is rank-deficient or poorly conditioned and the ridge
+//     lambda e^{-m} alone conditions the solve -- the normal-equation form then needs more
+//     than fp16/fp32 precision (rows just past 2d still reach about 2e-3 in fp16);
+//   * rows i >= 3d run here:
 //       lla_anchor_kernel   per-head sums of the keys and values of positions [0, 2d) (the
 //                           centring anchor a: every row of this path has them in its prefix);
 //       lla_pack_kernel     K, V once into fp16 tiles centred at a (the LDS image the
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
     }
 }
 
-// Score pass with a running max (rows i >= 2d): m_i = max_{j <= i} q_i.k_j / h, in log2
+// Score pass with a running max (rows i >= 3d): m_i = max_{j <= i} q_i.k_j / h, in log2
 // units.  Block = 4 waves x 2 sets of 16 queries (the sets share the key operands); 64-key
 // tiles of the key-major image stream through a ring of three LDS buffers (copied straight
 // from the workspace); scores on MFMA (bf16): S^T block kb of a tile, lane (g, c) register
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256) void lla_rowmax_kernel(const uint16_t* __restr
 __device__ __forceinline__ constexpr int ublk(int I, int J) { return I * 4 - I * (I - 1) / 2 + (J - I); }
 
 // ---------------------------------------------------------------------------------------
-// Rows i >= 2d: the cross moment C_vk is never formed.  Pass 1 (the key-moment blocks) builds
+// Rows i >= 3d: the cross moment C_vk is never formed.  Pass 1 (the key-moment blocks) builds
 // the key moments and solves for y; pass 2 (lla_probe_kernel) applies C_vk to y in one
 // attention-like sweep:
 //   b_i = vbar_i - C_vk y_i = a_v + (1/omega') sum_j w_ij t_ij (v_j - a_v),
@@ -1211,8 +1212,8 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Rows i < 2d of the bf16 path, in fp64: one wave per row, 4 consecutive rows per block
-// sharing the (at most 2d-key) prefix staged in LDS as bf16.
+// Rows i < 3d of the bf16 path, in fp64: one wave per row, 4 consecutive rows per block
+// sharing the (at most 3d-key) prefix staged in LDS as bf16.
 //   scores -> m, weights, omega; kbar, vbar (lane = feature);
 //   C_kk = R^T R with R[j] = sqrt(w_j) (k_j - kbar) in fp64 on the matrix cores
 //   (v_mfma_f64_16x16x4f64, 4 keys per step), ridge on the diagonal, then moved to
@@ -1221,7 +1222,8 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
 //   probe u_j = (k_j - kbar).y and b = vbar - sum_j w_j u_j (v_j - vbar)  (= vbar - C_vk y).
 // fp64 MFMA output layout: D[4 r + (l / 16)][l % 16] in double register r of lane l.
 constexpr int S_ROWS = 4;
-constexpr int S_KMAX = 2 * FD;
+constexpr int S_KMAX = 3 * FD;
+constexpr int S_KPL = S_KMAX / 64;   // keys per lane in the score and probe passes
 constexpr int S_KLD = FD + 2;   // bf16 row stride (halves): 33 words, conflict-free per row
 constexpr int S_TLD = FD + 1;   // fp64 row stride of the transposition buffer
 
@@ -1238,16 +1240,15 @@ __device__ __forceinline__ double wave_sum_d(double x) {
     return x;
 }
 
-// LDS of a short-row block: staged K, V (bf16), then per wave q, weights, kbar, the
-// pivot-column exchange (then y) and 16 rows of C_kk in transit (fp64).
+// LDS of a short-row block: staged K, V (bf16), then per wave q, weights, kbar, and 8 rows of
+// C_kk in transit (fp64), whose first FD entries then serve as the pivot-row exchange (then y).
 constexpr int SB_KS = 0;
 constexpr int SB_VS = SB_KS + S_KMAX * S_KLD * 2;
 constexpr int SB_QS = SB_VS + S_KMAX * S_KLD * 2;
 constexpr int SB_WS = SB_QS + S_ROWS * FD * 8;
 constexpr int SB_KBS = SB_WS + S_ROWS * S_KMAX * 8;
-constexpr int SB_XB = SB_KBS + S_ROWS * FD * 8;
-constexpr int SB_TB = SB_XB + S_ROWS * FD * 8;
-constexpr int S_SMEM = SB_TB + S_ROWS * 16 * S_TLD * 8;
+constexpr int SB_TB = SB_KBS + S_ROWS * FD * 8;
+constexpr int S_SMEM = SB_TB + S_ROWS * 8 * S_TLD * 8;
 static_assert(SB_QS % 16 == 0, "fp64 areas stay aligned");
 
 __device__ __forceinline__ void short_block(
@@ -1259,8 +1260,7 @@ __device__ __forceinline__ void short_block(
     double (*qs)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_QS);
     double (*ws)[S_KMAX] = reinterpret_cast<double (*)[S_KMAX]>(smem + SB_WS);
     double (*kbs)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_KBS);
-    double (*xb)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_XB);              // pivot-column exchange, then y
-    double (*tb)[16 * S_TLD] = reinterpret_cast<double (*)[16 * S_TLD]>(smem + SB_TB);   // 16 rows of C_kk in transit
+    double (*tb)[8 * S_TLD] = reinterpret_cast<double (*)[8 * S_TLD]>(smem + SB_TB);   // 8 rows of C_kk in transit
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c = lane & 15;
@@ -1286,10 +1286,11 @@ __device__ __forceinline__ void short_block(
     qs[w][lane] = static_cast<double>(bf16_bits_to_f32(q[base + static_cast<int64_t>(ic) * FD + lane]));
     __syncthreads();
 
-    // ---- scores of keys lane and lane + 64, running max, weights, omega
-    double s[2] = {-INFINITY, -INFINITY};
+    // ---- scores of keys lane + 64 h, running max, weights, omega
+    double s[S_KPL];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < S_KPL; ++h2) {
+        s[h2] = -INFINITY;
         const int j = lane + 64 * h2;
         if (j <= ic) {
             double acc = 0.0;
@@ -1298,14 +1299,18 @@ __device__ __forceinline__ void short_block(
             s[h2] = acc * inv_h;
         }
     }
-    const double m = wave_max_d(fmax(s[0], s[1]));
-    double wl[2];
+    double smax = s[0];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        wl[h2] = (lane + 64 * h2 <= ic) ? exp(s[h2] - m) : 0.0;
-        ws[w][lane + 64 * h2] = wl[h2];
+    for (int h2 = 1; h2 < S_KPL; ++h2) smax = fmax(smax, s[h2]);
+    const double m = wave_max_d(smax);
+    double wsum = 0.0;
+#pragma unroll
+    for (int h2 = 0; h2 < S_KPL; ++h2) {
+        const double wj = (lane + 64 * h2 <= ic) ? exp(s[h2] - m) : 0.0;
+        ws[w][lane + 64 * h2] = wj;
+        wsum += wj;
     }
-    const double omega = wave_sum_d(wl[0] + wl[1]);
+    const double omega = wave_sum_d(wsum);
     LDS_FENCE();
 
     // ---- weighted means, lane = feature
@@ -1363,11 +1368,13 @@ __device__ __forceinline__ void short_block(
     dmax = wave_max_d(dmax);
     const double thresh = lambda > 0.0 ? 0.0 : 1e-12 * dmax;
 
-    // ---- to lane-per-row form: pass p stages rows 16p .. 16p+15 and lanes 16p.. read them
+    // ---- to lane-per-row form: pass pp stages rows 8 pp .. 8 pp + 7 (half hh of block row
+    // P = pp / 2) and lanes 8 pp .. read them
     double cr[FD];
     double* T = tb[w];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int pp = 0; pp < 8; ++pp) {
+        const int P = pp / 2, hh = pp % 2;
         int idx = 0;
 #pragma unroll
         for (int I = 0; I < 4; ++I)
@@ -1376,22 +1383,25 @@ __device__ __forceinline__ void short_block(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     // block (I, J), register r: C[16I + 4r + g][16J + c]
-                    if (I == p) T[(4 * r + g) * S_TLD + 16 * J + c] = cacc[idx][r];
-                    else if (J == p) T[c * S_TLD + 16 * I + 4 * r + g] = cacc[idx][r];
+                    if (I == P) {
+                        if (r / 2 == hh) T[(4 * (r - 2 * hh) + g) * S_TLD + 16 * J + c] = cacc[idx][r];
+                    } else if (J == P) {
+                        if (c / 8 == hh) T[(c - 8 * hh) * S_TLD + 16 * I + 4 * r + g] = cacc[idx][r];
+                    }
                 }
                 ++idx;
             }
         LDS_FENCE();
-        if (g == p) {
+        if (lane / 8 == pp) {
 #pragma unroll
-            for (int b = 0; b < FD; ++b) cr[b] = T[c * S_TLD + b];
+            for (int b = 0; b < FD; ++b) cr[b] = T[(lane % 8) * S_TLD + b];
         }
         LDS_FENCE();
     }
     double z = ka - qs[w][lane];
 
     // ---- LDL^T elimination (lane owns row), then back substitution
-    double* xw = xb[w];
+    double* xw = T;   // the transposition buffer, no longer needed, holds the pivot row
 #pragma unroll
     for (int p = 0; p < FD; ++p) {
         xw[lane] = cr[p];
@@ -1417,20 +1427,22 @@ __device__ __forceinline__ void short_block(
     xw[lane] = ylane;
     LDS_FENCE();
 
-    // ---- probe: u_j = (k_j - kbar).y for keys lane, lane + 64; then b = vbar - C_vk y
-    double wu[2] = {0.0, 0.0};
+    // ---- probe: u_j = (k_j - kbar).y for keys lane + 64 h; then b = vbar - C_vk y
+    double wusum = 0.0;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < S_KPL; ++h2) {
         const int j = lane + 64 * h2;
+        double wu = 0.0;
         if (j <= ic) {
             double u = 0.0;
 #pragma unroll 16
             for (int a = 0; a < FD; ++a) u = fma(kval(j, a) - kbs[w][a], xw[a], u);
-            wu[h2] = wl[h2] * u;
+            wu = ws[w][j] * u;   // this lane's own weight entry, overwritten just below
         }
-        ws[w][lane + 64 * h2] = wu[h2];
+        ws[w][j] = wu;
+        wusum += wu;
     }
-    const double swu = wave_sum_d(wu[0] + wu[1]);
+    const double swu = wave_sum_d(wusum);
     LDS_FENCE();
     double acc = 0.0;
     for (int j = 0; j <= ic; ++j) acc = fma(ws[w][j], vval(j, lane), acc);
@@ -1657,7 +1669,7 @@ __global__ __launch_bounds__(RF_WAVES * 64) void lla_refine_kernel(
 }
 
 // All row work after the row maxima in one launch: short rows (fp64) and the key-moment
-// blocks of rows >= 2d.  The short blocks (the "aux" blocks) fill every other run of R_CHUNK
+// blocks of rows >= 3d.  The short blocks (the "aux" blocks) fill every other run of R_CHUNK
 // dispatch positions at the start, so that a CU tends to hold one aux block, mostly
 // latency-bound, beside a key-moment block, mostly on the matrix cores (the dispatcher places
 // blocks b and b + CU count together).
@@ -1715,16 +1727,16 @@ __global__ __launch_bounds__(256, 2) void lla_rows_kernel(const RowsArgs a) {
     }
 }
 
-// Rows [0, 2d): fp64 short-row kernel; [2d, n): key moments and probe pass.
-int fast_row0(int64_t n, int64_t d) { return static_cast<int>(n < 2 * d ? n : 2 * d); }
+// Rows [0, 3d): fp64 short-row blocks; [3d, n): key moments and probe pass.
+int fast_row0(int64_t n, int64_t d) { return static_cast<int>(n < 3 * d ? n : 3 * d); }
 
 // Fast-path workspace, each region 256-byte aligned:
-//   row maxima [B*H][n - 2d] | anchor partial sums [B*H][16][2d] | anchors [B*H][2d] |
+//   row maxima [B*H][n - 3d] | anchor partial sums [B*H][16][2d] | anchors [B*H][2d] |
 //   key/value tile images [B*H][tiles] | key-major key images (bf16, centred fp16)
-//   [B*H][tiles] | check images [B*H][tiles] | probe solutions (fp16 hi, lo) [B*H][n - 2d][2d] |
-//   probe scalars [B*H][n - 2d][8] | check targets [B*H][n - 2d][32] | guard: count of rows
+//   [B*H][tiles] | check images [B*H][tiles] | probe solutions (fp16 hi, lo) [B*H][n - 3d][2d] |
+//   probe scalars [B*H][n - 3d][8] | check targets [B*H][n - 3d][32] | guard: count of rows
 //   handed back, then per head the largest |k - a| and |v - a_v| (float bits) [1 + 2 B*H] |
-//   rows handed back [B*H][n - 2d].
+//   rows handed back [B*H][n - 3d].
 struct FastLayout {
     int64_t mrow, partial, anchors, packed, kimg, kuimg, yhl, qsc, chk, guard, list, total;
 };

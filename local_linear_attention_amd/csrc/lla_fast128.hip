@@ -14,8 +14,9 @@
 //
 // Work split (rows are query positions i of one head, d = 128):
 //   * rows i < 4d run on the fp64 kernel (prefixes of at most 4d keys: C_kk is rank-deficient
-//     or poorly conditioned there, and fp16 factors lose too much; emulation put the probe
-//     form of rows [2d, 4d) at 2.1e-3 of the 3e-3 bar);
+//     or poorly conditioned there; in fp16 the rows just past 2d reach about 2e-3, and with
+//     keys 64 times larger than the queries rows [2d, 4d) pass the 3e-3 bar unseen by the
+//     check below);
 //   * rows i >= 4d:
 //       lla8_anchor_kernel  per-head sums of the keys and values of positions [0, 2d): the
 //                           centring anchor a (every row here has them in its prefix);
@@ -26,7 +27,9 @@
 //                           C = R^T R on MFMA (36 upper 16x16 blocks, fp32 accumulate), block
 //                           sums S_k = sum w (k - a), omega' = sum w with w = fp16(sw^2); the
 //                           rank-one downdate and ridge, a blocked LDL^T solve in one wave;
-//       lla8_probe_kernel   the probe pass on MFMA, bitwise the same scores and weights.
+//       lla8_probe_kernel   the probe pass on MFMA, bitwise the same scores and weights, and
+//                           the per-row reproduction check;
+//       lla_exact_list_kernel  the rows handed back, in fp64.
 //
 // MFMA v_mfma_f32_16x16x32_{bf16,f16}: lane l supplies row/column (l % 16) of A/B and K-slots
 // 8 (l / 16) .. +8; D[4 (l / 16) + r][l % 16] is accumulator register r of lane l.

@@ -130,11 +130,11 @@ def fast_workspace_bytes(BH, n, d=64):
     """Scratch bytes of the bf16 matrix-core path, region by region (each rounded up to
     256 B where the library rounds it).
 
-    d = 64: row maxima of rows >= 2d, anchor partial sums, anchors, then per head and 64-key
+    d = 64: row maxima of rows >= 3d, anchor partial sums, anchors, then per head and 64-key
     tile the fp16 K/V image (72-half rows), the two key-major key images (bf16, centred
-    fp16) and the 5 KiB check image, then per row >= 2d the fp16 hi/lo solution, eight
+    fp16) and the 5 KiB check image, then per row >= 3d the fp16 hi/lo solution, eight
     scalars and 32 check targets, the guard words (count of rows handed back, two maxima per
-    head) and the hand-back list (one slot per row >= 2d).
+    head) and the hand-back list (one slot per row >= 3d).
 
     d = 128: the same regions for rows >= 4d, with the K and V feature-major images apart
     (72-half rows) and key-major rows of 136 halves."""
@@ -148,7 +148,7 @@ def fast_workspace_bytes(BH, n, d=64):
                 + BH * tiles * (2 * d * 72 * 2 + 2 * 64 * 136 * 2 + 5 * 1024)
                 + up(BH * prows * 2 * d * 2) + up(BH * prows * 8 * 4) + up(BH * prows * 32 * 4)
                 + up((1 + 2 * BH) * 4) + up(BH * prows * 4))
-    prows = n - min(n, 2 * d)
+    prows = n - min(n, 3 * d)
     if prows <= 0:
         return 0
     return (up(BH * prows * 4) + up(BH * 16 * 2 * d * 4) + up(BH * 2 * d * 4)

@@ -136,7 +136,10 @@ def test_workspace_size():
     assert lla.lla_workspace_size(1, 3, 300, 64, "bf16", "fast") == fast_bytes(3, 300)
     assert lla.lla_workspace_size(1, 8, 16384, 128, "bf16", "auto") == fast_bytes(8, 16384, 128)
     assert lla.lla_workspace_size(2, 3, 777, 128, "bf16", "fast") == fast_bytes(6, 777, 128)
-    assert lla.lla_workspace_size(1, 2, 512, 128, "bf16", "fast") == 0     # every row is short
+    assert lla.lla_workspace_size(1, 2, 512, 128, "bf16", "fast") == 0     # every row is short (i < 4d)
+    assert lla.lla_workspace_size(1, 2, 513, 128, "bf16", "fast") == fast_bytes(2, 513, 128) > 0
+    assert lla.lla_workspace_size(1, 2, 192, 64, "bf16", "fast") == 0      # every row is short (i < 3d)
+    assert lla.lla_workspace_size(1, 2, 193, 64, "bf16", "fast") == fast_bytes(2, 193) > 0
     # beyond the fast path's sequence limit AUTO falls back to the exact path (no scratch)
     assert lla.lla_workspace_size(1, 1, (1 << 22) + 1, 64, "bf16", "fast") == 0
     assert lla.lla_workspace_size(1, 1, (1 << 22) + 1, 64, "bf16", "auto") == 0
