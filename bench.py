@@ -95,7 +95,7 @@ KERNEL_BOUND = {
 }
 PATH_KERNELS = {
     "exact": ["lla_exact_kernel"],
-    "cg": ["lla_cg_kernel"],
+    "cg": ["lla_cg_kernel", "lla_exact_list_kernel"],   # the list: rows CG leaves unconverged
     # the last launch recomputes in fp64 the rows the range guard and the checks hand back
     "fast": ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel",
              "lla_probe_kernel", "lla_refine_kernel"],

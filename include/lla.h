@@ -75,20 +75,29 @@ typedef enum {
 typedef enum {
     LLA_PATH_AUTO = 0,   /* fp32 inputs -> EXACT; bf16 inputs -> FAST where built */
     LLA_PATH_EXACT = 1,  /* fp64 accumulation and solve, any supported (dtype, d) */
-    LLA_PATH_FAST = 2,   /* matrix-core path for bf16 inputs (d = 64); inputs must lie in the
-                            fp16 range, and rows i < 2d still run on the fp64 kernel */
+    LLA_PATH_FAST = 2,   /* matrix-core path for bf16 inputs, d = 64 (n up to 2^22) and d = 128
+                            (n up to 2^21): rows i < 3d (d = 64) or i < 4d (d = 128) run in
+                            fp64; the others on MFMA (fp16 operands centred at a per-head
+                            anchor, fp32 accumulation, fp32 solve), except the rows it hands
+                            back to the fp64 kernel: those of a head whose centred keys or
+                            values leave [2^-10, 2^14] (the fp16 range), rows whose output is
+                            not finite or whose solve dropped a pivot under a positive ridge,
+                            and rows whose reproduction check (the LLA weights applied to the
+                            keys must return q + lambda e^{-m} y) estimates a relative error
+                            above 1.5e-3.  lla_forward_fallback_rows counts them. */
     LLA_PATH_CG = 3      /* LLA entry points only: fp64 like EXACT, but each query's system
                             solved by conjugate gradient whose matrix-vector products are passes
                             over the prefix (the solver of the "Parallax" blog post, section 2,
                             "Difficulties in Scaling LLA"): no d x d state, one prefix pass per
                             iteration, at most 4d iterations, stop at residual 1e-10 of the
-                            right-hand side; any supported (dtype, d), no workspace; never
-                            chosen by AUTO.  A row whose iteration does not reach that residual
-                            within 4d iterations is written as NaN: CG needs about sqrt(cond)
-                            iterations, and a ridge lambda e^{-m} far below the spread of the
-                            weighted keys (sharp weights, prefixes shorter than d, lambda = 0)
-                            makes the system too ill-conditioned for that budget; EXACT serves
-                            those rows. */
+                            right-hand side; any supported (dtype, d); never chosen by AUTO.
+                            A row whose iteration does not reach that residual within 4d
+                            iterations (CG needs about sqrt(cond) iterations, and a ridge
+                            lambda e^{-m} far below the spread of the weighted keys -- sharp
+                            weights, prefixes shorter than d, lambda = 0 -- puts the system out
+                            of reach of that budget) is solved by the EXACT path's direct fp64
+                            elimination instead, in a launch after the CG one.  Its scratch
+                            (lla_workspace_size with this path) is the list of those rows. */
 } lla_path_t;
 
 /*
@@ -118,14 +127,19 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
                             lla_dtype_t dtype, void* stream, lla_path_t path);
 
 /* Bytes of device scratch that `path` needs for this problem (0 if none, or if the sizes,
- * dtype or path are invalid).  The fast path keeps there, in regions each rounded up to a
- * multiple of 256 bytes: one float per row at or beyond position 2d (its score maximum);
- * 16*2d floats per head of partial key/value sums and 2d floats per head of the centring
- * anchor; then, per head and tile of 64 keys, K and V as fp16 (2*d*72*2 bytes: feature-major
- * rows of 64 keys plus 8 halves of padding) and K key-major twice, as given and centred as
- * fp16 (2*64*72*2 bytes); then, per row at or beyond position 4d, the row's solution as two
- * fp16 parts (2*d*2 bytes) and four floats (16 bytes, one region each).  Nothing when
- * n <= 2d.  The fast path serves n up to 4194304 (2^22); AUTO uses the exact path beyond. */
+ * dtype or path are invalid).  With r0 = 3d (d = 64) or 4d (d = 128), the fast path keeps
+ * there, in regions each rounded up to a multiple of 256 bytes: one float per row at or
+ * beyond position r0 (its score maximum); 16*2d floats per head of partial key/value sums
+ * and 2d floats per head of the centring anchor; then, per head and tile of 64 keys, K and V
+ * as fp16 feature-major (rows of 64 keys plus 8 halves of padding), K key-major twice (as
+ * given and centred as fp16, rows of d + 8 halves), and a 5 KiB check image (the centred
+ * keys projected on 32 +-1 directions, fp16, and |v - a_v|^2 per key); then, per row at or
+ * beyond r0, the row's solution as two fp16 parts (2*d*2 bytes), eight floats and 32 check
+ * targets (one region each); then 1 + 2*B*H words (the count of rows handed back and the
+ * per-head range maxima) and one 32-bit slot per row at or beyond r0 for the rows handed
+ * back.  Nothing when n <= r0.  The CG path keeps the count of rows it hands to the direct
+ * solve (256 bytes) and one 32-bit slot per row.  AUTO uses the exact path where the fast
+ * path does not apply (n above its limit, fp32 inputs, d of 16 or 32). */
 size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                           lla_path_t path);
 

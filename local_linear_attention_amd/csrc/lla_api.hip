@@ -133,6 +133,19 @@ lla_status_t run(const lla::Problem& p, bool fast, void* ws, size_t ws_bytes, bo
                        [&](void* w) { return lla::launch_fast(p, w); });
 }
 
+lla_status_t run_cg(const lla::Problem& p, void* ws, size_t ws_bytes, bool may_allocate) {
+    const int64_t in_bytes = p.B * p.H * p.n * p.d * (p.dtype == LLA_DTYPE_F32 ? 4 : 2);
+    return run_scratch(lla::cg_workspace_bytes(p.B, p.H, p.n), p.stream, ws, ws_bytes, may_allocate,
+                       {{p.q, in_bytes}, {p.k, in_bytes}, {p.v, in_bytes}, {p.out, p.B * p.H * p.n * p.d * 4}},
+                       [&](void* w) { return lla::launch_cg(p, w); });
+}
+
+// Scratch bytes of an LLA forward on `path` (after validation and path resolution).
+size_t forward_scratch_bytes(int64_t B, int64_t H, int64_t n, int64_t d, lla_path_t path, bool fast) {
+    if (path == LLA_PATH_CG) return lla::cg_workspace_bytes(B, H, n);
+    return fast ? lla::fast_workspace_bytes(B, H, n, d) : 0;
+}
+
 // ---- Parallax
 lla_status_t validate_parallax(const void* q, const void* k, const void* v, const void* rho, const float* out,
                                int64_t B, int64_t H, int64_t n, int64_t d, double h, lla_dtype_t dtype) {
@@ -388,8 +401,8 @@ size_t lla_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_
                           lla_path_t path) {
     if (!supported_shape(d, dtype) || validate_sizes(B, H, n, d) != LLA_OK) return 0;
     bool fast = false;
-    if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast) || !fast) return 0;
-    return lla::fast_workspace_bytes(B, H, n, d);
+    if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return 0;
+    return forward_scratch_bytes(B, H, n, d, path, fast);
 }
 
 size_t lla_forward_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype) {
@@ -406,10 +419,11 @@ lla_status_t lla_forward_fallback_rows(const void* workspace, size_t workspace_b
     if (st != LLA_OK) return st;
     bool fast = false;
     if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
-    if (!fast) return LLA_OK;
-    const int64_t off = lla::fast_fallback_count_offset(B, H, n, d);
+    if (!fast && path != LLA_PATH_CG) return LLA_OK;
+    const int64_t off = path == LLA_PATH_CG ? 0 : lla::fast_fallback_count_offset(B, H, n, d);
     if (off < 0) return LLA_OK;
-    if (workspace == nullptr || workspace_bytes < lla::fast_workspace_bytes(B, H, n, d)) return LLA_ERR_WORKSPACE;
+    if (workspace == nullptr || workspace_bytes < forward_scratch_bytes(B, H, n, d, path, fast))
+        return LLA_ERR_WORKSPACE;
     uint32_t count = 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(&count, static_cast<const unsigned char*>(workspace) + off, sizeof(count),
@@ -438,7 +452,7 @@ lla_status_t lla_forward_ws(const void* q, const void* k, const void* v, float* 
     if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
     const lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream)};
-    if (path == LLA_PATH_CG) return lla::launch_cg(p) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    if (path == LLA_PATH_CG) return run_cg(p, workspace, workspace_bytes, false);
     return run(p, fast, workspace, workspace_bytes, false);
 }
 
@@ -450,7 +464,7 @@ lla_status_t lla_forward_noalloc(const void* q, const void* k, const void* v, fl
     if (st != LLA_OK) return st;
     bool fast = false;
     if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
-    const size_t need = fast ? lla::fast_workspace_bytes(B, H, n, d) : 0;
+    const size_t need = forward_scratch_bytes(B, H, n, d, path, fast);
     if (need > kNoAllocScratchBytes) return LLA_ERR_SCRATCH_LIMIT;
     void* ws = nullptr;
     if (need > 0 && scratch_for_current_device(&ws) != hipSuccess) return LLA_ERR_HIP;
@@ -467,7 +481,7 @@ lla_status_t lla_forward_ex(const void* q, const void* k, const void* v, float* 
     if (!resolve_fast(path, static_cast<int>(dtype), d, n, &fast)) return LLA_ERR_UNSUPPORTED;
     const lla::Problem p{q, k, v, out, B, H, n, d, h, lambda, static_cast<int>(dtype),
                          static_cast<hipStream_t>(stream)};
-    if (path == LLA_PATH_CG) return lla::launch_cg(p) == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+    if (path == LLA_PATH_CG) return run_cg(p, nullptr, 0, true);
     return run(p, fast, nullptr, 0, true);
 }
 

@@ -10,12 +10,12 @@
 //              A p = sum_j wt_j ((k_j - kbar) . p) (k_j - kbar) + lambda e^{-m} p,
 //            then the usual CG updates (x from 0); it stops when |r| <= tol |kbar - q|, when
 //            p.Ap is not positive, or after max_iter iterations
-//   output   b = vbar - sum_j wt_j ((k_j - kbar) . x) (v_j - vbar)   (= vbar - C_vk x), or NaN
-//            in every feature when the residual did not reach the tolerance: CG needs about
-//            sqrt(cond A) iterations, and a ridge lambda e^{-m} far below the spread of the
-//            weighted keys (sharp weights, prefixes shorter than d) leaves cond A near 1e8,
-//            out of reach of a budget proportional to d -- the ill-conditioning the pages name
-//            as CG's weakness.  A NaN row says so rather than returning an unconverged value.
+//   output   b = vbar - sum_j wt_j ((k_j - kbar) . x) (v_j - vbar)   (= vbar - C_vk x).
+//   A row whose residual did not reach the tolerance is handed to the direct fp64 solve
+//   (lla_exact_kernel in list mode, after this launch): CG needs about sqrt(cond A)
+//   iterations, and a ridge lambda e^{-m} far below the spread of the weighted keys (sharp
+//   weights, prefixes shorter than d) leaves cond A near 1e8, out of reach of a budget
+//   proportional to d -- the ill-conditioning the pages name as CG's weakness.
 //
 // The same centred system as the direct fp64 path (lla_exact.hip), so both give the LLA
 // intercept; this one keeps only d-vectors per query (no d x d state) at the price of one
@@ -37,7 +37,8 @@ template <typename TIn, int D>
 __global__ __launch_bounds__(CG_NT) void lla_cg_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                        const TIn* __restrict__ v, float* __restrict__ out, int n,
                                                        int BH, double inv_h, double lambda, int max_iter,
-                                                       double tol) {
+                                                       double tol, unsigned* __restrict__ count,
+                                                       int* __restrict__ list) {
     constexpr int NT = CG_NT;
     constexpr int CHK = 2048 / D;   // keys per staged chunk (16 KiB of fp64 per array)
     constexpr int G = NT / CHK;     // threads per key in the dot products
@@ -198,6 +199,10 @@ __global__ __launch_bounds__(CG_NT) void lla_cg_kernel(const TIn* __restrict__ q
         }
     }
     const bool converged = rho <= stop;   // uniform
+    if (!converged) {   // the direct solve takes the row
+        if (tid == 0) list[atomicAdd(count, 1u)] = bh * n + i;
+        return;
+    }
     __syncthreads();
     if (tid < D) xs[tid] = xr;
     __syncthreads();
@@ -216,37 +221,52 @@ __global__ __launch_bounds__(CG_NT) void lla_cg_kernel(const TIn* __restrict__ q
         __syncthreads();
     }
     const double so = feature_sum(ao);
-    if (tid < D)
-        out[base + static_cast<int64_t>(i) * D + tid] = converged ? static_cast<float>(vbar[tid] - so) : NAN;
+    if (tid < D) out[base + static_cast<int64_t>(i) * D + tid] = static_cast<float>(vbar[tid] - so);
 }
 
+// The count of rows handed to the direct solve starts at zero (a kernel, not a memset, so
+// that the sequence can be captured in a graph).
+__global__ void lla_cg_clear_kernel(unsigned* __restrict__ count) { *count = 0u; }
+
 template <typename TIn, int D>
-hipError_t launch_cg_t(const Problem& p) {
+hipError_t launch_cg_t(const Problem& p, unsigned* count, int* list) {
     const int BH = static_cast<int>(p.B * p.H);
     const unsigned blocks = static_cast<unsigned>(p.B * p.H * p.n);
+    lla_cg_clear_kernel<<<dim3(1), dim3(1), 0, p.stream>>>(count);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
     prof_begin(p.stream, "lla_cg_kernel");
     lla_cg_kernel<TIn, D><<<dim3(blocks), dim3(CG_NT), 0, p.stream>>>(
         static_cast<const TIn*>(p.q), static_cast<const TIn*>(p.k), static_cast<const TIn*>(p.v), p.out,
-        static_cast<int>(p.n), BH, 1.0 / p.h, p.lambda, kCgMaxIterFactor * static_cast<int>(p.d), kCgTol);
+        static_cast<int>(p.n), BH, 1.0 / p.h, p.lambda, kCgMaxIterFactor * static_cast<int>(p.d), kCgTol, count,
+        list);
     prof_end(p.stream);
-    return hipGetLastError();
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int64_t rows = p.B * p.H * p.n;
+    return launch_exact_list(p, list, reinterpret_cast<const int*>(count), static_cast<int>(rows < 2048 ? rows : 2048));
 }
 
 template <typename TIn>
-hipError_t launch_cg_d(const Problem& p) {
+hipError_t launch_cg_d(const Problem& p, unsigned* count, int* list) {
     switch (p.d) {
-        case 16: return launch_cg_t<TIn, 16>(p);
-        case 32: return launch_cg_t<TIn, 32>(p);
-        case 64: return launch_cg_t<TIn, 64>(p);
-        case 128: return launch_cg_t<TIn, 128>(p);
+        case 16: return launch_cg_t<TIn, 16>(p, count, list);
+        case 32: return launch_cg_t<TIn, 32>(p, count, list);
+        case 64: return launch_cg_t<TIn, 64>(p, count, list);
+        case 128: return launch_cg_t<TIn, 128>(p, count, list);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_cg(const Problem& p) {
-    return p.dtype == 0 ? launch_cg_d<float>(p) : launch_cg_d<uint16_t>(p);
+size_t cg_workspace_bytes(int64_t B, int64_t H, int64_t n) {
+    return 256 + ((static_cast<size_t>(B * H * n) * 4 + 255) & ~size_t(255));
+}
+
+hipError_t launch_cg(const Problem& p, void* workspace) {
+    auto* count = static_cast<unsigned*>(workspace);
+    auto* list = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + 256);
+    return p.dtype == 0 ? launch_cg_d<float>(p, count, list) : launch_cg_d<uint16_t>(p, count, list);
 }
 
 }  // namespace lla

@@ -36,8 +36,11 @@ hipError_t launch_exact(const Problem& p, int rows);
 hipError_t launch_exact_list(const Problem& p, const int* list, const int* count, int blocks);
 
 // fp64 path with each query's system solved by conjugate gradient over its prefix (no
-// d x d state): every (dtype, d); no workspace.
-hipError_t launch_cg(const Problem& p);
+// d x d state): every (dtype, d).  Workspace (cg_workspace_bytes): the count of rows whose
+// iteration did not converge (a 32-bit unsigned at offset 0), then their list; those rows
+// are solved directly (launch_exact_list) after the CG launch.
+size_t cg_workspace_bytes(int64_t B, int64_t H, int64_t n);
+hipError_t launch_cg(const Problem& p, void* workspace);
 
 // Matrix-core path for bf16 inputs: rows i < 2d on the fp64 kernel, the rest on MFMA
 // kernels that keep per-row statistics and packed key/value tiles in `workspace`

@@ -263,13 +263,15 @@ def test_parallax_unknown_or_uncovered_path_is_rejected():
     assert call_parallax(lib, path=3) == 4            # CG solves the LLA system; Parallax has none
 
 
-def test_cg_path_is_an_lla_path_without_scratch():
+def test_cg_path_is_an_lla_path_with_a_row_list_scratch():
+    # The CG path keeps no d x d state; its scratch is the list of rows whose iteration did not
+    # converge (a count, then one 32-bit entry per row), which the direct solve then takes.
     from local_linear_attention_amd import lla
     lib = _lib()
     for dt in ("f32", "bf16"):
         for d in (16, 32, 64, 128):
             assert lla.lla_path_available("cg", dt, d)
-            assert lla.lla_workspace_size(2, 3, 500, d, dt, "cg") == 0
+            assert lla.lla_workspace_size(2, 3, 500, d, dt, "cg") == 256 + (6 * 500 * 4 + 255) // 256 * 256
     assert not lla.lla_path_available("cg", "bf16", 48)
     assert not lla.lla_parallax_path_available("cg", "bf16", 64)
     # validation happens before any launch on the CG path too
@@ -278,6 +280,12 @@ def test_cg_path_is_an_lla_path_without_scratch():
     assert call(lib, path=3, lam=-1.0) == 3
     assert call(lib, path=3, d=48) == 4
     assert call(lib, path=3, out=Q + 16) == 7
+    # the _ws entry point needs that scratch on the CG path
+    need = lla.lla_workspace_size(1, 2, 4096, 64, "bf16", "cg")
+    args = [ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(V), ctypes.c_void_p(OUT),
+            1, 2, 4096, 64, 8.0, 0.1, 1, None, 3]
+    assert lib.lla_forward_ws(*args, None, 0) == 5
+    assert lib.lla_forward_ws(*args, ctypes.c_void_p(0x7e0000000000), need - 1) == 5
 
 
 def parallax_workspace_bytes(BH, n):

@@ -5,8 +5,9 @@ oracle, and against the direct fp64 path on the same inputs.
 Small shapes compare every row (several staged key chunks and a ragged tail, every head
 size, both dtypes, lambda = 0 on rows i >= d); the d = 128 workload at full length compares
 a seeded sample of rows.  Rows whose system is too ill-conditioned for the iteration budget
-come back as NaN, and only those.  Bars: the contract's (1e-4 fp32 inputs, 3e-3 bf16), and 1e-5
-against the oracle on these inputs (the CG stops at a relative residual of 1e-10).
+are solved directly in fp64 instead, so every row is finite and within the bar.  Bars: the
+contract's (1e-4 fp32 inputs, 3e-3 bf16), and 1e-5 against the oracle on these inputs (the CG
+stops at a relative residual of 1e-10).
 """
 import numpy as np
 import pytest
@@ -50,32 +51,24 @@ def test_every_row(name, shape):
     check(got, ref, w.dtype, f"{name}{shape}")
 
 
-def test_ill_conditioned_rows_are_flagged():
+def test_ill_conditioned_rows_take_the_direct_solve():
     # fp32 inputs with h = 4 at d = 128: sharp weights and prefixes shorter than d give
-    # systems with condition numbers up to ~1e8, beyond CG's 4d-iteration budget.  Every row
-    # must either match the oracle or be NaN, and only ill-conditioned rows may be NaN.
-    require_gpu()
+    # systems with condition numbers up to ~1e8, beyond CG's 4d-iteration budget.  Those rows
+    # go to the direct fp64 solve: every row is finite and matches the oracle.
+    torch = require_gpu()
+    from local_linear_attention_amd.lla import lla_forward_fallback_rows, lla_forward_ws, lla_workspace_size
+    from parity_util import to_device
     w, q, k, v = workload_arrays("tiny", B=1, H=2, n=130, d=128, dtype="f32")
     ref = oracle_forward(q, k, v, w.h, w.lam)
-    got = run_gpu(q, k, v, w.dtype, w.h, w.lam, path="cg")
-    flagged = np.isnan(got).all(-1)
-    assert np.array_equal(np.isnan(got).any(-1), flagged)   # whole rows only
-    ok = ~flagged
-    err = row_errors(got[ok], ref[ok])
-    conds = []
-    for hh in range(w.H):
-        for i in range(w.n):
-            if flagged[0, hh, i]:
-                kk, qq = k[0, hh, : i + 1].astype(np.float64), q[0, hh, i].astype(np.float64)
-                s = kk @ qq / w.h
-                wt = np.exp(s - s.max())
-                kc = kk - wt @ kk / wt.sum()
-                A = kc.T @ (wt[:, None] * kc) + w.lam * np.exp(-s.max()) * np.eye(w.d)
-                conds.append(np.linalg.cond(A))
-    print(f"[cg flagged] {int(flagged.sum())} of {flagged.size} rows NaN, min cond of those "
-          f"{min(conds) if conds else float('nan'):.1e}; others max_row_err={float(err.max()):.2e}", flush=True)
+    tq, tk, tv = (to_device(x, "f32") for x in (q, k, v))
+    ws = torch.empty(lla_workspace_size(w.B, w.H, w.n, w.d, "f32", "cg"), dtype=torch.uint8, device="cuda")
+    got = lla_forward_ws(tq, tk, tv, w.h, w.lam, ws, path="cg").cpu().numpy().astype(np.float64)
+    back = lla_forward_fallback_rows(ws, (w.B, w.H, w.n, w.d), "f32", "cg")
+    err = row_errors(got, ref)
+    print(f"[cg] {back} of {w.B * w.H * w.n} rows solved directly; max_row_err={float(err.max()):.2e}", flush=True)
+    assert back > 0   # the recipe does produce rows beyond the iteration budget
+    assert np.isfinite(got).all()
     assert float(err.max()) <= CG_BOUND
-    assert not conds or min(conds) > 1e5
 
 
 def test_lambda_zero_rows_beyond_d():
