@@ -85,11 +85,27 @@ __device__ __forceinline__ void hand_back(unsigned* guard, int* list, int bh, in
     const unsigned slot = atomicAdd(guard, 1u);
     list[slot] = bh * n + i;
 }
-// Largest |x| over the wave, then one atomic max per wave into *dst (x >= 0 or NaN).
-__device__ __forceinline__ void wave_atomic_max(unsigned* dst, float x) {
+// Largest x >= 0 over the wave (in every lane).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    if ((threadIdx.x & 63) == 0) atomicMax(dst, __float_as_uint(x));
+    return x;
+}
+
+// In-place Walsh-Hadamard transform of N values in registers (N a power of two):
+// x[m] <- sum_f (-1)^popcount(f & m) x[f].
+template <int N>
+__device__ __forceinline__ void walsh_transform(float (&x)[N]) {
+#pragma unroll
+    for (int hh = 1; hh < N; hh <<= 1)
+#pragma unroll
+        for (int i = 0; i < N; i += 2 * hh)
+#pragma unroll
+            for (int e = i; e < i + hh; ++e) {
+                const float a0 = x[e], a1 = x[e + hh];
+                x[e] = a0 + a1;
+                x[e + hh] = a0 - a1;
+            }
 }
 
 // Block b -> (head bh, row block blk).  Work-groups go round-robin to the 8 XCDs, so

@@ -138,8 +138,9 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
                                                        unsigned* __restrict__ guard, int n,
                                                        int ntiles) {
     __shared__ float anc[2 * FD];
-    __shared__ float kst[MT][FD + 1];   // centred fp16 keys of the tile, as floats
+    __shared__ float ys[MT][8][5];      // per key and feature group: odd-index 8-point transforms
     __shared__ float vpart[8][MT];      // |v - a_v|^2 over each thread's 8 features
+    __shared__ float wmax[4][2];        // per wave: largest |k - a|, |v - a_v|
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
     const int tid = threadIdx.x, pr = tid & 31, fg = tid >> 5;
     if (tid < 2 * FD) {
@@ -209,9 +210,14 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
                 mv = fmaxf(mv, fabsf(f(vb[e >> 1]) - av));
             }
         }
-        wave_atomic_max(guard + 1 + 2 * bh, mk);
-        wave_atomic_max(guard + 2 + 2 * bh, mv);
+        mk = wave_max_nonneg(mk);
+        mv = wave_max_nonneg(mv);
+        if ((tid & 63) == 0) {
+            wmax[tid >> 6][0] = mk;
+            wmax[tid >> 6][1] = mv;
+        }
     }
+    float xa[8], xb[8];   // centred fp16 keys 2p, 2p+1 of this thread's features, as floats
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int row = 8 * fg + e;
@@ -229,42 +235,56 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
             dst[row * (M_LD / 2) + MT / 2 + pr] = 0u;
             dst[(FD + row) * (M_LD / 2) + MT / 2 + pr] = 0u;
         }
-        kst[2 * pr][row] = static_cast<float>(kk[0]);
-        kst[2 * pr + 1][row] = static_cast<float>(kk[1]);
+        xa[e] = static_cast<float>(kk[0]);
+        xb[e] = static_cast<float>(kk[1]);
         vsa = fmaf(static_cast<float>(vv[0]), static_cast<float>(vv[0]), vsa);
         vsb = fmaf(static_cast<float>(vv[1]), static_cast<float>(vv[1]), vsb);
     }
     vpart[fg][2 * pr] = vsa;
     vpart[fg][2 * pr + 1] = vsb;
+    // Check image: the 64-point Walsh-Hadamard transform of each key's centred values,
+    // X[m] = sum_f (-1)^popcount(f & m) x_f with f = 8 fg + e, m = 8 mh + ml, splits into
+    // 8-point transforms over e (here, per thread) and then over fg (below, per key); only
+    // odd m (odd ml) are kept: direction t = (m - 1) / 2.
+    walsh_transform(xa);
+    walsh_transform(xb);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        ys[2 * pr][fg][q4] = xa[2 * q4 + 1];
+        ys[2 * pr + 1][fg][q4] = xb[2 * q4 + 1];
+    }
     __syncthreads();
-    // Check image: thread j < 64 takes key j through a 64-point Walsh-Hadamard transform
-    // (X[m] = sum_f (-1)^popcount(f & m) x_f) and keeps the odd-index coefficients.
+    if (tid == 0) {   // the block's range maxima, one atomic each
+        float mk = 0.0f, mv = 0.0f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+            mk = fmaxf(mk, wmax[w4][0]);
+            mv = fmaxf(mv, wmax[w4][1]);
+        }
+        atomicMax(guard + 1 + 2 * bh, __float_as_uint(mk));
+        atomicMax(guard + 2 + 2 * bh, __float_as_uint(mv));
+    }
     unsigned char* kut = kuimg + (static_cast<int64_t>(bh) * ntiles + t) * KU_TILE_BYTES;
-    if (tid < MT) {
-        float x[FD];
+    {   // thread -> key j, ml = 2 q4 + 1: the 8-point transform over the feature groups
+        const int j = tid & (MT - 1), q4 = tid >> 6;
+        float x8[8];
 #pragma unroll
-        for (int f = 0; f < FD; ++f) x[f] = kst[tid][f];
-#pragma unroll
-        for (int hh = 1; hh < FD; hh <<= 1)
-#pragma unroll
-            for (int i = 0; i < FD; i += 2 * hh)
-#pragma unroll
-                for (int e = i; e < i + hh; ++e) {
-                    const float a0 = x[e], a1 = x[e + hh];
-                    x[e] = a0 + a1;
-                    x[e + hh] = a0 - a1;
-                }
+        for (int g8 = 0; g8 < 8; ++g8) x8[g8] = ys[j][g8][q4];
+        walsh_transform(x8);
         _Float16* kur = reinterpret_cast<_Float16*>(kut);
 #pragma unroll
-        for (int tq = 0; tq < NCHK; ++tq) kur[tq * M_LD + tid] = static_cast<_Float16>(x[2 * tq + 1]);
-        float nv = 0.0f;
+        for (int mh = 0; mh < 8; ++mh) kur[(4 * mh + q4) * M_LD + j] = static_cast<_Float16>(x8[mh]);
+        if (q4 == 0) {
+            float nv = 0.0f;
 #pragma unroll
-        for (int f8 = 0; f8 < 8; ++f8) nv += vpart[f8][tid];
-        reinterpret_cast<float*>(kut + KU_NRM)[tid] = nv;
-    } else if (tid < MT + NCHK) {   // row padding of the projections
-        *reinterpret_cast<uint4*>(kut + (tid - MT) * M_LD * 2 + MT * 2) = make_uint4(0, 0, 0, 0);
-    } else if (tid < MT + NCHK + 16) {   // tail after the norms
-        *reinterpret_cast<uint4*>(kut + KU_NRM + MT * 4 + (tid - MT - NCHK) * 16) = make_uint4(0, 0, 0, 0);
+            for (int f8 = 0; f8 < 8; ++f8) nv += vpart[f8][j];
+            reinterpret_cast<float*>(kut + KU_NRM)[j] = nv;
+        }
+    }
+    if (tid < NCHK) {   // row padding of the projections
+        *reinterpret_cast<uint4*>(kut + tid * M_LD * 2 + MT * 2) = make_uint4(0, 0, 0, 0);
+    } else if (tid < NCHK + 16) {   // tail after the norms
+        *reinterpret_cast<uint4*>(kut + KU_NRM + MT * 4 + (tid - NCHK) * 16) = make_uint4(0, 0, 0, 0);
     }
 }
 

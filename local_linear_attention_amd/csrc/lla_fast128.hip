@@ -121,8 +121,9 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
                                                         unsigned char* __restrict__ kuf,
                                                         unsigned* __restrict__ guard, int n, int ntiles) {
     __shared__ float anc[2 * D8];
-    __shared__ float kst[T8][D8 + 1];   // centred fp16 keys of the tile, as floats
+    __shared__ float ys[T8][16][3];     // per key and feature group: the 8-point transforms kept
     __shared__ float vpart[8][T8];      // |v - a_v|^2 over each thread's 16 features
+    __shared__ float wmax[4][2];        // per wave: largest |k - a|, |v - a_v|
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
     const int tid = threadIdx.x;
     {
@@ -187,8 +188,6 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int f = 8 * fg + e;
-            kst[2 * pr][f] = static_cast<float>(ca[e]);
-            kst[2 * pr + 1][f] = static_cast<float>(cb[e]);
             vsa = fmaf(static_cast<float>(va[e]), static_cast<float>(va[e]), vsa);
             vsb = fmaf(static_cast<float>(vb[e]), static_cast<float>(vb[e]), vsb);
             const h16x2 kk = {ca[e], cb[e]}, vv = {va[e], vb[e]};
@@ -199,40 +198,68 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
                 vft[f * (F_LD / 2) + T8 / 2 + pr] = 0u;
             }
         }
+        // check image, first stage: 8-point transforms over this feature group (ml = 1, 5)
+        float xa[8], xb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            xa[e] = static_cast<float>(ca[e]);
+            xb[e] = static_cast<float>(cb[e]);
+        }
+        walsh_transform(xa);
+        walsh_transform(xb);
+        ys[2 * pr][fg][0] = xa[1];
+        ys[2 * pr][fg][1] = xa[5];
+        ys[2 * pr + 1][fg][0] = xb[1];
+        ys[2 * pr + 1][fg][1] = xb[5];
     }
-    wave_atomic_max(guard + 1 + 2 * bh, mk);
-    wave_atomic_max(guard + 2 + 2 * bh, mv);
+    mk = wave_max_nonneg(mk);
+    mv = wave_max_nonneg(mv);
+    if ((tid & 63) == 0) {
+        wmax[tid >> 6][0] = mk;
+        wmax[tid >> 6][1] = mv;
+    }
     vpart[tid >> 5][2 * pr] = vsa;
     vpart[tid >> 5][2 * pr + 1] = vsb;
     __syncthreads();
-    // Check image: thread j < 64 takes key j through a 128-point Walsh-Hadamard transform
-    // (X[m] = sum_f (-1)^popcount(f & m) x_f) and keeps the coefficients m = 4t + 1.
+    if (tid == 0) {   // the block's range maxima, one atomic each
+        float bk = 0.0f, bv = 0.0f;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+            bk = fmaxf(bk, wmax[w4][0]);
+            bv = fmaxf(bv, wmax[w4][1]);
+        }
+        atomicMax(guard + 1 + 2 * bh, __float_as_uint(bk));
+        atomicMax(guard + 2 + 2 * bh, __float_as_uint(bv));
+    }
+    // Check image: the 128-point Walsh-Hadamard transform of each key's centred values,
+    // X[m] = sum_f (-1)^popcount(f & m) x_f with f = 8 fh + e and m = 8 mh + ml, splits into
+    // 8-point transforms over e (in the loop above, per thread and feature group; ml of 1 and
+    // 5 kept) and 16-point transforms over fh (here, per key); the directions are
+    // m = 4t + 1, i.e. t = 2 mh + (ml == 5).
     unsigned char* kut = kuf + tile * KU_TILE_BYTES;
-    if (tid < T8) {
-        float x[D8];
+    {   // thread -> key j, ml = 1 + 4 s, half hb of the mh range
+        const int j = tid & (T8 - 1), sl = (tid >> 6) & 1, hb = tid >> 7;
+        float x16[16];
 #pragma unroll
-        for (int f = 0; f < D8; ++f) x[f] = kst[tid][f];
-#pragma unroll
-        for (int hh = 1; hh < D8; hh <<= 1)
-#pragma unroll
-            for (int i = 0; i < D8; i += 2 * hh)
-#pragma unroll
-                for (int e = i; e < i + hh; ++e) {
-                    const float a0 = x[e], a1 = x[e + hh];
-                    x[e] = a0 + a1;
-                    x[e + hh] = a0 - a1;
-                }
+        for (int g16 = 0; g16 < 16; ++g16) x16[g16] = ys[j][g16][sl];
+        walsh_transform(x16);
         _Float16* kur = reinterpret_cast<_Float16*>(kut);
 #pragma unroll
-        for (int tq = 0; tq < NCHK; ++tq) kur[tq * F_LD + tid] = static_cast<_Float16>(x[chk8_mask(tq)]);
-        float nv = 0.0f;
+        for (int u8 = 0; u8 < 8; ++u8) {
+            const int mh = 8 * hb + u8;
+            kur[(2 * mh + sl) * F_LD + j] = static_cast<_Float16>(hb ? x16[8 + u8] : x16[u8]);
+        }
+        if (tid < T8) {
+            float nv = 0.0f;
 #pragma unroll
-        for (int f8 = 0; f8 < 8; ++f8) nv += vpart[f8][tid];
-        reinterpret_cast<float*>(kut + KU8_NRM)[tid] = nv;
-    } else if (tid < T8 + NCHK) {   // row padding of the projections
-        *reinterpret_cast<uint4*>(kut + (tid - T8) * F_LD * 2 + T8 * 2) = make_uint4(0, 0, 0, 0);
-    } else if (tid < T8 + NCHK + 16) {   // tail after the norms
-        *reinterpret_cast<uint4*>(kut + KU8_NRM + T8 * 4 + (tid - T8 - NCHK) * 16) = make_uint4(0, 0, 0, 0);
+            for (int f8 = 0; f8 < 8; ++f8) nv += vpart[f8][j];
+            reinterpret_cast<float*>(kut + KU8_NRM)[j] = nv;
+        }
+    }
+    if (tid < NCHK) {   // row padding of the projections
+        *reinterpret_cast<uint4*>(kut + tid * F_LD * 2 + T8 * 2) = make_uint4(0, 0, 0, 0);
+    } else if (tid < NCHK + 16) {   // tail after the norms
+        *reinterpret_cast<uint4*>(kut + KU8_NRM + T8 * 4 + (tid - NCHK) * 16) = make_uint4(0, 0, 0, 0);
     }
 }
 
