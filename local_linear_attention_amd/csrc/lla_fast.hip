@@ -66,6 +66,12 @@ constexpr int M_LD = MT + 8;             // feature-major fp16 row (elements), 1
 // padding that keeps the 16-byte operand reads conflict-free), 18 KiB per tile.
 constexpr int PACK_TILE_BYTES = 2 * FD * M_LD * 2;
 constexpr int M_NBUF = 3;                // tile ring: compute t, t+1 landing, t+2 in flight
+// Column of key jt (0..63) in the value half of the tile image and in the check image: within
+// each 32-key group, key 16h + 4g + r sits at 8g + 4h + r, so that the 8 keys the MFMA
+// K-slot g takes from the probe weights (keys 4g.. and 16 + 4g..) are one 16-byte read.
+__host__ __device__ constexpr int vcol(int jt) {
+    return (jt & ~31) | (((jt >> 2) & 3) << 3) | (((jt >> 4) & 1) << 2) | (jt & 3);
+}
 constexpr int ANCHOR_SLICES = 16;        // key slices of the per-head anchor sums
 // Keys of one tile key-major (bf16 as given, rows of KM_LD halves: 64 features + 8 of
 // padding), the score operand of the row-max kernel, 9 KiB per tile.
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
         vv[0] = static_cast<_Float16>(za ? 0.0f : __uint_as_float(hi ? (vwa & 0xffff0000u) : (vwa << 16)) - av);
         vv[1] = static_cast<_Float16>(zb ? 0.0f : __uint_as_float(hi ? (vwb & 0xffff0000u) : (vwb << 16)) - av);
         dst[row * (M_LD / 2) + pr] = __builtin_bit_cast(uint32_t, kk);
-        dst[(FD + row) * (M_LD / 2) + pr] = __builtin_bit_cast(uint32_t, vv);
+        dst[(FD + row) * (M_LD / 2) + vcol(2 * pr) / 2] = __builtin_bit_cast(uint32_t, vv);
         if (pr < (M_LD - MT) / 2) {   // row padding
             dst[row * (M_LD / 2) + MT / 2 + pr] = 0u;
             dst[(FD + row) * (M_LD / 2) + MT / 2 + pr] = 0u;
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(256) void lla_pack_kernel(const uint16_t* __restric
         walsh_transform(x8);
         _Float16* kur = reinterpret_cast<_Float16*>(kut);
 #pragma unroll
-        for (int mh = 0; mh < 8; ++mh) kur[(4 * mh + q4) * M_LD + j] = static_cast<_Float16>(x8[mh]);
+        for (int mh = 0; mh < 8; ++mh) kur[(4 * mh + q4) * M_LD + vcol(j)] = static_cast<_Float16>(x8[mh]);
         if (q4 == 0) {
             float nv = 0.0f;
 #pragma unroll
@@ -1157,10 +1163,7 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int fv = 0; fv < 4; ++fv) {
-                    const _Float16* vr = VI + (fv * 16 + c) * M_LD + 32 * ks + 4 * g;
-                    const half4 v0 = *reinterpret_cast<const half4*>(vr);
-                    const half4 v1 = *reinterpret_cast<const half4*>(vr + 16);
-                    const half8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const half8 vb = *reinterpret_cast<const half8*>(VI + (fv * 16 + c) * M_LD + 32 * ks + 8 * g);
 #pragma unroll
                     for (int st = 0; st < P_SETS; ++st) {
                         const half8 pa = __builtin_shufflevector(p[st][2 * ks], p[st][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1169,10 +1172,7 @@ __global__ __launch_bounds__(P_WAVES * 64, 2) void lla_probe_kernel(
                 }
 #pragma unroll
                 for (int db = 0; db < NCHK / 16; ++db) {
-                    const _Float16* ur = UI + (db * 16 + c) * M_LD + 32 * ks + 4 * g;
-                    const half4 u0 = *reinterpret_cast<const half4*>(ur);
-                    const half4 u1 = *reinterpret_cast<const half4*>(ur + 16);
-                    const half8 ub = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const half8 ub = *reinterpret_cast<const half8*>(UI + (db * 16 + c) * M_LD + 32 * ks + 8 * g);
 #pragma unroll
                     for (int st = 0; st < P_SETS; ++st) {
                         const half8 pa = __builtin_shufflevector(p[st][2 * ks], p[st][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
