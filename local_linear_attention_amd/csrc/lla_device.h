@@ -26,6 +26,13 @@ constexpr float LOG2E = 1.4426950408889634f;
 // kernel.
 constexpr int NCHK = 32;
 constexpr int KU_TILE_BYTES = 5 * 1024;
+// Column of key jt (0..63 within a 64-key tile) in the feature-major value images and check
+// images the probe passes read: within each 32-key group, key 16h + 4g + r sits at
+// 8g + 4h + r, so that the 8 keys MFMA K-slot g takes from the probe weights (keys 4g..
+// and 16 + 4g.. of the score layout) are one 16-byte read.
+__host__ __device__ constexpr int vcol(int jt) {
+    return (jt & ~31) | (((jt >> 2) & 3) << 3) | (((jt >> 4) & 1) << 2) | (jt & 3);
+}
 constexpr float CHK_TOL = 1.5e-3f;
 
 // Compiler fence for wave-private LDS exchanges: a lane reads words that other lanes of

@@ -66,12 +66,6 @@ constexpr int M_LD = MT + 8;             // feature-major fp16 row (elements), 1
 // padding that keeps the 16-byte operand reads conflict-free), 18 KiB per tile.
 constexpr int PACK_TILE_BYTES = 2 * FD * M_LD * 2;
 constexpr int M_NBUF = 3;                // tile ring: compute t, t+1 landing, t+2 in flight
-// Column of key jt (0..63) in the value half of the tile image and in the check image: within
-// each 32-key group, key 16h + 4g + r sits at 8g + 4h + r, so that the 8 keys the MFMA
-// K-slot g takes from the probe weights (keys 4g.. and 16 + 4g..) are one 16-byte read.
-__host__ __device__ constexpr int vcol(int jt) {
-    return (jt & ~31) | (((jt >> 2) & 3) << 3) | (((jt >> 4) & 1) << 2) | (jt & 3);
-}
 constexpr int ANCHOR_SLICES = 16;        // key slices of the per-head anchor sums
 // Keys of one tile key-major (bf16 as given, rows of KM_LD halves: 64 features + 8 of
 // padding), the score operand of the row-max kernel, 9 KiB per tile.

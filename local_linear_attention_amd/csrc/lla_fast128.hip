@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
             vsb = fmaf(static_cast<float>(vb[e]), static_cast<float>(vb[e]), vsb);
             const h16x2 kk = {ca[e], cb[e]}, vv = {va[e], vb[e]};
             kft[f * (F_LD / 2) + pr] = __builtin_bit_cast(uint32_t, kk);
-            vft[f * (F_LD / 2) + pr] = __builtin_bit_cast(uint32_t, vv);
+            vft[f * (F_LD / 2) + vcol(2 * pr) / 2] = __builtin_bit_cast(uint32_t, vv);
             if (pr < (F_LD - T8) / 2) {
                 kft[f * (F_LD / 2) + T8 / 2 + pr] = 0u;
                 vft[f * (F_LD / 2) + T8 / 2 + pr] = 0u;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void lla8_pack_kernel(const uint16_t* __restri
 #pragma unroll
         for (int u8 = 0; u8 < 8; ++u8) {
             const int mh = 8 * hb + u8;
-            kur[(2 * mh + sl) * F_LD + j] = static_cast<_Float16>(hb ? x16[8 + u8] : x16[u8]);
+            kur[(2 * mh + sl) * F_LD + vcol(j)] = static_cast<_Float16>(hb ? x16[8 + u8] : x16[u8]);
         }
         if (tid < T8) {
             float nv = 0.0f;
@@ -1066,10 +1066,7 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int fv = 0; fv < 8; ++fv) {
-                    const _Float16* vr = VI + (fv * 16 + c) * F_LD + 32 * ks + 4 * g;
-                    const half4 v0 = *reinterpret_cast<const half4*>(vr);
-                    const half4 v1 = *reinterpret_cast<const half4*>(vr + 16);
-                    const half8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const half8 vb = *reinterpret_cast<const half8*>(VI + (fv * 16 + c) * F_LD + 32 * ks + 8 * g);
 #pragma unroll
                     for (int st = 0; st < P8_SETS; ++st) {
                         const half8 pa = __builtin_shufflevector(p[st][2 * ks], p[st][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1078,10 +1075,7 @@ __global__ __launch_bounds__(256, 1) void lla8_probe_kernel(
                 }
 #pragma unroll
                 for (int db = 0; db < NCHK / 16; ++db) {
-                    const _Float16* ur = UI + (db * 16 + c) * F_LD + 32 * ks + 4 * g;
-                    const half4 u0 = *reinterpret_cast<const half4*>(ur);
-                    const half4 u1 = *reinterpret_cast<const half4*>(ur + 16);
-                    const half8 ub = __builtin_shufflevector(u0, u1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const half8 ub = *reinterpret_cast<const half8*>(UI + (db * 16 + c) * F_LD + 32 * ks + 8 * g);
 #pragma unroll
                     for (int st = 0; st < P8_SETS; ++st) {
                         const half8 pa = __builtin_shufflevector(p[st][2 * ks], p[st][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
