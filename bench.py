@@ -65,6 +65,7 @@ KERNEL_BOUND = {
     "lla_refine_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_cg_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_short_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla8_short_kernel": ("mfma", PEAK["mfma_f64_TFLOPs"]),
     "lla_rowmax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_anchor_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
@@ -99,8 +100,9 @@ PATH_KERNELS = {
     # the last launch recomputes in fp64 the rows the range guard and the checks hand back
     "fast": ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel",
              "lla_probe_kernel", "lla_refine_kernel"],
-    # d = 128: rows i < 4d on the fp64 kernel, the rest on the d = 128 matrix-core kernels
-    "fast128": ["lla_exact_kernel", "lla8_anchor_kernel", "lla8_pack_kernel", "lla8_rowmax_kernel",
+    # d = 128: rows i < 4d on the fp64 short-row kernel, the rest on the d = 128 matrix-core
+    # kernels
+    "fast128": ["lla8_short_kernel", "lla8_anchor_kernel", "lla8_pack_kernel", "lla8_rowmax_kernel",
                 "lla8_keymom_kernel", "lla8_probe_kernel", "lla_exact_list_kernel"],
 }
 
@@ -128,23 +130,27 @@ def pair_count(BH, lo, hi):
 
 def kernel_flops(name, B, H, n, d, path):
     """Algorithmic flops of one launch of a kernel, in the formulation that kernel executes.
-    The exact path and the fast path's fp64 rows form the value-key cross moment (NS); the
-    fast path's other rows apply it through the probe pass (min).  Fast path, d = 64: rows
-    [0, 2d) fp64 short-row kernel; the row-max kernel owns the score term of rows >= 2d; rows
-    [2d, n) the key-moment kernel (first moments, C_kk, solve) and the probe kernel (probe
-    scores and the weighted value sum); d = 128 the same with 4d for 2d.  Scores a kernel
-    recomputes, and the probe's check sums (a verification, not part of the estimator), are
-    not counted."""
+    The exact and CG paths form the value-key cross moment (NS); the fast path applies it
+    through a pass over the values (min), its fp64 short rows included.  Fast path, d = 64:
+    rows [0, 3d) on the fp64 short-row blocks of the rows kernel; the row-max kernel owns the
+    score term of rows >= 3d; rows [3d, n) the key-moment blocks (first moments, C_kk, solve)
+    and the probe kernel (probe scores and the weighted value sum); d = 128 the same with 4d
+    for 3d and its own short-row kernel.  Scores a kernel recomputes, and the probe's check
+    sums (a verification, not part of the estimator), are not counted."""
     BH = B * H
-    # fp64 rows (NS): i < 3d at d = 64 (short-row blocks), i < 4d at d = 128 (fp64 kernel); the
-    # rest key moments + probe (min)
+    # fp64 short rows: i < 3d at d = 64 (short-row blocks), i < 4d at d = 128 (short-row
+    # kernel); the rest key moments + probe
     row0 = rowp = (min(n, 4 * d) if d == 128 else min(n, 3 * d)) if path == "fast" else n
     per_query = d ** 3 / 3 + 4 * d * d + 2 * d
     moments = 2 * (1 + 2 * d) + d * (d + 1)
-    if name in ("lla_exact_kernel", "lla_short_kernel", "lla_cg_kernel"):
+    if name in ("lla_exact_kernel", "lla_cg_kernel"):
         # the CG kernel is credited with the direct formulation's count, so that both fp64
         # paths report comparable rates (its own work depends on the iteration counts)
         return pair_count(BH, 0, row0) * (2 * d + moments + 2 * d * d) + BH * row0 * per_query
+    if name in ("lla_short_kernel", "lla8_short_kernel"):
+        # fp64 short rows in the probe form: per pair the score, first moments, C_kk, then
+        # u_j (2d) and the weighted value sums (2d + 2); per query the solve
+        return pair_count(BH, 0, row0) * (2 * d + moments + 4 * d + 2) + BH * row0 * (d ** 3 / 3 + 2 * d * d)
     if name in ("lla_anchor_kernel", "lla_pack_kernel", "lla8_anchor_kernel", "lla8_pack_kernel"):
         return 0                      # data movement only (K, V summed and repacked once)
     if name in ("lla_exact_list_kernel", "lla_refine_kernel"):
@@ -783,7 +789,7 @@ def main():
         config_text = (f"{w.name}: B{w.B} H{w.H} n{w.n} d{w.d} {w.dtype} inputs, h={w.h:g}, "
                        f"lambda={w.lam:g}")
         split = "4d" if w.d == 128 else "3d"
-        flop_count = {"formulation": (f"NS for rows i < {split}, min (probe pass) for rows i >= {split}"
+        flop_count = {"formulation": (f"min (probe form) for every row; rows i < {split} in fp64"
                                       if path == "fast" else "NS"),
                       "flops": flops,
                       "F_NS": alg_flops(w.B, w.H, w.n, w.d, "NS"),

@@ -1207,7 +1207,7 @@ hipError_t launch_fast128(const Problem& p, void* workspace) {
     const int n = static_cast<int>(p.n);
     const int BH = static_cast<int>(p.B * p.H);
     const int row0 = fast8_row0(p.n);
-    if ((err = launch_exact(p, row0)) != hipSuccess) return err;
+    if ((err = launch_short128(p, row0)) != hipSuccess) return err;
     if (n <= row0) return hipSuccess;
     if ((err = ensure_attributes8()) != hipSuccess) return err;
     const float sl2 = static_cast<float>(LOG2E / p.h);

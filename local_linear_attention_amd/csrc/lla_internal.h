@@ -34,6 +34,10 @@ hipError_t launch_exact(const Problem& p, int rows);
 // The same fp64 computation for the *count rows in `list` (entries bh * n + i, device
 // memory, count read by the kernel), over `blocks` workgroups.
 hipError_t launch_exact_list(const Problem& p, const int* list, const int* count, int blocks);
+// Rows 0 .. rows-1 (rows <= 4d) of every head for bf16 inputs with d = 128, in fp64: one
+// workgroup per row, C_kk on the fp64 matrix cores, the cross moment applied through one pass
+// over the values (lla_short128.hip).
+hipError_t launch_short128(const Problem& p, int rows);
 
 // fp64 path with each query's system solved by conjugate gradient over its prefix (no
 // d x d state): every (dtype, d).  Workspace (cg_workspace_bytes): the count of rows whose
