@@ -40,30 +40,40 @@ constexpr int S8_MAXK = 4 * SD;         // longest prefix: rows i < 4d
 constexpr int S8_CH = 64;               // keys per staged chunk
 constexpr int S8_KLD = SD + 16;         // bf16 row stride (halves): 72 words, so that the 4 keys
                                         // of an MFMA step fall on distinct bank octets
-constexpr int S8_TLD = SD + 1;          // fp64 row stride of the transfer buffer
 constexpr int S8_CB = SD + 2;           // one pivot column (128 rows) + the pivot's z (+ pad)
 constexpr int S8_ALD = 65;              // fp64 row stride: wave 1's multipliers in transit
 
-// LDS (bytes): staged chunks (then the solve's buffers), then the per-row vectors.
+// LDS (bytes), sized for two workgroups per CU.  Region M is reused phase by phase:
+//   pass 1:   K chunk | V chunk | scores s_j            | partial sums (2 x 128)
+//   pass 2:   K chunk |         | sqrt(w_j)
+//   transfer: the 36 upper 16x16 blocks of C_kk + ridge (2 KiB each, XOR-swizzled columns)
+//   solve:    pivot columns | wave 1's multipliers | phase 2 pivot rows
+//   pass 3:   K chunk | V chunk |                      | partial sums
+// then the vectors q, kbar, vbar, y, the chunk's w_j u_j, and four reduction slots.
 constexpr int S8_KC = 0;
 constexpr int S8_VC = S8_KC + S8_CH * S8_KLD * 2;
-constexpr int S8_STAGE = S8_VC + S8_CH * S8_KLD * 2;
-//   solve buffers inside the staging area:
-constexpr int S8_T = 0;                                   // 16 matrix rows in transit
-constexpr int S8_COL = S8_T + 16 * S8_TLD * 8;            // two pivot columns (alternating)
-constexpr int S8_A21 = 0;                                 // wave 1's rows (after phase 1)
+constexpr int S8_SC = S8_VC + S8_CH * S8_KLD * 2;         // scores, then sqrt(w_j)
+constexpr int S8_PART = S8_SC + S8_MAXK * 8;              // 2 x 128 partial sums
+constexpr int S8_BLK = 0;                                 // the 36 blocks
+constexpr int S8_COL = 0;                                 // two pivot columns (alternating)
+constexpr int S8_A21 = 4096;                              // wave 1's rows (after phase 1)
 constexpr int S8_XW = S8_A21 + 64 * S8_ALD * 8;           // phase 2 pivot rows, one per wave
-static_assert(S8_COL + 2 * S8_CB * 8 <= S8_STAGE && S8_XW + 4 * 64 * 8 <= S8_STAGE,
-              "solve buffers fit in the staging area");
-constexpr int S8_QS = S8_STAGE;                           // q (fp64)
-constexpr int S8_SC = S8_QS + SD * 8;                     // scores, then weights w_j
-constexpr int S8_SW = S8_SC + S8_MAXK * 8;                // sqrt(w_j) (zero past the prefix)
-constexpr int S8_KB = S8_SW + S8_MAXK * 8;                // kbar
+constexpr int S8_MSZ = 36 * 256 * 8;
+static_assert(S8_PART + 2 * SD * 8 <= S8_MSZ && S8_COL + 2 * S8_CB * 8 <= S8_A21 && S8_XW + 4 * 64 * 8 <= S8_MSZ,
+              "the phases' buffers fit in region M");
+constexpr int S8_QS = S8_MSZ;                             // q (fp64)
+constexpr int S8_KB = S8_QS + SD * 8;                     // kbar
 constexpr int S8_VB = S8_KB + SD * 8;                     // vbar
 constexpr int S8_YS = S8_VB + SD * 8;                     // y
 constexpr int S8_WU = S8_YS + SD * 8;                     // chunk weights, then w_j u_j of a chunk
-constexpr int S8_RED = S8_WU + S8_CH * 8;                 // reductions: 2 x 128 partials
-constexpr int S8_SMEM = S8_RED + 2 * SD * 8;
+constexpr int S8_RED = S8_WU + S8_CH * 8;                 // four reduction slots
+constexpr int S8_SMEM = S8_RED + 8 * 8;
+static_assert(2 * S8_SMEM <= 160 * 1024, "two workgroups per CU");
+
+// Block (I, J), I <= J, of the upper 8 x 8 block triangle, and the LDS double index of its
+// entry (m, n): rows of 16, column n stored at n ^ m (conflict-free for row and column reads).
+__host__ __device__ constexpr int s8_bidx(int I, int J) { return I * 8 - I * (I - 1) / 2 + (J - I); }
+__device__ __forceinline__ int s8_elem(int I, int J, int m, int nn) { return s8_bidx(I, J) * 256 + m * 16 + (nn ^ m); }
 
 // Upper 16x16 blocks (I, J) of C_kk per wave: 9 each, so that waves 0 and 1 need 4 feature
 // blocks of R and waves 2 and 3 at most 7.
@@ -102,6 +112,13 @@ __device__ __forceinline__ void s8_chunk(double4v (&acc)[9], const uint16_t* __r
                  :                                                                                 \
                  : "memory")
 
+// 1 / x from the hardware reciprocal and one Newton step (a pivot's multiplier needs no
+// correctly rounded division; the step brings the estimate to full fp64 precision).
+__device__ __forceinline__ double s8_rcp(double x) {
+    const double r = __builtin_amdgcn_rcp(x);
+    return fma(r, fma(-x, r, 1.0), r);
+}
+
 __device__ __forceinline__ double bf2d(uint16_t b) { return static_cast<double>(bf16_bits_to_f32(b)); }
 
 __device__ __forceinline__ double wave_max_dd(double x) {
@@ -115,7 +132,7 @@ __device__ __forceinline__ double wave_sum_dd(double x) {
     return x;
 }
 
-__global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 2) void lla8_short_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          float* __restrict__ out, int n, int rows, int BH,
@@ -134,7 +151,8 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
     uint16_t* VC = reinterpret_cast<uint16_t*>(smem + S8_VC);
     double* QS = reinterpret_cast<double*>(smem + S8_QS);
     double* SC = reinterpret_cast<double*>(smem + S8_SC);
-    double* SW = reinterpret_cast<double*>(smem + S8_SW);
+    double* SW = SC;   // sqrt(w_j) replaces the scores after pass 1
+    double* PART = reinterpret_cast<double*>(smem + S8_PART);
     double* KB = reinterpret_cast<double*>(smem + S8_KB);
     double* VB = reinterpret_cast<double*>(smem + S8_VB);
     double* YS = reinterpret_cast<double*>(smem + S8_YS);
@@ -214,19 +232,18 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
     double wpart = 0.0;
     for (int j = tid; j < S8_MAXK; j += 256) {
         const double wj = j < nk ? exp(SC[j] - m) : 0.0;
-        SC[j] = wj;
         SW[j] = sqrt(wj);
         wpart += wj;
     }
     const double omega = block_sum(wpart);
     __syncthreads();
-    RED[par * SD + f] = ka;
+    PART[par * SD + f] = ka;
     __syncthreads();
-    if (tid < SD) KB[tid] = (RED[tid] + RED[SD + tid]) / omega;
+    if (tid < SD) KB[tid] = (PART[tid] + PART[SD + tid]) / omega;
     __syncthreads();
-    RED[par * SD + f] = va;
+    PART[par * SD + f] = va;
     __syncthreads();
-    if (tid < SD) VB[tid] = (RED[tid] + RED[SD + tid]) / omega;
+    if (tid < SD) VB[tid] = (PART[tid] + PART[SD + tid]) / omega;
     __syncthreads();
 
     // ---- pass 2: C_kk, upper blocks (I, J) of this wave, 4 keys per MFMA step
@@ -285,29 +302,24 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
     // a panel unrolled (code that stays in the instruction cache); between panels the row
     // rotates by 16 entries, so that the active panel always sits in cr[0..15] and no
     // register is indexed at run time.  After four panels the row is back in order.
-    double* T = reinterpret_cast<double*>(smem + S8_T);
-    double cr[64];
-#pragma unroll
-    for (int t = 0; t < 64; ++t) cr[t] = 0.0;
+    double* BL = reinterpret_cast<double*>(smem + S8_BLK);
     const int colb = w < 2 ? 0 : 64;                  // first column this wave holds
     const int row = lane + (w == 0 ? 0 : 64);          // its row
-    for (int R = 0; R < 8; ++R) {
-        __syncthreads();   // T free (the previous round's readers are done; pass 2 done with KC)
+    __syncthreads();   // pass 2 done with region M
 #pragma unroll
-        for (int b = 0; b < 9; ++b) {
-            const int I = s8_bi[w][b], J = s8_bj[w][b];
+    for (int b = 0; b < 9; ++b) {
+        const int I = s8_bi[w][b], J = s8_bj[w][b];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // block (I, J), register r: C[16 I + 4 r + g][16 J + c]
-                if (I == R) T[(4 * r + g) * S8_TLD + 16 * J + c] = acc[b][r];
-                else if (J == R) T[c * S8_TLD + 16 * I + 4 * r + g] = acc[b][r];
-            }
-        }
-        __syncthreads();
-        if ((row >> 4) == R) {
-            const double* src = T + (row & 15) * S8_TLD + colb;
+        for (int r = 0; r < 4; ++r) BL[s8_elem(I, J, 4 * r + g, c)] = acc[b][r];   // C[16 I + 4r + g][16 J + c]
+    }
+    __syncthreads();
+    double cr[64];
+    {
+        const int I = row >> 4, m = row & 15;
 #pragma unroll
-            for (int t = 0; t < 64; ++t) cr[t] = src[t];
+        for (int t = 0; t < 64; ++t) {
+            const int J = (colb + t) >> 4, nn = t & 15;   // J wave-uniform
+            cr[t] = BL[I <= J ? s8_elem(I, J, m, nn) : s8_elem(J, I, nn, m)];
         }
     }
     auto rotate16 = [&] {   // cr[t] <- cr[(t + 16) % 64]
@@ -328,6 +340,7 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
     // zero multiplier, so that no branch splits the row's registers).  In panel P, entry group
     // G (cr[16 G ..]) holds the original columns of panel (P + G) mod 4.
     double* CB = reinterpret_cast<double*>(smem + S8_COL);
+    __syncthreads();   // every row read out of the blocks before the pivot columns overwrite them
     for (int P = 0; P < 4; ++P) {
 #pragma unroll
         for (int pp = 0; pp < 16; ++pp) {
@@ -339,7 +352,7 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
             }
             __syncthreads();
             const double piv = cb[p];
-            const double inv = piv > thresh ? 1.0 / piv : 0.0;
+            const double inv = piv > thresh ? s8_rcp(piv) : 0.0;
             const double fr = row > p ? cb[row] * inv : 0.0;
             z = fma(-fr, cb[SD], z);
             const double frl = colb != 0 ? fr : 0.0;
@@ -371,7 +384,7 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
                 const double cp = P == 3 ? cr[48 + pp] : P == 2 ? cr[32 + pp] : P == 1 ? cr[16 + pp] : cr[pp];
                 const double dp = __shfl(cp, p);
                 const double zp = __shfl(zz, p);
-                const double yp = dp > thresh ? zp / dp : 0.0;
+                const double yp = dp > thresh ? zp * s8_rcp(dp) : 0.0;
                 ylane = lane == p ? yp : ylane;
                 zz = fma(-cp, yp, zz);
             }
@@ -398,7 +411,7 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
                 xw[lane] = cp;
                 LDS_FENCE();
                 const double piv = xw[p];
-                const double inv = piv > thresh ? 1.0 / piv : 0.0;
+                const double inv = piv > thresh ? s8_rcp(piv) : 0.0;
                 const double fr = act && lane > p ? cp * inv : 0.0;
                 const double zp = __shfl(z, p);
                 z = fma(-fr, zp, z);
@@ -444,15 +457,20 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
             }
             __syncthreads();
             const int j = ch * S8_CH + sk;
-            double u = 0.0;
+            double u = 0.0, sj = 0.0;   // (k_j - kbar).y and q.k_j over this thread's 32 features
 #pragma unroll 8
             for (int e = 0; e < 32; ++e) {
                 const int a = 32 * sq + e;
-                u = fma(bf2d(KC[sk * S8_KLD + a]) - KB[a], YS[a], u);
+                const double kv = bf2d(KC[sk * S8_KLD + a]);
+                u = fma(kv - KB[a], YS[a], u);
+                sj = fma(QS[a], kv, sj);
             }
             u += __shfl_xor(u, 1);
             u += __shfl_xor(u, 2);
-            if (sq == 0) WU[sk] = j < nk ? SC[j] * u : 0.0;
+            sj += __shfl_xor(sj, 1);
+            sj += __shfl_xor(sj, 2);
+            // w_j recomputed with pass 1's arithmetic (the same sum order, then exp(s - m))
+            if (sq == 0) WU[sk] = j < nk ? exp(sj * inv_h - m) * u : 0.0;
             __syncthreads();
             for (int kk = par; kk < S8_CH; kk += 2) {
                 const double wu = WU[kk];
@@ -462,14 +480,14 @@ __global__ __launch_bounds__(256) void lla8_short_kernel(const uint16_t* __restr
         }
     }
     __syncthreads();
-    RED[par * SD + f] = acc_o;
+    PART[par * SD + f] = acc_o;
     __syncthreads();
-    const double accf = RED[f] + RED[SD + f];
+    const double accf = PART[f] + PART[SD + f];
     __syncthreads();
-    RED[par * SD + f] = swu;
+    PART[par * SD + f] = swu;
     __syncthreads();
     if (tid < SD) {
-        const double sw_all = RED[f] + RED[SD + f];
+        const double sw_all = PART[f] + PART[SD + f];
         out[base + static_cast<int64_t>(i) * SD + f] = static_cast<float>(VB[f] - (accf - VB[f] * sw_all));
     }
 }
