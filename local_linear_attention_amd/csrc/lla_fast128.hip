@@ -648,12 +648,17 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
     auto sbuf = [&](int tt) { return smem + K8_SRING + (tt % K8_NBUF) * KM_BYTES; };
     // Scores of key block w (16 keys) of tile tt from its score image: lane (g, c) register
     // r = key 16 w + 4 g + r, query c; sqrt-weights and fp16 weights into the key buffer of tt.
-    auto scores = [&](int tt) {
+    // The MFMAs are issued before the tile's key moments and their results used after the
+    // first half, so that the chain's latency hides behind the moment MFMAs.
+    auto scores_mfma = [&](int tt) {
         const unsigned char* sb = sbuf(tt);
         float4v s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             s = mfma_bf16(*reinterpret_cast<const bf16x8*>(sb + (16 * wu + c) * (K_LD * 2) + 64 * ks + 16 * g), qf[ks], s);
+        return s;
+    };
+    auto scores_store = [&](float4v s, int tt) {
         const int j0 = tt * T8;
         float e[4];
 #pragma unroll
@@ -734,28 +739,68 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
         __builtin_amdgcn_s_barrier();
         LDS_FENCE();
     };
-    // One 32-key half of tile t: R = sw (k - a) (one rounding, packed fp16 multiplies, in
+    // Tile t, in two 32-key halves: R = sw (k - a) (one rounding, packed fp16 multiplies, in
     // place over the key rows), the 36 upper blocks of R^T R and the block sums of the 8
-    // queries for feature block w.
-    auto compute = [&](int t, int sub) {
+    // queries for feature block w.  The key rows of a half are read in two groups of four
+    // feature blocks, each group's reads issued while the MFMAs of the previous group run:
+    // group B of a half during the blocks within group A, group A of the next half during
+    // the blocks within group B (the fences keep the reads from being hoisted further).
+    auto compute_tile = [&](int t, bool second, auto&& after_first) {
         const unsigned char* cur = kbuf(t);
         const _Float16* Kt = reinterpret_cast<const _Float16*>(cur);
         const _Float16* Sw = reinterpret_cast<const _Float16*>(cur + K8_SW);
         const _Float16* Sw2 = reinterpret_cast<const _Float16*>(cur + K8_SW2);
-        const int ko = 32 * sub + 8 * g;
-        half8 rk[8];
+        half8 ra[4], rb[4];
+        auto read_group = [&](half8 (&r)[4], int fb0, int ko) {
 #pragma unroll
-        for (int fb = 0; fb < 8; ++fb) rk[fb] = *reinterpret_cast<const half8*>(Kt + (fb * 16 + c) * F_LD + ko);
-        const half8 sw = *reinterpret_cast<const half8*>(Sw + wu * F_LD + ko);
-        const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * F_LD + ko);
-        const half8 kw = *reinterpret_cast<const half8*>(Kt + (wu * 16 + c) * F_LD + ko);
+            for (int fb = 0; fb < 4; ++fb) r[fb] = *reinterpret_cast<const half8*>(Kt + ((fb0 + fb) * 16 + c) * F_LD + ko);
+        };
+        read_group(ra, 0, 8 * g);
 #pragma unroll
-        for (int fb = 0; fb < 8; ++fb) rk[fb] = rk[fb] * sw;
+        for (int sub = 0; sub < 2; ++sub) {
+            if (sub == 1 && !second) break;   // block-uniform: past every query of the block
+            const int ko = 32 * sub + 8 * g;
+            const half8 sw = *reinterpret_cast<const half8*>(Sw + wu * F_LD + ko);
+            const half8 w8 = *reinterpret_cast<const half8*>(Sw2 + c * F_LD + ko);
+            const half8 kw = *reinterpret_cast<const half8*>(Kt + (wu * 16 + c) * F_LD + ko);
 #pragma unroll
-        for (int I = 0; I < 8; ++I)
+            for (int fb = 0; fb < 4; ++fb) ra[fb] = ra[fb] * sw;
+            LDS_FENCE();
+            read_group(rb, 4, ko);
 #pragma unroll
-            for (int J = I; J < 8; ++J) ckk[ub8(I, J)] = mfma_f16(rk[I], rk[J], ckk[ub8(I, J)]);
-        sk = mfma_f16(w8, kw, sk);
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int J = I; J < 4; ++J) ckk[ub8(I, J)] = mfma_f16(ra[I], ra[J], ckk[ub8(I, J)]);
+            // The blocks within group A are issued before group B's rows are waited for.
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int J = I; J < 4; ++J) asm volatile("" : "+v"(ckk[ub8(I, J)]));
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) asm volatile("" : "+v"(rb[fb]));
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) rb[fb] = rb[fb] * sw;
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int J = 4; J < 8; ++J) ckk[ub8(I, J)] = mfma_f16(ra[I], rb[J - 4], ckk[ub8(I, J)]);
+            sk = mfma_f16(w8, kw, sk);
+            if (sub == 0) after_first();
+            if (sub == 0 && second) {
+                // the last uses of group A's rows are issued before the next half's rows land
+                // in their registers
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int J = 4; J < 8; ++J) asm volatile("" : "+v"(ckk[ub8(I, J)]));
+                LDS_FENCE();
+                read_group(ra, 0, 32 + 8 * g);
+            }
+#pragma unroll
+            for (int I = 4; I < 8; ++I)
+#pragma unroll
+                for (int J = I; J < 8; ++J) ckk[ub8(I, J)] = mfma_f16(rb[I - 4], rb[J - 4], ckk[ub8(I, J)]);
+        }
     };
     // Prologue: score image 0, then (key image s + 2, score image s + 3) for s = -2, -1 as in
     // the loop.  Once score images 0 and 1 and key image 0 have landed, the scores of tile 0.
@@ -766,15 +811,17 @@ __global__ __launch_bounds__(KW8 * 64, 1) void lla8_keymom_kernel(
     issue_s(2);
     __builtin_amdgcn_s_waitcnt(K8_VM | (0x7 << 4) | (0xF << 8));   // s0, k0, s1 landed
     ring_barrier();
-    if (scorer) scores(0);
+    if (scorer) scores_store(scores_mfma(0), 0);
     ring_barrier();
     // Step t: key image t and its weights are in LDS, and score image t + 1.
     for (int t = 0; t < ntiles; ++t) {
         issue_k(t + 2);
         issue_s(t + 3);
-        if (scorer) scores(t + 1);
-        compute(t, 0);
-        if (t * T8 + 32 <= last) compute(t, 1);
+        float4v sv = {0.f, 0.f, 0.f, 0.f};
+        if (scorer) sv = scores_mfma(t + 1);
+        compute_tile(t, t * T8 + 32 <= last, [&] {
+            if (scorer) scores_store(sv, t + 1);
+        });
         wait_tiles();   // key image t + 1 and score image t + 2
         ring_barrier();
     }
