@@ -452,7 +452,7 @@ constexpr int GS_QS = 16 * GS_LD + 16;       // query stride: the 4 queries' row
 constexpr int K_SOLVE_FLOATS = KQ * GS_QS + KQ * FD;   // per wave: staging + pivots
 constexpr int K_SOLVE_BYTES = K_SOLVE_FLOATS * 4 * B_WAVES;
 constexpr int K_MEAN_OFF = K_SOLVE_BYTES > M_NBUF * K_BUF ? K_SOLVE_BYTES : M_NBUF * K_BUF;
-constexpr int K_SMEM = K_MEAN_OFF + (K_BQ * FD + B_WAVES * 16) * 4;
+constexpr int K_SMEM = K_MEAN_OFF + (K_BQ * FD + B_WAVES * 16 + 16) * 4;   // + the check's key scales
 constexpr int P_YLD = 2 * FD;                // per query: yh hi (fp16) | yh lo (fp16)
 constexpr int P_QSC = 8;                     // per query: gamma, 2^-e, 1/omega', dropped-pivot flag,
                                              // weighted mean |k - a|^2, 3 unused
@@ -862,13 +862,13 @@ __device__ __forceinline__ void keymom_block(
     for (int t = 0; t < B_WAVES; ++t) om2 += omp[t * 16 + qlG];
     const float iom2 = 1.0f / om2;   // >= 1: the query's top-scoring key has weight 1
     const float* mqG = skm + qlG * FD;
-    float zr[4], skv[4], sks[4], yr[4];
+    float zr[4], sks[4], yr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int a = l + 16 * j;
-        skv[j] = mqG[a];
-        sks[j] = skv[j] * iom2;
-        zr[j] = fmaf(skv[j], iom2, anc[a]) - bf16_bits_to_f32(q[base + static_cast<int64_t>(iqc) * FD + a]);
+        const float skv = mqG[a];
+        sks[j] = skv * iom2;
+        zr[j] = fmaf(skv, iom2, anc[a]) - bf16_bits_to_f32(q[base + static_cast<int64_t>(iqc) * FD + a]);
     }
     // lambda > 0: drop only pivots that rounding made non-positive; lambda = 0: also drop
     // directions the prefix leaves (numerically) undetermined, below 1e-6 of the largest
@@ -907,10 +907,17 @@ __device__ __forceinline__ void keymom_block(
             for (int r = 0; r < 4; ++r) tr += 4 * g + r == c ? ckk[qq][ublk(I, I)][r] : 0.0f;
         trq[qq] = wave_sum_f(tr);
     }
-    const float trG = G == 0 ? trq[0] : G == 1 ? trq[1] : G == 2 ? trq[2] : trq[3];
-    const float lamG = G == 0 ? lam_q[0] : G == 1 ? lam_q[1] : G == 2 ? lam_q[2] : lam_q[3];
+    // Values needed after the solve go through LDS or are derived again there, so that
+    // nothing but the solve's own state is live across it.
+    float* trs = omp + B_WAVES * 16;   // [query] the check's key scale
+    if (lane == 0) {
+#pragma unroll
+        for (int qq = 0; qq < KQ; ++qq) trs[wu + 4 * qq] = trq[qq];
+    }
     float dropped = 0.0f;
     group_solve(ckk, zr, thr, lam_q, sks, mqG, Sg, yr, g, c, dropped);
+    const float trG = trs[qlG];
+    const float lamG = lambda * exp2f(-mrow[static_cast<int64_t>(bh) * nrows + (iqc - row0)]);
     // Check target: the LLA weights reproduce linear functions of the keys, so applied to the
     // centred keys they give q - a + lambda e^{-m} y (exactly, for the y they were formed
     // with); projected on the NCHK directions, direction t at feature f = l + 16 j carrying
@@ -956,7 +963,7 @@ __device__ __forceinline__ void keymom_block(
         const float ys = yh[j] * sig;
         hi[j] = static_cast<_Float16>(ys);
         lo[j] = static_cast<_Float16>(ys - static_cast<float>(hi[j]));
-        dot = fmaf(skv[j], static_cast<float>(hi[j]) + static_cast<float>(lo[j]), dot);
+        dot = fmaf(mqG[l + 16 * j], static_cast<float>(hi[j]) + static_cast<float>(lo[j]), dot);
     }
     dot = row_sum_f(dot);
     if (iqG < n) {
@@ -1261,8 +1268,10 @@ constexpr int SB_VS = SB_KS + S_KMAX * S_KLD * 2;
 constexpr int SB_QS = SB_VS + S_KMAX * S_KLD * 2;
 constexpr int SB_WS = SB_QS + S_ROWS * FD * 8;
 constexpr int SB_KBS = SB_WS + S_ROWS * S_KMAX * 8;
-constexpr int SB_TB = SB_KBS + S_ROWS * FD * 8;
+constexpr int SB_VBS = SB_KBS + S_ROWS * FD * 8;           // vbar (held in LDS across the solve)
+constexpr int SB_TB = SB_VBS + S_ROWS * FD * 8;
 constexpr int S_SMEM = SB_TB + S_ROWS * 8 * S_TLD * 8;
+static_assert(2 * (S_SMEM > K_SMEM ? S_SMEM : K_SMEM) <= 160 * 1024, "two blocks per CU");
 static_assert(SB_QS % 16 == 0, "fp64 areas stay aligned");
 
 __device__ __forceinline__ void short_block(
@@ -1274,6 +1283,7 @@ __device__ __forceinline__ void short_block(
     double (*qs)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_QS);
     double (*ws)[S_KMAX] = reinterpret_cast<double (*)[S_KMAX]>(smem + SB_WS);
     double (*kbs)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_KBS);
+    double (*vbs)[FD] = reinterpret_cast<double (*)[FD]>(smem + SB_VBS);
     double (*tb)[8 * S_TLD] = reinterpret_cast<double (*)[8 * S_TLD]>(smem + SB_TB);   // 8 rows of C_kk in transit
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1337,6 +1347,7 @@ __device__ __forceinline__ void short_block(
     ka /= omega;
     va /= omega;
     kbs[w][lane] = ka;
+    vbs[w][lane] = va;
     LDS_FENCE();
 
     // ---- C_kk on the matrix cores: upper 16x16 blocks (I, J), I <= J, 4 keys per step.
@@ -1460,7 +1471,8 @@ __device__ __forceinline__ void short_block(
     LDS_FENCE();
     double acc = 0.0;
     for (int j = 0; j <= ic; ++j) acc = fma(ws[w][j], vval(j, lane), acc);
-    if (valid) out[base + static_cast<int64_t>(i) * FD + lane] = static_cast<float>(va - (acc - va * swu));
+    const double vb = vbs[w][lane];
+    if (valid) out[base + static_cast<int64_t>(i) * FD + lane] = static_cast<float>(vb - (acc - vb * swu));
 }
 
 // Rows handed back by the range guard and the checks, in fp64: one wave per listed row, its
