@@ -89,7 +89,8 @@ def workload_arrays(name, **shape):
     return w, q, k, v
 
 
-ENVELOPE_CASES = ("sharp_h", "q_x3", "rank16_keys", "v_2^-16", "v_2^17", "k_offset", "k_x64_h_x64")
+ENVELOPE_CASES = ("sharp_h", "q_x3", "rank16_keys", "v_2^-16", "v_2^17", "k_offset", "k_x64_h_x64",
+                  "k_x1024_h_x1024")
 
 
 def envelope_case(name, case):
@@ -98,7 +99,8 @@ def envelope_case(name, case):
     sharp_h: h / 2 (sharper weights); q_x3: queries x 3 (the same, through q); rank16_keys:
     keys confined to a random 16-dimensional subspace, re-normalised; v_2^-16, v_2^17:
     values scaled out of fp16's normal range either way; k_offset: keys + 4 (a common
-    offset); k_x64_h_x64: keys x 64 with h x 64 (the same weights, large keys)."""
+    offset); k_x64_h_x64, k_x1024_h_x1024: keys x 64 (x 1024) with h scaled alike (the same
+    weights, large keys: the ridge shrinks against the key moments)."""
     import lla_inputs
     shape = dict(B=1, H=2, n=700) if lla_inputs.WORKLOADS[name].d == 128 else dict(B=1, H=2, n=600)
     w, q, k, v = workload_arrays(name, **shape)
@@ -121,6 +123,8 @@ def envelope_case(name, case):
         k = r(k + 4.0)
     elif case == "k_x64_h_x64":
         k, h = r(k * 64.0), w.h * 64.0
+    elif case == "k_x1024_h_x1024":
+        k, h = r(k * 1024.0), w.h * 1024.0
     else:
         raise KeyError(case)
     return w, q, k, v, h, lam

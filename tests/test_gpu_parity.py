@@ -125,7 +125,7 @@ def test_fast_path_d128_extreme_ridge(lam):
 
 @pytest.mark.parametrize("name", ["d24", "long"])
 @pytest.mark.parametrize("case", ["sharp_h", "q_x3", "rank16_keys", "v_2^-16", "v_2^17", "k_offset",
-                                  "k_x64_h_x64"])
+                                  "k_x64_h_x64", "k_x1024_h_x1024"])
 def test_default_path_envelope_every_row(name, case):
     # Inputs outside the RMS-normalised regime: AUTO (the matrix-core path for bf16) must still
     # hold the tolerance on every row, handing the rows its checks reject to the fp64 kernel.
