@@ -50,13 +50,23 @@
 extern "C" {
 #endif
 
+/* The enumerations below are int-sized.  A caller may pass any int where one is expected:
+ * values other than the listed ones are rejected (LLA_ERR_UNSUPPORTED; "unknown status"
+ * from lla_status_string).  C++ gives them int as their fixed underlying type so that such
+ * values are well defined inside the library too. */
+#ifdef __cplusplus
+#define LLA_ENUM_INT : int
+#else
+#define LLA_ENUM_INT
+#endif
+
 /* Element type of q, k and v. */
-typedef enum {
+typedef enum LLA_ENUM_INT {
     LLA_DTYPE_F32 = 0,   /* IEEE binary32 */
     LLA_DTYPE_BF16 = 1   /* bfloat16 (upper half of binary32) */
 } lla_dtype_t;
 
-typedef enum {
+typedef enum LLA_ENUM_INT {
     LLA_OK = 0,
     LLA_ERR_NULL = 1,         /* a required pointer is NULL */
     LLA_ERR_SHAPE = 2,        /* B, H or n < 1, or sizes overflow the index range */
@@ -72,7 +82,7 @@ typedef enum {
 } lla_status_t;
 
 /* Kernel path selection for lla_forward_ex. */
-typedef enum {
+typedef enum LLA_ENUM_INT {
     LLA_PATH_AUTO = 0,   /* fp32 inputs -> EXACT; bf16 inputs -> FAST where built */
     LLA_PATH_EXACT = 1,  /* fp64 accumulation and solve, any supported (dtype, d) */
     LLA_PATH_FAST = 2,   /* matrix-core path for bf16 inputs, d = 64 (n up to 2^22) and d = 128
@@ -101,7 +111,7 @@ typedef enum {
 } lla_path_t;
 
 /*
- * Causal LLA forward (spec signature; dtype and stream appended).
+ * Causal LLA forward (arguments of the operation itself, then dtype and stream).
  *   q, k, v : device pointers to [B, H, n, d] arrays of `dtype`
  *   out     : device pointer to [B, H, n, d] fp32 output
  *   B, H, n : batch, heads, sequence length (>= 1)
@@ -370,9 +380,11 @@ lla_status_t lla_pool_trim(void);
 
 /* Kernel-level timing.  While enabled, every kernel launch of the library is bracketed by
  * HIP events on its stream.  lla_profile_collect waits for the recorded events, writes up to
- * max_entries kernel names (static strings) and durations in milliseconds in launch order,
- * returns how many it wrote, and clears the record.  Meant for single-threaded measurement;
- * lla_profile_enable returns the previous setting. */
+ * max_entries kernel names (static strings) and durations in milliseconds, in the order the
+ * launches were enqueued (by any thread, on any device), returns how many it wrote, and
+ * clears the record.  Threads may launch concurrently: each thread's launches
+ * are bracketed on their own, and events stay with the device they were made on.  The
+ * switch is process-wide; lla_profile_enable returns the previous setting. */
 int lla_profile_enable(int enable);
 int lla_profile_collect(const char** names, float* ms, int max_entries);
 

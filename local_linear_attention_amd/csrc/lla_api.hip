@@ -163,6 +163,7 @@ bool resolve_parallax_bwd_fast(lla_path_t path, int dtype, int64_t d, int64_t n,
         case LLA_PATH_EXACT: *fast = false; return true;
         case LLA_PATH_FAST: *fast = true; return lla::parallax_bwd_fast_supports(dtype, d, n);
         case LLA_PATH_AUTO: *fast = lla::parallax_bwd_fast_supports(dtype, d, n); return true;
+        case LLA_PATH_CG: return false;   // an LLA-only solver
     }
     return false;
 }
@@ -172,6 +173,7 @@ bool resolve_parallax_fast(lla_path_t path, int dtype, int64_t d, int64_t n, boo
         case LLA_PATH_EXACT: *fast = false; return true;
         case LLA_PATH_FAST: *fast = true; return lla::parallax_fast_supports(dtype, d, n);
         case LLA_PATH_AUTO: *fast = lla::parallax_fast_supports(dtype, d, n); return true;
+        case LLA_PATH_CG: return false;   // an LLA-only solver
     }
     return false;
 }
@@ -328,19 +330,29 @@ hipError_t scratch_for_current_device(void** ptr) {
 }
 
 // ---- kernel-level timing
+// A begin/end pair brackets one launch made by the calling thread, so the open entry is
+// per thread; finished entries and spare events are shared under g_prof_mu.  Events belong
+// to the device that was current when they were created, so spares are kept with it.
 struct ProfEntry {
     const char* name;
     hipEvent_t start, stop;
+    int dev;
+};
+struct ProfEvent {
+    hipEvent_t ev;
+    int dev;
 };
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
 std::vector<ProfEntry> g_prof_done;
-std::vector<hipEvent_t> g_prof_free;
-ProfEntry g_prof_open = {nullptr, nullptr, nullptr};
+std::vector<ProfEvent> g_prof_free;
+thread_local ProfEntry g_prof_open = {nullptr, nullptr, nullptr, -1};
 
-hipEvent_t prof_event() {
-    if (!g_prof_free.empty()) {
-        hipEvent_t e = g_prof_free.back();
+hipEvent_t prof_event(int dev) {   // caller holds g_prof_mu; dev is the current device
+    for (size_t i = g_prof_free.size(); i-- > 0;) {
+        if (g_prof_free[i].dev != dev) continue;
+        hipEvent_t e = g_prof_free[i].ev;
+        g_prof_free[i] = g_prof_free.back();
         g_prof_free.pop_back();
         return e;
     }
@@ -354,19 +366,28 @@ namespace lla {
 
 void prof_begin(hipStream_t stream, const char* kernel) {
     if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return;
     std::lock_guard<std::mutex> lock(g_prof_mu);
-    g_prof_open = {kernel, prof_event(), nullptr};
-    if (g_prof_open.start) (void)hipEventRecord(g_prof_open.start, stream);
+    g_prof_open = {kernel, prof_event(dev), nullptr, dev};
+    if (g_prof_open.start && hipEventRecord(g_prof_open.start, stream) != hipSuccess) {
+        g_prof_free.push_back({g_prof_open.start, dev});
+        g_prof_open.start = nullptr;
+    }
 }
 
 void prof_end(hipStream_t stream) {
     if (!g_prof_on.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> lock(g_prof_mu);
     if (!g_prof_open.start) return;
-    g_prof_open.stop = prof_event();
-    if (g_prof_open.stop && hipEventRecord(g_prof_open.stop, stream) == hipSuccess)
+    g_prof_open.stop = prof_event(g_prof_open.dev);
+    if (g_prof_open.stop && hipEventRecord(g_prof_open.stop, stream) == hipSuccess) {
         g_prof_done.push_back(g_prof_open);
-    g_prof_open = {nullptr, nullptr, nullptr};
+    } else {
+        g_prof_free.push_back({g_prof_open.start, g_prof_open.dev});
+        if (g_prof_open.stop) g_prof_free.push_back({g_prof_open.stop, g_prof_open.dev});
+    }
+    g_prof_open = {nullptr, nullptr, nullptr, -1};
 }
 
 }  // namespace lla
@@ -599,8 +620,8 @@ int lla_profile_collect(const char** names, float* ms, int max_entries) {
             if (ms) ms[count] = t;
             ++count;
         }
-        g_prof_free.push_back(e.start);
-        g_prof_free.push_back(e.stop);
+        g_prof_free.push_back({e.start, e.dev});
+        g_prof_free.push_back({e.stop, e.dev});
     }
     g_prof_done.clear();
     return count;

@@ -151,8 +151,8 @@ def test_workspace_size():
 
 
 def test_boundary_contract_names():
-    # The scope table's boundary: lla_forward with the spec argument list (dtype and
-    # stream appended), the caller-workspace pair, status strings and the version.
+    # The boundary: lla_forward with the operation's own arguments (then dtype and stream),
+    # the caller-workspace pair, status strings and the version.
     lib = _lib()
     for name in ("lla_forward", "lla_forward_workspace_bytes", "lla_forward_ws", "lla_status_string",
                  "lla_version"):
