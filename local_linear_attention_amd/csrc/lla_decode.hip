@@ -29,6 +29,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -970,16 +971,26 @@ hipError_t launch_lla_decode_t(const Problem& p, void* workspace) {
     constexpr bool kSplit = std::is_same<TA, float>::value;
     static_assert(!kSplit || std::is_same<TIn, uint16_t>::value, "split-operand moments take bf16 inputs");
     static_assert(kSplit || mom_smem_bytes<D, TA>() <= 150 * 1024, "LDS");
-    static const hipError_t attr_err = [] {   // once per instantiation
-        if constexpr (kSplit)
-            return hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_split_kernel<TIn, D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, msp_smem_bytes<D>());
-        else
-            return hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
-    }();
-    hipError_t err = attr_err;
+    // The dynamic LDS limit, raised once per instantiation and device (the current one).
+    static std::mutex attr_mu;
+    static bool attr_done[64] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    {
+        std::lock_guard<std::mutex> lock(attr_mu);
+        if (!attr_done[dev]) {
+            if constexpr (kSplit)
+                err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_split_kernel<TIn, D>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, msp_smem_bytes<D>());
+            else
+                err = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_decode_moments_kernel<TIn, D, TA>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, mom_smem_bytes<D, TA>());
+            if (err != hipSuccess) return err;
+            attr_done[dev] = true;
+        }
+    }
     const unsigned blocks = static_cast<unsigned>(BH * S);
     prof_begin(p.stream, "lla_decode_stats_kernel");
     lla_decode_stats_kernel<TIn, D><<<dim3(blocks), dim3(DC_THREADS), 0, p.stream>>>(

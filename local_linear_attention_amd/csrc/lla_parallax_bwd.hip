@@ -45,6 +45,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 namespace lla {
@@ -693,18 +694,27 @@ hipError_t launch_parallax_bwd_fast(const BwdProblem& b, void* workspace) {
     const int ntiles = static_cast<int>(bwd_tiles(p.n));
     unsigned char* qimg = static_cast<unsigned char*>(workspace);
     unsigned char* kimg = qimg + static_cast<int64_t>(BH) * ntiles * QIMG;
-    static const hipError_t attr_err = [] {   // once: dynamic LDS above the default limit
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_kv_kernel<KV_NBUF>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, KV_NBUF * QIMG);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_qr_kernel<true>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 2 * KIMG);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_qr_kernel<false>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 2 * KIMG);
-        return e;
-    }();
-    if (attr_err != hipSuccess) return attr_err;
+    {   // dynamic LDS above the default limit, raised once per device (the current one)
+        static std::mutex attr_mu;
+        static bool attr_done[64] = {};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        std::lock_guard<std::mutex> lock(attr_mu);
+        if (!attr_done[dev]) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_kv_kernel<KV_NBUF>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, KV_NBUF * QIMG);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_qr_kernel<true>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * KIMG);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lla_parallax_bwd_qr_kernel<false>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * KIMG);
+            if (e != hipSuccess) return e;
+            attr_done[dev] = true;
+        }
+    }
     prof_begin(p.stream, "lla_parallax_bwd_pack_kernel");
     lla_parallax_bwd_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ntiles), dim3(256), 0, p.stream>>>(
         static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k), static_cast<const uint16_t*>(p.v),
