@@ -607,18 +607,28 @@ __global__ __launch_bounds__(DC_THREADS, 1) void lla_decode_moments_kernel(
 // 16x16 block then takes the products hh, hl, lh on v_mfma_f32_16x16x32_bf16 (32 keys per
 // instruction): the dropped terms are below 2^-16 of each product (with three parts and six
 // products, 2^-24; measured 1.3 times slower for errors that the two-part form already keeps
-// near 1e-5).  Staging per sub-tile of 64 keys: 16-byte loads of the rows (in flight during
-// the current sub-tile's MFMAs) go to a row-major LDS tile with one weight per key; then
-// thread -> (K or V, feature f, 8 consecutive keys) forms the parts and writes each with one
-// 16-byte store into the feature-major operand image.
+// near 1e-5).  Staging per sub-tile of 64 keys: a thread takes 16-byte row pieces (8 features
+// of one key, loaded a sub-tile ahead), forms their parts in fp32 and stores each part
+// row-major, [part][K, V][key][D + 8], with one 16-byte store.  The MFMA operands want 8
+// consecutive keys of one feature per lane; the LDS transpose read (ds_read_b64_tr_b16, two
+// per operand) delivers them from the row-major image: in each group of 16 lanes, lane L
+// gives 4 consecutive features of key L / 4 and receives one feature of 4 consecutive keys.
+// Two images alternate, so the parts of sub-tile t + 1 are formed while the products of
+// sub-tile t run, with one barrier per sub-tile.
 typedef __bf16 bf16x8d __attribute__((ext_vector_type(8)));
+typedef short short4x __attribute__((ext_vector_type(4)));
 constexpr int M3_PARTS = 2;         // bf16 parts per operand (2: hi + lo; 3: hi + mid + lo)
-constexpr int M3_SUB = 64;          // keys per sub-tile: two 32-key MFMA steps
-constexpr int M3_KG = M3_SUB / 8;   // groups of 8 keys per sub-tile
-constexpr int M3_LD = M3_SUB + 8;   // feature row of a part (halves): 144 bytes
+// Keys per sub-tile: 32 (one MFMA step; four blocks per CU at d <= 64, two at d = 128), 64 at
+// d = 16 (where 32 keys would leave threads without a piece).
+template <int D>
+constexpr int msp_sub() { return D == 16 ? 64 : 32; }
 
 template <int D>
-constexpr int msp_buf_bytes() { return M3_PARTS * 2 * D * M3_LD * 2; }   // [part][K, V][feature][M3_LD]
+constexpr int msp_row() { return D + 8; }   // halves per key row of a part image
+template <int D>
+constexpr int msp_img_bytes() { return M3_PARTS * 2 * msp_sub<D>() * msp_row<D>() * 2; }   // [part][K, V][key][D + 8]
+template <int D>
+constexpr int msp_smem_bytes() { return 2 * msp_img_bytes<D>(); }
 
 __device__ __forceinline__ float4x mfma_bf(bf16x8d a, bf16x8d b, float4x c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -649,98 +659,91 @@ __device__ __forceinline__ void mfma_split_blocks(const bf16x8d (&kop)[D / 16][M
      ...);
 }
 
-// Row-major staging tile of one sub-tile (bf16 as given): [K, V][key][D + 8].
-template <int D>
-constexpr int msp_raw_bytes() { return 2 * M3_SUB * (D + 8) * 2; }
-template <int D>
-constexpr int msp_smem_bytes() { return msp_buf_bytes<D>() + msp_raw_bytes<D>(); }
+// MFMA operand from a row-major part image: lane (g, c) receives feature f0 + c of keys
+// k0 + 8 g .. k0 + 8 g + 7 (elements are `RL` halves apart from key to key).
+template <int RL>
+__device__ __forceinline__ bf16x8d tr_operand(const unsigned char* part, int k0, int f0, int g, int c) {
+    const short* p = reinterpret_cast<const short*>(part) + (k0 + 8 * g + (c >> 2)) * RL + f0 + 4 * (c & 3);
+    typedef __attribute__((address_space(3))) short4x* lds_short4x;
+    const short4x lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4x)(const_cast<short*>(p)));
+    const short4x hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4x)(const_cast<short*>(p + 4 * RL)));
+    return __builtin_bit_cast(bf16x8d, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
+// Wave W of a block: the moment blocks [B0, B1) over keys [j0, jend), and this thread's
+// partial sums S_v of its 8 features (8 (tid mod D/8) ..) in sv.
 template <typename TIn, int D, int W>
 __device__ __forceinline__ void moments_split_wave(const TIn* __restrict__ kh, const TIn* __restrict__ vh,
-                                              const float* __restrict__ xh, const float* kbf, unsigned char* img,
-                                              uint16_t* raw, float* swl, float* svs, float Mf, int j0, int jend,
-                                              int tid, float* __restrict__ mo) {
+                                              const float* __restrict__ xh, const float* kbf, unsigned char* lds,
+                                              float Mf, int j0, int jend, int tid, float* __restrict__ mo,
+                                              float (&sv)[8]) {
     using MB = MomBlocks<D>;
     constexpr int NB = D / 16;
     constexpr int B0 = W * MB::NT / 4, B1 = (W + 1) * MB::NT / 4;
     constexpr int NA = B1 > B0 ? B1 - B0 : 1;
-    constexpr int PAIRS = 2 * D * M3_KG;                         // (K or V, feature, 8 keys)
-    constexpr int PPT = (PAIRS + DC_THREADS - 1) / DC_THREADS;
-    constexpr int CHUNKS = 2 * M3_SUB * D / 8;                   // 16-byte row pieces per sub-tile
-    constexpr int CPT = (CHUNKS + DC_THREADS - 1) / DC_THREADS;
-    constexpr int RLD = D + 8;                                   // raw row (halves)
+    constexpr int RL = msp_row<D>();
+    constexpr int M3_SUB = msp_sub<D>();
+    constexpr int PK = D / 8;                        // 16-byte pieces per key row
+    constexpr int APIECES = M3_SUB * PK;             // pieces of K (then of V) per sub-tile
+    constexpr int CPT = 2 * APIECES / DC_THREADS;    // pieces per thread
+    constexpr int PART = 2 * M3_SUB * RL * 2;        // bytes per part image
     constexpr int VB = B0 > MB::NKK ? B0 : MB::NKK;
     constexpr int VI0 = B1 > MB::NKK ? MB::I(VB) : 0;
     constexpr int VI1 = B1 > MB::NKK ? MB::I(B1 - 1) : -1;
     static_assert(sizeof(TIn) == 2, "split-operand moments take bf16 inputs");
+    static_assert(CPT >= 1 && (2 * APIECES) % DC_THREADS == 0 && DC_THREADS % PK == 0, "piece mapping");
     const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+    const int fc = tid % PK;                         // this thread's features 8 fc .. 8 fc + 7
+    float kb8[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kb8[t] = kbf[8 * fc + t];
     float4x acc[NA];
 #pragma unroll
     for (int t = 0; t < NA; ++t) acc[t] = float4x{0.f, 0.f, 0.f, 0.f};
-    float sv[PPT];
-#pragma unroll
-    for (int e = 0; e < PPT; ++e) sv[e] = 0.0f;
     uint4 pre[CPT];
-    float xpre = -INFINITY;
-    // 16-byte pieces: piece u -> array u / (M3_SUB D/8), key, features 8 (u % (D/8)) ..
+    float xpre[CPT];
+    // piece u = tid + 256 e: K (u < APIECES) or V, key (u mod APIECES) / PK, features 8 fc ..
     auto fetch = [&](int js) {
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
             const int u = tid + DC_THREADS * e;
-            const int arr = u / (M3_SUB * D / 8), rem = u % (M3_SUB * D / 8), key = rem / (D / 8), fc = rem % (D / 8);
+            const int arr = u / APIECES, key = (u % APIECES) / PK;
             const int j = js + key;
             pre[e] = uint4{0u, 0u, 0u, 0u};
-            if (u < CHUNKS && j < jend)
+            xpre[e] = -INFINITY;
+            if (j < jend) {
                 pre[e] = *reinterpret_cast<const uint4*>((arr == 0 ? kh : vh) + static_cast<int64_t>(j) * D + 8 * fc);
+                xpre[e] = xh[j];
+            }
         }
-        xpre = tid < M3_SUB && js + tid < jend ? xh[js + tid] : -INFINITY;
     };
-    // raw pieces and weights to LDS, then (after a barrier) the parts of R_k, R_v
-    auto stash = [&](unsigned char* buf) {
+    auto stash = [&](unsigned char* img) {
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
             const int u = tid + DC_THREADS * e;
-            if (u < CHUNKS) {
-                const int arr = u / (M3_SUB * D / 8), rem = u % (M3_SUB * D / 8), key = rem / (D / 8), fc = rem % (D / 8);
-                *reinterpret_cast<uint4*>(raw + (arr * M3_SUB + key) * RLD + 8 * fc) = pre[e];
-            }
-        }
-        if (tid < M3_SUB) swl[tid] = exp2f((xpre - Mf) * 0.5f);
-        __syncthreads();
+            const int arr = u / APIECES, key = (u % APIECES) / PK;
+            const float sw = exp2f((xpre[e] - Mf) * 0.5f);
+            const uint32_t wd[4] = {pre[e].x, pre[e].y, pre[e].z, pre[e].w};
+            bf16x8d part[M3_PARTS];
 #pragma unroll
-        for (int e = 0; e < PPT; ++e) {
-            const int pp = tid + DC_THREADS * e;
-            if (pp < PAIRS) {
-                const int arr = pp / (M3_KG * D), rem = pp % (M3_KG * D), f = rem % D, kg = rem / D;
-                const float sub = arr == 0 ? kbf[f] : 0.0f;
-                bf16x8d part[M3_PARTS];
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t w2 = wd[t >> 1];
+                const float x = __uint_as_float((t & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+                float r = sw * (x - (arr == 0 ? kb8[t] : 0.0f));
+                if (arr == 1) sv[t] = fmaf(sw * sw, x, sv[t]);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float sw = swl[8 * kg + t];
-                    const float x = __uint_as_float(static_cast<uint32_t>(raw[(arr * M3_SUB + 8 * kg + t) * RLD + f]) << 16);
-                    float r = sw * (x - sub);
-                    if (arr == 1) sv[e] = fmaf(sw * sw, x, sv[e]);
-#pragma unroll
-                    for (int lv = 0; lv < M3_PARTS; ++lv) {
-                        const __bf16 hp = static_cast<__bf16>(r);
-                        part[lv][t] = hp;
-                        r -= static_cast<float>(hp);
-                    }
+                for (int lv = 0; lv < M3_PARTS; ++lv) {
+                    const __bf16 hp = static_cast<__bf16>(r);
+                    part[lv][t] = hp;
+                    r -= static_cast<float>(hp);
                 }
-                unsigned char* row = buf + (arr * D + f) * (M3_LD * 2) + 16 * kg;
-#pragma unroll
-                for (int lv = 0; lv < M3_PARTS; ++lv) *reinterpret_cast<bf16x8d*>(row + lv * 2 * D * M3_LD * 2) = part[lv];
             }
+#pragma unroll
+            for (int lv = 0; lv < M3_PARTS; ++lv)
+                *reinterpret_cast<bf16x8d*>(img + lv * PART + ((arr * M3_SUB + key) * RL + 8 * fc) * 2) = part[lv];
         }
     };
-    // One operand image: stash's first barrier comes after every wave's MFMAs on it, its
-    // second (the loop's) before the next sub-tile's.
-    const int nsub = (jend - j0 + M3_SUB - 1) / M3_SUB;
-    fetch(j0);
-    stash(img);
-    __syncthreads();
-    for (int t = 0; t < nsub; ++t) {
-        if (t + 1 < nsub) fetch(j0 + (t + 1) * M3_SUB);
+    auto products = [&](const unsigned char* img) {
         if constexpr (B1 > B0) {
 #pragma unroll
             for (int ks = 0; ks < M3_SUB / 32; ++ks) {
@@ -748,47 +751,52 @@ __device__ __forceinline__ void moments_split_wave(const TIn* __restrict__ kh, c
 #pragma unroll
                 for (int R = 0; R < NB; ++R)
 #pragma unroll
-                    for (int lv = 0; lv < M3_PARTS; ++lv)
-                        kop[R][lv] = *reinterpret_cast<const bf16x8d*>(
-                            img + ((2 * lv) * D + 16 * R + c) * (M3_LD * 2) + 64 * ks + 16 * g);
+                    for (int lv = 0; lv < M3_PARTS; ++lv) kop[R][lv] = tr_operand<RL>(img + lv * PART, 32 * ks, 16 * R, g, c);
 #pragma unroll
                 for (int R = VI0; R <= VI1; ++R)
 #pragma unroll
                     for (int lv = 0; lv < M3_PARTS; ++lv)
-                        vop[R][lv] = *reinterpret_cast<const bf16x8d*>(
-                            img + ((2 * lv + 1) * D + 16 * R + c) * (M3_LD * 2) + 64 * ks + 16 * g);
+                        vop[R][lv] = tr_operand<RL>(img + lv * PART + M3_SUB * RL * 2, 32 * ks, 16 * R, g, c);
                 mfma_split_blocks<D, B0>(kop, vop, acc, std::make_integer_sequence<int, B1 - B0>{});
             }
         }
-        if (t + 1 < nsub) stash(img);
+    };
+    // Sub-tile t's products read image t mod 2; meanwhile the parts of t + 1 go into the
+    // other image (last read before the previous barrier) and the rows of t + 2 are loaded.
+    const int nsub = (jend - j0 + M3_SUB - 1) / M3_SUB;
+    unsigned char* img0 = lds;
+    unsigned char* img1 = lds + msp_img_bytes<D>();
+    fetch(j0);
+    stash(img0);
+    if (nsub > 1) fetch(j0 + M3_SUB);
+    __syncthreads();
+    for (int t = 0; t < nsub; ++t) {
+        products((t & 1) ? img1 : img0);
+        if (t + 1 < nsub) {
+            stash(((t + 1) & 1) ? img1 : img0);
+            if (t + 2 < nsub) fetch(j0 + (t + 2) * M3_SUB);
+        }
         __syncthreads();
     }
 #pragma unroll
     for (int b = B0; b < B1; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mo[b * 256 + (4 * g + r) * 16 + c] = acc[b - B0][r];
-#pragma unroll
-    for (int e = 0; e < PPT; ++e) {
-        const int pp = tid + DC_THREADS * e;
-        if (pp < PAIRS && pp >= M3_KG * D) svs[pp - M3_KG * D] = sv[e];   // [kg][f]
-    }
 }
 
 template <typename TIn, int D>
-__global__ __launch_bounds__(DC_THREADS, D <= 64 ? 2 : 1) void lla_decode_moments_split_kernel(
+__global__ __launch_bounds__(DC_THREADS, D <= 64 ? 4 : 2) void lla_decode_moments_split_kernel(
     const TIn* __restrict__ k, const TIn* __restrict__ v, const double* __restrict__ stats,
     const float* __restrict__ xsc, float* __restrict__ mom, int L, int S, int C) {
     using MB = MomBlocks<D>;
     static_assert(D <= 128, "split-operand moments serve d <= 128");
+    static_assert(DC_THREADS * 8 * 4 <= 2 * msp_img_bytes<D>(), "S_v partials fit in the images");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ double sh[DC_THREADS];
     __shared__ double kbd[D];
     __shared__ float kbf[D];
-    __shared__ float svs[M3_KG * D];
-    __shared__ float swl[M3_SUB];
     const int tid = threadIdx.x;
     const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint16_t* raw = reinterpret_cast<uint16_t*>(lds + msp_buf_bytes<D>());
     const int bh = static_cast<int>(blockIdx.x) / S, sidx = static_cast<int>(blockIdx.x) % S;
     const int j0 = sidx * C;
     const int jend = min(L, j0 + C);
@@ -801,17 +809,22 @@ __global__ __launch_bounds__(DC_THREADS, D <= 64 ? 2 : 1) void lla_decode_moment
     const TIn* vh = v + static_cast<int64_t>(bh) * L * D;
     const float* xh = xsc + static_cast<int64_t>(bh) * L;
     float* mo = mom + (static_cast<int64_t>(bh) * S + sidx) * (MB::NT * 256 + D);
+    float sv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     switch (wu) {
-        case 0: moments_split_wave<TIn, D, 0>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
-        case 1: moments_split_wave<TIn, D, 1>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
-        case 2: moments_split_wave<TIn, D, 2>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
-        default: moments_split_wave<TIn, D, 3>(kh, vh, xh, kbf, lds, raw, swl, svs, Mf, j0, jend, tid, mo); break;
+        case 0: moments_split_wave<TIn, D, 0>(kh, vh, xh, kbf, lds, Mf, j0, jend, tid, mo, sv); break;
+        case 1: moments_split_wave<TIn, D, 1>(kh, vh, xh, kbf, lds, Mf, j0, jend, tid, mo, sv); break;
+        case 2: moments_split_wave<TIn, D, 2>(kh, vh, xh, kbf, lds, Mf, j0, jend, tid, mo, sv); break;
+        default: moments_split_wave<TIn, D, 3>(kh, vh, xh, kbf, lds, Mf, j0, jend, tid, mo, sv); break;
     }
+    // S_v: every thread's partial sums of its 8 features, through the (now free) images.
+    float* svp = reinterpret_cast<float*>(lds);   // [thread][8]
+    *reinterpret_cast<float4x*>(svp + tid * 8) = float4x{sv[0], sv[1], sv[2], sv[3]};
+    *reinterpret_cast<float4x*>(svp + tid * 8 + 4) = float4x{sv[4], sv[5], sv[6], sv[7]};
     __syncthreads();
     if (tid < D) {
+        constexpr int PK = D / 8;
         float t = 0.0f;
-#pragma unroll
-        for (int kg = 0; kg < M3_KG; ++kg) t += svs[kg * D + tid];
+        for (int th = tid / 8; th < DC_THREADS; th += PK) t += svp[th * 8 + (tid & 7)];
         mo[MB::NT * 256 + tid] = t;
     }
 }
