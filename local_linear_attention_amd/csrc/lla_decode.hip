@@ -911,7 +911,10 @@ __global__ __launch_bounds__(DC_THREADS) void lla_decode_solve_kernel(
             __syncthreads();
             const double piv = cb[p];
             if (piv > thr) {
-                const double f = 1.0 / piv;
+                // 1 / piv: the hardware reciprocal and two Newton steps (about 1 ulp)
+                double f = __builtin_amdgcn_rcp(piv);
+                f = fma(f, fma(-piv, f, 1.0), f);
+                f = fma(f, fma(-piv, f, 1.0), f);
                 double rp[TS];
 #pragma unroll
                 for (int ib = 0; ib < TS; ++ib) rp[ib] = tj * TS + ib > p ? cb[tj * TS + ib] : 0.0;
