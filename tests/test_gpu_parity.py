@@ -182,6 +182,59 @@ def test_profiling_records_each_kernel():
     assert all(ms > 0 for _, ms in rec)
 
 
+def test_concurrent_host_threads_and_profiling():
+    # Two host threads launch forwards on streams of their own at the same time, with the kernel
+    # timing on: each output equals its single-threaded result bit for bit, and the timing
+    # record holds every launch of both threads, each bracketed on its own.
+    torch = require_gpu()
+    import threading
+    from local_linear_attention_amd import (lla_forward_ws, lla_profile_collect, lla_profile_enable,
+                                            lla_workspace_size)
+    from parity_util import to_device
+    w, q, k, v = workload_arrays("d24", B=1, H=2, n=300)
+    cases = [(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")),
+             (to_device(q, "bf16"), to_device(k, "bf16"), to_device(2.0 * v, "bf16"))]
+    nbytes = lla_workspace_size(w.B, w.H, w.n, w.d, "bf16", "fast")
+    refs = []
+    for tq, tk, tv in cases:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        refs.append(lla_forward_ws(tq, tk, tv, w.h, w.lam, ws, path="fast"))
+    torch.cuda.synchronize()
+    outs, errors = [None, None], []
+    reps = 3
+
+    def worker(i):
+        try:
+            stream = torch.cuda.Stream()
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                for _ in range(reps):
+                    outs[i] = lla_forward_ws(*cases[i], w.h, w.lam, ws, path="fast", stream=stream)
+            stream.synchronize()
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    lla_profile_enable(True)
+    try:
+        threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        torch.cuda.synchronize()
+        rec = lla_profile_collect()
+    finally:
+        lla_profile_enable(False)
+    assert not errors, errors
+    for got, ref in zip(outs, refs):
+        assert torch.equal(got, ref)
+    kernels = ["lla_anchor_kernel", "lla_pack_kernel", "lla_rowmax_kernel", "lla_rows_kernel", "lla_probe_kernel",
+               "lla_refine_kernel"]
+    assert sorted(name for name, _ in rec) == sorted(kernels * (2 * reps))
+    assert all(ms > 0 for _, ms in rec)
+
+
 def test_tiny_affine_lambda_zero_rows_beyond_d():
     require_gpu()
     w, q, k, v = workload_arrays("tiny_affine")
