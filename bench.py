@@ -76,6 +76,7 @@ KERNEL_BOUND = {
     "lla_parallax_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_parallax_kernel": ("mfma", PEAK["mfma_f16_TFLOPs"]),
     "lla_parallax_exact_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
+    "lla_parallax_fallback_kernel": ("alu", PEAK["valu_f64_TFLOPs"]),
     "lla_parallax_decode_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_parallax_merge_kernel": ("hbm", PEAK["hbm_GBps"]),
     "lla_parallax_bwd_pack_kernel": ("hbm", PEAK["hbm_GBps"]),
@@ -111,7 +112,7 @@ def path_kernels(path, d):
     return PATH_KERNELS["fast128" if (path == "fast" and d == 128) else path]
 PARALLAX_KERNELS = {
     "exact": ["lla_parallax_exact_kernel"],
-    "fast": ["lla_parallax_pack_kernel", "lla_parallax_kernel"],
+    "fast": ["lla_parallax_pack_kernel", "lla_parallax_kernel", "lla_parallax_fallback_kernel"],
 }
 
 
@@ -174,6 +175,8 @@ def kernel_flops(name, B, H, n, d, path):
         return parallax_flops(B, H, n, d)
     if name == "lla_parallax_pack_kernel":
         return 0                      # data movement only (K, V repacked once)
+    if name == "lla_parallax_fallback_kernel":
+        return 0                      # heads the range guard hands to fp64 (none on the synthetic workloads)
     raise KeyError(name)
 
 

@@ -209,8 +209,10 @@ lla_status_t lla_forward_noalloc(const void* q, const void* k, const void* v, fl
  * produce it by a learned projection of the layer input, which stays with the caller).
  * A zero probe gives softmax attention.  Arguments as for lla_forward, without lambda;
  * out must not overlap q, k, v or rho.  Paths: FAST is one streaming pass on the matrix
- * cores for bf16 inputs with d = 64 and n up to 4194304 (keys and values must lie in the
- * fp16 range); EXACT accumulates in fp64 and serves every supported (dtype, d); AUTO takes
+ * cores for bf16 inputs with d = 64 and n up to 4194304; it holds the values as fp16, so a
+ * head whose largest |v| is not finite or lies outside [2^-10, 2^16) is computed instead by
+ * the fp64 row code (a third launch over the heads so listed; it exits at once when there
+ * are none); EXACT accumulates in fp64 and serves every supported (dtype, d); AUTO takes
  * FAST where it applies.  Validation, errors, streams and scratch ownership are as for the
  * LLA entry points above (lla_parallax_forward and _ex take scratch from the library pool;
  * _ws allocates nothing).
@@ -227,7 +229,9 @@ lla_status_t lla_parallax_forward_ex(const void* q, const void* k, const void* v
  * invalid).  The fast path keeps there, per head and tile of 64 keys, in regions each rounded
  * up to a multiple of 256 bytes: the tile image of 18432 bytes (K key-major as given, 64*72*2
  * bytes, then V feature-major as fp16, 64*68*2 bytes, then padding), the tile's key sum
- * (d floats) and its largest key norm (one float).  The exact path needs none. */
+ * (d floats), its largest key norm (one float) and its largest |v| (one float); then the
+ * count of heads left to the fp64 row code (one unsigned) and the list of those heads (one
+ * int per head).  The exact path needs none. */
 size_t lla_parallax_workspace_size(int64_t B, int64_t H, int64_t n, int64_t d, lla_dtype_t dtype,
                                    lla_path_t path);
 

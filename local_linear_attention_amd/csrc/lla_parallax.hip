@@ -23,6 +23,11 @@
 //     |s2| <= |rho| (max_j |k_j| + |a|)), so that P2 fits fp16; the merge divides by it;
 //   * P1 and P2 enter the P V products as fp16 (v as fp16, exact for bf16 values in the fp16
 //     range); d1 and d2 sum the same rounded values, so the rounding only perturbs weights.
+// Range guard: a head whose largest |v| lies outside [2^-10, 2^16) (or is not finite) is left
+// to the fp64 row code: fp16 would overflow above, and below, its subnormal spacing 2^-24
+// would no longer be negligible against the head's values.  The pack kernel records each
+// tile's largest |v|; the streaming kernel's blocks of such a head exit at once and list the
+// head; a fallback launch runs the generic row code over the listed heads.
 // Generic path (fp32 or bf16, d in {16, 32, 64, 128}): fp64, one block per row.
 #include "lla_device.h"
 #include "lla_internal.h"
@@ -70,10 +75,16 @@ __global__ __launch_bounds__(256) void lla_parallax_pack_kernel(const uint16_t* 
                                                                 const uint16_t* __restrict__ v,
                                                                 unsigned char* __restrict__ img,
                                                                 float* __restrict__ ksum,
-                                                                float* __restrict__ kmax, int n,
+                                                                float* __restrict__ kmax,
+                                                                float* __restrict__ vmax,
+                                                                unsigned* __restrict__ nlisted, int n,
                                                                 int ntiles) {
     __shared__ float red[32][FD + 1];
     __shared__ float nrm[8][MT];
+    __shared__ float vmw[4];
+    // The list of heads left to the fallback starts empty (nothing else of this call has
+    // touched it yet; the streaming kernel runs after this one).
+    if (blockIdx.x == 0 && threadIdx.x == 0) *nlisted = 0u;
     const int bh = static_cast<int>(blockIdx.x) / ntiles, t = static_cast<int>(blockIdx.x) % ntiles;
     const int tid = threadIdx.x, pr = tid & 31, fg = tid >> 5;
     const int64_t base = static_cast<int64_t>(bh) * n * FD;
@@ -97,7 +108,7 @@ __global__ __launch_bounds__(256) void lla_parallax_pack_kernel(const uint16_t* 
     uint32_t* vd = reinterpret_cast<uint32_t*>(ti + X_KIMG);
     const uint32_t ka[4] = {k0.x, k0.y, k0.z, k0.w}, kb[4] = {k1.x, k1.y, k1.z, k1.w};
     const uint32_t va[4] = {v0.x, v0.y, v0.z, v0.w}, vb[4] = {v1.x, v1.y, v1.z, v1.w};
-    float na = 0.0f, nb = 0.0f;
+    float na = 0.0f, nb = 0.0f, vm = 0.0f;   // vm: largest |v| of this thread (a NaN counts as inf)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int row = 8 * fg + e, hi = e & 1;
@@ -106,16 +117,23 @@ __global__ __launch_bounds__(256) void lla_parallax_pack_kernel(const uint16_t* 
         red[pr][row] = xa + xb;
         na = fmaf(xa, xa, na);
         nb = fmaf(xb, xb, nb);
+        const float ya = __uint_as_float(hi ? (va[e >> 1] & 0xffff0000u) : (va[e >> 1] << 16));
+        const float yb = __uint_as_float(hi ? (vb[e >> 1] & 0xffff0000u) : (vb[e >> 1] << 16));
+        vm = fmaxf(vm, ya == ya ? fabsf(ya) : INFINITY);
+        vm = fmaxf(vm, yb == yb ? fabsf(yb) : INFINITY);
         h16x2 vv;
-        vv[0] = static_cast<_Float16>(__uint_as_float(hi ? (va[e >> 1] & 0xffff0000u) : (va[e >> 1] << 16)));
-        vv[1] = static_cast<_Float16>(__uint_as_float(hi ? (vb[e >> 1] & 0xffff0000u) : (vb[e >> 1] << 16)));
+        vv[0] = static_cast<_Float16>(ya);
+        vv[1] = static_cast<_Float16>(yb);
         vd[row * (V_LD / 2) + pr] = __builtin_bit_cast(uint32_t, vv);
         if (pr < (V_LD - MT) / 2) vd[row * (V_LD / 2) + MT / 2 + pr] = 0u;   // row padding
     }
     nrm[fg][2 * pr] = na;
     nrm[fg][2 * pr + 1] = nb;
+    vm = wave_max64(vm);
+    if ((tid & 63) == 0) vmw[tid >> 6] = vm;
     __syncthreads();
     const int64_t tix = static_cast<int64_t>(bh) * ntiles + t;
+    if (tid == 0) vmax[tix] = fmaxf(fmaxf(vmw[0], vmw[1]), fmaxf(vmw[2], vmw[3]));
     if (tid < FD) {
         float s = 0.0f;
         for (int p = 0; p < 32; ++p) s += red[p][tid];
@@ -143,11 +161,13 @@ __global__ __launch_bounds__(256) void lla_parallax_pack_kernel(const uint16_t* 
 template <bool kStats>   // kStats: also write the per-row statistics the backward reads
 __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const unsigned char* __restrict__ img,
-    const float* __restrict__ ksum, const float* __restrict__ kmax, float* __restrict__ out,
+    const float* __restrict__ ksum, const float* __restrict__ kmax, const float* __restrict__ vmax,
+    unsigned* __restrict__ nlisted, int* __restrict__ hlist, float* __restrict__ out,
     float* __restrict__ stats, int n, int BH, float sl2) {
     __shared__ __attribute__((aligned(16))) unsigned char ring[X_NBUF * X_TILE];
     __shared__ float akm[FD];
     __shared__ float kbound;
+    __shared__ int vout;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const int g = lane >> 4, c = lane & 15;
@@ -172,8 +192,18 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
         for (int t = lane; t < ptiles; t += 64) mx = fmaxf(mx, kmax[static_cast<int64_t>(bh) * ptiles + t]);
         mx = wave_max64(mx);
         if (lane == 0) kbound = mx;
+    } else if (wu == 2) {
+        // Range guard: the head's largest |v| must lie in [2^-10, 2^16) (or be 0: all values 0).
+        float mx = 0.0f;
+        for (int t = lane; t < ptiles; t += 64) mx = fmaxf(mx, vmax[static_cast<int64_t>(bh) * ptiles + t]);
+        mx = wave_max64(mx);
+        if (lane == 0) vout = !(mx < 65536.0f) || (mx > 0.0f && mx < 0x1p-10f);
     }
     __syncthreads();
+    if (vout) {   // block-uniform: the head goes to the fallback, listed once (by its first block)
+        if (blk == 0 && tid == 0) hlist[atomicAdd(nlisted, 1u)] = bh;
+        return;
+    }
     const float anorm = sqrtf(wave_sum64(akm[lane] * akm[lane]));
     const float rbound = kbound + anorm;   // >= |k_j - a| for every key of the head
 
@@ -435,17 +465,16 @@ __global__ __launch_bounds__(X_WAVES * 64, 2) void lla_parallax_kernel(
 constexpr int G_NT = 256;
 constexpr int G_CHK = 256;
 
+// Row i of head bh, by the whole block (every thread calls it with the same i and bh).
 template <typename TIn, int D>
-__global__ __launch_bounds__(G_NT) void lla_parallax_exact_kernel(
+__device__ __forceinline__ void parallax_exact_row(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, const TIn* __restrict__ rho,
-    float* __restrict__ out, float* __restrict__ stats, int n, int BH, double inv_h) {
+    float* __restrict__ out, float* __restrict__ stats, int n, double inv_h, int i, int bh) {
     constexpr int KL = G_NT / D;   // key lanes of the per-feature sums
     __shared__ double qs[D], rs[D], kbar[D], vbar[D];
     __shared__ double ws[G_CHK];
     __shared__ double red[G_NT];
     const int tid = threadIdx.x;
-    const int i = n - 1 - static_cast<int>(blockIdx.x / BH);   // longest rows first
-    const int bh = static_cast<int>(blockIdx.x % BH);
     const int64_t base = static_cast<int64_t>(bh) * n * D;
     const int cnt = i + 1;
     for (int e = tid; e < D; e += G_NT) {
@@ -533,6 +562,33 @@ __global__ __launch_bounds__(G_NT) void lla_parallax_exact_kernel(
     }
     if (stats != nullptr && tid == 0)   // the row's log-sum-exp of the scores, base 2
         stats[static_cast<int64_t>(bh) * n + i] = static_cast<float>((m + log(omega)) * 1.4426950408889634);
+    __syncthreads();   // the shared arrays are free for the block's next row
+}
+
+template <typename TIn, int D>
+__global__ __launch_bounds__(G_NT) void lla_parallax_exact_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v, const TIn* __restrict__ rho,
+    float* __restrict__ out, float* __restrict__ stats, int n, int BH, double inv_h) {
+    const int i = n - 1 - static_cast<int>(blockIdx.x / BH);   // longest rows first
+    const int bh = static_cast<int>(blockIdx.x % BH);
+    parallax_exact_row<TIn, D>(q, k, v, rho, out, stats, n, inv_h, i, bh);
+}
+
+// The rows of the heads the matrix-core kernel listed (range guard), by the same fp64 row
+// code: a fixed grid strides over (listed head, row) pairs, longest rows first; with no head
+// listed every block exits at once.
+constexpr int G_FALLBACK_BLOCKS = 512;
+__global__ __launch_bounds__(G_NT) void lla_parallax_fallback_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ rho, float* __restrict__ out, float* __restrict__ stats,
+    const unsigned* __restrict__ nlisted, const int* __restrict__ hlist, int n, double inv_h) {
+    const unsigned nh = *nlisted;
+    const int64_t items = static_cast<int64_t>(nh) * n;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int bh = hlist[it % nh];
+        const int i = n - 1 - static_cast<int>(it / nh);
+        parallax_exact_row<uint16_t, FD>(q, k, v, rho, out, stats, n, inv_h, i, bh);
+    }
 }
 
 template <typename TIn, int D>
@@ -559,9 +615,10 @@ hipError_t launch_parallax_exact_d(const Problem& p) {
 }
 
 // Workspace: tile images [B*H][tiles][X_TILE] | tile key sums [B*H][tiles][d] floats |
-// tile max key norms [B*H][tiles] floats, regions 256-byte aligned.
+// tile max key norms [B*H][tiles] floats | tile max |v| [B*H][tiles] floats | count of
+// listed heads (one unsigned) | listed heads [B*H] ints, regions 256-byte aligned.
 struct ParallaxLayout {
-    int64_t img, ksum, kmax, total;
+    int64_t img, ksum, kmax, vmax, nlisted, hlist, total;
 };
 
 ParallaxLayout parallax_layout(int64_t BH, int64_t n) {
@@ -571,7 +628,10 @@ ParallaxLayout parallax_layout(int64_t BH, int64_t n) {
     L.img = 0;
     L.ksum = L.img + up(BH * tiles * X_TILE);
     L.kmax = L.ksum + up(BH * tiles * FD * 4);
-    L.total = L.kmax + up(BH * tiles * 4);
+    L.vmax = L.kmax + up(BH * tiles * 4);
+    L.nlisted = L.vmax + up(BH * tiles * 4);
+    L.hlist = L.nlisted + up(4);
+    L.total = L.hlist + up(BH * 4);
     return L;
 }
 
@@ -596,11 +656,14 @@ hipError_t launch_parallax_fast(const Problem& p, void* workspace) {
     unsigned char* img = ws + L.img;
     float* ksum = reinterpret_cast<float*>(ws + L.ksum);
     float* kmax = reinterpret_cast<float*>(ws + L.kmax);
+    float* vmax = reinterpret_cast<float*>(ws + L.vmax);
+    unsigned* nlisted = reinterpret_cast<unsigned*>(ws + L.nlisted);
+    int* hlist = reinterpret_cast<int*>(ws + L.hlist);
     const auto* k = static_cast<const uint16_t*>(p.k);
     const auto* v = static_cast<const uint16_t*>(p.v);
     prof_begin(p.stream, "lla_parallax_pack_kernel");
     lla_parallax_pack_kernel<<<dim3(static_cast<unsigned>(BH) * ptiles), dim3(256), 0, p.stream>>>(
-        k, v, img, ksum, kmax, n, ptiles);
+        k, v, img, ksum, kmax, vmax, nlisted, n, ptiles);
     prof_end(p.stream);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -608,12 +671,21 @@ hipError_t launch_parallax_fast(const Problem& p, void* workspace) {
     prof_begin(p.stream, "lla_parallax_kernel");
     if (p.stats != nullptr)
         lla_parallax_kernel<true><<<dim3(blocks), dim3(X_WAVES * 64), 0, p.stream>>>(
-            static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.rho), img, ksum, kmax, p.out, p.stats,
-            n, BH, static_cast<float>(LOG2E / p.h));
+            static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.rho), img, ksum, kmax, vmax, nlisted,
+            hlist, p.out, p.stats, n, BH, static_cast<float>(LOG2E / p.h));
     else
         lla_parallax_kernel<false><<<dim3(blocks), dim3(X_WAVES * 64), 0, p.stream>>>(
-            static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.rho), img, ksum, kmax, p.out, nullptr,
-            n, BH, static_cast<float>(LOG2E / p.h));
+            static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.rho), img, ksum, kmax, vmax, nlisted,
+            hlist, p.out, nullptr, n, BH, static_cast<float>(LOG2E / p.h));
+    prof_end(p.stream);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t rows_all = static_cast<int64_t>(BH) * n;
+    const unsigned fb = static_cast<unsigned>(rows_all < G_FALLBACK_BLOCKS ? rows_all : G_FALLBACK_BLOCKS);
+    prof_begin(p.stream, "lla_parallax_fallback_kernel");
+    lla_parallax_fallback_kernel<<<dim3(fb), dim3(G_NT), 0, p.stream>>>(
+        static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k), static_cast<const uint16_t*>(p.v),
+        static_cast<const uint16_t*>(p.rho), p.out, p.stats, nlisted, hlist, n, 1.0 / p.h);
     prof_end(p.stream);
     return hipGetLastError();
 }

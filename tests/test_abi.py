@@ -291,12 +291,14 @@ def test_cg_path_is_an_lla_path_with_a_row_list_scratch():
 def parallax_workspace_bytes(BH, n):
     """Scratch of the Parallax matrix-core path: per head and 64-key tile the image (bf16 K
     key-major with 72-half rows, fp16 V feature-major with 68-half rows, padded to whole KiB),
-    the tile key sum (64 floats) and the largest key norm (one float), each region rounded
-    up to 256 B."""
+    the tile key sum (64 floats), the largest key norm and the largest |v| (one float each);
+    then the count of heads left to the fp64 fallback (one unsigned) and their list (one int
+    per head); each region rounded up to 256 B."""
     up = lambda x: (x + 255) // 256 * 256
     tiles = -(-n // 64)
     image = -(-(64 * 72 * 2 + 64 * 68 * 2) // 1024) * 1024
-    return up(BH * tiles * image) + up(BH * tiles * 64 * 4) + up(BH * tiles * 4)
+    return (up(BH * tiles * image) + up(BH * tiles * 64 * 4) + 2 * up(BH * tiles * 4) + up(4)
+            + up(BH * 4))
 
 
 def test_parallax_workspace_size_and_paths():

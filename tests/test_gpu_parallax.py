@@ -125,6 +125,43 @@ def test_key_offset():
     check(got, ref, w.dtype, "fast", "keys + 4")
 
 
+@pytest.mark.parametrize("scale", [2.0 ** -16, 2.0 ** 17])
+def test_value_range_guard(scale):
+    # The matrix-core path holds the values as fp16: a head whose largest |v| falls below
+    # 2^-10 or reaches 2^16 goes to the fp64 row code instead.  Only head 1 of three is
+    # scaled (a power of two, exact in bf16); every row of every head is compared, and the
+    # listed head must carry the fp64 path's accuracy.
+    require_gpu()
+    w, q, k, v, rho = arrays("parallax_d24", B=1, H=3, n=333)
+    v2 = v.copy()
+    v2[:, 1] = lla_inputs.round_to_bf16((v[:, 1] * scale).astype(np.float32))
+    ref = oracle_forward(q, k, v2, rho, w.h)
+    got = run(q, k, v2, rho, w.dtype, w.h, path="auto")
+    check(got, ref, w.dtype, "fast", f"head 1 values x {scale:g}")
+    listed = float(row_errors(got[:, 1:2], ref[:, 1:2]).max())
+    assert listed <= EXACT_BOUND, listed
+
+
+def test_value_range_guard_list_is_per_call():
+    # Two calls on one workspace: the first lists a head, the second (values in range) must
+    # not run the fp64 code over a stale list -- its result equals a fresh call's, bitwise.
+    torch = require_gpu()
+    from local_linear_attention_amd import lla_parallax_forward, lla_parallax_forward_ws, lla_parallax_workspace_size
+    w, q, k, v, rho = arrays("parallax_d24", B=1, H=2, n=300)
+    v2 = v.copy()
+    v2[:, 0] = lla_inputs.round_to_bf16((v[:, 0] * 2.0 ** 18).astype(np.float32))
+    tq, tk, tv, tv2, tr = (to_device(x, "bf16") for x in (q, k, v, v2, rho))
+    ws = torch.empty(lla_parallax_workspace_size(w.B, w.H, w.n, w.d, "bf16", "fast"), dtype=torch.uint8,
+                     device="cuda")
+    first = lla_parallax_forward_ws(tq, tk, tv2, tr, w.h, ws, path="fast")
+    second = lla_parallax_forward_ws(tq, tk, tv, tr, w.h, ws, path="fast")
+    fresh = lla_parallax_forward(tq, tk, tv, tr, w.h, path="fast")
+    torch.cuda.synchronize()
+    assert torch.equal(second, fresh)
+    ref = oracle_forward(q, k, v2, rho, w.h)
+    check(first.cpu().numpy().astype(np.float64), ref, w.dtype, "fast", "head 0 values x 2^18")
+
+
 def test_workspace_entry_point_matches():
     torch = require_gpu()
     from local_linear_attention_amd import (LLAError, lla_parallax_forward, lla_parallax_forward_ws,
@@ -153,7 +190,8 @@ def test_profiling_records_each_kernel():
     finally:
         lla_profile_enable(False)
     torch.cuda.synchronize()
-    assert [name for name, _ in rec] == ["lla_parallax_pack_kernel", "lla_parallax_kernel"]
+    assert [name for name, _ in rec] == ["lla_parallax_pack_kernel", "lla_parallax_kernel",
+                                         "lla_parallax_fallback_kernel"]
     assert all(ms > 0 for _, ms in rec)
 
 
