@@ -447,8 +447,10 @@ constexpr int K_WLOADS = (K_LOADS + B_WAVES - 1) / B_WAVES;
 constexpr int K_SW = K_IMG;                  // sqrt-weights [query][key], rows of M_LD halves
 constexpr int K_SW2 = K_SW + K_BQ * M_LD * 2;   // fp16 weights, 16 rows (rows >= K_BQ zero)
 constexpr int K_BUF = K_SW2 + 16 * M_LD * 2;
-constexpr int GS_LD = 68;                    // solve staging: row stride (floats)
-constexpr int GS_QS = 16 * GS_LD + 16;       // query stride: the 4 queries' rows on distinct banks
+// Solve staging, per query: a 64 x 16 float array T[col][t] (a block row of the matrix,
+// transposed), its 16-byte chunks XOR-swizzled by bits 1-2 of col so that the 16-byte reads
+// and writes of 8 consecutive lanes fall on distinct bank groups.
+constexpr int GS_QS = 16 * 68 + 16;          // query stride (floats)
 constexpr int K_SOLVE_FLOATS = KQ * GS_QS + KQ * FD;   // per wave: staging + pivots
 constexpr int K_SOLVE_BYTES = K_SOLVE_FLOATS * 4 * B_WAVES;
 constexpr int K_MEAN_OFF = K_SOLVE_BYTES > M_NBUF * K_BUF ? K_SOLVE_BYTES : M_NBUF * K_BUF;
@@ -501,6 +503,9 @@ __device__ __forceinline__ float row_bcast(float x, int p) {
 // C_IJ -= L_IK D_K L_JK^T (fp32 16x16x4 MFMAs, per query) of the blocks still in the
 // accumulators; the multipliers stay in registers for the back substitution, which forms
 // each y_P as x_P minus a row-of-16 reduction.  Returns y in yr[j].
+// Offset (floats) of chunk tc (entries 4 tc .. 4 tc + 3) of column col in a query's staging.
+__device__ __forceinline__ int gs_chunk(int col, int tc) { return col * 16 + ((tc ^ ((col >> 1) & 3)) << 2); }
+
 // Panel K of group_solve (a template, so that every register index is a constant).
 template <int K>
 __device__ __forceinline__ void group_panel(float4v (&ckk)[KQ][10], float (&zr)[4], const float thr,
@@ -509,24 +514,30 @@ __device__ __forceinline__ void group_panel(float4v (&ckk)[KQ][10], float (&zr)[
                                             const int c) {
     const int G = g, l = c;   // row layout: query G, row offset l
     float* Dg = Sg + KQ * GS_QS;
-    // Block row K of every query, ridge on the diagonal: Sg[q][t][col] = C_q[16 K + t][col].
+    // Block row K of every query, ridge on the diagonal, transposed: T_q[col][t] =
+    // C_q[16 K + t][col]; lane (g, c) holds t = 4g .. 4g + 3 of column 16 J + c, one chunk.
 #pragma unroll
     for (int q = 0; q < KQ; ++q)
 #pragma unroll
-        for (int J = K; J < 4; ++J)
+        for (int J = K; J < 4; ++J) {
+            float4v val = ckk[q][ublk(K, J)];
+            if (J == K) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float val = ckk[q][ublk(K, J)][r];
-                if (J == K) val += 4 * g + r == c ? lam[q] : 0.0f;
-                Sg[q * GS_QS + (4 * g + r) * GS_LD + 16 * J + c] = val;
+                for (int r = 0; r < 4; ++r) val[r] += 4 * g + r == c ? lam[q] : 0.0f;
             }
+            *reinterpret_cast<float4v*>(Sg + q * GS_QS + gs_chunk(16 * J + c, g)) = val;
+        }
     LDS_FENCE();
     // Panel rows of this lane's query: Lf[j][t] = C[16 K + t][l + 16 j] = C[l + 16 j][16 K + t].
     float Lf[4][16];
 #pragma unroll
     for (int j = K; j < 4; ++j)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) Lf[j][t] = Sg[G * GS_QS + t * GS_LD + 16 * j + l];
+        for (int tc = 0; tc < 4; ++tc) {
+            const float4v x = *reinterpret_cast<const float4v*>(Sg + G * GS_QS + gs_chunk(16 * j + l, tc));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Lf[j][4 * tc + r] = x[r];
+        }
     LDS_FENCE();
     // Rank-one downdate, applied to each entry once, as its panel is staged (the trailing
     // updates are linear, so it commutes with them): C -= S_k S_k^T / omega'.
@@ -568,23 +579,29 @@ __device__ __forceinline__ void group_panel(float4v (&ckk)[KQ][10], float (&zr)[
 #pragma unroll
         for (int t = 0; t < 16; ++t) Lk[K][j][t] = Lf[j][t];
     if (K < 3) {
-        // Multipliers of the later blocks' rows and the pivots, read back per query as
-        // MFMA operands over the panel columns 16 K + 4 s + g (K-slot g of step s).
+        // Multipliers of the later blocks' rows (transposed as above: T[l + 16 j][t] =
+        // L[l + 16 j][16 K + t]) and the pivots, read back per query as MFMA operands over
+        // the panel columns 16 K + 4 g + s (K-slot g of step s: one chunk per operand).
 #pragma unroll
         for (int j = K + 1; j < 4; ++j)
 #pragma unroll
-            for (int t = 0; t < 16; ++t) Sg[G * GS_QS + t * GS_LD + 16 * j + l] = Lf[j][t];
+            for (int tc = 0; tc < 4; ++tc)
+                *reinterpret_cast<float4v*>(Sg + G * GS_QS + gs_chunk(16 * j + l, tc)) =
+                    float4v{Lf[j][4 * tc], Lf[j][4 * tc + 1], Lf[j][4 * tc + 2], Lf[j][4 * tc + 3]};
         Dg[G * FD + 16 * K + l] = d;
         LDS_FENCE();
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
             float dv[4], Lo[4][4];
+            const float4v dq = *reinterpret_cast<const float4v*>(Dg + q * FD + 16 * K + 4 * g);
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                dv[s4] = Dg[q * FD + 16 * K + 4 * s4 + g];
+            for (int X = K + 1; X < 4; ++X) {
+                const float4v x = *reinterpret_cast<const float4v*>(Sg + q * GS_QS + gs_chunk(16 * X + c, g));
 #pragma unroll
-                for (int X = K + 1; X < 4; ++X) Lo[X][s4] = Sg[q * GS_QS + (4 * s4 + g) * GS_LD + 16 * X + c];
+                for (int s4 = 0; s4 < 4; ++s4) Lo[X][s4] = x[s4];
             }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) dv[s4] = dq[s4];
 #pragma unroll
             for (int I = K + 1; I < 4; ++I)
 #pragma unroll
