@@ -125,6 +125,34 @@ def test_forward_log_sum_exp(path):
     assert err <= (1e-3 if path == "fast" else 1e-5)
 
 
+def test_forward_range_guard_stats_feed_the_backward():
+    # A head whose values the forward's matrix-core path cannot hold as fp16 (x 2^17) runs on
+    # the fp64 row code, which also writes that head's log-sum-exp: it must agree with the
+    # definition like the matrix-core rows' do, and the backward fed with it must still meet
+    # the bar on every gradient row of every head.
+    torch = require_gpu()
+    from local_linear_attention_amd import lla_parallax_forward_stats
+    w, q, k, v, rho, dout = arrays("parallax_d24", B=1, H=2, n=300)
+    v = v.copy()
+    v[:, 1] = lla_inputs.round_to_bf16((v[:, 1] * 2.0 ** 17).astype(np.float32))
+    t = [to_device(x, "bf16") for x in (q, k, v, rho)]
+    _, lse = lla_parallax_forward_stats(*t, w.h, path="fast")
+    torch.cuda.synchronize()
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    q64, k64 = q.astype(np.float64), k.astype(np.float64)
+    for hh in range(w.H):
+        s = q64[0, hh] @ k64[0, hh].T / w.h
+        s[np.triu_indices(w.n, 1)] = -np.inf
+        m = s.max(-1)
+        ref_lse = (m + np.log(np.sum(np.exp(s - m[:, None]), -1))) / np.log(2.0)
+        err = float(np.max(np.abs(got_lse[0, hh] - ref_lse)))
+        print(f"[parallax lse, head {hh} values x {2 ** 17 if hh == 1 else 1}] max abs error {err:.2e}", flush=True)
+        assert err <= (1e-5 if hh == 1 else 1e-3)
+    got = run(q, k, v, rho, dout, "bf16", w.h, "fast")
+    ref = oracle_backward(q, k, v, rho, w.h, dout)
+    check(got, ref, "bf16", "fast", "head 1 values x 2^17")
+
+
 def test_zero_probe_and_determinism():
     require_gpu()
     w, q, k, v, rho, dout = arrays("parallax_d24", B=1, H=2, n=200)
